@@ -1,0 +1,215 @@
+"""CPU oracle for the fused SwiGLU MLP GEMM -- TEST INFRASTRUCTURE ONLY.
+
+Only the test suite, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import this package.  The HIP library and its Python binding
+never import, link or call it, and it imports nothing from them: the two sides
+meet only in the tests, through the bf16 bit patterns the seeded input
+generator produces.
+
+The arithmetic lives in ``oracle.c`` (plain C, fp32, k-ascending sums, no FMA
+contraction), which follows the gist.science page "Riepilogo Tecnico:
+Sovrapposizione delle Attivazioni a Livello di Tile per l'Inferenza Efficiente
+di LLM" (summary of arXiv 2607.02521):
+
+* §Definizione del Problema -- Y = SiLU(A x W1) (.) (A x W2);
+* §Metodologia, Kernel-2 -- W_fused [K, 2N], Gate in even, Up in odd columns;
+* §Contributi Chiave, item 3 -- accuracy is judged against an FP32 reference.
+
+This module only marshals numpy arrays to the C functions.  Every function
+here is pinned by CPU tests against facts that do not come from it (exact
+brute force, closed forms, invariants, a float64 cross-check).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+
+LAYOUT_SEPARATE = 0
+LAYOUT_INTERLEAVED = 1
+
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile oracle.c with gcc into liboracle.so (fp32, no FMA contraction)."""
+    if force or not os.path.exists(_LIB):
+        tmp = _LIB + ".tmp"
+        cmd = ["gcc", "-O2", "-std=c11", "-ffp-contract=off", "-fno-fast-math",
+               "-fPIC", "-shared", "-pthread", "-o", tmp, _SRC, "-lm"]
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB):
+        build(force=False)
+    lib = ctypes.CDLL(_LIB)
+    p, i64, c_int = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+    for name in ("oracle_swiglu_rows", "oracle_swiglu_cols"):
+        fn = getattr(lib, name)
+        fn.argtypes = [p, p, p, c_int, i64, i64, i64, p, i64, p, p, p, c_int]
+        fn.restype = c_int
+    lib.oracle_silu.argtypes = [p, p, i64]
+    lib.oracle_gate.argtypes = [p, p, p, i64]
+    lib.oracle_round_bf16.argtypes = [p, p, i64]
+    lib.oracle_decode_bf16.argtypes = [p, p, i64]
+    lib.oracle_pack_interleaved.argtypes = [p, p, p, i64, i64]
+    for fn in (lib.oracle_silu, lib.oracle_gate, lib.oracle_round_bf16,
+               lib.oracle_decode_bf16, lib.oracle_pack_interleaved):
+        fn.restype = None
+    _lib = lib
+    return lib
+
+
+def default_threads() -> int:
+    try:
+        return max(1, len(os.sched_getaffinity(0)))
+    except AttributeError:  # pragma: no cover
+        return max(1, os.cpu_count() or 1)
+
+
+def _u16(x, name):
+    x = np.ascontiguousarray(x)
+    if x.dtype != np.uint16:
+        raise TypeError(f"{name} must hold bf16 bit patterns as uint16, got {x.dtype}")
+    return x
+
+
+def _ptr(x):
+    return None if x is None else x.ctypes.data
+
+
+def _shapes(a, w1, w2, layout):
+    a = _u16(a, "A")
+    M, K = a.shape
+    w1 = _u16(w1, "W1")
+    if layout == LAYOUT_INTERLEAVED:
+        if w1.shape[0] != K or w1.shape[1] % 2:
+            raise ValueError("W_fused must be [K, 2N]")
+        N = w1.shape[1] // 2
+        w2 = None
+    else:
+        w2 = _u16(w2, "W2")
+        if w1.shape != w2.shape or w1.shape[0] != K:
+            raise ValueError("W1 and W2 must both be [K, N]")
+        N = w1.shape[1]
+    return a, w1, w2, M, N, K
+
+
+def swiglu_rows(a, w1, w2=None, layout=LAYOUT_SEPARATE, rows=None,
+                with_gate_up=False, nthreads=None):
+    """fp32 y = SiLU(g) * u (and optionally g, u) for the listed rows.
+
+    a: uint16 [M, K]; w1, w2: uint16 [K, N] (separate) or w1 = W_fused
+    uint16 [K, 2N] (interleaved).  Returns y [len(rows), N] (all rows when
+    rows is None), or (y, g, u).
+    """
+    a, w1, w2, M, N, K = _shapes(a, w1, w2, layout)
+    lib = _load()
+    if rows is None:
+        ridx, nr = None, M
+    else:
+        ridx = np.ascontiguousarray(rows, dtype=np.int64)
+        nr = ridx.size
+    y = np.empty((nr, N), np.float32)
+    g = np.empty((nr, N), np.float32) if with_gate_up else None
+    u = np.empty((nr, N), np.float32) if with_gate_up else None
+    rc = lib.oracle_swiglu_rows(_ptr(a), _ptr(w1), _ptr(w2), layout, M, N, K,
+                                _ptr(ridx), nr, _ptr(y), _ptr(g), _ptr(u),
+                                nthreads or default_threads())
+    if rc < 0:
+        raise ValueError("oracle_swiglu_rows rejected its arguments")
+    return (y, g, u) if with_gate_up else y
+
+
+def swiglu_cols(a, w1, w2=None, layout=LAYOUT_SEPARATE, cols=(),
+                with_gate_up=False, nthreads=None):
+    """fp32 y (and optionally g, u) for every row and the listed columns: [M, len(cols)]."""
+    a, w1, w2, M, N, K = _shapes(a, w1, w2, layout)
+    lib = _load()
+    cidx = np.ascontiguousarray(cols, dtype=np.int64)
+    nc = cidx.size
+    y = np.empty((M, nc), np.float32)
+    g = np.empty((M, nc), np.float32) if with_gate_up else None
+    u = np.empty((M, nc), np.float32) if with_gate_up else None
+    rc = lib.oracle_swiglu_cols(_ptr(a), _ptr(w1), _ptr(w2), layout, M, N, K,
+                                _ptr(cidx), nc, _ptr(y), _ptr(g), _ptr(u),
+                                nthreads or default_threads())
+    if rc < 0:
+        raise ValueError("oracle_swiglu_cols rejected its arguments")
+    return (y, g, u) if with_gate_up else y
+
+
+def swiglu(a, w1, w2=None, layout=LAYOUT_SEPARATE, nthreads=None):
+    """fp32 y for the whole [M, N] output."""
+    return swiglu_rows(a, w1, w2, layout, None, False, nthreads)
+
+
+def silu(x):
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    out = np.empty_like(x)
+    _load().oracle_silu(_ptr(x), _ptr(out), x.size)
+    return out
+
+
+def gate(g, u):
+    """fp32 SiLU(g) * u element-wise."""
+    g = np.ascontiguousarray(g, dtype=np.float32)
+    u = np.ascontiguousarray(u, dtype=np.float32)
+    if g.shape != u.shape:
+        raise ValueError("g and u differ in shape")
+    y = np.empty_like(g)
+    _load().oracle_gate(_ptr(g), _ptr(u), _ptr(y), g.size)
+    return y
+
+
+def round_bf16(x):
+    """fp32 -> bf16 bit patterns (uint16), round to nearest even."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    out = np.empty(x.shape, np.uint16)
+    _load().oracle_round_bf16(_ptr(x), _ptr(out), x.size)
+    return out
+
+
+def decode_bf16(x):
+    """bf16 bit patterns (uint16) -> exact fp32."""
+    x = _u16(x, "x")
+    out = np.empty(x.shape, np.float32)
+    _load().oracle_decode_bf16(_ptr(x), _ptr(out), x.size)
+    return out
+
+
+def pack_interleaved(w1, w2):
+    """W_fused [K, 2N] from W1, W2 [K, N]: even columns Gate, odd columns Up."""
+    w1 = _u16(w1, "W1")
+    w2 = _u16(w2, "W2")
+    if w1.shape != w2.shape:
+        raise ValueError("W1 and W2 differ in shape")
+    K, N = w1.shape
+    wf = np.empty((K, 2 * N), np.uint16)
+    _load().oracle_pack_interleaved(_ptr(w1), _ptr(w2), _ptr(wf), K, N)
+    return wf
+
+
+def swiglu_unfused_emulation(a, w1, w2, rows=None, nthreads=None):
+    """What an unfused pipeline that stores Gate and Up as bf16 computes.
+
+    Returns (y_fp32, g_bf16_bits, u_bf16_bits): y = SiLU(bf16(g)) * bf16(u) in
+    fp32, for the listed rows (all when None).  The page's baseline writes both
+    intermediates to HBM between the GEMMs and the activation (§Definizione
+    del Problema); bf16 is the storage type of those tensors here.
+    """
+    _, g, u = swiglu_rows(a, w1, w2, LAYOUT_SEPARATE, rows, True, nthreads)
+    gb, ub = round_bf16(g), round_bf16(u)
+    return gate(decode_bf16(gb), decode_bf16(ub)), gb, ub

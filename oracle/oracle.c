@@ -1,0 +1,292 @@
+/*
+ * oracle.c -- plain CPU reference for the fused SwiGLU MLP GEMM.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing on the product path may include, link,
+ * load or call this file: only the test suite, the smoke check and the
+ * benchmark's CPU-baseline leg use it.  It shares no header, source, table or
+ * helper with the HIP library; both sides receive the same bf16 bit patterns
+ * from the seeded input generator and nothing else.
+ *
+ * Source of truth: the gist.science page "Riepilogo Tecnico: Sovrapposizione
+ * delle Attivazioni a Livello di Tile per l'Inferenza Efficiente di LLM"
+ * (a summary of arXiv 2607.02521), cited below as [RT].
+ *
+ *   [RT §Definizione del Problema]  the gated MLP output is
+ *       Y = SiLU(A x W1) (.) (A x W2): two independent matrix products, then an
+ *       element-wise gate (SiLU of the first product times the second).
+ *   [RT §Metodologia, Kernel-2]      the fused weight W_fused has K rows and
+ *       2N columns; column 2n holds W1[:,n] (Gate) and column 2n+1 holds
+ *       W2[:,n] (Up); the epilogue pairs D[m,2n] with D[m,2n+1].
+ *   [RT §Contributi Chiave, item 3] accuracy is judged against an FP32
+ *       reference, so this oracle works in fp32 (the page fixes the precision).
+ *
+ * Arithmetic, element by element (this is the plain definition; loops may be
+ * interchanged but every output element sees exactly this sequence):
+ *     a, w1, w2 : exact fp32 decodes of the bf16 inputs (bits << 16)
+ *     g = ((a[m,0]*w1[0,n]) + a[m,1]*w1[1,n]) + ... ,  k ascending, each
+ *         product and each sum rounded to fp32 separately (no FMA contraction:
+ *         build with -ffp-contract=off)
+ *     u = the same with w2
+ *     s = g / (1 + expf(-g))             SiLU with beta = 1 ("Swish")
+ *     y = s * u                            fp32, returned unrounded
+ * Rounding to bf16 (round-to-nearest-even) is a separate, explicit step.
+ *
+ * Parity pins (the tests check this file against facts that do not come from
+ * it): exact brute force with correctly rounded sums on tiny shapes, SiLU
+ * closed forms, the A = I special case, invariants (W1 = 0 or W2 = 0 gives 0,
+ * interleaved equals separate bit for bit, permutation equivariance, scaling
+ * W2 by a power of two scales Y by it) and a float64 cross-check at full size.
+ */
+#include <math.h>
+#include <pthread.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define ORACLE_LAYOUT_SEPARATE 0
+#define ORACLE_LAYOUT_INTERLEAVED 1
+
+/* Exact decode of a bf16 bit pattern: bf16 is the upper half of an fp32. */
+static float bf16_to_f32(uint16_t h) {
+  uint32_t bits = (uint32_t)h << 16;
+  float f;
+  memcpy(&f, &bits, sizeof f);
+  return f;
+}
+
+/* fp32 -> bf16, round to nearest, ties to even, on the bit pattern.
+ * NaN stays NaN (quietened); infinities and overflow behave as IEEE rounding
+ * says (values that round past the largest finite bf16 become infinity). */
+static uint16_t f32_to_bf16_rne(float f) {
+  uint32_t bits;
+  memcpy(&bits, &f, sizeof bits);
+  if ((bits & 0x7f800000u) == 0x7f800000u && (bits & 0x007fffffu) != 0u)
+    return (uint16_t)((bits >> 16) | 0x0040u);
+  uint32_t lsb = (bits >> 16) & 1u;
+  bits += 0x7fffu + lsb;
+  return (uint16_t)(bits >> 16);
+}
+
+/* SiLU(x) = x * sigmoid(x) = x / (1 + e^-x), in fp32.  For x << 0 the
+ * exponential overflows to +inf and the quotient is -0; for x >> 0 it is x. */
+static float silu_f32(float x) { return x / (1.0f + expf(-x)); }
+
+/* Weight element w_t[k, n] for t = 0 (Gate, W1) or t = 1 (Up, W2) under either
+ * storage layout.  Separate: W1, W2 are row-major [K, N].  Interleaved:
+ * W_fused is row-major [K, 2N] with Gate in even and Up in odd columns. */
+static float weight_at(const uint16_t* w1, const uint16_t* w2, int layout,
+                       int64_t N, int64_t k, int64_t n, int t) {
+  if (layout == ORACLE_LAYOUT_INTERLEAVED)
+    return bf16_to_f32(w1[k * 2 * N + 2 * n + t]);
+  return bf16_to_f32((t == 0 ? w1 : w2)[k * N + n]);
+}
+
+/* ------------------------------------------------------------------------ */
+/* Work split over threads: each worker takes a contiguous slice of a list  */
+/* of row (or column) indices.  Splitting never changes any element's sum.  */
+/* ------------------------------------------------------------------------ */
+typedef struct {
+  const uint16_t *a, *w1, *w2;
+  int layout;
+  int64_t M, N, K;
+  const int64_t* idx; /* rows (row mode) or columns (column mode) */
+  int64_t lo, hi;     /* slice of idx this worker owns */
+  float *y, *g, *u;   /* outputs; g, u may be NULL */
+} job_t;
+
+/* Row mode: output row r of y/g/u (length N) is model row idx[r].
+ * For one row, g[n] for all n is accumulated together with k as the outer
+ * loop; each g[n] still receives its terms in ascending k. */
+static void* rows_worker(void* p) {
+  job_t* j = (job_t*)p;
+  const int64_t N = j->N, K = j->K;
+  float* gacc = (float*)malloc(sizeof(float) * (size_t)(N > 0 ? N : 1));
+  float* uacc = (float*)malloc(sizeof(float) * (size_t)(N > 0 ? N : 1));
+  for (int64_t r = j->lo; r < j->hi; ++r) {
+    const int64_t m = j->idx[r];
+    for (int64_t n = 0; n < N; ++n) gacc[n] = 0.0f, uacc[n] = 0.0f;
+    for (int64_t k = 0; k < K; ++k) {
+      const float a = bf16_to_f32(j->a[m * K + k]);
+      if (j->layout == ORACLE_LAYOUT_INTERLEAVED) {
+        const uint16_t* wf = j->w1 + k * 2 * N; /* row k of W_fused */
+        for (int64_t n = 0; n < N; ++n) {
+          const float p1 = a * bf16_to_f32(wf[2 * n]);     /* Gate column */
+          const float p2 = a * bf16_to_f32(wf[2 * n + 1]); /* Up column */
+          gacc[n] = gacc[n] + p1;
+          uacc[n] = uacc[n] + p2;
+        }
+      } else {
+        const uint16_t* w1 = j->w1 + k * N; /* row k of W1 */
+        const uint16_t* w2 = j->w2 + k * N; /* row k of W2 */
+        for (int64_t n = 0; n < N; ++n) {
+          const float p1 = a * bf16_to_f32(w1[n]);
+          const float p2 = a * bf16_to_f32(w2[n]);
+          gacc[n] = gacc[n] + p1;
+          uacc[n] = uacc[n] + p2;
+        }
+      }
+    }
+    for (int64_t n = 0; n < N; ++n) {
+      const float s = silu_f32(gacc[n]);
+      j->y[r * N + n] = s * uacc[n];
+      if (j->g) j->g[r * N + n] = gacc[n];
+      if (j->u) j->u[r * N + n] = uacc[n];
+    }
+  }
+  free(gacc), free(uacc);
+  return NULL;
+}
+
+/* Column mode: output column c of y/g/u (each [M, ncols]) is model column
+ * idx[c].  The column of W1 and W2 is gathered once, then every row's dot
+ * product runs over k ascending -- the same sequence as row mode. */
+typedef struct {
+  job_t base;
+  int64_t ncols;
+} colsjob_t;
+
+static void* cols_worker(void* p) {
+  colsjob_t* cj = (colsjob_t*)p;
+  job_t* j = &cj->base;
+  const int64_t M = j->M, K = j->K, C = cj->ncols;
+  float* w1col = (float*)malloc(sizeof(float) * (size_t)(K > 0 ? K : 1));
+  float* w2col = (float*)malloc(sizeof(float) * (size_t)(K > 0 ? K : 1));
+  for (int64_t c = j->lo; c < j->hi; ++c) {
+    const int64_t n = j->idx[c];
+    for (int64_t k = 0; k < K; ++k) {
+      w1col[k] = weight_at(j->w1, j->w2, j->layout, j->N, k, n, 0);
+      w2col[k] = weight_at(j->w1, j->w2, j->layout, j->N, k, n, 1);
+    }
+    for (int64_t m = 0; m < M; ++m) {
+      float g = 0.0f, u = 0.0f;
+      for (int64_t k = 0; k < K; ++k) {
+        const float a = bf16_to_f32(j->a[m * K + k]);
+        const float p1 = a * w1col[k];
+        const float p2 = a * w2col[k];
+        g = g + p1;
+        u = u + p2;
+      }
+      const float s = silu_f32(g);
+      j->y[m * C + c] = s * u;
+      if (j->g) j->g[m * C + c] = g;
+      if (j->u) j->u[m * C + c] = u;
+    }
+  }
+  free(w1col), free(w2col);
+  return NULL;
+}
+
+static int run_split(void* (*fn)(void*), void* jobs, size_t job_size, int64_t count,
+                     int nthreads) {
+  if (nthreads < 1) nthreads = 1;
+  if (nthreads > 256) nthreads = 256;
+  if ((int64_t)nthreads > count) nthreads = (int)(count > 0 ? count : 1);
+  pthread_t th[256];
+  int started[256] = {0};
+  for (int t = 0; t < nthreads; ++t) {
+    job_t* j = (job_t*)((char*)jobs + (size_t)t * job_size);
+    j->lo = count * t / nthreads;
+    j->hi = count * (t + 1) / nthreads;
+    if (t > 0 && pthread_create(&th[t], NULL, fn, j) == 0) started[t] = 1;
+  }
+  /* thread 0's share (and any share whose thread could not start) runs here */
+  for (int t = 0; t < nthreads; ++t) {
+    if (t == 0 || !started[t]) fn((char*)jobs + (size_t)t * job_size);
+  }
+  for (int t = 1; t < nthreads; ++t)
+    if (started[t]) pthread_join(th[t], NULL);
+  return nthreads;
+}
+
+/*
+ * oracle_swiglu_rows: y (and optionally g, u) for the model rows listed in
+ * rows[0..nrows) (rows == NULL means all M rows in order).  Outputs are
+ * row-major [nrows, N] fp32.  w2 is ignored (may be NULL) when layout is
+ * interleaved, in which case w1 is W_fused [K, 2N].  Returns the number of
+ * threads used, or -1 on a bad argument.
+ */
+int oracle_swiglu_rows(const uint16_t* a, const uint16_t* w1, const uint16_t* w2,
+                       int layout, int64_t M, int64_t N, int64_t K,
+                       const int64_t* rows, int64_t nrows, float* y, float* g,
+                       float* u, int nthreads) {
+  if (M < 0 || N < 0 || K < 0 || nrows < 0 || !y) return -1;
+  if (layout != ORACLE_LAYOUT_SEPARATE && layout != ORACLE_LAYOUT_INTERLEAVED) return -1;
+  if (layout == ORACLE_LAYOUT_SEPARATE && K > 0 && N > 0 && (!w1 || !w2)) return -1;
+  int64_t* all = NULL;
+  if (!rows) {
+    nrows = M;
+    all = (int64_t*)malloc(sizeof(int64_t) * (size_t)(M > 0 ? M : 1));
+    for (int64_t i = 0; i < M; ++i) all[i] = i;
+    rows = all;
+  }
+  for (int64_t i = 0; i < nrows; ++i)
+    if (rows[i] < 0 || rows[i] >= M) {
+      free(all);
+      return -1;
+    }
+  job_t jobs[256];
+  for (int t = 0; t < 256; ++t) {
+    job_t j = {a, w1, w2, layout, M, N, K, rows, 0, 0, y, g, u};
+    jobs[t] = j;
+  }
+  int used = run_split(rows_worker, jobs, sizeof(job_t), nrows, nthreads);
+  free(all);
+  return used;
+}
+
+/*
+ * oracle_swiglu_cols: y (and optionally g, u) for every row and the model
+ * columns listed in cols[0..ncols); outputs are row-major [M, ncols] fp32.
+ * Bit-identical to oracle_swiglu_rows on shared elements.
+ */
+int oracle_swiglu_cols(const uint16_t* a, const uint16_t* w1, const uint16_t* w2,
+                       int layout, int64_t M, int64_t N, int64_t K,
+                       const int64_t* cols, int64_t ncols, float* y, float* g,
+                       float* u, int nthreads) {
+  if (M < 0 || N < 0 || K < 0 || ncols < 0 || !y || !cols) return -1;
+  if (layout != ORACLE_LAYOUT_SEPARATE && layout != ORACLE_LAYOUT_INTERLEAVED) return -1;
+  if (layout == ORACLE_LAYOUT_SEPARATE && K > 0 && N > 0 && (!w1 || !w2)) return -1;
+  for (int64_t i = 0; i < ncols; ++i)
+    if (cols[i] < 0 || cols[i] >= N) return -1;
+  colsjob_t jobs[256];
+  for (int t = 0; t < 256; ++t) {
+    job_t j = {a, w1, w2, layout, M, N, K, cols, 0, 0, y, g, u};
+    jobs[t].base = j;
+    jobs[t].ncols = ncols;
+  }
+  return run_split(cols_worker, jobs, sizeof(colsjob_t), ncols, nthreads);
+}
+
+/* Element-wise SiLU in fp32 (the same function the row/column paths use). */
+void oracle_silu(const float* x, float* out, int64_t n) {
+  for (int64_t i = 0; i < n; ++i) out[i] = silu_f32(x[i]);
+}
+
+/* Element-wise gate: y = SiLU(g) * u in fp32.  With g, u taken from bf16
+ * tensors this is what an unfused pipeline computes after materialising
+ * Gate and Up [RT §Definizione del Problema: the standard implementation
+ * writes both intermediates to HBM before the activation]. */
+void oracle_gate(const float* g, const float* u, float* y, int64_t n) {
+  for (int64_t i = 0; i < n; ++i) y[i] = silu_f32(g[i]) * u[i];
+}
+
+/* fp32 -> bf16 bit patterns, round to nearest even. */
+void oracle_round_bf16(const float* x, uint16_t* out, int64_t n) {
+  for (int64_t i = 0; i < n; ++i) out[i] = f32_to_bf16_rne(x[i]);
+}
+
+/* bf16 bit patterns -> fp32 (exact). */
+void oracle_decode_bf16(const uint16_t* x, float* out, int64_t n) {
+  for (int64_t i = 0; i < n; ++i) out[i] = bf16_to_f32(x[i]);
+}
+
+/* W_fused[k, 2n] = W1[k, n], W_fused[k, 2n+1] = W2[k, n]  [RT §Metodologia,
+ * Kernel-2]: a bit copy, no arithmetic. */
+void oracle_pack_interleaved(const uint16_t* w1, const uint16_t* w2, uint16_t* wf,
+                             int64_t K, int64_t N) {
+  for (int64_t k = 0; k < K; ++k)
+    for (int64_t n = 0; n < N; ++n) {
+      wf[k * 2 * N + 2 * n] = w1[k * N + n];
+      wf[k * 2 * N + 2 * n + 1] = w2[k * N + n];
+    }
+}
