@@ -1,0 +1,242 @@
+#!/usr/bin/env python3
+"""Benchmark of the fused SwiGLU MLP GEMM on one MI355X.
+
+One step = one fused forward Y = SiLU(A W1) (.) (A W2) over one batch of the
+chosen Qwen2.5-shaped workload (default: the Qwen2.5-1.5B MLP, M=2048, K=1536,
+N=8960), inputs already resident in HBM.  Batches rotate through enough copies
+of {A, W, Y} to exceed the 256 MB Infinity Cache several times, so every step
+streams its operands from HBM.  Prints ONE JSON line.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--layout L]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense BF16 MFMA
+PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
+METRIC = "fused SwiGLU GEMM TFLOP/s (bf16) and % MFMA peak, Qwen2.5-shaped MLPs"
+KERNEL_SRC = os.path.join(ROOT, "gemm_epilogues_mlp_amd", "csrc", "swiglu_kernels.hip")
+
+
+def kernel_source_hash() -> str:
+    return hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
+
+
+def parse():
+    p = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=200)
+    p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--workload", default="qwen2.5-1.5b-mlp")
+    p.add_argument("--layout", choices=["auto", "separate", "interleaved"], default="auto")
+    p.add_argument("--config", type=int, default=-1, help="force a fused config id")
+    p.add_argument("--rotate-bytes", type=float, default=1.0 * 2 ** 30,
+                   help="minimum footprint of the rotated buffers (bytes)")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-unfused", action="store_true")
+    p.add_argument("--copy-calibration", action="store_true",
+                   help="also run a 1 GiB device copy (counter calibration runs)")
+    return p.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures a single GPU; --gpus {args.gpus} is not supported "
+              "(the op needs no collective; see the sharding note in the design notes).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import gemm_epilogues_mlp_amd as sw
+    from gemm_epilogues_mlp_amd import inputs as I
+
+    wl = I.BY_NAME[args.workload]
+    M, K, N = wl.M, wl.K, wl.N
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    h = sw.swiglu_create(0)
+
+    a_np, w1_np, w2_np = I.workload_inputs(wl)
+    a0 = torch.from_numpy(a_np.view(np.int16)).to(dev)
+    w10 = torch.from_numpy(w1_np.view(np.int16)).to(dev)
+    w20 = torch.from_numpy(w2_np.view(np.int16)).to(dev)
+    stream = torch.cuda.current_stream()
+
+    if args.layout == "auto":
+        _, _, rec = sw.swiglu_query(h, M, N, K, sw.LAYOUT_SEPARATE)
+        layout = rec
+    else:
+        layout = sw.LAYOUT_INTERLEAVED if args.layout == "interleaved" else sw.LAYOUT_SEPARATE
+    variant, tile, _ = sw.swiglu_query(h, M, N, K, layout)
+    if args.config >= 0:
+        tile = sw.swiglu_config_info(args.config)
+
+    wf0 = None
+    if layout == sw.LAYOUT_INTERLEAVED:
+        wf0 = torch.empty((K, 2 * N), dtype=torch.int16, device=dev)
+        sw.swiglu_pack_interleaved(h, w10, w20, wf0, K, N)
+
+    set_bytes = wl.fused_bytes
+    nsets = max(1, int(np.ceil(args.rotate_bytes / set_bytes)))
+    sets = []
+    for i in range(nsets):
+        a = a0 if i == 0 else a0.clone()
+        if layout == sw.LAYOUT_INTERLEAVED:
+            ws = (wf0 if i == 0 else wf0.clone(), None)
+        else:
+            ws = (w10 if i == 0 else w10.clone(), w20 if i == 0 else w20.clone())
+        y = torch.empty((M, N), dtype=torch.int16, device=dev)
+        sets.append((a, ws[0], ws[1], y))
+    torch.cuda.synchronize()
+
+    def fused_step(i):
+        a, w1, w2, y = sets[i % nsets]
+        sw.swiglu_forward_ex(h, a, w1, w2, y, M, N, K, layout, sw.VARIANT_AUTO, args.config,
+                             stream)
+
+    def timed(step_fn, steps, warmup):
+        for i in range(warmup):
+            step_fn(i)
+        torch.cuda.synchronize()
+        start = torch.cuda.Event(enable_timing=True)
+        stop = torch.cuda.Event(enable_timing=True)
+        start.record(stream)
+        for i in range(steps):
+            step_fn(warmup + i)
+        stop.record(stream)
+        torch.cuda.synchronize()
+        return start.elapsed_time(stop) / steps  # ms per step
+
+    ms = timed(fused_step, args.steps, args.warmup)
+    tflops = wl.flops / (ms * 1e-3) / 1e12
+    hbm_gbs = wl.fused_bytes / (ms * 1e-3) / 1e9
+
+    # ---- unfused baseline on the same GEMM core (3 launches per step) -------
+    unfused = None
+    if not args.no_unfused:
+        ws_buf = torch.empty((2, M, N), dtype=torch.int16, device=dev)
+        usets = []
+        if layout == sw.LAYOUT_SEPARATE:
+            usets = [(s[0], s[1], s[2], s[3]) for s in sets]
+        else:
+            usets = [(a0, w10, w20, sets[0][3])]
+            for i in range(1, max(1, int(np.ceil(args.rotate_bytes / wl.unfused_bytes)))):
+                usets.append((a0.clone(), w10.clone(), w20.clone(),
+                              torch.empty((M, N), dtype=torch.int16, device=dev)))
+
+        def unfused_step(i):
+            a, w1, w2, y = usets[i % len(usets)]
+            sw.swiglu_forward_unfused(h, a, w1, w2, ws_buf, y, M, N, K, -1, stream)
+
+        ums = timed(unfused_step, max(10, args.steps // 2), max(3, args.warmup // 2))
+        unfused = {"ms_per_step": round(ums, 5),
+                   "tflops": round(wl.flops / (ums * 1e-3) / 1e12, 2),
+                   "fusion_speedup": round(ums / ms, 3),
+                   "gemm_tile": sw.swiglu_query_unfused(h, M, N, K)}
+        del usets, ws_buf
+
+    if args.copy_calibration:
+        src = torch.empty(2 ** 30 // 2, dtype=torch.int16, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    # ---- roofline of the dominant kernel (the fused kernel: 1 launch/step) --
+    bound = "mfma" if wl.flops / wl.fused_bytes > PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9) \
+        else "hbm"
+    if bound == "mfma":
+        roofline = {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS,
+                    "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4)}
+    else:
+        roofline = {"bound": "hbm", "achieved": round(hbm_gbs, 1), "peak": PEAK_HBM_GBS,
+                    "unit": "GB/s", "frac": round(hbm_gbs / PEAK_HBM_GBS, 4)}
+    roofline["traffic"] = counter_traffic(wl.name, layout, tile)
+
+    # ---- CPU baseline: the oracle on a bounded sample of the same workload --
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(wl, a_np, w1_np, w2_np)
+
+    line = {
+        "metric": METRIC,
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) activations, N(0,1/K) weights)",
+        "config": {"workload": wl.name, "M": M, "K": K, "N": N,
+                   "layout": "interleaved" if layout == sw.LAYOUT_INTERLEAVED else "separate",
+                   "variant": "interleave" if variant == sw.VARIANT_INTERLEAVE else "sync",
+                   "tile": tile, "rotated_sets": nsets, "parallelism": "single-gpu"},
+        "pct_mfma_peak": round(100 * tflops / PEAK_BF16_TFLOPS, 2),
+        "hbm_gbs_algorithmic": round(hbm_gbs, 1),
+        "unfused": unfused,
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    sw.swiglu_destroy(h)
+    print(json.dumps(line), flush=True)
+
+
+def counter_traffic(workload, layout, tile):
+    """HBM bytes per launch from the committed rocprofv3 counter summary for
+    this kernel configuration and workload, if it was taken on the current
+    kernel source; otherwise None."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        data = json.load(open(path))
+    except ValueError:
+        return None
+    key = f"{workload}/{'interleaved' if layout else 'separate'}/config{tile.get('id')}"
+    entry = data.get(key)
+    if not entry or entry.get("kernel_source_sha") != kernel_source_hash():
+        return None
+    return entry.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(wl, a, w1, w2):
+    """Time the CPU oracle (as it is) on a bounded row sample of the workload."""
+    import numpy as np
+
+    import oracle
+    nthreads = oracle.default_threads()
+    per_row = 4.0 * wl.N * wl.K
+    probe = min(wl.M, 8)
+    t0 = time.perf_counter()
+    oracle.swiglu_rows(a, w1, w2, rows=np.arange(probe), nthreads=nthreads)
+    dt = time.perf_counter() - t0
+    rate = probe * per_row / max(dt, 1e-9)
+    rows = int(min(wl.M, max(probe, 12.0 * rate / per_row)))  # about 12 s of work
+    t0 = time.perf_counter()
+    oracle.swiglu_rows(a, w1, w2, rows=np.arange(rows), nthreads=nthreads)
+    dt = time.perf_counter() - t0
+    return {"value": round(rows * per_row / dt / 1e12, 5), "unit": "TFLOP/s",
+            "cores": min(nthreads, rows), "kind": "oracle",
+            "sample": f"first {rows} of {wl.M} rows of Y (all {wl.N} columns), "
+                      f"{dt:.1f} s wall"}
+
+
+if __name__ == "__main__":
+    main()

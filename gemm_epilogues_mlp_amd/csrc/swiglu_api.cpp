@@ -1,0 +1,282 @@
+// swiglu_api.cpp -- the extern "C" boundary: argument checks, handle, dispatch.
+// Every check runs before anything is enqueued; see include/swiglu.h for the
+// contract of each entry point.
+#include "swiglu.h"
+
+#include <hip/hip_runtime_api.h>
+#include <stdio.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include <new>
+
+#include "swiglu_internal.h"
+
+struct swiglu_ctx {
+  int device;
+  int cu_count;
+  char arch[64];
+  int log;  // SWIGLU_LOG=1: print the configuration chosen for each call
+};
+
+namespace {
+
+using namespace swiglu;
+
+constexpr long long kMaxDim = 0x7fffffffLL;
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+// [p, p + bytes) and [q, q + qbytes) overlap (empty ranges never do)
+bool overlaps(const void* p, long long bytes, const void* q, long long qbytes) {
+  if (!p || !q || bytes <= 0 || qbytes <= 0) return false;
+  const uintptr_t a = (uintptr_t)p, b = (uintptr_t)q;
+  return a < b + (uintptr_t)qbytes && b < a + (uintptr_t)bytes;
+}
+
+swiglu_status_t check_device(const swiglu_ctx* h) {
+  int cur = -1;
+  if (hipGetDevice(&cur) != hipSuccess) return SWIGLU_ERR_DEVICE;
+  return cur == h->device ? SWIGLU_OK : SWIGLU_ERR_DEVICE;
+}
+
+// Shared argument validation of the forward entry points.  *noop is set when
+// there is nothing to compute (M == 0 or N == 0).
+swiglu_status_t check_forward(const swiglu_ctx* h, const void* A, const void* W1,
+                              const void* W2, const void* Y, int64_t M, int64_t N,
+                              int64_t K, int layout, bool* noop) {
+  *noop = false;
+  if (!h) return SWIGLU_ERR_INVALID_ARG;
+  if (M < 0 || N < 0 || K < 0) return SWIGLU_ERR_INVALID_ARG;
+  if (layout != SWIGLU_LAYOUT_SEPARATE && layout != SWIGLU_LAYOUT_INTERLEAVED)
+    return SWIGLU_ERR_INVALID_ARG;
+  if (layout == SWIGLU_LAYOUT_INTERLEAVED && W2 != nullptr) return SWIGLU_ERR_INVALID_ARG;
+  if (M == 0 || N == 0) {
+    *noop = true;
+    return SWIGLU_OK;
+  }
+  if (!Y) return SWIGLU_ERR_INVALID_ARG;
+  if (K > 0) {
+    if (!A || !W1) return SWIGLU_ERR_INVALID_ARG;
+    if (layout == SWIGLU_LAYOUT_SEPARATE && !W2) return SWIGLU_ERR_INVALID_ARG;
+  }
+  if (M > kMaxDim || K > kMaxDim || N > (kMaxDim >> 1)) return SWIGLU_ERR_UNSUPPORTED;
+  if (N % 8 != 0 || K % 8 != 0) return SWIGLU_ERR_UNSUPPORTED;
+  if (!aligned16(Y) || !aligned16(A) || !aligned16(W1) || !aligned16(W2))
+    return SWIGLU_ERR_UNSUPPORTED;
+  const long long ybytes = 2LL * M * N;
+  const long long abytes = 2LL * M * K;
+  const long long wbytes = (layout == SWIGLU_LAYOUT_INTERLEAVED ? 4LL : 2LL) * K * N;
+  if (K > 0 && (overlaps(Y, ybytes, A, abytes) || overlaps(Y, ybytes, W1, wbytes) ||
+                (layout == SWIGLU_LAYOUT_SEPARATE && overlaps(Y, ybytes, W2, wbytes))))
+    return SWIGLU_ERR_INVALID_ARG;
+  return check_device(h);
+}
+
+// a skinny configuration launches ceil(M / bm) workgroups along grid y
+bool config_fits(const KernelConfig* c, long long M) {
+  if (c->family == 1) return (M + c->bm - 1) / c->bm <= 65535;
+  return true;
+}
+
+swiglu_status_t run(const swiglu_ctx* h, const KernelConfig* cfg, int id, const void* A,
+                    const void* W1, const void* W2, void* Y, int64_t M, int64_t N,
+                    int64_t K, hipStream_t stream) {
+  if (!config_fits(cfg, M)) return SWIGLU_ERR_UNSUPPORTED;
+  LaunchArgs a;
+  a.A = (const uint16_t*)A;
+  a.W1 = (const uint16_t*)W1;
+  a.W2 = (const uint16_t*)W2;
+  a.Y = (uint16_t*)Y;
+  a.M = (int)M, a.N = (int)N, a.K = (int)K;
+  a.group_m = 0;
+  a.stream = stream;
+  if (h->log)
+    fprintf(stderr, "[swiglu] M=%lld N=%lld K=%lld -> config %d (variant %d family %d %dx%d)\n",
+            (long long)M, (long long)N, (long long)K, id, cfg->variant, cfg->family, cfg->bm,
+            cfg->bn);
+  (void)hipGetLastError();  // clear a stale error so the check below is ours
+  return cfg->launch(a) == hipSuccess ? SWIGLU_OK : SWIGLU_ERR_LAUNCH;
+}
+
+void fill_tile(int id, swiglu_tile_t* t) {
+  const KernelConfig* c = config_at(id);
+  t->id = id;
+  t->variant = c->variant;
+  t->family = c->family;
+  t->bm = c->bm;
+  t->bn = c->bn;
+  t->bk = c->bk;
+  t->waves = c->waves;
+  t->split_k = c->split_k;
+  t->lds_bytes = c->lds_bytes;
+}
+
+}  // namespace
+
+extern "C" {
+
+swiglu_status_t swiglu_create(swiglu_handle_t* out, int device) {
+  if (!out) return SWIGLU_ERR_INVALID_ARG;
+  *out = nullptr;
+  int count = 0;
+  if (hipGetDeviceCount(&count) != hipSuccess || count <= 0) {
+    (void)hipGetLastError();
+    return SWIGLU_ERR_DEVICE;
+  }
+  if (device < 0 || device >= count) return SWIGLU_ERR_DEVICE;
+  hipDeviceProp_t prop;
+  if (hipGetDeviceProperties(&prop, device) != hipSuccess) {
+    (void)hipGetLastError();
+    return SWIGLU_ERR_DEVICE;
+  }
+  if (strncmp(prop.gcnArchName, "gfx950", 6) != 0) return SWIGLU_ERR_DEVICE;
+  swiglu_ctx* h = new (std::nothrow) swiglu_ctx;
+  if (!h) return SWIGLU_ERR_ALLOC;
+  h->device = device;
+  h->cu_count = prop.multiProcessorCount;
+  strncpy(h->arch, prop.gcnArchName, sizeof(h->arch) - 1);
+  h->arch[sizeof(h->arch) - 1] = 0;
+  const char* lg = getenv("SWIGLU_LOG");
+  h->log = (lg && lg[0] == '1') ? 1 : 0;
+  *out = h;
+  return SWIGLU_OK;
+}
+
+swiglu_status_t swiglu_destroy(swiglu_handle_t h) {
+  delete h;
+  return SWIGLU_OK;
+}
+
+swiglu_status_t swiglu_forward_ex(swiglu_handle_t h, const void* A, const void* W1,
+                                  const void* W2, void* Y, int64_t M, int64_t N, int64_t K,
+                                  swiglu_layout_t layout, swiglu_variant_t variant,
+                                  int32_t config_id, hipStream_t stream) {
+  bool noop = false;
+  swiglu_status_t st = check_forward(h, A, W1, W2, Y, M, N, K, (int)layout, &noop);
+  if (st != SWIGLU_OK) return st;
+  const int want = layout == SWIGLU_LAYOUT_INTERLEAVED ? VAR_INTERLEAVE : VAR_SYNC;
+  if (variant != SWIGLU_VARIANT_AUTO && (int)variant != want) return SWIGLU_ERR_INVALID_ARG;
+  int id = config_id;
+  if (id >= 0) {
+    const KernelConfig* c = config_at(id);
+    if (!c || c->variant != want) return SWIGLU_ERR_INVALID_ARG;
+  }
+  if (noop) return SWIGLU_OK;
+  if (id < 0) id = select_config(want, M, N, K, h->cu_count);
+  if (id < 0) return SWIGLU_ERR_UNSUPPORTED;
+  return run(h, config_at(id), id, A, W1, W2, Y, M, N, K, stream);
+}
+
+swiglu_status_t swiglu_forward(swiglu_handle_t h, const void* A, const void* W1,
+                               const void* W2, void* Y, int64_t M, int64_t N, int64_t K,
+                               swiglu_layout_t layout, hipStream_t stream) {
+  return swiglu_forward_ex(h, A, W1, W2, Y, M, N, K, layout, SWIGLU_VARIANT_AUTO, -1, stream);
+}
+
+int64_t swiglu_unfused_workspace_bytes(int64_t M, int64_t N) {
+  if (M < 0 || N < 0) return 0;
+  return 4 * M * N;
+}
+
+swiglu_status_t swiglu_forward_unfused(swiglu_handle_t h, const void* A, const void* W1,
+                                       const void* W2, void* workspace, void* Y, int64_t M,
+                                       int64_t N, int64_t K, int32_t gemm_config_id,
+                                       hipStream_t stream) {
+  bool noop = false;
+  swiglu_status_t st =
+      check_forward(h, A, W1, W2, Y, M, N, K, SWIGLU_LAYOUT_SEPARATE, &noop);
+  if (st != SWIGLU_OK) return st;
+  int id = gemm_config_id;
+  if (id >= 0) {
+    const KernelConfig* c = config_at(id);
+    if (!c || c->variant != VAR_GEMM) return SWIGLU_ERR_INVALID_ARG;
+  }
+  if (noop) return SWIGLU_OK;
+  if (!workspace) return SWIGLU_ERR_INVALID_ARG;
+  if (!aligned16(workspace)) return SWIGLU_ERR_UNSUPPORTED;
+  const long long wsb = 4LL * M * N;
+  const long long wb = 2LL * K * N;
+  if (overlaps(workspace, wsb, Y, 2LL * M * N) || overlaps(workspace, wsb, A, 2LL * M * K) ||
+      overlaps(workspace, wsb, W1, wb) || overlaps(workspace, wsb, W2, wb))
+    return SWIGLU_ERR_INVALID_ARG;
+  if (id < 0) id = select_config(VAR_GEMM, M, N, K, h->cu_count);
+  if (id < 0) return SWIGLU_ERR_UNSUPPORTED;
+  uint16_t* G = (uint16_t*)workspace;
+  uint16_t* U = G + (size_t)M * (size_t)N;
+  st = run(h, config_at(id), id, A, W1, nullptr, G, M, N, K, stream);
+  if (st != SWIGLU_OK) return st;
+  st = run(h, config_at(id), id, A, W2, nullptr, U, M, N, K, stream);
+  if (st != SWIGLU_OK) return st;
+  (void)hipGetLastError();
+  if (launch_gate(G, U, (uint16_t*)Y, (size_t)M * (size_t)N, stream, h->cu_count) != hipSuccess)
+    return SWIGLU_ERR_LAUNCH;
+  return SWIGLU_OK;
+}
+
+swiglu_status_t swiglu_pack_interleaved(swiglu_handle_t h, const void* W1, const void* W2,
+                                        void* W_fused, int64_t K, int64_t N,
+                                        hipStream_t stream) {
+  if (!h || K < 0 || N < 0) return SWIGLU_ERR_INVALID_ARG;
+  if (K == 0 || N == 0) return SWIGLU_OK;
+  if (!W1 || !W2 || !W_fused) return SWIGLU_ERR_INVALID_ARG;
+  if (N % 8 != 0) return SWIGLU_ERR_UNSUPPORTED;
+  if (!aligned16(W1) || !aligned16(W2) || !aligned16(W_fused)) return SWIGLU_ERR_UNSUPPORTED;
+  const long long wb = 2LL * K * N;
+  if (overlaps(W_fused, 2 * wb, W1, wb) || overlaps(W_fused, 2 * wb, W2, wb))
+    return SWIGLU_ERR_INVALID_ARG;
+  swiglu_status_t st = check_device(h);
+  if (st != SWIGLU_OK) return st;
+  (void)hipGetLastError();
+  if (launch_pack((const uint16_t*)W1, (const uint16_t*)W2, (uint16_t*)W_fused,
+                  (size_t)K * (size_t)N, stream, h->cu_count) != hipSuccess)
+    return SWIGLU_ERR_LAUNCH;
+  return SWIGLU_OK;
+}
+
+swiglu_status_t swiglu_query(swiglu_handle_t h, int64_t M, int64_t N, int64_t K,
+                             swiglu_layout_t layout, swiglu_variant_t* chosen,
+                             swiglu_tile_t* tile, swiglu_layout_t* recommended_layout) {
+  if (!h || M < 0 || N < 0 || K < 0) return SWIGLU_ERR_INVALID_ARG;
+  if (layout != SWIGLU_LAYOUT_SEPARATE && layout != SWIGLU_LAYOUT_INTERLEAVED)
+    return SWIGLU_ERR_INVALID_ARG;
+  const int want = layout == SWIGLU_LAYOUT_INTERLEAVED ? VAR_INTERLEAVE : VAR_SYNC;
+  const int id = select_config(want, M, N, K, h->cu_count);
+  if (id < 0) return SWIGLU_ERR_UNSUPPORTED;
+  if (chosen) *chosen = (swiglu_variant_t)want;
+  if (tile) fill_tile(id, tile);
+  if (recommended_layout)
+    *recommended_layout = (swiglu_layout_t)recommend_layout(M, N, K, h->cu_count);
+  return SWIGLU_OK;
+}
+
+swiglu_status_t swiglu_query_unfused(swiglu_handle_t h, int64_t M, int64_t N, int64_t K,
+                                     swiglu_tile_t* tile) {
+  if (!h || M < 0 || N < 0 || K < 0) return SWIGLU_ERR_INVALID_ARG;
+  const int id = select_config(VAR_GEMM, M, N, K, h->cu_count);
+  if (id < 0) return SWIGLU_ERR_UNSUPPORTED;
+  if (tile) fill_tile(id, tile);
+  return SWIGLU_OK;
+}
+
+int32_t swiglu_config_count(void) { return config_count(); }
+
+swiglu_status_t swiglu_config_info(int32_t config_id, swiglu_tile_t* out) {
+  if (!out || !config_at(config_id)) return SWIGLU_ERR_INVALID_ARG;
+  fill_tile(config_id, out);
+  return SWIGLU_OK;
+}
+
+const char* swiglu_status_str(swiglu_status_t s) {
+  switch (s) {
+    case SWIGLU_OK: return "ok";
+    case SWIGLU_ERR_INVALID_ARG: return "invalid argument";
+    case SWIGLU_ERR_UNSUPPORTED: return "unsupported shape, alignment or configuration";
+    case SWIGLU_ERR_DEVICE: return "no usable gfx950 device";
+    case SWIGLU_ERR_LAUNCH: return "kernel launch failed";
+    case SWIGLU_ERR_ALLOC: return "host allocation failed";
+  }
+  return "unknown status";
+}
+
+}  // extern "C"

@@ -1,0 +1,90 @@
+// swiglu_device.hpp -- gfx950 device building blocks for the fused SwiGLU GEMMs.
+//
+// MFMA operand conventions used throughout (CDNA3/CDNA4 matrix-core layout,
+// 64-lane waves; the k placement only has to agree between the two sources):
+//   v_mfma_f32_32x32x16_bf16  A: lane l holds row l%32, k = 8*(l/32) + [0,8)
+//                             B: lane l holds col l%32, k = 8*(l/32) + [0,8)
+//                             D: lane l, reg r -> col l%32,
+//                                row 8*(r/4) + 4*(l/32) + r%4
+//   v_mfma_f32_16x16x32_bf16  A: lane l holds row l%16, k = 8*(l/16) + [0,8)
+//                             B: lane l holds col l%16, k = 8*(l/16) + [0,8)
+//                             D: lane l, reg r -> col l%16, row 4*(l/16) + r
+// Both sources want 8 consecutive k per lane.  A [M,K] is k-contiguous in HBM;
+// the weights [K,N] are n-contiguous, so weight tiles are transposed in
+// registers (8x8 blocks of bf16 with v_perm_b32) on their way to LDS or to the
+// MFMA.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace swiglu {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+__device__ __forceinline__ u32x4 load16(const void* p) {
+  return *reinterpret_cast<const u32x4*>(p);
+}
+__device__ __forceinline__ u32x2 load8(const void* p) {
+  return *reinterpret_cast<const u32x2*>(p);
+}
+
+// SiLU(x) = x * sigmoid(x) = x / (1 + e^-x) in fp32 on the hardware exp and
+// reciprocal (each within about an ulp).  x << 0: e^-x -> +inf, rcp -> 0,
+// result -0; x >> 0: result x.  No NaN for finite x.
+__device__ __forceinline__ float silu(float x) {
+  return x * __builtin_amdgcn_rcpf(1.0f + __expf(-x));
+}
+
+// fp32 -> bf16 bits, round to nearest even (v_cvt_pk_bf16_f32 on gfx950).
+__device__ __forceinline__ uint16_t bf16_bits(float x) {
+  return __builtin_bit_cast(uint16_t, static_cast<__bf16>(x));
+}
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return (uint32_t)bf16_bits(lo) | ((uint32_t)bf16_bits(hi) << 16);
+}
+__device__ __forceinline__ float bf16_to_float(uint16_t h) {
+  return __builtin_bit_cast(float, (uint32_t)h << 16);
+}
+
+// Transpose an 8 (k) x 8 (n) block of bf16.  row[i] holds k-row i as four
+// dwords, dword j = (n = 2j low half, n = 2j+1 high half).  col[c] receives
+// column n = c as four dwords, dword p = (k = 2p low, k = 2p+1 high), i.e. the
+// 8 consecutive k of one column that an MFMA source lane wants.
+__device__ __forceinline__ void transpose8x8(const u32x4 row[8], u32x4 col[8]) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      const uint32_t lo = row[2 * p][j];      // k = 2p
+      const uint32_t hi = row[2 * p + 1][j];  // k = 2p+1
+      // even column 2j: low halves of both; odd column 2j+1: high halves.
+      col[2 * j][p] = __builtin_amdgcn_perm(hi, lo, 0x05040100u);
+      col[2 * j + 1][p] = __builtin_amdgcn_perm(hi, lo, 0x07060302u);
+    }
+  }
+}
+
+__device__ __forceinline__ f32x16 mfma32(const u32x4& a, const u32x4& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(b), c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma16(const u32x4& a, const u32x4& b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), as_bf16x8(b), c, 0, 0, 0);
+}
+
+// Workgroup id -> tile id so that each of the 8 XCDs (which receive workgroups
+// round-robin in launch order) works on one contiguous range of tile ids, and
+// the tiles that run together on an XCD share operand panels in its L2.
+__device__ __forceinline__ int xcd_remap(int b, int nwg) {
+  const int q = nwg / 8, r = nwg % 8;
+  const int x = b % 8, i = b / 8;
+  return x * q + (x < r ? x : r) + i;
+}
+
+}  // namespace swiglu

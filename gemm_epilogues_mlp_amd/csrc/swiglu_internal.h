@@ -1,0 +1,45 @@
+// swiglu_internal.h -- declarations shared by the C-ABI layer and the kernels.
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace swiglu {
+
+enum Variant { VAR_AUTO = 0, VAR_SYNC = 1, VAR_INTERLEAVE = 2, VAR_GEMM = 3 };
+
+struct LaunchArgs {
+  const uint16_t* A;
+  const uint16_t* W1;  // W1, W_fused, or the single GEMM weight
+  const uint16_t* W2;  // W2 (sync) or unused
+  uint16_t* Y;         // Y, or G / U for the unfused GEMMs
+  int M, N, K;         // N = output columns (Y columns, or G columns)
+  int group_m;         // tile rows per GROUP_M band (<= 0: default)
+  hipStream_t stream;
+};
+
+typedef hipError_t (*LaunchFn)(const LaunchArgs&);
+
+struct KernelConfig {
+  int variant;  // Variant
+  int family;   // 0 tiled, 1 skinny
+  int bm, bn, bk, waves, split_k, lds_bytes;
+  LaunchFn launch;
+};
+
+int config_count();
+const KernelConfig* config_at(int id);
+
+hipError_t launch_gate(const uint16_t* G, const uint16_t* U, uint16_t* Y, size_t n,
+                       hipStream_t stream, int cu_count);
+hipError_t launch_pack(const uint16_t* W1, const uint16_t* W2, uint16_t* WF, size_t n,
+                       hipStream_t stream, int cu_count);
+
+// Per-shape choice (tile table + fallback rule).  variant is SYNC, INTERLEAVE
+// or GEMM; returns a config id of that variant.
+int select_config(int variant, long long M, long long N, long long K, int cu_count);
+// Layout the table recommends for a shape: 0 separate, 1 interleaved.
+int recommend_layout(long long M, long long N, long long K, int cu_count);
+
+}  // namespace swiglu

@@ -1,0 +1,173 @@
+/*
+ * swiglu.h -- C ABI of the MI355X (gfx950) fused SwiGLU MLP GEMM library.
+ *
+ * Computes  Y = SiLU(A x W1) (.) (A x W2)  with bf16 inputs, fp32 accumulation
+ * and a bf16 result, in which the Gate (A x W1) and Up (A x W2) products never
+ * leave the chip.  The operation is defined on the gist.science page
+ * "Riepilogo Tecnico: Sovrapposizione delle Attivazioni a Livello di Tile per
+ * l'Inferenza Efficiente di LLM" (summary of arXiv 2607.02521), cited as [RT]:
+ *   [RT §Definizione del Problema]  the gated MLP formula, two independent
+ *                                   GEMMs followed by an element-wise gate;
+ *   [RT §Metodologia, Kernel-1]     "sync": the Gate tile is finished first,
+ *                                   SiLU is applied to its register-resident
+ *                                   accumulator while the Up weight tiles are
+ *                                   being loaded, the product is formed and
+ *                                   stored in the epilogue (large batches);
+ *   [RT §Metodologia, Kernel-2]     "interleave": W1 and W2 are stored as one
+ *                                   [K, 2N] matrix with Gate in even and Up in
+ *                                   odd columns, one [M, 2N, K] GEMM runs and
+ *                                   the epilogue multiplies SiLU(even column)
+ *                                   by the odd column (small batches);
+ *   [RT §Definizione del Problema]  the unfused baseline that writes Gate and
+ *                                   Up to HBM before a separate activation.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - All functions are extern "C", never throw and never exit; they return a
+ *    swiglu_status_t.  Argument checks run synchronously before anything is
+ *    enqueued; on any error nothing is enqueued.
+ *  - Tensors are device pointers (memory from hipMalloc or any allocator that
+ *    returns device-accessible memory, e.g. torch), dense and row-major with
+ *    no strides, holding bf16 values (raw 16-bit patterns).
+ *      A       [M, K]           activations
+ *      W1, W2  [K, N]           Gate and Up weights   (SWIGLU_LAYOUT_SEPARATE)
+ *      W_fused [K, 2N]          W_fused[k, 2n] = W1[k, n], [k, 2n+1] = W2[k, n]
+ *                               (SWIGLU_LAYOUT_INTERLEAVED; passed as W1, W2
+ *                               must then be NULL)
+ *      Y       [M, N]           output, bf16 rounded to nearest even from fp32
+ *  - The caller owns every buffer and keeps it alive until the stream work has
+ *    completed.  The library never allocates device memory, never frees or
+ *    retains caller pointers.  Y must not overlap any input.
+ *  - Shapes: M, N, K >= 0.  M == 0 or N == 0 is a no-op (pointers may then be
+ *    NULL).  K == 0 writes Y = 0 (empty sums).  The kernels need N % 8 == 0,
+ *    K % 8 == 0 and 16-byte aligned pointers; other shapes or alignments give
+ *    SWIGLU_ERR_UNSUPPORTED.  M is unrestricted (ragged row tiles are masked).
+ *    Every byte offset must fit in 31 bits (each tensor < 2 GiB), otherwise
+ *    SWIGLU_ERR_UNSUPPORTED.
+ *  - Execution is asynchronous on the given stream (0 = the null stream of the
+ *    current device); SWIGLU_OK means "enqueued".  A failed launch
+ *    (hipGetLastError after the launch) gives SWIGLU_ERR_LAUNCH.
+ *  - A handle holds host state only, is immutable after creation and may be
+ *    used from several host threads and streams at once.  It is bound to the
+ *    device it was created for; that device must be current when calling.
+ */
+#ifndef SWIGLU_H
+#define SWIGLU_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct swiglu_ctx* swiglu_handle_t;
+
+typedef enum {
+  SWIGLU_OK = 0,
+  SWIGLU_ERR_INVALID_ARG = 1, /* NULL pointer, negative size, unknown enum   */
+  SWIGLU_ERR_UNSUPPORTED = 2, /* shape/alignment/config the kernels cannot take */
+  SWIGLU_ERR_DEVICE = 3,      /* no device, bad ordinal or not gfx950         */
+  SWIGLU_ERR_LAUNCH = 4,      /* the HIP launch reported an error             */
+  SWIGLU_ERR_ALLOC = 5        /* host allocation of the handle failed         */
+} swiglu_status_t;
+
+typedef enum {
+  SWIGLU_LAYOUT_SEPARATE = 0,   /* W1, W2 each [K, N]                          */
+  SWIGLU_LAYOUT_INTERLEAVED = 1 /* W1 = W_fused [K, 2N], W2 = NULL             */
+} swiglu_layout_t;
+
+typedef enum {
+  SWIGLU_VARIANT_AUTO = 0,       /* table choice for the layout and shape      */
+  SWIGLU_VARIANT_SYNC = 1,       /* Kernel-1 family: separate layout           */
+  SWIGLU_VARIANT_INTERLEAVE = 2, /* Kernel-2 family: interleaved layout        */
+  SWIGLU_VARIANT_GEMM = 3        /* plain bf16 GEMM (unfused baseline only)    */
+} swiglu_variant_t;
+
+/* Description of one compiled kernel configuration. */
+typedef struct swiglu_tile {
+  int32_t id;          /* index in [0, swiglu_config_count())                */
+  int32_t variant;     /* swiglu_variant_t: SYNC, INTERLEAVE or GEMM          */
+  int32_t family;      /* 0 = LDS-tiled MFMA 32x32x16, 1 = split-K streaming
+                          MFMA 16x16x32 (weights straight to registers)       */
+  int32_t bm;          /* output rows per workgroup                           */
+  int32_t bn;          /* output (Y or G) columns per workgroup               */
+  int32_t bk;          /* K depth of one pipeline stage                       */
+  int32_t waves;       /* waves (64 lanes) per workgroup                      */
+  int32_t split_k;     /* waves of one workgroup that split K (1 = none)      */
+  int32_t lds_bytes;   /* LDS per workgroup                                   */
+} swiglu_tile_t;
+
+/* Create a handle for HIP device `device`.  Checks that the device exists and
+ * is gfx950; reads its compute-unit count.  *out is set to NULL on error.
+ * Errors: INVALID_ARG (out NULL), DEVICE, ALLOC. */
+swiglu_status_t swiglu_create(swiglu_handle_t* out, int device);
+
+/* Release a handle (NULL is accepted).  No call using it may be executing. */
+swiglu_status_t swiglu_destroy(swiglu_handle_t h);
+
+/* Fused forward [RT §Metodologia]: SEPARATE layout runs the sync family
+ * (Kernel-1), INTERLEAVED runs the interleave family (Kernel-2); the tile
+ * configuration comes from the per-shape table. */
+swiglu_status_t swiglu_forward(swiglu_handle_t h, const void* A, const void* W1,
+                               const void* W2, void* Y, int64_t M, int64_t N,
+                               int64_t K, swiglu_layout_t layout, hipStream_t stream);
+
+/* As swiglu_forward with an explicit variant and configuration (config_id < 0
+ * uses the table).  The variant must match the layout (SYNC <-> SEPARATE,
+ * INTERLEAVE <-> INTERLEAVED) and a given config must belong to that variant,
+ * otherwise INVALID_ARG.  Used by tuning sweeps and tests. */
+swiglu_status_t swiglu_forward_ex(swiglu_handle_t h, const void* A, const void* W1,
+                                  const void* W2, void* Y, int64_t M, int64_t N,
+                                  int64_t K, swiglu_layout_t layout,
+                                  swiglu_variant_t variant, int32_t config_id,
+                                  hipStream_t stream);
+
+/* Bytes of caller-owned device workspace the unfused baseline needs: Gate and
+ * Up as bf16 [M, N] each, i.e. 4*M*N (0 for negative sizes). */
+int64_t swiglu_unfused_workspace_bytes(int64_t M, int64_t N);
+
+/* Unfused baseline [RT §Definizione del Problema]: G = A W1 and U = A W2 are
+ * written to `workspace` as bf16 ([M, N] G followed by [M, N] U, 16-byte
+ * aligned, at least swiglu_unfused_workspace_bytes(M, N) bytes), then a
+ * separate element-wise kernel computes Y = bf16(SiLU(G) * U) in fp32.  Three
+ * launches; separate layout only.  gemm_config_id < 0 uses the table's GEMM
+ * configuration (config ids of variant GEMM only). */
+swiglu_status_t swiglu_forward_unfused(swiglu_handle_t h, const void* A,
+                                       const void* W1, const void* W2,
+                                       void* workspace, void* Y, int64_t M,
+                                       int64_t N, int64_t K, int32_t gemm_config_id,
+                                       hipStream_t stream);
+
+/* Build W_fused [K, 2N] from W1, W2 [K, N] [RT §Metodologia, Kernel-2]:
+ * W_fused[k, 2n] = W1[k, n], W_fused[k, 2n+1] = W2[k, n].  A bit copy done
+ * once per weight set, outside the forward.  N % 8 == 0 and 16-byte aligned
+ * pointers required (else UNSUPPORTED); W_fused must not overlap W1 or W2. */
+swiglu_status_t swiglu_pack_interleaved(swiglu_handle_t h, const void* W1,
+                                        const void* W2, void* W_fused, int64_t K,
+                                        int64_t N, hipStream_t stream);
+
+/* What swiglu_forward / _ex(AUTO) would run for this shape and layout, and
+ * which layout the table recommends for the shape (the per-batch choice of
+ * kernel family [RT §Contributi Chiave, item 2]).  Any out-pointer may be NULL.
+ * For variant GEMM pass layout SEPARATE to ask for the unfused GEMM config. */
+swiglu_status_t swiglu_query(swiglu_handle_t h, int64_t M, int64_t N, int64_t K,
+                             swiglu_layout_t layout, swiglu_variant_t* chosen,
+                             swiglu_tile_t* tile, swiglu_layout_t* recommended_layout);
+
+/* Same question for the unfused baseline's GEMM configuration. */
+swiglu_status_t swiglu_query_unfused(swiglu_handle_t h, int64_t M, int64_t N,
+                                     int64_t K, swiglu_tile_t* tile);
+
+/* Number of compiled kernel configurations and their descriptions. */
+int32_t swiglu_config_count(void);
+swiglu_status_t swiglu_config_info(int32_t config_id, swiglu_tile_t* out);
+
+/* Static string for a status code ("unknown status" for other values). */
+const char* swiglu_status_str(swiglu_status_t status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SWIGLU_H */

@@ -1,0 +1,96 @@
+"""The C ABI on a machine without a GPU: the library loads, exports every
+function include/swiglu.h declares, and rejects bad calls before touching the
+device.  No compute entry point runs here."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import gemm_epilogues_mlp_amd as sw
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "swiglu.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(swiglu_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for must in ("swiglu_create", "swiglu_forward", "swiglu_destroy", "swiglu_forward_ex",
+                 "swiglu_forward_unfused", "swiglu_pack_interleaved", "swiglu_query"):
+        assert must in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = sw.load()
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    out = subprocess.run(["nm", "-D", "--defined-only", sw.lib_path()], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (swiglu_\w+)", out))
+    assert set(declared_functions()) <= exported
+
+
+def test_library_is_built_for_gfx950():
+    data = open(sw.lib_path(), "rb").read()
+    assert b"gfx950" in data
+
+
+def test_header_compiles_as_c():
+    src = '#include "swiglu.h"\nint main(void){ return (int)swiglu_config_count(); }\n'
+    cmd = ["gcc", "-std=c11", "-fsyntax-only", "-x", "c", "-I", os.path.join(ROOT, "include"),
+           "-I", "/opt/rocm/include", "-D__HIP_PLATFORM_AMD__", "-"]
+    r = subprocess.run(cmd, input=src, capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+
+
+def test_null_handle_and_bad_arguments_rejected():
+    lib = sw.load()
+    assert lib.swiglu_forward(None, 16, 16, 16, 16, 8, 8, 8, 0, None) == sw.ERR_INVALID_ARG
+    assert lib.swiglu_forward_unfused(None, 16, 16, 16, 16, 16, 8, 8, 8, -1, None) == \
+        sw.ERR_INVALID_ARG
+    assert lib.swiglu_pack_interleaved(None, 16, 16, 16, 8, 8, None) == sw.ERR_INVALID_ARG
+    assert lib.swiglu_query(None, 8, 8, 8, 0, None, None, None) == sw.ERR_INVALID_ARG
+    assert lib.swiglu_create(None, 0) == sw.ERR_INVALID_ARG
+    assert lib.swiglu_destroy(None) == sw.OK
+    assert lib.swiglu_config_info(-1, None) == sw.ERR_INVALID_ARG
+    assert lib.swiglu_config_info(sw.swiglu_config_count(), None) == sw.ERR_INVALID_ARG
+
+
+def test_status_strings_and_workspace_size():
+    assert sw.swiglu_status_str(0) == "ok"
+    assert "unknown" in sw.swiglu_status_str(99)
+    assert sw.swiglu_unfused_workspace_bytes(3, 8) == 4 * 3 * 8
+    assert sw.swiglu_unfused_workspace_bytes(-1, 8) == 0
+
+
+def test_config_list_is_consistent():
+    n = sw.swiglu_config_count()
+    assert n > 0
+    seen = {sw.VARIANT_SYNC: 0, sw.VARIANT_INTERLEAVE: 0, sw.VARIANT_GEMM: 0}
+    for i in range(n):
+        c = sw.swiglu_config_info(i)
+        assert c["id"] == i
+        assert c["variant"] in seen
+        seen[c["variant"]] += 1
+        assert c["family"] in (0, 1)
+        assert 0 < c["lds_bytes"] <= 160 * 1024
+        assert c["waves"] * 64 <= 1024
+        if c["family"] == 0:
+            assert c["bm"] % 32 == 0 and c["bn"] % 32 == 0
+    assert all(v > 0 for v in seen.values())
+
+
+def test_create_without_device_reports_device_error():
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present; the GPU tests cover creation")
+    with pytest.raises(sw.SwiGLUError) as e:
+        sw.swiglu_create(0)
+    assert e.value.status == sw.ERR_DEVICE
