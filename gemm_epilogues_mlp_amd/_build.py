@@ -27,7 +27,7 @@ def hipcc() -> str:
 
 def flags(extra=()):
     return [
-        f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
+        f"--offload-arch={ARCH}", "-O3", "-std=c++20", "-fPIC",
         # packed fp32 VALU ops stay off: ordinary fp32 code only
         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
         "-I", INCLUDE, "-I", CSRC, *extra,

@@ -35,6 +35,59 @@ __device__ __forceinline__ u32x2 load8(const void* p) {
   return *reinterpret_cast<const u32x2*>(p);
 }
 
+// ---- direct HBM -> LDS loads ------------------------------------------------
+typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+
+// Byte offset that lies past every buffer resource used here (tensors are
+// limited to < 2^31 bytes): a load at this offset returns zeros.
+constexpr uint32_t kOutOfRange = 0x80000000u;
+
+// Raw buffer resource over [p, p + bytes): stride 0, bounds-checked by byte
+// offset (loads past num_records return 0), gfx9 default data format word.
+__device__ __forceinline__ i32x4 make_rsrc(const void* p, uint32_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(p);
+  i32x4 r;
+  r[0] = __builtin_amdgcn_readfirstlane((int32_t)(uint32_t)a);
+  r[1] = __builtin_amdgcn_readfirstlane((int32_t)(uint32_t)((a >> 32) & 0xffffu));
+  r[2] = __builtin_amdgcn_readfirstlane((int32_t)bytes);
+  r[3] = 0x00020000;
+  return r;
+}
+
+// LDS address (byte offset in the workgroup's LDS) of a shared-memory pointer.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
+// One 16-byte-per-lane DMA from global memory into LDS: lane i's 16 bytes land
+// at lds_wave_base + 16 i (lds_wave_base is wave-uniform).  Issued as inline
+// assembly so the compiler does not add a conservative vmcnt(0) in front of
+// every LDS read; completion is tracked with wait_vmcnt<>() by the caller.
+__device__ __forceinline__ void lds_dma16(uint32_t lds_wave_base, uint32_t voffset, i32x4 rsrc) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :
+               : "s"(lds_wave_base), "v"(voffset), "s"(rsrc)
+               : "memory");
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N <= 63, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
+}
+
+// Transposing LDS read (gfx950): within each group of 16 lanes, source lane
+// s supplies 4 consecutive 16-bit elements at its address, and lane 4a+b
+// receives element b of source lanes a, 4+a, 8+a, 12+a.  With source lane s
+// pointing at row (s/4) and columns 4*(s%4)..+3 of a row-major [k][n] tile,
+// lane i of the group receives column i at rows 0..3.
+__device__ __forceinline__ u32x2 lds_read_tr16(const void* p) {
+  const i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) i16x4*)(p));
+  return __builtin_bit_cast(u32x2, v);
+}
+
 // SiLU(x) = x * sigmoid(x) = x / (1 + e^-x) in fp32 on the hardware exp and
 // reciprocal (each within about an ulp).  x << 0: e^-x -> +inf, rcp -> 0,
 // result -0; x >> 0: result x.  No NaN for finite x.

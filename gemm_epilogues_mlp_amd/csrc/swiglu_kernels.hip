@@ -37,6 +37,9 @@
 #include "swiglu_device.hpp"
 #include "swiglu_internal.h"
 
+#include <type_traits>
+#include <utility>
+
 namespace swiglu {
 
 enum Mode { MODE_INTERLEAVE = 0, MODE_SYNC = 1, MODE_GEMM = 2 };
@@ -44,40 +47,105 @@ enum Mode { MODE_INTERLEAVE = 0, MODE_SYNC = 1, MODE_GEMM = 2 };
 // ============================================================================
 // LDS-tiled MFMA kernel
 // ============================================================================
-template <int MODE, int BM, int BNY, int BK, int WGM, int WGN>
+// One workgroup (4 waves) computes BM rows of A against BNW weight columns
+// (interleave: BNW W_fused columns = BNW/2 Y columns; sync: BNW columns of W1
+// and then of W2; gemm: BNW columns of one weight).  Each K step of depth BK
+// moves A[BM, BK] and W[BK, BNW] from HBM into one of STAGES LDS buffers by
+// direct DMA (buffer_load ... lds, no registers), STAGES-1 steps ahead of the
+// MFMAs, with one barrier per K step.  Rows, columns and k outside the tensors
+// arrive as zeros (buffer loads past the resource size return 0).
+//
+// Orientation: the MFMA computes D^T = W^T A^T.  Its first source is a weight
+// fragment (32 weight columns x 16 k) read with the transposing LDS read from
+// the n-contiguous weight tile; its second is an activation fragment (32 rows
+// of A x 16 k, one ds_read_b128).  A lane then holds one row of A and, per
+// accumulator, four runs of 4 consecutive weight columns in 4 consecutive
+// registers: the interleave pair (Gate column 2n, Up column 2n+1) is two
+// adjacent registers of one lane, and the pair-multiply epilogue is local.
+//
+// LDS layouts (16-byte chunks, XOR-swizzled so that the fragment reads are
+// free of bank conflicts):
+//   A stage  [BM][BK]   row-major, chunk c of row r stored at c ^ a_swz(r)
+//   W stage  [BK][BNW]  row-major, chunk c of row k stored at c ^ w_swz(k)
+template <int MODE, int BM, int BNW, int BK, int STAGES, int WGM, int WGN>
 struct Tiled {
   static constexpr int kThreads = 256;
   static_assert(WGM * WGN == 4, "four waves per workgroup");
-  // weight columns staged per K step
-  static constexpr int NC = (MODE == MODE_INTERLEAVE) ? 2 * BNY : BNY;
-  static constexpr int WTM = BM / WGM;  // rows per wave
-  static constexpr int WTN = BNY / WGN; // output columns per wave
-  static constexpr int FM = WTM / 32;
-  static constexpr int FN = WTN / 32;
-  static_assert(FM >= 1 && FN >= 1 && WTM % 32 == 0 && WTN % 32 == 0, "wave tile");
-  static_assert(BK % 16 == 0 && BK >= 16, "BK");
-  static constexpr int LDK = BK + 8;  // padded LDS row, elements (16 B pad)
-  static constexpr int A_CHUNKS = BM * BK / 8;
-  static_assert(A_CHUNKS % kThreads == 0, "A tile must split evenly");
-  static constexpr int A_PER_T = A_CHUNKS / kThreads;
-  static constexpr int W_BLOCKS = (BK / 8) * (NC / 8);
-  static constexpr int W_PER_T = (W_BLOCKS + kThreads - 1) / kThreads;
-  static constexpr int LDS_A = BM * LDK;  // elements per stage
-  static constexpr int LDS_B = NC * LDK;
-  static constexpr int LDS_BYTES = 2 * (LDS_A + LDS_B) * 2;
+  static constexpr int BNY = (MODE == MODE_INTERLEAVE) ? BNW / 2 : BNW;  // output columns
+  static constexpr int WTM = BM / WGM;   // A rows per wave
+  static constexpr int WTW = BNW / WGN;  // weight columns per wave
+  static constexpr int FA = WTM / 32;    // 32-row blocks of A per wave
+  static constexpr int FW = WTW / 32;    // 32-column blocks of W per wave
+  static_assert(FA >= 1 && FW >= 1 && WTM % 32 == 0 && WTW % 32 == 0, "wave tile");
+  static constexpr int NACC = (MODE == MODE_SYNC) ? 2 : 1;
+  static constexpr int NSUB = BK / 16;
+  static_assert(BK % 32 == 0, "BK: an even number of 16-deep MFMA steps");
+  static constexpr int ACH = BK / 8;     // 16-byte chunks per A row of a stage
+  static_assert(ACH == 4 || ACH == 8, "A swizzle covers 4 or 8 chunks");
+  static constexpr int WCH = BNW / 8;    // 16-byte chunks per weight row
+  static_assert(WCH % 8 == 0, "W swizzle stays inside groups of 8 chunks");
+  static constexpr int A_BYTES = BM * BK * 2;
+  static constexpr int W_BYTES = BK * BNW * 2;
+  static constexpr int STAGE_BYTES = A_BYTES + W_BYTES;
+  static_assert((BM * ACH) % kThreads == 0 && (BK * WCH) % kThreads == 0, "even split");
+  static constexpr int A_LOADS = BM * ACH / kThreads;  // DMA instructions per thread
+  static constexpr int W_LOADS = BK * WCH / kThreads;
+  static constexpr int LOADS = A_LOADS + W_LOADS;
+  static_assert(STAGES >= 2 && LOADS * (STAGES - 2) + LOADS / 2 <= 63, "vmcnt range");
+  static constexpr int YLD = BNY + 8;    // padded row of the output staging tile
+  static constexpr int Y_BYTES = BM * YLD * 2;
+  static constexpr int LDS_BYTES =
+      STAGES * STAGE_BYTES > Y_BYTES ? STAGES * STAGE_BYTES : Y_BYTES;
   static_assert(LDS_BYTES <= 160 * 1024, "LDS");
+  static_assert(WCH == 8 || WCH % 16 == 0, "W swizzle needs 8 or a multiple of 16 chunks");
+
+  // Swizzles: a fragment read touches 16 B per lane; lanes that the LDS
+  // serves together (8 lanes per 128 B, or 16 per 256 B) must hit distinct
+  // 16-byte bank groups.  A reads take 32 consecutive rows at one logical
+  // chunk; W transposing reads take 4 consecutive k rows at 2 (16-lane group)
+  // or 4 (32 lanes) consecutive chunks.
+  __host__ __device__ static constexpr int a_swz(int row) {
+    if (ACH == 8) return (row ^ (row >> 3)) & 7;  // 128 B rows
+    return (((row >> 2) & 1) << 1) | (((row >> 1) ^ (row >> 3)) & 1);  // 64 B rows
+  }
+  // chunk XOR 2*g: the four rows of a 16-lane group land in distinct 32 B
+  // slots of 128 B, and together with the neighbouring group in distinct
+  // slots of 256 B.  Rows of 128 B alternate halves of 256 B by themselves,
+  // so g = k % 4 suffices there; wider rows all start at the same bank and
+  // take g = 0, 3, 5, 6 for k % 4 = 0..3.
+  __host__ __device__ static constexpr int w_swz(int row) {
+    if (WCH == 8) return (row & 3) << 1;
+    return ((0x6530 >> (4 * (row & 3))) & 0xf) << 1;
+  }
+  // every swizzle must permute the chunks of its own row (checked at compile
+  // time for each instantiated tile: a swizzle that left the row would read
+  // or write another row's data)
+  static constexpr bool swizzles_permute_rows() {
+    for (int r = 0; r < 16; ++r) {
+      unsigned a_seen = 0, w_seen = 0;
+      for (int c = 0; c < ACH; ++c) a_seen |= 1u << (c ^ a_swz(r));
+      for (int c = 0; c < WCH; ++c) {
+        const int x = c ^ w_swz(r);
+        if (x < 0 || x >= WCH) return false;
+        w_seen |= 1u << x;
+      }
+      if (a_seen != (1u << ACH) - 1 || w_seen != (WCH >= 32 ? 0xffffffffu : (1u << WCH) - 1))
+        return false;
+    }
+    return true;
+  }
 };
 
-template <int MODE, int BM, int BNY, int BK, int WGM, int WGN>
+
+template <int MODE, int BM, int BNW, int BK, int STAGES, int WGM, int WGN>
 __global__ __launch_bounds__(256) void tiled_kernel(const uint16_t* __restrict__ A,
                                                     const uint16_t* __restrict__ W1,
                                                     const uint16_t* __restrict__ W2,
                                                     uint16_t* __restrict__ Y, int M, int N,
                                                     int K, int group_m) {
-  using C = Tiled<MODE, BM, BNY, BK, WGM, WGN>;
-  __shared__ __attribute__((aligned(16))) uint16_t smem[C::LDS_BYTES / 2];
-  uint16_t* As = smem;                     // [2][BM][LDK]
-  uint16_t* Bs = smem + 2 * C::LDS_A;      // [2][NC][LDK]
+  using C = Tiled<MODE, BM, BNW, BK, STAGES, WGM, WGN>;
+  static_assert(C::swizzles_permute_rows(), "LDS swizzle is not a permutation of a row");
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[C::LDS_BYTES];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -86,7 +154,7 @@ __global__ __launch_bounds__(256) void tiled_kernel(const uint16_t* __restrict__
 
   // ---- tile id: XCD-contiguous ranges, then GROUP_M-major order -------------
   const int ntm = (M + BM - 1) / BM;
-  const int ntn = (N + BNY - 1) / BNY;
+  const int ntn = (N + C::BNY - 1) / C::BNY;
   const int t = xcd_remap(blockIdx.x, gridDim.x);
   const int per_group = group_m * ntn;
   const int grp = t / per_group;
@@ -95,171 +163,240 @@ __global__ __launch_bounds__(256) void tiled_kernel(const uint16_t* __restrict__
   const int tm = first_m + (t % per_group) % gsz;
   const int tn = (t % per_group) / gsz;
   const int m0 = tm * BM;
-  const int n0 = tn * BNY;  // first output column
+  const int wc0 = tn * BNW;  // first weight column (W_fused, W1/W2 or W)
+  const int y0 = tn * C::BNY;
 
+  // K steps, padded to a multiple of STAGES so the main loop can be unrolled
+  // over the stage ring with compile-time stage offsets.  Padded steps (and,
+  // in the sync variant, each phase separately) load zeros and add nothing.
   const int nk = (K + BK - 1) / BK;
-  const int total = (MODE == MODE_SYNC) ? 2 * nk : nk;
+  const int nk_pad = (nk + STAGES - 1) / STAGES * STAGES;
+  const int total = (MODE == MODE_SYNC) ? 2 * nk_pad : nk_pad;
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);  // wave id in an SGPR
 
-  // ---- global -> register staging ------------------------------------------
-  u32x4 ra[C::A_PER_T];
-  u32x4 rw[C::W_PER_T][8];
+  // ---- DMA of one K step into a stage ----------------------------------------
+  // Per-thread parts of the byte offsets do not change with k.  A chunk of A
+  // is zero-filled if its row or its k is out of range; a weight chunk if its
+  // column is (rows past K lie past the end of the weight buffer, so the
+  // buffer bound zero-fills them by itself).
+  const int ldw = (MODE == MODE_INTERLEAVE) ? 2 * N : N;
+  const i32x4 rsA = make_rsrc(A, (uint32_t)((size_t)M * K * 2));
+  const i32x4 rsW1 = make_rsrc(W1, (uint32_t)((size_t)K * ldw * 2));
+  const i32x4 rsW2 = (MODE == MODE_SYNC) ? make_rsrc(W2, (uint32_t)((size_t)K * ldw * 2)) : rsW1;
+  const uint32_t lds0 = lds_addr(smem);
 
-  auto gload = [&](int it) {
-    const int kt = (MODE == MODE_SYNC) ? (it < nk ? it : it - nk) : it;
-    const int k0 = kt * BK;
+  uint32_t a_off[C::A_LOADS];
+  int a_k[C::A_LOADS];  // k of the chunk within the step, or a huge value if the row is out
 #pragma unroll
-    for (int i = 0; i < C::A_PER_T; ++i) {
-      const int idx = tid + C::kThreads * i;
-      const int row = idx / (BK / 8), kc = idx % (BK / 8);
-      const int gm = m0 + row, gk = k0 + kc * 8;
-      ra[i] = (gm < M && gk < K) ? load16(A + (size_t)gm * K + gk) : u32x4{0, 0, 0, 0};
-    }
-    const uint16_t* W;
-    int ldw, ncols, cbase;
-    if (MODE == MODE_INTERLEAVE) {
-      W = W1, ldw = 2 * N, ncols = 2 * N, cbase = 2 * n0;
-    } else if (MODE == MODE_SYNC) {
-      W = (it < nk) ? W1 : W2, ldw = N, ncols = N, cbase = n0;
+  for (int i = 0; i < C::A_LOADS; ++i) {
+    const int p = tid + C::kThreads * i;
+    const int row = p / C::ACH;
+    const int c = (p % C::ACH) ^ C::a_swz(row);
+    a_off[i] = (uint32_t)((m0 + row) * K + c * 8) * 2u;
+    a_k[i] = (m0 + row < M) ? c * 8 : 0x3fffffff;
+  }
+  uint32_t w_off[C::W_LOADS];  // kOutOfRange-based if the column is out of range
+#pragma unroll
+  for (int i = 0; i < C::W_LOADS; ++i) {
+    const int p = tid + C::kThreads * i;
+    const int row = p / C::WCH;
+    const int c = (p % C::WCH) ^ C::w_swz(row);
+    w_off[i] = (wc0 + c * 8 < ldw) ? (uint32_t)(row * ldw + wc0 + c * 8) * 2u : kOutOfRange;
+  }
+
+  // DMA instruction q (A chunks first, then W chunks) of K step `it` into
+  // stage ST.  k0 is capped at K for steps past the end, which keeps every
+  // offset below 2^32 and out of range.
+  auto dma = [&](int it, auto st_c, int q) {
+    constexpr int ST = decltype(st_c)::value;
+    const bool up = MODE == MODE_SYNC && it >= nk_pad;
+    const int kt = up ? it - nk_pad : it;
+    const int k0 = (it < total && kt < nk) ? kt * BK : K;
+    const uint32_t sbase = lds0 + ST * C::STAGE_BYTES;
+    if (q < C::A_LOADS) {
+      const uint32_t off = (k0 + a_k[q] < K) ? a_off[q] + (uint32_t)k0 * 2u : kOutOfRange;
+      lds_dma16(sbase + (C::kThreads * q + 64 * wave_u) * 16, off, rsA);
     } else {
-      W = W1, ldw = N, ncols = N, cbase = n0;
-    }
-#pragma unroll
-    for (int i = 0; i < C::W_PER_T; ++i) {
-      const int idx = tid + C::kThreads * i;
-      const int kb = idx / (C::NC / 8), nb = idx % (C::NC / 8);
-      const int col = cbase + nb * 8;
-      const int gk = k0 + kb * 8;
-      const bool ok = (idx < C::W_BLOCKS) && gk < K && col < ncols;
-      const uint16_t* p = W + (size_t)gk * ldw + col;
-#pragma unroll
-      for (int r = 0; r < 8; ++r)
-        rw[i][r] = ok ? load16(p + (size_t)r * ldw) : u32x4{0, 0, 0, 0};
+      const int i = q - C::A_LOADS;
+      const uint32_t off = w_off[i] + (uint32_t)k0 * (uint32_t)ldw * 2u;
+      lds_dma16(sbase + C::A_BYTES + (C::kThreads * i + 64 * wave_u) * 16, off, up ? rsW2 : rsW1);
     }
   };
 
-  auto swrite = [&](int buf) {
-    uint16_t* as = As + buf * C::LDS_A;
-    uint16_t* bs = Bs + buf * C::LDS_B;
-#pragma unroll
-    for (int i = 0; i < C::A_PER_T; ++i) {
-      const int idx = tid + C::kThreads * i;
-      const int row = idx / (BK / 8), kc = idx % (BK / 8);
-      *reinterpret_cast<u32x4*>(as + row * C::LDK + kc * 8) = ra[i];
+  // ---- fragments ---------------------------------------------------------------
+  // weight fragment: lane l -> weight column 32-block + l%32, k = 8*(l/32)+[0,8)
+  const int g16 = lane >> 4, s16 = lane & 15;
+  const int w_row = 8 * (g16 >> 1) + (s16 >> 2);                   // + kk, + 4 for 2nd read
+  const int w_col = wn * C::WTW + 16 * (g16 & 1) + 4 * (s16 & 3);  // + 32 fw
+  // activation fragment: lane l -> A row 32-block + l%32, k = 8*(l/32)+[0,8)
+  const int a_row = wm * C::WTM + (lane & 31);                      // + 32 fa
+  const int a_chk = lane >> 5;                                     // + kk/8
+  constexpr int NFRAG = 2 * C::FW + C::FA;  // LDS reads per sub-step
+
+  u32x4 wf[2][C::FW], af[2][C::FA];
+  // fragment read r of sub-step `sub` of stage ST (r < 2 FW: half r%2 of
+  // weight block r/2; otherwise A block r - 2 FW)
+  auto frag = [&](auto st_c, int sub, int fb, int r) {
+    constexpr int ST = decltype(st_c)::value;
+    const uint8_t* st = smem + ST * C::STAGE_BYTES;
+    const int kk = sub * 16;
+    if (r < 2 * C::FW) {
+      const int fw = r >> 1, h = r & 1;
+      const int col = w_col + fw * 32;
+      const int row = kk + w_row + 4 * h;
+      const int chunk = (col >> 3) ^ C::w_swz(row);
+      const u32x2 v =
+          lds_read_tr16(st + C::A_BYTES + row * (BNW * 2) + chunk * 16 + ((col >> 2) & 1) * 8);
+      wf[fb][fw][2 * h] = v[0];
+      wf[fb][fw][2 * h + 1] = v[1];
+    } else {
+      const int fa = r - 2 * C::FW;
+      const int row = a_row + fa * 32;
+      const int chunk = (kk / 8 + a_chk) ^ C::a_swz(row);
+      af[fb][fa] = *reinterpret_cast<const u32x4*>(st + row * (BK * 2) + chunk * 16);
     }
+  };
+
+  f32x16 acc[C::NACC][C::FW][C::FA];
 #pragma unroll
-    for (int i = 0; i < C::W_PER_T; ++i) {
-      const int idx = tid + C::kThreads * i;
-      if (idx < C::W_BLOCKS) {
-        const int kb = idx / (C::NC / 8), nb = idx % (C::NC / 8);
-        u32x4 col[8];
-        transpose8x8(rw[i], col);
+  for (int p = 0; p < C::NACC; ++p)
 #pragma unroll
-        for (int c = 0; c < 8; ++c) {
-          const int lc = nb * 8 + c;
-          // interleave: even W_fused column -> Gate row lc/2, odd -> Up row BNY + lc/2
-          const int lrow = (MODE == MODE_INTERLEAVE) ? ((lc & 1) * BNY + (lc >> 1)) : lc;
-          *reinterpret_cast<u32x4*>(bs + lrow * C::LDK + kb * 8) = col[c];
+    for (int i = 0; i < C::FW; ++i)
+#pragma unroll
+      for (int j = 0; j < C::FA; ++j) acc[p][i][j] = f32x16{};
+
+  // One K step on stage ST.  The MFMAs of each sub-step are interleaved with
+  // the fragment reads of the next sub-step (first half of the MFMAs) and
+  // with half a step of DMA (second half): sub-step 0 finishes step
+  // it+STAGES-1, and after the barrier -- once every wave has finished
+  // reading stage ST -- the last sub-step starts step it+STAGES into stage ST
+  // itself.  Spreading the DMA keeps the address FIFO from backing up into
+  // the MFMA stream, and the barrier overlaps the MFMA tail of sub-step 0.
+  constexpr int LH = C::LOADS / 2;  // DMA instructions in the first half-step
+  auto kstep = [&](int it, auto st_c, auto phase_c) {
+    constexpr int ST = decltype(st_c)::value;
+    constexpr int PH = decltype(phase_c)::value;
+    constexpr int NMF = C::FW * C::FA;
+    // fragment reads ride on MFMA slots [0, HALF), the DMA on [DBEGIN, NMF);
+    // with a single MFMA per sub-step both use slot 0
+    constexpr int HALF = NMF / 2 > 0 ? NMF / 2 : 1;
+    constexpr int DSLOTS = NMF - HALF > 0 ? NMF - HALF : 1;
+    constexpr int DBEGIN = NMF - DSLOTS;
+    using Next = std::integral_constant<int, (ST + 1) % STAGES>;
+    using Prev = std::integral_constant<int, (ST + STAGES - 1) % STAGES>;
+#pragma unroll
+    for (int sub = 0; sub < C::NSUB; ++sub) {
+      const int fb = sub & 1;
+      const bool last = sub == C::NSUB - 1;
+      if (last) {
+        wait_vmcnt<(STAGES - 2) * C::LOADS>();
+        __syncthreads();
+      }
+      // this sub-step's DMA: [d0, d1) of step dstep into stage DS
+      const int nd = (sub == 0) ? C::LOADS - LH : (last ? LH : 0);
+#pragma unroll
+      for (int q = 0; q < NMF; ++q) {
+        const int i = q / C::FA, j = q % C::FA;
+        acc[PH][i][j] = mfma32(wf[fb][i], af[fb][j], acc[PH][i][j]);
+        if (q < HALF) {
+#pragma unroll
+          for (int x = q * NFRAG / HALF; x < (q + 1) * NFRAG / HALF; ++x) {
+            if (last) frag(Next{}, 0, fb ^ 1, x);
+            else frag(st_c, sub + 1, fb ^ 1, x);
+          }
+        }
+        if (nd > 0 && q >= DBEGIN) {
+#pragma unroll
+          for (int x = (q - DBEGIN) * nd / DSLOTS; x < (q - DBEGIN + 1) * nd / DSLOTS; ++x) {
+            if (sub == 0) dma(it + STAGES - 1, Prev{}, LH + x);
+            else dma(it + STAGES, st_c, x);
+          }
+        }
+        // keep this MFMA and its share of memory work together, in order
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+  };
+
+  // STAGES K steps, the stage ring unrolled
+  auto round = [&](int it0, auto phase_c) {
+    [&]<int... S>(std::integer_sequence<int, S...>) {
+      (kstep(it0 + S, std::integral_constant<int, S>{}, phase_c), ...);
+    }(std::make_integer_sequence<int, STAGES>{});
+  };
+
+  // ---- prologue -------------------------------------------------------------------
+  // steps 0..STAGES-2 whole and the first half of step STAGES-1, as if the
+  // loop had already been running
+  auto fill = [&](int it, auto st_c, int q0, int q1) {
+#pragma unroll
+    for (int q = 0; q < C::LOADS; ++q)
+      if (q >= q0 && q < q1) dma(it, st_c, q);
+  };
+  [&]<int... S>(std::integer_sequence<int, S...>) {
+    (fill(S, std::integral_constant<int, S>{}, 0, C::LOADS), ...);
+  }(std::make_integer_sequence<int, STAGES - 1>{});
+  fill(STAGES - 1, std::integral_constant<int, STAGES - 1>{}, 0, LH);
+  wait_vmcnt<(STAGES - 2) * C::LOADS + LH>();
+  __syncthreads();
+#pragma unroll
+  for (int r = 0; r < NFRAG; ++r) frag(std::integral_constant<int, 0>{}, 0, 0, r);
+
+  // ---- main loop ----------------------------------------------------------------
+  if constexpr (MODE == MODE_SYNC) {
+    for (int it = 0; it < nk_pad; it += STAGES) round(it, std::integral_constant<int, 0>{});
+    // Gate finished: SiLU on the register-resident Gate accumulator while the
+    // next Up weight tiles are still in flight.
+#pragma unroll
+    for (int i = 0; i < C::FW; ++i)
+#pragma unroll
+      for (int j = 0; j < C::FA; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[0][i][j][r] = silu(acc[0][i][j][r]);
+    for (int it = nk_pad; it < total; it += STAGES) round(it, std::integral_constant<int, 1>{});
+  } else {
+    for (int it = 0; it < total; it += STAGES) round(it, std::integral_constant<int, 0>{});
+  }
+
+  // ---- epilogue: bf16 tile through LDS, then 16-byte row stores -------------------
+  wait_vmcnt<0>();
+  __syncthreads();
+  uint16_t* ys = reinterpret_cast<uint16_t*>(smem);  // [BM][YLD]
+  const int h32 = lane >> 5;
+#pragma unroll
+  for (int i = 0; i < C::FW; ++i)
+#pragma unroll
+    for (int j = 0; j < C::FA; ++j) {
+      const int row = a_row + j * 32;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        // registers 4q..4q+3 hold weight columns wcl..wcl+3 of this lane's row
+        const int wcl = wn * C::WTW + i * 32 + 8 * q + 4 * h32;
+        const f32x16& d = acc[0][i][j];
+        if constexpr (MODE == MODE_INTERLEAVE) {
+          const float ya = silu(d[4 * q + 0]) * d[4 * q + 1];  // pair (wcl, wcl+1)
+          const float yb = silu(d[4 * q + 2]) * d[4 * q + 3];  // pair (wcl+2, wcl+3)
+          *reinterpret_cast<uint32_t*>(ys + row * C::YLD + wcl / 2) = pack_bf16x2(ya, yb);
+        } else {
+          float y[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            y[e] = (MODE == MODE_SYNC) ? d[4 * q + e] * acc[C::NACC - 1][i][j][4 * q + e]
+                                       : d[4 * q + e];
+          *reinterpret_cast<u32x2*>(ys + row * C::YLD + wcl) =
+              u32x2{pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3])};
         }
       }
     }
-  };
-
-  f32x16 acc0[C::FM][C::FN];
-  f32x16 acc1[(MODE == MODE_GEMM) ? 1 : C::FM][(MODE == MODE_GEMM) ? 1 : C::FN];
-#pragma unroll
-  for (int i = 0; i < C::FM; ++i)
-#pragma unroll
-    for (int j = 0; j < C::FN; ++j) {
-      acc0[i][j] = f32x16{};
-      if (MODE != MODE_GEMM) acc1[i][j] = f32x16{};
-    }
-
-  // per-lane fragment coordinates
-  const int frow = lane & 31;        // row (A) or column (B) inside a 32 block
-  const int fk = (lane >> 5) * 8;    // k offset inside a 16-deep step
-
-  auto compute = [&](int buf, int phase) {
-    const uint16_t* as = As + buf * C::LDS_A;
-    const uint16_t* bs = Bs + buf * C::LDS_B;
-#pragma unroll
-    for (int kk = 0; kk < BK; kk += 16) {
-      u32x4 af[C::FM], bf[C::FN];
-#pragma unroll
-      for (int i = 0; i < C::FM; ++i)
-        af[i] = *reinterpret_cast<const u32x4*>(as + (wm * C::WTM + i * 32 + frow) * C::LDK + kk + fk);
-#pragma unroll
-      for (int j = 0; j < C::FN; ++j)
-        bf[j] = *reinterpret_cast<const u32x4*>(bs + (wn * C::WTN + j * 32 + frow) * C::LDK + kk + fk);
-      if (MODE == MODE_INTERLEAVE) {
-        u32x4 bu[C::FN];
-#pragma unroll
-        for (int j = 0; j < C::FN; ++j)
-          bu[j] = *reinterpret_cast<const u32x4*>(bs + (BNY + wn * C::WTN + j * 32 + frow) * C::LDK + kk + fk);
-#pragma unroll
-        for (int i = 0; i < C::FM; ++i)
-#pragma unroll
-          for (int j = 0; j < C::FN; ++j) {
-            acc0[i][j] = mfma32(af[i], bf[j], acc0[i][j]);
-            acc1[i][j] = mfma32(af[i], bu[j], acc1[i][j]);
-          }
-      } else if (MODE == MODE_SYNC && phase != 0) {
-#pragma unroll
-        for (int i = 0; i < C::FM; ++i)
-#pragma unroll
-          for (int j = 0; j < C::FN; ++j) acc1[i][j] = mfma32(af[i], bf[j], acc1[i][j]);
-      } else {
-#pragma unroll
-        for (int i = 0; i < C::FM; ++i)
-#pragma unroll
-          for (int j = 0; j < C::FN; ++j) acc0[i][j] = mfma32(af[i], bf[j], acc0[i][j]);
-      }
-    }
-  };
-
-  // ---- main loop: one barrier per K step -----------------------------------
-  if (total > 0) {
-    gload(0);
-    swrite(0);
-  }
   __syncthreads();
-  if (total > 1) gload(1);
-  for (int it = 0; it < total; ++it) {
-    const int cur = it & 1;
-    const int phase = (MODE == MODE_SYNC && it >= nk) ? 1 : 0;
-    compute(cur, phase);
-    if (it + 1 < total) swrite(cur ^ 1);
-    if (it + 2 < total) gload(it + 2);
-    if (MODE == MODE_SYNC && it == nk - 1) {
-      // Gate finished: SiLU on the register-resident Gate accumulator while
-      // the first Up weight tiles are in flight.
-#pragma unroll
-      for (int i = 0; i < C::FM; ++i)
-#pragma unroll
-        for (int j = 0; j < C::FN; ++j)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) acc0[i][j][r] = silu(acc0[i][j][r]);
-    }
-    __syncthreads();
+  constexpr int YCH = C::BNY / 8;
+  for (int p = tid; p < BM * YCH; p += C::kThreads) {
+    const int row = p / YCH, cq = p % YCH;
+    const int gr = m0 + row, gc = y0 + cq * 8;
+    if (gr < M && gc < N)
+      *reinterpret_cast<u32x4*>(Y + (size_t)gr * N + gc) =
+          *reinterpret_cast<const u32x4*>(ys + row * C::YLD + cq * 8);
   }
-
-  // ---- epilogue ------------------------------------------------------------
-  const int col_in = lane & 31;
-  const int row_q = (lane >> 5) * 4;
-#pragma unroll
-  for (int i = 0; i < C::FM; ++i)
-#pragma unroll
-    for (int j = 0; j < C::FN; ++j) {
-      const int col = n0 + wn * C::WTN + j * 32 + col_in;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = m0 + wm * C::WTM + i * 32 + (r >> 2) * 8 + row_q + (r & 3);
-        float v;
-        if (MODE == MODE_INTERLEAVE) v = silu(acc0[i][j][r]) * acc1[i][j][r];
-        else if (MODE == MODE_SYNC) v = acc0[i][j][r] * acc1[i][j][r];
-        else v = acc0[i][j][r];
-        if (row < M && col < N) Y[(size_t)row * N + col] = bf16_bits(v);
-      }
-    }
 }
 
 // ============================================================================
@@ -466,16 +603,16 @@ __global__ __launch_bounds__(256) void pack_kernel(const uint16_t* __restrict__ 
 // ============================================================================
 // Configuration list and launchers
 // ============================================================================
-template <int MODE, int BM, int BNY, int BK, int WGM, int WGN>
+template <int MODE, int BM, int BNW, int BK, int STAGES, int WGM, int WGN>
 static hipError_t launch_tiled(const LaunchArgs& a) {
-  using C = Tiled<MODE, BM, BNY, BK, WGM, WGN>;
-  const int ntm = (a.M + BM - 1) / BM, ntn = (a.N + BNY - 1) / BNY;
+  using C = Tiled<MODE, BM, BNW, BK, STAGES, WGM, WGN>;
+  const int ntm = (a.M + BM - 1) / BM, ntn = (a.N + C::BNY - 1) / C::BNY;
   const long long nwg = (long long)ntm * ntn;
   if (nwg <= 0) return hipSuccess;
   if (nwg > 0x7fffffffLL) return hipErrorInvalidValue;
   int group_m = a.group_m > 0 ? a.group_m : 8;
   if (group_m > ntm) group_m = ntm;
-  hipLaunchKernelGGL((tiled_kernel<MODE, BM, BNY, BK, WGM, WGN>), dim3((unsigned)nwg),
+  hipLaunchKernelGGL((tiled_kernel<MODE, BM, BNW, BK, STAGES, WGM, WGN>), dim3((unsigned)nwg),
                      dim3(C::kThreads), 0, a.stream, a.A, a.W1, a.W2, a.Y, a.M, a.N, a.K,
                      group_m);
   return hipGetLastError();
@@ -493,38 +630,38 @@ static hipError_t launch_skinny(const LaunchArgs& a) {
   return hipGetLastError();
 }
 
-#define TILED(mode, v, bm, bn, bk, wgm, wgn)                                               \
-  {v, 0, bm, bn, bk, 4, 1, Tiled<mode, bm, bn, bk, wgm, wgn>::LDS_BYTES,                  \
-   &launch_tiled<mode, bm, bn, bk, wgm, wgn>}
+#define TILED(mode, v, bm, bnw, bk, st, wgm, wgn)                                          \
+  {v, 0, bm, Tiled<mode, bm, bnw, bk, st, wgm, wgn>::BNY, bk, 4, 1,                         \
+   Tiled<mode, bm, bnw, bk, st, wgm, wgn>::LDS_BYTES, &launch_tiled<mode, bm, bnw, bk, st, wgm, wgn>}
 #define SKINNY(mode, v, mt, nw)                                                            \
   {v, 1, (mt) * 16, Skinny<mode, mt, nw>::SLAB_Y, 32, nw, nw, Skinny<mode, mt, nw>::LDS_BYTES, \
    &launch_skinny<mode, mt, nw>}
 
 static const KernelConfig kConfigs[] = {
     // ---- interleave (Kernel-2 family) --------------------------------------
-    TILED(MODE_INTERLEAVE, VAR_INTERLEAVE, 256, 128, 64, 2, 2),  // 0
-    TILED(MODE_INTERLEAVE, VAR_INTERLEAVE, 128, 128, 64, 2, 2),  // 1
-    TILED(MODE_INTERLEAVE, VAR_INTERLEAVE, 128, 64, 64, 2, 2),   // 2
-    TILED(MODE_INTERLEAVE, VAR_INTERLEAVE, 64, 64, 64, 2, 2),    // 3
-    SKINNY(MODE_INTERLEAVE, VAR_INTERLEAVE, 1, 8),               // 4
-    SKINNY(MODE_INTERLEAVE, VAR_INTERLEAVE, 2, 8),               // 5
-    SKINNY(MODE_INTERLEAVE, VAR_INTERLEAVE, 4, 4),               // 6
+    TILED(MODE_INTERLEAVE, VAR_INTERLEAVE, 256, 256, 32, 4, 2, 2),  // 0
+    TILED(MODE_INTERLEAVE, VAR_INTERLEAVE, 128, 256, 32, 4, 2, 2),  // 1
+    TILED(MODE_INTERLEAVE, VAR_INTERLEAVE, 128, 128, 32, 4, 2, 2),  // 2
+    TILED(MODE_INTERLEAVE, VAR_INTERLEAVE, 64, 128, 32, 4, 2, 2),   // 3
+    SKINNY(MODE_INTERLEAVE, VAR_INTERLEAVE, 1, 8),                  // 4
+    SKINNY(MODE_INTERLEAVE, VAR_INTERLEAVE, 2, 8),                  // 5
+    SKINNY(MODE_INTERLEAVE, VAR_INTERLEAVE, 4, 4),                  // 6
     // ---- sync (Kernel-1 family) --------------------------------------------
-    TILED(MODE_SYNC, VAR_SYNC, 256, 128, 64, 2, 2),              // 7
-    TILED(MODE_SYNC, VAR_SYNC, 128, 128, 64, 2, 2),              // 8
-    TILED(MODE_SYNC, VAR_SYNC, 128, 64, 64, 2, 2),               // 9
-    TILED(MODE_SYNC, VAR_SYNC, 64, 64, 64, 2, 2),                // 10
-    SKINNY(MODE_SYNC, VAR_SYNC, 1, 8),                           // 11
-    SKINNY(MODE_SYNC, VAR_SYNC, 2, 8),                           // 12
-    SKINNY(MODE_SYNC, VAR_SYNC, 4, 4),                           // 13
+    TILED(MODE_SYNC, VAR_SYNC, 256, 128, 32, 4, 2, 2),              // 7
+    TILED(MODE_SYNC, VAR_SYNC, 128, 128, 32, 4, 2, 2),              // 8
+    TILED(MODE_SYNC, VAR_SYNC, 128, 64, 32, 4, 2, 2),               // 9
+    TILED(MODE_SYNC, VAR_SYNC, 64, 64, 32, 4, 2, 2),                // 10
+    SKINNY(MODE_SYNC, VAR_SYNC, 1, 8),                              // 11
+    SKINNY(MODE_SYNC, VAR_SYNC, 2, 8),                              // 12
+    SKINNY(MODE_SYNC, VAR_SYNC, 4, 4),                              // 13
     // ---- plain GEMM for the unfused baseline -------------------------------
-    TILED(MODE_GEMM, VAR_GEMM, 256, 256, 64, 2, 2),              // 14
-    TILED(MODE_GEMM, VAR_GEMM, 256, 128, 64, 2, 2),              // 15
-    TILED(MODE_GEMM, VAR_GEMM, 128, 128, 64, 2, 2),              // 16
-    TILED(MODE_GEMM, VAR_GEMM, 64, 64, 64, 2, 2),                // 17
-    SKINNY(MODE_GEMM, VAR_GEMM, 1, 8),                           // 18
-    SKINNY(MODE_GEMM, VAR_GEMM, 2, 8),                           // 19
-    SKINNY(MODE_GEMM, VAR_GEMM, 4, 4),                           // 20
+    TILED(MODE_GEMM, VAR_GEMM, 256, 256, 32, 4, 2, 2),              // 14
+    TILED(MODE_GEMM, VAR_GEMM, 256, 128, 32, 4, 2, 2),              // 15
+    TILED(MODE_GEMM, VAR_GEMM, 128, 128, 32, 4, 2, 2),              // 16
+    TILED(MODE_GEMM, VAR_GEMM, 64, 64, 32, 4, 2, 2),                // 17
+    SKINNY(MODE_GEMM, VAR_GEMM, 1, 8),                              // 18
+    SKINNY(MODE_GEMM, VAR_GEMM, 2, 8),                              // 19
+    SKINNY(MODE_GEMM, VAR_GEMM, 4, 4),                              // 20
 };
 
 int config_count() { return (int)(sizeof(kConfigs) / sizeof(kConfigs[0])); }
