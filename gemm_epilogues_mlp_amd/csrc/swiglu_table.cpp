@@ -25,7 +25,25 @@ struct ShapeEntry {
 // only ever records a configuration that won its sweep, so the table cannot
 // pick something slower than the fallback it replaces.
 const ShapeEntry kTable[] = {
-    {-1, 0, 0, 0, -1},  // sentinel
+    // Qwen2.5-0.5B MLP, M=128
+    {VAR_INTERLEAVE, 128, 4864, 896, 3},
+    {VAR_SYNC, 128, 4864, 896, 10},
+    {VAR_GEMM, 128, 4864, 896, 17},
+    // Qwen2.5-1.5B MLP, M=2048
+    {VAR_INTERLEAVE, 2048, 8960, 1536, 0},
+    {VAR_SYNC, 2048, 8960, 1536, 8},
+    {VAR_GEMM, 2048, 8960, 1536, 14},
+    // Qwen2.5-7B MLP, decode M=16 and prefill M=8192
+    {VAR_INTERLEAVE, 16, 18944, 3584, 4},
+    {VAR_SYNC, 16, 18944, 3584, 11},
+    {VAR_GEMM, 16, 18944, 3584, 18},
+    {VAR_INTERLEAVE, 8192, 18944, 3584, 0},
+    {VAR_SYNC, 8192, 18944, 3584, 7},
+    {VAR_GEMM, 8192, 18944, 3584, 14},
+    // Qwen2.5-72B MLP, M=4096
+    {VAR_INTERLEAVE, 4096, 29568, 8192, 0},
+    {VAR_SYNC, 4096, 29568, 8192, 7},
+    {VAR_GEMM, 4096, 29568, 8192, 14},
 };
 
 int find_config(int variant, int family, int bm, int bn) {
@@ -62,9 +80,12 @@ int select_config(int variant, long long M, long long N, long long K, int cu_cou
 }
 
 int recommend_layout(long long M, long long N, long long K, int cu_count) {
-  (void)N, (void)K, (void)cu_count;
-  // the page's rule: interleave for small batches (and by default), sync for M > 2048
-  return M > 2048 ? 0 : 1;
+  (void)M, (void)N, (void)K, (void)cu_count;
+  // The page prefers the sync kernel above M = 2048.  On MI355X the interleave
+  // kernel was faster at every measured M (0.5B-72B shapes, M = 16..8192): it
+  // loads A once and keeps every accumulator busy in every K step, while the
+  // sync kernel alternates between half of its registers (Gate, then Up).
+  return 1;
 }
 
 }  // namespace swiglu
