@@ -65,6 +65,11 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 // assembly so the compiler does not add a conservative vmcnt(0) in front of
 // every LDS read; completion is tracked with wait_vmcnt<>() by the caller.
 __device__ __forceinline__ void lds_dma16(uint32_t lds_wave_base, uint32_t voffset, i32x4 rsrc) {
+  // both operands are wave-uniform by construction; readfirstlane makes that
+  // visible to the compiler where its divergence analysis cannot prove it
+  lds_wave_base = __builtin_amdgcn_readfirstlane(lds_wave_base);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) rsrc[i] = __builtin_amdgcn_readfirstlane(rsrc[i]);
   asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
                :
                : "s"(lds_wave_base), "v"(voffset), "s"(rsrc)

@@ -69,8 +69,9 @@ enum Mode { MODE_INTERLEAVE = 0, MODE_SYNC = 1, MODE_GEMM = 2 };
 //   W stage  [BK][BNW]  row-major, chunk c of row k stored at c ^ w_swz(k)
 template <int MODE, int BM, int BNW, int BK, int STAGES, int WGM, int WGN>
 struct Tiled {
-  static constexpr int kThreads = 256;
-  static_assert(WGM * WGN == 4, "four waves per workgroup");
+  static constexpr int kWaves = WGM * WGN;
+  static_assert(kWaves == 4 || kWaves == 8, "four waves (one per SIMD) or eight (two per SIMD)");
+  static constexpr int kThreads = 64 * kWaves;
   static constexpr int BNY = (MODE == MODE_INTERLEAVE) ? BNW / 2 : BNW;  // output columns
   static constexpr int WTM = BM / WGM;   // A rows per wave
   static constexpr int WTW = BNW / WGN;  // weight columns per wave
@@ -87,17 +88,21 @@ struct Tiled {
   static constexpr int A_BYTES = BM * BK * 2;
   static constexpr int W_BYTES = BK * BNW * 2;
   static constexpr int STAGE_BYTES = A_BYTES + W_BYTES;
-  static_assert((BM * ACH) % kThreads == 0 && (BK * WCH) % kThreads == 0, "even split");
-  static constexpr int A_LOADS = BM * ACH / kThreads;  // DMA instructions per thread
-  static constexpr int W_LOADS = BK * WCH / kThreads;
+  // DMA instructions per thread (a whole wave without a chunk of its own in
+  // the last round loads zeros into a junk slot, so that every wave issues
+  // the same number of loads per step and the vmcnt accounting stays uniform)
+  static constexpr int A_CHUNKS = BM * ACH, W_CHUNKS = BK * WCH;
+  static_assert(A_CHUNKS % 64 == 0 && W_CHUNKS % 64 == 0, "whole waves of chunks");
+  static constexpr int A_LOADS = (A_CHUNKS + kThreads - 1) / kThreads;
+  static constexpr int W_LOADS = (W_CHUNKS + kThreads - 1) / kThreads;
   static constexpr int LOADS = A_LOADS + W_LOADS;
   static_assert(STAGES >= 2 && LOADS * (STAGES - 2) + LOADS / 2 <= 63, "vmcnt range");
   static constexpr int YLD = BNY + 8;    // padded row of the output staging tile
   static constexpr int Y_BYTES = BM * YLD * 2;
-  static constexpr int LDS_BYTES =
-      STAGES * STAGE_BYTES > Y_BYTES ? STAGES * STAGE_BYTES : Y_BYTES;
+  static constexpr int JUNK = STAGES * STAGE_BYTES;  // 1 KB slot for zero DMA
+  static constexpr int LDS_BYTES = JUNK + 1024 > Y_BYTES ? JUNK + 1024 : Y_BYTES;
   static_assert(LDS_BYTES <= 160 * 1024, "LDS");
-  static_assert(WCH == 8 || WCH % 16 == 0, "W swizzle needs 8 or a multiple of 16 chunks");
+  static_assert(WCH % 8 == 0, "W swizzle works on aligned groups of 8 chunks");
 
   // Swizzles: a fragment read touches 16 B per lane; lanes that the LDS
   // serves together (8 lanes per 128 B, or 16 per 256 B) must hit distinct
@@ -110,11 +115,11 @@ struct Tiled {
   }
   // chunk XOR 2*g: the four rows of a 16-lane group land in distinct 32 B
   // slots of 128 B, and together with the neighbouring group in distinct
-  // slots of 256 B.  Rows of 128 B alternate halves of 256 B by themselves,
-  // so g = k % 4 suffices there; wider rows all start at the same bank and
-  // take g = 0, 3, 5, 6 for k % 4 = 0..3.
+  // slots of 256 B.  Rows that are an odd multiple of 128 B alternate halves
+  // of 256 B by themselves, so g = k % 4 suffices there; rows a multiple of
+  // 256 B all start at the same bank and take g = 0, 3, 5, 6 for k % 4 = 0..3.
   __host__ __device__ static constexpr int w_swz(int row) {
-    if (WCH == 8) return (row & 3) << 1;
+    if ((WCH / 8) % 2 == 1) return (row & 3) << 1;  // rows an odd multiple of 128 B
     return ((0x6530 >> (4 * (row & 3))) & 0xf) << 1;
   }
   // every swizzle must permute the chunks of its own row (checked at compile
@@ -138,7 +143,7 @@ struct Tiled {
 
 
 template <int MODE, int BM, int BNW, int BK, int STAGES, int WGM, int WGN>
-__global__ __launch_bounds__(256) void tiled_kernel(const uint16_t* __restrict__ A,
+__global__ __launch_bounds__(64 * WGM * WGN) void tiled_kernel(const uint16_t* __restrict__ A,
                                                     const uint16_t* __restrict__ W1,
                                                     const uint16_t* __restrict__ W2,
                                                     uint16_t* __restrict__ Y, int M, int N,
@@ -166,12 +171,14 @@ __global__ __launch_bounds__(256) void tiled_kernel(const uint16_t* __restrict__
   const int wc0 = tn * BNW;  // first weight column (W_fused, W1/W2 or W)
   const int y0 = tn * C::BNY;
 
-  // K steps, padded to a multiple of STAGES so the main loop can be unrolled
-  // over the stage ring with compile-time stage offsets.  Padded steps (and,
-  // in the sync variant, each phase separately) load zeros and add nothing.
+  // K steps.  Step `it` always uses stage it % STAGES and the main loop is
+  // unrolled over the stage ring, so every stage offset is a compile-time
+  // constant.  The sync variant runs the K steps twice (Gate, then Up); its
+  // Gate phase is padded with zero-filled steps to a ring boundary (nk0) so
+  // that the Up phase starts on stage 0.
   const int nk = (K + BK - 1) / BK;
-  const int nk_pad = (nk + STAGES - 1) / STAGES * STAGES;
-  const int total = (MODE == MODE_SYNC) ? 2 * nk_pad : nk_pad;
+  const int nk0 = (MODE == MODE_SYNC) ? (nk + STAGES - 1) / STAGES * STAGES : nk;
+  const int total = (MODE == MODE_SYNC) ? nk0 + nk : nk;
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);  // wave id in an SGPR
 
   // ---- DMA of one K step into a stage ----------------------------------------
@@ -207,19 +214,24 @@ __global__ __launch_bounds__(256) void tiled_kernel(const uint16_t* __restrict__
   // DMA instruction q (A chunks first, then W chunks) of K step `it` into
   // stage ST.  k0 is capped at K for steps past the end, which keeps every
   // offset below 2^32 and out of range.
-  auto dma = [&](int it, auto st_c, int q) {
+  auto dma = [&](int it, auto st_c, int q) __attribute__((always_inline)) {
     constexpr int ST = decltype(st_c)::value;
-    const bool up = MODE == MODE_SYNC && it >= nk_pad;
-    const int kt = up ? it - nk_pad : it;
+    const bool up = MODE == MODE_SYNC && it >= nk0;
+    const int kt = up ? it - nk0 : it;
     const int k0 = (it < total && kt < nk) ? kt * BK : K;
     const uint32_t sbase = lds0 + ST * C::STAGE_BYTES;
     if (q < C::A_LOADS) {
-      const uint32_t off = (k0 + a_k[q] < K) ? a_off[q] + (uint32_t)k0 * 2u : kOutOfRange;
-      lds_dma16(sbase + (C::kThreads * q + 64 * wave_u) * 16, off, rsA);
+      const int p0 = C::kThreads * q + 64 * wave_u;  // first chunk of this wave
+      const bool own = p0 < C::A_CHUNKS;
+      const uint32_t off =
+          (own && k0 + a_k[q] < K) ? a_off[q] + (uint32_t)k0 * 2u : kOutOfRange;
+      lds_dma16(own ? sbase + p0 * 16 : lds0 + C::JUNK, off, rsA);
     } else {
       const int i = q - C::A_LOADS;
-      const uint32_t off = w_off[i] + (uint32_t)k0 * (uint32_t)ldw * 2u;
-      lds_dma16(sbase + C::A_BYTES + (C::kThreads * i + 64 * wave_u) * 16, off, up ? rsW2 : rsW1);
+      const int p0 = C::kThreads * i + 64 * wave_u;
+      const bool own = p0 < C::W_CHUNKS;
+      const uint32_t off = own ? w_off[i] + (uint32_t)k0 * (uint32_t)ldw * 2u : kOutOfRange;
+      lds_dma16(own ? sbase + C::A_BYTES + p0 * 16 : lds0 + C::JUNK, off, up ? rsW2 : rsW1);
     }
   };
 
@@ -236,7 +248,7 @@ __global__ __launch_bounds__(256) void tiled_kernel(const uint16_t* __restrict__
   u32x4 wf[2][C::FW], af[2][C::FA];
   // fragment read r of sub-step `sub` of stage ST (r < 2 FW: half r%2 of
   // weight block r/2; otherwise A block r - 2 FW)
-  auto frag = [&](auto st_c, int sub, int fb, int r) {
+  auto frag = [&](auto st_c, int sub, int fb, int r) __attribute__((always_inline)) {
     constexpr int ST = decltype(st_c)::value;
     const uint8_t* st = smem + ST * C::STAGE_BYTES;
     const int kk = sub * 16;
@@ -273,7 +285,7 @@ __global__ __launch_bounds__(256) void tiled_kernel(const uint16_t* __restrict__
   // itself.  Spreading the DMA keeps the address FIFO from backing up into
   // the MFMA stream, and the barrier overlaps the MFMA tail of sub-step 0.
   constexpr int LH = C::LOADS / 2;  // DMA instructions in the first half-step
-  auto kstep = [&](int it, auto st_c, auto phase_c) {
+  auto kstep = [&](int it, auto st_c, auto phase_c) __attribute__((always_inline)) {
     constexpr int ST = decltype(st_c)::value;
     constexpr int PH = decltype(phase_c)::value;
     constexpr int NMF = C::FW * C::FA;
@@ -319,21 +331,30 @@ __global__ __launch_bounds__(256) void tiled_kernel(const uint16_t* __restrict__
   };
 
   // STAGES K steps, the stage ring unrolled
-  auto round = [&](int it0, auto phase_c) {
-    [&]<int... S>(std::integer_sequence<int, S...>) {
+  auto round = [&](int it0, auto phase_c) __attribute__((always_inline)) {
+    [&]<int... S>(std::integer_sequence<int, S...>) __attribute__((always_inline)) {
       (kstep(it0 + S, std::integral_constant<int, S>{}, phase_c), ...);
     }(std::make_integer_sequence<int, STAGES>{});
+  };
+  // steps [b, e) with b on a ring boundary: whole rounds, then the remaining
+  // steps (fewer than STAGES), each with its compile-time stage
+  auto run = [&](int b, int e, auto phase_c) __attribute__((always_inline)) {
+    int it = b;
+    for (; it + STAGES <= e; it += STAGES) round(it, phase_c);
+    [&]<int... S>(std::integer_sequence<int, S...>) __attribute__((always_inline)) {
+      ((it + S < e ? (kstep(it + S, std::integral_constant<int, S>{}, phase_c), 0) : 0), ...);
+    }(std::make_integer_sequence<int, STAGES - 1>{});
   };
 
   // ---- prologue -------------------------------------------------------------------
   // steps 0..STAGES-2 whole and the first half of step STAGES-1, as if the
   // loop had already been running
-  auto fill = [&](int it, auto st_c, int q0, int q1) {
+  auto fill = [&](int it, auto st_c, int q0, int q1) __attribute__((always_inline)) {
 #pragma unroll
     for (int q = 0; q < C::LOADS; ++q)
       if (q >= q0 && q < q1) dma(it, st_c, q);
   };
-  [&]<int... S>(std::integer_sequence<int, S...>) {
+  [&]<int... S>(std::integer_sequence<int, S...>) __attribute__((always_inline)) {
     (fill(S, std::integral_constant<int, S>{}, 0, C::LOADS), ...);
   }(std::make_integer_sequence<int, STAGES - 1>{});
   fill(STAGES - 1, std::integral_constant<int, STAGES - 1>{}, 0, LH);
@@ -344,7 +365,7 @@ __global__ __launch_bounds__(256) void tiled_kernel(const uint16_t* __restrict__
 
   // ---- main loop ----------------------------------------------------------------
   if constexpr (MODE == MODE_SYNC) {
-    for (int it = 0; it < nk_pad; it += STAGES) round(it, std::integral_constant<int, 0>{});
+    run(0, nk0, std::integral_constant<int, 0>{});
     // Gate finished: SiLU on the register-resident Gate accumulator while the
     // next Up weight tiles are still in flight.
 #pragma unroll
@@ -353,9 +374,9 @@ __global__ __launch_bounds__(256) void tiled_kernel(const uint16_t* __restrict__
       for (int j = 0; j < C::FA; ++j)
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[0][i][j][r] = silu(acc[0][i][j][r]);
-    for (int it = nk_pad; it < total; it += STAGES) round(it, std::integral_constant<int, 1>{});
+    run(nk0, total, std::integral_constant<int, 1>{});
   } else {
-    for (int it = 0; it < total; it += STAGES) round(it, std::integral_constant<int, 0>{});
+    run(0, total, std::integral_constant<int, 0>{});
   }
 
   // ---- epilogue: bf16 tile through LDS, then 16-byte row stores -------------------
@@ -454,7 +475,8 @@ __device__ __forceinline__ void skinny_load(const uint16_t* __restrict__ A,
 }
 
 template <int MODE, int MT, int NW>
-__global__ __launch_bounds__(64 * NW) void skinny_kernel(const uint16_t* __restrict__ A,
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(MT == 1 ? 4 : 2)))
+void skinny_kernel(const uint16_t* __restrict__ A,
                                                          const uint16_t* __restrict__ W1,
                                                          const uint16_t* __restrict__ W2,
                                                          uint16_t* __restrict__ Y, int M, int N,
@@ -488,18 +510,14 @@ __global__ __launch_bounds__(64 * NW) void skinny_kernel(const uint16_t* __restr
       for (int mt = 0; mt < MT; ++mt) acc[mt][c] = mfma16(af[mt], col[c], acc[mt][c]);
   };
 
-  // two register sets: the loads of step s+1 are in flight while step s computes
-  u32x4 r0[8], r1[8];
-  u32x4 a0[MT], a1[MT];
-  int s = s_begin;
-  if (s < s_end) skinny_load<MODE, MT>(A, W1, W2, M, N, K, m0, slab, lane, s, r0, a0);
-  while (s < s_end) {
-    if (s + 1 < s_end) skinny_load<MODE, MT>(A, W1, W2, M, N, K, m0, slab, lane, s + 1, r1, a1);
-    mma(r0, a0);
-    if (s + 1 >= s_end) break;
-    if (s + 2 < s_end) skinny_load<MODE, MT>(A, W1, W2, M, N, K, m0, slab, lane, s + 2, r0, a0);
-    mma(r1, a1);
-    s += 2;
+  // One register set per wave: while a wave transposes and multiplies, the
+  // other waves of the SIMD (four per SIMD at MT = 1) have their loads in
+  // flight, which keeps more bytes outstanding per CU than a per-wave double
+  // buffer that would cost the occupancy.
+  for (int s = s_begin; s < s_end; ++s) {
+    u32x4 rows[8], af[MT];
+    skinny_load<MODE, MT>(A, W1, W2, M, N, K, m0, slab, lane, s, rows, af);
+    mma(rows, af);
   }
 
   // ---- split-K reduction through LDS (fixed order: wave 0, 1, ..., NW-1) ----
@@ -631,7 +649,7 @@ static hipError_t launch_skinny(const LaunchArgs& a) {
 }
 
 #define TILED(mode, v, bm, bnw, bk, st, wgm, wgn)                                          \
-  {v, 0, bm, Tiled<mode, bm, bnw, bk, st, wgm, wgn>::BNY, bk, 4, 1,                         \
+  {v, 0, bm, Tiled<mode, bm, bnw, bk, st, wgm, wgn>::BNY, bk, (wgm) * (wgn), 1,             \
    Tiled<mode, bm, bnw, bk, st, wgm, wgn>::LDS_BYTES, &launch_tiled<mode, bm, bnw, bk, st, wgm, wgn>}
 #define SKINNY(mode, v, mt, nw)                                                            \
   {v, 1, (mt) * 16, Skinny<mode, mt, nw>::SLAB_Y, 32, nw, nw, Skinny<mode, mt, nw>::LDS_BYTES, \
@@ -662,6 +680,25 @@ static const KernelConfig kConfigs[] = {
     SKINNY(MODE_GEMM, VAR_GEMM, 1, 8),                              // 18
     SKINNY(MODE_GEMM, VAR_GEMM, 2, 8),                              // 19
     SKINNY(MODE_GEMM, VAR_GEMM, 4, 4),                              // 20
+    // ---- tiles sized for wave quantisation on 256 CUs ----------------------
+    TILED(MODE_INTERLEAVE, VAR_INTERLEAVE, 256, 192, 32, 4, 2, 2),  // 21
+    TILED(MODE_GEMM, VAR_GEMM, 256, 192, 32, 4, 2, 2),              // 22
+    // ---- small M with four waves per workgroup (two workgroups per CU) -----
+    SKINNY(MODE_INTERLEAVE, VAR_INTERLEAVE, 1, 4),                  // 23
+    SKINNY(MODE_INTERLEAVE, VAR_INTERLEAVE, 2, 4),                  // 24
+    SKINNY(MODE_SYNC, VAR_SYNC, 1, 4),                              // 25
+    SKINNY(MODE_GEMM, VAR_GEMM, 1, 4),                              // 26
+    // ---- small tiles with deep stage rings (latency-bound shapes) ----------
+    TILED(MODE_INTERLEAVE, VAR_INTERLEAVE, 64, 128, 32, 8, 2, 2),   // 27
+    TILED(MODE_INTERLEAVE, VAR_INTERLEAVE, 128, 128, 32, 8, 2, 2),  // 28
+    TILED(MODE_SYNC, VAR_SYNC, 64, 64, 32, 8, 2, 2),                // 29
+    TILED(MODE_GEMM, VAR_GEMM, 64, 64, 32, 8, 2, 2),                // 30
+    // ---- eight waves per workgroup: two per SIMD hide each other's stalls ----
+    TILED(MODE_INTERLEAVE, VAR_INTERLEAVE, 256, 256, 32, 4, 2, 4),  // 31
+    TILED(MODE_INTERLEAVE, VAR_INTERLEAVE, 256, 256, 32, 4, 4, 2),  // 32
+    TILED(MODE_GEMM, VAR_GEMM, 256, 256, 32, 4, 2, 4),              // 33
+    TILED(MODE_SYNC, VAR_SYNC, 256, 128, 32, 4, 2, 4),              // 34
+    TILED(MODE_INTERLEAVE, VAR_INTERLEAVE, 256, 192, 32, 4, 4, 2),  // 35
 };
 
 int config_count() { return (int)(sizeof(kConfigs) / sizeof(kConfigs[0])); }

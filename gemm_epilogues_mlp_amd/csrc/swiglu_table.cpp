@@ -27,29 +27,31 @@ struct ShapeEntry {
 const ShapeEntry kTable[] = {
     // Qwen2.5-0.5B MLP, M=128
     {VAR_INTERLEAVE, 128, 4864, 896, 3},
-    {VAR_SYNC, 128, 4864, 896, 10},
-    {VAR_GEMM, 128, 4864, 896, 17},
+    {VAR_SYNC, 128, 4864, 896, 29},
+    {VAR_GEMM, 128, 4864, 896, 30},
     // Qwen2.5-1.5B MLP, M=2048
-    {VAR_INTERLEAVE, 2048, 8960, 1536, 0},
+    {VAR_INTERLEAVE, 2048, 8960, 1536, 31},
     {VAR_SYNC, 2048, 8960, 1536, 8},
-    {VAR_GEMM, 2048, 8960, 1536, 14},
+    {VAR_GEMM, 2048, 8960, 1536, 33},
     // Qwen2.5-7B MLP, decode M=16 and prefill M=8192
-    {VAR_INTERLEAVE, 16, 18944, 3584, 4},
-    {VAR_SYNC, 16, 18944, 3584, 11},
-    {VAR_GEMM, 16, 18944, 3584, 18},
-    {VAR_INTERLEAVE, 8192, 18944, 3584, 0},
+    {VAR_INTERLEAVE, 16, 18944, 3584, 3},
+    {VAR_SYNC, 16, 18944, 3584, 12},
+    {VAR_GEMM, 16, 18944, 3584, 26},
+    {VAR_INTERLEAVE, 8192, 18944, 3584, 31},
     {VAR_SYNC, 8192, 18944, 3584, 7},
-    {VAR_GEMM, 8192, 18944, 3584, 14},
+    {VAR_GEMM, 8192, 18944, 3584, 33},
     // Qwen2.5-72B MLP, M=4096
-    {VAR_INTERLEAVE, 4096, 29568, 8192, 0},
+    {VAR_INTERLEAVE, 4096, 29568, 8192, 32},
     {VAR_SYNC, 4096, 29568, 8192, 7},
-    {VAR_GEMM, 4096, 29568, 8192, 14},
+    {VAR_GEMM, 4096, 29568, 8192, 33},
 };
 
-int find_config(int variant, int family, int bm, int bn) {
+int find_config(int variant, int family, int bm, int bn, int waves) {
   for (int i = 0; i < config_count(); ++i) {
     const KernelConfig* c = config_at(i);
-    if (c->variant == variant && c->family == family && c->bm == bm && c->bn == bn) return i;
+    if (c->variant == variant && c->family == family && c->bm == bm && c->bn == bn &&
+        (waves == 0 || c->waves == waves))
+      return i;
   }
   return -1;
 }
@@ -68,15 +70,19 @@ int select_config(int variant, long long M, long long N, long long K, int cu_cou
   if (M <= 64) {
     // decode-sized batches: split-K weight streaming, 16-row MFMA blocks
     const int mt = M <= 16 ? 1 : (M <= 32 ? 2 : 4);
-    return find_config(variant, 1, mt * 16, variant == VAR_GEMM ? 128 : 64);
+    return find_config(variant, 1, mt * 16, variant == VAR_GEMM ? 128 : 64, 0);
   }
-  // LDS-tiled: the largest tile that still gives two workgroups per CU
-  static const int kFused[][2] = {{256, 128}, {128, 128}, {128, 64}, {64, 64}};
-  static const int kGemm[][2] = {{256, 256}, {256, 128}, {128, 128}, {64, 64}};
-  const int(*cand)[2] = variant == VAR_GEMM ? kGemm : kFused;
+  // LDS-tiled: the largest tile that still gives two workgroups per CU; the
+  // 256-row tiles run eight waves (two per SIMD), the smaller ones four
+  struct Cand { int bm, bn, waves; };
+  static const Cand kFused[] = {{256, 128, 8}, {128, 128, 4}, {128, 64, 4}, {64, 64, 4}};
+  static const Cand kSync[] = {{256, 128, 4}, {128, 128, 4}, {128, 64, 4}, {64, 64, 4}};
+  static const Cand kGemm[] = {{256, 256, 8}, {256, 128, 4}, {128, 128, 4}, {64, 64, 4}};
+  const Cand* cand = variant == VAR_GEMM ? kGemm : (variant == VAR_SYNC ? kSync : kFused);
   for (int i = 0; i < 4; ++i)
-    if (tiles(M, N, cand[i][0], cand[i][1]) >= 2 * cus) return find_config(variant, 0, cand[i][0], cand[i][1]);
-  return find_config(variant, 0, cand[3][0], cand[3][1]);
+    if (tiles(M, N, cand[i].bm, cand[i].bn) >= 2 * cus)
+      return find_config(variant, 0, cand[i].bm, cand[i].bn, cand[i].waves);
+  return find_config(variant, 0, cand[3].bm, cand[3].bn, cand[3].waves);
 }
 
 int recommend_layout(long long M, long long N, long long K, int cu_count) {
