@@ -79,6 +79,15 @@ bool config_fits(const KernelConfig* c, long long M) {
   return true;
 }
 
+swiglu_status_t launch(const swiglu_ctx* h, const KernelConfig* cfg, int id,
+                       const LaunchArgs& a) {
+  if (h->log)
+    fprintf(stderr, "[swiglu] M=%d N=%d K=%d -> config %d (variant %d family %d %dx%d)\n", a.M,
+            a.N, a.K, id, cfg->variant, cfg->family, cfg->bm, cfg->bn);
+  (void)hipGetLastError();  // clear a stale error so the check below is ours
+  return cfg->launch(a) == hipSuccess ? SWIGLU_OK : SWIGLU_ERR_LAUNCH;
+}
+
 swiglu_status_t run(const swiglu_ctx* h, const KernelConfig* cfg, int id, const void* A,
                     const void* W1, const void* W2, void* Y, int64_t M, int64_t N,
                     int64_t K, hipStream_t stream) {
@@ -89,14 +98,11 @@ swiglu_status_t run(const swiglu_ctx* h, const KernelConfig* cfg, int id, const 
   a.W2 = (const uint16_t*)W2;
   a.Y = (uint16_t*)Y;
   a.M = (int)M, a.N = (int)N, a.K = (int)K;
+  a.ldw = cfg->variant == VAR_INTERLEAVE ? (int)(2 * N) : (int)N;
+  a.ldy = (int)N;
   a.group_m = 0;
   a.stream = stream;
-  if (h->log)
-    fprintf(stderr, "[swiglu] M=%lld N=%lld K=%lld -> config %d (variant %d family %d %dx%d)\n",
-            (long long)M, (long long)N, (long long)K, id, cfg->variant, cfg->family, cfg->bm,
-            cfg->bn);
-  (void)hipGetLastError();  // clear a stale error so the check below is ours
-  return cfg->launch(a) == hipSuccess ? SWIGLU_OK : SWIGLU_ERR_LAUNCH;
+  return launch(h, cfg, id, a);
 }
 
 void fill_tile(int id, swiglu_tile_t* t) {

@@ -15,6 +15,7 @@ struct LaunchArgs {
   const uint16_t* W2;  // W2 (sync) or unused
   uint16_t* Y;         // Y, or G / U for the unfused GEMMs
   int M, N, K;         // N = output columns (Y columns, or G columns)
+  int ldw, ldy;        // row strides (elements) of the weights and of Y
   int group_m;         // tile rows per GROUP_M band (<= 0: default)
   hipStream_t stream;
 };

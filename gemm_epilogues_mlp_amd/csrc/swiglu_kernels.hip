@@ -147,7 +147,10 @@ __global__ __launch_bounds__(64 * WGM * WGN) void tiled_kernel(const uint16_t* _
                                                     const uint16_t* __restrict__ W1,
                                                     const uint16_t* __restrict__ W2,
                                                     uint16_t* __restrict__ Y, int M, int N,
-                                                    int K, int group_m) {
+                                                    int K, int ldw, int ldy, int group_m) {
+  // N: output columns computed here; ldw, ldy: row strides (elements) of the
+  // weights and of Y, so that a launch can cover a column range of a larger
+  // problem (the dispatcher splits N to fill whole rounds of workgroups)
   using C = Tiled<MODE, BM, BNW, BK, STAGES, WGM, WGN>;
   static_assert(C::swizzles_permute_rows(), "LDS swizzle is not a permutation of a row");
   __shared__ __attribute__((aligned(1024))) uint8_t smem[C::LDS_BYTES];
@@ -186,10 +189,11 @@ __global__ __launch_bounds__(64 * WGM * WGN) void tiled_kernel(const uint16_t* _
   // is zero-filled if its row or its k is out of range; a weight chunk if its
   // column is (rows past K lie past the end of the weight buffer, so the
   // buffer bound zero-fills them by itself).
-  const int ldw = (MODE == MODE_INTERLEAVE) ? 2 * N : N;
+  const int wcols = (MODE == MODE_INTERLEAVE) ? 2 * N : N;  // weight columns in range
+  const uint32_t wbytes = K > 0 ? (uint32_t)(((size_t)(K - 1) * ldw + wcols) * 2) : 0u;
   const i32x4 rsA = make_rsrc(A, (uint32_t)((size_t)M * K * 2));
-  const i32x4 rsW1 = make_rsrc(W1, (uint32_t)((size_t)K * ldw * 2));
-  const i32x4 rsW2 = (MODE == MODE_SYNC) ? make_rsrc(W2, (uint32_t)((size_t)K * ldw * 2)) : rsW1;
+  const i32x4 rsW1 = make_rsrc(W1, wbytes);
+  const i32x4 rsW2 = (MODE == MODE_SYNC) ? make_rsrc(W2, wbytes) : rsW1;
   const uint32_t lds0 = lds_addr(smem);
 
   uint32_t a_off[C::A_LOADS];
@@ -208,7 +212,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void tiled_kernel(const uint16_t* _
     const int p = tid + C::kThreads * i;
     const int row = p / C::WCH;
     const int c = (p % C::WCH) ^ C::w_swz(row);
-    w_off[i] = (wc0 + c * 8 < ldw) ? (uint32_t)(row * ldw + wc0 + c * 8) * 2u : kOutOfRange;
+    w_off[i] = (wc0 + c * 8 < wcols) ? (uint32_t)(row * ldw + wc0 + c * 8) * 2u : kOutOfRange;
   }
 
   // DMA instruction q (A chunks first, then W chunks) of K step `it` into
@@ -415,7 +419,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void tiled_kernel(const uint16_t* _
     const int row = p / YCH, cq = p % YCH;
     const int gr = m0 + row, gc = y0 + cq * 8;
     if (gr < M && gc < N)
-      *reinterpret_cast<u32x4*>(Y + (size_t)gr * N + gc) =
+      *reinterpret_cast<u32x4*>(Y + (size_t)gr * ldy + gc) =
           *reinterpret_cast<const u32x4*>(ys + row * C::YLD + cq * 8);
   }
 }
@@ -632,7 +636,7 @@ static hipError_t launch_tiled(const LaunchArgs& a) {
   if (group_m > ntm) group_m = ntm;
   hipLaunchKernelGGL((tiled_kernel<MODE, BM, BNW, BK, STAGES, WGM, WGN>), dim3((unsigned)nwg),
                      dim3(C::kThreads), 0, a.stream, a.A, a.W1, a.W2, a.Y, a.M, a.N, a.K,
-                     group_m);
+                     a.ldw, a.ldy, group_m);
   return hipGetLastError();
 }
 

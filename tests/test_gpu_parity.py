@@ -126,3 +126,4 @@ def test_k_zero_writes_zeros(handle):
         sw.swiglu_forward(handle, 0, 0, w2, y, M, N, 0, layout)
         t.cuda.synchronize()
         assert np.all(decode(host(y)) == 0.0)
+
