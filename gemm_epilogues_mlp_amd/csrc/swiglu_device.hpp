@@ -34,6 +34,14 @@ __device__ __forceinline__ u32x4 load16(const void* p) {
 __device__ __forceinline__ u32x2 load8(const void* p) {
   return *reinterpret_cast<const u32x2*>(p);
 }
+// Streaming loads of data that is read exactly once (weights at decode-sized
+// batches): the nontemporal hint keeps them from displacing reusable lines.
+__device__ __forceinline__ u32x4 load16_stream(const void* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+}
+__device__ __forceinline__ u32x2 load8_stream(const void* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p));
+}
 
 // ---- direct HBM -> LDS loads ------------------------------------------------
 typedef int32_t i32x4 __attribute__((ext_vector_type(4)));

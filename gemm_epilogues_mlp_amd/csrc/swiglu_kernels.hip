@@ -459,8 +459,11 @@ __device__ __forceinline__ void skinny_load(const uint16_t* __restrict__ A,
     const uint16_t* p2 = W2 + (size_t)k * N + c;
 #pragma unroll
     for (int r = 0; r < 8; ++r) {
-      u32x2 g = ok ? load8(p1 + (size_t)r * N) : u32x2{0, 0};
-      u32x2 u = ok ? load8(p2 + (size_t)r * N) : u32x2{0, 0};
+      // MT == 1 is chosen for M <= 16: one row group, each weight read once
+      u32x2 g = ok ? (MT == 1 ? load8_stream(p1 + (size_t)r * N) : load8(p1 + (size_t)r * N))
+                   : u32x2{0, 0};
+      u32x2 u = ok ? (MT == 1 ? load8_stream(p2 + (size_t)r * N) : load8(p2 + (size_t)r * N))
+                   : u32x2{0, 0};
       rows[r] = u32x4{g[0], g[1], u[0], u[1]};
     }
   } else {
@@ -469,7 +472,9 @@ __device__ __forceinline__ void skinny_load(const uint16_t* __restrict__ A,
     const bool ok = kin && c < ld;
     const uint16_t* p = W1 + (size_t)k * ld + c;
 #pragma unroll
-    for (int r = 0; r < 8; ++r) rows[r] = ok ? load16(p + (size_t)r * ld) : u32x4{0, 0, 0, 0};
+    for (int r = 0; r < 8; ++r)
+      rows[r] = ok ? (MT == 1 ? load16_stream(p + (size_t)r * ld) : load16(p + (size_t)r * ld))
+                   : u32x4{0, 0, 0, 0};
   }
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {

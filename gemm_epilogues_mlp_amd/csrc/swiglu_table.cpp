@@ -34,9 +34,9 @@ const ShapeEntry kTable[] = {
     {VAR_SYNC, 2048, 8960, 1536, 8},
     {VAR_GEMM, 2048, 8960, 1536, 33},
     // Qwen2.5-7B MLP, decode M=16 and prefill M=8192
-    {VAR_INTERLEAVE, 16, 18944, 3584, 3},
+    {VAR_INTERLEAVE, 16, 18944, 3584, 23},
     {VAR_SYNC, 16, 18944, 3584, 12},
-    {VAR_GEMM, 16, 18944, 3584, 26},
+    {VAR_GEMM, 16, 18944, 3584, 18},
     {VAR_INTERLEAVE, 8192, 18944, 3584, 31},
     {VAR_SYNC, 8192, 18944, 3584, 7},
     {VAR_GEMM, 8192, 18944, 3584, 33},
