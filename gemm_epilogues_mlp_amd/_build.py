@@ -43,8 +43,9 @@ def build(save_temps: str | None = None, verbose: bool = False) -> str:
         extra = ["-x", "hip"] if src.endswith(".hip") else ["-x", "hip"]
         cmd = [cc, *flags(extra), "-c", os.path.join(CSRC, src), "-o", obj]
         if save_temps:
+            # keep the device assembly (.s) and IR next to each other in save_temps
             os.makedirs(save_temps, exist_ok=True)
-            cmd.insert(1, f"-save-temps={save_temps}") if False else None
+            cmd.insert(1, "-save-temps")
         if verbose:
             print(" ".join(cmd), flush=True)
         subprocess.run(cmd, check=True, cwd=save_temps or PKG)

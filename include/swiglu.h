@@ -89,7 +89,9 @@ typedef struct swiglu_tile {
   int32_t id;          /* index in [0, swiglu_config_count())                */
   int32_t variant;     /* swiglu_variant_t: SYNC, INTERLEAVE or GEMM          */
   int32_t family;      /* 0 = LDS-tiled MFMA 32x32x16, 1 = split-K streaming
-                          MFMA 16x16x32 (weights straight to registers)       */
+                          MFMA 16x16x32 (weights straight to registers),
+                          2 = LDS-tiled with two wave groups alternating
+                          MFMA and memory phases (ping-pong)                  */
   int32_t bm;          /* output rows per workgroup                           */
   int32_t bn;          /* output (Y or G) columns per workgroup               */
   int32_t bk;          /* K depth of one pipeline stage                       */

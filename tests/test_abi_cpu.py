@@ -79,10 +79,10 @@ def test_config_list_is_consistent():
         assert c["id"] == i
         assert c["variant"] in seen
         seen[c["variant"]] += 1
-        assert c["family"] in (0, 1)
+        assert c["family"] in (0, 1, 2)
         assert 0 < c["lds_bytes"] <= 160 * 1024
         assert c["waves"] * 64 <= 1024
-        if c["family"] == 0:
+        if c["family"] in (0, 2):
             assert c["bm"] % 32 == 0 and c["bn"] % 32 == 0
     assert all(v > 0 for v in seen.values())
 
