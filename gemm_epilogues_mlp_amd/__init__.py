@@ -41,7 +41,8 @@ class SwiGLUError(RuntimeError):
 
 class Tile(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in
-                ("id", "variant", "family", "bm", "bn", "bk", "waves", "split_k", "lds_bytes")]
+                ("id", "variant", "family", "bm", "bn", "bk", "waves", "split_k", "lds_bytes",
+                 "tail_split")]
 
     def as_dict(self):
         return {n: getattr(self, n) for n, _ in self._fields_}

@@ -101,6 +101,7 @@ swiglu_status_t run(const swiglu_ctx* h, const KernelConfig* cfg, int id, const 
   a.ldw = cfg->variant == VAR_INTERLEAVE ? (int)(2 * N) : (int)N;
   a.ldy = (int)N;
   a.group_m = 0;
+  a.cu_count = h->cu_count;
   a.stream = stream;
   return launch(h, cfg, id, a);
 }
@@ -116,6 +117,7 @@ void fill_tile(int id, swiglu_tile_t* t) {
   t->waves = c->waves;
   t->split_k = c->split_k;
   t->lds_bytes = c->lds_bytes;
+  t->tail_split = c->tail_split;
 }
 
 }  // namespace

@@ -17,6 +17,7 @@ struct LaunchArgs {
   int M, N, K;         // N = output columns (Y columns, or G columns)
   int ldw, ldy;        // row strides (elements) of the weights and of Y
   int group_m;         // tile rows per GROUP_M band (<= 0: default)
+  int cu_count;        // compute units of the device (workgroups per round)
   hipStream_t stream;
 };
 
@@ -27,6 +28,7 @@ struct KernelConfig {
   int family;   // 0 tiled, 1 skinny
   int bm, bn, bk, waves, split_k, lds_bytes;
   LaunchFn launch;
+  int tail_split;  // 0, or 4: big tiles of a partial last round run as quarter tiles
 };
 
 int config_count();

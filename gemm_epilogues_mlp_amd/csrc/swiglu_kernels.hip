@@ -142,35 +142,34 @@ struct Tiled {
 };
 
 
+// Position of tile t in the launch order: GROUP_M bands of tile rows, and
+// within a band column-major, so that the workgroups running together share
+// weight columns and rows of A.
+__device__ __forceinline__ void tile_of(int t, int ntm, int ntn, int group_m, int& tm, int& tn) {
+  const int per_group = group_m * ntn;
+  const int first_m = t / per_group * group_m;
+  const int gsz = min(ntm - first_m, group_m);
+  tm = first_m + (t % per_group) % gsz;
+  tn = (t % per_group) / gsz;
+}
+
+// One output tile: rows [m0, m0 + BM) of A against weight columns
+// [tn BNW, (tn + 1) BNW), i.e. output columns [tn BNY, (tn + 1) BNY).
+// N: output columns of the problem; ldw, ldy: row strides (elements) of the
+// weights and of Y.  smem: the workgroup's LDS (at least C::LDS_BYTES).
 template <int MODE, int BM, int BNW, int BK, int STAGES, int WGM, int WGN>
-__global__ __launch_bounds__(64 * WGM * WGN) void tiled_kernel(const uint16_t* __restrict__ A,
-                                                    const uint16_t* __restrict__ W1,
-                                                    const uint16_t* __restrict__ W2,
-                                                    uint16_t* __restrict__ Y, int M, int N,
-                                                    int K, int ldw, int ldy, int group_m) {
-  // N: output columns computed here; ldw, ldy: row strides (elements) of the
-  // weights and of Y, so that a launch can cover a column range of a larger
-  // problem (the dispatcher splits N to fill whole rounds of workgroups)
+__device__ __forceinline__ void tiled_tile(const uint16_t* __restrict__ A,
+                                           const uint16_t* __restrict__ W1,
+                                           const uint16_t* __restrict__ W2,
+                                           uint16_t* __restrict__ Y, int M, int N, int K,
+                                           int ldw, int ldy, int m0, int tn, uint8_t* smem) {
   using C = Tiled<MODE, BM, BNW, BK, STAGES, WGM, WGN>;
   static_assert(C::swizzles_permute_rows(), "LDS swizzle is not a permutation of a row");
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[C::LDS_BYTES];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int wm = wave / WGN, wn = wave % WGN;
-
-  // ---- tile id: XCD-contiguous ranges, then GROUP_M-major order -------------
-  const int ntm = (M + BM - 1) / BM;
-  const int ntn = (N + C::BNY - 1) / C::BNY;
-  const int t = xcd_remap(blockIdx.x, gridDim.x);
-  const int per_group = group_m * ntn;
-  const int grp = t / per_group;
-  const int first_m = grp * group_m;
-  const int gsz = min(ntm - first_m, group_m);
-  const int tm = first_m + (t % per_group) % gsz;
-  const int tn = (t % per_group) / gsz;
-  const int m0 = tm * BM;
   const int wc0 = tn * BNW;  // first weight column (W_fused, W1/W2 or W)
   const int y0 = tn * C::BNY;
 
@@ -424,6 +423,59 @@ __global__ __launch_bounds__(64 * WGM * WGN) void tiled_kernel(const uint16_t* _
   }
 }
 
+template <int MODE, int BM, int BNW, int BK, int STAGES, int WGM, int WGN>
+__global__ __launch_bounds__(64 * WGM * WGN) void tiled_kernel(const uint16_t* __restrict__ A,
+                                                    const uint16_t* __restrict__ W1,
+                                                    const uint16_t* __restrict__ W2,
+                                                    uint16_t* __restrict__ Y, int M, int N,
+                                                    int K, int ldw, int ldy, int group_m) {
+  using C = Tiled<MODE, BM, BNW, BK, STAGES, WGM, WGN>;
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[C::LDS_BYTES];
+  // workgroups of one XCD (8 per chip, each with its own L2) take a
+  // contiguous range of the tile order
+  const int ntm = (M + BM - 1) / BM;
+  const int ntn = (N + C::BNY - 1) / C::BNY;
+  int tm, tn;
+  tile_of(xcd_remap(blockIdx.x, gridDim.x), ntm, ntn, group_m, tm, tn);
+  tiled_tile<MODE, BM, BNW, BK, STAGES, WGM, WGN>(A, W1, W2, Y, M, N, K, ldw, ldy, tm * BM, tn,
+                                                  smem);
+}
+
+// Same tiles, with a split tail: when the tiles do not fill whole rounds of
+// workgroups (one per CU), the big tiles of the last, partial round are each
+// computed as four quarter tiles (BM/2 x BNW/2) by four workgroups, which
+// spreads that round over four times as many CUs.  Workgroups [0, n_big)
+// take big tiles 0 .. n_big-1 of the tile order; workgroup n_big + u takes
+// quarter u % 4 of big tile n_big + u / 4.  Both tile kinds run on the same
+// eight waves (SWGM x SWGN for the quarter tiles).
+template <int MODE, int BM, int BNW, int BK, int STAGES, int WGM, int WGN, int SWGM, int SWGN>
+__global__ __launch_bounds__(64 * WGM * WGN) void tiled_split_kernel(
+    const uint16_t* __restrict__ A, const uint16_t* __restrict__ W1,
+    const uint16_t* __restrict__ W2, uint16_t* __restrict__ Y, int M, int N, int K, int ldw,
+    int ldy, int group_m, int n_big) {
+  using Big = Tiled<MODE, BM, BNW, BK, STAGES, WGM, WGN>;
+  using Small = Tiled<MODE, BM / 2, BNW / 2, BK, STAGES, SWGM, SWGN>;
+  static_assert(Big::kThreads == Small::kThreads, "one workgroup size for both tile kinds");
+  constexpr int LDS = Big::LDS_BYTES > Small::LDS_BYTES ? Big::LDS_BYTES : Small::LDS_BYTES;
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[LDS];
+  const int ntm = (M + BM - 1) / BM;
+  const int ntn = (N + Big::BNY - 1) / Big::BNY;
+  int tm, tn;
+  if ((int)blockIdx.x < n_big) {
+    tile_of(xcd_remap(blockIdx.x, n_big), ntm, ntn, group_m, tm, tn);
+    tiled_tile<MODE, BM, BNW, BK, STAGES, WGM, WGN>(A, W1, W2, Y, M, N, K, ldw, ldy, tm * BM,
+                                                    tn, smem);
+  } else {
+    const int u = blockIdx.x - n_big, q = u & 3;
+    tile_of(n_big + u / 4, ntm, ntn, group_m, tm, tn);
+    const int m0 = tm * BM + (q >> 1) * (BM / 2);
+    const int tq = 2 * tn + (q & 1);  // column tile in quarter-tile units
+    if (m0 >= M || tq * Small::BNY >= N) return;  // quarter past a ragged edge
+    tiled_tile<MODE, BM / 2, BNW / 2, BK, STAGES, SWGM, SWGN>(A, W1, W2, Y, M, N, K, ldw, ldy,
+                                                              m0, tq, smem);
+  }
+}
+
 // ============================================================================
 // LDS-tiled MFMA kernel, ping-pong schedule
 // ============================================================================
@@ -489,12 +541,8 @@ __global__ __launch_bounds__(512) void pingpong_kernel(const uint16_t* __restric
   // ---- tile id (as tiled_kernel) ---------------------------------------------
   const int ntm = (M + BM - 1) / BM;
   const int ntn = (N + C::BNY - 1) / C::BNY;
-  const int t = xcd_remap(blockIdx.x, gridDim.x);
-  const int per_group = group_m * ntn;
-  const int first_m = t / per_group * group_m;
-  const int gsz = min(ntm - first_m, group_m);
-  const int tm = first_m + (t % per_group) % gsz;
-  const int tn = (t % per_group) / gsz;
+  int tm, tn;
+  tile_of(xcd_remap(blockIdx.x, gridDim.x), ntm, ntn, group_m, tm, tn);
   const int m0 = tm * BM;
   const int wc0 = tn * BNW;
   const int y0 = tn * C::BNY;
@@ -904,6 +952,27 @@ static hipError_t launch_tiled(const LaunchArgs& a) {
   return hipGetLastError();
 }
 
+// Split-tail launch: whole rounds of big tiles plus, when the last round is at
+// most a quarter full, its tiles as quarter tiles; otherwise the plain kernel.
+template <int MODE, int BM, int BNW, int BK, int STAGES, int WGM, int WGN, int SWGM, int SWGN>
+static hipError_t launch_tiled_split(const LaunchArgs& a) {
+  using C = Tiled<MODE, BM, BNW, BK, STAGES, WGM, WGN>;
+  const int ntm = (a.M + BM - 1) / BM, ntn = (a.N + C::BNY - 1) / C::BNY;
+  const long long nt = (long long)ntm * ntn;
+  if (nt <= 0) return hipSuccess;
+  if (4 * nt > 0x7fffffffLL) return hipErrorInvalidValue;
+  const long long slots = a.cu_count > 0 ? a.cu_count : 256;  // one big workgroup per CU
+  const long long n_big = nt / slots * slots, tail = nt - n_big;
+  if (tail == 0 || 4 * tail > slots)
+    return launch_tiled<MODE, BM, BNW, BK, STAGES, WGM, WGN>(a);
+  int group_m = a.group_m > 0 ? a.group_m : 8;
+  if (group_m > ntm) group_m = ntm;
+  hipLaunchKernelGGL((tiled_split_kernel<MODE, BM, BNW, BK, STAGES, WGM, WGN, SWGM, SWGN>),
+                     dim3((unsigned)(n_big + 4 * tail)), dim3(C::kThreads), 0, a.stream, a.A,
+                     a.W1, a.W2, a.Y, a.M, a.N, a.K, a.ldw, a.ldy, group_m, (int)n_big);
+  return hipGetLastError();
+}
+
 template <int MODE>
 static hipError_t launch_pingpong(const LaunchArgs& a) {
   using P = PingPong<MODE>;
@@ -933,6 +1002,10 @@ static hipError_t launch_skinny(const LaunchArgs& a) {
 #define TILED(mode, v, bm, bnw, bk, st, wgm, wgn)                                          \
   {v, 0, bm, Tiled<mode, bm, bnw, bk, st, wgm, wgn>::BNY, bk, (wgm) * (wgn), 1,             \
    Tiled<mode, bm, bnw, bk, st, wgm, wgn>::LDS_BYTES, &launch_tiled<mode, bm, bnw, bk, st, wgm, wgn>}
+#define TILED_SPLIT(mode, v, bm, bnw, bk, st, wgm, wgn, swgm, swgn)                          \
+  {v, 0, bm, Tiled<mode, bm, bnw, bk, st, wgm, wgn>::BNY, bk, (wgm) * (wgn), 1,             \
+   Tiled<mode, bm, bnw, bk, st, wgm, wgn>::LDS_BYTES,                                       \
+   &launch_tiled_split<mode, bm, bnw, bk, st, wgm, wgn, swgm, swgn>, 4}
 #define PINGPONG(mode, v) \
   {v, 2, 256, PingPong<mode>::BNY, 32, 8, 1, PingPong<mode>::LDS_BYTES, &launch_pingpong<mode>}
 #define SKINNY(mode, v, mt, nw)                                                            \
@@ -989,6 +1062,10 @@ static const KernelConfig kConfigs[] = {
     // ---- eight waves as 4 x 2 (64-row wave tiles) for the other modes -----
     TILED(MODE_GEMM, VAR_GEMM, 256, 256, 32, 4, 4, 2),              // 38
     TILED(MODE_SYNC, VAR_SYNC, 256, 128, 32, 4, 4, 2),              // 39
+    // ---- 256 x 256 tiles whose partial last round runs as quarter tiles ----
+    TILED_SPLIT(MODE_INTERLEAVE, VAR_INTERLEAVE, 256, 256, 32, 4, 4, 2, 2, 4),  // 40
+    TILED_SPLIT(MODE_GEMM, VAR_GEMM, 256, 256, 32, 4, 4, 2, 2, 4),              // 41
+    TILED_SPLIT(MODE_SYNC, VAR_SYNC, 256, 128, 32, 4, 4, 2, 4, 2),              // 42
 };
 
 int config_count() { return (int)(sizeof(kConfigs) / sizeof(kConfigs[0])); }

@@ -30,20 +30,20 @@ const ShapeEntry kTable[] = {
     {VAR_SYNC, 128, 4864, 896, 29},
     {VAR_GEMM, 128, 4864, 896, 30},
     // Qwen2.5-1.5B MLP, M=2048
-    {VAR_INTERLEAVE, 2048, 8960, 1536, 32},
-    {VAR_SYNC, 2048, 8960, 1536, 8},
-    {VAR_GEMM, 2048, 8960, 1536, 33},
+    {VAR_INTERLEAVE, 2048, 8960, 1536, 40},
+    {VAR_SYNC, 2048, 8960, 1536, 42},
+    {VAR_GEMM, 2048, 8960, 1536, 41},
     // Qwen2.5-7B MLP, decode M=16 and prefill M=8192
     {VAR_INTERLEAVE, 16, 18944, 3584, 23},
     {VAR_SYNC, 16, 18944, 3584, 12},
     {VAR_GEMM, 16, 18944, 3584, 18},
-    {VAR_INTERLEAVE, 8192, 18944, 3584, 32},
-    {VAR_SYNC, 8192, 18944, 3584, 39},
-    {VAR_GEMM, 8192, 18944, 3584, 38},
+    {VAR_INTERLEAVE, 8192, 18944, 3584, 40},
+    {VAR_SYNC, 8192, 18944, 3584, 42},
+    {VAR_GEMM, 8192, 18944, 3584, 41},
     // Qwen2.5-72B MLP, M=4096
-    {VAR_INTERLEAVE, 4096, 29568, 8192, 32},
-    {VAR_SYNC, 4096, 29568, 8192, 39},
-    {VAR_GEMM, 4096, 29568, 8192, 38},
+    {VAR_INTERLEAVE, 4096, 29568, 8192, 40},
+    {VAR_SYNC, 4096, 29568, 8192, 42},
+    {VAR_GEMM, 4096, 29568, 8192, 41},
 };
 
 int find_config(int variant, int family, int bm, int bn, int waves) {
@@ -73,12 +73,13 @@ int select_config(int variant, long long M, long long N, long long K, int cu_cou
     return find_config(variant, 1, mt * 16, variant == VAR_GEMM ? 128 : 64, 0);
   }
   // LDS-tiled: the largest tile that still gives two workgroups per CU.  The
-  // 256-row tiles run eight waves (two per SIMD: 4x2 waves for the fused
-  // kernel, which measured faster than 2x4 at every large shape), the smaller
-  // ones four.  Candidates are config ids, largest tile first.
-  static const int kFused[] = {32, 1, 2, 3};   // 256x128 (8 waves), 128x128, 128x64, 64x64
-  static const int kSync[] = {7, 8, 9, 10};    // 256x128, 128x128, 128x64, 64x64
-  static const int kGemm[] = {33, 15, 16, 17}; // 256x256 (8 waves), 256x128, 128x128, 64x64
+  // 256-row tiles run eight waves (two per SIMD, as 4x2, which measured faster
+  // than 2x4 at every large shape) and split a short last round into quarter
+  // tiles; the smaller ones run four waves.  Candidates are config ids,
+  // largest tile first.
+  static const int kFused[] = {40, 1, 2, 3};   // 256x128 (8 waves, split tail), 128x128, 128x64, 64x64
+  static const int kSync[] = {42, 8, 9, 10};   // 256x128 (8 waves, split tail), 128x128, 128x64, 64x64
+  static const int kGemm[] = {41, 15, 16, 17}; // 256x256 (8 waves, split tail), 256x128, 128x128, 64x64
   const int* cand = variant == VAR_GEMM ? kGemm : (variant == VAR_SYNC ? kSync : kFused);
   for (int i = 0; i < 4; ++i) {
     const KernelConfig* c = config_at(cand[i]);

@@ -98,6 +98,9 @@ typedef struct swiglu_tile {
   int32_t waves;       /* waves (64 lanes) per workgroup                      */
   int32_t split_k;     /* waves of one workgroup that split K (1 = none)      */
   int32_t lds_bytes;   /* LDS per workgroup                                   */
+  int32_t tail_split;  /* 0, or 4: when the tiles leave a last round of
+                          workgroups at most a quarter full, each of its tiles
+                          runs as four (bm/2 x bn/2) tiles in the same launch */
 } swiglu_tile_t;
 
 /* Create a handle for HIP device `device`.  Checks that the device exists and

@@ -80,6 +80,9 @@ def test_config_list_is_consistent():
         assert c["variant"] in seen
         seen[c["variant"]] += 1
         assert c["family"] in (0, 1, 2)
+        assert c["tail_split"] in (0, 4)
+        if c["tail_split"]:
+            assert c["family"] == 0 and c["bm"] % 64 == 0 and c["bn"] % 64 == 0
         assert 0 < c["lds_bytes"] <= 160 * 1024
         assert c["waves"] * 64 <= 1024
         if c["family"] in (0, 2):

@@ -91,6 +91,43 @@ def test_unfused_config_parity(handle, cases, cfg, shape):
     assert_parity(y, y_ref, f"unfused Y cfg {cfg} {shape}")
 
 
+def _split_configs():
+    return [i for i in range(sw.swiglu_config_count()) if sw.swiglu_config_info(i)["tail_split"]]
+
+
+@pytest.mark.parametrize("cfg", _split_configs())
+def test_split_tail_parity(handle, cfg):
+    """A launch whose tiles fill whole rounds of workgroups (one per CU) plus a
+    short last round, which the split-tail configs run as quarter tiles: both
+    tile kinds, their boundary in the tile order, and ragged edges in M, N, K."""
+    t = __import__("torch")
+    info = sw.swiglu_config_info(cfg)
+    cus = t.cuda.get_device_properties(0).multi_processor_count
+    bm, bn = info["bm"], info["bn"]
+    K = 72
+    M = 8 * bm - 40                       # 8 tile rows, the last one ragged
+    ntn = cus // 8 + 1                    # 8 * ntn tiles: whole rounds plus 8
+    N = ntn * bn - 8                      # last tile column ragged
+    nt = 8 * ntn
+    n_big, tail = nt // cus * cus, nt % cus
+    assert n_big > 0 and 0 < 4 * tail <= cus, "shape must exercise both tile kinds"
+    a, w1, w2 = _inputs(M, N, K, 777)
+    log(f"split-tail config {cfg} {info} shape {(M, N, K)} big {n_big} tail {tail}")
+    if info["variant"] == sw.VARIANT_GEMM:
+        y, g, u = Run(handle).unfused(dev(a), dev(w1), dev(w2), M, N, K, cfg)
+        g_ref = oracle.swiglu_rows(a, w1, w2, with_gate_up=True)[1]
+        assert_parity(host(g), g_ref, f"split-tail G cfg {cfg}")
+    elif info["variant"] == sw.VARIANT_SYNC:
+        y = Run(handle).fused(dev(a), dev(w1), dev(w2), M, N, K, sw.LAYOUT_SEPARATE, cfg,
+                              sw.VARIANT_SYNC)
+        assert_parity(host(y), oracle.swiglu_rows(a, w1, w2), f"split-tail cfg {cfg}")
+    else:
+        wf = I.interleave_columns(w1, w2)
+        y = Run(handle).fused(dev(a), dev(wf), None, M, N, K, sw.LAYOUT_INTERLEAVED, cfg,
+                              sw.VARIANT_INTERLEAVE)
+        assert_parity(host(y), oracle.swiglu_rows(a, w1, w2), f"split-tail cfg {cfg}")
+
+
 @pytest.mark.parametrize("layout", [sw.LAYOUT_SEPARATE, sw.LAYOUT_INTERLEAVED])
 @pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "x".join(map(str, s)))
 def test_auto_selection_parity(handle, cases, shape, layout):
