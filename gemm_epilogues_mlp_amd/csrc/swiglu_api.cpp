@@ -24,6 +24,7 @@ namespace {
 using namespace swiglu;
 
 constexpr long long kMaxDim = 0x7fffffffLL;
+constexpr long long kMaxBytes = 1LL << 31;  // each tensor must be smaller
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
@@ -67,6 +68,10 @@ swiglu_status_t check_forward(const swiglu_ctx* h, const void* A, const void* W1
   const long long ybytes = 2LL * M * N;
   const long long abytes = 2LL * M * K;
   const long long wbytes = (layout == SWIGLU_LAYOUT_INTERLEAVED ? 4LL : 2LL) * K * N;
+  // the kernels address A and the weights with 32-bit byte offsets, and use
+  // offset 2^31 as "past every tensor"
+  if (ybytes >= kMaxBytes || abytes >= kMaxBytes || wbytes >= kMaxBytes)
+    return SWIGLU_ERR_UNSUPPORTED;
   if (K > 0 && (overlaps(Y, ybytes, A, abytes) || overlaps(Y, ybytes, W1, wbytes) ||
                 (layout == SWIGLU_LAYOUT_SEPARATE && overlaps(Y, ybytes, W2, wbytes))))
     return SWIGLU_ERR_INVALID_ARG;
@@ -228,6 +233,7 @@ swiglu_status_t swiglu_pack_interleaved(swiglu_handle_t h, const void* W1, const
   if (!h || K < 0 || N < 0) return SWIGLU_ERR_INVALID_ARG;
   if (K == 0 || N == 0) return SWIGLU_OK;
   if (!W1 || !W2 || !W_fused) return SWIGLU_ERR_INVALID_ARG;
+  if (K > kMaxDim || N > (kMaxDim >> 1)) return SWIGLU_ERR_UNSUPPORTED;
   if (N % 8 != 0) return SWIGLU_ERR_UNSUPPORTED;
   if (!aligned16(W1) || !aligned16(W2) || !aligned16(W_fused)) return SWIGLU_ERR_UNSUPPORTED;
   const long long wb = 2LL * K * N;

@@ -106,6 +106,27 @@ def test_unsupported_shapes_and_alignment(env):
     assert np.all(host(e["y"]) == 0xFFFF)
 
 
+def test_tensors_of_2gib_are_rejected(env):
+    """Each tensor must stay below 2 GiB (32-bit byte offsets in the kernels):
+    a shape over the limit is refused before anything is launched, so the
+    small buffers passed here are never touched."""
+    e = env
+    h = e["h"]
+    S, IL = sw.LAYOUT_SEPARATE, sw.LAYOUT_INTERLEAVED
+    f = sw.swiglu_forward
+    big_m = 1 << 20                                  # A = 2 * 2^20 * 1024 B = 2 GiB
+    assert _status(f, h, e["a"], e["w1"], e["w2"], e["y"], big_m, 8, 1024, S) == \
+        sw.ERR_UNSUPPORTED
+    assert _status(f, h, e["a"], e["w1"], e["w2"], e["y"], 8, 1 << 20, 1024, S) == \
+        sw.ERR_UNSUPPORTED                          # W1 = 2 GiB
+    assert _status(f, h, e["a"], e["wf"], None, e["y"], 8, 1 << 19, 1024, IL) == \
+        sw.ERR_UNSUPPORTED                          # W_fused = 4 * 2^19 * 1024 B = 2 GiB
+    assert _status(f, h, e["a"], e["w1"], e["w2"], e["y"], 1 << 20, 1024, 8, S) == \
+        sw.ERR_UNSUPPORTED                          # Y = 2 GiB
+    e["torch"].cuda.synchronize()
+    assert np.all(host(e["y"]) == 0xFFFF), "a rejected call wrote Y"
+
+
 def test_empty_is_noop(env):
     e = env
     h = e["h"]
