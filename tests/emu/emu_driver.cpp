@@ -1,0 +1,167 @@
+// CPU bounds emulation of every kernel configuration: the kernel source is
+// compiled for the host against a stand-in device header (swiglu_device.hpp
+// in this directory), each workgroup's threads are run one after another
+// through the real launch functions, and every LDS offset, DMA source and
+// direct global load is checked against the buffers actually allocated (the
+// build adds AddressSanitizer for the plain pointer accesses: LDS staging,
+// global stores).  Barriers are no-ops, so the data is not meaningful; only
+// where each access goes is checked.
+//
+// usage: emu_driver [cfg ...]          all shapes for the listed configs (default: all)
+//        emu_driver --shape M N K cfg  one shape
+#include <stdio.h>
+#include <stdlib.h>
+
+#include <string>
+#include <vector>
+
+#include "swiglu_kernels_emu.cpp"
+
+dim3 threadIdx, blockIdx, gridDim, blockDim;
+
+namespace {
+struct Alloc {
+  const uint8_t* p;
+  size_t n;
+  const char* name;
+};
+std::vector<Alloc> g_allocs;
+uint8_t* g_lds = nullptr;
+size_t g_lds_size = 0;
+long g_errors = 0;
+long g_lds_checks = 0, g_global_checks = 0, g_threads = 0;
+std::string g_ctx;
+
+void report(const char* what, const void* p, size_t n) {
+  if (g_errors < 20)
+    fprintf(stderr, "OUT OF BOUNDS: %s (%zu bytes at %p) in %s, block (%u,%u) thread %u\n", what,
+            n, p, g_ctx.c_str(), blockIdx.x, blockIdx.y, threadIdx.x);
+  ++g_errors;
+}
+}  // namespace
+
+uint8_t* emu_lds(size_t bytes) {
+  if (bytes != g_lds_size || !g_lds) {
+    free(g_lds);
+    g_lds = (uint8_t*)malloc(bytes ? bytes : 1);
+    memset(g_lds, 0, bytes);
+    g_lds_size = bytes;
+  }
+  return g_lds;
+}
+uint8_t* emu_lds_base() { return g_lds; }
+void emu_barrier() {}
+void emu_check_lds(uint32_t off, size_t n, const char* what) {
+  ++g_lds_checks;
+  if (!g_lds || (size_t)off + n > g_lds_size) report(what, g_lds ? g_lds + off : nullptr, n);
+}
+void emu_check_global(const void* p, size_t n, const char* what) {
+  ++g_global_checks;
+  const uint8_t* b = (const uint8_t*)p;
+  if (b)
+    for (const Alloc& a : g_allocs)
+      if (b >= a.p && b + n <= a.p + a.n) return;
+  report(what, p, n);
+}
+
+namespace {
+uint16_t* alloc16(size_t elems, const char* name) {
+  const size_t n = elems * 2;
+  uint16_t* p = (uint16_t*)malloc(n ? n : 1);
+  memset(p, 0, n);
+  g_allocs.push_back({(const uint8_t*)p, n, name});
+  return p;
+}
+void free_all() {
+  for (const Alloc& a : g_allocs) free((void*)a.p);
+  g_allocs.clear();
+}
+
+// one configuration on one shape, through the same LaunchArgs the C ABI builds
+bool run_config(int id, int M, int N, int K) {
+  using namespace swiglu;
+  const KernelConfig* c = config_at(id);
+  if (!c) return false;
+  char buf[160];
+  snprintf(buf, sizeof buf, "config %d (variant %d family %d %dx%d) shape M=%d N=%d K=%d", id,
+           c->variant, c->family, c->bm, c->bn, M, N, K);
+  g_ctx = buf;
+  const long before = g_errors;
+  const long l0 = g_lds_checks, g0 = g_global_checks;
+  LaunchArgs a{};
+  a.M = M, a.N = N, a.K = K;
+  a.A = alloc16((size_t)M * K, "A");
+  if (c->variant == VAR_INTERLEAVE) {
+    a.W1 = alloc16((size_t)K * 2 * N, "W_fused");
+    a.W2 = nullptr;
+    a.ldw = 2 * N;
+  } else if (c->variant == VAR_SYNC) {
+    a.W1 = alloc16((size_t)K * N, "W1");
+    a.W2 = alloc16((size_t)K * N, "W2");
+    a.ldw = N;
+  } else {
+    a.W1 = alloc16((size_t)K * N, "W");
+    a.W2 = nullptr;
+    a.ldw = N;
+  }
+  a.Y = alloc16((size_t)M * N, "Y");
+  a.ldy = N;
+  a.group_m = 0;
+  a.cu_count = 256;
+  a.stream = nullptr;
+  const hipError_t e = c->launch(a);
+  free_all();
+  if (e != hipSuccess) fprintf(stderr, "launch refused: %s\n", g_ctx.c_str());
+  printf("%s: %s (%ld LDS accesses, %ld global reads checked)\n", g_ctx.c_str(),
+         g_errors == before ? "ok" : "OUT OF BOUNDS", g_lds_checks - l0, g_global_checks - g0);
+  return g_errors == before;
+}
+
+bool run_elementwise(size_t n) {
+  using namespace swiglu;
+  g_ctx = "gate/pack n=" + std::to_string(n);
+  const long before = g_errors;
+  uint16_t* g = alloc16(n, "G");
+  uint16_t* u = alloc16(n, "U");
+  uint16_t* y = alloc16(n, "Y");
+  launch_gate(g, u, y, n, nullptr, 256);
+  uint16_t* wf = alloc16(2 * n, "WF");
+  launch_pack(g, u, wf, n, nullptr, 256);
+  free_all();
+  printf("%s: %s\n", g_ctx.c_str(), g_errors == before ? "ok" : "OUT OF BOUNDS");
+  return g_errors == before;
+}
+}  // namespace
+
+int main(int argc, char** argv) {
+  using namespace swiglu;
+  std::vector<int> ids;
+  int shape[3] = {0, 0, 0};
+  bool one_shape = false;
+  for (int i = 1; i < argc; ++i) {
+    if (std::string(argv[i]) == "--shape" && i + 3 < argc) {
+      shape[0] = atoi(argv[i + 1]), shape[1] = atoi(argv[i + 2]), shape[2] = atoi(argv[i + 3]);
+      one_shape = true;
+      i += 3;
+    } else {
+      ids.push_back(atoi(argv[i]));
+    }
+  }
+  if (ids.empty())
+    for (int i = 0; i < config_count(); ++i) ids.push_back(i);
+  // the GPU parity shapes (ragged tails in every dimension) and K = 0
+  const int shapes[][3] = {{300, 264, 200}, {37, 136, 520}, {1, 8, 8}, {129, 520, 96}, {40, 72, 0}};
+  for (int id : ids) {
+    if (one_shape) {
+      run_config(id, shape[0], shape[1], shape[2]);
+    } else {
+      for (const auto& s : shapes) run_config(id, s[0], s[1], s[2]);
+    }
+  }
+  if (!one_shape) {
+    run_elementwise(8);
+    run_elementwise(200 * 264);
+  }
+  printf("errors: %ld\n", g_errors);
+  return g_errors ? 1 : 0;
+}

@@ -1,0 +1,190 @@
+// Host stand-in for swiglu_device.hpp: the same names and signatures, with
+// every LDS and global access bounds-checked instead of executed on a GPU.
+// Used only by the CPU bounds emulation (tests/emu); numerical results are
+// not produced (the MFMAs return their accumulator unchanged).
+//
+// LDS: the emulation rewrites each kernel's shared array into a call to
+// emu_lds(bytes), which returns one heap buffer of exactly that size; LDS
+// "addresses" are byte offsets into it.  Global memory: the driver registers
+// every buffer it passes in; a DMA or load from outside a registered buffer
+// is reported (on the GPU it would be a memory fault).
+#pragma once
+
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+
+#include "hip/hip_runtime_api.h"
+
+// ---- emulation state (defined in emu_driver.cpp) ------------------------------
+extern dim3 threadIdx, blockIdx, gridDim, blockDim;
+uint8_t* emu_lds(size_t bytes);
+void emu_barrier();
+void emu_check_global(const void* p, size_t n, const char* what);
+void emu_check_lds(uint32_t off, size_t n, const char* what);
+uint8_t* emu_lds_base();
+
+#define __global__
+#define __device__
+#define __host__
+#define __forceinline__ inline
+#define __launch_bounds__(...)
+inline void __syncthreads() { emu_barrier(); }
+// device-side integer min/max as HIP provides them
+inline int min(int a, int b) { return a < b ? a : b; }
+inline int max(int a, int b) { return a > b ? a : b; }
+#define __builtin_amdgcn_readfirstlane(x) (x)
+#define __builtin_amdgcn_sched_barrier(x) ((void)0)
+inline uint32_t emu_perm(uint32_t s0, uint32_t s1, uint32_t sel) {
+  const uint64_t v = ((uint64_t)s0 << 32) | s1;
+  uint32_t r = 0;
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t b = (sel >> (8 * i)) & 0xff;
+    const uint32_t byte = b < 8 ? (uint32_t)((v >> (8 * b)) & 0xff) : 0u;
+    r |= byte << (8 * i);
+  }
+  return r;
+}
+#define __builtin_amdgcn_perm(a, b, s) emu_perm((a), (b), (s))
+
+template <class K, class... Args>
+void emu_launch(K kernel, dim3 grid, dim3 block, Args... args) {
+  gridDim = grid;
+  blockDim = block;
+  for (unsigned by = 0; by < grid.y; ++by)
+    for (unsigned bx = 0; bx < grid.x; ++bx) {
+      blockIdx = dim3(bx, by, 0);
+      for (unsigned t = 0; t < block.x; ++t) {
+        threadIdx = dim3(t, 0, 0);
+        kernel(args...);
+      }
+    }
+}
+#define hipLaunchKernelGGL(K, G, B, SHM, STREAM, ...) emu_launch(K, dim3(G), dim3(B), __VA_ARGS__)
+
+namespace swiglu {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+
+inline bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+inline u32x4 load16(const void* p) {
+  emu_check_global(p, 16, "load16");
+  u32x4 r;
+  memcpy(&r, p, 16);
+  return r;
+}
+inline u32x2 load8(const void* p) {
+  emu_check_global(p, 8, "load8");
+  u32x2 r;
+  memcpy(&r, p, 8);
+  return r;
+}
+inline u32x4 load16_stream(const void* p) { return load16(p); }
+inline u32x2 load8_stream(const void* p) { return load8(p); }
+
+constexpr uint32_t kOutOfRange = 0x80000000u;
+
+// the resource keeps the full host pointer (words 0-1) and the byte bound (2)
+inline i32x4 make_rsrc(const void* p, uint32_t bytes) {
+  const uint64_t a = (uint64_t)(uintptr_t)p;
+  i32x4 r;
+  r[0] = (int32_t)(uint32_t)a;
+  r[1] = (int32_t)(uint32_t)(a >> 32);
+  r[2] = (int32_t)bytes;
+  r[3] = 0x00020000;
+  return r;
+}
+inline uint32_t lds_addr(const void* p) {
+  const uint8_t* b = emu_lds_base();
+  const ptrdiff_t d = (const uint8_t*)p - b;
+  emu_check_lds((uint32_t)d, 0, "lds_addr");
+  return (uint32_t)d;
+}
+// lane = threadIdx.x % 64 moves 16 bytes from base + voffset (zeros if
+// voffset >= the resource bound) to LDS offset lds_wave_base + 16 lane
+inline void lds_dma16(uint32_t lds_wave_base, uint32_t voffset, i32x4 rsrc) {
+  const uint32_t lane = threadIdx.x & 63u;
+  const uint32_t dst = lds_wave_base + 16u * lane;
+  emu_check_lds(dst, 16, "lds_dma16 destination");
+  uint8_t* d = emu_lds_base() + dst;
+  const uint32_t bound = (uint32_t)rsrc[2];
+  if (voffset >= bound) {
+    memset(d, 0, 16);
+    return;
+  }
+  if (voffset + 16u > bound) emu_check_global(nullptr, 0, "lds_dma16 read straddles the resource bound");
+  const uint8_t* base =
+      (const uint8_t*)(uintptr_t)(((uint64_t)(uint32_t)rsrc[1] << 32) | (uint32_t)rsrc[0]);
+  emu_check_global(base + voffset, 16, "lds_dma16 source");
+  memcpy(d, base + voffset, 16);
+}
+template <int N>
+inline void wait_vmcnt() {
+  static_assert(N >= 0 && N <= 63, "vmcnt range");
+}
+inline u32x2 lds_read_tr16(const void* p) {
+  const uint8_t* b = emu_lds_base();
+  emu_check_lds((uint32_t)((const uint8_t*)p - b), 8, "lds_read_tr16");
+  u32x2 r;
+  memcpy(&r, p, 8);
+  return r;
+}
+inline u32x4 lds_load16_at(uint32_t addr) {
+  emu_check_lds(addr, 16, "lds_load16_at");
+  u32x4 r;
+  memcpy(&r, emu_lds_base() + addr, 16);
+  return r;
+}
+inline u32x2 lds_read_tr16_at(uint32_t addr) {
+  emu_check_lds(addr, 8, "lds_read_tr16_at");
+  u32x2 r;
+  memcpy(&r, emu_lds_base() + addr, 8);
+  return r;
+}
+template <int OFF>
+inline u32x4 lds_load16_async(uint32_t addr) {
+  return lds_load16_at(addr + OFF);
+}
+template <int OFF>
+inline u32x2 lds_read_tr16_async(uint32_t addr) {
+  return lds_read_tr16_at(addr + OFF);
+}
+inline u32x4 join(u32x2 lo, u32x2 hi) { return u32x4{lo[0], lo[1], hi[0], hi[1]}; }
+template <int N>
+inline void lgkm_wait(u32x4&) {
+  static_assert(N >= 0 && N <= 15, "lgkmcnt range");
+}
+template <int N>
+inline void lgkm_wait(u32x4&, u32x4&, u32x4&) {
+  static_assert(N >= 0 && N <= 15, "lgkmcnt range");
+}
+inline float silu(float x) { return x / (1.0f + expf(-x)); }
+inline uint16_t bf16_bits(float x) { return __builtin_bit_cast(uint16_t, static_cast<__bf16>(x)); }
+inline uint32_t pack_bf16x2(float lo, float hi) {
+  return (uint32_t)bf16_bits(lo) | ((uint32_t)bf16_bits(hi) << 16);
+}
+inline float bf16_to_float(uint16_t h) { return __builtin_bit_cast(float, (uint32_t)h << 16); }
+inline void transpose8x8(const u32x4 row[8], u32x4 col[8]) {
+  for (int j = 0; j < 4; ++j)
+    for (int p = 0; p < 4; ++p) {
+      const uint32_t lo = row[2 * p][j], hi = row[2 * p + 1][j];
+      col[2 * j][p] = emu_perm(hi, lo, 0x05040100u);
+      col[2 * j + 1][p] = emu_perm(hi, lo, 0x07060302u);
+    }
+}
+inline f32x16 mfma32(const u32x4&, const u32x4&, const f32x16& c) { return c; }
+inline f32x4 mfma16(const u32x4&, const u32x4&, const f32x4& c) { return c; }
+inline int xcd_remap(int b, int nwg) {
+  const int q = nwg / 8, r = nwg % 8;
+  const int x = b % 8, i = b / 8;
+  return x * q + (x < r ? x : r) + i;
+}
+
+}  // namespace swiglu

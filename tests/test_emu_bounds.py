@@ -1,0 +1,59 @@
+"""CPU bounds emulation of every kernel configuration (no GPU).
+
+The kernel source is compiled for the host against a stand-in device header
+(tests/emu/swiglu_device.hpp) with AddressSanitizer, and every workgroup's
+threads are run through the real launch functions: each LDS offset, DMA
+source, direct global load and (via the sanitizer) global store and LDS
+pointer access is checked against the buffers actually allocated.  A kernel
+that would touch memory outside its inputs, outputs or LDS fails here instead
+of faulting a GPU.  Data values are not checked (barriers are no-ops);
+parity is the GPU tests' job.
+"""
+import os
+import subprocess
+import sys
+
+import pytest
+
+sys.path.insert(0, os.path.join(os.path.dirname(__file__), "emu"))
+import build as emu_build  # noqa: E402
+
+
+@pytest.fixture(scope="module")
+def emu(tmp_path_factory):
+    if emu_build.clangxx() is None:
+        pytest.skip("no host clang++")
+    return emu_build.build(str(tmp_path_factory.mktemp("emu")))
+
+
+def _run(exe, *args, timeout=600):
+    env = dict(os.environ, ASAN_OPTIONS="detect_leaks=0")
+    r = subprocess.run([exe, *map(str, args)], capture_output=True, text=True, timeout=timeout,
+                       env=env)
+    return r.returncode, r.stdout + r.stderr
+
+
+def test_all_configs_on_the_parity_shapes(emu):
+    rc, out = _run(emu)
+    assert rc == 0 and "errors: 0" in out, out[-4000:]
+    assert out.count(": ok") >= 5 * 40  # every config ran on every shape
+
+
+# (M, N, K, configs): launches whose tile counts exercise the split tail
+# (whole rounds of 256-row tiles plus a short last round), the table's
+# choices at the workloads' M and N, and decode-sized streaming
+CASES = [
+    (2008, 4216, 72, [40, 42]),        # 264 tiles: 256 big + 8 split
+    (2008, 8440, 72, [41]),            # the same for the 256-column GEMM tiles
+    (2048, 8960, 40, [40, 41, 42]),    # 1.5B M and N: 512 big + 48 split
+    (128, 4864, 40, [3, 29, 30]),      # 0.5B M and N
+    (16, 18944, 64, [23, 12, 18]),     # 7B decode M and N
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=lambda c: f"{c[0]}x{c[1]}x{c[2]}")
+def test_table_configs_at_workload_sizes(emu, case):
+    M, N, K, cfgs = case
+    for cfg in cfgs:
+        rc, out = _run(emu, "--shape", M, N, K, cfg)
+        assert rc == 0 and "errors: 0" in out, out[-4000:]
