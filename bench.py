@@ -106,20 +106,26 @@ def main():
         sw.swiglu_forward_ex(h, a, w1, w2, y, M, N, K, layout, sw.VARIANT_AUTO, args.config,
                              stream)
 
-    def timed(step_fn, steps, warmup):
+    def timed(step_fn, steps, warmup, batches=5):
+        """ms per step over all `steps` (one span of HIP events on the launch
+        stream), plus the per-step time of each of `batches` equal batches."""
         for i in range(warmup):
             step_fn(i)
         torch.cuda.synchronize()
-        start = torch.cuda.Event(enable_timing=True)
-        stop = torch.cuda.Event(enable_timing=True)
-        start.record(stream)
-        for i in range(steps):
-            step_fn(warmup + i)
-        stop.record(stream)
+        nb = max(1, min(batches, steps))
+        bounds = [round(b * steps / nb) for b in range(nb + 1)]
+        events = [torch.cuda.Event(enable_timing=True) for _ in range(nb + 1)]
+        events[0].record(stream)
+        for b in range(nb):
+            for i in range(bounds[b], bounds[b + 1]):
+                step_fn(warmup + i)
+            events[b + 1].record(stream)
         torch.cuda.synchronize()
-        return start.elapsed_time(stop) / steps  # ms per step
+        per_batch = [events[b].elapsed_time(events[b + 1]) / (bounds[b + 1] - bounds[b])
+                     for b in range(nb)]
+        return events[0].elapsed_time(events[nb]) / steps, per_batch
 
-    ms = timed(fused_step, args.steps, args.warmup)
+    ms, fused_batches = timed(fused_step, args.steps, args.warmup)
     tflops = wl.flops / (ms * 1e-3) / 1e12
     hbm_gbs = wl.fused_bytes / (ms * 1e-3) / 1e9
 
@@ -140,10 +146,20 @@ def main():
             a, w1, w2, y = usets[i % len(usets)]
             sw.swiglu_forward_unfused(h, a, w1, w2, ws_buf, y, M, N, K, -1, stream)
 
-        ums = timed(unfused_step, max(10, args.steps // 2), max(3, args.warmup // 2))
+        ums, _ = timed(unfused_step, max(10, args.steps // 2), max(3, args.warmup // 2))
+        # fusion efficiency: time saved / time to move the saved bytes at the
+        # device-to-device copy rate (1 GiB copy, bytes read + written)
+        csrc = torch.empty(2 ** 29, dtype=torch.int16, device=dev)
+        cdst = torch.empty_like(csrc)
+        cms, _ = timed(lambda i: cdst.copy_(csrc), 10, 3, batches=1)
+        copy_gbs = 2 * csrc.numel() * 2 / (cms * 1e-3) / 1e9
+        del csrc, cdst
+        saved = wl.unfused_bytes - wl.fused_bytes
         unfused = {"ms_per_step": round(ums, 5),
                    "tflops": round(wl.flops / (ums * 1e-3) / 1e12, 2),
                    "fusion_speedup": round(ums / ms, 3),
+                   "bytes_saved": saved, "copy_gbs": round(copy_gbs, 1),
+                   "fusion_efficiency": round((ums - ms) * 1e-3 / (saved / (copy_gbs * 1e9)), 3),
                    "gemm_tile": sw.swiglu_query_unfused(h, M, N, K)}
         del usets, ws_buf
 
@@ -188,6 +204,12 @@ def main():
                    "layout": "interleaved" if layout == sw.LAYOUT_INTERLEAVED else "separate",
                    "variant": "interleave" if variant == sw.VARIANT_INTERLEAVE else "sync",
                    "tile": tile, "rotated_sets": nsets, "parallelism": "single-gpu"},
+        "batches": {"n": len(fused_batches),
+                    "median_ms_per_step": round(sorted(fused_batches)[len(fused_batches) // 2], 5),
+                    "min_ms_per_step": round(min(fused_batches), 5)},
+        "env": {"device": torch.cuda.get_device_name(dev),
+                "compute_units": torch.cuda.get_device_properties(dev).multi_processor_count,
+                "torch": torch.__version__, "hip": torch.version.hip},
         "pct_mfma_peak": round(100 * tflops / PEAK_BF16_TFLOPS, 2),
         "hbm_gbs_algorithmic": round(hbm_gbs, 1),
         "unfused": unfused,

@@ -7,8 +7,8 @@
 // delle Attivazioni a Livello di Tile...", §Metodologia, Kernel-1 and Kernel-2
 // "Ottimizzazione"; §Contributi Chiave item 2).  Here the same decision is
 // re-made for MI355X: exact entries come from measured sweeps on the
-// Qwen2.5-shaped MLP workloads; every other shape takes the fallback rule,
-// which only looks at how many workgroups a tile size yields on the 256 CUs.
+// Qwen2.5-shaped MLP workloads; every other shape takes the fallback rule, a
+// choice by M measured on an M sweep (256 ... 8192) at the 1.5B K and N.
 #include "swiglu_internal.h"
 
 namespace swiglu {
@@ -56,36 +56,25 @@ int find_config(int variant, int family, int bm, int bn, int waves) {
   return -1;
 }
 
-long long tiles(long long M, long long N, int bm, int bn) {
-  return ((M + bm - 1) / bm) * ((N + bn - 1) / bn);
-}
-
 }  // namespace
 
 int select_config(int variant, long long M, long long N, long long K, int cu_count) {
   for (const ShapeEntry& e : kTable)
     if (e.variant == variant && e.M == M && e.N == N && e.K == K) return e.config_id;
-  const long long cus = cu_count > 0 ? cu_count : 256;
-  (void)K;
+  (void)N, (void)K, (void)cu_count;
   if (M <= 64) {
     // decode-sized batches: split-K weight streaming, 16-row MFMA blocks
     const int mt = M <= 16 ? 1 : (M <= 32 ? 2 : 4);
     return find_config(variant, 1, mt * 16, variant == VAR_GEMM ? 128 : 64, 0);
   }
-  // LDS-tiled: the largest tile that still gives two workgroups per CU.  The
-  // 256-row tiles run eight waves (two per SIMD, as 4x2, which measured faster
-  // than 2x4 at every large shape) and split a short last round into quarter
-  // tiles; the smaller ones run four waves.  Candidates are config ids,
-  // largest tile first.
-  static const int kFused[] = {40, 1, 2, 3};   // 256x128 (8 waves, split tail), 128x128, 128x64, 64x64
-  static const int kSync[] = {42, 8, 9, 10};   // 256x128 (8 waves, split tail), 128x128, 128x64, 64x64
-  static const int kGemm[] = {41, 15, 16, 17}; // 256x256 (8 waves, split tail), 256x128, 128x128, 64x64
-  const int* cand = variant == VAR_GEMM ? kGemm : (variant == VAR_SYNC ? kSync : kFused);
-  for (int i = 0; i < 4; ++i) {
-    const KernelConfig* c = config_at(cand[i]);
-    if (c && c->variant == variant && tiles(M, N, c->bm, c->bn) >= 2 * cus) return cand[i];
-  }
-  return cand[3];
+  // LDS-tiled, by M (measured at K = 1536, N = 8960 for M = 256 ... 8192 and
+  // on the workload shapes): 64-row tiles with deep stage rings around
+  // M = 128, 128-row tiles around M = 256, and from M = 512 on the 256-row
+  // eight-wave tiles (4x2 waves, short last round split into quarter tiles),
+  // which won even where they leave CUs idle (M = 512: 140 tiles on 256 CUs).
+  if (variant == VAR_GEMM) return M <= 192 ? 30 : (M <= 384 ? 16 : 41);
+  if (variant == VAR_SYNC) return M <= 192 ? 29 : (M <= 384 ? 8 : 42);
+  return M <= 192 ? 3 : (M <= 384 ? 1 : 40);
 }
 
 int recommend_layout(long long M, long long N, long long K, int cu_count) {
