@@ -21,6 +21,7 @@ __all__ = [
     "swiglu_forward_unfused", "swiglu_unfused_workspace_bytes",
     "swiglu_pack_interleaved", "swiglu_query", "swiglu_query_unfused",
     "swiglu_config_count", "swiglu_config_info", "swiglu_status_str",
+    "swiglu_config_signature", "swiglu_tuned_check", "swiglu_create_tuned",
     "LAYOUT_SEPARATE", "LAYOUT_INTERLEAVED",
     "VARIANT_AUTO", "VARIANT_SYNC", "VARIANT_INTERLEAVE", "VARIANT_GEMM",
 ]
@@ -86,6 +87,9 @@ def load():
         "swiglu_config_count": ([], i32),
         "swiglu_config_info": ([i32, ctypes.POINTER(Tile)], st),
         "swiglu_status_str": ([ctypes.c_int], ctypes.c_char_p),
+        "swiglu_config_signature": ([], ctypes.c_uint64),
+        "swiglu_tuned_check": ([ctypes.c_char_p, ctypes.POINTER(i32)], st),
+        "swiglu_create_tuned": ([ctypes.POINTER(p), ctypes.c_int, ctypes.c_char_p], st),
     }
     for name, (args, res) in sig.items():
         fn = getattr(lib, name)
@@ -126,6 +130,25 @@ def swiglu_create(device: int = 0) -> int:
     """Returns the opaque handle (an address)."""
     h = ctypes.c_void_p()
     _check(load().swiglu_create(ctypes.byref(h), device), "swiglu_create")
+    return h.value
+
+
+def swiglu_config_signature() -> int:
+    return load().swiglu_config_signature()
+
+
+def swiglu_tuned_check(path: str) -> int:
+    """Number of entries of a valid tuned file; raises SwiGLUError otherwise."""
+    n = ctypes.c_int32()
+    _check(load().swiglu_tuned_check(os.fsencode(path), ctypes.byref(n)), "swiglu_tuned_check")
+    return n.value
+
+
+def swiglu_create_tuned(device: int = 0, path: str | None = None) -> int:
+    h = ctypes.c_void_p()
+    _check(load().swiglu_create_tuned(ctypes.byref(h), device,
+                                      os.fsencode(path) if path is not None else None),
+           "swiglu_create_tuned")
     return h.value
 
 

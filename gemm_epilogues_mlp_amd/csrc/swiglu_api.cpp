@@ -9,14 +9,22 @@
 #include <string.h>
 
 #include <new>
+#include <vector>
 
 #include "swiglu_internal.h"
+
+struct swiglu_tuned_entry {
+  int variant;
+  long long M, N, K;
+  int config_id;
+};
 
 struct swiglu_ctx {
   int device;
   int cu_count;
   char arch[64];
   int log;  // SWIGLU_LOG=1: print the configuration chosen for each call
+  std::vector<swiglu_tuned_entry> tuned;  // exact-shape overrides, read at creation
 };
 
 namespace {
@@ -33,6 +41,84 @@ bool overlaps(const void* p, long long bytes, const void* q, long long qbytes) {
   if (!p || !q || bytes <= 0 || qbytes <= 0) return false;
   const uintptr_t a = (uintptr_t)p, b = (uintptr_t)q;
   return a < b + (uintptr_t)qbytes && b < a + (uintptr_t)bytes;
+}
+
+// The configuration for a shape: an exact tuned entry of the handle if there
+// is one, else the built-in table and its fallback rule.
+int choose(const swiglu_ctx* h, int variant, long long M, long long N, long long K) {
+  for (const swiglu_tuned_entry& e : h->tuned)
+    if (e.variant == variant && e.M == M && e.N == N && e.K == K) return e.config_id;
+  return select_config(variant, M, N, K, h->cu_count);
+}
+
+// ---- tuned-configuration files ---------------------------------------------
+// Text, one entry per line after a header line
+//   swiglu-tuned <signature, 16 hex digits> <arch>
+//   <variant> <M> <N> <K> <config id> [anything else: provenance, ignored]
+// '#' starts a comment line; blank lines are skipped.
+constexpr int kMaxTunedEntries = 4096;
+
+uint64_t config_signature() {
+  uint64_t h = 1469598103934665603ull;  // FNV-1a over the configuration list
+  auto mix = [&](long long v) {
+    for (int i = 0; i < 8; ++i) {
+      h ^= (uint64_t)((v >> (8 * i)) & 0xff);
+      h *= 1099511628211ull;
+    }
+  };
+  mix(config_count());
+  for (int i = 0; i < config_count(); ++i) {
+    const KernelConfig* c = config_at(i);
+    for (long long v : {(long long)c->variant, (long long)c->family, (long long)c->bm,
+                        (long long)c->bn, (long long)c->bk, (long long)c->waves,
+                        (long long)c->split_k, (long long)c->lds_bytes, (long long)c->tail_split})
+      mix(v);
+  }
+  return h;
+}
+
+swiglu_status_t read_tuned(const char* path, std::vector<swiglu_tuned_entry>* out) {
+  if (!path) return SWIGLU_ERR_INVALID_ARG;
+  FILE* f = fopen(path, "r");
+  if (!f) return SWIGLU_ERR_INVALID_ARG;
+  char line[512];
+  bool header = false;
+  swiglu_status_t st = SWIGLU_OK;
+  while (st == SWIGLU_OK && fgets(line, sizeof line, f)) {
+    if (!strchr(line, '\n') && !feof(f)) {  // longer than any valid line
+      st = SWIGLU_ERR_INVALID_ARG;
+      break;
+    }
+    const char* p = line;
+    while (*p == ' ' || *p == '\t') ++p;
+    if (*p == '#' || *p == '\n' || *p == '\r' || *p == 0) continue;
+    if (!header) {
+      unsigned long long sig = 0;
+      char arch[64];
+      if (sscanf(p, "swiglu-tuned %16llx %63s", &sig, arch) != 2) {
+        st = SWIGLU_ERR_INVALID_ARG;
+      } else if (sig != config_signature()) {
+        st = SWIGLU_ERR_UNSUPPORTED;  // written for another build's configurations
+      }
+      header = true;
+      continue;
+    }
+    swiglu_tuned_entry e;
+    if (sscanf(p, "%d %lld %lld %lld %d", &e.variant, &e.M, &e.N, &e.K, &e.config_id) != 5 ||
+        e.M < 0 || e.N < 0 || e.K < 0 || e.M > kMaxDim || e.N > kMaxDim || e.K > kMaxDim) {
+      st = SWIGLU_ERR_INVALID_ARG;
+      break;
+    }
+    const KernelConfig* c = config_at(e.config_id);
+    if (!c || c->variant != e.variant || (int)out->size() >= kMaxTunedEntries) {
+      st = SWIGLU_ERR_INVALID_ARG;
+      break;
+    }
+    out->push_back(e);
+  }
+  fclose(f);
+  if (st == SWIGLU_OK && !header) st = SWIGLU_ERR_INVALID_ARG;
+  return st;
 }
 
 swiglu_status_t check_device(const swiglu_ctx* h) {
@@ -176,7 +262,7 @@ swiglu_status_t swiglu_forward_ex(swiglu_handle_t h, const void* A, const void* 
     if (!c || c->variant != want) return SWIGLU_ERR_INVALID_ARG;
   }
   if (noop) return SWIGLU_OK;
-  if (id < 0) id = select_config(want, M, N, K, h->cu_count);
+  if (id < 0) id = choose(h, want, M, N, K);
   if (id < 0) return SWIGLU_ERR_UNSUPPORTED;
   return run(h, config_at(id), id, A, W1, W2, Y, M, N, K, stream);
 }
@@ -213,7 +299,7 @@ swiglu_status_t swiglu_forward_unfused(swiglu_handle_t h, const void* A, const v
   if (overlaps(workspace, wsb, Y, 2LL * M * N) || overlaps(workspace, wsb, A, 2LL * M * K) ||
       overlaps(workspace, wsb, W1, wb) || overlaps(workspace, wsb, W2, wb))
     return SWIGLU_ERR_INVALID_ARG;
-  if (id < 0) id = select_config(VAR_GEMM, M, N, K, h->cu_count);
+  if (id < 0) id = choose(h, VAR_GEMM, M, N, K);
   if (id < 0) return SWIGLU_ERR_UNSUPPORTED;
   uint16_t* G = (uint16_t*)workspace;
   uint16_t* U = G + (size_t)M * (size_t)N;
@@ -255,7 +341,7 @@ swiglu_status_t swiglu_query(swiglu_handle_t h, int64_t M, int64_t N, int64_t K,
   if (layout != SWIGLU_LAYOUT_SEPARATE && layout != SWIGLU_LAYOUT_INTERLEAVED)
     return SWIGLU_ERR_INVALID_ARG;
   const int want = layout == SWIGLU_LAYOUT_INTERLEAVED ? VAR_INTERLEAVE : VAR_SYNC;
-  const int id = select_config(want, M, N, K, h->cu_count);
+  const int id = choose(h, want, M, N, K);
   if (id < 0) return SWIGLU_ERR_UNSUPPORTED;
   if (chosen) *chosen = (swiglu_variant_t)want;
   if (tile) fill_tile(id, tile);
@@ -267,9 +353,34 @@ swiglu_status_t swiglu_query(swiglu_handle_t h, int64_t M, int64_t N, int64_t K,
 swiglu_status_t swiglu_query_unfused(swiglu_handle_t h, int64_t M, int64_t N, int64_t K,
                                      swiglu_tile_t* tile) {
   if (!h || M < 0 || N < 0 || K < 0) return SWIGLU_ERR_INVALID_ARG;
-  const int id = select_config(VAR_GEMM, M, N, K, h->cu_count);
+  const int id = choose(h, VAR_GEMM, M, N, K);
   if (id < 0) return SWIGLU_ERR_UNSUPPORTED;
   if (tile) fill_tile(id, tile);
+  return SWIGLU_OK;
+}
+
+uint64_t swiglu_config_signature(void) { return config_signature(); }
+
+swiglu_status_t swiglu_tuned_check(const char* path, int32_t* n_entries) {
+  std::vector<swiglu_tuned_entry> e;
+  const swiglu_status_t st = read_tuned(path, &e);
+  if (n_entries) *n_entries = st == SWIGLU_OK ? (int32_t)e.size() : 0;
+  return st;
+}
+
+swiglu_status_t swiglu_create_tuned(swiglu_handle_t* out, int device, const char* path) {
+  if (!out) return SWIGLU_ERR_INVALID_ARG;
+  *out = nullptr;
+  std::vector<swiglu_tuned_entry> e;
+  if (path) {
+    const swiglu_status_t st = read_tuned(path, &e);
+    if (st != SWIGLU_OK) return st;
+  }
+  swiglu_handle_t h = nullptr;
+  const swiglu_status_t st = swiglu_create(&h, device);
+  if (st != SWIGLU_OK) return st;
+  h->tuned.swap(e);
+  *out = h;
   return SWIGLU_OK;
 }
 

@@ -164,6 +164,30 @@ swiglu_status_t swiglu_query(swiglu_handle_t h, int64_t M, int64_t N, int64_t K,
 swiglu_status_t swiglu_query_unfused(swiglu_handle_t h, int64_t M, int64_t N,
                                      int64_t K, swiglu_tile_t* tile);
 
+/* Tuned per-shape configurations.  A tuned file (written by the package's
+ * tuner, python -m gemm_epilogues_mlp_amd.tune) is text:
+ *   swiglu-tuned <signature: 16 hex digits> <arch>        first non-comment line
+ *   <variant 1|2|3> <M> <N> <K> <config id> [ignored provenance]   one per shape
+ * with '#' comment lines.  The signature (swiglu_config_signature) identifies
+ * the list of compiled configurations; a file written for a library with a
+ * different list is refused, so an id can never name the wrong kernel.
+ * Entries only add exact shapes: every other shape keeps the built-in table
+ * [RT §Contributi Chiave, item 2: the per-batch choice of kernel]. */
+uint64_t swiglu_config_signature(void);
+
+/* Read and validate a tuned file without a device.  *n_entries (may be NULL)
+ * receives the number of entries.  Errors: INVALID_ARG (NULL path, unreadable
+ * or malformed file, a config id that does not exist or is not of the entry's
+ * variant, more than 4096 entries), UNSUPPORTED (signature of another build). */
+swiglu_status_t swiglu_tuned_check(const char* path, int32_t* n_entries);
+
+/* swiglu_create plus the entries of a tuned file (path NULL: none), which then
+ * take precedence over the built-in table for their exact (variant, M, N, K)
+ * in swiglu_forward, _ex with config_id < 0, _unfused and the queries.  The
+ * file is read once here; the handle stays immutable.  Errors: those of
+ * swiglu_tuned_check, then those of swiglu_create. */
+swiglu_status_t swiglu_create_tuned(swiglu_handle_t* out, int device, const char* path);
+
 /* Number of compiled kernel configurations and their descriptions. */
 int32_t swiglu_config_count(void);
 swiglu_status_t swiglu_config_info(int32_t config_id, swiglu_tile_t* out);
