@@ -297,7 +297,7 @@ def test_unfused_emulation_rounds_intermediates(medium):
 
 
 # --------------------------------------------------------------------------- full size vs float64
-@pytest.mark.parametrize("wl", I.WORKLOADS[:3], ids=lambda w: w.name)
+@pytest.mark.parametrize("wl", I.WORKLOADS, ids=lambda w: w.name)
 def test_fullsize_rows_against_float64(wl):
     """Oracle rows at the workloads' real sizes vs a float64 matmul of the same bits.
 
