@@ -9,6 +9,7 @@
 //
 // usage: emu_driver [cfg ...]          all shapes for the listed configs (default: all)
 //        emu_driver --shape M N K cfg  one shape
+//        --last-blocks B               only the last B workgroups of each launch
 #include <stdio.h>
 #include <stdlib.h>
 
@@ -18,6 +19,7 @@
 #include "swiglu_kernels_emu.cpp"
 
 dim3 threadIdx, blockIdx, gridDim, blockDim;
+long g_emu_last_blocks = 0;
 
 namespace {
 struct Alloc {
@@ -139,7 +141,9 @@ int main(int argc, char** argv) {
   int shape[3] = {0, 0, 0};
   bool one_shape = false;
   for (int i = 1; i < argc; ++i) {
-    if (std::string(argv[i]) == "--shape" && i + 3 < argc) {
+    if (std::string(argv[i]) == "--last-blocks" && i + 1 < argc) {
+      g_emu_last_blocks = atol(argv[++i]);
+    } else if (std::string(argv[i]) == "--shape" && i + 3 < argc) {
       shape[0] = atoi(argv[i + 1]), shape[1] = atoi(argv[i + 2]), shape[2] = atoi(argv[i + 3]);
       one_shape = true;
       i += 3;

@@ -47,12 +47,18 @@ inline uint32_t emu_perm(uint32_t s0, uint32_t s1, uint32_t sel) {
 }
 #define __builtin_amdgcn_perm(a, b, s) emu_perm((a), (b), (s))
 
+// emulate only the last g_emu_last_blocks workgroups of each launch (0: all);
+// the last workgroups of a launch touch the largest offsets
+extern long g_emu_last_blocks;
 template <class K, class... Args>
 void emu_launch(K kernel, dim3 grid, dim3 block, Args... args) {
   gridDim = grid;
   blockDim = block;
+  const long total = (long)grid.x * grid.y;
+  const long first = g_emu_last_blocks > 0 && g_emu_last_blocks < total ? total - g_emu_last_blocks : 0;
   for (unsigned by = 0; by < grid.y; ++by)
     for (unsigned bx = 0; bx < grid.x; ++bx) {
+      if ((long)by * grid.x + bx < first) continue;
       blockIdx = dim3(bx, by, 0);
       for (unsigned t = 0; t < block.x; ++t) {
         threadIdx = dim3(t, 0, 0);

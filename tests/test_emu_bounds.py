@@ -57,3 +57,21 @@ def test_table_configs_at_workload_sizes(emu, case):
     for cfg in cfgs:
         rc, out = _run(emu, "--shape", M, N, K, cfg)
         assert rc == 0 and "errors: 0" in out, out[-4000:]
+
+
+# tensors just under the 2 GiB limit (largest byte offsets the kernels form):
+# A = 2 * 65536 * 16376 B, and W_fused = 4 * 16376 * 32768 B; only the last
+# workgroups of each launch are emulated (they touch the largest offsets)
+LIMIT_CASES = [
+    (65536, 64, 16376, [40, 42, 41], 4),
+    (16, 32768, 16376, [4, 11, 18, 23, 12], 8),
+    (256, 32768, 16376, [1, 8, 16], 4),
+]
+
+
+@pytest.mark.parametrize("case", LIMIT_CASES, ids=lambda c: f"{c[0]}x{c[1]}x{c[2]}")
+def test_tensors_just_under_2gib(emu, case):
+    M, N, K, cfgs, last = case
+    for cfg in cfgs:
+        rc, out = _run(emu, "--last-blocks", last, "--shape", M, N, K, cfg, timeout=900)
+        assert rc == 0 and "errors: 0" in out, out[-4000:]
