@@ -13,7 +13,10 @@ di LLM" (summary of arXiv 2607.02521):
 
 * §Definizione del Problema -- Y = SiLU(A x W1) (.) (A x W2);
 * §Metodologia, Kernel-2 -- W_fused [K, 2N], Gate in even, Up in odd columns;
-* §Contributi Chiave, item 3 -- accuracy is judged against an FP32 reference.
+* §Contributi Chiave, item 3 -- accuracy is judged against an FP32 reference;
+* §Definizione del Problema names FP8 quantisation, and the page "Ottimizzazione
+  delle GEMM: la chiave per l'efficienza dei Large Language Models" MXFP8: the
+  FP8 functions below read that as OCP E4M3 codes with per-tensor scales.
 
 This module only marshals numpy arrays to the C functions.  Every function
 here is pinned by CPU tests against facts that do not come from it (exact
@@ -65,9 +68,17 @@ def _load():
     lib.oracle_round_bf16.argtypes = [p, p, i64]
     lib.oracle_decode_bf16.argtypes = [p, p, i64]
     lib.oracle_pack_interleaved.argtypes = [p, p, p, i64, i64]
+    lib.oracle_decode_e4m3.argtypes = [p, p, i64]
+    lib.oracle_quantize_e4m3.argtypes = [p, ctypes.c_float, p, i64]
+    lib.oracle_pack_fp8_kmajor.argtypes = [p, p, p, i64, i64]
     for fn in (lib.oracle_silu, lib.oracle_gate, lib.oracle_round_bf16,
-               lib.oracle_decode_bf16, lib.oracle_pack_interleaved):
+               lib.oracle_decode_bf16, lib.oracle_pack_interleaved, lib.oracle_decode_e4m3,
+               lib.oracle_quantize_e4m3, lib.oracle_pack_fp8_kmajor):
         fn.restype = None
+    f32 = ctypes.c_float
+    lib.oracle_swiglu_fp8_rows.argtypes = [p, p, p, i64, i64, i64, f32, f32, f32, p, i64,
+                                           p, p, p, c_int]
+    lib.oracle_swiglu_fp8_rows.restype = c_int
     _lib = lib
     return lib
 
@@ -213,3 +224,76 @@ def swiglu_unfused_emulation(a, w1, w2, rows=None, nthreads=None):
     _, g, u = swiglu_rows(a, w1, w2, LAYOUT_SEPARATE, rows, True, nthreads)
     gb, ub = round_bf16(g), round_bf16(u)
     return gate(decode_bf16(gb), decode_bf16(ub)), gb, ub
+
+
+# ---- FP8 (OCP E4M3) inputs --------------------------------------------------
+# Reading of the pages (they name FP8 and MXFP8 but fix no encoding): OCP E4M3
+# codes with one fp32 scale per tensor, a code q standing for scale * decode(q).
+# The arithmetic is in oracle.c.
+
+
+def _u8(x, name):
+    x = np.ascontiguousarray(x)
+    if x.dtype != np.uint8:
+        raise TypeError(f"{name} must hold E4M3 codes as uint8, got {x.dtype}")
+    return x
+
+
+def decode_e4m3(x):
+    """E4M3 codes (uint8) -> exact float64 values (NaN for S.1111.111)."""
+    x = _u8(x, "x")
+    out = np.empty(x.shape, np.float64)
+    _load().oracle_decode_e4m3(_ptr(x), _ptr(out), x.size)
+    return out
+
+
+def quantize_e4m3(x, inv_scale=1.0):
+    """fp32 values -> E4M3 codes of fp32(x * inv_scale), nearest-even, saturating at 448."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    out = np.empty(x.shape, np.uint8)
+    _load().oracle_quantize_e4m3(_ptr(x), float(np.float32(inv_scale)), _ptr(out), x.size)
+    return out
+
+
+def pack_fp8_kmajor(w1, w2):
+    """W8 [2N, K] from W1, W2 [K, N] E4M3: row 2n = Gate column n, row 2n+1 = Up column n."""
+    w1 = _u8(w1, "W1")
+    w2 = _u8(w2, "W2")
+    if w1.shape != w2.shape:
+        raise ValueError("W1 and W2 differ in shape")
+    K, N = w1.shape
+    w8 = np.empty((2 * N, K), np.uint8)
+    _load().oracle_pack_fp8_kmajor(_ptr(w1), _ptr(w2), _ptr(w8), K, N)
+    return w8
+
+
+def swiglu_fp8_rows(a, w1, w2, s_a=1.0, s_w1=1.0, s_w2=1.0, rows=None,
+                    with_gate_up=False, nthreads=None):
+    """fp32 y = SiLU(g) * u of the FP8 forward (and optionally g, u) for the listed rows.
+
+    a: uint8 E4M3 [M, K]; w1, w2: uint8 E4M3 [K, N]; s_*: the per-tensor fp32
+    scales.  g = s_a s_w1 (exact dot product of the decoded codes), rounded to fp32.
+    """
+    a = _u8(a, "A")
+    w1 = _u8(w1, "W1")
+    w2 = _u8(w2, "W2")
+    M, K = a.shape
+    if w1.shape != w2.shape or w1.shape[0] != K:
+        raise ValueError("W1 and W2 must both be [K, N]")
+    N = w1.shape[1]
+    lib = _load()
+    if rows is None:
+        ridx, nr = None, M
+    else:
+        ridx = np.ascontiguousarray(rows, dtype=np.int64)
+        nr = ridx.size
+    y = np.empty((nr, N), np.float32)
+    g = np.empty((nr, N), np.float32) if with_gate_up else None
+    u = np.empty((nr, N), np.float32) if with_gate_up else None
+    f = lambda v: float(np.float32(v))
+    rc = lib.oracle_swiglu_fp8_rows(_ptr(a), _ptr(w1), _ptr(w2), M, N, K, f(s_a), f(s_w1),
+                                    f(s_w2), _ptr(ridx), nr, _ptr(y), _ptr(g), _ptr(u),
+                                    nthreads or default_threads())
+    if rc < 0:
+        raise ValueError("oracle_swiglu_fp8_rows rejected its arguments")
+    return (y, g, u) if with_gate_up else y

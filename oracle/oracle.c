@@ -31,6 +31,11 @@
  *     y = s * u                            fp32, returned unrounded
  * Rounding to bf16 (round-to-nearest-even) is a separate, explicit step.
  *
+ * FP8 inputs (OCP E4M3 codes with per-tensor scales; the reading is stated
+ * at the FP8 section below): exact decode, round-to-nearest-even saturating
+ * quantisation, the k-contiguous Gate/Up pairing of the weights, and the same
+ * forward on the decoded values with an exact (fp64) dot product.
+ *
  * Parity pins (the tests check this file against facts that do not come from
  * it): exact brute force with correctly rounded sums on tiny shapes, SiLU
  * closed forms, the A = I special case, invariants (W1 = 0 or W2 = 0 gives 0,
@@ -289,4 +294,179 @@ void oracle_pack_interleaved(const uint16_t* w1, const uint16_t* w2, uint16_t* w
       wf[k * 2 * N + 2 * n] = w1[k * N + n];
       wf[k * 2 * N + 2 * n + 1] = w2[k * N + n];
     }
+}
+
+/* ======================================================================== */
+/* FP8 inputs                                                                */
+/* ======================================================================== */
+/*
+ * [RT §Definizione del Problema] names FP8 quantisation as the step that makes
+ * the memory-bound activation a larger share of the MLP; the page "Ottimizzazione
+ * delle GEMM: la chiave per l'efficienza dei Large Language Models"
+ * (§Impatto sui deployment on-premise e la sovranita dei dati) reports GEMM
+ * benchmarks on MXFP8.  Neither page fixes an encoding or a scaling scheme.
+ * Reading taken here: the OCP 8-bit floating-point format E4M3 (1 sign bit,
+ * 4 exponent bits with bias 7, 3 mantissa bits; no infinities; S.1111.111 is
+ * NaN; largest finite 448), with one fp32 scale per tensor, so that a stored
+ * code q stands for the real value scale * decode(q).
+ *
+ * The fp8 forward is then the same definition as the bf16 one, on those real
+ * values:   g = s_a s_w1 sum_k decode(a[m,k]) decode(w1[k,n]),   u likewise,
+ *           y = SiLU(g) * u.
+ * Every decoded product is an integer multiple of 2^-18 of magnitude at most
+ * 448^2 < 2^18, so for K <= 2^17 every partial sum is a multiple of 2^-18
+ * below 2^35 and an fp64 accumulator holds the dot product exactly, in any
+ * order.  g and u are that exact value times s_a s_w (fp64), rounded to fp32;
+ * SiLU and the product are the fp32 steps of the bf16 path above.
+ */
+
+/* Real value of an E4M3 code, from the format's definition. */
+static double e4m3_value(uint8_t b) {
+  const int s = b >> 7, e = (b >> 3) & 15, m = b & 7;
+  double v;
+  if (e == 15 && m == 7) return NAN;
+  if (e == 0)
+    v = ldexp((double)m, -9);      /* subnormal: (m / 8) * 2^(1 - 7) */
+  else
+    v = ldexp(8.0 + m, e - 10);    /* normal: (1 + m / 8) * 2^(e - 7) */
+  return s ? -v : v;
+}
+
+/* fp32 -> E4M3, round to nearest with ties to even, saturating: magnitudes at
+ * or above 448 (and infinities) become +-448, NaN becomes S.1111.111.  The
+ * sign of zero and of values that round to zero is kept. */
+static uint8_t e4m3_from_f32(float x) {
+  const uint8_t sign = signbit(x) ? 0x80 : 0x00;
+  if (isnan(x)) return sign | 0x7F;
+  const double a = fabs((double)x);
+  if (a >= 448.0) return sign | 0x7E;
+  int code;
+  if (a < ldexp(1.0, -6)) {
+    /* below the smallest normal the codes are the multiples of 2^-9; the
+     * rounded count 8 is the code of 2^-6 itself */
+    code = (int)nearbyint(a * 512.0);
+  } else {
+    int e2;
+    (void)frexp(a, &e2);          /* a in [2^(e2-1), 2^e2) */
+    const int e = e2 - 1;
+    const int q = (int)nearbyint(ldexp(a, 3 - e));  /* 8 .. 16 eighths of 2^e */
+    code = ((e + 7) << 3) + (q - 8);                 /* q = 16 carries into e + 1 */
+  }
+  if (code > 0x7E) code = 0x7E;
+  return (uint8_t)(sign | code);
+}
+
+void oracle_decode_e4m3(const uint8_t* x, double* out, int64_t n) {
+  for (int64_t i = 0; i < n; ++i) out[i] = e4m3_value(x[i]);
+}
+
+/* q[i] = E4M3(fp32(x[i] * inv_scale)) for fp32 x: the product is rounded to
+ * fp32 first, then to E4M3 as above. */
+void oracle_quantize_e4m3(const float* x, float inv_scale, uint8_t* out, int64_t n) {
+  for (int64_t i = 0; i < n; ++i) {
+    const float v = x[i] * inv_scale;
+    out[i] = e4m3_from_f32(v);
+  }
+}
+
+/* W8[2n, k] = W1[k, n], W8[2n+1, k] = W2[k, n]: the Kernel-2 pairing of Gate
+ * and Up columns [RT §Metodologia, Kernel-2], stored with k contiguous (each
+ * W_fused column becomes a row).  A bit copy. */
+void oracle_pack_fp8_kmajor(const uint8_t* w1, const uint8_t* w2, uint8_t* w8, int64_t K,
+                            int64_t N) {
+  for (int64_t n = 0; n < N; ++n)
+    for (int64_t k = 0; k < K; ++k) {
+      w8[(2 * n) * K + k] = w1[k * N + n];
+      w8[(2 * n + 1) * K + k] = w2[k * N + n];
+    }
+}
+
+typedef struct {
+  const uint8_t *a, *w1, *w2; /* A [M, K]; W1, W2 [K, N], E4M3 codes */
+  int64_t M, N, K;
+  double sg, su;              /* s_a * s_w1, s_a * s_w2 */
+  const int64_t* idx;
+  int64_t lo, hi;
+  float *y, *g, *u;
+} job8_t;
+
+static void* rows8_worker(void* p) {
+  job8_t* j = (job8_t*)p;
+  const int64_t N = j->N, K = j->K;
+  double lut[256];
+  for (int c = 0; c < 256; ++c) lut[c] = e4m3_value((uint8_t)c);
+  double* gacc = (double*)malloc(sizeof(double) * (size_t)(N > 0 ? N : 1));
+  double* uacc = (double*)malloc(sizeof(double) * (size_t)(N > 0 ? N : 1));
+  for (int64_t r = j->lo; r < j->hi; ++r) {
+    const int64_t m = j->idx[r];
+    for (int64_t n = 0; n < N; ++n) gacc[n] = 0.0, uacc[n] = 0.0;
+    for (int64_t k = 0; k < K; ++k) {
+      const double a = lut[j->a[m * K + k]];
+      const uint8_t* w1 = j->w1 + k * N;
+      const uint8_t* w2 = j->w2 + k * N;
+      for (int64_t n = 0; n < N; ++n) {
+        gacc[n] += a * lut[w1[n]];
+        uacc[n] += a * lut[w2[n]];
+      }
+    }
+    for (int64_t n = 0; n < N; ++n) {
+      const float g = (float)(gacc[n] * j->sg);
+      const float u = (float)(uacc[n] * j->su);
+      j->y[r * N + n] = silu_f32(g) * u;
+      if (j->g) j->g[r * N + n] = g;
+      if (j->u) j->u[r * N + n] = u;
+    }
+  }
+  free(gacc), free(uacc);
+  return NULL;
+}
+
+/*
+ * oracle_swiglu_fp8_rows: fp32 y (and optionally g, u) of the FP8 forward for
+ * the model rows listed in rows[0..nrows) (NULL: all rows).  a: E4M3 [M, K];
+ * w1, w2: E4M3 [K, N] row-major; scales as described above.  Returns the
+ * number of threads used, or -1 on a bad argument.
+ */
+int oracle_swiglu_fp8_rows(const uint8_t* a, const uint8_t* w1, const uint8_t* w2,
+                           int64_t M, int64_t N, int64_t K, float s_a, float s_w1,
+                           float s_w2, const int64_t* rows, int64_t nrows, float* y,
+                           float* g, float* u, int nthreads) {
+  if (M < 0 || N < 0 || K < 0 || nrows < 0 || !y) return -1;
+  if (K > 0 && N > 0 && (!a || !w1 || !w2)) return -1;
+  int64_t* all = NULL;
+  if (!rows) {
+    nrows = M;
+    all = (int64_t*)malloc(sizeof(int64_t) * (size_t)(M > 0 ? M : 1));
+    for (int64_t i = 0; i < M; ++i) all[i] = i;
+    rows = all;
+  }
+  for (int64_t i = 0; i < nrows; ++i)
+    if (rows[i] < 0 || rows[i] >= M) {
+      free(all);
+      return -1;
+    }
+  job8_t jobs[256];
+  for (int t = 0; t < 256; ++t) {
+    job8_t j = {a, w1, w2, M, N, K, (double)s_a * (double)s_w1, (double)s_a * (double)s_w2,
+                rows, 0, 0, y, g, u};
+    jobs[t] = j;
+  }
+  /* run_split fills lo/hi through the job_t prefix; job8_t keeps its own
+   * fields, so split here */
+  if (nthreads < 1) nthreads = 1;
+  if (nthreads > 256) nthreads = 256;
+  if ((int64_t)nthreads > nrows) nthreads = (int)(nrows > 0 ? nrows : 1);
+  pthread_t th[256];
+  int started[256] = {0};
+  for (int t = 0; t < nthreads; ++t) {
+    jobs[t].lo = nrows * t / nthreads;
+    jobs[t].hi = nrows * (t + 1) / nthreads;
+    if (t > 0 && pthread_create(&th[t], NULL, rows8_worker, &jobs[t]) == 0) started[t] = 1;
+  }
+  for (int t = 0; t < nthreads; ++t)
+    if (t == 0 || !started[t]) rows8_worker(&jobs[t]);
+  for (int t = 1; t < nthreads; ++t)
+    if (started[t]) pthread_join(th[t], NULL);
+  free(all);
+  return nthreads;
 }
