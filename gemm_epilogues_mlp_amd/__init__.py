@@ -22,8 +22,9 @@ __all__ = [
     "swiglu_pack_interleaved", "swiglu_query", "swiglu_query_unfused",
     "swiglu_config_count", "swiglu_config_info", "swiglu_status_str",
     "swiglu_config_signature", "swiglu_tuned_check", "swiglu_create_tuned",
+    "swiglu_forward_fp8", "swiglu_quantize_fp8", "swiglu_pack_fp8", "swiglu_query_fp8",
     "LAYOUT_SEPARATE", "LAYOUT_INTERLEAVED",
-    "VARIANT_AUTO", "VARIANT_SYNC", "VARIANT_INTERLEAVE", "VARIANT_GEMM",
+    "VARIANT_AUTO", "VARIANT_SYNC", "VARIANT_INTERLEAVE", "VARIANT_GEMM", "VARIANT_FP8",
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -31,7 +32,7 @@ _LIB_PATH = os.path.join(_PKG, "libswiglu.so")
 
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_DEVICE, ERR_LAUNCH, ERR_ALLOC = range(6)
 LAYOUT_SEPARATE, LAYOUT_INTERLEAVED = 0, 1
-VARIANT_AUTO, VARIANT_SYNC, VARIANT_INTERLEAVE, VARIANT_GEMM = 0, 1, 2, 3
+VARIANT_AUTO, VARIANT_SYNC, VARIANT_INTERLEAVE, VARIANT_GEMM, VARIANT_FP8 = 0, 1, 2, 3, 4
 
 
 class SwiGLUError(RuntimeError):
@@ -90,6 +91,11 @@ def load():
         "swiglu_config_signature": ([], ctypes.c_uint64),
         "swiglu_tuned_check": ([ctypes.c_char_p, ctypes.POINTER(i32)], st),
         "swiglu_create_tuned": ([ctypes.POINTER(p), ctypes.c_int, ctypes.c_char_p], st),
+        "swiglu_forward_fp8": ([p, p, p, p, i64, i64, i64, ctypes.c_float, ctypes.c_float,
+                                ctypes.c_float, i32, p], st),
+        "swiglu_quantize_fp8": ([p, p, p, i64, ctypes.c_float, p], st),
+        "swiglu_pack_fp8": ([p, p, p, p, i64, i64, p], st),
+        "swiglu_query_fp8": ([p, i64, i64, i64, ctypes.POINTER(Tile)], st),
     }
     for name, (args, res) in sig.items():
         fn = getattr(lib, name)
@@ -195,6 +201,30 @@ def swiglu_query(handle, M, N, K, layout=LAYOUT_SEPARATE):
 def swiglu_query_unfused(handle, M, N, K):
     t = Tile()
     _check(load().swiglu_query_unfused(handle, M, N, K, ctypes.byref(t)), "swiglu_query_unfused")
+    return t.as_dict()
+
+
+def swiglu_forward_fp8(handle, A8, W8, Y, M, N, K, scale_a=1.0, scale_w1=1.0, scale_w2=1.0,
+                       config_id=-1, stream=None):
+    """A8 [M, K] and W8 [2N, K] hold E4M3 codes (uint8 tensors); Y bf16 [M, N]."""
+    _check(load().swiglu_forward_fp8(handle, _ptr(A8), _ptr(W8), _ptr(Y), M, N, K, scale_a,
+                                     scale_w1, scale_w2, config_id, _stream(stream)),
+           "swiglu_forward_fp8")
+
+
+def swiglu_quantize_fp8(handle, X, Q, count, inv_scale=1.0, stream=None):
+    _check(load().swiglu_quantize_fp8(handle, _ptr(X), _ptr(Q), count, inv_scale,
+                                      _stream(stream)), "swiglu_quantize_fp8")
+
+
+def swiglu_pack_fp8(handle, W1, W2, W8, K, N, stream=None):
+    _check(load().swiglu_pack_fp8(handle, _ptr(W1), _ptr(W2), _ptr(W8), K, N, _stream(stream)),
+           "swiglu_pack_fp8")
+
+
+def swiglu_query_fp8(handle, M, N, K):
+    t = Tile()
+    _check(load().swiglu_query_fp8(handle, M, N, K, ctypes.byref(t)), "swiglu_query_fp8")
     return t.as_dict()
 
 

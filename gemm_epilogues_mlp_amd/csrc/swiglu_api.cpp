@@ -334,6 +334,92 @@ swiglu_status_t swiglu_pack_interleaved(swiglu_handle_t h, const void* W1, const
   return SWIGLU_OK;
 }
 
+swiglu_status_t swiglu_forward_fp8(swiglu_handle_t h, const void* A8, const void* W8, void* Y,
+                                   int64_t M, int64_t N, int64_t K, float scale_a,
+                                   float scale_w1, float scale_w2, int32_t config_id,
+                                   hipStream_t stream) {
+  if (!h || M < 0 || N < 0 || K < 0) return SWIGLU_ERR_INVALID_ARG;
+  int id = config_id;
+  if (id >= 0) {
+    const KernelConfig* c = config_at(id);
+    if (!c || c->variant != VAR_F8) return SWIGLU_ERR_INVALID_ARG;
+  }
+  if (M == 0 || N == 0) return SWIGLU_OK;
+  if (!Y || (K > 0 && (!A8 || !W8))) return SWIGLU_ERR_INVALID_ARG;
+  if (M > kMaxDim || K > kMaxDim || N > (kMaxDim >> 1)) return SWIGLU_ERR_UNSUPPORTED;
+  if (N % 8 != 0 || K % 16 != 0) return SWIGLU_ERR_UNSUPPORTED;
+  if (!aligned16(Y) || !aligned16(A8) || !aligned16(W8)) return SWIGLU_ERR_UNSUPPORTED;
+  const long long ybytes = 2LL * M * N, abytes = M * K, wbytes = 2LL * N * K;
+  if (ybytes >= kMaxBytes || abytes >= kMaxBytes || wbytes >= kMaxBytes)
+    return SWIGLU_ERR_UNSUPPORTED;
+  if (K > 0 && (overlaps(Y, ybytes, A8, abytes) || overlaps(Y, ybytes, W8, wbytes)))
+    return SWIGLU_ERR_INVALID_ARG;
+  swiglu_status_t st = check_device(h);
+  if (st != SWIGLU_OK) return st;
+  if (id < 0) id = choose(h, VAR_F8, M, N, K);
+  if (id < 0) return SWIGLU_ERR_UNSUPPORTED;
+  LaunchArgs a;
+  a.A = (const uint16_t*)A8;  // byte tensors; the FP8 launchers take them as such
+  a.W1 = (const uint16_t*)W8;
+  a.W2 = nullptr;
+  a.Y = (uint16_t*)Y;
+  a.M = (int)M, a.N = (int)N, a.K = (int)K;
+  a.ldw = (int)K;
+  a.ldy = (int)N;
+  a.group_m = 0;
+  a.cu_count = h->cu_count;
+  a.scale_g = scale_a * scale_w1;
+  a.scale_u = scale_a * scale_w2;
+  a.stream = stream;
+  return launch(h, config_at(id), id, a);
+}
+
+swiglu_status_t swiglu_quantize_fp8(swiglu_handle_t h, const void* X, void* Q, int64_t count,
+                                    float inv_scale, hipStream_t stream) {
+  if (!h || count < 0) return SWIGLU_ERR_INVALID_ARG;
+  if (count == 0) return SWIGLU_OK;
+  if (!X || !Q) return SWIGLU_ERR_INVALID_ARG;
+  if (count % 16 != 0 || !aligned16(X) || !aligned16(Q)) return SWIGLU_ERR_UNSUPPORTED;
+  if (count > (1LL << 40)) return SWIGLU_ERR_UNSUPPORTED;
+  if (overlaps(Q, count, X, 2 * count)) return SWIGLU_ERR_INVALID_ARG;
+  swiglu_status_t st = check_device(h);
+  if (st != SWIGLU_OK) return st;
+  (void)hipGetLastError();
+  if (launch_quantize_f8((const uint16_t*)X, (uint8_t*)Q, (size_t)count, inv_scale, stream,
+                         h->cu_count) != hipSuccess)
+    return SWIGLU_ERR_LAUNCH;
+  return SWIGLU_OK;
+}
+
+swiglu_status_t swiglu_pack_fp8(swiglu_handle_t h, const void* W1, const void* W2, void* W8,
+                                int64_t K, int64_t N, hipStream_t stream) {
+  if (!h || K < 0 || N < 0) return SWIGLU_ERR_INVALID_ARG;
+  if (K == 0 || N == 0) return SWIGLU_OK;
+  if (!W1 || !W2 || !W8) return SWIGLU_ERR_INVALID_ARG;
+  if (K > kMaxDim || N > (kMaxDim >> 1)) return SWIGLU_ERR_UNSUPPORTED;
+  if (N % 8 != 0 || K % 16 != 0) return SWIGLU_ERR_UNSUPPORTED;
+  if (!aligned16(W1) || !aligned16(W2) || !aligned16(W8)) return SWIGLU_ERR_UNSUPPORTED;
+  const long long wb = K * N;
+  if (2 * wb >= kMaxBytes) return SWIGLU_ERR_UNSUPPORTED;
+  if (overlaps(W8, 2 * wb, W1, wb) || overlaps(W8, 2 * wb, W2, wb)) return SWIGLU_ERR_INVALID_ARG;
+  swiglu_status_t st = check_device(h);
+  if (st != SWIGLU_OK) return st;
+  (void)hipGetLastError();
+  if (launch_pack_f8((const uint8_t*)W1, (const uint8_t*)W2, (uint8_t*)W8, (int)N, (int)K, stream,
+                     h->cu_count) != hipSuccess)
+    return SWIGLU_ERR_LAUNCH;
+  return SWIGLU_OK;
+}
+
+swiglu_status_t swiglu_query_fp8(swiglu_handle_t h, int64_t M, int64_t N, int64_t K,
+                                 swiglu_tile_t* tile) {
+  if (!h || M < 0 || N < 0 || K < 0) return SWIGLU_ERR_INVALID_ARG;
+  const int id = choose(h, VAR_F8, M, N, K);
+  if (id < 0) return SWIGLU_ERR_UNSUPPORTED;
+  if (tile) fill_tile(id, tile);
+  return SWIGLU_OK;
+}
+
 swiglu_status_t swiglu_query(swiglu_handle_t h, int64_t M, int64_t N, int64_t K,
                              swiglu_layout_t layout, swiglu_variant_t* chosen,
                              swiglu_tile_t* tile, swiglu_layout_t* recommended_layout) {

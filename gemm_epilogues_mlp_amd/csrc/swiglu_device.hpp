@@ -188,6 +188,41 @@ __device__ __forceinline__ f32x4 mfma16(const u32x4& a, const u32x4& b, const f3
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), as_bf16x8(b), c, 0, 0, 0);
 }
 
+// v_mfma_scale_f32_32x32x64_f8f6f4 with both sources in E4M3 (format 0) and
+// unit block scales (E8M0 exponent 127 = 2^0): D = A B + C over 64 k.  Each
+// source lane holds 32 bytes (one row or column, 32 of the 64 k) as two
+// 16-byte halves; the output layout is that of v_mfma_f32_32x32x16_bf16.
+typedef int32_t i32x8 __attribute__((ext_vector_type(8)));
+__device__ __forceinline__ f32x16 mfma32_f8(const u32x4 (&a)[2], const u32x4 (&b)[2],
+                                            const f32x16& c) {
+  const i32x8 x = __builtin_bit_cast(i32x8, __builtin_shufflevector(a[0], a[1], 0, 1, 2, 3, 4, 5, 6, 7));
+  const i32x8 y = __builtin_bit_cast(i32x8, __builtin_shufflevector(b[0], b[1], 0, 1, 2, 3, 4, 5, 6, 7));
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(x, y, c, 0, 0, 0, 127, 0, 127);
+}
+
+// fp32 -> OCP E4M3 code, round to nearest even, saturating: |v| >= 448 (and
+// infinities) -> +-448, NaN -> S.1111.111; the sign of zero is kept.  Below
+// 2^-6 the codes count multiples of 2^-9; above, the 3-bit mantissa is the
+// rounded number of eighths of 2^e, and a carry to 16 eighths moves into the
+// next binade by itself (code arithmetic).  Scaling by powers of two is exact.
+__device__ __forceinline__ uint32_t e4m3_code(float v) {
+  const uint32_t sign = (__builtin_bit_cast(uint32_t, v) >> 24) & 0x80u;
+  const float a = __builtin_fabsf(v);
+  uint32_t code;
+  if (!(a == a)) {
+    code = 0x7Fu;
+  } else if (a >= 448.0f) {
+    code = 0x7Eu;
+  } else if (a < 0.015625f) {
+    code = (uint32_t)__builtin_rintf(a * 512.0f);
+  } else {
+    const int e = (int)((__builtin_bit_cast(uint32_t, a) >> 23) & 0xffu) - 127;
+    const float q = __builtin_rintf(__builtin_ldexpf(a, 3 - e));  // 8 .. 16
+    code = (uint32_t)((e + 7) << 3) + (uint32_t)q - 8u;
+  }
+  return sign | code;
+}
+
 // Workgroup id -> tile id so that each of the 8 XCDs (which receive workgroups
 // round-robin in launch order) works on one contiguous range of tile ids, and
 // the tiles that run together on an XCD share operand panels in its L2.

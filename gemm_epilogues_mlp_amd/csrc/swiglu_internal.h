@@ -7,7 +7,8 @@
 
 namespace swiglu {
 
-enum Variant { VAR_AUTO = 0, VAR_SYNC = 1, VAR_INTERLEAVE = 2, VAR_GEMM = 3 };
+// VAR_F8: interleave pairing on FP8 (E4M3) inputs with k-contiguous weights
+enum Variant { VAR_AUTO = 0, VAR_SYNC = 1, VAR_INTERLEAVE = 2, VAR_GEMM = 3, VAR_F8 = 4 };
 
 struct LaunchArgs {
   const uint16_t* A;
@@ -18,6 +19,7 @@ struct LaunchArgs {
   int ldw, ldy;        // row strides (elements) of the weights and of Y
   int group_m;         // tile rows per GROUP_M band (<= 0: default)
   int cu_count;        // compute units of the device (workgroups per round)
+  float scale_g, scale_u;  // FP8: s_a * s_w1 and s_a * s_w2 (unused otherwise)
   hipStream_t stream;
 };
 
@@ -38,6 +40,12 @@ hipError_t launch_gate(const uint16_t* G, const uint16_t* U, uint16_t* Y, size_t
                        hipStream_t stream, int cu_count);
 hipError_t launch_pack(const uint16_t* W1, const uint16_t* W2, uint16_t* WF, size_t n,
                        hipStream_t stream, int cu_count);
+// FP8: bf16 -> E4M3 of x * inv_scale (n a multiple of 16); W1, W2 [K, N] E4M3 ->
+// W8 [2N, K] (K a multiple of 16)
+hipError_t launch_quantize_f8(const uint16_t* X, uint8_t* Q, size_t n, float inv_scale,
+                              hipStream_t stream, int cu_count);
+hipError_t launch_pack_f8(const uint8_t* W1, const uint8_t* W2, uint8_t* W8, int N, int K,
+                          hipStream_t stream, int cu_count);
 
 // Per-shape choice (tile table + fallback rule).  variant is SYNC, INTERLEAVE
 // or GEMM; returns a config id of that variant.

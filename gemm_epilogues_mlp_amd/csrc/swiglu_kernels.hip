@@ -885,6 +885,317 @@ void skinny_kernel(const uint16_t* __restrict__ A,
 }
 
 // ============================================================================
+// FP8 (OCP E4M3) inputs: LDS-tiled interleave kernel
+// ============================================================================
+// A8 [M, K] and W8 [2N, K] hold E4M3 codes with k contiguous in both; row 2n
+// of W8 is Gate column n and row 2n+1 Up column n (the Kernel-2 pairing of
+// [RT §Metodologia], each W_fused column stored as a row).  A stored code q
+// stands for scale * q with one fp32 scale per tensor; the kernel multiplies
+// the finished fp32 accumulators by s_a s_w1 (Gate) and s_a s_w2 (Up) before
+// SiLU, so the MFMAs run with unit block scales.
+//
+// Same skeleton as tiled_kernel: eight (or four) waves, direct HBM -> LDS
+// DMA STAGES-1 steps ahead, one barrier per K step, XCD-aware tile order.
+// What differs: K steps of 64 (one v_mfma_scale_f32_32x32x64_f8f6f4 per
+// 32 x 32 block and step, twice the bf16 rate per cycle) and both tiles are
+// k-contiguous rows of 64 bytes with one swizzle and one fragment read: lane
+// l takes row l%32 and the 16-byte chunks l/32 and 2 + l/32 of the step, for
+// the activation and for the weight source alike (the MFMA only needs the
+// two sources to place k the same way).  Per step a wave issues its MFMAs
+// weight block by weight block; a weight fragment is re-read for the next
+// step as soon as its last MFMA is issued, and the activation fragments are
+// double-buffered by step parity (the stage ring has an even length, so the
+// parity is a compile-time constant of the unrolled ring).
+template <int BM, int BNW, int STAGES, int WGM, int WGN>
+struct F8Tiled {
+  static constexpr int kWaves = WGM * WGN;
+  static_assert(kWaves == 4 || kWaves == 8, "four waves (one per SIMD) or eight (two per SIMD)");
+  static constexpr int kThreads = 64 * kWaves;
+  static constexpr int BK = 64;          // k per step = bytes per tile row
+  static constexpr int BNY = BNW / 2;    // output columns
+  static constexpr int WTM = BM / WGM;   // A rows per wave
+  static constexpr int WTW = BNW / WGN;  // W8 rows per wave
+  static constexpr int FA = WTM / 32;
+  static constexpr int FW = WTW / 32;
+  static_assert(FA >= 1 && FW >= 1 && WTM % 32 == 0 && WTW % 32 == 0, "wave tile");
+  static constexpr int A_BYTES = BM * BK;
+  static constexpr int W_BYTES = BNW * BK;
+  static constexpr int STAGE_BYTES = A_BYTES + W_BYTES;
+  static constexpr int A_CHUNKS = BM * 4, W_CHUNKS = BNW * 4;  // 16-byte chunks
+  static_assert(A_CHUNKS % 64 == 0 && W_CHUNKS % 64 == 0, "whole waves of chunks");
+  static constexpr int A_LOADS = (A_CHUNKS + kThreads - 1) / kThreads;
+  static constexpr int W_LOADS = (W_CHUNKS + kThreads - 1) / kThreads;
+  static constexpr int LOADS = A_LOADS + W_LOADS;
+  static_assert(STAGES >= 2 && STAGES % 2 == 0, "an even stage ring");
+  static_assert((STAGES - 1) * LOADS <= 63, "vmcnt range");
+  static constexpr int YLD = BNY + 8;
+  static constexpr int Y_BYTES = BM * YLD * 2;
+  static constexpr int JUNK = STAGES * STAGE_BYTES;  // 1 KB slot for zero DMA
+  static constexpr int LDS_BYTES = JUNK + 1024 > Y_BYTES ? JUNK + 1024 : Y_BYTES;
+  static_assert(LDS_BYTES <= 160 * 1024, "LDS");
+  // chunk c of row r stored at c ^ swz(r): the 64-byte-row swizzle of the
+  // bf16 A tile (the fragment read pattern is the same: 32 consecutive rows,
+  // chunk h for lanes of half h, then chunk 2 + h)
+  __host__ __device__ static constexpr int swz(int row) {
+    return (((row >> 2) & 1) << 1) | (((row >> 1) ^ (row >> 3)) & 1);
+  }
+};
+
+template <int BM, int BNW, int STAGES, int WGM, int WGN>
+__device__ __forceinline__ void f8_tile(const uint8_t* __restrict__ A,
+                                        const uint8_t* __restrict__ W,
+                                        uint16_t* __restrict__ Y, int M, int N, int K,
+                                        float sg, float su, int m0, int tn, uint8_t* smem) {
+  using C = F8Tiled<BM, BNW, STAGES, WGM, WGN>;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int wm = wave / WGN, wn = wave % WGN;
+  const int wr0 = tn * BNW;  // first W8 row of the tile
+  const int y0 = tn * C::BNY;
+  const int nk = (K + C::BK - 1) / C::BK;
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+
+  // ---- DMA of one K step ----------------------------------------------------------
+  // A chunk or a weight chunk is zero-filled when its row is out of range or
+  // its k is (rows are k-contiguous, so a chunk past K would read the next
+  // row: both sources check k).  All sums below stay under 2^32: offsets are
+  // < 2^31 (tensors are smaller) and k0 <= K < 2^31.
+  const i32x4 rsA = make_rsrc(A, (uint32_t)((size_t)M * K));
+  const i32x4 rsW = make_rsrc(W, (uint32_t)((size_t)2 * N * K));
+  const uint32_t lds0 = lds_addr(smem);
+  constexpr uint32_t kRowOut = 0x80000000u;  // k of a chunk whose row is out of range
+  uint32_t a_off[C::A_LOADS], a_k[C::A_LOADS];
+#pragma unroll
+  for (int i = 0; i < C::A_LOADS; ++i) {
+    const int p = tid + C::kThreads * i;
+    const int row = p / 4;
+    const int c = (p % 4) ^ C::swz(row);
+    const bool in = m0 + row < M;
+    a_off[i] = in ? (uint32_t)((size_t)(m0 + row) * K + c * 16) : 0u;
+    a_k[i] = in ? (uint32_t)(c * 16) : kRowOut;
+  }
+  uint32_t w_off[C::W_LOADS], w_k[C::W_LOADS];
+#pragma unroll
+  for (int i = 0; i < C::W_LOADS; ++i) {
+    const int p = tid + C::kThreads * i;
+    const int row = p / 4;
+    const int c = (p % 4) ^ C::swz(row);
+    const bool in = wr0 + row < 2 * N;
+    w_off[i] = in ? (uint32_t)((size_t)(wr0 + row) * K + c * 16) : 0u;
+    w_k[i] = in ? (uint32_t)(c * 16) : kRowOut;
+  }
+  // DMA instruction q (A chunks first, then weight chunks) of K step `it`
+  // into stage ST; steps past the end load zeros (k0 = K)
+  auto dma = [&](int it, auto st_c, int q) __attribute__((always_inline)) {
+    constexpr int ST = decltype(st_c)::value;
+    const uint32_t k0 = it < nk ? (uint32_t)it * C::BK : (uint32_t)K;
+    const uint32_t sbase = lds0 + ST * C::STAGE_BYTES;
+    if (q < C::A_LOADS) {
+      const int p0 = C::kThreads * q + 64 * wave_u;
+      const bool own = p0 < C::A_CHUNKS;
+      const uint32_t off = (own && k0 + a_k[q] < (uint32_t)K) ? a_off[q] + k0 : kOutOfRange;
+      lds_dma16(own ? sbase + p0 * 16 : lds0 + C::JUNK, off, rsA);
+    } else {
+      const int i = q - C::A_LOADS;
+      const int p0 = C::kThreads * i + 64 * wave_u;
+      const bool own = p0 < C::W_CHUNKS;
+      const uint32_t off = (own && k0 + w_k[i] < (uint32_t)K) ? w_off[i] + k0 : kOutOfRange;
+      lds_dma16(own ? sbase + C::A_BYTES + p0 * 16 : lds0 + C::JUNK, off, rsW);
+    }
+  };
+
+  // ---- fragments ------------------------------------------------------------------
+  const int h = lane >> 5;
+  const int a_row = wm * C::WTM + (lane & 31);  // + 32 fa
+  const int w_row = wn * C::WTW + (lane & 31);  // + 32 fw
+  auto read = [&](const uint8_t* tile, int row, u32x4 (&f)[2]) __attribute__((always_inline)) {
+    const uint8_t* r = tile + row * C::BK;
+    f[0] = *reinterpret_cast<const u32x4*>(r + ((h ^ C::swz(row)) * 16));
+    f[1] = *reinterpret_cast<const u32x4*>(r + (((2 + h) ^ C::swz(row)) * 16));
+  };
+  u32x4 wf[C::FW][2];
+  u32x4 af[2][C::FA][2];
+  f32x16 acc[C::FW][C::FA];
+#pragma unroll
+  for (int i = 0; i < C::FW; ++i)
+#pragma unroll
+    for (int j = 0; j < C::FA; ++j) acc[i][j] = f32x16{};
+
+  // One K step on stage ST.  After the barrier, every wave has the loads of
+  // step it+1 in LDS and has finished reading stage ST, so the MFMAs of step
+  // `it` run beside the fragment reads of step it+1 (stage ST+1) and the DMA
+  // of step it+STAGES into stage ST.
+  constexpr int NMF = C::FW * C::FA;
+  constexpr int DBEGIN = NMF / 2;
+  constexpr int DSLOTS = NMF - DBEGIN;
+  auto kstep = [&](int it, auto st_c) __attribute__((always_inline)) {
+    constexpr int ST = decltype(st_c)::value;
+    constexpr int P = ST & 1;
+    using Next = std::integral_constant<int, (ST + 1) % STAGES>;
+    const uint8_t* nxt = smem + Next::value * C::STAGE_BYTES;
+    wait_vmcnt<(STAGES - 2) * C::LOADS>();
+    __syncthreads();
+#pragma unroll
+    for (int q = 0; q < NMF; ++q) {
+      const int i = q / C::FA, j = q % C::FA;
+      acc[i][j] = mfma32_f8(wf[i], af[P][j], acc[i][j]);
+      if (q < C::FA) read(nxt, a_row + 32 * q, af[P ^ 1][q]);
+      if (j == C::FA - 1) read(nxt + C::A_BYTES, w_row + 32 * i, wf[i]);
+      if (q >= DBEGIN) {
+#pragma unroll
+        for (int x = (q - DBEGIN) * C::LOADS / DSLOTS; x < (q - DBEGIN + 1) * C::LOADS / DSLOTS;
+             ++x)
+          dma(it + STAGES, st_c, x);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  auto run = [&]() __attribute__((always_inline)) {
+    int it = 0;
+    for (; it + STAGES <= nk; it += STAGES)
+      [&]<int... S>(std::integer_sequence<int, S...>) __attribute__((always_inline)) {
+        (kstep(it + S, std::integral_constant<int, S>{}), ...);
+      }(std::make_integer_sequence<int, STAGES>{});
+    [&]<int... S>(std::integer_sequence<int, S...>) __attribute__((always_inline)) {
+      ((it + S < nk ? (kstep(it + S, std::integral_constant<int, S>{}), 0) : 0), ...);
+    }(std::make_integer_sequence<int, STAGES - 1>{});
+  };
+
+  // ---- prologue: steps 0 .. STAGES-1 in flight, fragments of step 0 --------------
+  [&]<int... S>(std::integer_sequence<int, S...>) __attribute__((always_inline)) {
+    ((
+         [&] {
+#pragma unroll
+           for (int q = 0; q < C::LOADS; ++q) dma(S, std::integral_constant<int, S>{}, q);
+         }()),
+     ...);
+  }(std::make_integer_sequence<int, STAGES>{});
+  wait_vmcnt<(STAGES - 1) * C::LOADS>();
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < C::FA; ++j) read(smem, a_row + 32 * j, af[0][j]);
+#pragma unroll
+  for (int i = 0; i < C::FW; ++i) read(smem + C::A_BYTES, w_row + 32 * i, wf[i]);
+
+  run();
+
+  // ---- epilogue: scales, SiLU(Gate) * Up, bf16 tile through LDS, row stores -------
+  wait_vmcnt<0>();
+  __syncthreads();
+  uint16_t* ys = reinterpret_cast<uint16_t*>(smem);  // [BM][YLD]
+#pragma unroll
+  for (int i = 0; i < C::FW; ++i)
+#pragma unroll
+    for (int j = 0; j < C::FA; ++j) {
+      const int row = a_row + j * 32;
+      const f32x16& d = acc[i][j];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        // registers 4q..4q+3: W8 rows wcl..wcl+3 = Gate/Up of columns wcl/2, wcl/2+1
+        const int wcl = wn * C::WTW + i * 32 + 8 * q + 4 * h;
+        const float ya = silu(sg * d[4 * q + 0]) * (su * d[4 * q + 1]);
+        const float yb = silu(sg * d[4 * q + 2]) * (su * d[4 * q + 3]);
+        *reinterpret_cast<uint32_t*>(ys + row * C::YLD + wcl / 2) = pack_bf16x2(ya, yb);
+      }
+    }
+  __syncthreads();
+  constexpr int YCH = C::BNY / 8;
+  for (int p = tid; p < BM * YCH; p += C::kThreads) {
+    const int row = p / YCH, cq = p % YCH;
+    const int gr = m0 + row, gc = y0 + cq * 8;
+    if (gr < M && gc < N)
+      *reinterpret_cast<u32x4*>(Y + (size_t)gr * N + gc) =
+          *reinterpret_cast<const u32x4*>(ys + row * C::YLD + cq * 8);
+  }
+}
+
+template <int BM, int BNW, int STAGES, int WGM, int WGN>
+__global__ __launch_bounds__(64 * WGM * WGN) void f8_kernel(const uint8_t* __restrict__ A,
+                                                             const uint8_t* __restrict__ W,
+                                                             uint16_t* __restrict__ Y, int M,
+                                                             int N, int K, float sg, float su,
+                                                             int group_m) {
+  using C = F8Tiled<BM, BNW, STAGES, WGM, WGN>;
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[C::LDS_BYTES];
+  const int ntm = (M + BM - 1) / BM;
+  const int ntn = (N + C::BNY - 1) / C::BNY;
+  int tm, tn;
+  tile_of(xcd_remap(blockIdx.x, gridDim.x), ntm, ntn, group_m, tm, tn);
+  f8_tile<BM, BNW, STAGES, WGM, WGN>(A, W, Y, M, N, K, sg, su, tm * BM, tn, smem);
+}
+
+// The split tail of tiled_split_kernel for the FP8 tiles: workgroups
+// [0, n_big) take whole tiles, the rest quarter tiles of the partial last round.
+template <int BM, int BNW, int STAGES, int WGM, int WGN, int SWGM, int SWGN>
+__global__ __launch_bounds__(64 * WGM * WGN) void f8_split_kernel(
+    const uint8_t* __restrict__ A, const uint8_t* __restrict__ W, uint16_t* __restrict__ Y,
+    int M, int N, int K, float sg, float su, int group_m, int n_big) {
+  using Big = F8Tiled<BM, BNW, STAGES, WGM, WGN>;
+  using Small = F8Tiled<BM / 2, BNW / 2, STAGES, SWGM, SWGN>;
+  static_assert(Big::kThreads == Small::kThreads, "one workgroup size for both tile kinds");
+  constexpr int LDS = Big::LDS_BYTES > Small::LDS_BYTES ? Big::LDS_BYTES : Small::LDS_BYTES;
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[LDS];
+  const int ntm = (M + BM - 1) / BM;
+  const int ntn = (N + Big::BNY - 1) / Big::BNY;
+  int tm, tn;
+  if ((int)blockIdx.x < n_big) {
+    tile_of(xcd_remap(blockIdx.x, n_big), ntm, ntn, group_m, tm, tn);
+    f8_tile<BM, BNW, STAGES, WGM, WGN>(A, W, Y, M, N, K, sg, su, tm * BM, tn, smem);
+  } else {
+    const int u = blockIdx.x - n_big, q = u & 3;
+    tile_of(n_big + u / 4, ntm, ntn, group_m, tm, tn);
+    const int m0 = tm * BM + (q >> 1) * (BM / 2);
+    const int tq = 2 * tn + (q & 1);
+    if (m0 >= M || tq * Small::BNY >= N) return;
+    f8_tile<BM / 2, BNW / 2, STAGES, SWGM, SWGN>(A, W, Y, M, N, K, sg, su, m0, tq, smem);
+  }
+}
+
+// bf16 -> E4M3 codes of fp32(x * inv_scale); 16 elements (32 B in, 16 B out)
+// per thread per iteration, grid-stride.
+__global__ __launch_bounds__(256) void quantize_kernel(const uint16_t* __restrict__ X,
+                                                       uint8_t* __restrict__ Q, size_t n16,
+                                                       float inv_scale) {
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n16;
+       i += (size_t)gridDim.x * blockDim.x) {
+    const u32x4 lo = load16(X + i * 16);
+    const u32x4 hi = load16(X + i * 16 + 8);
+    u32x4 o;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const u32x4& s = w < 2 ? lo : hi;
+      const uint32_t d0 = s[(2 * w) & 3], d1 = s[(2 * w + 1) & 3];
+      const uint32_t c0 = e4m3_code(bf16_to_float((uint16_t)(d0 & 0xffffu)) * inv_scale);
+      const uint32_t c1 = e4m3_code(bf16_to_float((uint16_t)(d0 >> 16)) * inv_scale);
+      const uint32_t c2 = e4m3_code(bf16_to_float((uint16_t)(d1 & 0xffffu)) * inv_scale);
+      const uint32_t c3 = e4m3_code(bf16_to_float((uint16_t)(d1 >> 16)) * inv_scale);
+      o[w] = c0 | (c1 << 8) | (c2 << 16) | (c3 << 24);
+    }
+    *reinterpret_cast<u32x4*>(Q + i * 16) = o;
+  }
+}
+
+// W8[2n + p, k] = Wp[k, n] (p = 0: W1, 1: W2), E4M3 bytes.  A thread writes
+// one 16-byte run of k of one W8 row; neighbouring threads take neighbouring
+// rows, so the 16 byte loads of a wave read consecutive columns.
+__global__ __launch_bounds__(256) void pack_f8_kernel(const uint8_t* __restrict__ W1,
+                                                      const uint8_t* __restrict__ W2,
+                                                      uint8_t* __restrict__ W8, int N, int K) {
+  const size_t rows = 2 * (size_t)N, runs = rows * (size_t)(K / 16);
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < runs;
+       i += (size_t)gridDim.x * blockDim.x) {
+    const size_t r = i % rows, c = i / rows;
+    const int n = (int)(r >> 1);
+    const uint8_t* src = ((r & 1) ? W2 : W1) + c * 16 * (size_t)N + n;
+    uint32_t d[4] = {0, 0, 0, 0};
+#pragma unroll
+    for (int t = 0; t < 16; ++t) d[t >> 2] |= (uint32_t)src[(size_t)t * N] << (8 * (t & 3));
+    *reinterpret_cast<u32x4*>(W8 + r * (size_t)K + c * 16) = u32x4{d[0], d[1], d[2], d[3]};
+  }
+}
+
+// ============================================================================
 // Unfused baseline element-wise gate and the W_fused pack kernel
 // ============================================================================
 // Y = bf16(SiLU(G) * U) element-wise, G and U bf16, fp32 arithmetic; 8
@@ -999,6 +1310,47 @@ static hipError_t launch_skinny(const LaunchArgs& a) {
   return hipGetLastError();
 }
 
+template <int BM, int BNW, int STAGES, int WGM, int WGN>
+static hipError_t launch_f8(const LaunchArgs& a) {
+  using C = F8Tiled<BM, BNW, STAGES, WGM, WGN>;
+  const int ntm = (a.M + BM - 1) / BM, ntn = (a.N + C::BNY - 1) / C::BNY;
+  const long long nwg = (long long)ntm * ntn;
+  if (nwg <= 0) return hipSuccess;
+  if (nwg > 0x7fffffffLL) return hipErrorInvalidValue;
+  int group_m = a.group_m > 0 ? a.group_m : 8;
+  if (group_m > ntm) group_m = ntm;
+  hipLaunchKernelGGL((f8_kernel<BM, BNW, STAGES, WGM, WGN>), dim3((unsigned)nwg),
+                     dim3(C::kThreads), 0, a.stream, (const uint8_t*)a.A,
+                     (const uint8_t*)a.W1, a.Y, a.M, a.N, a.K, a.scale_g, a.scale_u, group_m);
+  return hipGetLastError();
+}
+
+template <int BM, int BNW, int STAGES, int WGM, int WGN, int SWGM, int SWGN>
+static hipError_t launch_f8_split(const LaunchArgs& a) {
+  using C = F8Tiled<BM, BNW, STAGES, WGM, WGN>;
+  const int ntm = (a.M + BM - 1) / BM, ntn = (a.N + C::BNY - 1) / C::BNY;
+  const long long nt = (long long)ntm * ntn;
+  if (nt <= 0) return hipSuccess;
+  if (4 * nt > 0x7fffffffLL) return hipErrorInvalidValue;
+  const long long slots = a.cu_count > 0 ? a.cu_count : 256;
+  const long long n_big = nt / slots * slots, tail = nt - n_big;
+  if (tail == 0 || 4 * tail > slots) return launch_f8<BM, BNW, STAGES, WGM, WGN>(a);
+  int group_m = a.group_m > 0 ? a.group_m : 8;
+  if (group_m > ntm) group_m = ntm;
+  hipLaunchKernelGGL((f8_split_kernel<BM, BNW, STAGES, WGM, WGN, SWGM, SWGN>),
+                     dim3((unsigned)(n_big + 4 * tail)), dim3(C::kThreads), 0, a.stream,
+                     (const uint8_t*)a.A, (const uint8_t*)a.W1, a.Y, a.M, a.N, a.K, a.scale_g,
+                     a.scale_u, group_m, (int)n_big);
+  return hipGetLastError();
+}
+
+#define F8(bm, bnw, st, wgm, wgn)                                                          \
+  {VAR_F8, 0, bm, F8Tiled<bm, bnw, st, wgm, wgn>::BNY, 64, (wgm) * (wgn), 1,               \
+   F8Tiled<bm, bnw, st, wgm, wgn>::LDS_BYTES, &launch_f8<bm, bnw, st, wgm, wgn>}
+#define F8_SPLIT(bm, bnw, st, wgm, wgn, swgm, swgn)                                        \
+  {VAR_F8, 0, bm, F8Tiled<bm, bnw, st, wgm, wgn>::BNY, 64, (wgm) * (wgn), 1,               \
+   F8Tiled<bm, bnw, st, wgm, wgn>::LDS_BYTES,                                              \
+   &launch_f8_split<bm, bnw, st, wgm, wgn, swgm, swgn>, 4}
 #define TILED(mode, v, bm, bnw, bk, st, wgm, wgn)                                          \
   {v, 0, bm, Tiled<mode, bm, bnw, bk, st, wgm, wgn>::BNY, bk, (wgm) * (wgn), 1,             \
    Tiled<mode, bm, bnw, bk, st, wgm, wgn>::LDS_BYTES, &launch_tiled<mode, bm, bnw, bk, st, wgm, wgn>}
@@ -1066,6 +1418,12 @@ static const KernelConfig kConfigs[] = {
     TILED_SPLIT(MODE_INTERLEAVE, VAR_INTERLEAVE, 256, 256, 32, 4, 4, 2, 2, 4),  // 40
     TILED_SPLIT(MODE_GEMM, VAR_GEMM, 256, 256, 32, 4, 4, 2, 2, 4),              // 41
     TILED_SPLIT(MODE_SYNC, VAR_SYNC, 256, 128, 32, 4, 4, 2, 4, 2),              // 42
+    // ---- FP8 (E4M3) inputs, k-contiguous paired weights ----------------------
+    F8_SPLIT(256, 256, 4, 4, 2, 2, 4),                              // 43
+    F8(256, 256, 4, 4, 2),                                          // 44
+    F8(128, 256, 4, 2, 2),                                          // 45
+    F8(64, 128, 4, 2, 2),                                           // 46
+    F8(64, 128, 8, 2, 2),                                           // 47
 };
 
 int config_count() { return (int)(sizeof(kConfigs) / sizeof(kConfigs[0])); }
@@ -1081,6 +1439,30 @@ hipError_t launch_gate(const uint16_t* G, const uint16_t* U, uint16_t* Y, size_t
   const size_t cap = (size_t)(cu_count > 0 ? cu_count : 256) * 8;
   if (blocks > cap) blocks = cap;
   hipLaunchKernelGGL(gate_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, G, U, Y, n8);
+  return hipGetLastError();
+}
+
+hipError_t launch_quantize_f8(const uint16_t* X, uint8_t* Q, size_t n, float inv_scale,
+                              hipStream_t stream, int cu_count) {
+  const size_t n16 = n / 16;
+  if (n16 == 0) return hipSuccess;
+  size_t blocks = (n16 + 255) / 256;
+  const size_t cap = (size_t)(cu_count > 0 ? cu_count : 256) * 8;
+  if (blocks > cap) blocks = cap;
+  hipLaunchKernelGGL(quantize_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, X, Q, n16,
+                     inv_scale);
+  return hipGetLastError();
+}
+
+hipError_t launch_pack_f8(const uint8_t* W1, const uint8_t* W2, uint8_t* W8, int N, int K,
+                          hipStream_t stream, int cu_count) {
+  const size_t runs = 2 * (size_t)N * (size_t)(K / 16);
+  if (runs == 0) return hipSuccess;
+  size_t blocks = (runs + 255) / 256;
+  const size_t cap = (size_t)(cu_count > 0 ? cu_count : 256) * 8;
+  if (blocks > cap) blocks = cap;
+  hipLaunchKernelGGL(pack_f8_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, W1, W2, W8, N,
+                     K);
   return hipGetLastError();
 }
 

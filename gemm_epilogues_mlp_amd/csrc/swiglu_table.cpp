@@ -62,6 +62,11 @@ int select_config(int variant, long long M, long long N, long long K, int cu_cou
   for (const ShapeEntry& e : kTable)
     if (e.variant == variant && e.M == M && e.N == N && e.K == K) return e.config_id;
   (void)N, (void)K, (void)cu_count;
+  if (variant == VAR_F8) {
+    // FP8: 64 x 128 tiles with a deep ring for small M, 128-row tiles around
+    // M = 256, the eight-wave 256 x 256 tiles with the split tail above
+    return M <= 192 ? 47 : (M <= 384 ? 45 : 43);
+  }
   if (M <= 64) {
     // decode-sized batches: split-K weight streaming, 16-row MFMA blocks
     const int mt = M <= 16 ? 1 : (M <= 32 ? 2 : 4);

@@ -81,14 +81,17 @@ typedef enum {
   SWIGLU_VARIANT_AUTO = 0,       /* table choice for the layout and shape      */
   SWIGLU_VARIANT_SYNC = 1,       /* Kernel-1 family: separate layout           */
   SWIGLU_VARIANT_INTERLEAVE = 2, /* Kernel-2 family: interleaved layout        */
-  SWIGLU_VARIANT_GEMM = 3        /* plain bf16 GEMM (unfused baseline only)    */
+  SWIGLU_VARIANT_GEMM = 3,       /* plain bf16 GEMM (unfused baseline only)    */
+  SWIGLU_VARIANT_FP8 = 4         /* Kernel-2 pairing on FP8 inputs
+                                    (swiglu_forward_fp8 only)                  */
 } swiglu_variant_t;
 
 /* Description of one compiled kernel configuration. */
 typedef struct swiglu_tile {
   int32_t id;          /* index in [0, swiglu_config_count())                */
-  int32_t variant;     /* swiglu_variant_t: SYNC, INTERLEAVE or GEMM          */
-  int32_t family;      /* 0 = LDS-tiled MFMA 32x32x16, 1 = split-K streaming
+  int32_t variant;     /* swiglu_variant_t: SYNC, INTERLEAVE, GEMM or FP8      */
+  int32_t family;      /* 0 = LDS-tiled MFMA 32x32x16 (FP8: 32x32x64 with
+                          unit block scales), 1 = split-K streaming
                           MFMA 16x16x32 (weights straight to registers),
                           2 = LDS-tiled with two wave groups alternating
                           MFMA and memory phases (ping-pong)                  */
@@ -167,7 +170,7 @@ swiglu_status_t swiglu_query_unfused(swiglu_handle_t h, int64_t M, int64_t N,
 /* Tuned per-shape configurations.  A tuned file (written by the package's
  * tuner, python -m gemm_epilogues_mlp_amd.tune) is text:
  *   swiglu-tuned <signature: 16 hex digits> <arch>        first non-comment line
- *   <variant 1|2|3> <M> <N> <K> <config id> [ignored provenance]   one per shape
+ *   <variant 1|2|3|4> <M> <N> <K> <config id> [ignored provenance]  one per shape
  * with '#' comment lines.  The signature (swiglu_config_signature) identifies
  * the list of compiled configurations; a file written for a library with a
  * different list is refused, so an id can never name the wrong kernel.
@@ -183,10 +186,54 @@ swiglu_status_t swiglu_tuned_check(const char* path, int32_t* n_entries);
 
 /* swiglu_create plus the entries of a tuned file (path NULL: none), which then
  * take precedence over the built-in table for their exact (variant, M, N, K)
- * in swiglu_forward, _ex with config_id < 0, _unfused and the queries.  The
+ * in swiglu_forward, _ex with config_id < 0, _unfused, _fp8 with config_id < 0
+ * and the queries.  The
  * file is read once here; the handle stays immutable.  Errors: those of
  * swiglu_tuned_check, then those of swiglu_create. */
 swiglu_status_t swiglu_create_tuned(swiglu_handle_t* out, int device, const char* path);
+
+/* ---- FP8 inputs -----------------------------------------------------------
+ * [RT §Definizione del Problema] names FP8 quantisation as what makes the
+ * memory-bound activation a larger share of the MLP, and the page
+ * "Ottimizzazione delle GEMM: la chiave per l'efficienza dei Large Language
+ * Models" (§Impatto sui deployment on-premise) benchmarks MXFP8 GEMMs; neither
+ * fixes the format.  Taken here: OCP FP8 E4M3 codes (one byte: sign, 4
+ * exponent bits with bias 7, 3 mantissa bits; no infinities; S.1111.111 is
+ * NaN; largest finite 448) with one fp32 scale per tensor, a code q standing
+ * for scale * value(q).
+ *   A8  [M, K]   E4M3 activations, row-major
+ *   W8  [2N, K]  E4M3 weights with k contiguous: row 2n is column n of W1
+ *                (Gate), row 2n+1 column n of W2 (Up) -- the Kernel-2 pairing
+ *                [RT §Metodologia], each W_fused column stored as a row
+ * The FP8 calls need N % 8 == 0, K % 16 == 0, 16-byte aligned pointers and
+ * tensors under 2 GiB (else UNSUPPORTED); otherwise the conventions above. */
+
+/* Y = bf16(SiLU(g) * u) with g = fp32(scale_a * scale_w1) * (A8 x W1) and
+ * u = fp32(scale_a * scale_w2) * (A8 x W2): the E4M3 products are exact and
+ * accumulate in fp32; the scales apply to the finished sums, before SiLU.
+ * config_id < 0 uses the table; a given id must be of variant FP8 (else
+ * INVALID_ARG).  Y must not overlap A8 or W8. */
+swiglu_status_t swiglu_forward_fp8(swiglu_handle_t h, const void* A8, const void* W8, void* Y,
+                                   int64_t M, int64_t N, int64_t K, float scale_a,
+                                   float scale_w1, float scale_w2, int32_t config_id,
+                                   hipStream_t stream);
+
+/* Q[i] = E4M3(fp32(X[i] * inv_scale)) for `count` bf16 values X: round to
+ * nearest even; magnitudes >= 448 and infinities saturate to +-448; NaN gives
+ * the NaN code; the sign of zero is kept.  count % 16 == 0; Q (count bytes)
+ * must not overlap X.  Quantises activations per forward or weights once. */
+swiglu_status_t swiglu_quantize_fp8(swiglu_handle_t h, const void* X, void* Q, int64_t count,
+                                    float inv_scale, hipStream_t stream);
+
+/* W8 [2N, K] from E4M3 W1, W2 [K, N] (row-major): W8[2n, k] = W1[k, n],
+ * W8[2n+1, k] = W2[k, n].  A bit copy done once per weight set.  W8 must not
+ * overlap W1 or W2. */
+swiglu_status_t swiglu_pack_fp8(swiglu_handle_t h, const void* W1, const void* W2, void* W8,
+                                int64_t K, int64_t N, hipStream_t stream);
+
+/* The configuration swiglu_forward_fp8 with config_id < 0 runs for a shape. */
+swiglu_status_t swiglu_query_fp8(swiglu_handle_t h, int64_t M, int64_t N, int64_t K,
+                                 swiglu_tile_t* tile);
 
 /* Number of compiled kernel configurations and their descriptions. */
 int32_t swiglu_config_count(void);

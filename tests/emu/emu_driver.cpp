@@ -106,6 +106,12 @@ bool run_config(int id, int M, int N, int K) {
     a.W2 = nullptr;
     a.ldw = N;
   }
+  if (c->variant == VAR_F8) {  // byte tensors: A8 [M, K], W8 [2N, K]
+    a.A = alloc16(((size_t)M * K + 1) / 2, "A8");
+    a.W1 = alloc16((size_t)N * K, "W8");
+    a.ldw = K;
+    a.scale_g = a.scale_u = 1.0f;
+  }
   a.Y = alloc16((size_t)M * N, "Y");
   a.ldy = N;
   a.group_m = 0;
@@ -129,6 +135,17 @@ bool run_elementwise(size_t n) {
   launch_gate(g, u, y, n, nullptr, 256);
   uint16_t* wf = alloc16(2 * n, "WF");
   launch_pack(g, u, wf, n, nullptr, 256);
+  free_all();
+  // FP8 quantisation (n bf16 -> n bytes) and the k-major pack of two [K, N]
+  // byte matrices (K = 16 rows, N = n / 16 columns)
+  uint16_t* x = alloc16(n, "X");
+  uint8_t* q = (uint8_t*)alloc16((n + 1) / 2, "Q");
+  launch_quantize_f8(x, q, n, 1.0f, nullptr, 256);
+  const int K = 16, N = (int)(n / 16);
+  uint8_t* w1 = (uint8_t*)alloc16((size_t)K * N / 2, "W1_8");
+  uint8_t* w2 = (uint8_t*)alloc16((size_t)K * N / 2, "W2_8");
+  uint8_t* w8 = (uint8_t*)alloc16((size_t)K * N, "W8");
+  launch_pack_f8(w1, w2, w8, N, K, nullptr, 256);
   free_all();
   printf("%s: %s\n", g_ctx.c_str(), g_errors == before ? "ok" : "OUT OF BOUNDS");
   return g_errors == before;
@@ -155,11 +172,16 @@ int main(int argc, char** argv) {
     for (int i = 0; i < config_count(); ++i) ids.push_back(i);
   // the GPU parity shapes (ragged tails in every dimension) and K = 0
   const int shapes[][3] = {{300, 264, 200}, {37, 136, 520}, {1, 8, 8}, {129, 520, 96}, {40, 72, 0}};
+  // FP8 tiles need K % 16 == 0: the same shapes with K rounded up to 16
+  const int shapes_f8[][3] = {{300, 264, 208}, {37, 136, 528}, {1, 8, 16}, {129, 520, 96}, {40, 72, 0}};
   for (int id : ids) {
     if (one_shape) {
       run_config(id, shape[0], shape[1], shape[2]);
     } else {
-      for (const auto& s : shapes) run_config(id, s[0], s[1], s[2]);
+      if (config_at(id) && config_at(id)->variant == VAR_F8)
+        for (const auto& s : shapes_f8) run_config(id, s[0], s[1], s[2]);
+      else
+        for (const auto& s : shapes) run_config(id, s[0], s[1], s[2]);
     }
   }
   if (!one_shape) {

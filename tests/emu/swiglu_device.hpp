@@ -187,6 +187,20 @@ inline void transpose8x8(const u32x4 row[8], u32x4 col[8]) {
 }
 inline f32x16 mfma32(const u32x4&, const u32x4&, const f32x16& c) { return c; }
 inline f32x4 mfma16(const u32x4&, const u32x4&, const f32x4& c) { return c; }
+inline f32x16 mfma32_f8(const u32x4 (&)[2], const u32x4 (&)[2], const f32x16& c) { return c; }
+inline uint32_t e4m3_code(float v) {
+  uint32_t bits;
+  memcpy(&bits, &v, 4);
+  const uint32_t sign = (bits >> 24) & 0x80u;
+  const float a = fabsf(v);
+  if (!(a == a)) return sign | 0x7Fu;
+  if (a >= 448.0f) return sign | 0x7Eu;
+  if (a < 0.015625f) return sign | (uint32_t)rintf(a * 512.0f);
+  uint32_t ab;
+  memcpy(&ab, &a, 4);
+  const int e = (int)((ab >> 23) & 0xffu) - 127;
+  return sign | ((uint32_t)((e + 7) << 3) + (uint32_t)rintf(ldexpf(a, 3 - e)) - 8u);
+}
 inline int xcd_remap(int b, int nwg) {
   const int q = nwg / 8, r = nwg % 8;
   const int x = b % 8, i = b / 8;
