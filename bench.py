@@ -23,6 +23,7 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense BF16 MFMA
 PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
+PEAK_FP8_TFLOPS = 5000.0   # MI355X dense FP8 MFMA
 METRIC = "fused SwiGLU GEMM TFLOP/s (bf16) and % MFMA peak, Qwen2.5-shaped MLPs"
 KERNEL_SRC = os.path.join(ROOT, "gemm_epilogues_mlp_amd", "csrc", "swiglu_kernels.hip")
 
@@ -43,6 +44,7 @@ def parse():
                    help="minimum footprint of the rotated buffers (bytes)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-unfused", action="store_true")
+    p.add_argument("--no-fp8", action="store_true", help="skip the FP8 (E4M3) side measurement")
     p.add_argument("--copy-calibration", action="store_true",
                    help="also run a 1 GiB device copy (counter calibration runs)")
     return p.parse_args()
@@ -163,6 +165,11 @@ def main():
                    "gemm_tile": sw.swiglu_query_unfused(h, M, N, K)}
         del usets, ws_buf
 
+    # ---- FP8 (E4M3) inputs, per-tensor scales: a side measurement ----------
+    fp8 = None
+    if not args.no_fp8:
+        fp8 = fp8_side(sw, h, wl, a_np, w1_np, w2_np, a0, w10, w20, timed, stream, args, ms)
+
     if args.copy_calibration:
         src = torch.empty(2 ** 30 // 2, dtype=torch.int16, device=dev)
         dst = torch.empty_like(src)
@@ -213,11 +220,63 @@ def main():
         "pct_mfma_peak": round(100 * tflops / PEAK_BF16_TFLOPS, 2),
         "hbm_gbs_algorithmic": round(hbm_gbs, 1),
         "unfused": unfused,
+        "fp8": fp8,
         "roofline": roofline,
         "cpu_baseline": cpu,
     }
     sw.swiglu_destroy(h)
     print(json.dumps(line), flush=True)
+
+
+def fp8_side(sw, h, wl, a_np, w1_np, w2_np, a0, w10, w20, timed, stream, args, bf16_ms):
+    """The same workload on FP8 inputs: A, W1 and W2 quantised on the device
+    (scale = max|x| / 448 per tensor), W1 and W2 packed k-major once, then
+    the fused FP8 forward timed like the bf16 one.  The per-forward cost of
+    quantising bf16 activations is timed separately."""
+    import numpy as np
+    import torch
+    from gemm_epilogues_mlp_amd import inputs as I
+    M, K, N = wl.M, wl.K, wl.N
+    dev = a0.device
+
+    def scale(bits):
+        amax = float(np.max(np.abs(I.bf16_bits_to_f32(bits))))
+        return float(np.float32(amax / 448.0)) if amax > 0 else 1.0
+
+    sa, s1, s2 = scale(a_np), scale(w1_np), scale(w2_np)
+    a8 = torch.empty((M, K), dtype=torch.uint8, device=dev)
+    w18 = torch.empty((K, N), dtype=torch.uint8, device=dev)
+    w28 = torch.empty_like(w18)
+    sw.swiglu_quantize_fp8(h, a0, a8, M * K, 1.0 / sa, stream)
+    sw.swiglu_quantize_fp8(h, w10, w18, K * N, 1.0 / s1, stream)
+    sw.swiglu_quantize_fp8(h, w20, w28, K * N, 1.0 / s2, stream)
+    w8 = torch.empty((2 * N, K), dtype=torch.uint8, device=dev)
+    sw.swiglu_pack_fp8(h, w18, w28, w8, K, N, stream)
+    del w18, w28
+    bytes8 = M * K + 2 * N * K + 2 * M * N
+    nsets = max(1, int(np.ceil(args.rotate_bytes / bytes8)))
+    sets = [(a8 if i == 0 else a8.clone(), w8 if i == 0 else w8.clone(),
+             torch.empty((M, N), dtype=torch.int16, device=dev)) for i in range(nsets)]
+    torch.cuda.synchronize()
+
+    def step(i):
+        a, w, y = sets[i % nsets]
+        sw.swiglu_forward_fp8(h, a, w, y, M, N, K, sa, s1, s2, -1, stream)
+
+    fms, batches = timed(step, args.steps, args.warmup)
+    qms, _ = timed(lambda i: sw.swiglu_quantize_fp8(h, a0, a8, M * K, 1.0 / sa, stream),
+                   max(10, args.steps // 2), 3, batches=1)
+    tf = wl.flops / (fms * 1e-3) / 1e12
+    out = {"ms_per_step": round(fms, 5), "tflops": round(tf, 2),
+           "pct_fp8_mfma_peak": round(100 * tf / PEAK_FP8_TFLOPS, 2),
+           "speedup_vs_bf16": round(bf16_ms / fms, 3),
+           "hbm_gbs_algorithmic": round(bytes8 / (fms * 1e-3) / 1e9, 1),
+           "min_batch_ms_per_step": round(min(batches), 5),
+           "quantize_activations_ms": round(qms, 5),
+           "format": "OCP E4M3, per-tensor fp32 scales", "rotated_sets": nsets,
+           "tile": sw.swiglu_query_fp8(h, M, N, K)}
+    del sets, a8, w8
+    return out
 
 
 def counter_traffic(workload, layout, tile):

@@ -358,6 +358,7 @@ swiglu_status_t swiglu_forward_fp8(swiglu_handle_t h, const void* A8, const void
   if (st != SWIGLU_OK) return st;
   if (id < 0) id = choose(h, VAR_F8, M, N, K);
   if (id < 0) return SWIGLU_ERR_UNSUPPORTED;
+  if (!config_fits(config_at(id), M)) return SWIGLU_ERR_UNSUPPORTED;
   LaunchArgs a;
   a.A = (const uint16_t*)A8;  // byte tensors; the FP8 launchers take them as such
   a.W1 = (const uint16_t*)W8;

@@ -200,6 +200,16 @@ __device__ __forceinline__ f32x16 mfma32_f8(const u32x4 (&a)[2], const u32x4 (&b
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(x, y, c, 0, 0, 0, 127, 0, 127);
 }
 
+// v_mfma_scale_f32_16x16x128_f8f6f4, E4M3 sources and unit block scales:
+// each source lane holds 32 bytes (one row or column, 32 of the 128 k); the
+// output layout is that of v_mfma_f32_16x16x32_bf16.
+__device__ __forceinline__ f32x4 mfma16_f8(const u32x4 (&a)[2], const u32x4 (&b)[2],
+                                           const f32x4& c) {
+  const i32x8 x = __builtin_bit_cast(i32x8, __builtin_shufflevector(a[0], a[1], 0, 1, 2, 3, 4, 5, 6, 7));
+  const i32x8 y = __builtin_bit_cast(i32x8, __builtin_shufflevector(b[0], b[1], 0, 1, 2, 3, 4, 5, 6, 7));
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(x, y, c, 0, 0, 0, 127, 0, 127);
+}
+
 // fp32 -> OCP E4M3 code, round to nearest even, saturating: |v| >= 448 (and
 // infinities) -> +-448, NaN -> S.1111.111; the sign of zero is kept.  Below
 // 2^-6 the codes count multiples of 2^-9; above, the 3-bit mantissa is the

@@ -1152,6 +1152,113 @@ __global__ __launch_bounds__(64 * WGM * WGN) void f8_split_kernel(
   }
 }
 
+// FP8 weight streaming for decode-sized batches (M <= 16 MT): split-K over
+// the waves of a workgroup, v_mfma_scale_f32_16x16x128_f8f6f4 with unit block
+// scales.  W8 is k-contiguous, so a weight fragment (16 W8 rows x 128 k) is
+// two plain 16-byte loads per lane straight from HBM into the MFMA source
+// registers -- no transposition, no LDS.  Lane l takes row l%16 and the
+// 16-byte chunks l/16 and 4 + l/16 of the step (one instruction reads 64
+// contiguous bytes of each row), the same for the activation rows.  Each
+// wave keeps the next step's loads in flight while it multiplies; the fp32
+// partial sums of the waves are added through LDS in a fixed order before
+// the scales and SiLU (the activation needs the complete sum).
+template <int MT, int NB, int NW>
+struct F8Skinny {
+  static constexpr int kThreads = 64 * NW;
+  static constexpr int SLAB_W = 16 * NB;  // W8 rows per workgroup
+  static constexpr int SLAB_Y = SLAB_W / 2;
+  static constexpr int LDS_BYTES = NW * MT * NB * 64 * 16;
+  static_assert(LDS_BYTES <= 160 * 1024, "LDS");
+};
+
+template <int MT, int NB, int NW>
+__global__ __launch_bounds__(64 * NW) void f8_skinny_kernel(const uint8_t* __restrict__ A,
+                                                             const uint8_t* __restrict__ W,
+                                                             uint16_t* __restrict__ Y, int M,
+                                                             int N, int K, float sg,
+                                                             float su) {
+  using C = F8Skinny<MT, NB, NW>;
+  __shared__ __attribute__((aligned(16))) f32x4 red[NW * MT * NB * 64];
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int slab = xcd_remap(blockIdx.x, gridDim.x);
+  const int m0 = blockIdx.y * MT * 16;
+  const int r16 = lane & 15, g = lane >> 4;
+
+  const int nsteps = (K + 127) / 128;
+  const int per = (nsteps + NW - 1) / NW;
+  const int s_begin = wave * per;
+  const int s_end = min(nsteps, s_begin + per);
+
+  // byte offsets of this lane's rows (k = 0); rows out of range load zeros
+  const int wrow0 = slab * C::SLAB_W + r16;
+  f32x4 acc[MT][NB];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int b = 0; b < NB; ++b) acc[mt][b] = f32x4{};
+
+  auto load = [&](int s, u32x4 (&wv)[NB][2], u32x4 (&av)[MT][2]) __attribute__((always_inline)) {
+    const int k0 = s * 128 + 16 * g, k1 = k0 + 64;
+    const bool in0 = k0 < K, in1 = k1 < K;  // K % 16 == 0: chunks are whole
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      const int row = wrow0 + 16 * b;
+      const bool ok = row < 2 * N;
+      const uint8_t* p = W + (size_t)row * K;
+      const u32x4 z{0, 0, 0, 0};
+      wv[b][0] = (ok && in0) ? (MT == 1 ? load16_stream(p + k0) : load16(p + k0)) : z;
+      wv[b][1] = (ok && in1) ? (MT == 1 ? load16_stream(p + k1) : load16(p + k1)) : z;
+    }
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      const int m = m0 + mt * 16 + r16;
+      const bool ok = m < M;
+      const uint8_t* p = A + (size_t)m * K;
+      av[mt][0] = (ok && in0) ? load16(p + k0) : u32x4{0, 0, 0, 0};
+      av[mt][1] = (ok && in1) ? load16(p + k1) : u32x4{0, 0, 0, 0};
+    }
+  };
+  auto mma = [&](const u32x4 (&wv)[NB][2], const u32x4 (&av)[MT][2]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int b = 0; b < NB; ++b)
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) acc[mt][b] = mfma16_f8(wv[b], av[mt], acc[mt][b]);
+  };
+
+  // two register sets: the loads of step s+1 are in flight while step s multiplies
+  u32x4 wa[NB][2], aa[MT][2], wb[NB][2], ab[MT][2];
+  int s = s_begin;
+  if (s < s_end) load(s, wa, aa);
+  for (; s < s_end; s += 2) {
+    if (s + 1 < s_end) load(s + 1, wb, ab);
+    mma(wa, aa);
+    if (s + 1 >= s_end) break;
+    if (s + 2 < s_end) load(s + 2, wa, aa);
+    mma(wb, ab);
+  }
+
+  // ---- split-K reduction through LDS (fixed order: wave 0, 1, ..., NW-1) ----
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int b = 0; b < NB; ++b) red[((wave * MT + mt) * NB + b) * 64 + lane] = acc[mt][b];
+  __syncthreads();
+  for (int q = wave; q < MT * NB; q += NW) {
+    const int mt = q / NB, b = q % NB;
+    f32x4 v = red[(mt * NB + b) * 64 + lane];
+    for (int w = 1; w < NW; ++w) v += red[((w * MT + mt) * NB + b) * 64 + lane];
+    // lane: A row r16 of the block, W8 rows 4g..4g+3 = (Gate, Up) of two columns
+    const int row = m0 + mt * 16 + r16;
+    const int col = slab * C::SLAB_Y + 8 * b + 2 * g;
+    if (row < M && col < N) {
+      const float y0 = silu(sg * v[0]) * (su * v[1]);
+      const float y1 = silu(sg * v[2]) * (su * v[3]);
+      *reinterpret_cast<uint32_t*>(Y + (size_t)row * N + col) = pack_bf16x2(y0, y1);
+    }
+  }
+}
+
 // bf16 -> E4M3 codes of fp32(x * inv_scale); 16 elements (32 B in, 16 B out)
 // per thread per iteration, grid-stride.
 __global__ __launch_bounds__(256) void quantize_kernel(const uint16_t* __restrict__ X,
@@ -1344,6 +1451,22 @@ static hipError_t launch_f8_split(const LaunchArgs& a) {
   return hipGetLastError();
 }
 
+template <int MT, int NB, int NW>
+static hipError_t launch_f8_skinny(const LaunchArgs& a) {
+  using C = F8Skinny<MT, NB, NW>;
+  const long long nslab = (2LL * a.N + C::SLAB_W - 1) / C::SLAB_W;
+  const long long nmb = (a.M + MT * 16 - 1) / (MT * 16);
+  if (nslab <= 0 || nmb <= 0) return hipSuccess;
+  if (nslab > 0x7fffffffLL || nmb > 65535) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((f8_skinny_kernel<MT, NB, NW>), dim3((unsigned)nslab, (unsigned)nmb),
+                     dim3(C::kThreads), 0, a.stream, (const uint8_t*)a.A, (const uint8_t*)a.W1,
+                     a.Y, a.M, a.N, a.K, a.scale_g, a.scale_u);
+  return hipGetLastError();
+}
+
+#define F8_SKINNY(mt, nb, nw)                                                              \
+  {VAR_F8, 1, (mt) * 16, F8Skinny<mt, nb, nw>::SLAB_Y, 128, nw, nw,                         \
+   F8Skinny<mt, nb, nw>::LDS_BYTES, &launch_f8_skinny<mt, nb, nw>}
 #define F8(bm, bnw, st, wgm, wgn)                                                          \
   {VAR_F8, 0, bm, F8Tiled<bm, bnw, st, wgm, wgn>::BNY, 64, (wgm) * (wgn), 1,               \
    F8Tiled<bm, bnw, st, wgm, wgn>::LDS_BYTES, &launch_f8<bm, bnw, st, wgm, wgn>}
@@ -1424,6 +1547,12 @@ static const KernelConfig kConfigs[] = {
     F8(128, 256, 4, 2, 2),                                          // 45
     F8(64, 128, 4, 2, 2),                                           // 46
     F8(64, 128, 8, 2, 2),                                           // 47
+    F8_SKINNY(1, 8, 4),                                             // 48
+    F8_SKINNY(1, 4, 4),                                             // 49
+    F8_SKINNY(2, 8, 4),                                             // 50
+    F8_SKINNY(4, 4, 4),                                             // 51
+    // one wave per workgroup, each streaming 32 W8 rows over the whole K
+    F8_SKINNY(1, 2, 1),                                             // 52
 };
 
 int config_count() { return (int)(sizeof(kConfigs) / sizeof(kConfigs[0])); }

@@ -63,9 +63,13 @@ int select_config(int variant, long long M, long long N, long long K, int cu_cou
     if (e.variant == variant && e.M == M && e.N == N && e.K == K) return e.config_id;
   (void)N, (void)K, (void)cu_count;
   if (variant == VAR_F8) {
-    // FP8: 64 x 128 tiles with a deep ring for small M, 128-row tiles around
-    // M = 256, the eight-wave 256 x 256 tiles with the split tail above
-    return M <= 192 ? 47 : (M <= 384 ? 45 : 43);
+    // FP8: split-K weight streaming up to M = 64, then 64 x 128 tiles, 128-row
+    // tiles around M = 256, and the eight-wave 256 x 256 tiles (split tail)
+    // (measured: M = 16 and 32 at K = 3584, N = 18944; M = 64 there and at
+    // K = 896, N = 4864; M = 128 at the 0.5B shape)
+    if (M <= 16) return 52;
+    if (M <= 32) return 51;
+    return M <= 192 ? 46 : (M <= 384 ? 45 : 43);
   }
   if (M <= 64) {
     // decode-sized batches: split-K weight streaming, 16-row MFMA blocks

@@ -188,6 +188,7 @@ inline void transpose8x8(const u32x4 row[8], u32x4 col[8]) {
 inline f32x16 mfma32(const u32x4&, const u32x4&, const f32x16& c) { return c; }
 inline f32x4 mfma16(const u32x4&, const u32x4&, const f32x4& c) { return c; }
 inline f32x16 mfma32_f8(const u32x4 (&)[2], const u32x4 (&)[2], const f32x16& c) { return c; }
+inline f32x4 mfma16_f8(const u32x4 (&)[2], const u32x4 (&)[2], const f32x4& c) { return c; }
 inline uint32_t e4m3_code(float v) {
   uint32_t bits;
   memcpy(&bits, &v, 4);

@@ -93,7 +93,7 @@ def test_config_list_is_consistent():
         if c["family"] in (0, 2):
             assert c["bm"] % 32 == 0 and c["bn"] % 32 == 0
         if c["variant"] == sw.VARIANT_FP8:
-            assert c["family"] == 0 and c["bk"] == 64
+            assert (c["family"], c["bk"]) in ((0, 64), (1, 128))
     assert all(v > 0 for v in seen.values())
 
 
