@@ -274,7 +274,7 @@ def fp8_side(sw, h, wl, a_np, w1_np, w2_np, a0, w10, w20, timed, stream, args, b
            "min_batch_ms_per_step": round(min(batches), 5),
            "quantize_activations_ms": round(qms, 5),
            "format": "OCP E4M3, per-tensor fp32 scales", "rotated_sets": nsets,
-           "tile": sw.swiglu_query_fp8(h, M, N, K)}
+           "tile": sw.swiglu_query_fp8(h, M, N, K, sw.VARIANT_AUTO)}
     del sets, a8, w8
     return out
 

@@ -25,6 +25,7 @@ __all__ = [
     "swiglu_forward_fp8", "swiglu_quantize_fp8", "swiglu_pack_fp8", "swiglu_query_fp8",
     "LAYOUT_SEPARATE", "LAYOUT_INTERLEAVED",
     "VARIANT_AUTO", "VARIANT_SYNC", "VARIANT_INTERLEAVE", "VARIANT_GEMM", "VARIANT_FP8",
+    "VARIANT_FP8_SYNC",
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -32,7 +33,8 @@ _LIB_PATH = os.path.join(_PKG, "libswiglu.so")
 
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_DEVICE, ERR_LAUNCH, ERR_ALLOC = range(6)
 LAYOUT_SEPARATE, LAYOUT_INTERLEAVED = 0, 1
-VARIANT_AUTO, VARIANT_SYNC, VARIANT_INTERLEAVE, VARIANT_GEMM, VARIANT_FP8 = 0, 1, 2, 3, 4
+VARIANT_AUTO, VARIANT_SYNC, VARIANT_INTERLEAVE, VARIANT_GEMM, VARIANT_FP8, VARIANT_FP8_SYNC = \
+    0, 1, 2, 3, 4, 5
 
 
 class SwiGLUError(RuntimeError):
@@ -92,10 +94,10 @@ def load():
         "swiglu_tuned_check": ([ctypes.c_char_p, ctypes.POINTER(i32)], st),
         "swiglu_create_tuned": ([ctypes.POINTER(p), ctypes.c_int, ctypes.c_char_p], st),
         "swiglu_forward_fp8": ([p, p, p, p, i64, i64, i64, ctypes.c_float, ctypes.c_float,
-                                ctypes.c_float, i32, p], st),
+                                ctypes.c_float, ctypes.c_int, i32, p], st),
         "swiglu_quantize_fp8": ([p, p, p, i64, ctypes.c_float, p], st),
         "swiglu_pack_fp8": ([p, p, p, p, i64, i64, p], st),
-        "swiglu_query_fp8": ([p, i64, i64, i64, ctypes.POINTER(Tile)], st),
+        "swiglu_query_fp8": ([p, i64, i64, i64, ctypes.c_int, ctypes.POINTER(Tile)], st),
     }
     for name, (args, res) in sig.items():
         fn = getattr(lib, name)
@@ -205,10 +207,10 @@ def swiglu_query_unfused(handle, M, N, K):
 
 
 def swiglu_forward_fp8(handle, A8, W8, Y, M, N, K, scale_a=1.0, scale_w1=1.0, scale_w2=1.0,
-                       config_id=-1, stream=None):
+                       config_id=-1, stream=None, variant=VARIANT_AUTO):
     """A8 [M, K] and W8 [2N, K] hold E4M3 codes (uint8 tensors); Y bf16 [M, N]."""
     _check(load().swiglu_forward_fp8(handle, _ptr(A8), _ptr(W8), _ptr(Y), M, N, K, scale_a,
-                                     scale_w1, scale_w2, config_id, _stream(stream)),
+                                     scale_w1, scale_w2, variant, config_id, _stream(stream)),
            "swiglu_forward_fp8")
 
 
@@ -222,9 +224,10 @@ def swiglu_pack_fp8(handle, W1, W2, W8, K, N, stream=None):
            "swiglu_pack_fp8")
 
 
-def swiglu_query_fp8(handle, M, N, K):
+def swiglu_query_fp8(handle, M, N, K, variant=VARIANT_AUTO):
     t = Tile()
-    _check(load().swiglu_query_fp8(handle, M, N, K, ctypes.byref(t)), "swiglu_query_fp8")
+    _check(load().swiglu_query_fp8(handle, M, N, K, variant, ctypes.byref(t)),
+           "swiglu_query_fp8")
     return t.as_dict()
 
 

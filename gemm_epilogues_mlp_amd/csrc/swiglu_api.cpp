@@ -211,6 +211,14 @@ void fill_tile(int id, swiglu_tile_t* t) {
   t->tail_split = c->tail_split;
 }
 
+// FP8 family of a public variant: AUTO and INTERLEAVE -> the interleave
+// kernels, SYNC -> the sync kernels; -1 for anything else
+int fp8_family(int variant) {
+  if (variant == SWIGLU_VARIANT_AUTO || variant == SWIGLU_VARIANT_INTERLEAVE) return VAR_F8;
+  if (variant == SWIGLU_VARIANT_SYNC) return VAR_F8_SYNC;
+  return -1;
+}
+
 }  // namespace
 
 extern "C" {
@@ -336,13 +344,15 @@ swiglu_status_t swiglu_pack_interleaved(swiglu_handle_t h, const void* W1, const
 
 swiglu_status_t swiglu_forward_fp8(swiglu_handle_t h, const void* A8, const void* W8, void* Y,
                                    int64_t M, int64_t N, int64_t K, float scale_a,
-                                   float scale_w1, float scale_w2, int32_t config_id,
-                                   hipStream_t stream) {
+                                   float scale_w1, float scale_w2, swiglu_variant_t variant,
+                                   int32_t config_id, hipStream_t stream) {
   if (!h || M < 0 || N < 0 || K < 0) return SWIGLU_ERR_INVALID_ARG;
+  const int want = fp8_family((int)variant);
+  if (want < 0) return SWIGLU_ERR_INVALID_ARG;
   int id = config_id;
   if (id >= 0) {
     const KernelConfig* c = config_at(id);
-    if (!c || c->variant != VAR_F8) return SWIGLU_ERR_INVALID_ARG;
+    if (!c || c->variant != want) return SWIGLU_ERR_INVALID_ARG;
   }
   if (M == 0 || N == 0) return SWIGLU_OK;
   if (!Y || (K > 0 && (!A8 || !W8))) return SWIGLU_ERR_INVALID_ARG;
@@ -356,7 +366,7 @@ swiglu_status_t swiglu_forward_fp8(swiglu_handle_t h, const void* A8, const void
     return SWIGLU_ERR_INVALID_ARG;
   swiglu_status_t st = check_device(h);
   if (st != SWIGLU_OK) return st;
-  if (id < 0) id = choose(h, VAR_F8, M, N, K);
+  if (id < 0) id = choose(h, want, M, N, K);
   if (id < 0) return SWIGLU_ERR_UNSUPPORTED;
   if (!config_fits(config_at(id), M)) return SWIGLU_ERR_UNSUPPORTED;
   LaunchArgs a;
@@ -413,9 +423,11 @@ swiglu_status_t swiglu_pack_fp8(swiglu_handle_t h, const void* W1, const void* W
 }
 
 swiglu_status_t swiglu_query_fp8(swiglu_handle_t h, int64_t M, int64_t N, int64_t K,
-                                 swiglu_tile_t* tile) {
+                                 swiglu_variant_t variant, swiglu_tile_t* tile) {
   if (!h || M < 0 || N < 0 || K < 0) return SWIGLU_ERR_INVALID_ARG;
-  const int id = choose(h, VAR_F8, M, N, K);
+  const int want = fp8_family((int)variant);
+  if (want < 0) return SWIGLU_ERR_INVALID_ARG;
+  const int id = choose(h, want, M, N, K);
   if (id < 0) return SWIGLU_ERR_UNSUPPORTED;
   if (tile) fill_tile(id, tile);
   return SWIGLU_OK;

@@ -7,8 +7,11 @@
 
 namespace swiglu {
 
-// VAR_F8: interleave pairing on FP8 (E4M3) inputs with k-contiguous weights
-enum Variant { VAR_AUTO = 0, VAR_SYNC = 1, VAR_INTERLEAVE = 2, VAR_GEMM = 3, VAR_F8 = 4 };
+// VAR_F8 / VAR_F8_SYNC: interleave / sync order on FP8 (E4M3) inputs with
+// k-contiguous paired weights
+enum Variant {
+  VAR_AUTO = 0, VAR_SYNC = 1, VAR_INTERLEAVE = 2, VAR_GEMM = 3, VAR_F8 = 4, VAR_F8_SYNC = 5
+};
 
 struct LaunchArgs {
   const uint16_t* A;

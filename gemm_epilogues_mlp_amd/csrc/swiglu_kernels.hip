@@ -885,7 +885,7 @@ void skinny_kernel(const uint16_t* __restrict__ A,
 }
 
 // ============================================================================
-// FP8 (OCP E4M3) inputs: LDS-tiled interleave kernel
+// FP8 (OCP E4M3) inputs: LDS-tiled interleave and sync kernels
 // ============================================================================
 // A8 [M, K] and W8 [2N, K] hold E4M3 codes with k contiguous in both; row 2n
 // of W8 is Gate column n and row 2n+1 Up column n (the Kernel-2 pairing of
@@ -906,15 +906,23 @@ void skinny_kernel(const uint16_t* __restrict__ A,
 // step as soon as its last MFMA is issued, and the activation fragments are
 // double-buffered by step parity (the stage ring has an even length, so the
 // parity is a compile-time constant of the unrolled ring).
-template <int BM, int BNW, int STAGES, int WGM, int WGN>
+//
+// The sync mode ([RT §Metodologia, Kernel-1]) reads the same W8: its tile
+// holds BNW output columns, the Gate phase streams W8 rows 2n (W1 columns)
+// and the Up phase rows 2n+1, each over the whole K; between the phases the
+// Gate accumulators are scaled and passed through SiLU in registers while
+// the first Up tiles are already in flight (the stage ring runs on across
+// the phase boundary).
+template <int MODE, int BM, int BNW, int STAGES, int WGM, int WGN>
 struct F8Tiled {
   static constexpr int kWaves = WGM * WGN;
   static_assert(kWaves == 4 || kWaves == 8, "four waves (one per SIMD) or eight (two per SIMD)");
   static constexpr int kThreads = 64 * kWaves;
   static constexpr int BK = 64;          // k per step = bytes per tile row
-  static constexpr int BNY = BNW / 2;    // output columns
+  static constexpr int BNY = MODE == MODE_SYNC ? BNW : BNW / 2;  // output columns
+  static constexpr int NACC = MODE == MODE_SYNC ? 2 : 1;           // accumulator sets
   static constexpr int WTM = BM / WGM;   // A rows per wave
-  static constexpr int WTW = BNW / WGN;  // W8 rows per wave
+  static constexpr int WTW = BNW / WGN;  // W8 rows per wave (per phase in sync mode)
   static constexpr int FA = WTM / 32;
   static constexpr int FW = WTW / 32;
   static_assert(FA >= 1 && FW >= 1 && WTM % 32 == 0 && WTW % 32 == 0, "wave tile");
@@ -941,19 +949,26 @@ struct F8Tiled {
   }
 };
 
-template <int BM, int BNW, int STAGES, int WGM, int WGN>
+template <int MODE, int BM, int BNW, int STAGES, int WGM, int WGN>
 __device__ __forceinline__ void f8_tile(const uint8_t* __restrict__ A,
                                         const uint8_t* __restrict__ W,
                                         uint16_t* __restrict__ Y, int M, int N, int K,
                                         float sg, float su, int m0, int tn, uint8_t* smem) {
-  using C = F8Tiled<BM, BNW, STAGES, WGM, WGN>;
+  using C = F8Tiled<MODE, BM, BNW, STAGES, WGM, WGN>;
+  static_assert(MODE == MODE_INTERLEAVE || MODE == MODE_SYNC, "FP8 modes");
+  constexpr bool kSync = MODE == MODE_SYNC;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int wm = wave / WGN, wn = wave % WGN;
-  const int wr0 = tn * BNW;  // first W8 row of the tile
+  const int wr0 = tn * BNW;  // first W8 row of the tile (interleave)
   const int y0 = tn * C::BNY;
+  // K steps: the sync mode runs them twice (Gate, then Up), its Gate phase
+  // padded with zero steps to a ring boundary (nk0) so that the Up phase
+  // starts on stage 0 with the same fragment-buffer parity
   const int nk = (K + C::BK - 1) / C::BK;
+  const int nk0 = kSync ? (nk + STAGES - 1) / STAGES * STAGES : nk;
+  const int total = kSync ? nk0 + nk : nk;
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
 
   // ---- DMA of one K step ----------------------------------------------------------
@@ -975,21 +990,25 @@ __device__ __forceinline__ void f8_tile(const uint8_t* __restrict__ A,
     a_off[i] = in ? (uint32_t)((size_t)(m0 + row) * K + c * 16) : 0u;
     a_k[i] = in ? (uint32_t)(c * 16) : kRowOut;
   }
+  // weight tile row r: W8 row wr0 + r (interleave), or 2 (y0 + r) + phase (sync)
   uint32_t w_off[C::W_LOADS], w_k[C::W_LOADS];
 #pragma unroll
   for (int i = 0; i < C::W_LOADS; ++i) {
     const int p = tid + C::kThreads * i;
     const int row = p / 4;
     const int c = (p % 4) ^ C::swz(row);
-    const bool in = wr0 + row < 2 * N;
-    w_off[i] = in ? (uint32_t)((size_t)(wr0 + row) * K + c * 16) : 0u;
+    const bool in = kSync ? y0 + row < N : wr0 + row < 2 * N;
+    const size_t wrow = kSync ? 2 * (size_t)(y0 + row) : (size_t)(wr0 + row);
+    w_off[i] = in ? (uint32_t)(wrow * K + c * 16) : 0u;
     w_k[i] = in ? (uint32_t)(c * 16) : kRowOut;
   }
   // DMA instruction q (A chunks first, then weight chunks) of K step `it`
-  // into stage ST; steps past the end load zeros (k0 = K)
+  // into stage ST; padding steps and steps past the end load zeros (k0 = K)
   auto dma = [&](int it, auto st_c, int q) __attribute__((always_inline)) {
     constexpr int ST = decltype(st_c)::value;
-    const uint32_t k0 = it < nk ? (uint32_t)it * C::BK : (uint32_t)K;
+    const bool up = kSync && it >= nk0;
+    const int kt = up ? it - nk0 : it;
+    const uint32_t k0 = (it < total && kt < nk) ? (uint32_t)kt * C::BK : (uint32_t)K;
     const uint32_t sbase = lds0 + ST * C::STAGE_BYTES;
     if (q < C::A_LOADS) {
       const int p0 = C::kThreads * q + 64 * wave_u;
@@ -1000,7 +1019,9 @@ __device__ __forceinline__ void f8_tile(const uint8_t* __restrict__ A,
       const int i = q - C::A_LOADS;
       const int p0 = C::kThreads * i + 64 * wave_u;
       const bool own = p0 < C::W_CHUNKS;
-      const uint32_t off = (own && k0 + w_k[i] < (uint32_t)K) ? w_off[i] + k0 : kOutOfRange;
+      const uint32_t off = (own && k0 + w_k[i] < (uint32_t)K)
+                               ? w_off[i] + (up ? (uint32_t)K : 0u) + k0
+                               : kOutOfRange;
       lds_dma16(own ? sbase + C::A_BYTES + p0 * 16 : lds0 + C::JUNK, off, rsW);
     }
   };
@@ -1016,11 +1037,13 @@ __device__ __forceinline__ void f8_tile(const uint8_t* __restrict__ A,
   };
   u32x4 wf[C::FW][2];
   u32x4 af[2][C::FA][2];
-  f32x16 acc[C::FW][C::FA];
+  f32x16 acc[C::NACC][C::FW][C::FA];
 #pragma unroll
-  for (int i = 0; i < C::FW; ++i)
+  for (int p = 0; p < C::NACC; ++p)
 #pragma unroll
-    for (int j = 0; j < C::FA; ++j) acc[i][j] = f32x16{};
+    for (int i = 0; i < C::FW; ++i)
+#pragma unroll
+      for (int j = 0; j < C::FA; ++j) acc[p][i][j] = f32x16{};
 
   // One K step on stage ST.  After the barrier, every wave has the loads of
   // step it+1 in LDS and has finished reading stage ST, so the MFMAs of step
@@ -1029,8 +1052,9 @@ __device__ __forceinline__ void f8_tile(const uint8_t* __restrict__ A,
   constexpr int NMF = C::FW * C::FA;
   constexpr int DBEGIN = NMF / 2;
   constexpr int DSLOTS = NMF - DBEGIN;
-  auto kstep = [&](int it, auto st_c) __attribute__((always_inline)) {
+  auto kstep = [&](int it, auto st_c, auto phase_c) __attribute__((always_inline)) {
     constexpr int ST = decltype(st_c)::value;
+    constexpr int PH = decltype(phase_c)::value;
     constexpr int P = ST & 1;
     using Next = std::integral_constant<int, (ST + 1) % STAGES>;
     const uint8_t* nxt = smem + Next::value * C::STAGE_BYTES;
@@ -1039,7 +1063,7 @@ __device__ __forceinline__ void f8_tile(const uint8_t* __restrict__ A,
 #pragma unroll
     for (int q = 0; q < NMF; ++q) {
       const int i = q / C::FA, j = q % C::FA;
-      acc[i][j] = mfma32_f8(wf[i], af[P][j], acc[i][j]);
+      acc[PH][i][j] = mfma32_f8(wf[i], af[P][j], acc[PH][i][j]);
       if (q < C::FA) read(nxt, a_row + 32 * q, af[P ^ 1][q]);
       if (j == C::FA - 1) read(nxt + C::A_BYTES, w_row + 32 * i, wf[i]);
       if (q >= DBEGIN) {
@@ -1051,14 +1075,15 @@ __device__ __forceinline__ void f8_tile(const uint8_t* __restrict__ A,
       __builtin_amdgcn_sched_barrier(0);
     }
   };
-  auto run = [&]() __attribute__((always_inline)) {
-    int it = 0;
-    for (; it + STAGES <= nk; it += STAGES)
+  // steps [b, e) with b on a ring boundary: whole rounds, then the rest
+  auto run = [&](int b, int e, auto phase_c) __attribute__((always_inline)) {
+    int it = b;
+    for (; it + STAGES <= e; it += STAGES)
       [&]<int... S>(std::integer_sequence<int, S...>) __attribute__((always_inline)) {
-        (kstep(it + S, std::integral_constant<int, S>{}), ...);
+        (kstep(it + S, std::integral_constant<int, S>{}, phase_c), ...);
       }(std::make_integer_sequence<int, STAGES>{});
     [&]<int... S>(std::integer_sequence<int, S...>) __attribute__((always_inline)) {
-      ((it + S < nk ? (kstep(it + S, std::integral_constant<int, S>{}), 0) : 0), ...);
+      ((it + S < e ? (kstep(it + S, std::integral_constant<int, S>{}, phase_c), 0) : 0), ...);
     }(std::make_integer_sequence<int, STAGES - 1>{});
   };
 
@@ -1078,7 +1103,19 @@ __device__ __forceinline__ void f8_tile(const uint8_t* __restrict__ A,
 #pragma unroll
   for (int i = 0; i < C::FW; ++i) read(smem + C::A_BYTES, w_row + 32 * i, wf[i]);
 
-  run();
+  if constexpr (kSync) {
+    run(0, nk0, std::integral_constant<int, 0>{});
+    // Gate finished: scale and SiLU in registers while Up tiles are in flight
+#pragma unroll
+    for (int i = 0; i < C::FW; ++i)
+#pragma unroll
+      for (int j = 0; j < C::FA; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[0][i][j][r] = silu(sg * acc[0][i][j][r]);
+    run(nk0, total, std::integral_constant<int, 1>{});
+  } else {
+    run(0, total, std::integral_constant<int, 0>{});
+  }
 
   // ---- epilogue: scales, SiLU(Gate) * Up, bf16 tile through LDS, row stores -------
   wait_vmcnt<0>();
@@ -1089,14 +1126,25 @@ __device__ __forceinline__ void f8_tile(const uint8_t* __restrict__ A,
 #pragma unroll
     for (int j = 0; j < C::FA; ++j) {
       const int row = a_row + j * 32;
-      const f32x16& d = acc[i][j];
+      const f32x16& d = acc[0][i][j];
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        // registers 4q..4q+3: W8 rows wcl..wcl+3 = Gate/Up of columns wcl/2, wcl/2+1
+        // registers 4q..4q+3: weight tile rows wcl..wcl+3
         const int wcl = wn * C::WTW + i * 32 + 8 * q + 4 * h;
-        const float ya = silu(sg * d[4 * q + 0]) * (su * d[4 * q + 1]);
-        const float yb = silu(sg * d[4 * q + 2]) * (su * d[4 * q + 3]);
-        *reinterpret_cast<uint32_t*>(ys + row * C::YLD + wcl / 2) = pack_bf16x2(ya, yb);
+        if constexpr (kSync) {
+          // output columns wcl..wcl+3: SiLU(Gate) (already applied) * Up
+          const f32x16& u = acc[C::NACC - 1][i][j];
+          float y[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) y[e] = d[4 * q + e] * (su * u[4 * q + e]);
+          *reinterpret_cast<u32x2*>(ys + row * C::YLD + wcl) =
+              u32x2{pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3])};
+        } else {
+          // W8 rows wcl..wcl+3 = Gate/Up of output columns wcl/2, wcl/2+1
+          const float ya = silu(sg * d[4 * q + 0]) * (su * d[4 * q + 1]);
+          const float yb = silu(sg * d[4 * q + 2]) * (su * d[4 * q + 3]);
+          *reinterpret_cast<uint32_t*>(ys + row * C::YLD + wcl / 2) = pack_bf16x2(ya, yb);
+        }
       }
     }
   __syncthreads();
@@ -1110,29 +1158,29 @@ __device__ __forceinline__ void f8_tile(const uint8_t* __restrict__ A,
   }
 }
 
-template <int BM, int BNW, int STAGES, int WGM, int WGN>
+template <int MODE, int BM, int BNW, int STAGES, int WGM, int WGN>
 __global__ __launch_bounds__(64 * WGM * WGN) void f8_kernel(const uint8_t* __restrict__ A,
                                                              const uint8_t* __restrict__ W,
                                                              uint16_t* __restrict__ Y, int M,
                                                              int N, int K, float sg, float su,
                                                              int group_m) {
-  using C = F8Tiled<BM, BNW, STAGES, WGM, WGN>;
+  using C = F8Tiled<MODE, BM, BNW, STAGES, WGM, WGN>;
   __shared__ __attribute__((aligned(1024))) uint8_t smem[C::LDS_BYTES];
   const int ntm = (M + BM - 1) / BM;
   const int ntn = (N + C::BNY - 1) / C::BNY;
   int tm, tn;
   tile_of(xcd_remap(blockIdx.x, gridDim.x), ntm, ntn, group_m, tm, tn);
-  f8_tile<BM, BNW, STAGES, WGM, WGN>(A, W, Y, M, N, K, sg, su, tm * BM, tn, smem);
+  f8_tile<MODE, BM, BNW, STAGES, WGM, WGN>(A, W, Y, M, N, K, sg, su, tm * BM, tn, smem);
 }
 
 // The split tail of tiled_split_kernel for the FP8 tiles: workgroups
 // [0, n_big) take whole tiles, the rest quarter tiles of the partial last round.
-template <int BM, int BNW, int STAGES, int WGM, int WGN, int SWGM, int SWGN>
+template <int MODE, int BM, int BNW, int STAGES, int WGM, int WGN, int SWGM, int SWGN>
 __global__ __launch_bounds__(64 * WGM * WGN) void f8_split_kernel(
     const uint8_t* __restrict__ A, const uint8_t* __restrict__ W, uint16_t* __restrict__ Y,
     int M, int N, int K, float sg, float su, int group_m, int n_big) {
-  using Big = F8Tiled<BM, BNW, STAGES, WGM, WGN>;
-  using Small = F8Tiled<BM / 2, BNW / 2, STAGES, SWGM, SWGN>;
+  using Big = F8Tiled<MODE, BM, BNW, STAGES, WGM, WGN>;
+  using Small = F8Tiled<MODE, BM / 2, BNW / 2, STAGES, SWGM, SWGN>;
   static_assert(Big::kThreads == Small::kThreads, "one workgroup size for both tile kinds");
   constexpr int LDS = Big::LDS_BYTES > Small::LDS_BYTES ? Big::LDS_BYTES : Small::LDS_BYTES;
   __shared__ __attribute__((aligned(1024))) uint8_t smem[LDS];
@@ -1141,14 +1189,14 @@ __global__ __launch_bounds__(64 * WGM * WGN) void f8_split_kernel(
   int tm, tn;
   if ((int)blockIdx.x < n_big) {
     tile_of(xcd_remap(blockIdx.x, n_big), ntm, ntn, group_m, tm, tn);
-    f8_tile<BM, BNW, STAGES, WGM, WGN>(A, W, Y, M, N, K, sg, su, tm * BM, tn, smem);
+    f8_tile<MODE, BM, BNW, STAGES, WGM, WGN>(A, W, Y, M, N, K, sg, su, tm * BM, tn, smem);
   } else {
     const int u = blockIdx.x - n_big, q = u & 3;
     tile_of(n_big + u / 4, ntm, ntn, group_m, tm, tn);
     const int m0 = tm * BM + (q >> 1) * (BM / 2);
     const int tq = 2 * tn + (q & 1);
     if (m0 >= M || tq * Small::BNY >= N) return;
-    f8_tile<BM / 2, BNW / 2, STAGES, SWGM, SWGN>(A, W, Y, M, N, K, sg, su, m0, tq, smem);
+    f8_tile<MODE, BM / 2, BNW / 2, STAGES, SWGM, SWGN>(A, W, Y, M, N, K, sg, su, m0, tq, smem);
   }
 }
 
@@ -1417,34 +1465,34 @@ static hipError_t launch_skinny(const LaunchArgs& a) {
   return hipGetLastError();
 }
 
-template <int BM, int BNW, int STAGES, int WGM, int WGN>
+template <int MODE, int BM, int BNW, int STAGES, int WGM, int WGN>
 static hipError_t launch_f8(const LaunchArgs& a) {
-  using C = F8Tiled<BM, BNW, STAGES, WGM, WGN>;
+  using C = F8Tiled<MODE, BM, BNW, STAGES, WGM, WGN>;
   const int ntm = (a.M + BM - 1) / BM, ntn = (a.N + C::BNY - 1) / C::BNY;
   const long long nwg = (long long)ntm * ntn;
   if (nwg <= 0) return hipSuccess;
   if (nwg > 0x7fffffffLL) return hipErrorInvalidValue;
   int group_m = a.group_m > 0 ? a.group_m : 8;
   if (group_m > ntm) group_m = ntm;
-  hipLaunchKernelGGL((f8_kernel<BM, BNW, STAGES, WGM, WGN>), dim3((unsigned)nwg),
+  hipLaunchKernelGGL((f8_kernel<MODE, BM, BNW, STAGES, WGM, WGN>), dim3((unsigned)nwg),
                      dim3(C::kThreads), 0, a.stream, (const uint8_t*)a.A,
                      (const uint8_t*)a.W1, a.Y, a.M, a.N, a.K, a.scale_g, a.scale_u, group_m);
   return hipGetLastError();
 }
 
-template <int BM, int BNW, int STAGES, int WGM, int WGN, int SWGM, int SWGN>
+template <int MODE, int BM, int BNW, int STAGES, int WGM, int WGN, int SWGM, int SWGN>
 static hipError_t launch_f8_split(const LaunchArgs& a) {
-  using C = F8Tiled<BM, BNW, STAGES, WGM, WGN>;
+  using C = F8Tiled<MODE, BM, BNW, STAGES, WGM, WGN>;
   const int ntm = (a.M + BM - 1) / BM, ntn = (a.N + C::BNY - 1) / C::BNY;
   const long long nt = (long long)ntm * ntn;
   if (nt <= 0) return hipSuccess;
   if (4 * nt > 0x7fffffffLL) return hipErrorInvalidValue;
   const long long slots = a.cu_count > 0 ? a.cu_count : 256;
   const long long n_big = nt / slots * slots, tail = nt - n_big;
-  if (tail == 0 || 4 * tail > slots) return launch_f8<BM, BNW, STAGES, WGM, WGN>(a);
+  if (tail == 0 || 4 * tail > slots) return launch_f8<MODE, BM, BNW, STAGES, WGM, WGN>(a);
   int group_m = a.group_m > 0 ? a.group_m : 8;
   if (group_m > ntm) group_m = ntm;
-  hipLaunchKernelGGL((f8_split_kernel<BM, BNW, STAGES, WGM, WGN, SWGM, SWGN>),
+  hipLaunchKernelGGL((f8_split_kernel<MODE, BM, BNW, STAGES, WGM, WGN, SWGM, SWGN>),
                      dim3((unsigned)(n_big + 4 * tail)), dim3(C::kThreads), 0, a.stream,
                      (const uint8_t*)a.A, (const uint8_t*)a.W1, a.Y, a.M, a.N, a.K, a.scale_g,
                      a.scale_u, group_m, (int)n_big);
@@ -1467,13 +1515,13 @@ static hipError_t launch_f8_skinny(const LaunchArgs& a) {
 #define F8_SKINNY(mt, nb, nw)                                                              \
   {VAR_F8, 1, (mt) * 16, F8Skinny<mt, nb, nw>::SLAB_Y, 128, nw, nw,                         \
    F8Skinny<mt, nb, nw>::LDS_BYTES, &launch_f8_skinny<mt, nb, nw>}
-#define F8(bm, bnw, st, wgm, wgn)                                                          \
-  {VAR_F8, 0, bm, F8Tiled<bm, bnw, st, wgm, wgn>::BNY, 64, (wgm) * (wgn), 1,               \
-   F8Tiled<bm, bnw, st, wgm, wgn>::LDS_BYTES, &launch_f8<bm, bnw, st, wgm, wgn>}
-#define F8_SPLIT(bm, bnw, st, wgm, wgn, swgm, swgn)                                        \
-  {VAR_F8, 0, bm, F8Tiled<bm, bnw, st, wgm, wgn>::BNY, 64, (wgm) * (wgn), 1,               \
-   F8Tiled<bm, bnw, st, wgm, wgn>::LDS_BYTES,                                              \
-   &launch_f8_split<bm, bnw, st, wgm, wgn, swgm, swgn>, 4}
+#define F8(mode, v, bm, bnw, st, wgm, wgn)                                                 \
+  {v, 0, bm, F8Tiled<mode, bm, bnw, st, wgm, wgn>::BNY, 64, (wgm) * (wgn), 1,              \
+   F8Tiled<mode, bm, bnw, st, wgm, wgn>::LDS_BYTES, &launch_f8<mode, bm, bnw, st, wgm, wgn>}
+#define F8_SPLIT(mode, v, bm, bnw, st, wgm, wgn, swgm, swgn)                               \
+  {v, 0, bm, F8Tiled<mode, bm, bnw, st, wgm, wgn>::BNY, 64, (wgm) * (wgn), 1,              \
+   F8Tiled<mode, bm, bnw, st, wgm, wgn>::LDS_BYTES,                                        \
+   &launch_f8_split<mode, bm, bnw, st, wgm, wgn, swgm, swgn>, 4}
 #define TILED(mode, v, bm, bnw, bk, st, wgm, wgn)                                          \
   {v, 0, bm, Tiled<mode, bm, bnw, bk, st, wgm, wgn>::BNY, bk, (wgm) * (wgn), 1,             \
    Tiled<mode, bm, bnw, bk, st, wgm, wgn>::LDS_BYTES, &launch_tiled<mode, bm, bnw, bk, st, wgm, wgn>}
@@ -1542,17 +1590,21 @@ static const KernelConfig kConfigs[] = {
     TILED_SPLIT(MODE_GEMM, VAR_GEMM, 256, 256, 32, 4, 4, 2, 2, 4),              // 41
     TILED_SPLIT(MODE_SYNC, VAR_SYNC, 256, 128, 32, 4, 4, 2, 4, 2),              // 42
     // ---- FP8 (E4M3) inputs, k-contiguous paired weights ----------------------
-    F8_SPLIT(256, 256, 4, 4, 2, 2, 4),                              // 43
-    F8(256, 256, 4, 4, 2),                                          // 44
-    F8(128, 256, 4, 2, 2),                                          // 45
-    F8(64, 128, 4, 2, 2),                                           // 46
-    F8(64, 128, 8, 2, 2),                                           // 47
+    F8_SPLIT(MODE_INTERLEAVE, VAR_F8, 256, 256, 4, 4, 2, 2, 4),     // 43
+    F8(MODE_INTERLEAVE, VAR_F8, 256, 256, 4, 4, 2),                 // 44
+    F8(MODE_INTERLEAVE, VAR_F8, 128, 256, 4, 2, 2),                 // 45
+    F8(MODE_INTERLEAVE, VAR_F8, 64, 128, 4, 2, 2),                  // 46
+    F8(MODE_INTERLEAVE, VAR_F8, 64, 128, 8, 2, 2),                  // 47
     F8_SKINNY(1, 8, 4),                                             // 48
     F8_SKINNY(1, 4, 4),                                             // 49
     F8_SKINNY(2, 8, 4),                                             // 50
     F8_SKINNY(4, 4, 4),                                             // 51
     // one wave per workgroup, each streaming 32 W8 rows over the whole K
     F8_SKINNY(1, 2, 1),                                             // 52
+    // ---- FP8 sync (Kernel-1 order) on the same W8 ----------------------------
+    F8_SPLIT(MODE_SYNC, VAR_F8_SYNC, 256, 128, 4, 4, 2, 4, 2),      // 53
+    F8(MODE_SYNC, VAR_F8_SYNC, 128, 128, 4, 2, 2),                  // 54
+    F8(MODE_SYNC, VAR_F8_SYNC, 64, 64, 4, 2, 2),                    // 55
 };
 
 int config_count() { return (int)(sizeof(kConfigs) / sizeof(kConfigs[0])); }

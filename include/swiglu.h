@@ -82,14 +82,17 @@ typedef enum {
   SWIGLU_VARIANT_SYNC = 1,       /* Kernel-1 family: separate layout           */
   SWIGLU_VARIANT_INTERLEAVE = 2, /* Kernel-2 family: interleaved layout        */
   SWIGLU_VARIANT_GEMM = 3,       /* plain bf16 GEMM (unfused baseline only)    */
-  SWIGLU_VARIANT_FP8 = 4         /* Kernel-2 pairing on FP8 inputs
-                                    (swiglu_forward_fp8 only)                  */
+  SWIGLU_VARIANT_FP8 = 4,        /* config descriptions: Kernel-2 order on FP8
+                                    inputs (swiglu_forward_fp8, INTERLEAVE)    */
+  SWIGLU_VARIANT_FP8_SYNC = 5    /* config descriptions: Kernel-1 order on FP8
+                                    inputs (swiglu_forward_fp8, SYNC)          */
 } swiglu_variant_t;
 
 /* Description of one compiled kernel configuration. */
 typedef struct swiglu_tile {
   int32_t id;          /* index in [0, swiglu_config_count())                */
-  int32_t variant;     /* swiglu_variant_t: SYNC, INTERLEAVE, GEMM or FP8      */
+  int32_t variant;     /* swiglu_variant_t: SYNC, INTERLEAVE, GEMM, FP8 or
+                          FP8_SYNC                                            */
   int32_t family;      /* 0 = LDS-tiled MFMA 32x32x16 (FP8: 32x32x64 with
                           unit block scales), 1 = split-K streaming
                           MFMA 16x16x32 (weights straight to registers),
@@ -170,7 +173,7 @@ swiglu_status_t swiglu_query_unfused(swiglu_handle_t h, int64_t M, int64_t N,
 /* Tuned per-shape configurations.  A tuned file (written by the package's
  * tuner, python -m gemm_epilogues_mlp_amd.tune) is text:
  *   swiglu-tuned <signature: 16 hex digits> <arch>        first non-comment line
- *   <variant 1|2|3|4> <M> <N> <K> <config id> [ignored provenance]  one per shape
+ *   <variant 1..5> <M> <N> <K> <config id> [ignored provenance]    one per shape
  * with '#' comment lines.  The signature (swiglu_config_signature) identifies
  * the list of compiled configurations; a file written for a library with a
  * different list is refused, so an id can never name the wrong kernel.
@@ -211,12 +214,17 @@ swiglu_status_t swiglu_create_tuned(swiglu_handle_t* out, int device, const char
 /* Y = bf16(SiLU(g) * u) with g = fp32(scale_a * scale_w1) * (A8 x W1) and
  * u = fp32(scale_a * scale_w2) * (A8 x W2): the E4M3 products are exact and
  * accumulate in fp32; the scales apply to the finished sums, before SiLU.
- * config_id < 0 uses the table; a given id must be of variant FP8 (else
- * INVALID_ARG).  Y must not overlap A8 or W8. */
+ * Both kernel orders read the same W8: variant INTERLEAVE (or AUTO) runs one
+ * GEMM over the paired rows with the pair-multiply epilogue [RT §Metodologia,
+ * Kernel-2]; SYNC runs the Gate rows over the whole K, applies SiLU in
+ * registers while the Up tiles load, then the Up rows [RT §Metodologia,
+ * Kernel-1]; any other variant is INVALID_ARG.  config_id < 0 uses the table;
+ * a given id must be of variant FP8 (INTERLEAVE) or FP8_SYNC (SYNC), else
+ * INVALID_ARG.  Y must not overlap A8 or W8. */
 swiglu_status_t swiglu_forward_fp8(swiglu_handle_t h, const void* A8, const void* W8, void* Y,
                                    int64_t M, int64_t N, int64_t K, float scale_a,
-                                   float scale_w1, float scale_w2, int32_t config_id,
-                                   hipStream_t stream);
+                                   float scale_w1, float scale_w2, swiglu_variant_t variant,
+                                   int32_t config_id, hipStream_t stream);
 
 /* Q[i] = E4M3(fp32(X[i] * inv_scale)) for `count` bf16 values X: round to
  * nearest even; magnitudes >= 448 and infinities saturate to +-448; NaN gives
@@ -231,9 +239,10 @@ swiglu_status_t swiglu_quantize_fp8(swiglu_handle_t h, const void* X, void* Q, i
 swiglu_status_t swiglu_pack_fp8(swiglu_handle_t h, const void* W1, const void* W2, void* W8,
                                 int64_t K, int64_t N, hipStream_t stream);
 
-/* The configuration swiglu_forward_fp8 with config_id < 0 runs for a shape. */
+/* The configuration swiglu_forward_fp8 with config_id < 0 runs for a shape
+ * and variant (AUTO, INTERLEAVE or SYNC). */
 swiglu_status_t swiglu_query_fp8(swiglu_handle_t h, int64_t M, int64_t N, int64_t K,
-                                 swiglu_tile_t* tile);
+                                 swiglu_variant_t variant, swiglu_tile_t* tile);
 
 /* Number of compiled kernel configurations and their descriptions. */
 int32_t swiglu_config_count(void);

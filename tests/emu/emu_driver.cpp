@@ -106,7 +106,7 @@ bool run_config(int id, int M, int N, int K) {
     a.W2 = nullptr;
     a.ldw = N;
   }
-  if (c->variant == VAR_F8) {  // byte tensors: A8 [M, K], W8 [2N, K]
+  if (c->variant == VAR_F8 || c->variant == VAR_F8_SYNC) {  // byte tensors: A8 [M, K], W8 [2N, K]
     a.A = alloc16(((size_t)M * K + 1) / 2, "A8");
     a.W1 = alloc16((size_t)N * K, "W8");
     a.ldw = K;
@@ -178,7 +178,7 @@ int main(int argc, char** argv) {
     if (one_shape) {
       run_config(id, shape[0], shape[1], shape[2]);
     } else {
-      if (config_at(id) && config_at(id)->variant == VAR_F8)
+      if (config_at(id) && (config_at(id)->variant == VAR_F8 || config_at(id)->variant == VAR_F8_SYNC))
         for (const auto& s : shapes_f8) run_config(id, s[0], s[1], s[2]);
       else
         for (const auto& s : shapes) run_config(id, s[0], s[1], s[2]);

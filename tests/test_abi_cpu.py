@@ -61,11 +61,11 @@ def test_null_handle_and_bad_arguments_rejected():
     assert lib.swiglu_destroy(None) == sw.OK
     assert lib.swiglu_config_info(-1, None) == sw.ERR_INVALID_ARG
     assert lib.swiglu_config_info(sw.swiglu_config_count(), None) == sw.ERR_INVALID_ARG
-    assert lib.swiglu_forward_fp8(None, 16, 16, 16, 8, 8, 16, 1.0, 1.0, 1.0, -1, None) == \
+    assert lib.swiglu_forward_fp8(None, 16, 16, 16, 8, 8, 16, 1.0, 1.0, 1.0, 0, -1, None) == \
         sw.ERR_INVALID_ARG
     assert lib.swiglu_quantize_fp8(None, 16, 16, 16, 1.0, None) == sw.ERR_INVALID_ARG
     assert lib.swiglu_pack_fp8(None, 16, 16, 16, 16, 8, None) == sw.ERR_INVALID_ARG
-    assert lib.swiglu_query_fp8(None, 8, 8, 16, None) == sw.ERR_INVALID_ARG
+    assert lib.swiglu_query_fp8(None, 8, 8, 16, 0, None) == sw.ERR_INVALID_ARG
 
 
 def test_status_strings_and_workspace_size():
@@ -78,7 +78,8 @@ def test_status_strings_and_workspace_size():
 def test_config_list_is_consistent():
     n = sw.swiglu_config_count()
     assert n > 0
-    seen = {sw.VARIANT_SYNC: 0, sw.VARIANT_INTERLEAVE: 0, sw.VARIANT_GEMM: 0, sw.VARIANT_FP8: 0}
+    seen = {sw.VARIANT_SYNC: 0, sw.VARIANT_INTERLEAVE: 0, sw.VARIANT_GEMM: 0, sw.VARIANT_FP8: 0,
+            sw.VARIANT_FP8_SYNC: 0}
     for i in range(n):
         c = sw.swiglu_config_info(i)
         assert c["id"] == i
@@ -92,7 +93,7 @@ def test_config_list_is_consistent():
         assert c["waves"] * 64 <= 1024
         if c["family"] in (0, 2):
             assert c["bm"] % 32 == 0 and c["bn"] % 32 == 0
-        if c["variant"] == sw.VARIANT_FP8:
+        if c["variant"] in (sw.VARIANT_FP8, sw.VARIANT_FP8_SYNC):
             assert (c["family"], c["bk"]) in ((0, 64), (1, 128))
     assert all(v > 0 for v in seen.values())
 

@@ -2,9 +2,10 @@
 
 * quantisation: every bf16 bit pattern, several scales, bit for bit;
 * the k-major Gate/Up pack: bit for bit;
-* the forward: every FP8 configuration on seeded shapes with ragged tails in
-  M, N and K, a launch that exercises the split tail, K = 0, and the five
-  Qwen2.5-shaped workloads at full size in the table's configuration (the
+* the forward, in both kernel orders (interleave and sync, on the same W8):
+  every FP8 configuration on seeded shapes with ragged tails in M, N and K,
+  launches that exercise the split tail, K = 0, and the five Qwen2.5-shaped
+  workloads at full size in the table's configuration (the
   whole Y checked for unwritten or non-finite elements, sampled rows against
   the oracle).  Bar: |y - y_ref| <= 0.01 |y_ref| + 2^-10 against the oracle's
   fp32 value computed from the same E4M3 codes and scales.
@@ -62,10 +63,18 @@ def fp8_inputs(M, N, K, seed):
     return a8, w18, w28, sa, s1, s2
 
 
-def forward(handle, a8, w8, M, N, K, scales, cfg=-1):
+def variant_of(cfg):
+    return sw.VARIANT_SYNC if sw.swiglu_config_info(cfg)["variant"] == sw.VARIANT_FP8_SYNC \
+        else sw.VARIANT_INTERLEAVE
+
+
+def forward(handle, a8, w8, M, N, K, scales, cfg=-1, variant=sw.VARIANT_AUTO):
     t = torch()
     y = empty_poisoned((M, N))
-    sw.swiglu_forward_fp8(handle, dev8(a8), dev8(w8), y, M, N, K, *scales, config_id=cfg)
+    if cfg >= 0:
+        variant = variant_of(cfg)
+    sw.swiglu_forward_fp8(handle, dev8(a8), dev8(w8), y, M, N, K, *scales, config_id=cfg,
+                          variant=variant)
     t.cuda.synchronize()
     return host(y)
 
@@ -124,7 +133,7 @@ SHAPES = [
 
 def fp8_configs():
     return [i for i in range(sw.swiglu_config_count())
-            if sw.swiglu_config_info(i)["variant"] == sw.VARIANT_FP8]
+            if sw.swiglu_config_info(i)["variant"] in (sw.VARIANT_FP8, sw.VARIANT_FP8_SYNC)]
 
 
 @pytest.fixture(scope="module")
@@ -181,6 +190,18 @@ def test_fp8_k_zero_and_errors(handle):
     with pytest.raises(sw.SwiGLUError) as e:               # a bf16 config id
         sw.swiglu_forward_fp8(handle, a, w, y, M, N, 16, config_id=0)
     assert e.value.status == sw.ERR_INVALID_ARG
+    sync_cfg = [i for i in fp8_configs() if variant_of(i) == sw.VARIANT_SYNC][0]
+    with pytest.raises(sw.SwiGLUError) as e:               # a sync config, interleave order
+        sw.swiglu_forward_fp8(handle, a, w, y, M, N, 16, config_id=sync_cfg,
+                              variant=sw.VARIANT_INTERLEAVE)
+    assert e.value.status == sw.ERR_INVALID_ARG
+    with pytest.raises(sw.SwiGLUError) as e:               # not an FP8 order
+        sw.swiglu_forward_fp8(handle, a, w, y, M, N, 16, variant=sw.VARIANT_GEMM)
+    assert e.value.status == sw.ERR_INVALID_ARG
+    y.fill_(-1)                                            # K = 0 in sync order
+    sw.swiglu_forward_fp8(handle, 0, 0, y, M, N, 0, variant=sw.VARIANT_SYNC)
+    t.cuda.synchronize()
+    assert np.all(decode(host(y)) == 0.0)
 
 
 def test_fp8_scales_apply_before_silu(handle):
@@ -189,9 +210,11 @@ def test_fp8_scales_apply_before_silu(handle):
     M, N, K = 64, 128, 256
     a8, w18, w28, sa, s1, s2 = fp8_inputs(M, N, K, 77)
     w8 = oracle.pack_fp8_kmajor(w18, w28)
-    for scales in [(sa, s1, s2), (sa, s1, s2 * 8), (sa, s1 * 0.5, s2), (sa * 4, s1, s2)]:
-        y = forward(handle, a8, w8, M, N, K, scales)
-        assert_parity(y, oracle.swiglu_fp8_rows(a8, w18, w28, *scales), f"fp8 scales {scales}")
+    for variant in (sw.VARIANT_INTERLEAVE, sw.VARIANT_SYNC):
+        for scales in [(sa, s1, s2), (sa, s1, s2 * 8), (sa, s1 * 0.5, s2), (sa * 4, s1, s2)]:
+            y = forward(handle, a8, w8, M, N, K, scales, variant=variant)
+            assert_parity(y, oracle.swiglu_fp8_rows(a8, w18, w28, *scales),
+                          f"fp8 variant {variant} scales {scales}")
 
 
 # --------------------------------------------------------------------------- workloads
@@ -209,12 +232,13 @@ def workload(request):
     return dict(w=w, a8=a8, w8=w8, w18=w18, w28=w28, s=(sa, s1, s2), rows=rows, y_ref=y_ref)
 
 
-def test_fp8_workload_parity(handle, workload):
+@pytest.mark.parametrize("variant", [sw.VARIANT_AUTO, sw.VARIANT_SYNC], ids=["auto", "sync"])
+def test_fp8_workload_parity(handle, workload, variant):
     d = workload
     w = d["w"]
-    cfg = sw.swiglu_query_fp8(handle, w.M, w.N, w.K)
-    log(f"fp8 {w.name}: config {cfg['id']}")
-    y = forward(handle, d["a8"], d["w8"], w.M, w.N, w.K, d["s"])
+    cfg = sw.swiglu_query_fp8(handle, w.M, w.N, w.K, variant)
+    log(f"fp8 {w.name} variant {variant}: config {cfg['id']}")
+    y = forward(handle, d["a8"], d["w8"], w.M, w.N, w.K, d["s"], variant=variant)
     yv = decode(y)
     assert np.all(np.isfinite(yv)), "unwritten or non-finite outputs"
     assert_parity(y[d["rows"]], d["y_ref"], f"fp8 {w.name} sampled rows")
