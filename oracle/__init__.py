@@ -75,6 +75,14 @@ def _load():
                lib.oracle_decode_bf16, lib.oracle_pack_interleaved, lib.oracle_decode_e4m3,
                lib.oracle_quantize_e4m3, lib.oracle_pack_fp8_kmajor):
         fn.restype = None
+    lib.oracle_quantize_mx.argtypes = [p, i64, i64, i64, p, p]
+    lib.oracle_decode_mx.argtypes = [p, p, i64, i64, i64, p]
+    lib.oracle_pack_kmajor_bf16.argtypes = [p, p, p, i64, i64]
+    for fn in (lib.oracle_quantize_mx, lib.oracle_decode_mx, lib.oracle_pack_kmajor_bf16):
+        fn.restype = None
+    lib.oracle_swiglu_mx_rows.argtypes = [p, p, p, p, i64, i64, i64, i64, p, i64, p, p, p,
+                                          c_int]
+    lib.oracle_swiglu_mx_rows.restype = c_int
     f32 = ctypes.c_float
     lib.oracle_swiglu_fp8_rows.argtypes = [p, p, p, i64, i64, i64, f32, f32, f32, p, i64,
                                            p, p, p, c_int]
@@ -296,4 +304,76 @@ def swiglu_fp8_rows(a, w1, w2, s_a=1.0, s_w1=1.0, s_w2=1.0, rows=None,
                                     nthreads or default_threads())
     if rc < 0:
         raise ValueError("oracle_swiglu_fp8_rows rejected its arguments")
+    return (y, g, u) if with_gate_up else y
+
+
+# ---- MXFP8 (OCP Microscaling, E4M3 elements, E8M0 scale per 32 along K) ------
+
+
+def mx_scale_stride(K: int) -> int:
+    """Row stride (bytes) of the E8M0 scale tensors: K/32 rounded up to 16."""
+    return -(-(K // 32) // 16) * 16
+
+
+def quantize_mx(x, ks=None):
+    """fp32 rows [R, K] (K % 32 == 0) -> (E4M3 codes [R, K], E8M0 scales [R, ks])."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    R, K = x.shape
+    if K % 32:
+        raise ValueError("K must be a multiple of 32")
+    ks = mx_scale_stride(K) if ks is None else ks
+    q = np.empty((R, K), np.uint8)
+    s = np.empty((R, ks), np.uint8)
+    _load().oracle_quantize_mx(_ptr(x), R, K, ks, _ptr(q), _ptr(s))
+    return q, s
+
+
+def decode_mx(q, s):
+    """Real values (float64 [R, K]) of MX rows."""
+    q = _u8(q, "q")
+    s = _u8(s, "s")
+    R, K = q.shape
+    out = np.empty((R, K), np.float64)
+    _load().oracle_decode_mx(_ptr(q), _ptr(s), R, K, s.shape[1], _ptr(out))
+    return out
+
+
+def pack_kmajor_bf16(w1, w2):
+    """Wt [2N, K] (bf16 bits) from W1, W2 [K, N]: row 2n = W1[:, n], row 2n+1 = W2[:, n]."""
+    w1 = _u16(w1, "W1")
+    w2 = _u16(w2, "W2")
+    if w1.shape != w2.shape:
+        raise ValueError("W1 and W2 differ in shape")
+    K, N = w1.shape
+    wt = np.empty((2 * N, K), np.uint16)
+    _load().oracle_pack_kmajor_bf16(_ptr(w1), _ptr(w2), _ptr(wt), K, N)
+    return wt
+
+
+def swiglu_mx_rows(a, sa, w, sw, rows=None, with_gate_up=False, nthreads=None):
+    """fp32 y of the MXFP8 forward (and optionally g, u) for the listed rows.
+
+    a [M, K] E4M3 + sa [M, ks] E8M0; w [2N, K] E4M3 (row 2n Gate, 2n+1 Up) +
+    sw [2N, ks].  The dot products are summed in fp64 over the decoded values.
+    """
+    a, sa, w, sw = _u8(a, "A"), _u8(sa, "SA"), _u8(w, "W"), _u8(sw, "SW")
+    M, K = a.shape
+    if w.shape[1] != K or w.shape[0] % 2 or sa.shape[0] != M or sw.shape[0] != w.shape[0] \
+            or sa.shape[1] != sw.shape[1]:
+        raise ValueError("shapes do not match")
+    N = w.shape[0] // 2
+    lib = _load()
+    if rows is None:
+        ridx, nr = None, M
+    else:
+        ridx = np.ascontiguousarray(rows, dtype=np.int64)
+        nr = ridx.size
+    y = np.empty((nr, N), np.float32)
+    g = np.empty((nr, N), np.float32) if with_gate_up else None
+    u = np.empty((nr, N), np.float32) if with_gate_up else None
+    rc = lib.oracle_swiglu_mx_rows(_ptr(a), _ptr(sa), _ptr(w), _ptr(sw), M, N, K, sa.shape[1],
+                                   _ptr(ridx), nr, _ptr(y), _ptr(g), _ptr(u),
+                                   nthreads or default_threads())
+    if rc < 0:
+        raise ValueError("oracle_swiglu_mx_rows rejected its arguments")
     return (y, g, u) if with_gate_up else y

@@ -470,3 +470,158 @@ int oracle_swiglu_fp8_rows(const uint8_t* a, const uint8_t* w1, const uint8_t* w
   free(all);
   return nthreads;
 }
+
+/* ======================================================================== */
+/* MXFP8 inputs (OCP Microscaling: E4M3 elements, one E8M0 scale per 32)    */
+/* ======================================================================== */
+/*
+ * The TorchInductor/CuteDSL page (§Impatto sui deployment on-premise) reports
+ * MXFP8 GEMMs.  Reading taken here: the OCP Microscaling (MX) format with E4M3
+ * elements: each block of 32 consecutive elements along the reduction
+ * dimension K shares one E8M0 scale byte e, which stands for 2^(e - 127)
+ * (e = 255 is NaN), so element k of a row stands for 2^(e(k/32) - 127) *
+ * value(q[k]).  Scales are stored row-major with a row stride of ks bytes
+ * (ks >= K/32; bytes past K/32 are ignored).
+ *
+ * Quantisation of a block V_0..V_31 (the MX conversion rule): the shared
+ * exponent is floor(log2(max |V_i|)) - 8 (8 = the exponent of E4M3's largest
+ * normal, 448 = 1.75 * 2^8), clamped to [-127, 127]; an all-zero block (or one
+ * of NaNs only) takes -127; each element is V_i / 2^shared rounded to E4M3 as
+ * above (nearest even, saturating at 448; NaN stays NaN).  NaN elements do not
+ * take part in the maximum.
+ */
+
+static double e8m0_value(uint8_t e) { return e == 255 ? NAN : ldexp(1.0, (int)e - 127); }
+
+/* Quantise rows of K fp32 values (row-major [rows, K], K % 32 == 0) to E4M3
+ * codes q [rows, K] and E8M0 scales s [rows, ks]. */
+void oracle_quantize_mx(const float* x, int64_t rows, int64_t K, int64_t ks, uint8_t* q,
+                        uint8_t* s) {
+  for (int64_t r = 0; r < rows; ++r) {
+    for (int64_t b = 0; b < ks; ++b) s[r * ks + b] = 0;
+    for (int64_t b = 0; b < K / 32; ++b) {
+      const float* v = x + r * K + 32 * b;
+      double amax = 0.0;
+      for (int i = 0; i < 32; ++i)
+        if (!isnan(v[i]) && fabs((double)v[i]) > amax) amax = fabs((double)v[i]);
+      int shared = -127;
+      if (amax > 0.0) {
+        int e2;
+        (void)frexp(amax, &e2); /* amax in [2^(e2-1), 2^e2): floor(log2 amax) = e2 - 1 */
+        shared = (e2 - 1) - 8;
+        if (shared < -127) shared = -127;
+        if (shared > 127) shared = 127;
+      }
+      s[r * ks + b] = (uint8_t)(shared + 127);
+      for (int i = 0; i < 32; ++i) {
+        const double scaled = ldexp((double)v[i], -shared); /* exact: a power of two */
+        q[r * K + 32 * b + i] = e4m3_from_f32((float)scaled);
+      }
+    }
+  }
+}
+
+/* Real values of MX rows: out [rows, K] = 2^(s - 127) * value(q), fp64. */
+void oracle_decode_mx(const uint8_t* q, const uint8_t* s, int64_t rows, int64_t K, int64_t ks,
+                      double* out) {
+  for (int64_t r = 0; r < rows; ++r)
+    for (int64_t k = 0; k < K; ++k)
+      out[r * K + k] = e8m0_value(s[r * ks + k / 32]) * e4m3_value(q[r * K + k]);
+}
+
+/* bf16 W1, W2 [K, N] -> Wt [2N, K] bf16: row 2n = W1[:, n], row 2n+1 = W2[:, n]
+ * (the Kernel-2 pairing with k contiguous), a bit copy. */
+void oracle_pack_kmajor_bf16(const uint16_t* w1, const uint16_t* w2, uint16_t* wt, int64_t K,
+                             int64_t N) {
+  for (int64_t n = 0; n < N; ++n)
+    for (int64_t k = 0; k < K; ++k) {
+      wt[(2 * n) * K + k] = w1[k * N + n];
+      wt[(2 * n + 1) * K + k] = w2[k * N + n];
+    }
+}
+
+typedef struct {
+  const uint8_t *a, *sa, *w, *sw; /* A [M,K] + SA [M,ks]; W8 [2N,K] + SW [2N,ks] */
+  int64_t M, N, K, ks;
+  const int64_t* idx;
+  int64_t lo, hi;
+  float *y, *g, *u;
+} jobmx_t;
+
+/* One output row: g[n] = sum_k a(m,k) w(2n,k), u[n] likewise with row 2n+1,
+ * in fp64 over the decoded values (k ascending), then fp32 as in the bf16 path. */
+static void* rowsmx_worker(void* p) {
+  jobmx_t* j = (jobmx_t*)p;
+  const int64_t N = j->N, K = j->K, ks = j->ks;
+  double lut[256], slut[256];
+  for (int c = 0; c < 256; ++c) lut[c] = e4m3_value((uint8_t)c), slut[c] = e8m0_value((uint8_t)c);
+  double* arow = (double*)malloc(sizeof(double) * (size_t)(K > 0 ? K : 1));
+  for (int64_t r = j->lo; r < j->hi; ++r) {
+    const int64_t m = j->idx[r];
+    for (int64_t k = 0; k < K; ++k)
+      arow[k] = slut[j->sa[m * ks + k / 32]] * lut[j->a[m * K + k]];
+    for (int64_t n = 0; n < N; ++n) {
+      double gs = 0.0, us = 0.0;
+      const uint8_t* wg = j->w + (2 * n) * K;
+      const uint8_t* wu = j->w + (2 * n + 1) * K;
+      const uint8_t* sg = j->sw + (2 * n) * ks;
+      const uint8_t* su = j->sw + (2 * n + 1) * ks;
+      for (int64_t k = 0; k < K; ++k) {
+        gs += arow[k] * (slut[sg[k / 32]] * lut[wg[k]]);
+        us += arow[k] * (slut[su[k / 32]] * lut[wu[k]]);
+      }
+      const float g = (float)gs, u = (float)us;
+      j->y[r * N + n] = silu_f32(g) * u;
+      if (j->g) j->g[r * N + n] = g;
+      if (j->u) j->u[r * N + n] = u;
+    }
+  }
+  free(arow);
+  return NULL;
+}
+
+/*
+ * oracle_swiglu_mx_rows: fp32 y (and optionally g, u) of the MXFP8 forward for
+ * the listed rows (NULL: all).  a [M, K] + sa [M, ks]; w [2N, K] + sw [2N, ks]
+ * (row 2n Gate column n, row 2n+1 Up column n).  Returns threads used or -1.
+ */
+int oracle_swiglu_mx_rows(const uint8_t* a, const uint8_t* sa, const uint8_t* w,
+                          const uint8_t* sw, int64_t M, int64_t N, int64_t K, int64_t ks,
+                          const int64_t* rows, int64_t nrows, float* y, float* g, float* u,
+                          int nthreads) {
+  if (M < 0 || N < 0 || K < 0 || nrows < 0 || !y || K % 32 != 0 || ks < K / 32) return -1;
+  if (K > 0 && N > 0 && (!a || !sa || !w || !sw)) return -1;
+  int64_t* all = NULL;
+  if (!rows) {
+    nrows = M;
+    all = (int64_t*)malloc(sizeof(int64_t) * (size_t)(M > 0 ? M : 1));
+    for (int64_t i = 0; i < M; ++i) all[i] = i;
+    rows = all;
+  }
+  for (int64_t i = 0; i < nrows; ++i)
+    if (rows[i] < 0 || rows[i] >= M) {
+      free(all);
+      return -1;
+    }
+  jobmx_t jobs[256];
+  for (int t = 0; t < 256; ++t) {
+    jobmx_t jb = {a, sa, w, sw, M, N, K, ks, rows, 0, 0, y, g, u};
+    jobs[t] = jb;
+  }
+  if (nthreads < 1) nthreads = 1;
+  if (nthreads > 256) nthreads = 256;
+  if ((int64_t)nthreads > nrows) nthreads = (int)(nrows > 0 ? nrows : 1);
+  pthread_t th[256];
+  int started[256] = {0};
+  for (int t = 0; t < nthreads; ++t) {
+    jobs[t].lo = nrows * t / nthreads;
+    jobs[t].hi = nrows * (t + 1) / nthreads;
+    if (t > 0 && pthread_create(&th[t], NULL, rowsmx_worker, &jobs[t]) == 0) started[t] = 1;
+  }
+  for (int t = 0; t < nthreads; ++t)
+    if (t == 0 || !started[t]) rowsmx_worker(&jobs[t]);
+  for (int t = 1; t < nthreads; ++t)
+    if (started[t]) pthread_join(th[t], NULL);
+  free(all);
+  return nthreads;
+}

@@ -224,3 +224,111 @@ def test_fp8_invariants():
     # rows can be listed in any order
     rows = np.array([5, 0, 3])
     assert np.array_equal(oracle.swiglu_fp8_rows(a, w1, w2, rows=rows), y[rows])
+
+
+# --------------------------------------------------------------------------- MXFP8
+# OCP Microscaling reading: E4M3 elements, one E8M0 scale (2^(e-127)) per 32
+# consecutive k; shared exponent floor(log2 max|V|) - 8, clamped to [-127, 127].
+def test_decode_mx_anchor_values():
+    q = np.array([[0x38] * 32 + [0x40] * 32], np.uint8)
+    for e, f in [(127, 1.0), (128, 2.0), (0, 2.0 ** -127), (254, 2.0 ** 127)]:
+        s = np.array([[e, 127] + [0] * 14], np.uint8)
+        v = oracle.decode_mx(q, s)
+        assert np.all(v[0, :32] == f) and np.all(v[0, 32:] == 2.0)
+    v = oracle.decode_mx(q, np.array([[255, 127] + [0] * 14], np.uint8))
+    assert np.all(np.isnan(v[0, :32])) and np.all(v[0, 32:] == 2.0)
+
+
+def test_quantize_mx_hand_cases():
+    x = np.zeros((4, 64), np.float32)
+    x[0, :32] = 448.0                     # max 448: shared exponent 0 (e = 127), codes unchanged
+    x[0, 32:] = 1.0                       # max 1: shared -8 (e = 119), 1 -> 256 = code 0x78
+    x[1, 3] = -3.0                        # one non-zero: shared floor(log2 3) - 8 = -7
+    x[2, :] = 2.0 ** -140                 # tiny: shared clamped to -127 (e = 0)
+    q, s = oracle.quantize_mx(x)
+    assert s.shape == (4, 16)
+    assert list(s[0, :2]) == [127, 119] and np.all(q[0, :32] == 0x7E) and np.all(q[0, 32:] == 0x78)
+    assert s[1, 0] == 120 and q[1, 3] == (0x80 | oracle.quantize_e4m3(np.float32([3 * 128.0]))[0])
+    assert s[1, 1] == 0 and np.all(q[1, 32:] == 0)          # all-zero block: e = 0, codes 0
+    assert s[2, 0] == 0
+    assert np.all(s[:, 2:] == 0)                             # padding bytes of the scale rows
+
+
+@settings(max_examples=30, deadline=None)
+@given(seed=st.integers(0, 2 ** 31 - 1), spread=st.sampled_from([1e-3, 1.0, 37.0, 1e5]))
+def test_quantize_mx_against_exhaustive_search(seed, spread):
+    rng = np.random.default_rng(seed)
+    x = (rng.standard_normal((3, 96)) * spread).astype(np.float32)
+    q, s = oracle.quantize_mx(x)
+    for r in range(3):
+        for b in range(3):
+            v = x[r, 32 * b: 32 * b + 32].astype(np.float64)
+            X = 2.0 ** (int(s[r, b]) - 127)
+            # the largest magnitude lands in E4M3's top binade [256, 512)
+            assert 256.0 <= np.max(np.abs(v)) / X < 512.0
+            assert np.array_equal(q[r, 32 * b: 32 * b + 32], nearest_code(v / X))
+
+
+def test_pack_kmajor_bf16_is_transpose_interleave():
+    rng = np.random.default_rng(2)
+    w1 = rng.integers(0, 65536, (40, 24), dtype=np.uint16)
+    w2 = rng.integers(0, 65536, (40, 24), dtype=np.uint16)
+    wt = oracle.pack_kmajor_bf16(w1, w2)
+    assert wt.shape == (48, 40)
+    assert np.array_equal(wt[0::2], w1.T) and np.array_equal(wt[1::2], w2.T)
+
+
+def mx_case(rng, M, N, K):
+    a = rng.standard_normal((M, K)).astype(np.float32) * np.float32(3.0)
+    w = (rng.standard_normal((2 * N, K)) / np.sqrt(K)).astype(np.float32)
+    w[:, :32] *= np.float32(50.0)                      # blocks of very different scale
+    (qa, sa), (qw, sw) = oracle.quantize_mx(a), oracle.quantize_mx(w)
+    return qa, sa, qw, sw
+
+
+def test_mx_forward_with_unit_scales_equals_fp8_forward():
+    rng = np.random.default_rng(12)
+    M, N, K = 5, 24, 128
+    qa, sa, qw, sw = mx_case(rng, M, N, K)
+    y_mx, g_mx, u_mx = oracle.swiglu_mx_rows(qa, np.full_like(sa, 127), qw,
+                                             np.full_like(sw, 127), with_gate_up=True)
+    y8, g8, u8 = oracle.swiglu_fp8_rows(qa, np.ascontiguousarray(qw[0::2].T),
+                                        np.ascontiguousarray(qw[1::2].T), with_gate_up=True)
+    assert np.array_equal(g_mx, g8) and np.array_equal(u_mx, u8) and np.array_equal(y_mx, y8)
+
+
+@settings(max_examples=25, deadline=None)
+@given(M=st.integers(1, 4), N=st.integers(1, 5), KB=st.integers(1, 3),
+       seed=st.integers(0, 2 ** 31 - 1))
+def test_mx_forward_matches_exact_brute_force(M, N, KB, seed):
+    K = 32 * KB
+    rng = np.random.default_rng(seed)
+    qa, sa, qw, sw = mx_case(rng, M, N, K)
+    y, g, u = oracle.swiglu_mx_rows(qa, sa, qw, sw, with_gate_up=True, nthreads=2)
+    A = [[Fraction(float(v)) for v in row] for row in torch_decode(qa)]
+    Wv = [[Fraction(float(v)) for v in row] for row in torch_decode(qw)]
+    SA = lambda m, k: Fraction(2) ** (int(sa[m, k // 32]) - 127)
+    SW = lambda r, k: Fraction(2) ** (int(sw[r, k // 32]) - 127)
+    ulp = lambda x: np.spacing(np.abs(np.float32(x))).astype(np.float64)
+    for m in range(M):
+        for n in range(N):
+            G = float(sum(SA(m, k) * A[m][k] * SW(2 * n, k) * Wv[2 * n][k] for k in range(K)))
+            U = float(sum(SA(m, k) * A[m][k] * SW(2 * n + 1, k) * Wv[2 * n + 1][k]
+                          for k in range(K)))
+            assert abs(g[m, n] - G) <= ulp(G) and abs(u[m, n] - U) <= ulp(U)
+            with np.errstate(over="ignore"):
+                Y = G / (1.0 + np.exp(-G)) * U
+            assert abs(y[m, n] - Y) <= 1.1 * ulp(G) * abs(U) + abs(G) * ulp(U) + 2.0 ** -20 * abs(Y) + 1e-40
+
+
+def test_mx_up_scale_doubles_y():
+    rng = np.random.default_rng(13)
+    qa, sa, qw, sw = mx_case(rng, 4, 16, 96)
+    y = oracle.swiglu_mx_rows(qa, sa, qw, sw)
+    sw2 = sw.copy()
+    sw2[1::2, :3] += 1                                   # every Up block scale x 2
+    assert np.array_equal(oracle.swiglu_mx_rows(qa, sa, qw, sw2), y * 2)
+    sw0 = sw.copy()
+    qw0 = qw.copy()
+    qw0[1::2] = 0                                        # Up = 0 -> Y = 0
+    assert np.all(oracle.swiglu_mx_rows(qa, sa, qw0, sw0) == 0)
