@@ -25,7 +25,8 @@ __all__ = [
     "swiglu_forward_fp8", "swiglu_quantize_fp8", "swiglu_pack_fp8", "swiglu_query_fp8",
     "LAYOUT_SEPARATE", "LAYOUT_INTERLEAVED",
     "VARIANT_AUTO", "VARIANT_SYNC", "VARIANT_INTERLEAVE", "VARIANT_GEMM", "VARIANT_FP8",
-    "VARIANT_FP8_SYNC",
+    "VARIANT_FP8_SYNC", "VARIANT_MXFP8", "swiglu_forward_mx", "swiglu_quantize_mx",
+    "swiglu_pack_kmajor",
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -33,8 +34,8 @@ _LIB_PATH = os.path.join(_PKG, "libswiglu.so")
 
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_DEVICE, ERR_LAUNCH, ERR_ALLOC = range(6)
 LAYOUT_SEPARATE, LAYOUT_INTERLEAVED = 0, 1
-VARIANT_AUTO, VARIANT_SYNC, VARIANT_INTERLEAVE, VARIANT_GEMM, VARIANT_FP8, VARIANT_FP8_SYNC = \
-    0, 1, 2, 3, 4, 5
+VARIANT_AUTO, VARIANT_SYNC, VARIANT_INTERLEAVE, VARIANT_GEMM, VARIANT_FP8, VARIANT_FP8_SYNC, \
+    VARIANT_MXFP8 = 0, 1, 2, 3, 4, 5, 6
 
 
 class SwiGLUError(RuntimeError):
@@ -98,6 +99,9 @@ def load():
         "swiglu_quantize_fp8": ([p, p, p, i64, ctypes.c_float, p], st),
         "swiglu_pack_fp8": ([p, p, p, p, i64, i64, p], st),
         "swiglu_query_fp8": ([p, i64, i64, i64, ctypes.c_int, ctypes.POINTER(Tile)], st),
+        "swiglu_forward_mx": ([p, p, p, p, p, p, i64, i64, i64, i64, i32, p], st),
+        "swiglu_quantize_mx": ([p, p, p, p, i64, i64, i64, p], st),
+        "swiglu_pack_kmajor": ([p, p, p, p, i64, i64, p], st),
     }
     for name, (args, res) in sig.items():
         fn = getattr(lib, name)
@@ -212,6 +216,27 @@ def swiglu_forward_fp8(handle, A8, W8, Y, M, N, K, scale_a=1.0, scale_w1=1.0, sc
     _check(load().swiglu_forward_fp8(handle, _ptr(A8), _ptr(W8), _ptr(Y), M, N, K, scale_a,
                                      scale_w1, scale_w2, variant, config_id, _stream(stream)),
            "swiglu_forward_fp8")
+
+
+def swiglu_forward_mx(handle, A8, SA, W8, SW, Y, M, N, K, ks, config_id=-1, stream=None):
+    """MXFP8: A8 [M, K] + SA [M, ks], W8 [2N, K] + SW [2N, ks] (uint8); Y bf16 [M, N]."""
+    _check(load().swiglu_forward_mx(handle, _ptr(A8), _ptr(SA), _ptr(W8), _ptr(SW), _ptr(Y), M,
+                                    N, K, ks, config_id, _stream(stream)), "swiglu_forward_mx")
+
+
+def swiglu_quantize_mx(handle, X, Q, S, rows, K, ks, stream=None):
+    _check(load().swiglu_quantize_mx(handle, _ptr(X), _ptr(Q), _ptr(S), rows, K, ks,
+                                     _stream(stream)), "swiglu_quantize_mx")
+
+
+def swiglu_pack_kmajor(handle, W1, W2, Wt, K, N, stream=None):
+    _check(load().swiglu_pack_kmajor(handle, _ptr(W1), _ptr(W2), _ptr(Wt), K, N,
+                                     _stream(stream)), "swiglu_pack_kmajor")
+
+
+def mx_scale_stride(K: int) -> int:
+    """Row stride (bytes) of MX scale tensors used by this package: K/32 rounded up to 16."""
+    return -(-(K // 32) // 16) * 16
 
 
 def swiglu_quantize_fp8(handle, X, Q, count, inv_scale=1.0, stream=None):

@@ -216,6 +216,7 @@ void fill_tile(int id, swiglu_tile_t* t) {
 int fp8_family(int variant) {
   if (variant == SWIGLU_VARIANT_AUTO || variant == SWIGLU_VARIANT_INTERLEAVE) return VAR_F8;
   if (variant == SWIGLU_VARIANT_SYNC) return VAR_F8_SYNC;
+  if (variant == SWIGLU_VARIANT_MXFP8) return VAR_MX;  // queries only
   return -1;
 }
 
@@ -348,7 +349,7 @@ swiglu_status_t swiglu_forward_fp8(swiglu_handle_t h, const void* A8, const void
                                    int32_t config_id, hipStream_t stream) {
   if (!h || M < 0 || N < 0 || K < 0) return SWIGLU_ERR_INVALID_ARG;
   const int want = fp8_family((int)variant);
-  if (want < 0) return SWIGLU_ERR_INVALID_ARG;
+  if (want < 0 || want == VAR_MX) return SWIGLU_ERR_INVALID_ARG;
   int id = config_id;
   if (id >= 0) {
     const KernelConfig* c = config_at(id);
@@ -383,6 +384,94 @@ swiglu_status_t swiglu_forward_fp8(swiglu_handle_t h, const void* A8, const void
   a.scale_u = scale_a * scale_w2;
   a.stream = stream;
   return launch(h, config_at(id), id, a);
+}
+
+swiglu_status_t swiglu_forward_mx(swiglu_handle_t h, const void* A8, const void* SA,
+                                  const void* W8, const void* SW, void* Y, int64_t M, int64_t N,
+                                  int64_t K, int64_t ks, int32_t config_id, hipStream_t stream) {
+  if (!h || M < 0 || N < 0 || K < 0 || ks < 0) return SWIGLU_ERR_INVALID_ARG;
+  int id = config_id;
+  if (id >= 0) {
+    const KernelConfig* c = config_at(id);
+    if (!c || c->variant != VAR_MX) return SWIGLU_ERR_INVALID_ARG;
+  }
+  if (M == 0 || N == 0) return SWIGLU_OK;
+  if (!Y || (K > 0 && (!A8 || !W8 || !SA || !SW))) return SWIGLU_ERR_INVALID_ARG;
+  if (ks < K / 32) return SWIGLU_ERR_INVALID_ARG;
+  if (M > kMaxDim || K > kMaxDim || N > (kMaxDim >> 1) || ks > kMaxDim)
+    return SWIGLU_ERR_UNSUPPORTED;
+  if (N % 8 != 0 || K % 64 != 0 || ks % 16 != 0) return SWIGLU_ERR_UNSUPPORTED;
+  if (!aligned16(Y) || !aligned16(A8) || !aligned16(W8) || !aligned16(SA) || !aligned16(SW))
+    return SWIGLU_ERR_UNSUPPORTED;
+  const long long ybytes = 2LL * M * N, abytes = M * K, wbytes = 2LL * N * K;
+  const long long sabytes = M * ks, swbytes = 2LL * N * ks;
+  if (ybytes >= kMaxBytes || abytes >= kMaxBytes || wbytes >= kMaxBytes ||
+      sabytes >= kMaxBytes || swbytes >= kMaxBytes)
+    return SWIGLU_ERR_UNSUPPORTED;
+  if (K > 0 && (overlaps(Y, ybytes, A8, abytes) || overlaps(Y, ybytes, W8, wbytes) ||
+                overlaps(Y, ybytes, SA, sabytes) || overlaps(Y, ybytes, SW, swbytes)))
+    return SWIGLU_ERR_INVALID_ARG;
+  swiglu_status_t st = check_device(h);
+  if (st != SWIGLU_OK) return st;
+  if (id < 0) id = choose(h, VAR_MX, M, N, K);
+  if (id < 0) return SWIGLU_ERR_UNSUPPORTED;
+  LaunchArgs a;
+  a.A = (const uint16_t*)A8;
+  a.W1 = (const uint16_t*)W8;
+  a.W2 = nullptr;
+  a.Y = (uint16_t*)Y;
+  a.M = (int)M, a.N = (int)N, a.K = (int)K;
+  a.ldw = (int)K;
+  a.ldy = (int)N;
+  a.group_m = 0;
+  a.cu_count = h->cu_count;
+  a.scale_g = a.scale_u = 1.0f;
+  a.SA = (const uint8_t*)SA;
+  a.SW = (const uint8_t*)SW;
+  a.ks = (int)ks;
+  a.stream = stream;
+  return launch(h, config_at(id), id, a);
+}
+
+swiglu_status_t swiglu_quantize_mx(swiglu_handle_t h, const void* X, void* Q, void* S,
+                                   int64_t rows, int64_t K, int64_t ks, hipStream_t stream) {
+  if (!h || rows < 0 || K < 0 || ks < 0) return SWIGLU_ERR_INVALID_ARG;
+  if (rows == 0 || K == 0) return SWIGLU_OK;
+  if (!X || !Q || !S || ks < K / 32) return SWIGLU_ERR_INVALID_ARG;
+  if (K % 32 != 0 || ks % 16 != 0) return SWIGLU_ERR_UNSUPPORTED;
+  if (!aligned16(X) || !aligned16(Q) || !aligned16(S)) return SWIGLU_ERR_UNSUPPORTED;
+  if (rows > kMaxDim || K > kMaxDim || rows * K > (1LL << 40) || rows * ks > (1LL << 40))
+    return SWIGLU_ERR_UNSUPPORTED;
+  if (overlaps(Q, rows * K, X, 2 * rows * K) || overlaps(S, rows * ks, X, 2 * rows * K) ||
+      overlaps(S, rows * ks, Q, rows * K))
+    return SWIGLU_ERR_INVALID_ARG;
+  swiglu_status_t st = check_device(h);
+  if (st != SWIGLU_OK) return st;
+  (void)hipGetLastError();
+  if (launch_quantize_mx((const uint16_t*)X, (uint8_t*)Q, (uint8_t*)S, (int)rows, (int)K,
+                         (int)ks, stream, h->cu_count) != hipSuccess)
+    return SWIGLU_ERR_LAUNCH;
+  return SWIGLU_OK;
+}
+
+swiglu_status_t swiglu_pack_kmajor(swiglu_handle_t h, const void* W1, const void* W2, void* Wt,
+                                   int64_t K, int64_t N, hipStream_t stream) {
+  if (!h || K < 0 || N < 0) return SWIGLU_ERR_INVALID_ARG;
+  if (K == 0 || N == 0) return SWIGLU_OK;
+  if (!W1 || !W2 || !Wt) return SWIGLU_ERR_INVALID_ARG;
+  if (K > kMaxDim || N > (kMaxDim >> 1)) return SWIGLU_ERR_UNSUPPORTED;
+  if (N % 8 != 0 || K % 8 != 0) return SWIGLU_ERR_UNSUPPORTED;
+  if (!aligned16(W1) || !aligned16(W2) || !aligned16(Wt)) return SWIGLU_ERR_UNSUPPORTED;
+  const long long wb = 2LL * K * N;
+  if (2 * wb >= kMaxBytes) return SWIGLU_ERR_UNSUPPORTED;
+  if (overlaps(Wt, 2 * wb, W1, wb) || overlaps(Wt, 2 * wb, W2, wb)) return SWIGLU_ERR_INVALID_ARG;
+  swiglu_status_t st = check_device(h);
+  if (st != SWIGLU_OK) return st;
+  (void)hipGetLastError();
+  if (launch_pack_kmajor((const uint16_t*)W1, (const uint16_t*)W2, (uint16_t*)Wt, (int)N, (int)K,
+                         stream, h->cu_count) != hipSuccess)
+    return SWIGLU_ERR_LAUNCH;
+  return SWIGLU_OK;
 }
 
 swiglu_status_t swiglu_quantize_fp8(swiglu_handle_t h, const void* X, void* Q, int64_t count,

@@ -200,6 +200,20 @@ __device__ __forceinline__ f32x16 mfma32_f8(const u32x4 (&a)[2], const u32x4 (&b
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(x, y, c, 0, 0, 0, 127, 0, 127);
 }
 
+// The same with E8M0 block scales (2^(e - 127)) taken from the low byte of a
+// per-lane value: sw scales the first source, sa the second.  Lane l's scale
+// covers the k block of 32 that lanes l % 32 and l % 32 + 32 hold in bytes
+// 16 (l / 32) .. 16 (l / 32) + 15 of their fragments (block 0: bytes 0-15 of
+// both lane halves, block 1: bytes 16-31), for row or column l % 32.
+__device__ __forceinline__ f32x16 mfma32_f8_scaled(const u32x4 (&a)[2], const u32x4 (&b)[2],
+                                                   const f32x16& c, uint32_t sa_src0,
+                                                   uint32_t sb_src1) {
+  const i32x8 x = __builtin_bit_cast(i32x8, __builtin_shufflevector(a[0], a[1], 0, 1, 2, 3, 4, 5, 6, 7));
+  const i32x8 y = __builtin_bit_cast(i32x8, __builtin_shufflevector(b[0], b[1], 0, 1, 2, 3, 4, 5, 6, 7));
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(x, y, c, 0, 0, 0, (int)sa_src0, 0,
+                                                          (int)sb_src1);
+}
+
 // v_mfma_scale_f32_16x16x128_f8f6f4, E4M3 sources and unit block scales:
 // each source lane holds 32 bytes (one row or column, 32 of the 128 k); the
 // output layout is that of v_mfma_f32_16x16x32_bf16.

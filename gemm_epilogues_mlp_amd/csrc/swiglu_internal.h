@@ -9,8 +9,10 @@ namespace swiglu {
 
 // VAR_F8 / VAR_F8_SYNC: interleave / sync order on FP8 (E4M3) inputs with
 // k-contiguous paired weights
+// VAR_MX: interleave order on MXFP8 inputs (E4M3 + E8M0 scale per 32 along K)
 enum Variant {
-  VAR_AUTO = 0, VAR_SYNC = 1, VAR_INTERLEAVE = 2, VAR_GEMM = 3, VAR_F8 = 4, VAR_F8_SYNC = 5
+  VAR_AUTO = 0, VAR_SYNC = 1, VAR_INTERLEAVE = 2, VAR_GEMM = 3, VAR_F8 = 4, VAR_F8_SYNC = 5,
+  VAR_MX = 6
 };
 
 struct LaunchArgs {
@@ -23,6 +25,9 @@ struct LaunchArgs {
   int group_m;         // tile rows per GROUP_M band (<= 0: default)
   int cu_count;        // compute units of the device (workgroups per round)
   float scale_g, scale_u;  // FP8: s_a * s_w1 and s_a * s_w2 (unused otherwise)
+  const uint8_t* SA;       // MXFP8: E8M0 scales of A [M, ks] and of W8 [2N, ks]
+  const uint8_t* SW;
+  int ks;                  // MXFP8: scale row stride (bytes, a multiple of 16)
   hipStream_t stream;
 };
 
@@ -49,6 +54,12 @@ hipError_t launch_quantize_f8(const uint16_t* X, uint8_t* Q, size_t n, float inv
                               hipStream_t stream, int cu_count);
 hipError_t launch_pack_f8(const uint8_t* W1, const uint8_t* W2, uint8_t* W8, int N, int K,
                           hipStream_t stream, int cu_count);
+// MXFP8: bf16 rows [rows, K] -> E4M3 [rows, K] + E8M0 [rows, ks]; bf16 W1, W2
+// [K, N] -> Wt [2N, K] (k-major pairing)
+hipError_t launch_quantize_mx(const uint16_t* X, uint8_t* Q, uint8_t* S, int rows, int K, int ks,
+                              hipStream_t stream, int cu_count);
+hipError_t launch_pack_kmajor(const uint16_t* W1, const uint16_t* W2, uint16_t* Wt, int N, int K,
+                              hipStream_t stream, int cu_count);
 
 // Per-shape choice (tile table + fallback rule).  variant is SYNC, INTERLEAVE
 // or GEMM; returns a config id of that variant.

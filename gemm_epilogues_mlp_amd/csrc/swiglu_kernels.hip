@@ -42,7 +42,8 @@
 
 namespace swiglu {
 
-enum Mode { MODE_INTERLEAVE = 0, MODE_SYNC = 1, MODE_GEMM = 2 };
+// MODE_MX: the interleave pairing on MXFP8 inputs (FP8 tile kernel only)
+enum Mode { MODE_INTERLEAVE = 0, MODE_SYNC = 1, MODE_GEMM = 2, MODE_MX = 3 };
 
 // ============================================================================
 // LDS-tiled MFMA kernel
@@ -913,6 +914,17 @@ void skinny_kernel(const uint16_t* __restrict__ A,
 // Gate accumulators are scaled and passed through SiLU in registers while
 // the first Up tiles are already in flight (the stage ring runs on across
 // the phase boundary).
+//
+// The MX mode is the interleave pairing on MXFP8 inputs: every 32 consecutive
+// k of a row of A8 or W8 share one E8M0 scale byte (SA [M, ks], SW [2N, ks]).
+// The MFMA applies them itself (per lane, the scale of its row and of the k
+// block its fragment half belongs to), so the accumulators come out fully
+// scaled.  A 16-byte chunk of a scale row covers 8 K steps; the tile's chunks
+// (BM + BNW rows) are loaded by the same DMA into a two-slot ring in LDS, with
+// the K step that starts a group of 8; in the other steps the same
+// instruction loads nothing (a junk slot), so every step issues the same
+// number of loads.  Each lane reads its scale bytes for the next step with the
+// fragments.
 template <int MODE, int BM, int BNW, int STAGES, int WGM, int WGN>
 struct F8Tiled {
   static constexpr int kWaves = WGM * WGN;
@@ -934,12 +946,22 @@ struct F8Tiled {
   static constexpr int A_LOADS = (A_CHUNKS + kThreads - 1) / kThreads;
   static constexpr int W_LOADS = (W_CHUNKS + kThreads - 1) / kThreads;
   static constexpr int LOADS = A_LOADS + W_LOADS;
+  static constexpr bool MX = MODE == MODE_MX;
+  static constexpr int SC_CHUNKS = MX ? BM + BNW : 0;  // one 16-byte scale chunk per row
+  static constexpr int SC_LOADS = MX ? (SC_CHUNKS + kThreads - 1) / kThreads : 0;
+  static_assert(!MX || (BM % 64 == 0 && BNW % 64 == 0), "a wave's scale chunks share one tensor");
+  static constexpr int TLOADS = LOADS + SC_LOADS;  // DMA instructions per thread and K step
   static_assert(STAGES >= 2 && STAGES % 2 == 0, "an even stage ring");
-  static_assert((STAGES - 1) * LOADS <= 63, "vmcnt range");
+  static_assert((STAGES - 1) * TLOADS <= 63, "vmcnt range");
   static constexpr int YLD = BNY + 8;
   static constexpr int Y_BYTES = BM * YLD * 2;
-  static constexpr int JUNK = STAGES * STAGE_BYTES;  // 1 KB slot for zero DMA
-  static constexpr int LDS_BYTES = JUNK + 1024 > Y_BYTES ? JUNK + 1024 : Y_BYTES;
+  // LDS: [scale ring (MX only) | STAGES stages | 1 KB junk slot for zero DMA]
+  static constexpr int SC_OFF = 0;                    // scale ring: 2 slots of SC_CHUNKS x 16 B
+  static constexpr int SC_SLOT = SC_CHUNKS * 16;
+  static constexpr int ST0 = 2 * SC_SLOT;             // first stage
+  static constexpr int JUNK = ST0 + STAGES * STAGE_BYTES;
+  static constexpr int RING_END = JUNK + 1024;
+  static constexpr int LDS_BYTES = RING_END > Y_BYTES ? RING_END : Y_BYTES;
   static_assert(LDS_BYTES <= 160 * 1024, "LDS");
   // chunk c of row r stored at c ^ swz(r): the 64-byte-row swizzle of the
   // bf16 A tile (the fragment read pattern is the same: 32 consecutive rows,
@@ -949,13 +971,17 @@ struct F8Tiled {
   }
 };
 
+// SA, SW, ks: MXFP8 scales and their row stride (MX mode only; K % 64 == 0
+// and ks % 16 == 0 there).
 template <int MODE, int BM, int BNW, int STAGES, int WGM, int WGN>
 __device__ __forceinline__ void f8_tile(const uint8_t* __restrict__ A,
                                         const uint8_t* __restrict__ W,
                                         uint16_t* __restrict__ Y, int M, int N, int K,
-                                        float sg, float su, int m0, int tn, uint8_t* smem) {
+                                        float sg, float su, const uint8_t* __restrict__ SA,
+                                        const uint8_t* __restrict__ SW, int ks, int m0, int tn,
+                                        uint8_t* smem) {
   using C = F8Tiled<MODE, BM, BNW, STAGES, WGM, WGN>;
-  static_assert(MODE == MODE_INTERLEAVE || MODE == MODE_SYNC, "FP8 modes");
+  static_assert(MODE == MODE_INTERLEAVE || MODE == MODE_SYNC || MODE == MODE_MX, "FP8 modes");
   constexpr bool kSync = MODE == MODE_SYNC;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -1002,20 +1028,33 @@ __device__ __forceinline__ void f8_tile(const uint8_t* __restrict__ A,
     w_off[i] = in ? (uint32_t)(wrow * K + c * 16) : 0u;
     w_k[i] = in ? (uint32_t)(c * 16) : kRowOut;
   }
-  // DMA instruction q (A chunks first, then weight chunks) of K step `it`
-  // into stage ST; padding steps and steps past the end load zeros (k0 = K)
+  // MX: scale chunk p of the tile is row p of A's scales (p < BM) or row
+  // p - BM of W8's; group g of 8 K steps is bytes [16 g, 16 g + 16) of the row
+  const i32x4 rsSA = make_rsrc(SA, C::MX ? (uint32_t)((size_t)M * ks) : 0u);
+  const i32x4 rsSW = make_rsrc(SW, C::MX ? (uint32_t)((size_t)2 * N * ks) : 0u);
+  uint32_t sc_off[C::SC_LOADS > 0 ? C::SC_LOADS : 1];
+#pragma unroll
+  for (int i = 0; i < C::SC_LOADS; ++i) {
+    const int p = tid + C::kThreads * i;
+    const bool in = p < BM ? m0 + p < M : wr0 + (p - BM) < 2 * N;
+    const size_t row = p < BM ? (size_t)(m0 + p) : (size_t)(wr0 + p - BM);
+    sc_off[i] = in ? (uint32_t)(row * ks) : kOutOfRange;
+  }
+  // DMA instruction q (A chunks first, then weight chunks, then in MX mode the
+  // scale chunk) of K step `it` into stage ST; padding steps and steps past
+  // the end load zeros (k0 = K)
   auto dma = [&](int it, auto st_c, int q) __attribute__((always_inline)) {
     constexpr int ST = decltype(st_c)::value;
     const bool up = kSync && it >= nk0;
     const int kt = up ? it - nk0 : it;
     const uint32_t k0 = (it < total && kt < nk) ? (uint32_t)kt * C::BK : (uint32_t)K;
-    const uint32_t sbase = lds0 + ST * C::STAGE_BYTES;
+    const uint32_t sbase = lds0 + C::ST0 + ST * C::STAGE_BYTES;
     if (q < C::A_LOADS) {
       const int p0 = C::kThreads * q + 64 * wave_u;
       const bool own = p0 < C::A_CHUNKS;
       const uint32_t off = (own && k0 + a_k[q] < (uint32_t)K) ? a_off[q] + k0 : kOutOfRange;
       lds_dma16(own ? sbase + p0 * 16 : lds0 + C::JUNK, off, rsA);
-    } else {
+    } else if (q < C::LOADS) {
       const int i = q - C::A_LOADS;
       const int p0 = C::kThreads * i + 64 * wave_u;
       const bool own = p0 < C::W_CHUNKS;
@@ -1023,6 +1062,18 @@ __device__ __forceinline__ void f8_tile(const uint8_t* __restrict__ A,
                                ? w_off[i] + (up ? (uint32_t)K : 0u) + k0
                                : kOutOfRange;
       lds_dma16(own ? sbase + C::A_BYTES + p0 * 16 : lds0 + C::JUNK, off, rsW);
+    } else if constexpr (C::MX) {
+      // the scale chunks of group it / 8 with step it of a group start, else nothing
+      const int i = q - C::LOADS;
+      const int p0 = C::kThreads * i + 64 * wave_u;
+      const bool own = p0 < C::SC_CHUNKS;
+      const bool real = own && (it & 7) == 0 && it < nk;
+      const int g = it >> 3;
+      const uint32_t off = (real && sc_off[i] != kOutOfRange) ? sc_off[i] + (uint32_t)(16 * g)
+                                                              : kOutOfRange;
+      const uint32_t dst = real ? lds0 + C::SC_OFF + (g & 1) * C::SC_SLOT + p0 * 16
+                                : lds0 + C::JUNK;
+      lds_dma16(dst, off, p0 < BM ? rsSA : rsSW);
     }
   };
 
@@ -1037,6 +1088,14 @@ __device__ __forceinline__ void f8_tile(const uint8_t* __restrict__ A,
   };
   u32x4 wf[C::FW][2];
   u32x4 af[2][C::FA][2];
+  // MX: scale bytes of the lane's rows for the current step (A by parity)
+  uint32_t scw[C::FW], sca[2][C::FA];
+  // the scale byte of tile row r (A rows first, then W8 rows) for step s:
+  // group s / 8, block 2 s + h of the row (this lane's fragment half)
+  auto scale_of = [&](int s, int r) __attribute__((always_inline)) -> uint32_t {
+    const uint8_t* slot = smem + C::SC_OFF + ((s >> 3) & 1) * C::SC_SLOT;
+    return slot[r * 16 + ((2 * s + h) & 15)];
+  };
   f32x16 acc[C::NACC][C::FW][C::FA];
 #pragma unroll
   for (int p = 0; p < C::NACC; ++p)
@@ -1057,18 +1116,27 @@ __device__ __forceinline__ void f8_tile(const uint8_t* __restrict__ A,
     constexpr int PH = decltype(phase_c)::value;
     constexpr int P = ST & 1;
     using Next = std::integral_constant<int, (ST + 1) % STAGES>;
-    const uint8_t* nxt = smem + Next::value * C::STAGE_BYTES;
-    wait_vmcnt<(STAGES - 2) * C::LOADS>();
+    const uint8_t* nxt = smem + C::ST0 + Next::value * C::STAGE_BYTES;
+    wait_vmcnt<(STAGES - 2) * C::TLOADS>();
     __syncthreads();
 #pragma unroll
     for (int q = 0; q < NMF; ++q) {
       const int i = q / C::FA, j = q % C::FA;
-      acc[PH][i][j] = mfma32_f8(wf[i], af[P][j], acc[PH][i][j]);
-      if (q < C::FA) read(nxt, a_row + 32 * q, af[P ^ 1][q]);
-      if (j == C::FA - 1) read(nxt + C::A_BYTES, w_row + 32 * i, wf[i]);
+      if constexpr (C::MX)
+        acc[PH][i][j] = mfma32_f8_scaled(wf[i], af[P][j], acc[PH][i][j], scw[i], sca[P][j]);
+      else
+        acc[PH][i][j] = mfma32_f8(wf[i], af[P][j], acc[PH][i][j]);
+      if (q < C::FA) {
+        read(nxt, a_row + 32 * q, af[P ^ 1][q]);
+        if constexpr (C::MX) sca[P ^ 1][q] = scale_of(it + 1, a_row + 32 * q);
+      }
+      if (j == C::FA - 1) {
+        read(nxt + C::A_BYTES, w_row + 32 * i, wf[i]);
+        if constexpr (C::MX) scw[i] = scale_of(it + 1, BM + w_row + 32 * i);
+      }
       if (q >= DBEGIN) {
 #pragma unroll
-        for (int x = (q - DBEGIN) * C::LOADS / DSLOTS; x < (q - DBEGIN + 1) * C::LOADS / DSLOTS;
+        for (int x = (q - DBEGIN) * C::TLOADS / DSLOTS; x < (q - DBEGIN + 1) * C::TLOADS / DSLOTS;
              ++x)
           dma(it + STAGES, st_c, x);
       }
@@ -1092,16 +1160,22 @@ __device__ __forceinline__ void f8_tile(const uint8_t* __restrict__ A,
     ((
          [&] {
 #pragma unroll
-           for (int q = 0; q < C::LOADS; ++q) dma(S, std::integral_constant<int, S>{}, q);
+           for (int q = 0; q < C::TLOADS; ++q) dma(S, std::integral_constant<int, S>{}, q);
          }()),
      ...);
   }(std::make_integer_sequence<int, STAGES>{});
-  wait_vmcnt<(STAGES - 1) * C::LOADS>();
+  wait_vmcnt<(STAGES - 1) * C::TLOADS>();
   __syncthreads();
 #pragma unroll
-  for (int j = 0; j < C::FA; ++j) read(smem, a_row + 32 * j, af[0][j]);
+  for (int j = 0; j < C::FA; ++j) {
+    read(smem + C::ST0, a_row + 32 * j, af[0][j]);
+    if constexpr (C::MX) sca[0][j] = scale_of(0, a_row + 32 * j);
+  }
 #pragma unroll
-  for (int i = 0; i < C::FW; ++i) read(smem + C::A_BYTES, w_row + 32 * i, wf[i]);
+  for (int i = 0; i < C::FW; ++i) {
+    read(smem + C::ST0 + C::A_BYTES, w_row + 32 * i, wf[i]);
+    if constexpr (C::MX) scw[i] = scale_of(0, BM + w_row + 32 * i);
+  }
 
   if constexpr (kSync) {
     run(0, nk0, std::integral_constant<int, 0>{});
@@ -1163,14 +1237,17 @@ __global__ __launch_bounds__(64 * WGM * WGN) void f8_kernel(const uint8_t* __res
                                                              const uint8_t* __restrict__ W,
                                                              uint16_t* __restrict__ Y, int M,
                                                              int N, int K, float sg, float su,
-                                                             int group_m) {
+                                                             const uint8_t* __restrict__ SA,
+                                                             const uint8_t* __restrict__ SW,
+                                                             int ks, int group_m) {
   using C = F8Tiled<MODE, BM, BNW, STAGES, WGM, WGN>;
   __shared__ __attribute__((aligned(1024))) uint8_t smem[C::LDS_BYTES];
   const int ntm = (M + BM - 1) / BM;
   const int ntn = (N + C::BNY - 1) / C::BNY;
   int tm, tn;
   tile_of(xcd_remap(blockIdx.x, gridDim.x), ntm, ntn, group_m, tm, tn);
-  f8_tile<MODE, BM, BNW, STAGES, WGM, WGN>(A, W, Y, M, N, K, sg, su, tm * BM, tn, smem);
+  f8_tile<MODE, BM, BNW, STAGES, WGM, WGN>(A, W, Y, M, N, K, sg, su, SA, SW, ks, tm * BM, tn,
+                                           smem);
 }
 
 // The split tail of tiled_split_kernel for the FP8 tiles: workgroups
@@ -1178,7 +1255,8 @@ __global__ __launch_bounds__(64 * WGM * WGN) void f8_kernel(const uint8_t* __res
 template <int MODE, int BM, int BNW, int STAGES, int WGM, int WGN, int SWGM, int SWGN>
 __global__ __launch_bounds__(64 * WGM * WGN) void f8_split_kernel(
     const uint8_t* __restrict__ A, const uint8_t* __restrict__ W, uint16_t* __restrict__ Y,
-    int M, int N, int K, float sg, float su, int group_m, int n_big) {
+    int M, int N, int K, float sg, float su, const uint8_t* __restrict__ SA,
+    const uint8_t* __restrict__ SW, int ks, int group_m, int n_big) {
   using Big = F8Tiled<MODE, BM, BNW, STAGES, WGM, WGN>;
   using Small = F8Tiled<MODE, BM / 2, BNW / 2, STAGES, SWGM, SWGN>;
   static_assert(Big::kThreads == Small::kThreads, "one workgroup size for both tile kinds");
@@ -1189,14 +1267,16 @@ __global__ __launch_bounds__(64 * WGM * WGN) void f8_split_kernel(
   int tm, tn;
   if ((int)blockIdx.x < n_big) {
     tile_of(xcd_remap(blockIdx.x, n_big), ntm, ntn, group_m, tm, tn);
-    f8_tile<MODE, BM, BNW, STAGES, WGM, WGN>(A, W, Y, M, N, K, sg, su, tm * BM, tn, smem);
+    f8_tile<MODE, BM, BNW, STAGES, WGM, WGN>(A, W, Y, M, N, K, sg, su, SA, SW, ks, tm * BM, tn,
+                                             smem);
   } else {
     const int u = blockIdx.x - n_big, q = u & 3;
     tile_of(n_big + u / 4, ntm, ntn, group_m, tm, tn);
     const int m0 = tm * BM + (q >> 1) * (BM / 2);
     const int tq = 2 * tn + (q & 1);
     if (m0 >= M || tq * Small::BNY >= N) return;
-    f8_tile<MODE, BM / 2, BNW / 2, STAGES, SWGM, SWGN>(A, W, Y, M, N, K, sg, su, m0, tq, smem);
+    f8_tile<MODE, BM / 2, BNW / 2, STAGES, SWGM, SWGN>(A, W, Y, M, N, K, sg, su, SA, SW, ks, m0,
+                                                       tq, smem);
   }
 }
 
@@ -1304,6 +1384,82 @@ __global__ __launch_bounds__(64 * NW) void f8_skinny_kernel(const uint8_t* __res
       const float y1 = silu(sg * v[2]) * (su * v[3]);
       *reinterpret_cast<uint32_t*>(Y + (size_t)row * N + col) = pack_bf16x2(y0, y1);
     }
+  }
+}
+
+// MXFP8 quantisation of bf16 rows [rows, K] (K % 32 == 0): one thread per
+// block of 32 values along K.  Shared exponent = floor(log2 max |x|) - 8 (8 =
+// the exponent of E4M3's largest normal), clamped to [-127, 127], -127 for a
+// block of zeros or subnormals (NaN does not take part; an infinity counts as
+// 2^128); elements x * 2^-shared (exact) rounded as e4m3_code.  Threads past
+// K / 32 in a row write the zero padding of the scale row (stride ks).
+__global__ __launch_bounds__(256) void quantize_mx_kernel(const uint16_t* __restrict__ X,
+                                                          uint8_t* __restrict__ Q,
+                                                          uint8_t* __restrict__ S, int rows,
+                                                          int K, int ks) {
+  const size_t total = (size_t)rows * ks;
+  for (size_t t = (size_t)blockIdx.x * blockDim.x + threadIdx.x; t < total;
+       t += (size_t)gridDim.x * blockDim.x) {
+    const size_t r = t / ks;
+    const int b = (int)(t % ks);
+    if (b >= K / 32) {
+      S[t] = 0;
+      continue;
+    }
+    const uint16_t* x = X + r * K + 32 * b;
+    u32x4 v[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] = load16(x + 8 * i);
+    float amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float lo = __builtin_fabsf(bf16_to_float((uint16_t)(v[i][j] & 0xffffu)));
+        const float hi = __builtin_fabsf(bf16_to_float((uint16_t)(v[i][j] >> 16)));
+        if (lo > amax) amax = lo;  // comparisons with NaN are false: NaN is skipped
+        if (hi > amax) amax = hi;
+      }
+    const int ef = (int)((__builtin_bit_cast(uint32_t, amax) >> 23) & 0xffu);
+    int shared = ef == 0 ? -127 : ef - 127 - 8;
+    shared = shared < -127 ? -127 : (shared > 127 ? 127 : shared);
+    S[t] = (uint8_t)(shared + 127);
+    u32x4 o[2];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float lo = __builtin_ldexpf(bf16_to_float((uint16_t)(v[i][j] & 0xffffu)), -shared);
+        const float hi = __builtin_ldexpf(bf16_to_float((uint16_t)(v[i][j] >> 16)), -shared);
+        const uint32_t pair = e4m3_code(lo) | (e4m3_code(hi) << 8);
+        const int e = 4 * i + j;  // element pair e: bytes 2e, 2e+1 of the 32
+        if (e % 2 == 0)
+          o[e / 8][(e % 8) / 2] = pair;
+        else
+          o[e / 8][(e % 8) / 2] |= pair << 16;
+      }
+    *reinterpret_cast<u32x4*>(Q + r * K + 32 * b) = o[0];
+    *reinterpret_cast<u32x4*>(Q + r * K + 32 * b + 16) = o[1];
+  }
+}
+
+// bf16 W1, W2 [K, N] -> Wt [2N, K]: Wt[2n + p, k] = Wp[k, n]; a thread writes
+// one 16-byte run (8 k) of one row, neighbouring threads neighbouring rows.
+__global__ __launch_bounds__(256) void pack_kmajor_kernel(const uint16_t* __restrict__ W1,
+                                                          const uint16_t* __restrict__ W2,
+                                                          uint16_t* __restrict__ Wt, int N,
+                                                          int K) {
+  const size_t rows = 2 * (size_t)N, runs = rows * (size_t)(K / 8);
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < runs;
+       i += (size_t)gridDim.x * blockDim.x) {
+    const size_t r = i % rows, c = i / rows;
+    const int n = (int)(r >> 1);
+    const uint16_t* src = ((r & 1) ? W2 : W1) + c * 8 * (size_t)N + n;
+    uint32_t d[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+      d[t] = (uint32_t)src[(size_t)(2 * t) * N] | ((uint32_t)src[(size_t)(2 * t + 1) * N] << 16);
+    *reinterpret_cast<u32x4*>(Wt + r * (size_t)K + c * 8) = u32x4{d[0], d[1], d[2], d[3]};
   }
 }
 
@@ -1481,7 +1637,8 @@ static hipError_t launch_f8(const LaunchArgs& a) {
   if (group_m > ntm) group_m = ntm;
   hipLaunchKernelGGL((f8_kernel<MODE, BM, BNW, STAGES, WGM, WGN>), dim3((unsigned)nwg),
                      dim3(C::kThreads), 0, a.stream, (const uint8_t*)a.A,
-                     (const uint8_t*)a.W1, a.Y, a.M, a.N, a.K, a.scale_g, a.scale_u, group_m);
+                     (const uint8_t*)a.W1, a.Y, a.M, a.N, a.K, a.scale_g, a.scale_u, a.SA, a.SW,
+                     a.ks, group_m);
   return hipGetLastError();
 }
 
@@ -1500,7 +1657,7 @@ static hipError_t launch_f8_split(const LaunchArgs& a) {
   hipLaunchKernelGGL((f8_split_kernel<MODE, BM, BNW, STAGES, WGM, WGN, SWGM, SWGN>),
                      dim3((unsigned)(n_big + 4 * tail)), dim3(C::kThreads), 0, a.stream,
                      (const uint8_t*)a.A, (const uint8_t*)a.W1, a.Y, a.M, a.N, a.K, a.scale_g,
-                     a.scale_u, group_m, (int)n_big);
+                     a.scale_u, a.SA, a.SW, a.ks, group_m, (int)n_big);
   return hipGetLastError();
 }
 
@@ -1610,6 +1767,9 @@ static const KernelConfig kConfigs[] = {
     F8_SPLIT(MODE_SYNC, VAR_F8_SYNC, 256, 128, 4, 4, 2, 4, 2),      // 53
     F8(MODE_SYNC, VAR_F8_SYNC, 128, 128, 4, 2, 2),                  // 54
     F8(MODE_SYNC, VAR_F8_SYNC, 64, 64, 4, 2, 2),                    // 55
+    // ---- MXFP8 (E8M0 block scales applied by the MFMA) ---------------------
+    F8_SPLIT(MODE_MX, VAR_MX, 256, 256, 4, 4, 2, 2, 4),             // 56
+    F8(MODE_MX, VAR_MX, 64, 128, 4, 2, 2),                          // 57
 };
 
 int config_count() { return (int)(sizeof(kConfigs) / sizeof(kConfigs[0])); }
@@ -1637,6 +1797,30 @@ hipError_t launch_quantize_f8(const uint16_t* X, uint8_t* Q, size_t n, float inv
   if (blocks > cap) blocks = cap;
   hipLaunchKernelGGL(quantize_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, X, Q, n16,
                      inv_scale);
+  return hipGetLastError();
+}
+
+hipError_t launch_quantize_mx(const uint16_t* X, uint8_t* Q, uint8_t* S, int rows, int K, int ks,
+                              hipStream_t stream, int cu_count) {
+  const size_t total = (size_t)rows * ks;
+  if (total == 0) return hipSuccess;
+  size_t blocks = (total + 255) / 256;
+  const size_t cap = (size_t)(cu_count > 0 ? cu_count : 256) * 8;
+  if (blocks > cap) blocks = cap;
+  hipLaunchKernelGGL(quantize_mx_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, X, Q, S,
+                     rows, K, ks);
+  return hipGetLastError();
+}
+
+hipError_t launch_pack_kmajor(const uint16_t* W1, const uint16_t* W2, uint16_t* Wt, int N, int K,
+                              hipStream_t stream, int cu_count) {
+  const size_t runs = 2 * (size_t)N * (size_t)(K / 8);
+  if (runs == 0) return hipSuccess;
+  size_t blocks = (runs + 255) / 256;
+  const size_t cap = (size_t)(cu_count > 0 ? cu_count : 256) * 8;
+  if (blocks > cap) blocks = cap;
+  hipLaunchKernelGGL(pack_kmajor_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, W1, W2, Wt,
+                     N, K);
   return hipGetLastError();
 }
 

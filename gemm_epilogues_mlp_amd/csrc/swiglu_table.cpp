@@ -64,6 +64,8 @@ int select_config(int variant, long long M, long long N, long long K, int cu_cou
   (void)N, (void)K, (void)cu_count;
   // FP8 sync order (measured on the five workloads: 128 x 128 tiles won at
   // M = 2048, the split 256-row tiles at M = 4096 and 8192)
+  // MXFP8: 64 x 128 tiles for small M, the split 256 x 256 tiles above
+  if (variant == VAR_MX) return M <= 192 ? 57 : 56;
   if (variant == VAR_F8_SYNC) return M <= 192 ? 55 : (M <= 3072 ? 54 : 53);
   if (variant == VAR_F8) {
     // FP8: split-K weight streaming up to M = 64, then 64 x 128 tiles, 128-row

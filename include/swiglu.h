@@ -84,8 +84,10 @@ typedef enum {
   SWIGLU_VARIANT_GEMM = 3,       /* plain bf16 GEMM (unfused baseline only)    */
   SWIGLU_VARIANT_FP8 = 4,        /* config descriptions: Kernel-2 order on FP8
                                     inputs (swiglu_forward_fp8, INTERLEAVE)    */
-  SWIGLU_VARIANT_FP8_SYNC = 5    /* config descriptions: Kernel-1 order on FP8
+  SWIGLU_VARIANT_FP8_SYNC = 5,   /* config descriptions: Kernel-1 order on FP8
                                     inputs (swiglu_forward_fp8, SYNC)          */
+  SWIGLU_VARIANT_MXFP8 = 6       /* Kernel-2 order on MXFP8 inputs
+                                    (swiglu_forward_mx; swiglu_query_fp8)      */
 } swiglu_variant_t;
 
 /* Description of one compiled kernel configuration. */
@@ -173,7 +175,7 @@ swiglu_status_t swiglu_query_unfused(swiglu_handle_t h, int64_t M, int64_t N,
 /* Tuned per-shape configurations.  A tuned file (written by the package's
  * tuner, python -m gemm_epilogues_mlp_amd.tune) is text:
  *   swiglu-tuned <signature: 16 hex digits> <arch>        first non-comment line
- *   <variant 1..5> <M> <N> <K> <config id> [ignored provenance]    one per shape
+ *   <variant 1..6> <M> <N> <K> <config id> [ignored provenance]    one per shape
  * with '#' comment lines.  The signature (swiglu_config_signature) identifies
  * the list of compiled configurations; a file written for a library with a
  * different list is refused, so an id can never name the wrong kernel.
@@ -189,8 +191,8 @@ swiglu_status_t swiglu_tuned_check(const char* path, int32_t* n_entries);
 
 /* swiglu_create plus the entries of a tuned file (path NULL: none), which then
  * take precedence over the built-in table for their exact (variant, M, N, K)
- * in swiglu_forward, _ex with config_id < 0, _unfused, _fp8 with config_id < 0
- * and the queries.  The
+ * in swiglu_forward, _ex with config_id < 0, _unfused, _fp8 and _mx with
+ * config_id < 0, and the queries.  The
  * file is read once here; the handle stays immutable.  Errors: those of
  * swiglu_tuned_check, then those of swiglu_create. */
 swiglu_status_t swiglu_create_tuned(swiglu_handle_t* out, int device, const char* path);
@@ -239,8 +241,46 @@ swiglu_status_t swiglu_quantize_fp8(swiglu_handle_t h, const void* X, void* Q, i
 swiglu_status_t swiglu_pack_fp8(swiglu_handle_t h, const void* W1, const void* W2, void* W8,
                                 int64_t K, int64_t N, hipStream_t stream);
 
-/* The configuration swiglu_forward_fp8 with config_id < 0 runs for a shape
- * and variant (AUTO, INTERLEAVE or SYNC). */
+/* ---- MXFP8 inputs ----------------------------------------------------------
+ * The OCP Microscaling format with E4M3 elements, which the TorchInductor/
+ * CuteDSL page (§Impatto sui deployment on-premise) benchmarks: every 32
+ * consecutive k of a row share one E8M0 scale byte e standing for 2^(e-127)
+ * (e = 255: NaN), so element k of a row is 2^(e[k/32] - 127) * value(q[k]).
+ *   A8 [M, K] + SA [M, ks]       activations and their scales
+ *   W8 [2N, K] + SW [2N, ks]     the k-major paired weights (row 2n Gate
+ *                                column n, row 2n+1 Up column n) and scales
+ * Scale rows have a stride of ks bytes, ks a multiple of 16 and >= K/32;
+ * bytes past K/32 are not read by the forward.  The forward needs K % 64 == 0,
+ * N % 8 == 0, 16-byte aligned pointers and every tensor under 2 GiB (else
+ * UNSUPPORTED). */
+
+/* Y = bf16(SiLU(g) * u), g = A x W1 and u = A x W2 on the MX values: the MFMA
+ * applies the block scales to exact E4M3 products, fp32 accumulation.
+ * config_id < 0 uses the table; a given id must be of variant MXFP8 (else
+ * INVALID_ARG).  Y must not overlap any input. */
+swiglu_status_t swiglu_forward_mx(swiglu_handle_t h, const void* A8, const void* SA,
+                                  const void* W8, const void* SW, void* Y, int64_t M, int64_t N,
+                                  int64_t K, int64_t ks, int32_t config_id, hipStream_t stream);
+
+/* MX quantisation of bf16 rows X [rows, K] (k contiguous, K % 32 == 0) into
+ * Q [rows, K] E4M3 and S [rows, ks] E8M0 (ks % 16 == 0, ks >= K/32; bytes
+ * past K/32 are written as 0).  Per block of 32: shared exponent =
+ * floor(log2 max |x|) - 8 (E4M3's largest normal is 1.75 * 2^8), clamped to
+ * [-127, 127] (-127 for a block of zeros or subnormals; NaN is left out of the
+ * maximum, an infinity counts as 2^128); elements x * 2^-shared rounded to
+ * nearest even E4M3, saturating at +-448, NaN kept.  Outputs must not overlap
+ * X or each other. */
+swiglu_status_t swiglu_quantize_mx(swiglu_handle_t h, const void* X, void* Q, void* S,
+                                   int64_t rows, int64_t K, int64_t ks, hipStream_t stream);
+
+/* bf16 Wt [2N, K] from W1, W2 [K, N]: Wt[2n, k] = W1[k, n], Wt[2n+1, k] =
+ * W2[k, n] (the k-major pairing, a bit copy), the input of swiglu_quantize_mx
+ * for the weights.  K % 8 == 0, N % 8 == 0; Wt must not overlap W1 or W2. */
+swiglu_status_t swiglu_pack_kmajor(swiglu_handle_t h, const void* W1, const void* W2, void* Wt,
+                                   int64_t K, int64_t N, hipStream_t stream);
+
+/* The configuration swiglu_forward_fp8 (variant AUTO, INTERLEAVE or SYNC) or
+ * swiglu_forward_mx (variant MXFP8) with config_id < 0 runs for a shape. */
 swiglu_status_t swiglu_query_fp8(swiglu_handle_t h, int64_t M, int64_t N, int64_t K,
                                  swiglu_variant_t variant, swiglu_tile_t* tile);
 

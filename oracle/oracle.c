@@ -488,7 +488,7 @@ int oracle_swiglu_fp8_rows(const uint8_t* a, const uint8_t* w1, const uint8_t* w
  * normal, 448 = 1.75 * 2^8), clamped to [-127, 127]; an all-zero block (or one
  * of NaNs only) takes -127; each element is V_i / 2^shared rounded to E4M3 as
  * above (nearest even, saturating at 448; NaN stays NaN).  NaN elements do not
- * take part in the maximum.
+ * take part in the maximum; an infinity counts as 2^128 (shared exponent 120).
  */
 
 static double e8m0_value(uint8_t e) { return e == 255 ? NAN : ldexp(1.0, (int)e - 127); }
@@ -505,7 +505,9 @@ void oracle_quantize_mx(const float* x, int64_t rows, int64_t K, int64_t ks, uin
       for (int i = 0; i < 32; ++i)
         if (!isnan(v[i]) && fabs((double)v[i]) > amax) amax = fabs((double)v[i]);
       int shared = -127;
-      if (amax > 0.0) {
+      if (isinf(amax)) {
+        shared = 128 - 8; /* an infinity counts as 2^128 */
+      } else if (amax > 0.0) {
         int e2;
         (void)frexp(amax, &e2); /* amax in [2^(e2-1), 2^e2): floor(log2 amax) = e2 - 1 */
         shared = (e2 - 1) - 8;

@@ -106,11 +106,17 @@ bool run_config(int id, int M, int N, int K) {
     a.W2 = nullptr;
     a.ldw = N;
   }
-  if (c->variant == VAR_F8 || c->variant == VAR_F8_SYNC) {  // byte tensors: A8 [M, K], W8 [2N, K]
+  if (c->variant == VAR_F8 || c->variant == VAR_F8_SYNC || c->variant == VAR_MX) {
+    // byte tensors: A8 [M, K], W8 [2N, K]; MX scales SA [M, ks], SW [2N, ks]
     a.A = alloc16(((size_t)M * K + 1) / 2, "A8");
     a.W1 = alloc16((size_t)N * K, "W8");
     a.ldw = K;
     a.scale_g = a.scale_u = 1.0f;
+    if (c->variant == VAR_MX) {
+      a.ks = (K / 32 + 15) / 16 * 16;
+      a.SA = (const uint8_t*)alloc16(((size_t)M * a.ks + 1) / 2, "SA");
+      a.SW = (const uint8_t*)alloc16((size_t)N * a.ks, "SW");
+    }
   }
   a.Y = alloc16((size_t)M * N, "Y");
   a.ldy = N;
@@ -147,6 +153,20 @@ bool run_elementwise(size_t n) {
   uint8_t* w8 = (uint8_t*)alloc16((size_t)K * N, "W8");
   launch_pack_f8(w1, w2, w8, N, K, nullptr, 256);
   free_all();
+  // MX quantisation of rows of K = 96 (scale stride 16), and the bf16 k-major pack
+  {
+    const int Kq = 96, ksq = 16, rows = (int)(n / Kq);
+    uint16_t* xq = alloc16((size_t)rows * Kq, "Xmx");
+    uint8_t* qq = (uint8_t*)alloc16((size_t)rows * Kq / 2, "Qmx");
+    uint8_t* sq = (uint8_t*)alloc16((size_t)rows * ksq / 2, "Smx");
+    launch_quantize_mx(xq, qq, sq, rows, Kq, ksq, nullptr, 256);
+    const int Kp = 16, Np = (int)(n / 16);
+    uint16_t* p1 = alloc16((size_t)Kp * Np, "W1bf");
+    uint16_t* p2 = alloc16((size_t)Kp * Np, "W2bf");
+    uint16_t* pt = alloc16((size_t)2 * Kp * Np, "Wt");
+    launch_pack_kmajor(p1, p2, pt, Np, Kp, nullptr, 256);
+    free_all();
+  }
   printf("%s: %s\n", g_ctx.c_str(), g_errors == before ? "ok" : "OUT OF BOUNDS");
   return g_errors == before;
 }
@@ -174,11 +194,15 @@ int main(int argc, char** argv) {
   const int shapes[][3] = {{300, 264, 200}, {37, 136, 520}, {1, 8, 8}, {129, 520, 96}, {40, 72, 0}};
   // FP8 tiles need K % 16 == 0: the same shapes with K rounded up to 16
   const int shapes_f8[][3] = {{300, 264, 208}, {37, 136, 528}, {1, 8, 16}, {129, 520, 96}, {40, 72, 0}};
+  // MXFP8 tiles need K % 64 == 0
+  const int shapes_mx[][3] = {{300, 264, 256}, {37, 136, 576}, {1, 8, 64}, {129, 520, 128}, {40, 72, 0}};
   for (int id : ids) {
     if (one_shape) {
       run_config(id, shape[0], shape[1], shape[2]);
     } else {
-      if (config_at(id) && (config_at(id)->variant == VAR_F8 || config_at(id)->variant == VAR_F8_SYNC))
+      if (config_at(id) && config_at(id)->variant == VAR_MX)
+        for (const auto& s : shapes_mx) run_config(id, s[0], s[1], s[2]);
+      else if (config_at(id) && (config_at(id)->variant == VAR_F8 || config_at(id)->variant == VAR_F8_SYNC))
         for (const auto& s : shapes_f8) run_config(id, s[0], s[1], s[2]);
       else
         for (const auto& s : shapes) run_config(id, s[0], s[1], s[2]);

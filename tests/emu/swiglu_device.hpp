@@ -189,6 +189,10 @@ inline f32x16 mfma32(const u32x4&, const u32x4&, const f32x16& c) { return c; }
 inline f32x4 mfma16(const u32x4&, const u32x4&, const f32x4& c) { return c; }
 inline f32x16 mfma32_f8(const u32x4 (&)[2], const u32x4 (&)[2], const f32x16& c) { return c; }
 inline f32x4 mfma16_f8(const u32x4 (&)[2], const u32x4 (&)[2], const f32x4& c) { return c; }
+inline f32x16 mfma32_f8_scaled(const u32x4 (&)[2], const u32x4 (&)[2], const f32x16& c, uint32_t,
+                               uint32_t) {
+  return c;
+}
 inline uint32_t e4m3_code(float v) {
   uint32_t bits;
   memcpy(&bits, &v, 4);

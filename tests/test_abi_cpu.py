@@ -66,6 +66,10 @@ def test_null_handle_and_bad_arguments_rejected():
     assert lib.swiglu_quantize_fp8(None, 16, 16, 16, 1.0, None) == sw.ERR_INVALID_ARG
     assert lib.swiglu_pack_fp8(None, 16, 16, 16, 16, 8, None) == sw.ERR_INVALID_ARG
     assert lib.swiglu_query_fp8(None, 8, 8, 16, 0, None) == sw.ERR_INVALID_ARG
+    assert lib.swiglu_forward_mx(None, 16, 16, 16, 16, 16, 8, 8, 64, 16, -1, None) == \
+        sw.ERR_INVALID_ARG
+    assert lib.swiglu_quantize_mx(None, 16, 16, 16, 1, 32, 16, None) == sw.ERR_INVALID_ARG
+    assert lib.swiglu_pack_kmajor(None, 16, 16, 16, 8, 8, None) == sw.ERR_INVALID_ARG
 
 
 def test_status_strings_and_workspace_size():
@@ -79,7 +83,7 @@ def test_config_list_is_consistent():
     n = sw.swiglu_config_count()
     assert n > 0
     seen = {sw.VARIANT_SYNC: 0, sw.VARIANT_INTERLEAVE: 0, sw.VARIANT_GEMM: 0, sw.VARIANT_FP8: 0,
-            sw.VARIANT_FP8_SYNC: 0}
+            sw.VARIANT_FP8_SYNC: 0, sw.VARIANT_MXFP8: 0}
     for i in range(n):
         c = sw.swiglu_config_info(i)
         assert c["id"] == i
@@ -93,7 +97,7 @@ def test_config_list_is_consistent():
         assert c["waves"] * 64 <= 1024
         if c["family"] in (0, 2):
             assert c["bm"] % 32 == 0 and c["bn"] % 32 == 0
-        if c["variant"] in (sw.VARIANT_FP8, sw.VARIANT_FP8_SYNC):
+        if c["variant"] in (sw.VARIANT_FP8, sw.VARIANT_FP8_SYNC, sw.VARIANT_MXFP8):
             assert (c["family"], c["bk"]) in ((0, 64), (1, 128))
     assert all(v > 0 for v in seen.values())
 

@@ -252,6 +252,12 @@ def test_quantize_mx_hand_cases():
     assert s[1, 1] == 0 and np.all(q[1, 32:] == 0)          # all-zero block: e = 0, codes 0
     assert s[2, 0] == 0
     assert np.all(s[:, 2:] == 0)                             # padding bytes of the scale rows
+    y = np.zeros((1, 64), np.float32)
+    y[0, 0], y[0, 1] = np.inf, 1.0                           # infinity counts as 2^128
+    y[0, 32], y[0, 33] = np.nan, 2.0                         # NaN is left out of the maximum
+    q, s = oracle.quantize_mx(y)
+    assert s[0, 0] == 127 + 120 and q[0, 0] == 0x7E and q[0, 1] == 0
+    assert s[0, 1] == 127 - 7 and q[0, 32] == 0x7F and q[0, 33] == 0x78
 
 
 @settings(max_examples=30, deadline=None)
