@@ -205,12 +205,14 @@ __device__ __forceinline__ f32x16 mfma32_f8(const u32x4 (&a)[2], const u32x4 (&b
 // covers the k block of 32 that lanes l % 32 and l % 32 + 32 hold in bytes
 // 16 (l / 32) .. 16 (l / 32) + 15 of their fragments (block 0: bytes 0-15 of
 // both lane halves, block 1: bytes 16-31), for row or column l % 32.
+// SEL0 / SEL1 pick the byte of sa_src0 / sb_src1 that holds the scale.
+template <int SEL0, int SEL1>
 __device__ __forceinline__ f32x16 mfma32_f8_scaled(const u32x4 (&a)[2], const u32x4 (&b)[2],
                                                    const f32x16& c, uint32_t sa_src0,
                                                    uint32_t sb_src1) {
   const i32x8 x = __builtin_bit_cast(i32x8, __builtin_shufflevector(a[0], a[1], 0, 1, 2, 3, 4, 5, 6, 7));
   const i32x8 y = __builtin_bit_cast(i32x8, __builtin_shufflevector(b[0], b[1], 0, 1, 2, 3, 4, 5, 6, 7));
-  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(x, y, c, 0, 0, 0, (int)sa_src0, 0,
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(x, y, c, 0, 0, SEL0, (int)sa_src0, SEL1,
                                                           (int)sb_src1);
 }
 

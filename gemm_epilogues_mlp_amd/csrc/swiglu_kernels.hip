@@ -1081,15 +1081,32 @@ __device__ __forceinline__ void f8_tile(const uint8_t* __restrict__ A,
   const int h = lane >> 5;
   const int a_row = wm * C::WTM + (lane & 31);  // + 32 fa
   const int w_row = wn * C::WTW + (lane & 31);  // + 32 fw
-  auto read = [&](const uint8_t* tile, int row, u32x4 (&f)[2]) __attribute__((always_inline)) {
-    const uint8_t* r = tile + row * C::BK;
-    f[0] = *reinterpret_cast<const u32x4*>(r + ((h ^ C::swz(row)) * 16));
-    f[1] = *reinterpret_cast<const u32x4*>(r + (((2 + h) ^ C::swz(row)) * 16));
+  // The swizzle depends on row bits 1-3 only, so the rows +32, +64, ... of a
+  // lane's fragments share it: one pair of per-lane offsets per tile, the
+  // fragment index a compile-time displacement of 32 rows.
+  const int a_lo = a_row * C::BK + ((h ^ C::swz(a_row)) * 16);
+  const int a_hi = a_row * C::BK + (((2 + h) ^ C::swz(a_row)) * 16);
+  const int w_lo = C::A_BYTES + w_row * C::BK + ((h ^ C::swz(w_row)) * 16);
+  const int w_hi = C::A_BYTES + w_row * C::BK + (((2 + h) ^ C::swz(w_row)) * 16);
+  // fragment f of the A tile (f < FA) or of the weight tile (W) in a stage
+  auto readA = [&](const uint8_t* stage, int f, u32x4 (&d)[2]) __attribute__((always_inline)) {
+    d[0] = *reinterpret_cast<const u32x4*>(stage + a_lo + f * 32 * C::BK);
+    d[1] = *reinterpret_cast<const u32x4*>(stage + a_hi + f * 32 * C::BK);
+  };
+  auto readW = [&](const uint8_t* stage, int f, u32x4 (&d)[2]) __attribute__((always_inline)) {
+    d[0] = *reinterpret_cast<const u32x4*>(stage + w_lo + f * 32 * C::BK);
+    d[1] = *reinterpret_cast<const u32x4*>(stage + w_hi + f * 32 * C::BK);
   };
   u32x4 wf[C::FW][2];
   u32x4 af[2][C::FA][2];
-  // MX: scale bytes of the lane's rows for the current step (A by parity)
-  uint32_t scw[C::FW], sca[2][C::FA];
+  // MX: scale bytes of the lane's rows for the current step, packed (the MFMA
+  // selects a byte): weight block i in byte i of scw, activation block j of
+  // parity P in byte 2 P + j of sca
+  static_assert(!C::MX || (C::FW <= 4 && C::FA <= 2), "packed scale bytes");
+  uint32_t scw = 0, sca = 0;
+  auto put = [](uint32_t& w, int byte, uint32_t v) __attribute__((always_inline)) {
+    w = (w & ~(0xffu << (8 * byte))) | (v << (8 * byte));
+  };
   // the scale byte of tile row r (A rows first, then W8 rows) for step s:
   // group s / 8, block 2 s + h of the row (this lane's fragment half)
   auto scale_of = [&](int s, int r) __attribute__((always_inline)) -> uint32_t {
@@ -1119,29 +1136,34 @@ __device__ __forceinline__ void f8_tile(const uint8_t* __restrict__ A,
     const uint8_t* nxt = smem + C::ST0 + Next::value * C::STAGE_BYTES;
     wait_vmcnt<(STAGES - 2) * C::TLOADS>();
     __syncthreads();
-#pragma unroll
-    for (int q = 0; q < NMF; ++q) {
-      const int i = q / C::FA, j = q % C::FA;
+    // MFMA slot q (compile time): MFMA (i, j), then its share of the reads of
+    // step it+1 and of the DMA of step it+STAGES
+    auto slot = [&](auto q_c) __attribute__((always_inline)) {
+      constexpr int q = decltype(q_c)::value;
+      constexpr int i = q / C::FA, j = q % C::FA;
       if constexpr (C::MX)
-        acc[PH][i][j] = mfma32_f8_scaled(wf[i], af[P][j], acc[PH][i][j], scw[i], sca[P][j]);
+        acc[PH][i][j] = mfma32_f8_scaled<i, 2 * P + j>(wf[i], af[P][j], acc[PH][i][j], scw, sca);
       else
         acc[PH][i][j] = mfma32_f8(wf[i], af[P][j], acc[PH][i][j]);
-      if (q < C::FA) {
-        read(nxt, a_row + 32 * q, af[P ^ 1][q]);
-        if constexpr (C::MX) sca[P ^ 1][q] = scale_of(it + 1, a_row + 32 * q);
+      if constexpr (q < C::FA) {
+        readA(nxt, q, af[P ^ 1][q]);
+        if constexpr (C::MX) put(sca, 2 * (P ^ 1) + q, scale_of(it + 1, a_row + 32 * q));
       }
-      if (j == C::FA - 1) {
-        read(nxt + C::A_BYTES, w_row + 32 * i, wf[i]);
-        if constexpr (C::MX) scw[i] = scale_of(it + 1, BM + w_row + 32 * i);
+      if constexpr (j == C::FA - 1) {
+        readW(nxt, i, wf[i]);
+        if constexpr (C::MX) put(scw, i, scale_of(it + 1, BM + w_row + 32 * i));
       }
-      if (q >= DBEGIN) {
+      if constexpr (q >= DBEGIN) {
 #pragma unroll
         for (int x = (q - DBEGIN) * C::TLOADS / DSLOTS; x < (q - DBEGIN + 1) * C::TLOADS / DSLOTS;
              ++x)
           dma(it + STAGES, st_c, x);
       }
       __builtin_amdgcn_sched_barrier(0);
-    }
+    };
+    [&]<int... Q>(std::integer_sequence<int, Q...>) __attribute__((always_inline)) {
+      (slot(std::integral_constant<int, Q>{}), ...);
+    }(std::make_integer_sequence<int, NMF>{});
   };
   // steps [b, e) with b on a ring boundary: whole rounds, then the rest
   auto run = [&](int b, int e, auto phase_c) __attribute__((always_inline)) {
@@ -1168,13 +1190,13 @@ __device__ __forceinline__ void f8_tile(const uint8_t* __restrict__ A,
   __syncthreads();
 #pragma unroll
   for (int j = 0; j < C::FA; ++j) {
-    read(smem + C::ST0, a_row + 32 * j, af[0][j]);
-    if constexpr (C::MX) sca[0][j] = scale_of(0, a_row + 32 * j);
+    readA(smem + C::ST0, j, af[0][j]);
+    if constexpr (C::MX) put(sca, j, scale_of(0, a_row + 32 * j));
   }
 #pragma unroll
   for (int i = 0; i < C::FW; ++i) {
-    read(smem + C::ST0 + C::A_BYTES, w_row + 32 * i, wf[i]);
-    if constexpr (C::MX) scw[i] = scale_of(0, BM + w_row + 32 * i);
+    readW(smem + C::ST0, i, wf[i]);
+    if constexpr (C::MX) put(scw, i, scale_of(0, BM + w_row + 32 * i));
   }
 
   if constexpr (kSync) {

@@ -189,8 +189,10 @@ inline f32x16 mfma32(const u32x4&, const u32x4&, const f32x16& c) { return c; }
 inline f32x4 mfma16(const u32x4&, const u32x4&, const f32x4& c) { return c; }
 inline f32x16 mfma32_f8(const u32x4 (&)[2], const u32x4 (&)[2], const f32x16& c) { return c; }
 inline f32x4 mfma16_f8(const u32x4 (&)[2], const u32x4 (&)[2], const f32x4& c) { return c; }
+template <int SEL0, int SEL1>
 inline f32x16 mfma32_f8_scaled(const u32x4 (&)[2], const u32x4 (&)[2], const f32x16& c, uint32_t,
                                uint32_t) {
+  static_assert(SEL0 >= 0 && SEL0 < 4 && SEL1 >= 0 && SEL1 < 4, "byte select");
   return c;
 }
 inline uint32_t e4m3_code(float v) {
