@@ -44,7 +44,8 @@ def parse():
                    help="minimum footprint of the rotated buffers (bytes)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-unfused", action="store_true")
-    p.add_argument("--no-fp8", action="store_true", help="skip the FP8 (E4M3) side measurement")
+    p.add_argument("--no-fp8", action="store_true",
+                   help="skip the FP8 (E4M3) and MXFP8 side measurements")
     p.add_argument("--copy-calibration", action="store_true",
                    help="also run a 1 GiB device copy (counter calibration runs)")
     return p.parse_args()
@@ -169,6 +170,7 @@ def main():
     fp8 = None
     if not args.no_fp8:
         fp8 = fp8_side(sw, h, wl, a_np, w1_np, w2_np, a0, w10, w20, timed, stream, args, ms)
+        fp8["mxfp8"] = mx_side(sw, h, wl, a0, w10, w20, timed, stream, args, ms)
 
     if args.copy_calibration:
         src = torch.empty(2 ** 30 // 2, dtype=torch.int16, device=dev)
@@ -276,6 +278,50 @@ def fp8_side(sw, h, wl, a_np, w1_np, w2_np, a0, w10, w20, timed, stream, args, b
            "format": "OCP E4M3, per-tensor fp32 scales", "rotated_sets": nsets,
            "tile": sw.swiglu_query_fp8(h, M, N, K, sw.VARIANT_AUTO)}
     del sets, a8, w8
+    return out
+
+
+def mx_side(sw, h, wl, a0, w10, w20, timed, stream, args, bf16_ms):
+    """The same workload on MXFP8 inputs (E4M3 elements, an E8M0 scale per 32
+    consecutive k): weights paired k-major and quantised once on the device,
+    activations quantised on the device (timed separately), then the fused
+    MXFP8 forward timed like the bf16 one."""
+    import numpy as np
+    import torch
+    M, K, N = wl.M, wl.K, wl.N
+    dev = a0.device
+    ks = sw.mx_scale_stride(K)
+    wt = torch.empty((2 * N, K), dtype=torch.int16, device=dev)
+    sw.swiglu_pack_kmajor(h, w10, w20, wt, K, N, stream)
+    qw = torch.empty((2 * N, K), dtype=torch.uint8, device=dev)
+    sW = torch.empty((2 * N, ks), dtype=torch.uint8, device=dev)
+    sw.swiglu_quantize_mx(h, wt, qw, sW, 2 * N, K, ks, stream)
+    del wt
+    qa = torch.empty((M, K), dtype=torch.uint8, device=dev)
+    sa = torch.empty((M, ks), dtype=torch.uint8, device=dev)
+    sw.swiglu_quantize_mx(h, a0, qa, sa, M, K, ks, stream)
+    bytes_mx = M * K + 2 * N * K + 2 * M * N + (M + 2 * N) * ks
+    nsets = max(1, int(np.ceil(args.rotate_bytes / bytes_mx)))
+    sets = [tuple(t if i == 0 else t.clone() for t in (qa, sa, qw, sW)) +
+            (torch.empty((M, N), dtype=torch.int16, device=dev),) for i in range(nsets)]
+    torch.cuda.synchronize()
+
+    def step(i):
+        A8, SA, W8, SW, y = sets[i % nsets]
+        sw.swiglu_forward_mx(h, A8, SA, W8, SW, y, M, N, K, ks, -1, stream)
+
+    xms, batches = timed(step, args.steps, args.warmup)
+    qms, _ = timed(lambda i: sw.swiglu_quantize_mx(h, a0, qa, sa, M, K, ks, stream),
+                   max(10, args.steps // 2), 3, batches=1)
+    tf = wl.flops / (xms * 1e-3) / 1e12
+    out = {"ms_per_step": round(xms, 5), "tflops": round(tf, 2),
+           "pct_fp8_mfma_peak": round(100 * tf / PEAK_FP8_TFLOPS, 2),
+           "speedup_vs_bf16": round(bf16_ms / xms, 3),
+           "min_batch_ms_per_step": round(min(batches), 5),
+           "quantize_activations_ms": round(qms, 5),
+           "format": "OCP MX: E4M3 elements, E8M0 scale per 32 along K", "rotated_sets": nsets,
+           "tile": sw.swiglu_query_fp8(h, M, N, K, sw.VARIANT_MXFP8)}
+    del sets, qa, sa, qw, sW
     return out
 
 
