@@ -48,6 +48,13 @@ CASES = [
     (2048, 8960, 40, [40, 41, 42]),    # 1.5B M and N: 512 big + 48 split
     (128, 4864, 40, [3, 29, 30]),      # 0.5B M and N
     (16, 18944, 64, [23, 12, 18]),     # 7B decode M and N
+    # FP8 / MXFP8 (K a multiple of 64): split-tail tiles at 1.5B M and N in
+    # both orders and with block scales, the small-M tiles and the streaming
+    # kernel at the 0.5B and decode shapes
+    (2048, 8960, 1536, [43, 53, 56]),
+    (2008, 4216, 128, [43, 53, 56]),   # whole rounds plus a short split round
+    (128, 4864, 896, [46, 55, 57]),
+    (16, 18944, 3584, [52, 57]),
 ]
 
 
@@ -60,12 +67,16 @@ def test_table_configs_at_workload_sizes(emu, case):
 
 
 # tensors just under the 2 GiB limit (largest byte offsets the kernels form):
-# A = 2 * 65536 * 16376 B, and W_fused = 4 * 16376 * 32768 B; only the last
-# workgroups of each launch are emulated (they touch the largest offsets)
+# A = 2 * 65536 * 16376 B, and W_fused = 4 * 16376 * 32768 B (bf16), and the
+# byte tensors of the FP8 kernels; only the last workgroups of each launch are
+# emulated (they touch the largest offsets)
 LIMIT_CASES = [
     (65536, 64, 16376, [40, 42, 41], 4),
     (16, 32768, 16376, [4, 11, 18, 23, 12], 8),
     (256, 32768, 16376, [1, 8, 16], 4),
+    # byte tensors: A8 = 65536 x 32704 B, W8 = 2 x 32768 x 32704 B (K % 64 == 0)
+    (65536, 64, 32704, [43, 53, 56], 4),
+    (16, 32768, 32704, [47, 52, 55, 57], 8),
 ]
 
 
