@@ -11,7 +11,8 @@ compiled configurations by its signature, so it cannot outlive a rebuild
 that changes that list.
 
   python -m gemm_epilogues_mlp_amd.tune --shapes 2048x1536x8960 --out tuned.txt
-  (shapes are M x K x N, the order of the workload names)
+  (shapes are M x K x N, the order of the workload names; --variants picks
+  among interleave, sync, gemm, fp8, fp8-sync and mxfp8)
 """
 from __future__ import annotations
 
@@ -22,7 +23,11 @@ import sys
 
 import gemm_epilogues_mlp_amd as sw
 
-VARIANTS = {"interleave": sw.VARIANT_INTERLEAVE, "sync": sw.VARIANT_SYNC, "gemm": sw.VARIANT_GEMM}
+VARIANTS = {"interleave": sw.VARIANT_INTERLEAVE, "sync": sw.VARIANT_SYNC, "gemm": sw.VARIANT_GEMM,
+            "fp8": sw.VARIANT_FP8, "fp8-sync": sw.VARIANT_FP8_SYNC, "mxfp8": sw.VARIANT_MXFP8}
+# the forward's variant argument for each FP8 configuration family
+_FP8_ORDER = {sw.VARIANT_FP8: sw.VARIANT_INTERLEAVE, sw.VARIANT_FP8_SYNC: sw.VARIANT_SYNC,
+              sw.VARIANT_MXFP8: sw.VARIANT_MXFP8}
 
 
 def _candidates(variant, M, configs=None):
@@ -51,10 +56,23 @@ def _time_configs(h, variant, M, N, K, ids, reps, rotate_bytes, seed=0):
         return (torch.randn(shape, device=dev, generator=g) * scale).to(torch.bfloat16).view(
             torch.int16)
 
-    per_set = 2 * M * K + 4 * K * N + 2 * M * N
+    fp8 = variant in _FP8_ORDER
+    ks = sw.mx_scale_stride(K)
+    per_set = (M * K + 2 * K * N + 2 * M * N + (M + 2 * N) * ks) if fp8 else \
+        (2 * M * K + 4 * K * N + 2 * M * N)
     nsets = max(1, min(16, -(-int(rotate_bytes) // max(per_set, 1))))
     sets = []
     for _ in range(nsets):
+        if fp8:
+            # random finite E4M3 codes and E8M0 scales near 2^-7 (values do not
+            # change the timing)
+            codes = lambda shape: torch.randint(0, 0x7E, shape, device=dev, generator=g,
+                                                dtype=torch.uint8)
+            y = torch.empty((M, N), dtype=torch.int16, device=dev)
+            sets.append((codes((M, K)), codes((2 * N, K)),
+                         torch.full((M, ks), 120, dtype=torch.uint8, device=dev),
+                         torch.full((2 * N, ks), 120, dtype=torch.uint8, device=dev), y, None))
+            continue
         a = rnd((M, K))
         w1, w2 = rnd((K, N), K ** -0.5), rnd((K, N), K ** -0.5)
         wf = torch.empty((K, 2 * N), dtype=torch.int16, device=dev)
@@ -67,6 +85,14 @@ def _time_configs(h, variant, M, N, K, ids, reps, rotate_bytes, seed=0):
     stream = torch.cuda.current_stream()
 
     def call(i, cid):
+        if fp8:
+            a8, w8, sa, sw8, y, _ = sets[i % nsets]
+            if variant == sw.VARIANT_MXFP8:
+                sw.swiglu_forward_mx(h, a8, sa, w8, sw8, y, M, N, K, ks, cid, stream)
+            else:
+                sw.swiglu_forward_fp8(h, a8, w8, y, M, N, K, config_id=cid, stream=stream,
+                                      variant=_FP8_ORDER[variant])
+            return
         a, w1, w2, wf, y, ws = sets[i % nsets]
         if variant == sw.VARIANT_INTERLEAVE:
             sw.swiglu_forward_ex(h, a, wf, None, y, M, N, K, sw.LAYOUT_INTERLEAVED, variant, cid,
@@ -128,6 +154,8 @@ def tune(shapes, variants=("interleave", "sync", "gemm"), out=None, merge=None, 
                 v = VARIANTS[name]
                 if v == sw.VARIANT_GEMM:
                     builtin = sw.swiglu_query_unfused(h, M, N, K)["id"]
+                elif v in _FP8_ORDER:
+                    builtin = sw.swiglu_query_fp8(h, M, N, K, _FP8_ORDER[v])["id"]
                 else:
                     layout = sw.LAYOUT_INTERLEAVED if v == sw.VARIANT_INTERLEAVE else \
                         sw.LAYOUT_SEPARATE
@@ -171,7 +199,8 @@ def _parse_shapes(text):
 def main(argv=None):
     p = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     p.add_argument("--shapes", required=True, help="MxKxN[,MxKxN...]")
-    p.add_argument("--variants", default="interleave,sync,gemm")
+    p.add_argument("--variants", default="interleave,sync,gemm",
+                   help="any of " + ",".join(VARIANTS))
     p.add_argument("--out", required=True)
     p.add_argument("--merge", default=None, help="existing tuned file to extend")
     p.add_argument("--margin", type=float, default=0.03)

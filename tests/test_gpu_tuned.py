@@ -91,3 +91,63 @@ def test_tuner_writes_a_valid_file(tmp_path):
     h = sw.swiglu_create_tuned(0, str(out))
     sw.swiglu_destroy(h)
     assert n <= 2
+
+
+def test_tuner_covers_the_fp8_families(tmp_path):
+    """The tuner times the FP8 (both orders) and MXFP8 configurations and its
+    file is accepted; an FP8 entry it writes (or one written by hand) steers
+    swiglu_forward_fp8 / _mx with config_id < 0, with results within the bar."""
+    Mf, Kf, Nf = 192, 256, 264
+    out = tmp_path / "t8.txt"
+    msgs = []
+    T.tune([(Mf, Kf, Nf)], variants=("fp8", "fp8-sync", "mxfp8"), out=str(out), reps=3,
+           margin=0.0, log=msgs.append)
+    log("\n".join(msgs))
+    assert len(msgs) == 3
+    sw.swiglu_tuned_check(str(out))
+    # a hand-written entry for each family: the first configuration that is
+    # not the table's choice
+    h = sw.swiglu_create(0)
+    try:
+        picks = {}
+        for v, order in [(sw.VARIANT_FP8, sw.VARIANT_INTERLEAVE), (sw.VARIANT_FP8_SYNC, sw.VARIANT_SYNC),
+                         (sw.VARIANT_MXFP8, sw.VARIANT_MXFP8)]:
+            builtin = sw.swiglu_query_fp8(h, Mf, Nf, Kf, order)["id"]
+            picks[v] = next(i for i in range(sw.swiglu_config_count())
+                            if sw.swiglu_config_info(i)["variant"] == v and i != builtin
+                            and sw.swiglu_config_info(i)["family"] == 0)
+    finally:
+        sw.swiglu_destroy(h)
+    path = tmp_path / "hand8.txt"
+    path.write_text(f"swiglu-tuned {sw.swiglu_config_signature():016x} gfx950\n" +
+                    "".join(f"{v} {Mf} {Nf} {Kf} {c}\n" for v, c in picks.items()))
+    h = sw.swiglu_create_tuned(0, str(path))
+    try:
+        assert sw.swiglu_query_fp8(h, Mf, Nf, Kf, sw.VARIANT_AUTO)["id"] == picks[sw.VARIANT_FP8]
+        assert sw.swiglu_query_fp8(h, Mf, Nf, Kf, sw.VARIANT_SYNC)["id"] == \
+            picks[sw.VARIANT_FP8_SYNC]
+        assert sw.swiglu_query_fp8(h, Mf, Nf, Kf, sw.VARIANT_MXFP8)["id"] == \
+            picks[sw.VARIANT_MXFP8]
+        t = __import__("torch")
+        a, w1, w2 = I.make_inputs(Mf, Kf, Nf, 31)
+        qa, sa = oracle.quantize_mx(I.bf16_bits_to_f32(a))
+        qw, sW = oracle.quantize_mx(I.bf16_bits_to_f32(oracle.pack_kmajor_bf16(w1, w2)))
+        d8 = lambda x: t.from_numpy(np.ascontiguousarray(x)).cuda()
+        y = t.full((Mf, Nf), -1, dtype=t.int16, device="cuda")
+        sw.swiglu_forward_mx(h, d8(qa), d8(sa), d8(qw), d8(sW), y, Mf, Nf, Kf, sa.shape[1])
+        t.cuda.synchronize()
+        assert_parity(host(y), oracle.swiglu_mx_rows(qa, sa, qw, sW), "tuned MXFP8 forward")
+        # per-tensor FP8 (scale = max|x| / 448 per tensor), both orders
+        xs = [I.bf16_bits_to_f32(x) for x in (a, w1, w2)]
+        sc = [float(np.float32(np.max(np.abs(x)) / np.float32(448.0))) for x in xs]
+        a8, w18, w28 = (oracle.quantize_e4m3(x, np.float32(1.0) / np.float32(c))
+                        for x, c in zip(xs, sc))
+        ref = oracle.swiglu_fp8_rows(a8, w18, w28, *sc)
+        for order in (sw.VARIANT_AUTO, sw.VARIANT_SYNC):
+            y.fill_(-1)
+            sw.swiglu_forward_fp8(h, d8(a8), d8(oracle.pack_fp8_kmajor(w18, w28)), y, Mf, Nf, Kf,
+                                  *sc, variant=order)
+            t.cuda.synchronize()
+            assert_parity(host(y), ref, f"tuned FP8 forward, order {order}")
+    finally:
+        sw.swiglu_destroy(h)
