@@ -440,7 +440,8 @@ swiglu_status_t swiglu_quantize_mx(swiglu_handle_t h, const void* X, void* Q, vo
   if (!X || !Q || !S || ks < K / 32) return SWIGLU_ERR_INVALID_ARG;
   if (K % 32 != 0 || ks % 16 != 0) return SWIGLU_ERR_UNSUPPORTED;
   if (!aligned16(X) || !aligned16(Q) || !aligned16(S)) return SWIGLU_ERR_UNSUPPORTED;
-  if (rows > kMaxDim || K > kMaxDim || rows * K > (1LL << 40) || rows * ks > (1LL << 40))
+  if (rows > kMaxDim || K > kMaxDim || ks > kMaxDim || rows * K > (1LL << 40) ||
+      rows * ks > (1LL << 40))
     return SWIGLU_ERR_UNSUPPORTED;
   if (overlaps(Q, rows * K, X, 2 * rows * K) || overlaps(S, rows * ks, X, 2 * rows * K) ||
       overlaps(S, rows * ks, Q, rows * K))
