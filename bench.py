@@ -38,7 +38,8 @@ def parse():
     p.add_argument("--steps", type=int, default=200)
     p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--workload", default="qwen2.5-1.5b-mlp")
-    p.add_argument("--layout", choices=["auto", "separate", "interleaved"], default="auto")
+    p.add_argument("--layout", choices=["auto", "separate", "interleaved", "packed"],
+                   default="auto")
     p.add_argument("--config", type=int, default=-1, help="force a fused config id")
     p.add_argument("--rotate-bytes", type=float, default=1.0 * 2 ** 30,
                    help="minimum footprint of the rotated buffers (bytes)")
@@ -81,7 +82,8 @@ def main():
         _, _, rec = sw.swiglu_query(h, M, N, K, sw.LAYOUT_SEPARATE)
         layout = rec
     else:
-        layout = sw.LAYOUT_INTERLEAVED if args.layout == "interleaved" else sw.LAYOUT_SEPARATE
+        layout = {"interleaved": sw.LAYOUT_INTERLEAVED, "separate": sw.LAYOUT_SEPARATE,
+                  "packed": sw.LAYOUT_PACKED}[args.layout]
     variant, tile, _ = sw.swiglu_query(h, M, N, K, layout)
     if args.config >= 0:
         tile = sw.swiglu_config_info(args.config)
@@ -90,13 +92,16 @@ def main():
     if layout == sw.LAYOUT_INTERLEAVED:
         wf0 = torch.empty((K, 2 * N), dtype=torch.int16, device=dev)
         sw.swiglu_pack_interleaved(h, w10, w20, wf0, K, N)
+    elif layout == sw.LAYOUT_PACKED:  # fragment-ordered W_fused (offline pack)
+        wf0 = torch.empty((sw.swiglu_packed_bytes(N, K) // 2,), dtype=torch.int16, device=dev)
+        sw.swiglu_pack_fragments(h, w10, w20, wf0, K, N)
 
     set_bytes = wl.fused_bytes
     nsets = max(1, int(np.ceil(args.rotate_bytes / set_bytes)))
     sets = []
     for i in range(nsets):
         a = a0 if i == 0 else a0.clone()
-        if layout == sw.LAYOUT_INTERLEAVED:
+        if layout in (sw.LAYOUT_INTERLEAVED, sw.LAYOUT_PACKED):
             ws = (wf0 if i == 0 else wf0.clone(), None)
         else:
             ws = (w10 if i == 0 else w10.clone(), w20 if i == 0 else w20.clone())
@@ -210,8 +215,9 @@ def main():
         "dtype": "bf16",
         "data": "synthetic (seeded N(0,1) activations, N(0,1/K) weights)",
         "config": {"workload": wl.name, "M": M, "K": K, "N": N,
-                   "layout": "interleaved" if layout == sw.LAYOUT_INTERLEAVED else "separate",
-                   "variant": "interleave" if variant == sw.VARIANT_INTERLEAVE else "sync",
+                   "layout": {0: "separate", 1: "interleaved", 2: "packed"}[layout],
+                   "variant": {sw.VARIANT_INTERLEAVE: "interleave", sw.VARIANT_SYNC: "sync",
+                               sw.VARIANT_PACKED: "interleave (fragment-ordered weights)"}[variant],
                    "tile": tile, "rotated_sets": nsets, "parallelism": "single-gpu"},
         "batches": {"n": len(fused_batches),
                     "median_ms_per_step": round(sorted(fused_batches)[len(fused_batches) // 2], 5),
@@ -336,7 +342,8 @@ def counter_traffic(workload, layout, tile):
         data = json.load(open(path))
     except ValueError:
         return None
-    key = f"{workload}/{'interleaved' if layout else 'separate'}/config{tile.get('id')}"
+    name = {0: "separate", 1: "interleaved", 2: "packed"}.get(layout, str(layout))
+    key = f"{workload}/{name}/config{tile.get('id')}"
     entry = data.get(key)
     if not entry or entry.get("kernel_source_sha") != kernel_source_hash():
         return None

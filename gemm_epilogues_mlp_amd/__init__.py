@@ -26,16 +26,17 @@ __all__ = [
     "LAYOUT_SEPARATE", "LAYOUT_INTERLEAVED",
     "VARIANT_AUTO", "VARIANT_SYNC", "VARIANT_INTERLEAVE", "VARIANT_GEMM", "VARIANT_FP8",
     "VARIANT_FP8_SYNC", "VARIANT_MXFP8", "swiglu_forward_mx", "swiglu_quantize_mx",
-    "swiglu_pack_kmajor",
+    "swiglu_pack_kmajor", "LAYOUT_PACKED", "VARIANT_PACKED", "swiglu_packed_bytes",
+    "swiglu_pack_fragments",
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_PKG, "libswiglu.so")
 
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_DEVICE, ERR_LAUNCH, ERR_ALLOC = range(6)
-LAYOUT_SEPARATE, LAYOUT_INTERLEAVED = 0, 1
+LAYOUT_SEPARATE, LAYOUT_INTERLEAVED, LAYOUT_PACKED = 0, 1, 2
 VARIANT_AUTO, VARIANT_SYNC, VARIANT_INTERLEAVE, VARIANT_GEMM, VARIANT_FP8, VARIANT_FP8_SYNC, \
-    VARIANT_MXFP8 = 0, 1, 2, 3, 4, 5, 6
+    VARIANT_MXFP8, VARIANT_PACKED = 0, 1, 2, 3, 4, 5, 6, 7
 
 
 class SwiGLUError(RuntimeError):
@@ -102,6 +103,8 @@ def load():
         "swiglu_forward_mx": ([p, p, p, p, p, p, i64, i64, i64, i64, i32, p], st),
         "swiglu_quantize_mx": ([p, p, p, p, i64, i64, i64, p], st),
         "swiglu_pack_kmajor": ([p, p, p, p, i64, i64, p], st),
+        "swiglu_packed_bytes": ([i64, i64], i64),
+        "swiglu_pack_fragments": ([p, p, p, p, i64, i64, p], st),
     }
     for name, (args, res) in sig.items():
         fn = getattr(lib, name)
@@ -194,6 +197,15 @@ def swiglu_forward_unfused(handle, A, W1, W2, workspace, Y, M, N, K, gemm_config
 def swiglu_pack_interleaved(handle, W1, W2, W_fused, K, N, stream=None):
     _check(load().swiglu_pack_interleaved(handle, _ptr(W1), _ptr(W2), _ptr(W_fused), K, N,
                                           _stream(stream)), "swiglu_pack_interleaved")
+
+
+def swiglu_packed_bytes(N: int, K: int) -> int:
+    return int(load().swiglu_packed_bytes(N, K))
+
+
+def swiglu_pack_fragments(handle, W1, W2, P, K, N, stream=None):
+    _check(load().swiglu_pack_fragments(handle, _ptr(W1), _ptr(W2), _ptr(P), K, N,
+                                        _stream(stream)), "swiglu_pack_fragments")
 
 
 def swiglu_query(handle, M, N, K, layout=LAYOUT_SEPARATE):

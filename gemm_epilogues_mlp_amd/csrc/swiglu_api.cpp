@@ -135,9 +135,10 @@ swiglu_status_t check_forward(const swiglu_ctx* h, const void* A, const void* W1
   *noop = false;
   if (!h) return SWIGLU_ERR_INVALID_ARG;
   if (M < 0 || N < 0 || K < 0) return SWIGLU_ERR_INVALID_ARG;
-  if (layout != SWIGLU_LAYOUT_SEPARATE && layout != SWIGLU_LAYOUT_INTERLEAVED)
+  if (layout != SWIGLU_LAYOUT_SEPARATE && layout != SWIGLU_LAYOUT_INTERLEAVED &&
+      layout != SWIGLU_LAYOUT_PACKED)
     return SWIGLU_ERR_INVALID_ARG;
-  if (layout == SWIGLU_LAYOUT_INTERLEAVED && W2 != nullptr) return SWIGLU_ERR_INVALID_ARG;
+  if (layout != SWIGLU_LAYOUT_SEPARATE && W2 != nullptr) return SWIGLU_ERR_INVALID_ARG;
   if (M == 0 || N == 0) {
     *noop = true;
     return SWIGLU_OK;
@@ -153,7 +154,8 @@ swiglu_status_t check_forward(const swiglu_ctx* h, const void* A, const void* W1
     return SWIGLU_ERR_UNSUPPORTED;
   const long long ybytes = 2LL * M * N;
   const long long abytes = 2LL * M * K;
-  const long long wbytes = (layout == SWIGLU_LAYOUT_INTERLEAVED ? 4LL : 2LL) * K * N;
+  const long long wbytes = layout == SWIGLU_LAYOUT_PACKED ? 2LL * packed_elems(N, K)
+                           : (layout == SWIGLU_LAYOUT_INTERLEAVED ? 4LL : 2LL) * K * N;
   // the kernels address A and the weights with 32-bit byte offsets, and use
   // offset 2^31 as "past every tensor"
   if (ybytes >= kMaxBytes || abytes >= kMaxBytes || wbytes >= kMaxBytes)
@@ -195,6 +197,21 @@ swiglu_status_t run(const swiglu_ctx* h, const KernelConfig* cfg, int id, const 
   a.cu_count = h->cu_count;
   a.stream = stream;
   return launch(h, cfg, id, a);
+}
+
+// Kernel family of a bf16 layout: SEPARATE -> sync, INTERLEAVED -> interleave,
+// PACKED -> interleave on fragment-ordered weights
+int layout_family(int layout) {
+  if (layout == SWIGLU_LAYOUT_INTERLEAVED) return VAR_INTERLEAVE;
+  if (layout == SWIGLU_LAYOUT_PACKED) return VAR_PACKED;
+  return VAR_SYNC;
+}
+
+// public variants a forward on this layout accepts besides AUTO
+bool variant_matches(int layout, int variant) {
+  if (layout == SWIGLU_LAYOUT_PACKED)
+    return variant == SWIGLU_VARIANT_INTERLEAVE || variant == SWIGLU_VARIANT_PACKED;
+  return variant == layout_family(layout);
 }
 
 void fill_tile(int id, swiglu_tile_t* t) {
@@ -263,8 +280,9 @@ swiglu_status_t swiglu_forward_ex(swiglu_handle_t h, const void* A, const void* 
   bool noop = false;
   swiglu_status_t st = check_forward(h, A, W1, W2, Y, M, N, K, (int)layout, &noop);
   if (st != SWIGLU_OK) return st;
-  const int want = layout == SWIGLU_LAYOUT_INTERLEAVED ? VAR_INTERLEAVE : VAR_SYNC;
-  if (variant != SWIGLU_VARIANT_AUTO && (int)variant != want) return SWIGLU_ERR_INVALID_ARG;
+  const int want = layout_family((int)layout);
+  if (variant != SWIGLU_VARIANT_AUTO && !variant_matches((int)layout, (int)variant))
+    return SWIGLU_ERR_INVALID_ARG;
   int id = config_id;
   if (id >= 0) {
     const KernelConfig* c = config_at(id);
@@ -339,6 +357,31 @@ swiglu_status_t swiglu_pack_interleaved(swiglu_handle_t h, const void* W1, const
   (void)hipGetLastError();
   if (launch_pack((const uint16_t*)W1, (const uint16_t*)W2, (uint16_t*)W_fused,
                   (size_t)K * (size_t)N, stream, h->cu_count) != hipSuccess)
+    return SWIGLU_ERR_LAUNCH;
+  return SWIGLU_OK;
+}
+
+int64_t swiglu_packed_bytes(int64_t N, int64_t K) {
+  if (N <= 0 || K <= 0 || N > (kMaxDim >> 1) || K > kMaxDim) return 0;
+  return 2 * packed_elems(N, K);
+}
+
+swiglu_status_t swiglu_pack_fragments(swiglu_handle_t h, const void* W1, const void* W2,
+                                      void* P, int64_t K, int64_t N, hipStream_t stream) {
+  if (!h || K < 0 || N < 0) return SWIGLU_ERR_INVALID_ARG;
+  if (K == 0 || N == 0) return SWIGLU_OK;
+  if (!W1 || !W2 || !P) return SWIGLU_ERR_INVALID_ARG;
+  if (K > kMaxDim || N > (kMaxDim >> 1)) return SWIGLU_ERR_UNSUPPORTED;
+  if (N % 8 != 0 || K % 8 != 0) return SWIGLU_ERR_UNSUPPORTED;
+  if (!aligned16(W1) || !aligned16(W2) || !aligned16(P)) return SWIGLU_ERR_UNSUPPORTED;
+  const long long wb = 2LL * K * N, pb = 2LL * packed_elems(N, K);
+  if (wb >= kMaxBytes || pb >= kMaxBytes) return SWIGLU_ERR_UNSUPPORTED;
+  if (overlaps(P, pb, W1, wb) || overlaps(P, pb, W2, wb)) return SWIGLU_ERR_INVALID_ARG;
+  swiglu_status_t st = check_device(h);
+  if (st != SWIGLU_OK) return st;
+  (void)hipGetLastError();
+  if (launch_pack_frag((const uint16_t*)W1, (const uint16_t*)W2, (uint16_t*)P, (int)N, (int)K,
+                       stream, h->cu_count) != hipSuccess)
     return SWIGLU_ERR_LAUNCH;
   return SWIGLU_OK;
 }
@@ -527,9 +570,10 @@ swiglu_status_t swiglu_query(swiglu_handle_t h, int64_t M, int64_t N, int64_t K,
                              swiglu_layout_t layout, swiglu_variant_t* chosen,
                              swiglu_tile_t* tile, swiglu_layout_t* recommended_layout) {
   if (!h || M < 0 || N < 0 || K < 0) return SWIGLU_ERR_INVALID_ARG;
-  if (layout != SWIGLU_LAYOUT_SEPARATE && layout != SWIGLU_LAYOUT_INTERLEAVED)
+  if (layout != SWIGLU_LAYOUT_SEPARATE && layout != SWIGLU_LAYOUT_INTERLEAVED &&
+      layout != SWIGLU_LAYOUT_PACKED)
     return SWIGLU_ERR_INVALID_ARG;
-  const int want = layout == SWIGLU_LAYOUT_INTERLEAVED ? VAR_INTERLEAVE : VAR_SYNC;
+  const int want = layout_family((int)layout);
   const int id = choose(h, want, M, N, K);
   if (id < 0) return SWIGLU_ERR_UNSUPPORTED;
   if (chosen) *chosen = (swiglu_variant_t)want;

@@ -10,10 +10,19 @@ namespace swiglu {
 // VAR_F8 / VAR_F8_SYNC: interleave / sync order on FP8 (E4M3) inputs with
 // k-contiguous paired weights
 // VAR_MX: interleave order on MXFP8 inputs (E4M3 + E8M0 scale per 32 along K)
+// VAR_PACKED: interleave order on W_fused stored in MFMA fragment order
 enum Variant {
   VAR_AUTO = 0, VAR_SYNC = 1, VAR_INTERLEAVE = 2, VAR_GEMM = 3, VAR_F8 = 4, VAR_F8_SYNC = 5,
-  VAR_MX = 6
+  VAR_MX = 6, VAR_PACKED = 7
 };
+
+// Fragment-ordered W_fused: slabs of 128 columns times steps of 32 k, 4096
+// values per (slab, step) block.
+inline long long packed_slabs(long long N) { return (2 * N + 127) / 128; }
+inline long long packed_steps(long long K) { return (K + 31) / 32; }
+inline long long packed_elems(long long N, long long K) {
+  return packed_slabs(N) * packed_steps(K) * 4096;
+}
 
 struct LaunchArgs {
   const uint16_t* A;
@@ -58,13 +67,16 @@ hipError_t launch_pack_f8(const uint8_t* W1, const uint8_t* W2, uint8_t* W8, int
 // [K, N] -> Wt [2N, K] (k-major pairing)
 hipError_t launch_quantize_mx(const uint16_t* X, uint8_t* Q, uint8_t* S, int rows, int K, int ks,
                               hipStream_t stream, int cu_count);
+// bf16 W1, W2 [K, N] -> fragment-ordered W_fused (packed_elems(N, K) values)
+hipError_t launch_pack_frag(const uint16_t* W1, const uint16_t* W2, uint16_t* P, int N, int K,
+                           hipStream_t stream, int cu_count);
 hipError_t launch_pack_kmajor(const uint16_t* W1, const uint16_t* W2, uint16_t* Wt, int N, int K,
                               hipStream_t stream, int cu_count);
 
 // Per-shape choice (tile table + fallback rule).  variant is SYNC, INTERLEAVE
 // or GEMM; returns a config id of that variant.
 int select_config(int variant, long long M, long long N, long long K, int cu_count);
-// Layout the table recommends for a shape: 0 separate, 1 interleaved.
+// Layout the table recommends for a shape: 0 separate, 1 interleaved, 2 packed.
 int recommend_layout(long long M, long long N, long long K, int cu_count);
 
 }  // namespace swiglu

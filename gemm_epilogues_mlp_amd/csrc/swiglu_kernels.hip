@@ -886,6 +886,159 @@ void skinny_kernel(const uint16_t* __restrict__ A,
 }
 
 // ============================================================================
+// Fragment-ordered weights: split-K streaming without transposition
+// ============================================================================
+// W_fused [K, 2N] ([RT §Metodologia, Kernel-2]) stored once, offline, in the
+// order the 16x16x32 MFMA consumes it.  The columns are cut into slabs of 128
+// and K into steps of 32; block (slab s, step t) is 4096 values (8 KB):
+//   P[((s T + t) 8 + c) 512 + (16 g + l) 8 + e] = W_fused[32 t + 8 g + e][128 s + 8 l + c]
+// with T = ceil(K / 32), c, e < 8, g < 4, l < 16, and zeros outside [K, 2N].
+// The 1 KB run c of a block is the B fragment of MFMA c for all 64 lanes (lane
+// 16 g + l: 8 consecutive k of column 128 s + 8 l + c), so every load
+// instruction reads 1 KB contiguous, a block is 8 KB contiguous, and the
+// blocks of a slab follow one another: a workgroup streams one contiguous
+// span of the weights.  The accumulators of MFMA 2q and 2q+1 hold the Gate
+// and the Up column of output 64 s + 4 l + q in the same lane, as in the
+// skinny kernel.
+//
+// A workgroup takes CH of the 8 MFMA column groups of one slab (CH = 8, 4 or
+// 2; CH/2 outputs per lane and row), i.e. a contiguous CH KB run of every
+// block of the slab.  Each CU streams at a bounded rate, so the time follows
+// the most loaded CU: splitting a slab into 8/CH workgroups evens the load
+// (Qwen2.5-7B decode: 296 slabs on 256 CUs, but 1184 quarter slabs).
+//
+// Waves of a workgroup take the slab's steps in turn (wave w: t = w, w + NW,
+// ...), so at any time they read neighbouring blocks; each wave keeps two
+// steps of loads in flight (two register sets, the load of the step after
+// next issued as soon as a set's MFMAs are issued).  The fp32 partials are
+// reduced through LDS in wave order before SiLU, as in skinny_kernel.
+template <int MT, int NW, int CH>
+struct Packed {
+  static_assert(CH == 2 || CH == 4 || CH == 8, "column groups per workgroup");
+  static constexpr int kThreads = 64 * NW;
+  static constexpr int LDS_BYTES = NW * MT * CH * 64 * 16;
+  static_assert(LDS_BYTES <= 160 * 1024, "LDS");
+  static constexpr int PARTS = 8 / CH;     // workgroups per slab
+  static constexpr int COLS_Y = 8 * CH;    // output columns per workgroup
+};
+
+template <int MT, int CH>
+__device__ __forceinline__ void packed_load(const uint16_t* __restrict__ A,
+                                            const uint16_t* __restrict__ wp, int M, int K,
+                                            int m0, int lane, int step, u32x4 (&b)[CH],
+                                            u32x4 (&af)[MT]) {
+  // Activations first.  Every lane loads, so no branch skips a load and the
+  // in-order load counter stays exact: rows past M re-read row M-1 (an output
+  // row depends only on its own A row, and those rows are never stored), k
+  // past K re-reads the last octet and is zeroed by the caller right before
+  // its MFMAs (M >= 1 and K >= 8 here).
+  const int k = min(step * 32 + (lane >> 4) * 8, K - 8);
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
+    const int m = min(m0 + mt * 16 + (lane & 15), M - 1);
+    af[mt] = load16(A + (size_t)m * K + k);
+  }
+  const uint16_t* p = wp + (size_t)step * 4096;
+#pragma unroll
+  for (int c = 0; c < CH; ++c) b[c] = MT == 1 ? load16_stream(p + c * 512) : load16(p + c * 512);
+}
+
+template <int MT, int NW, int CH>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(MT == 1 ? 4 : 2)))
+void packed_kernel(const uint16_t* __restrict__ A, const uint16_t* __restrict__ P,
+                   uint16_t* __restrict__ Y, int M, int N, int K) {
+  using C = Packed<MT, NW, CH>;
+  __shared__ __attribute__((aligned(16))) f32x4 red[NW * MT * CH * 64];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int unit = xcd_remap(blockIdx.x, gridDim.x);
+  const int slab = unit / C::PARTS, part = unit % C::PARTS;
+  const int m0 = blockIdx.y * MT * 16;
+  const int nsteps = (K + 31) / 32;
+  // this lane's 16 bytes in each of the workgroup's 1 KB runs (column groups
+  // part*CH ... part*CH + CH-1) of the slab's blocks
+  const uint16_t* wp = P + (size_t)slab * (size_t)nsteps * 4096 + part * CH * 512 + lane * 8;
+
+  f32x4 acc[MT][CH];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int c = 0; c < CH; ++c) acc[mt][c] = f32x4{};
+
+  // MFMAs of one step; k of this lane's octet past K contributes zero
+  auto mma = [&](const u32x4 (&b)[CH], const u32x4 (&af)[MT], int step) {
+    const bool kin = step * 32 + (lane >> 4) * 8 < K;  // K % 8 == 0
+    u32x4 a[MT];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) a[mt] = kin ? af[mt] : u32x4{0, 0, 0, 0};
+#pragma unroll
+    for (int c = 0; c < CH; ++c)
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) acc[mt][c] = mfma16(a[mt], b[c], acc[mt][c]);
+  };
+
+  if (wave < nsteps) {
+    // this wave's steps: wave, wave + NW, ..., last (n of them), taken in
+    // pairs with both MFMA groups unconditional, then an odd one; a load
+    // past the last step re-reads it (in bounds, unused).  The scheduling
+    // barriers keep each set's loads issued before the MFMAs that wait for
+    // the other set, so two steps stay in flight.
+    const int n = (nsteps - 1 - wave) / NW + 1;
+    const int last = wave + (n - 1) * NW;
+    u32x4 b0[CH], a0[MT], b1[CH], a1[MT];
+    packed_load<MT, CH>(A, wp, M, K, m0, lane, wave, b0, a0);
+    int s = wave;
+    for (int i = 0; i < n / 2; ++i, s += 2 * NW) {
+      packed_load<MT, CH>(A, wp, M, K, m0, lane, s + NW, b1, a1);
+      __builtin_amdgcn_sched_barrier(0);
+      mma(b0, a0, s);
+      packed_load<MT, CH>(A, wp, M, K, m0, lane, min(s + 2 * NW, last), b0, a0);
+      __builtin_amdgcn_sched_barrier(0);
+      mma(b1, a1, s + NW);
+    }
+    if (n & 1) mma(b0, a0, last);  // b0 holds the last step
+  }
+
+  // ---- split-K reduction through LDS (fixed order: wave 0, 1, ..., NW-1) ----
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int c = 0; c < CH; ++c) red[((wave * MT + mt) * CH + c) * 64 + lane] = acc[mt][c];
+  __syncthreads();
+
+  // lane l holds W_fused columns 128 slab + 8 l + part*CH + c: the pair
+  // (c, c+1), c even, is output column 64 slab + 4 l + (part*CH + c) / 2
+  const int col = slab * 64 + (lane & 15) * 4 + part * CH / 2;
+  const int rq = (lane >> 4) * 4;
+  for (int mt = wave; mt < MT; mt += NW) {
+    f32x4 v[CH];
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+      v[c] = red[(mt * CH + c) * 64 + lane];
+      for (int w = 1; w < NW; ++w) v[c] += red[((w * MT + mt) * CH + c) * 64 + lane];
+    }
+    if (col >= N) continue;  // N % 8 == 0: a lane's outputs are all in or all out
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int row = m0 + mt * 16 + rq + r;
+      if (row >= M) continue;
+      float y[CH / 2];
+#pragma unroll
+      for (int q = 0; q < CH / 2; ++q) y[q] = silu(v[2 * q][r]) * v[2 * q + 1][r];
+      uint16_t* out = Y + (size_t)row * N + col;
+      if constexpr (CH == 8) {
+        *reinterpret_cast<u32x2*>(out) = u32x2{pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3])};
+      } else if constexpr (CH == 4) {
+        *reinterpret_cast<uint32_t*>(out) = pack_bf16x2(y[0], y[1]);
+      } else {
+        *out = bf16_bits(y[0]);
+      }
+    }
+  }
+}
+
+// ============================================================================
 // FP8 (OCP E4M3) inputs: LDS-tiled interleave and sync kernels
 // ============================================================================
 // A8 [M, K] and W8 [2N, K] hold E4M3 codes with k contiguous in both; row 2n
@@ -1578,6 +1731,38 @@ __global__ __launch_bounds__(256) void pack_kernel(const uint16_t* __restrict__ 
   }
 }
 
+// Fragment-ordered W_fused from W1, W2 [K, N] (layout in front of
+// packed_kernel): a thread writes one 16-byte run, the 8 consecutive k of
+// W_fused column j = 128 s + 8 l + c (Gate column j/2 of W1 for even j, Up
+// column j/2 of W2 for odd j), zeros outside [K, 2N].  Done once per weight
+// set; the 2-byte gathers are not on any hot path.
+__global__ __launch_bounds__(256) void pack_frag_kernel(const uint16_t* __restrict__ W1,
+                                                        const uint16_t* __restrict__ W2,
+                                                        uint16_t* __restrict__ P, int N, int K,
+                                                        size_t nruns) {
+  const int nsteps = (K + 31) / 32;
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < nruns;
+       i += (size_t)gridDim.x * blockDim.x) {
+    const int lane = (int)(i & 63);
+    const int c = (int)((i >> 6) & 7);
+    const size_t st = i >> 9;  // s * nsteps + t
+    const int t = (int)(st % (size_t)nsteps);
+    const long long s = (long long)(st / (size_t)nsteps);
+    const long long j = 128 * s + 8 * (lane & 15) + c;  // W_fused column
+    const int k0 = 32 * t + 8 * (lane >> 4);
+    const uint16_t* src = (j & 1) ? W2 : W1;
+    const long long n = j >> 1;
+    uint16_t v[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      v[e] = (n < N && k0 + e < K) ? src[(size_t)(k0 + e) * (size_t)N + (size_t)n] : 0;
+    u32x4 o;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) o[q] = (uint32_t)v[2 * q] | ((uint32_t)v[2 * q + 1] << 16);
+    *reinterpret_cast<u32x4*>(P + i * 8) = o;
+  }
+}
+
 // ============================================================================
 // Configuration list and launchers
 // ============================================================================
@@ -1648,6 +1833,18 @@ static hipError_t launch_skinny(const LaunchArgs& a) {
   return hipGetLastError();
 }
 
+template <int MT, int NW, int CH>
+static hipError_t launch_packed(const LaunchArgs& a) {
+  using C = Packed<MT, NW, CH>;
+  const long long nunit = packed_slabs(a.N) * C::PARTS;
+  const long long nmb = (a.M + MT * 16 - 1) / (MT * 16);
+  if (nunit <= 0 || nmb <= 0) return hipSuccess;
+  if (nunit > 0x7fffffffLL || nmb > 65535) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((packed_kernel<MT, NW, CH>), dim3((unsigned)nunit, (unsigned)nmb),
+                     dim3(C::kThreads), 0, a.stream, a.A, a.W1, a.Y, a.M, a.N, a.K);
+  return hipGetLastError();
+}
+
 template <int MODE, int BM, int BNW, int STAGES, int WGM, int WGN>
 static hipError_t launch_f8(const LaunchArgs& a) {
   using C = F8Tiled<MODE, BM, BNW, STAGES, WGM, WGN>;
@@ -1715,6 +1912,9 @@ static hipError_t launch_f8_skinny(const LaunchArgs& a) {
    &launch_tiled_split<mode, bm, bnw, bk, st, wgm, wgn, swgm, swgn>, 4}
 #define PINGPONG(mode, v) \
   {v, 2, 256, PingPong<mode>::BNY, 32, 8, 1, PingPong<mode>::LDS_BYTES, &launch_pingpong<mode>}
+#define PACKED(mt, nw, ch)                                                                 \
+  {VAR_PACKED, 1, (mt) * 16, Packed<mt, nw, ch>::COLS_Y, 32, nw, nw,                          \
+   Packed<mt, nw, ch>::LDS_BYTES, &launch_packed<mt, nw, ch>}
 #define SKINNY(mode, v, mt, nw)                                                            \
   {v, 1, (mt) * 16, Skinny<mode, mt, nw>::SLAB_Y, 32, nw, nw, Skinny<mode, mt, nw>::LDS_BYTES, \
    &launch_skinny<mode, mt, nw>}
@@ -1792,6 +1992,20 @@ static const KernelConfig kConfigs[] = {
     // ---- MXFP8 (E8M0 block scales applied by the MFMA) ---------------------
     F8_SPLIT(MODE_MX, VAR_MX, 256, 256, 4, 4, 2, 2, 4),             // 56
     F8(MODE_MX, VAR_MX, 64, 128, 4, 2, 2),                          // 57
+    // ---- fragment-ordered W_fused (split-K streaming, no transposition) ----
+    PACKED(1, 4, 8),                                                // 58
+    PACKED(1, 8, 8),                                                // 59
+    PACKED(2, 4, 8),                                                // 60
+    PACKED(2, 8, 8),                                                // 61
+    PACKED(4, 4, 8),                                                // 62
+    // a slab split over 4 or 2 workgroups (even load over the CUs)
+    PACKED(1, 4, 2),                                                // 63
+    PACKED(1, 8, 2),                                                // 64
+    PACKED(1, 4, 4),                                                // 65
+    PACKED(1, 8, 4),                                                // 66
+    PACKED(2, 4, 2),                                                // 67
+    PACKED(4, 4, 2),                                                // 68
+    PACKED(2, 4, 4),                                                // 69
 };
 
 int config_count() { return (int)(sizeof(kConfigs) / sizeof(kConfigs[0])); }
@@ -1855,6 +2069,18 @@ hipError_t launch_pack_f8(const uint8_t* W1, const uint8_t* W2, uint8_t* W8, int
   if (blocks > cap) blocks = cap;
   hipLaunchKernelGGL(pack_f8_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, W1, W2, W8, N,
                      K);
+  return hipGetLastError();
+}
+
+hipError_t launch_pack_frag(const uint16_t* W1, const uint16_t* W2, uint16_t* P, int N, int K,
+                           hipStream_t stream, int cu_count) {
+  const size_t nruns = (size_t)packed_slabs(N) * (size_t)packed_steps(K) * 512;
+  if (nruns == 0) return hipSuccess;
+  size_t blocks = (nruns + 255) / 256;
+  const size_t cap = (size_t)(cu_count > 0 ? cu_count : 256) * 8;
+  if (blocks > cap) blocks = cap;
+  hipLaunchKernelGGL(pack_frag_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, W1, W2, P,
+                     N, K, nruns);
   return hipGetLastError();
 }
 

@@ -61,11 +61,23 @@ int find_config(int variant, int family, int bm, int bn, int waves) {
 int select_config(int variant, long long M, long long N, long long K, int cu_count) {
   for (const ShapeEntry& e : kTable)
     if (e.variant == variant && e.M == M && e.N == N && e.K == K) return e.config_id;
-  (void)N, (void)K, (void)cu_count;
+  (void)K;
   // FP8 sync order (measured on the five workloads: 128 x 128 tiles won at
   // M = 2048, the split 256-row tiles at M = 4096 and 8192)
   // MXFP8: 64 x 128 tiles for small M, the split 256 x 256 tiles above
   if (variant == VAR_MX) return M <= 192 ? 57 : 56;
+  if (variant == VAR_PACKED) {
+    // fragment-ordered weights (measured at M = 16, 32, 48, 64 on the 0.5B,
+    // 7B and 72B K and N): each CU streams at a bounded rate, so a launch
+    // wants its slabs spread evenly over the CUs -- whole slabs when there
+    // are at least 1.75 per CU (72B: 462), half slabs from half a slab per
+    // CU (7B: 296 slabs -> 592 workgroups), quarter slabs below (0.5B: 76).
+    // Above M = 16 the 32- and 64-row blocks win; above M = 64 the weights
+    // are re-read once per 64 rows (a fallback, not a fast path).
+    const long long slabs = packed_slabs(N), cus = cu_count > 0 ? cu_count : 256;
+    if (M <= 16) return 4 * slabs >= 7 * cus ? 58 : (2 * slabs >= cus ? 65 : 63);
+    return M <= 32 ? 69 : 62;
+  }
   if (variant == VAR_F8_SYNC) return M <= 192 ? 55 : (M <= 3072 ? 54 : 53);
   if (variant == VAR_F8) {
     // FP8: split-K weight streaming up to M = 64, then 64 x 128 tiles, 128-row
@@ -92,12 +104,14 @@ int select_config(int variant, long long M, long long N, long long K, int cu_cou
 }
 
 int recommend_layout(long long M, long long N, long long K, int cu_count) {
-  (void)M, (void)N, (void)K, (void)cu_count;
+  (void)N, (void)K, (void)cu_count;
   // The page prefers the sync kernel above M = 2048.  On MI355X the interleave
   // kernel was faster at every measured M (0.5B-72B shapes, M = 16..8192): it
   // loads A once and keeps every accumulator busy in every K step, while the
   // sync kernel alternates between half of its registers (Gate, then Up).
-  return 1;
+  // Up to M = 64 the same Kernel-2 order on fragment-ordered weights streams
+  // them fastest (1.16-1.6x the interleaved layout at M = 16 ... 64).
+  return M <= 64 ? 2 : 1;
 }
 
 }  // namespace swiglu

@@ -24,7 +24,8 @@ import sys
 import gemm_epilogues_mlp_amd as sw
 
 VARIANTS = {"interleave": sw.VARIANT_INTERLEAVE, "sync": sw.VARIANT_SYNC, "gemm": sw.VARIANT_GEMM,
-            "fp8": sw.VARIANT_FP8, "fp8-sync": sw.VARIANT_FP8_SYNC, "mxfp8": sw.VARIANT_MXFP8}
+            "fp8": sw.VARIANT_FP8, "fp8-sync": sw.VARIANT_FP8_SYNC, "mxfp8": sw.VARIANT_MXFP8,
+            "packed": sw.VARIANT_PACKED}
 # the forward's variant argument for each FP8 configuration family
 _FP8_ORDER = {sw.VARIANT_FP8: sw.VARIANT_INTERLEAVE, sw.VARIANT_FP8_SYNC: sw.VARIANT_SYNC,
               sw.VARIANT_MXFP8: sw.VARIANT_MXFP8}
@@ -75,7 +76,11 @@ def _time_configs(h, variant, M, N, K, ids, reps, rotate_bytes, seed=0):
             continue
         a = rnd((M, K))
         w1, w2 = rnd((K, N), K ** -0.5), rnd((K, N), K ** -0.5)
-        wf = torch.empty((K, 2 * N), dtype=torch.int16, device=dev)
+        if variant == sw.VARIANT_PACKED:
+            wf = torch.empty((sw.swiglu_packed_bytes(N, K) // 2,), dtype=torch.int16, device=dev)
+            sw.swiglu_pack_fragments(h, w1, w2, wf, K, N)
+        else:
+            wf = torch.empty((K, 2 * N), dtype=torch.int16, device=dev)
         if variant == sw.VARIANT_INTERLEAVE:
             sw.swiglu_pack_interleaved(h, w1, w2, wf, K, N)
         y = torch.empty((M, N), dtype=torch.int16, device=dev)
@@ -96,6 +101,9 @@ def _time_configs(h, variant, M, N, K, ids, reps, rotate_bytes, seed=0):
         a, w1, w2, wf, y, ws = sets[i % nsets]
         if variant == sw.VARIANT_INTERLEAVE:
             sw.swiglu_forward_ex(h, a, wf, None, y, M, N, K, sw.LAYOUT_INTERLEAVED, variant, cid,
+                                 stream)
+        elif variant == sw.VARIANT_PACKED:
+            sw.swiglu_forward_ex(h, a, wf, None, y, M, N, K, sw.LAYOUT_PACKED, variant, cid,
                                  stream)
         elif variant == sw.VARIANT_SYNC:
             sw.swiglu_forward_ex(h, a, w1, w2, y, M, N, K, sw.LAYOUT_SEPARATE, variant, cid,
@@ -157,8 +165,8 @@ def tune(shapes, variants=("interleave", "sync", "gemm"), out=None, merge=None, 
                 elif v in _FP8_ORDER:
                     builtin = sw.swiglu_query_fp8(h, M, N, K, _FP8_ORDER[v])["id"]
                 else:
-                    layout = sw.LAYOUT_INTERLEAVED if v == sw.VARIANT_INTERLEAVE else \
-                        sw.LAYOUT_SEPARATE
+                    layout = {sw.VARIANT_INTERLEAVE: sw.LAYOUT_INTERLEAVED,
+                              sw.VARIANT_PACKED: sw.LAYOUT_PACKED}.get(v, sw.LAYOUT_SEPARATE)
                     builtin = sw.swiglu_query(h, M, N, K, layout)[1]["id"]
                 ids = sorted(set(_candidates(v, M, configs)) | {builtin})
                 flops = 4.0 * M * N * K

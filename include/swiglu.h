@@ -74,7 +74,9 @@ typedef enum {
 
 typedef enum {
   SWIGLU_LAYOUT_SEPARATE = 0,   /* W1, W2 each [K, N]                          */
-  SWIGLU_LAYOUT_INTERLEAVED = 1 /* W1 = W_fused [K, 2N], W2 = NULL             */
+  SWIGLU_LAYOUT_INTERLEAVED = 1, /* W1 = W_fused [K, 2N], W2 = NULL            */
+  SWIGLU_LAYOUT_PACKED = 2      /* W1 = W_fused in MFMA fragment order (see
+                                   swiglu_pack_fragments), W2 = NULL           */
 } swiglu_layout_t;
 
 typedef enum {
@@ -86,8 +88,10 @@ typedef enum {
                                     inputs (swiglu_forward_fp8, INTERLEAVE)    */
   SWIGLU_VARIANT_FP8_SYNC = 5,   /* config descriptions: Kernel-1 order on FP8
                                     inputs (swiglu_forward_fp8, SYNC)          */
-  SWIGLU_VARIANT_MXFP8 = 6       /* Kernel-2 order on MXFP8 inputs
+  SWIGLU_VARIANT_MXFP8 = 6,      /* Kernel-2 order on MXFP8 inputs
                                     (swiglu_forward_mx; swiglu_query_fp8)      */
+  SWIGLU_VARIANT_PACKED = 7      /* Kernel-2 order on fragment-ordered W_fused
+                                    (PACKED layout)                            */
 } swiglu_variant_t;
 
 /* Description of one compiled kernel configuration. */
@@ -120,16 +124,19 @@ swiglu_status_t swiglu_create(swiglu_handle_t* out, int device);
 swiglu_status_t swiglu_destroy(swiglu_handle_t h);
 
 /* Fused forward [RT §Metodologia]: SEPARATE layout runs the sync family
- * (Kernel-1), INTERLEAVED runs the interleave family (Kernel-2); the tile
- * configuration comes from the per-shape table. */
+ * (Kernel-1), INTERLEAVED runs the interleave family (Kernel-2), PACKED runs
+ * the Kernel-2 order on fragment-ordered W_fused (split-K weight streaming, any
+ * M; made for decode-sized batches); the tile configuration comes from the
+ * per-shape table. */
 swiglu_status_t swiglu_forward(swiglu_handle_t h, const void* A, const void* W1,
                                const void* W2, void* Y, int64_t M, int64_t N,
                                int64_t K, swiglu_layout_t layout, hipStream_t stream);
 
 /* As swiglu_forward with an explicit variant and configuration (config_id < 0
  * uses the table).  The variant must match the layout (SYNC <-> SEPARATE,
- * INTERLEAVE <-> INTERLEAVED) and a given config must belong to that variant,
- * otherwise INVALID_ARG.  Used by tuning sweeps and tests. */
+ * INTERLEAVE <-> INTERLEAVED, INTERLEAVE or PACKED <-> PACKED) and a given
+ * config must belong to the layout's family (variant SYNC, INTERLEAVE or
+ * PACKED), otherwise INVALID_ARG.  Used by tuning sweeps and tests. */
 swiglu_status_t swiglu_forward_ex(swiglu_handle_t h, const void* A, const void* W1,
                                   const void* W2, void* Y, int64_t M, int64_t N,
                                   int64_t K, swiglu_layout_t layout,
@@ -160,9 +167,33 @@ swiglu_status_t swiglu_pack_interleaved(swiglu_handle_t h, const void* W1,
                                         const void* W2, void* W_fused, int64_t K,
                                         int64_t N, hipStream_t stream);
 
+/* ---- fragment-ordered W_fused (SWIGLU_LAYOUT_PACKED) ------------------------
+ * W_fused [K, 2N] of [RT §Metodologia, Kernel-2] stored once, offline, in the
+ * order the decode kernel's 16x16x32 MFMAs consume it, so that every load
+ * instruction reads 1 KB contiguous and each workgroup streams one contiguous
+ * span.  With S = ceil(2N / 128) slabs of 128 W_fused columns and
+ * T = ceil(K / 32) steps of 32 k, P holds S * T * 4096 bf16 values:
+ *   P[((s*T + t)*8 + c)*512 + (16*g + l)*8 + e] = W_fused[32t + 8g + e][128s + 8l + c]
+ * for s < S, t < T, c < 8, g < 4, l < 16, e < 8, and 0 where the row is >= K
+ * or the column >= 2N.  Each 16-byte run is 8 consecutive k of one column (a
+ * k-contiguous layout: no transposition on the way to the MFMA). */
+
+/* Bytes of the fragment-ordered W_fused for N, K: 2 * S * T * 4096 (0 when
+ * N <= 0 or K <= 0 or a size is out of range). */
+int64_t swiglu_packed_bytes(int64_t N, int64_t K);
+
+/* Build the fragment-ordered W_fused P (swiglu_packed_bytes(N, K) bytes, padding
+ * included) from W1, W2 [K, N].  A bit copy done once per weight set, outside
+ * the forward.  N % 8 == 0, K % 8 == 0, 16-byte aligned pointers and tensors
+ * under 2 GiB required (else UNSUPPORTED); P must not overlap W1 or W2
+ * (INVALID_ARG).  K == 0 or N == 0 is a no-op. */
+swiglu_status_t swiglu_pack_fragments(swiglu_handle_t h, const void* W1, const void* W2,
+                                      void* P, int64_t K, int64_t N, hipStream_t stream);
+
 /* What swiglu_forward / _ex(AUTO) would run for this shape and layout, and
  * which layout the table recommends for the shape (the per-batch choice of
- * kernel family [RT §Contributi Chiave, item 2]).  Any out-pointer may be NULL.
+ * kernel family [RT §Contributi Chiave, item 2]): PACKED up to M = 64,
+ * INTERLEAVED above (measured on MI355X).  Any out-pointer may be NULL.
  * For variant GEMM pass layout SEPARATE to ask for the unfused GEMM config. */
 swiglu_status_t swiglu_query(swiglu_handle_t h, int64_t M, int64_t N, int64_t K,
                              swiglu_layout_t layout, swiglu_variant_t* chosen,
@@ -175,7 +206,7 @@ swiglu_status_t swiglu_query_unfused(swiglu_handle_t h, int64_t M, int64_t N,
 /* Tuned per-shape configurations.  A tuned file (written by the package's
  * tuner, python -m gemm_epilogues_mlp_amd.tune) is text:
  *   swiglu-tuned <signature: 16 hex digits> <arch>        first non-comment line
- *   <variant 1..6> <M> <N> <K> <config id> [ignored provenance]    one per shape
+ *   <variant 1..7> <M> <N> <K> <config id> [ignored provenance]    one per shape
  * with '#' comment lines.  The signature (swiglu_config_signature) identifies
  * the list of compiled configurations; a file written for a library with a
  * different list is refused, so an id can never name the wrong kernel.

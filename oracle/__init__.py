@@ -78,7 +78,9 @@ def _load():
     lib.oracle_quantize_mx.argtypes = [p, i64, i64, i64, p, p]
     lib.oracle_decode_mx.argtypes = [p, p, i64, i64, i64, p]
     lib.oracle_pack_kmajor_bf16.argtypes = [p, p, p, i64, i64]
-    for fn in (lib.oracle_quantize_mx, lib.oracle_decode_mx, lib.oracle_pack_kmajor_bf16):
+    lib.oracle_pack_fragments.argtypes = [p, p, p, i64, i64]
+    for fn in (lib.oracle_quantize_mx, lib.oracle_decode_mx, lib.oracle_pack_kmajor_bf16,
+               lib.oracle_pack_fragments):
         fn.restype = None
     lib.oracle_swiglu_mx_rows.argtypes = [p, p, p, p, i64, i64, i64, i64, p, i64, p, p, p,
                                           c_int]
@@ -348,6 +350,26 @@ def pack_kmajor_bf16(w1, w2):
     wt = np.empty((2 * N, K), np.uint16)
     _load().oracle_pack_kmajor_bf16(_ptr(w1), _ptr(w2), _ptr(wt), K, N)
     return wt
+
+
+def packed_size(N: int, K: int) -> int:
+    """Values of the fragment-ordered W_fused: ceil(2N/128) * ceil(K/32) * 4096."""
+    return ((2 * N + 127) // 128) * ((K + 31) // 32) * 4096
+
+
+def pack_fragments(w1, w2):
+    """Fragment-ordered W_fused (flat bf16 bits, packed_size(N, K) values) from
+    W1, W2 [K, N]: element W_fused[k, j] at ((s*T + t)*8 + c)*512 + (16g + l)*8 + e
+    (s = j // 128, l = j % 128 // 8, c = j % 8, t = k // 32, g = k % 32 // 8,
+    e = k % 8, T = ceil(K/32)), zeros elsewhere."""
+    w1 = _u16(w1, "W1")
+    w2 = _u16(w2, "W2")
+    if w1.shape != w2.shape:
+        raise ValueError("W1 and W2 differ in shape")
+    K, N = w1.shape
+    out = np.empty(packed_size(N, K), np.uint16)
+    _load().oracle_pack_fragments(_ptr(w1), _ptr(w2), _ptr(out), K, N)
+    return out
 
 
 def swiglu_mx_rows(a, sa, w, sw, rows=None, with_gate_up=False, nthreads=None):

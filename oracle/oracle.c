@@ -531,6 +531,26 @@ void oracle_decode_mx(const uint8_t* q, const uint8_t* s, int64_t rows, int64_t 
       out[r * K + k] = e8m0_value(s[r * ks + k / 32]) * e4m3_value(q[r * K + k]);
 }
 
+/* Fragment-ordered W_fused (the library's PACKED storage of the Kernel-2
+ * matrix, [RT §Metodologia, Kernel-2]): every element W_fused[k][j] (Gate
+ * W1[k][j/2] for even j, Up W2[k][j/2] for odd j) is placed at
+ *   ((s*T + t)*8 + c)*512 + (16*g + l)*8 + e
+ * with s = j / 128, l = (j % 128) / 8, c = j % 8, t = k / 32, g = (k % 32) / 8,
+ * e = k % 8 and T = ceil(K / 32); every other position of the
+ * ceil(2N / 128) * T * 4096 values is 0.  A bit copy. */
+void oracle_pack_fragments(const uint16_t* w1, const uint16_t* w2, uint16_t* p, int64_t K,
+                           int64_t N) {
+  const int64_t S = (2 * N + 127) / 128, T = (K + 31) / 32;
+  memset(p, 0, sizeof(uint16_t) * (size_t)(S * T * 4096));
+  for (int64_t k = 0; k < K; ++k)
+    for (int64_t j = 0; j < 2 * N; ++j) {
+      const uint16_t v = (j % 2 == 0) ? w1[k * N + j / 2] : w2[k * N + j / 2];
+      const int64_t s = j / 128, l = (j % 128) / 8, c = j % 8;
+      const int64_t t = k / 32, g = (k % 32) / 8, e = k % 8;
+      p[((s * T + t) * 8 + c) * 512 + (16 * g + l) * 8 + e] = v;
+    }
+}
+
 /* bf16 W1, W2 [K, N] -> Wt [2N, K] bf16: row 2n = W1[:, n], row 2n+1 = W2[:, n]
  * (the Kernel-2 pairing with k contiguous), a bit copy. */
 void oracle_pack_kmajor_bf16(const uint16_t* w1, const uint16_t* w2, uint16_t* wt, int64_t K,

@@ -97,6 +97,10 @@ bool run_config(int id, int M, int N, int K) {
     a.W1 = alloc16((size_t)K * 2 * N, "W_fused");
     a.W2 = nullptr;
     a.ldw = 2 * N;
+  } else if (c->variant == VAR_PACKED) {
+    a.W1 = alloc16((size_t)packed_elems(N, K), "P");  // fragment-ordered W_fused
+    a.W2 = nullptr;
+    a.ldw = 0;
   } else if (c->variant == VAR_SYNC) {
     a.W1 = alloc16((size_t)K * N, "W1");
     a.W2 = alloc16((size_t)K * N, "W2");
@@ -166,6 +170,18 @@ bool run_elementwise(size_t n) {
     uint16_t* pt = alloc16((size_t)2 * Kp * Np, "Wt");
     launch_pack_kmajor(p1, p2, pt, Np, Kp, nullptr, 256);
     free_all();
+  }
+  // fragment-ordered W_fused from [K, N] weights (K = 40, N = n / 40 rounded
+  // down to a multiple of 8: ragged slabs and steps)
+  {
+    const int Kf = 40, Nf = (int)(n / 40) / 8 * 8;
+    if (Nf > 0) {
+      uint16_t* f1 = alloc16((size_t)Kf * Nf, "W1f");
+      uint16_t* f2 = alloc16((size_t)Kf * Nf, "W2f");
+      uint16_t* pf = alloc16((size_t)packed_elems(Nf, Kf), "Pf");
+      launch_pack_frag(f1, f2, pf, Nf, Kf, nullptr, 256);
+      free_all();
+    }
   }
   printf("%s: %s\n", g_ctx.c_str(), g_errors == before ? "ok" : "OUT OF BOUNDS");
   return g_errors == before;

@@ -55,6 +55,11 @@ CASES = [
     (2008, 4216, 128, [43, 53, 56]),   # whole rounds plus a short split round
     (128, 4864, 896, [46, 55, 57]),
     (16, 18944, 3584, [52, 57]),
+    # fragment-ordered weights: decode, 0.5B and ragged shapes for every
+    # packed config (odd and even step counts per wave)
+    (16, 18944, 3584, list(range(58, 70))),
+    (128, 4864, 896, list(range(58, 70))),
+    (33, 72, 40, list(range(58, 70))),
 ]
 
 
@@ -73,6 +78,8 @@ def test_table_configs_at_workload_sizes(emu, case):
 LIMIT_CASES = [
     (65536, 64, 16376, [40, 42, 41], 4),
     (16, 32768, 16376, [4, 11, 18, 23, 12], 8),
+    # fragment-ordered W_fused just under 2 GiB: 511 slabs x 512 steps x 8 KB
+    (16, 32704, 16376, list(range(58, 70)), 8),
     (256, 32768, 16376, [1, 8, 16], 4),
     # byte tensors: A8 = 65536 x 32704 B, W8 = 2 x 32768 x 32704 B (K % 64 == 0)
     (65536, 64, 32704, [43, 53, 56], 4),

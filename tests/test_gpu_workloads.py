@@ -62,6 +62,15 @@ def workload(request):
     # pack kernel vs the host interleave on a few rows (bitwise)
     ks = np.unique([0, w.K - 1, w.K // 3])
     assert np.array_equal(host(wf[ks]), I.interleave_columns(w1[ks], w2[ks]))
+    # fragment-ordered W_fused: device pack vs the oracle's, whole buffer
+    pk = torch.empty((sw.swiglu_packed_bytes(w.N, w.K) // 2,), dtype=torch.int16,
+                     device="cuda")
+    h = sw.swiglu_create(0)
+    sw.swiglu_pack_fragments(h, d["w1"], d["w2"], pk, w.K, w.N)
+    torch.cuda.synchronize()
+    sw.swiglu_destroy(h)
+    assert np.array_equal(host(pk), oracle.pack_fragments(w1, w2))
+    d["pk"] = pk
     yield d
     del d
 
@@ -74,8 +83,9 @@ def _check_sampled(y_full, d, what):
     return yb
 
 
-@pytest.mark.parametrize("layout", [sw.LAYOUT_INTERLEAVED, sw.LAYOUT_SEPARATE],
-                         ids=["interleaved", "separate"])
+@pytest.mark.parametrize("layout", [sw.LAYOUT_INTERLEAVED, sw.LAYOUT_SEPARATE,
+                                    sw.LAYOUT_PACKED],
+                         ids=["interleaved", "separate", "packed"])
 def test_workload_fused_parity(handle, workload, layout):
     import torch
     d, w = workload, workload["w"]
@@ -84,6 +94,8 @@ def test_workload_fused_parity(handle, workload, layout):
     y = empty_poisoned((w.M, w.N))
     if layout == sw.LAYOUT_INTERLEAVED:
         sw.swiglu_forward(handle, d["a"], d["wf"], None, y, w.M, w.N, w.K, layout)
+    elif layout == sw.LAYOUT_PACKED:
+        sw.swiglu_forward(handle, d["a"], d["pk"], None, y, w.M, w.N, w.K, layout)
     else:
         sw.swiglu_forward(handle, d["a"], d["w1"], d["w2"], y, w.M, w.N, w.K, layout)
     torch.cuda.synchronize()

@@ -1,0 +1,84 @@
+"""Pins of the oracle's fragment-ordered W_fused (CPU, no GPU).
+
+The layout is the library's PACKED storage of the Kernel-2 matrix W_fused
+("Riepilogo Tecnico: Sovrapposizione delle Attivazioni a Livello di Tile...",
+§Metodologia, Kernel-2: Gate in even, Up in odd columns), cut into slabs of
+128 columns and steps of 32 k:
+    P[((s T + t) 8 + c) 512 + (16 g + l) 8 + e] = W_fused[32 t + 8 g + e][128 s + 8 l + c]
+with zeros outside [K, 2N].  The oracle places every element by that rule.
+Pinned here by positions derived by hand (tests/golden/fragment_layout.txt),
+by the permutation property (every weight appears once, everything else is
+zero), and by an independent derivation through numpy axis algebra on the
+zero-padded W_fused.
+"""
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+from gemm_epilogues_mlp_amd import inputs as I
+
+
+def _golden():
+    path = os.path.join(os.path.dirname(__file__), "golden", "fragment_layout.txt")
+    entries, shape = [], None
+    for line in open(path):
+        line = line.split("#")[0].strip()
+        if not line:
+            continue
+        if line.startswith("shape"):
+            shape = tuple(int(x) for x in line.split()[1:])
+            continue
+        i, v = line.split()
+        entries.append((int(i), int(v)))
+    return shape, entries
+
+
+def _coded(K, N):
+    k = np.arange(K, dtype=np.int64)[:, None]
+    n = np.arange(N, dtype=np.int64)[None, :]
+    return (1 + 72 * k + n).astype(np.uint16), (10001 + 72 * k + n).astype(np.uint16)
+
+
+def test_hand_derived_positions():
+    (K, N), entries = _golden()
+    w1, w2 = _coded(K, N)
+    p = oracle.pack_fragments(w1, w2)
+    assert p.size == 16384 == oracle.packed_size(N, K)
+    for i, v in entries:
+        assert int(p[i]) == v, f"P[{i}] = {int(p[i])}, hand derivation says {v}"
+
+
+@pytest.mark.parametrize("K,N", [(40, 72), (32, 64), (8, 8), (96, 264), (200, 72), (136, 120)])
+def test_every_weight_once_zeros_elsewhere(K, N):
+    rng = np.random.default_rng(K * 1000 + N)
+    # distinct nonzero codes for all 2NK weights
+    codes = rng.permutation(np.arange(1, 2 * N * K + 1, dtype=np.int64))
+    assert codes.max() < 65536
+    w1 = codes[:K * N].reshape(K, N).astype(np.uint16)
+    w2 = codes[K * N:].reshape(K, N).astype(np.uint16)
+    p = oracle.pack_fragments(w1, w2)
+    assert p.size == ((2 * N + 127) // 128) * ((K + 31) // 32) * 4096
+    nz = p[p != 0]
+    assert nz.size == 2 * N * K
+    assert np.array_equal(np.sort(nz.astype(np.int64)), np.sort(codes))
+
+
+@pytest.mark.parametrize("K,N", [(40, 72), (64, 128), (8, 8), (200, 264), (520, 136),
+                                 (3584, 64)])
+def test_matches_axis_algebra(K, N):
+    """Pad W_fused to [32T, 128S], split k as (t, g, e) and the column as
+    (s, l, c), and order the axes (s, t, c, g, l, e)."""
+    a, w1, w2 = I.make_inputs(1, K, N, 7)
+    wf = I.interleave_columns(w1, w2)           # [K, 2N], Gate even, Up odd
+    T, S = (K + 31) // 32, (2 * N + 127) // 128
+    pad = np.zeros((32 * T, 128 * S), np.uint16)
+    pad[:K, :2 * N] = wf
+    ref = pad.reshape(T, 4, 8, S, 16, 8).transpose(3, 0, 5, 1, 4, 2).reshape(-1)
+    assert np.array_equal(oracle.pack_fragments(w1, w2), ref)
+
+
+def test_empty():
+    w = np.zeros((0, 16), np.uint16)
+    assert oracle.pack_fragments(w, w).size == 0
