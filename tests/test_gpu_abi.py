@@ -140,10 +140,13 @@ def test_empty_is_noop(env):
 
 def test_query_reports_a_valid_config(env):
     h = env["h"]
-    for M in (1, 16, 33, 128, 2048, 8192):
-        for layout in (sw.LAYOUT_SEPARATE, sw.LAYOUT_INTERLEAVED):
+    family = {sw.LAYOUT_SEPARATE: sw.VARIANT_SYNC, sw.LAYOUT_INTERLEAVED: sw.VARIANT_INTERLEAVE,
+              sw.LAYOUT_PACKED: sw.VARIANT_PACKED}
+    for M in (1, 16, 33, 64, 65, 128, 2048, 8192):
+        for layout in family:
             v, tile, rec = sw.swiglu_query(h, M, 4864, 896, layout)
-            assert v == (sw.VARIANT_INTERLEAVE if layout else sw.VARIANT_SYNC)
+            assert v == family[layout]
             assert tile["variant"] == v
-            assert rec in (sw.LAYOUT_SEPARATE, sw.LAYOUT_INTERLEAVED)
+            # fragment-ordered weights up to M = 64, the interleaved layout above
+            assert rec == (sw.LAYOUT_PACKED if M <= 64 else sw.LAYOUT_INTERLEAVED)
         assert sw.swiglu_query_unfused(h, M, 4864, 896)["variant"] == sw.VARIANT_GEMM
