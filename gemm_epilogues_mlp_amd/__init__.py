@@ -27,7 +27,8 @@ __all__ = [
     "VARIANT_AUTO", "VARIANT_SYNC", "VARIANT_INTERLEAVE", "VARIANT_GEMM", "VARIANT_FP8",
     "VARIANT_FP8_SYNC", "VARIANT_MXFP8", "swiglu_forward_mx", "swiglu_quantize_mx",
     "swiglu_pack_kmajor", "LAYOUT_PACKED", "VARIANT_PACKED", "swiglu_packed_bytes",
-    "swiglu_pack_fragments",
+    "swiglu_pack_fragments", "VARIANT_FP8_PACKED", "swiglu_fp8_packed_bytes",
+    "swiglu_pack_fp8_fragments",
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -36,7 +37,7 @@ _LIB_PATH = os.path.join(_PKG, "libswiglu.so")
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_DEVICE, ERR_LAUNCH, ERR_ALLOC = range(6)
 LAYOUT_SEPARATE, LAYOUT_INTERLEAVED, LAYOUT_PACKED = 0, 1, 2
 VARIANT_AUTO, VARIANT_SYNC, VARIANT_INTERLEAVE, VARIANT_GEMM, VARIANT_FP8, VARIANT_FP8_SYNC, \
-    VARIANT_MXFP8, VARIANT_PACKED = 0, 1, 2, 3, 4, 5, 6, 7
+    VARIANT_MXFP8, VARIANT_PACKED, VARIANT_FP8_PACKED = 0, 1, 2, 3, 4, 5, 6, 7, 8
 
 
 class SwiGLUError(RuntimeError):
@@ -105,6 +106,8 @@ def load():
         "swiglu_pack_kmajor": ([p, p, p, p, i64, i64, p], st),
         "swiglu_packed_bytes": ([i64, i64], i64),
         "swiglu_pack_fragments": ([p, p, p, p, i64, i64, p], st),
+        "swiglu_fp8_packed_bytes": ([i64, i64], i64),
+        "swiglu_pack_fp8_fragments": ([p, p, p, i64, i64, p], st),
     }
     for name, (args, res) in sig.items():
         fn = getattr(lib, name)
@@ -206,6 +209,15 @@ def swiglu_packed_bytes(N: int, K: int) -> int:
 def swiglu_pack_fragments(handle, W1, W2, P, K, N, stream=None):
     _check(load().swiglu_pack_fragments(handle, _ptr(W1), _ptr(W2), _ptr(P), K, N,
                                         _stream(stream)), "swiglu_pack_fragments")
+
+
+def swiglu_fp8_packed_bytes(N: int, K: int) -> int:
+    return int(load().swiglu_fp8_packed_bytes(N, K))
+
+
+def swiglu_pack_fp8_fragments(handle, W8, P8, K, N, stream=None):
+    _check(load().swiglu_pack_fp8_fragments(handle, _ptr(W8), _ptr(P8), K, N, _stream(stream)),
+           "swiglu_pack_fp8_fragments")
 
 
 def swiglu_query(handle, M, N, K, layout=LAYOUT_SEPARATE):

@@ -234,6 +234,7 @@ int fp8_family(int variant) {
   if (variant == SWIGLU_VARIANT_AUTO || variant == SWIGLU_VARIANT_INTERLEAVE) return VAR_F8;
   if (variant == SWIGLU_VARIANT_SYNC) return VAR_F8_SYNC;
   if (variant == SWIGLU_VARIANT_MXFP8) return VAR_MX;  // queries only
+  if (variant == SWIGLU_VARIANT_FP8_PACKED) return VAR_F8_PACKED;
   return -1;
 }
 
@@ -361,6 +362,31 @@ swiglu_status_t swiglu_pack_interleaved(swiglu_handle_t h, const void* W1, const
   return SWIGLU_OK;
 }
 
+int64_t swiglu_fp8_packed_bytes(int64_t N, int64_t K) {
+  if (N <= 0 || K <= 0 || N > (kMaxDim >> 1) || K > kMaxDim) return 0;
+  return f8_packed_bytes(N, K);
+}
+
+swiglu_status_t swiglu_pack_fp8_fragments(swiglu_handle_t h, const void* W8, void* P8, int64_t K,
+                                          int64_t N, hipStream_t stream) {
+  if (!h || K < 0 || N < 0) return SWIGLU_ERR_INVALID_ARG;
+  if (K == 0 || N == 0) return SWIGLU_OK;
+  if (!W8 || !P8) return SWIGLU_ERR_INVALID_ARG;
+  if (K > kMaxDim || N > (kMaxDim >> 1)) return SWIGLU_ERR_UNSUPPORTED;
+  if (N % 8 != 0 || K % 16 != 0) return SWIGLU_ERR_UNSUPPORTED;
+  if (!aligned16(W8) || !aligned16(P8)) return SWIGLU_ERR_UNSUPPORTED;
+  const long long wb = 2LL * K * N, pb = f8_packed_bytes(N, K);
+  if (wb >= kMaxBytes || pb >= kMaxBytes) return SWIGLU_ERR_UNSUPPORTED;
+  if (overlaps(P8, pb, W8, wb)) return SWIGLU_ERR_INVALID_ARG;
+  swiglu_status_t st = check_device(h);
+  if (st != SWIGLU_OK) return st;
+  (void)hipGetLastError();
+  if (launch_pack_f8_frag((const uint8_t*)W8, (uint8_t*)P8, (int)(2 * N), (int)K, stream,
+                          h->cu_count) != hipSuccess)
+    return SWIGLU_ERR_LAUNCH;
+  return SWIGLU_OK;
+}
+
 int64_t swiglu_packed_bytes(int64_t N, int64_t K) {
   if (N <= 0 || K <= 0 || N > (kMaxDim >> 1) || K > kMaxDim) return 0;
   return 2 * packed_elems(N, K);
@@ -403,7 +429,8 @@ swiglu_status_t swiglu_forward_fp8(swiglu_handle_t h, const void* A8, const void
   if (M > kMaxDim || K > kMaxDim || N > (kMaxDim >> 1)) return SWIGLU_ERR_UNSUPPORTED;
   if (N % 8 != 0 || K % 16 != 0) return SWIGLU_ERR_UNSUPPORTED;
   if (!aligned16(Y) || !aligned16(A8) || !aligned16(W8)) return SWIGLU_ERR_UNSUPPORTED;
-  const long long ybytes = 2LL * M * N, abytes = M * K, wbytes = 2LL * N * K;
+  const long long ybytes = 2LL * M * N, abytes = M * K;
+  const long long wbytes = want == VAR_F8_PACKED ? f8_packed_bytes(N, K) : 2LL * N * K;
   if (ybytes >= kMaxBytes || abytes >= kMaxBytes || wbytes >= kMaxBytes)
     return SWIGLU_ERR_UNSUPPORTED;
   if (K > 0 && (overlaps(Y, ybytes, A8, abytes) || overlaps(Y, ybytes, W8, wbytes)))

@@ -1562,6 +1562,148 @@ __global__ __launch_bounds__(64 * NW) void f8_skinny_kernel(const uint8_t* __res
   }
 }
 
+// FP8 streaming on fragment-ordered W8: the layout of packed_kernel carried
+// over to the E4M3 k-major pairing.  W8 [2N, K] (row 2n Gate, 2n+1 Up) is cut
+// into blocks of 16 rows and steps of 128 k; block (rb, t) is 2 KB, the B
+// operand of one v_mfma_scale_f32_16x16x128_f8f6f4 for all 64 lanes, stored
+// as two 1 KB halves:
+//   P8[((rb T + t) 2 + h) 1024 + (16 g + i) 16 + e] = W8[16 rb + i][128 t + 64 h + 16 g + e]
+// with T = ceil(K / 128), h < 2, g < 4, i, e < 16, zeros past 2N and K.  Lane
+// 16 g + i reads 16 bytes of each half, so every load instruction reads 1 KB
+// contiguous and a row block is one contiguous span over K.  The workgroup
+// (NB row blocks, NW waves taking the steps in turn), the two register sets,
+// the LDS reduction in wave order and the epilogue are those of
+// f8_skinny_kernel; as in packed_kernel every load is issued unconditionally
+// (clamped addresses, k past K zeroed right before the MFMAs) so that the
+// in-order load counter stays exact.
+template <int MT, int NB, int NW>
+struct F8Packed {
+  static constexpr int kThreads = 64 * NW;
+  static constexpr int LDS_BYTES = NW * MT * NB * 64 * 16;
+  static_assert(LDS_BYTES <= 160 * 1024, "LDS");
+  static constexpr int SLAB_W = 16 * NB;  // W8 rows per workgroup
+  static constexpr int SLAB_Y = 8 * NB;   // output columns per workgroup
+};
+
+template <int MT, int NB, int NW>
+__global__ __launch_bounds__(64 * NW) void f8_packed_kernel(const uint8_t* __restrict__ A,
+                                                            const uint8_t* __restrict__ P,
+                                                            uint16_t* __restrict__ Y, int M,
+                                                            int N, int K, float sg, float su) {
+  using C = F8Packed<MT, NB, NW>;
+  __shared__ __attribute__((aligned(16))) f32x4 red[NW * MT * NB * 64];
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int unit = xcd_remap(blockIdx.x, gridDim.x);
+  const int m0 = blockIdx.y * MT * 16;
+  const int r16 = lane & 15, g = lane >> 4;
+  const int nsteps = (K + 127) / 128;
+  const int nrb = (2 * N + 15) / 16;  // row blocks in P8 (padding included)
+
+  // this lane's 16 bytes in the first half of each of the workgroup's row
+  // blocks; a block past the last one re-reads it (its outputs are past N)
+  const uint8_t* wp[NB];
+#pragma unroll
+  for (int b = 0; b < NB; ++b)
+    wp[b] = P + (size_t)min(unit * NB + b, nrb - 1) * (size_t)nsteps * 2048 + lane * 16;
+
+  f32x4 acc[MT][NB];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int b = 0; b < NB; ++b) acc[mt][b] = f32x4{};
+
+  auto load = [&](int s, u32x4 (&wv)[NB][2], u32x4 (&av)[MT][2]) __attribute__((always_inline)) {
+    // activations: rows past M re-read row M-1 (never stored), k past K
+    // re-reads the last 16 bytes (zeroed by mma); K % 16 == 0, K >= 16
+    const int k0 = min(s * 128 + 16 * g, K - 16), k1 = min(s * 128 + 64 + 16 * g, K - 16);
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      const uint8_t* p = A + (size_t)min(m0 + mt * 16 + r16, M - 1) * K;
+      av[mt][0] = load16(p + k0);
+      av[mt][1] = load16(p + k1);
+    }
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      const uint8_t* p = wp[b] + (size_t)s * 2048;
+      wv[b][0] = MT == 1 ? load16_stream(p) : load16(p);
+      wv[b][1] = MT == 1 ? load16_stream(p + 1024) : load16(p + 1024);
+    }
+  };
+  auto mma = [&](const u32x4 (&wv)[NB][2], const u32x4 (&av)[MT][2], int s)
+      __attribute__((always_inline)) {
+    const bool in0 = s * 128 + 16 * g < K, in1 = s * 128 + 64 + 16 * g < K;
+    const u32x4 z{0, 0, 0, 0};
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      const u32x4 a[2] = {in0 ? av[mt][0] : z, in1 ? av[mt][1] : z};
+#pragma unroll
+      for (int b = 0; b < NB; ++b) acc[mt][b] = mfma16_f8(wv[b], a, acc[mt][b]);
+    }
+  };
+
+  if (wave < nsteps) {
+    // steps wave, wave + NW, ..., last (n of them): pairs with unconditional
+    // MFMA groups, then an odd one (see packed_kernel)
+    const int n = (nsteps - 1 - wave) / NW + 1;
+    const int last = wave + (n - 1) * NW;
+    u32x4 wa[NB][2], aa[MT][2], wb[NB][2], ab[MT][2];
+    load(wave, wa, aa);
+    int s = wave;
+    for (int i = 0; i < n / 2; ++i, s += 2 * NW) {
+      load(s + NW, wb, ab);
+      __builtin_amdgcn_sched_barrier(0);
+      mma(wa, aa, s);
+      load(min(s + 2 * NW, last), wa, aa);
+      __builtin_amdgcn_sched_barrier(0);
+      mma(wb, ab, s + NW);
+    }
+    if (n & 1) mma(wa, aa, last);
+  }
+
+  // ---- split-K reduction through LDS (fixed order: wave 0, 1, ..., NW-1) ----
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int b = 0; b < NB; ++b) red[((wave * MT + mt) * NB + b) * 64 + lane] = acc[mt][b];
+  __syncthreads();
+  for (int q = wave; q < MT * NB; q += NW) {
+    const int mt = q / NB, b = q % NB;
+    f32x4 v = red[(mt * NB + b) * 64 + lane];
+    for (int w = 1; w < NW; ++w) v += red[((w * MT + mt) * NB + b) * 64 + lane];
+    // lane: A row r16 of the block, W8 rows 4g..4g+3 = (Gate, Up) of two columns
+    const int row = m0 + mt * 16 + r16;
+    const int col = unit * C::SLAB_Y + 8 * b + 2 * g;
+    if (row < M && col < N) {
+      const float y0 = silu(sg * v[0]) * (su * v[1]);
+      const float y1 = silu(sg * v[2]) * (su * v[3]);
+      *reinterpret_cast<uint32_t*>(Y + (size_t)row * N + col) = pack_bf16x2(y0, y1);
+    }
+  }
+}
+
+// Fragment-ordered W8 from W8 [R = 2N, K] (layout in front of
+// f8_packed_kernel): a thread copies one 16-byte chunk, row 16 rb + i, bytes
+// [128 t + 64 h + 16 g, +16), zeros past R and K.  Once per weight set.
+__global__ __launch_bounds__(256) void pack_f8_frag_kernel(const uint8_t* __restrict__ W8,
+                                                           uint8_t* __restrict__ P, int R, int K,
+                                                           size_t nchunks) {
+  const int nsteps = (K + 127) / 128;
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < nchunks;
+       i += (size_t)gridDim.x * blockDim.x) {
+    const int lane = (int)(i & 63);
+    const int h = (int)((i >> 6) & 1);
+    const size_t bt = i >> 7;  // rb * nsteps + t
+    const int t = (int)(bt % (size_t)nsteps);
+    const long long rb = (long long)(bt / (size_t)nsteps);
+    const long long r = 16 * rb + (lane & 15);
+    const int k0 = 128 * t + 64 * h + 16 * (lane >> 4);
+    u32x4 v{0, 0, 0, 0};
+    if (r < R && k0 < K) v = load16(W8 + (size_t)r * (size_t)K + k0);  // K % 16 == 0
+    *reinterpret_cast<u32x4*>(P + i * 16) = v;
+  }
+}
+
 // MXFP8 quantisation of bf16 rows [rows, K] (K % 32 == 0): one thread per
 // block of 32 values along K.  Shared exponent = floor(log2 max |x|) - 8 (8 =
 // the exponent of E4M3's largest normal), clamped to [-127, 127], -127 for a
@@ -1893,6 +2035,22 @@ static hipError_t launch_f8_skinny(const LaunchArgs& a) {
   return hipGetLastError();
 }
 
+template <int MT, int NB, int NW>
+static hipError_t launch_f8_packed(const LaunchArgs& a) {
+  using C = F8Packed<MT, NB, NW>;
+  const long long nunit = (2LL * a.N + C::SLAB_W - 1) / C::SLAB_W;
+  const long long nmb = (a.M + MT * 16 - 1) / (MT * 16);
+  if (nunit <= 0 || nmb <= 0) return hipSuccess;
+  if (nunit > 0x7fffffffLL || nmb > 65535) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((f8_packed_kernel<MT, NB, NW>), dim3((unsigned)nunit, (unsigned)nmb),
+                     dim3(C::kThreads), 0, a.stream, (const uint8_t*)a.A, (const uint8_t*)a.W1,
+                     a.Y, a.M, a.N, a.K, a.scale_g, a.scale_u);
+  return hipGetLastError();
+}
+
+#define F8_PACKED(mt, nb, nw)                                                              \
+  {VAR_F8_PACKED, 1, (mt) * 16, F8Packed<mt, nb, nw>::SLAB_Y, 128, nw, nw,                  \
+   F8Packed<mt, nb, nw>::LDS_BYTES, &launch_f8_packed<mt, nb, nw>}
 #define F8_SKINNY(mt, nb, nw)                                                              \
   {VAR_F8, 1, (mt) * 16, F8Skinny<mt, nb, nw>::SLAB_Y, 128, nw, nw,                         \
    F8Skinny<mt, nb, nw>::LDS_BYTES, &launch_f8_skinny<mt, nb, nw>}
@@ -2006,6 +2164,14 @@ static const KernelConfig kConfigs[] = {
     PACKED(2, 4, 2),                                                // 67
     PACKED(4, 4, 2),                                                // 68
     PACKED(2, 4, 4),                                                // 69
+    // ---- FP8 on fragment-ordered W8 (streaming) ------------------------------
+    F8_PACKED(1, 2, 1),                                             // 70
+    F8_PACKED(1, 1, 1),                                             // 71
+    F8_PACKED(1, 2, 2),                                             // 72
+    F8_PACKED(1, 4, 1),                                             // 73
+    F8_PACKED(1, 4, 2),                                             // 74
+    F8_PACKED(2, 2, 1),                                             // 75
+    F8_PACKED(4, 2, 1),                                             // 76
 };
 
 int config_count() { return (int)(sizeof(kConfigs) / sizeof(kConfigs[0])); }
@@ -2069,6 +2235,18 @@ hipError_t launch_pack_f8(const uint8_t* W1, const uint8_t* W2, uint8_t* W8, int
   if (blocks > cap) blocks = cap;
   hipLaunchKernelGGL(pack_f8_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, W1, W2, W8, N,
                      K);
+  return hipGetLastError();
+}
+
+hipError_t launch_pack_f8_frag(const uint8_t* W8, uint8_t* P, int R, int K, hipStream_t stream,
+                              int cu_count) {
+  const size_t nchunks = (size_t)((R + 15) / 16) * (size_t)((K + 127) / 128) * 128;
+  if (nchunks == 0) return hipSuccess;
+  size_t blocks = (nchunks + 255) / 256;
+  const size_t cap = (size_t)(cu_count > 0 ? cu_count : 256) * 8;
+  if (blocks > cap) blocks = cap;
+  hipLaunchKernelGGL(pack_f8_frag_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, W8, P, R,
+                     K, nchunks);
   return hipGetLastError();
 }
 

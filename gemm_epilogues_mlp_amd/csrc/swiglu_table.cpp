@@ -78,6 +78,8 @@ int select_config(int variant, long long M, long long N, long long K, int cu_cou
     if (M <= 16) return 4 * slabs >= 7 * cus ? 58 : (2 * slabs >= cus ? 65 : 63);
     return M <= 32 ? 69 : 62;
   }
+  // FP8 on fragment-ordered W8: streaming by 16-row groups at any M
+  if (variant == VAR_F8_PACKED) return M <= 16 ? 70 : (M <= 32 ? 75 : 76);
   if (variant == VAR_F8_SYNC) return M <= 192 ? 55 : (M <= 3072 ? 54 : 53);
   if (variant == VAR_F8) {
     // FP8: split-K weight streaming up to M = 64, then 64 x 128 tiles, 128-row

@@ -90,8 +90,10 @@ typedef enum {
                                     inputs (swiglu_forward_fp8, SYNC)          */
   SWIGLU_VARIANT_MXFP8 = 6,      /* Kernel-2 order on MXFP8 inputs
                                     (swiglu_forward_mx; swiglu_query_fp8)      */
-  SWIGLU_VARIANT_PACKED = 7      /* Kernel-2 order on fragment-ordered W_fused
+  SWIGLU_VARIANT_PACKED = 7,     /* Kernel-2 order on fragment-ordered W_fused
                                     (PACKED layout)                            */
+  SWIGLU_VARIANT_FP8_PACKED = 8  /* Kernel-2 order on FP8 inputs with
+                                    fragment-ordered W8 (swiglu_forward_fp8)   */
 } swiglu_variant_t;
 
 /* Description of one compiled kernel configuration. */
@@ -206,7 +208,7 @@ swiglu_status_t swiglu_query_unfused(swiglu_handle_t h, int64_t M, int64_t N,
 /* Tuned per-shape configurations.  A tuned file (written by the package's
  * tuner, python -m gemm_epilogues_mlp_amd.tune) is text:
  *   swiglu-tuned <signature: 16 hex digits> <arch>        first non-comment line
- *   <variant 1..7> <M> <N> <K> <config id> [ignored provenance]    one per shape
+ *   <variant 1..8> <M> <N> <K> <config id> [ignored provenance]    one per shape
  * with '#' comment lines.  The signature (swiglu_config_signature) identifies
  * the list of compiled configurations; a file written for a library with a
  * different list is refused, so an id can never name the wrong kernel.
@@ -251,9 +253,11 @@ swiglu_status_t swiglu_create_tuned(swiglu_handle_t* out, int device, const char
  * GEMM over the paired rows with the pair-multiply epilogue [RT §Metodologia,
  * Kernel-2]; SYNC runs the Gate rows over the whole K, applies SiLU in
  * registers while the Up tiles load, then the Up rows [RT §Metodologia,
- * Kernel-1]; any other variant is INVALID_ARG.  config_id < 0 uses the table;
- * a given id must be of variant FP8 (INTERLEAVE) or FP8_SYNC (SYNC), else
- * INVALID_ARG.  Y must not overlap A8 or W8. */
+ * Kernel-1]; FP8_PACKED runs the Kernel-2 order with W8 passed in fragment
+ * order (swiglu_pack_fp8_fragments; a streaming kernel made for decode-sized
+ * batches); any other variant is INVALID_ARG.  config_id < 0 uses the table;
+ * a given id must be of variant FP8 (INTERLEAVE), FP8_SYNC (SYNC) or
+ * FP8_PACKED, else INVALID_ARG.  Y must not overlap A8 or W8. */
 swiglu_status_t swiglu_forward_fp8(swiglu_handle_t h, const void* A8, const void* W8, void* Y,
                                    int64_t M, int64_t N, int64_t K, float scale_a,
                                    float scale_w1, float scale_w2, swiglu_variant_t variant,
@@ -271,6 +275,24 @@ swiglu_status_t swiglu_quantize_fp8(swiglu_handle_t h, const void* X, void* Q, i
  * overlap W1 or W2. */
 swiglu_status_t swiglu_pack_fp8(swiglu_handle_t h, const void* W1, const void* W2, void* W8,
                                 int64_t K, int64_t N, hipStream_t stream);
+
+/* Fragment-ordered W8 (variant FP8_PACKED): the W8 pairing above cut into
+ * blocks of 16 rows and steps of 128 k, each 2048-byte block the B operand of
+ * one 16x16x128 MFMA for 64 lanes, stored as two 1 KB halves.  With
+ * T = ceil(K / 128):
+ *   P8[((rb*T + t)*2 + h)*1024 + (16*g + i)*16 + e] = W8[16*rb + i][128*t + 64*h + 16*g + e]
+ * for rb < ceil(2N / 16), h < 2, g < 4, i < 16, e < 16, and 0 where the row
+ * is >= 2N or the byte >= K.  Every load instruction then reads 1 KB
+ * contiguous.  swiglu_fp8_packed_bytes gives its size (0 when N <= 0 or
+ * K <= 0 or a size is out of range). */
+int64_t swiglu_fp8_packed_bytes(int64_t N, int64_t K);
+
+/* P8 (swiglu_fp8_packed_bytes(N, K) bytes, padding included) from W8 [2N, K].
+ * A byte copy done once per weight set.  N % 8 == 0, K % 16 == 0, 16-byte
+ * aligned pointers and tensors under 2 GiB (else UNSUPPORTED); P8 must not
+ * overlap W8 (INVALID_ARG).  K == 0 or N == 0 is a no-op. */
+swiglu_status_t swiglu_pack_fp8_fragments(swiglu_handle_t h, const void* W8, void* P8,
+                                          int64_t K, int64_t N, hipStream_t stream);
 
 /* ---- MXFP8 inputs ----------------------------------------------------------
  * The OCP Microscaling format with E4M3 elements, which the TorchInductor/
@@ -310,8 +332,9 @@ swiglu_status_t swiglu_quantize_mx(swiglu_handle_t h, const void* X, void* Q, vo
 swiglu_status_t swiglu_pack_kmajor(swiglu_handle_t h, const void* W1, const void* W2, void* Wt,
                                    int64_t K, int64_t N, hipStream_t stream);
 
-/* The configuration swiglu_forward_fp8 (variant AUTO, INTERLEAVE or SYNC) or
- * swiglu_forward_mx (variant MXFP8) with config_id < 0 runs for a shape. */
+/* The configuration swiglu_forward_fp8 (variant AUTO, INTERLEAVE, SYNC or
+ * FP8_PACKED) or swiglu_forward_mx (variant MXFP8) with config_id < 0 runs for
+ * a shape. */
 swiglu_status_t swiglu_query_fp8(swiglu_handle_t h, int64_t M, int64_t N, int64_t K,
                                  swiglu_variant_t variant, swiglu_tile_t* tile);
 

@@ -79,8 +79,9 @@ def _load():
     lib.oracle_decode_mx.argtypes = [p, p, i64, i64, i64, p]
     lib.oracle_pack_kmajor_bf16.argtypes = [p, p, p, i64, i64]
     lib.oracle_pack_fragments.argtypes = [p, p, p, i64, i64]
+    lib.oracle_pack_fp8_fragments.argtypes = [p, p, i64, i64]
     for fn in (lib.oracle_quantize_mx, lib.oracle_decode_mx, lib.oracle_pack_kmajor_bf16,
-               lib.oracle_pack_fragments):
+               lib.oracle_pack_fragments, lib.oracle_pack_fp8_fragments):
         fn.restype = None
     lib.oracle_swiglu_mx_rows.argtypes = [p, p, p, p, i64, i64, i64, i64, p, i64, p, p, p,
                                           c_int]
@@ -369,6 +370,23 @@ def pack_fragments(w1, w2):
     K, N = w1.shape
     out = np.empty(packed_size(N, K), np.uint16)
     _load().oracle_pack_fragments(_ptr(w1), _ptr(w2), _ptr(out), K, N)
+    return out
+
+
+def fp8_packed_size(N: int, K: int) -> int:
+    """Bytes of the fragment-ordered W8: ceil(2N/16) * ceil(K/128) * 2048."""
+    return ((2 * N + 15) // 16) * ((K + 127) // 128) * 2048
+
+
+def pack_fp8_fragments(w8):
+    """Fragment-ordered W8 (flat bytes, fp8_packed_size(N, K)) from W8 [2N, K]:
+    byte W8[r, k] at ((rb*T + t)*2 + h)*1024 + (16g + i)*16 + e (rb = r // 16,
+    i = r % 16, t = k // 128, h = k % 128 // 64, g = k % 64 // 16, e = k % 16,
+    T = ceil(K/128)), zeros elsewhere."""
+    w8 = _u8(w8, "W8")
+    R, K = w8.shape
+    out = np.empty(((R + 15) // 16) * ((K + 127) // 128) * 2048, np.uint8)
+    _load().oracle_pack_fp8_fragments(_ptr(w8), _ptr(out), R, K)
     return out
 
 

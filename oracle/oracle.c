@@ -551,6 +551,23 @@ void oracle_pack_fragments(const uint16_t* w1, const uint16_t* w2, uint16_t* p, 
     }
 }
 
+/* Fragment-ordered W8 (the library's storage of the FP8 k-major pairing for
+ * its streaming kernel): every byte W8[r][k] of W8 [R, K] is placed at
+ *   ((rb*T + t)*2 + h)*1024 + (16*g + i)*16 + e
+ * with rb = r / 16, i = r % 16, t = k / 128, h = (k % 128) / 64,
+ * g = (k % 64) / 16, e = k % 16 and T = ceil(K / 128); every other position of
+ * the ceil(R / 16) * T * 2048 bytes is 0.  A byte copy. */
+void oracle_pack_fp8_fragments(const uint8_t* w8, uint8_t* p, int64_t R, int64_t K) {
+  const int64_t RB = (R + 15) / 16, T = (K + 127) / 128;
+  memset(p, 0, (size_t)(RB * T * 2048));
+  for (int64_t r = 0; r < R; ++r)
+    for (int64_t k = 0; k < K; ++k) {
+      const int64_t rb = r / 16, i = r % 16;
+      const int64_t t = k / 128, h = (k % 128) / 64, g = (k % 64) / 16, e = k % 16;
+      p[((rb * T + t) * 2 + h) * 1024 + (16 * g + i) * 16 + e] = w8[r * K + k];
+    }
+}
+
 /* bf16 W1, W2 [K, N] -> Wt [2N, K] bf16: row 2n = W1[:, n], row 2n+1 = W2[:, n]
  * (the Kernel-2 pairing with k contiguous), a bit copy. */
 void oracle_pack_kmajor_bf16(const uint16_t* w1, const uint16_t* w2, uint16_t* wt, int64_t K,

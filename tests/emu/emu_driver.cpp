@@ -110,10 +110,13 @@ bool run_config(int id, int M, int N, int K) {
     a.W2 = nullptr;
     a.ldw = N;
   }
-  if (c->variant == VAR_F8 || c->variant == VAR_F8_SYNC || c->variant == VAR_MX) {
-    // byte tensors: A8 [M, K], W8 [2N, K]; MX scales SA [M, ks], SW [2N, ks]
+  if (c->variant == VAR_F8 || c->variant == VAR_F8_SYNC || c->variant == VAR_MX ||
+      c->variant == VAR_F8_PACKED) {
+    // byte tensors: A8 [M, K], W8 [2N, K] (or its fragment order P8); MX
+    // scales SA [M, ks], SW [2N, ks]
     a.A = alloc16(((size_t)M * K + 1) / 2, "A8");
-    a.W1 = alloc16((size_t)N * K, "W8");
+    a.W1 = c->variant == VAR_F8_PACKED ? alloc16((size_t)f8_packed_bytes(N, K) / 2, "P8")
+                                       : alloc16((size_t)N * K, "W8");
     a.ldw = K;
     a.scale_g = a.scale_u = 1.0f;
     if (c->variant == VAR_MX) {
@@ -157,6 +160,17 @@ bool run_elementwise(size_t n) {
   uint8_t* w8 = (uint8_t*)alloc16((size_t)K * N, "W8");
   launch_pack_f8(w1, w2, w8, N, K, nullptr, 256);
   free_all();
+  // fragment-ordered W8 from W8 [R, 144] (R = n / 144 rounded down to a
+  // multiple of 16: a partial step of 128 k)
+  {
+    const int Kp8 = 144, Rp8 = (int)(n / 144) / 16 * 16;
+    if (Rp8 > 0) {
+      uint8_t* w8s = (uint8_t*)alloc16((size_t)Rp8 * Kp8 / 2, "W8s");
+      uint8_t* p8 = (uint8_t*)alloc16((size_t)f8_packed_bytes(Rp8 / 2, Kp8) / 2, "P8s");
+      launch_pack_f8_frag(w8s, p8, Rp8, Kp8, nullptr, 256);
+      free_all();
+    }
+  }
   // MX quantisation of rows of K = 96 (scale stride 16), and the bf16 k-major pack
   {
     const int Kq = 96, ksq = 16, rows = (int)(n / Kq);
@@ -218,7 +232,8 @@ int main(int argc, char** argv) {
     } else {
       if (config_at(id) && config_at(id)->variant == VAR_MX)
         for (const auto& s : shapes_mx) run_config(id, s[0], s[1], s[2]);
-      else if (config_at(id) && (config_at(id)->variant == VAR_F8 || config_at(id)->variant == VAR_F8_SYNC))
+      else if (config_at(id) && (config_at(id)->variant == VAR_F8 || config_at(id)->variant == VAR_F8_SYNC ||
+                                 config_at(id)->variant == VAR_F8_PACKED))
         for (const auto& s : shapes_f8) run_config(id, s[0], s[1], s[2]);
       else
         for (const auto& s : shapes) run_config(id, s[0], s[1], s[2]);

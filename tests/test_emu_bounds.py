@@ -60,6 +60,10 @@ CASES = [
     (16, 18944, 3584, list(range(58, 70))),
     (128, 4864, 896, list(range(58, 70))),
     (33, 72, 40, list(range(58, 70))),
+    # FP8 on fragment-ordered W8: decode, 0.5B, ragged (partial step of 128)
+    (16, 18944, 3584, list(range(70, 77))),
+    (128, 4864, 896, list(range(70, 77))),
+    (33, 72, 144, list(range(70, 77))),
 ]
 
 
@@ -80,6 +84,8 @@ LIMIT_CASES = [
     (16, 32768, 16376, [4, 11, 18, 23, 12], 8),
     # fragment-ordered W_fused just under 2 GiB: 511 slabs x 512 steps x 8 KB
     (16, 32704, 16376, list(range(58, 70)), 8),
+    # fragment-ordered W8 just under 2 GiB: 4096 row blocks x 255 steps x 2 KB
+    (16, 32768, 32640, list(range(70, 77)), 8),
     (256, 32768, 16376, [1, 8, 16], 4),
     # byte tensors: A8 = 65536 x 32704 B, W8 = 2 x 32768 x 32704 B (K % 64 == 0)
     (65536, 64, 32704, [43, 53, 56], 4),

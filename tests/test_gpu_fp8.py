@@ -64,8 +64,9 @@ def fp8_inputs(M, N, K, seed):
 
 
 def variant_of(cfg):
-    return sw.VARIANT_SYNC if sw.swiglu_config_info(cfg)["variant"] == sw.VARIANT_FP8_SYNC \
-        else sw.VARIANT_INTERLEAVE
+    v = sw.swiglu_config_info(cfg)["variant"]
+    return {sw.VARIANT_FP8_SYNC: sw.VARIANT_SYNC,
+            sw.VARIANT_FP8_PACKED: sw.VARIANT_FP8_PACKED}.get(v, sw.VARIANT_INTERLEAVE)
 
 
 def forward(handle, a8, w8, M, N, K, scales, cfg=-1, variant=sw.VARIANT_AUTO):
@@ -229,16 +230,19 @@ def workload(request):
     rows = np.unique(np.concatenate([[0, 1, w.M // 2, w.M - 1], rng.integers(0, w.M, 12)]))
     y_ref = oracle.swiglu_fp8_rows(a8, w18, w28, sa, s1, s2, rows=rows)
     w8 = oracle.pack_fp8_kmajor(w18, w28)
-    return dict(w=w, a8=a8, w8=w8, w18=w18, w28=w28, s=(sa, s1, s2), rows=rows, y_ref=y_ref)
+    return dict(w=w, a8=a8, w8=w8, p8=oracle.pack_fp8_fragments(w8), w18=w18, w28=w28,
+                s=(sa, s1, s2), rows=rows, y_ref=y_ref)
 
 
-@pytest.mark.parametrize("variant", [sw.VARIANT_AUTO, sw.VARIANT_SYNC], ids=["auto", "sync"])
+@pytest.mark.parametrize("variant", [sw.VARIANT_AUTO, sw.VARIANT_SYNC, sw.VARIANT_FP8_PACKED],
+                         ids=["auto", "sync", "packed"])
 def test_fp8_workload_parity(handle, workload, variant):
     d = workload
     w = d["w"]
     cfg = sw.swiglu_query_fp8(handle, w.M, w.N, w.K, variant)
     log(f"fp8 {w.name} variant {variant}: config {cfg['id']}")
-    y = forward(handle, d["a8"], d["w8"], w.M, w.N, w.K, d["s"], variant=variant)
+    wt = d["p8"] if variant == sw.VARIANT_FP8_PACKED else d["w8"]
+    y = forward(handle, d["a8"], wt, w.M, w.N, w.K, d["s"], variant=variant)
     yv = decode(y)
     assert np.all(np.isfinite(yv)), "unwritten or non-finite outputs"
     assert_parity(y[d["rows"]], d["y_ref"], f"fp8 {w.name} sampled rows")
@@ -254,9 +258,80 @@ def test_fp8_workload_device_pack_and_quantise_match(handle, workload):
     sw.swiglu_pack_fp8(handle, dev8(d["w18"]), dev8(d["w28"]), w8, w.K, w.N)
     t.cuda.synchronize()
     assert np.array_equal(host8(w8), d["w8"])
+    p8 = t.full((sw.swiglu_fp8_packed_bytes(w.N, w.K),), 0x55, dtype=t.uint8, device="cuda")
+    sw.swiglu_pack_fp8_fragments(handle, w8, p8, w.K, w.N)
+    t.cuda.synchronize()
+    assert np.array_equal(host8(p8), d["p8"])
+    del w8, p8
     a = I.make_a(w.M, w.K, 1000 * w.index + I.TENSOR_A)
     xa = t.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda()
     q = t.empty((w.M, w.K), dtype=t.uint8, device="cuda")
     sw.swiglu_quantize_fp8(handle, xa, q, w.M * w.K, float(np.float32(1.0) / np.float32(d["s"][0])))
     t.cuda.synchronize()
     assert np.array_equal(host8(q), d["a8"])
+
+
+# --------------------------------------------------------------------------- fragment order
+def fp8_packed_configs():
+    return [i for i in range(sw.swiglu_config_count())
+            if sw.swiglu_config_info(i)["variant"] == sw.VARIANT_FP8_PACKED]
+
+
+PACKED_SHAPES = SHAPES + [(33, 72, 144), (16, 4864, 896)]
+
+
+@pytest.fixture(scope="module")
+def packed_cases():
+    out = {}
+    for i, (M, N, K) in enumerate(PACKED_SHAPES):
+        a8, w18, w28, sa, s1, s2 = fp8_inputs(M, N, K, 500 + i)
+        w8 = oracle.pack_fp8_kmajor(w18, w28)
+        out[(M, N, K)] = dict(a8=a8, w8=w8, p8=oracle.pack_fp8_fragments(w8), s=(sa, s1, s2),
+                              y=oracle.swiglu_fp8_rows(a8, w18, w28, sa, s1, s2))
+    return out
+
+
+@pytest.mark.parametrize("shape", PACKED_SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_fp8_fragment_pack_bitwise(handle, packed_cases, shape):
+    t = torch()
+    M, N, K = shape
+    c = packed_cases[shape]
+    p8 = t.full((sw.swiglu_fp8_packed_bytes(N, K),), 0x55, dtype=t.uint8, device="cuda")
+    sw.swiglu_pack_fp8_fragments(handle, dev8(c["w8"]), p8, K, N)
+    t.cuda.synchronize()
+    assert np.array_equal(host8(p8), c["p8"])
+
+
+@pytest.mark.parametrize("shape", PACKED_SHAPES, ids=lambda s: "x".join(map(str, s)))
+@pytest.mark.parametrize("cfg", fp8_packed_configs())
+def test_fp8_packed_config_parity(handle, packed_cases, cfg, shape):
+    M, N, K = shape
+    c = packed_cases[shape]
+    log(f"fp8 packed config {cfg} {sw.swiglu_config_info(cfg)} shape {shape}")
+    y = forward(handle, c["a8"], c["p8"], M, N, K, c["s"], cfg)
+    assert_parity(y, c["y"], f"fp8 packed cfg {cfg} {shape}")
+
+
+def test_fp8_packed_k_zero_and_errors(handle):
+    t = torch()
+    M, N = 40, 72
+    y = t.full((M, N), -1, dtype=t.int16, device="cuda")
+    sw.swiglu_forward_fp8(handle, 0, 0, y, M, N, 0, variant=sw.VARIANT_FP8_PACKED)
+    t.cuda.synchronize()
+    assert np.all(decode(host(y)) == 0.0)
+    assert sw.swiglu_fp8_packed_bytes(N, 144) == ((2 * N + 15) // 16) * 2 * 2048
+    assert sw.swiglu_fp8_packed_bytes(N, 0) == 0
+    a = t.zeros((M, 144), dtype=t.uint8, device="cuda")
+    p = t.zeros((sw.swiglu_fp8_packed_bytes(N, 144),), dtype=t.uint8, device="cuda")
+    plain = [i for i in fp8_configs() if variant_of(i) == sw.VARIANT_INTERLEAVE][0]
+    with pytest.raises(sw.SwiGLUError) as e:               # a k-major config on P8
+        sw.swiglu_forward_fp8(handle, a, p, y, M, N, 144, config_id=plain,
+                              variant=sw.VARIANT_FP8_PACKED)
+    assert e.value.status == sw.ERR_INVALID_ARG
+    w8 = t.zeros((2 * N, 144), dtype=t.uint8, device="cuda")
+    with pytest.raises(sw.SwiGLUError) as e:               # N % 8
+        sw.swiglu_pack_fp8_fragments(handle, w8, p, 144, 68)
+    assert e.value.status == sw.ERR_UNSUPPORTED
+    with pytest.raises(sw.SwiGLUError) as e:               # P8 overlaps W8
+        sw.swiglu_pack_fp8_fragments(handle, p, p, 144, N)
+    assert e.value.status == sw.ERR_INVALID_ARG

@@ -82,3 +82,64 @@ def test_matches_axis_algebra(K, N):
 def test_empty():
     w = np.zeros((0, 16), np.uint16)
     assert oracle.pack_fragments(w, w).size == 0
+
+
+# ---- FP8: fragment-ordered W8 ------------------------------------------------
+# W8 [2N, K] (E4M3 bytes, row 2n Gate, 2n+1 Up) cut into blocks of 16 rows and
+# steps of 128 k, each 2 KB block stored as two 1 KB halves:
+#   P8[((rb T + t) 2 + h) 1024 + (16 g + i) 16 + e] = W8[16 rb + i][128 t + 64 h + 16 g + e]
+
+
+def _golden_fp8():
+    path = os.path.join(os.path.dirname(__file__), "golden", "fp8_fragment_layout.txt")
+    entries, shape = [], None
+    for line in open(path):
+        line = line.split("#")[0].strip()
+        if not line:
+            continue
+        if line.startswith("shape"):
+            shape = tuple(int(x) for x in line.split()[1:])
+            continue
+        i, v = line.split()
+        entries.append((int(i), int(v)))
+    return shape, entries
+
+
+def test_fp8_hand_derived_positions():
+    (N, K), entries = _golden_fp8()
+    r = np.arange(2 * N, dtype=np.int64)[:, None]
+    k = np.arange(K, dtype=np.int64)[None, :]
+    w8 = ((144 * r + k) % 251 + 1).astype(np.uint8)
+    p = oracle.pack_fp8_fragments(w8)
+    assert p.size == 8192 == oracle.fp8_packed_size(N, K)
+    for i, v in entries:
+        assert int(p[i]) == v, f"P8[{i}] = {int(p[i])}, hand derivation says {v}"
+
+
+@pytest.mark.parametrize("N,K", [(12, 144), (8, 16), (64, 256), (36, 400), (100, 128)])
+def test_fp8_every_byte_once_zeros_elsewhere(N, K):
+    """Distinct 16-bit tags split over two byte planes: each (row, k) appears
+    exactly once, padding is zero."""
+    R = 2 * N
+    tag = np.arange(1, R * K + 1, dtype=np.int64).reshape(R, K)
+    assert tag.max() < 65536
+    lo, hi = (tag & 0xFF).astype(np.uint8), (tag >> 8).astype(np.uint8)
+    plo, phi = oracle.pack_fp8_fragments(lo), oracle.pack_fp8_fragments(hi)
+    got = plo.astype(np.int64) | (phi.astype(np.int64) << 8)
+    assert got.size == ((R + 15) // 16) * ((K + 127) // 128) * 2048
+    nz = got[got != 0]
+    assert nz.size == R * K
+    assert np.array_equal(np.sort(nz), tag.reshape(-1))
+
+
+@pytest.mark.parametrize("N,K", [(12, 144), (8, 16), (64, 256), (36, 400), (9472, 3584)])
+def test_fp8_matches_axis_algebra(N, K):
+    """Pad W8 to [16 RB, 128 T], split the row as (rb, i) and k as (t, h, g, e),
+    and order the axes (rb, t, h, g, i, e)."""
+    rng = np.random.default_rng(N + K)
+    w8 = rng.integers(0, 256, (2 * N, K), dtype=np.uint8)
+    RB, T = (2 * N + 15) // 16, (K + 127) // 128
+    pad = np.zeros((16 * RB, 128 * T), np.uint8)
+    pad[:2 * N, :K] = w8
+    ref = pad.reshape(RB, 16, T, 2, 4, 16).transpose(0, 2, 3, 4, 1, 5).reshape(-1)
+    assert np.array_equal(oracle.pack_fp8_fragments(w8), ref)
