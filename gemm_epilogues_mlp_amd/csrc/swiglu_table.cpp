@@ -74,12 +74,21 @@ int select_config(int variant, long long M, long long N, long long K, int cu_cou
     // CU (7B: 296 slabs -> 592 workgroups), quarter slabs below (0.5B: 76).
     // Above M = 16 the 32- and 64-row blocks win; above M = 64 the weights
     // are re-read once per 64 rows (a fallback, not a fast path).
+    // Narrow N (under 64 slabs: one GPU's share under 8-way tensor
+    // parallelism) takes 8 waves per quarter slab (tuner: +3-5 %).
     const long long slabs = packed_slabs(N), cus = cu_count > 0 ? cu_count : 256;
-    if (M <= 16) return 4 * slabs >= 7 * cus ? 58 : (2 * slabs >= cus ? 65 : 63);
+    if (M <= 16)
+      return 4 * slabs >= 7 * cus ? 58 : (2 * slabs >= cus ? 65 : (slabs >= 64 ? 63 : 64));
     return M <= 32 ? 69 : 62;
   }
-  // FP8 on fragment-ordered W8: streaming by 16-row groups at any M
-  if (variant == VAR_F8_PACKED) return M <= 16 ? 70 : (M <= 32 ? 75 : 76);
+  // FP8 on fragment-ordered W8: streaming by 16-row groups at any M; one
+  // wave per 32 W8 rows, two waves splitting K when that leaves fewer than two
+  // workgroups per CU (tuner at N = 2368 and 3696: +29 %)
+  if (variant == VAR_F8_PACKED) {
+    const long long units = (2 * N + 31) / 32, cus = cu_count > 0 ? cu_count : 256;
+    if (M <= 16) return units >= 2 * cus ? 70 : 72;
+    return M <= 32 ? 75 : 76;
+  }
   if (variant == VAR_F8_SYNC) return M <= 192 ? 55 : (M <= 3072 ? 54 : 53);
   if (variant == VAR_F8) {
     // FP8: split-K weight streaming up to M = 64, then 64 x 128 tiles, 128-row
