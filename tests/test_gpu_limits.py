@@ -61,3 +61,56 @@ def test_largest_tensors(handle, shape):
     sw.swiglu_forward(handle, a, wf, None, y, M, N, K, sw.LAYOUT_INTERLEAVED)
     t.cuda.synchronize()
     assert_parity(host(y)[rows], y_ref, f"interleaved {shape}")
+
+
+# fragment-ordered W_fused just under 2 GiB: 511 slabs x 512 steps x 8 KB
+@pytest.mark.parametrize("M", [16, 40])
+def test_largest_packed_weights(handle, M):
+    import torch as t
+    N, K = 32704, 16376
+    pbytes = sw.swiglu_packed_bytes(N, K)
+    assert pbytes < 2 ** 31 <= pbytes + 2 ** 23
+    log(f"packed limit M={M} N={N} K={K} ({pbytes} bytes)")
+    g = t.Generator(device="cuda").manual_seed(M + 7)
+    a, w1, w2 = _bf16(t, (M, K), 1.0, g), _bf16(t, (K, N), K ** -0.5, g), \
+        _bf16(t, (K, N), K ** -0.5, g)
+    rows = np.unique(np.r_[0, M - 1, np.random.default_rng(M).integers(0, M, 2)])
+    y_ref = oracle.swiglu_rows(host(a[t.from_numpy(rows).cuda()]), host(w1), host(w2))
+    p = t.empty((pbytes // 2,), dtype=t.int16, device="cuda")
+    sw.swiglu_pack_fragments(handle, w1, w2, p, K, N)
+    del w1, w2
+    y = t.full((M, N), -1, dtype=t.int16, device="cuda")
+    sw.swiglu_forward(handle, a, p, None, y, M, N, K, sw.LAYOUT_PACKED)
+    t.cuda.synchronize()
+    assert_parity(host(y)[rows], y_ref, f"packed M={M}")
+    del p, y
+
+
+# fragment-ordered W8 just under 2 GiB: 4096 row blocks x 255 steps x 2 KB
+def test_largest_fp8_packed_weights(handle):
+    import torch as t
+    M, N, K = 16, 32768, 32640
+    pbytes = sw.swiglu_fp8_packed_bytes(N, K)
+    assert pbytes < 2 ** 31 <= pbytes + 2 ** 23 and 2 * N * K < 2 ** 31
+    log(f"fp8 packed limit M={M} N={N} K={K} ({pbytes} bytes)")
+    rng = np.random.default_rng(11)
+    # finite E4M3 codes of both signs, magnitudes up to 0.25 (code 0x28) so sums stay small
+    codes = lambda shape: (rng.integers(0, 0x29, shape, dtype=np.uint8) |
+                           (rng.integers(0, 2, shape, dtype=np.uint8) << 7))
+    a8, w18, w28 = codes((M, K)), codes((K, N)), codes((K, N))
+    scales = (1.0, 2.0 ** -4, 2.0 ** -4)
+    rows = np.array([0, 5, M - 1])
+    y_ref = oracle.swiglu_fp8_rows(a8, w18, w28, *scales, rows=rows)
+    w8 = t.empty((2 * N, K), dtype=t.uint8, device="cuda")
+    d1, d2 = t.from_numpy(w18).cuda(), t.from_numpy(w28).cuda()
+    sw.swiglu_pack_fp8(handle, d1, d2, w8, K, N)
+    del d1, d2
+    p8 = t.empty((pbytes,), dtype=t.uint8, device="cuda")
+    sw.swiglu_pack_fp8_fragments(handle, w8, p8, K, N)
+    del w8
+    y = t.full((M, N), -1, dtype=t.int16, device="cuda")
+    sw.swiglu_forward_fp8(handle, t.from_numpy(a8).cuda(), p8, y, M, N, K, *scales,
+                          variant=sw.VARIANT_FP8_PACKED)
+    t.cuda.synchronize()
+    assert_parity(host(y)[rows], y_ref, "fp8 packed limit")
+    del p8, y
