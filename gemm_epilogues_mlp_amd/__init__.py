@@ -28,7 +28,8 @@ __all__ = [
     "VARIANT_FP8_SYNC", "VARIANT_MXFP8", "swiglu_forward_mx", "swiglu_quantize_mx",
     "swiglu_pack_kmajor", "LAYOUT_PACKED", "VARIANT_PACKED", "swiglu_packed_bytes",
     "swiglu_pack_fragments", "VARIANT_FP8_PACKED", "swiglu_fp8_packed_bytes",
-    "swiglu_pack_fp8_fragments",
+    "swiglu_pack_fp8_fragments", "VARIANT_MXFP8_PACKED", "swiglu_forward_mx_packed",
+    "swiglu_mx_packed_bytes", "swiglu_pack_mx_fragments",
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -37,7 +38,8 @@ _LIB_PATH = os.path.join(_PKG, "libswiglu.so")
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_DEVICE, ERR_LAUNCH, ERR_ALLOC = range(6)
 LAYOUT_SEPARATE, LAYOUT_INTERLEAVED, LAYOUT_PACKED = 0, 1, 2
 VARIANT_AUTO, VARIANT_SYNC, VARIANT_INTERLEAVE, VARIANT_GEMM, VARIANT_FP8, VARIANT_FP8_SYNC, \
-    VARIANT_MXFP8, VARIANT_PACKED, VARIANT_FP8_PACKED = 0, 1, 2, 3, 4, 5, 6, 7, 8
+    VARIANT_MXFP8, VARIANT_PACKED, VARIANT_FP8_PACKED, VARIANT_MXFP8_PACKED = \
+    0, 1, 2, 3, 4, 5, 6, 7, 8, 9
 
 
 class SwiGLUError(RuntimeError):
@@ -108,6 +110,9 @@ def load():
         "swiglu_pack_fragments": ([p, p, p, p, i64, i64, p], st),
         "swiglu_fp8_packed_bytes": ([i64, i64], i64),
         "swiglu_pack_fp8_fragments": ([p, p, p, i64, i64, p], st),
+        "swiglu_forward_mx_packed": ([p, p, p, p, p, p, i64, i64, i64, i64, i32, p], st),
+        "swiglu_mx_packed_bytes": ([i64, i64], i64),
+        "swiglu_pack_mx_fragments": ([p, p, p, i64, i64, p], st),
     }
     for name, (args, res) in sig.items():
         fn = getattr(lib, name)
@@ -246,6 +251,22 @@ def swiglu_forward_mx(handle, A8, SA, W8, SW, Y, M, N, K, ks, config_id=-1, stre
     """MXFP8: A8 [M, K] + SA [M, ks], W8 [2N, K] + SW [2N, ks] (uint8); Y bf16 [M, N]."""
     _check(load().swiglu_forward_mx(handle, _ptr(A8), _ptr(SA), _ptr(W8), _ptr(SW), _ptr(Y), M,
                                     N, K, ks, config_id, _stream(stream)), "swiglu_forward_mx")
+
+
+def swiglu_forward_mx_packed(handle, A8, SA, P8, SW, Y, M, N, K, ks, config_id=-1,
+                             stream=None):
+    _check(load().swiglu_forward_mx_packed(handle, _ptr(A8), _ptr(SA), _ptr(P8), _ptr(SW),
+                                           _ptr(Y), M, N, K, ks, config_id, _stream(stream)),
+           "swiglu_forward_mx_packed")
+
+
+def swiglu_mx_packed_bytes(N: int, K: int) -> int:
+    return int(load().swiglu_mx_packed_bytes(N, K))
+
+
+def swiglu_pack_mx_fragments(handle, W8, P8, K, N, stream=None):
+    _check(load().swiglu_pack_mx_fragments(handle, _ptr(W8), _ptr(P8), K, N, _stream(stream)),
+           "swiglu_pack_mx_fragments")
 
 
 def swiglu_quantize_mx(handle, X, Q, S, rows, K, ks, stream=None):

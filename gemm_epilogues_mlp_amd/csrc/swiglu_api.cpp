@@ -235,6 +235,7 @@ int fp8_family(int variant) {
   if (variant == SWIGLU_VARIANT_SYNC) return VAR_F8_SYNC;
   if (variant == SWIGLU_VARIANT_MXFP8) return VAR_MX;  // queries only
   if (variant == SWIGLU_VARIANT_FP8_PACKED) return VAR_F8_PACKED;
+  if (variant == SWIGLU_VARIANT_MXFP8_PACKED) return VAR_MX_PACKED;  // queries only
   return -1;
 }
 
@@ -418,7 +419,7 @@ swiglu_status_t swiglu_forward_fp8(swiglu_handle_t h, const void* A8, const void
                                    int32_t config_id, hipStream_t stream) {
   if (!h || M < 0 || N < 0 || K < 0) return SWIGLU_ERR_INVALID_ARG;
   const int want = fp8_family((int)variant);
-  if (want < 0 || want == VAR_MX) return SWIGLU_ERR_INVALID_ARG;
+  if (want < 0 || want == VAR_MX || want == VAR_MX_PACKED) return SWIGLU_ERR_INVALID_ARG;
   int id = config_id;
   if (id >= 0) {
     const KernelConfig* c = config_at(id);
@@ -456,14 +457,19 @@ swiglu_status_t swiglu_forward_fp8(swiglu_handle_t h, const void* A8, const void
   return launch(h, config_at(id), id, a);
 }
 
-swiglu_status_t swiglu_forward_mx(swiglu_handle_t h, const void* A8, const void* SA,
-                                  const void* W8, const void* SW, void* Y, int64_t M, int64_t N,
-                                  int64_t K, int64_t ks, int32_t config_id, hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+// MXFP8 forward on W8 in k-major order (want = VAR_MX) or in the streaming
+// kernel's fragment order (want = VAR_MX_PACKED)
+swiglu_status_t forward_mx(swiglu_handle_t h, const void* A8, const void* SA, const void* W8,
+                           const void* SW, void* Y, int64_t M, int64_t N, int64_t K, int64_t ks,
+                           int32_t config_id, hipStream_t stream, int want) {
   if (!h || M < 0 || N < 0 || K < 0 || ks < 0) return SWIGLU_ERR_INVALID_ARG;
   int id = config_id;
   if (id >= 0) {
     const KernelConfig* c = config_at(id);
-    if (!c || c->variant != VAR_MX) return SWIGLU_ERR_INVALID_ARG;
+    if (!c || c->variant != want) return SWIGLU_ERR_INVALID_ARG;
   }
   if (M == 0 || N == 0) return SWIGLU_OK;
   if (!Y || (K > 0 && (!A8 || !W8 || !SA || !SW))) return SWIGLU_ERR_INVALID_ARG;
@@ -473,7 +479,8 @@ swiglu_status_t swiglu_forward_mx(swiglu_handle_t h, const void* A8, const void*
   if (N % 8 != 0 || K % 64 != 0 || ks % 16 != 0) return SWIGLU_ERR_UNSUPPORTED;
   if (!aligned16(Y) || !aligned16(A8) || !aligned16(W8) || !aligned16(SA) || !aligned16(SW))
     return SWIGLU_ERR_UNSUPPORTED;
-  const long long ybytes = 2LL * M * N, abytes = M * K, wbytes = 2LL * N * K;
+  const long long ybytes = 2LL * M * N, abytes = M * K;
+  const long long wbytes = want == VAR_MX_PACKED ? mx_packed_bytes(N, K) : 2LL * N * K;
   const long long sabytes = M * ks, swbytes = 2LL * N * ks;
   if (ybytes >= kMaxBytes || abytes >= kMaxBytes || wbytes >= kMaxBytes ||
       sabytes >= kMaxBytes || swbytes >= kMaxBytes)
@@ -483,7 +490,7 @@ swiglu_status_t swiglu_forward_mx(swiglu_handle_t h, const void* A8, const void*
     return SWIGLU_ERR_INVALID_ARG;
   swiglu_status_t st = check_device(h);
   if (st != SWIGLU_OK) return st;
-  if (id < 0) id = choose(h, VAR_MX, M, N, K);
+  if (id < 0) id = choose(h, want, M, N, K);
   if (id < 0) return SWIGLU_ERR_UNSUPPORTED;
   LaunchArgs a;
   a.A = (const uint16_t*)A8;
@@ -501,6 +508,48 @@ swiglu_status_t swiglu_forward_mx(swiglu_handle_t h, const void* A8, const void*
   a.ks = (int)ks;
   a.stream = stream;
   return launch(h, config_at(id), id, a);
+}
+
+}  // namespace
+
+extern "C" {
+
+swiglu_status_t swiglu_forward_mx(swiglu_handle_t h, const void* A8, const void* SA,
+                                  const void* W8, const void* SW, void* Y, int64_t M, int64_t N,
+                                  int64_t K, int64_t ks, int32_t config_id, hipStream_t stream) {
+  return forward_mx(h, A8, SA, W8, SW, Y, M, N, K, ks, config_id, stream, VAR_MX);
+}
+
+swiglu_status_t swiglu_forward_mx_packed(swiglu_handle_t h, const void* A8, const void* SA,
+                                         const void* P8, const void* SW, void* Y, int64_t M,
+                                         int64_t N, int64_t K, int64_t ks, int32_t config_id,
+                                         hipStream_t stream) {
+  return forward_mx(h, A8, SA, P8, SW, Y, M, N, K, ks, config_id, stream, VAR_MX_PACKED);
+}
+
+int64_t swiglu_mx_packed_bytes(int64_t N, int64_t K) {
+  if (N <= 0 || K <= 0 || K % 64 != 0 || N > (kMaxDim >> 1) || K > kMaxDim) return 0;
+  return mx_packed_bytes(N, K);
+}
+
+swiglu_status_t swiglu_pack_mx_fragments(swiglu_handle_t h, const void* W8, void* P8, int64_t K,
+                                         int64_t N, hipStream_t stream) {
+  if (!h || K < 0 || N < 0) return SWIGLU_ERR_INVALID_ARG;
+  if (K == 0 || N == 0) return SWIGLU_OK;
+  if (!W8 || !P8) return SWIGLU_ERR_INVALID_ARG;
+  if (K > kMaxDim || N > (kMaxDim >> 1)) return SWIGLU_ERR_UNSUPPORTED;
+  if (N % 8 != 0 || K % 64 != 0) return SWIGLU_ERR_UNSUPPORTED;
+  if (!aligned16(W8) || !aligned16(P8)) return SWIGLU_ERR_UNSUPPORTED;
+  const long long wb = 2LL * K * N, pb = mx_packed_bytes(N, K);
+  if (wb >= kMaxBytes || pb >= kMaxBytes) return SWIGLU_ERR_UNSUPPORTED;
+  if (overlaps(P8, pb, W8, wb)) return SWIGLU_ERR_INVALID_ARG;
+  swiglu_status_t st = check_device(h);
+  if (st != SWIGLU_OK) return st;
+  (void)hipGetLastError();
+  if (launch_pack_mx_frag((const uint8_t*)W8, (uint8_t*)P8, (int)(2 * N), (int)K, stream,
+                          h->cu_count) != hipSuccess)
+    return SWIGLU_ERR_LAUNCH;
+  return SWIGLU_OK;
 }
 
 swiglu_status_t swiglu_quantize_mx(swiglu_handle_t h, const void* X, void* Q, void* S,

@@ -12,9 +12,10 @@ namespace swiglu {
 // VAR_MX: interleave order on MXFP8 inputs (E4M3 + E8M0 scale per 32 along K)
 // VAR_PACKED: interleave order on W_fused stored in MFMA fragment order
 // VAR_F8_PACKED: interleave order on FP8 inputs with fragment-ordered W8
+// VAR_MX_PACKED: interleave order on MXFP8 inputs, W8 in the 32x32x64 fragment order
 enum Variant {
   VAR_AUTO = 0, VAR_SYNC = 1, VAR_INTERLEAVE = 2, VAR_GEMM = 3, VAR_F8 = 4, VAR_F8_SYNC = 5,
-  VAR_MX = 6, VAR_PACKED = 7, VAR_F8_PACKED = 8
+  VAR_MX = 6, VAR_PACKED = 7, VAR_F8_PACKED = 8, VAR_MX_PACKED = 9
 };
 
 // Fragment-ordered W_fused: slabs of 128 columns times steps of 32 k, 4096
@@ -28,6 +29,11 @@ inline long long packed_elems(long long N, long long K) {
 // steps of 128 k, 2048 bytes per block.
 inline long long f8_packed_bytes(long long N, long long K) {
   return ((2 * N + 15) / 16) * ((K + 127) / 128) * 2048;
+}
+// Fragment-ordered W8 (MXFP8, K % 64 == 0): blocks of 32 rows times steps of
+// 64 k, 2048 bytes per block.
+inline long long mx_packed_bytes(long long N, long long K) {
+  return ((2 * N + 31) / 32) * (K / 64) * 2048;
 }
 
 struct LaunchArgs {
@@ -73,6 +79,9 @@ hipError_t launch_pack_f8(const uint8_t* W1, const uint8_t* W2, uint8_t* W8, int
 // [K, N] -> Wt [2N, K] (k-major pairing)
 hipError_t launch_quantize_mx(const uint16_t* X, uint8_t* Q, uint8_t* S, int rows, int K, int ks,
                               hipStream_t stream, int cu_count);
+// E4M3 W8 [R = 2N, K] -> MX fragment-ordered W8 (mx_packed_bytes(N, K) bytes)
+hipError_t launch_pack_mx_frag(const uint8_t* W8, uint8_t* P, int R, int K, hipStream_t stream,
+                              int cu_count);
 // E4M3 W8 [R = 2N, K] -> fragment-ordered W8 (f8_packed_bytes(N, K) bytes)
 hipError_t launch_pack_f8_frag(const uint8_t* W8, uint8_t* P, int R, int K, hipStream_t stream,
                               int cu_count);

@@ -1682,6 +1682,166 @@ __global__ __launch_bounds__(64 * NW) void f8_packed_kernel(const uint8_t* __res
   }
 }
 
+// MXFP8 streaming on fragment-ordered W8, for M <= 32 per row group: the
+// layout of the 32x32x64 scaled MFMA's sources.  W8 [2N, K] (row 2n Gate, 2n+1
+// Up) is cut into blocks of 32 rows and steps of 64 k; block (rb, t) is 2 KB,
+// stored as two 1 KB halves (the lanes' bytes 0-15, then 16-31):
+//   P8[((rb T + t) 2 + v) 1024 + (i + 32 h) 16 + e] = W8[32 rb + i][64 t + 32 v + 16 h + e]
+// with T = K / 64, v, h < 2, i < 32, e < 16, zeros past 2N.  Half v holds k
+// block 2t + v of every row, so lane i + 32 h passes the scale of its row for
+// block 2t + h (the instruction's convention for both sources), read straight
+// from the E8M0 scale rows SW [2N, ks] and SA [M, ks]: 32 bytes per row cover
+// 16 steps.  One wave per workgroup streams NB row blocks over the whole K
+// (no split, no reduction); the next step's loads are in flight while a step
+// multiplies.  Output: lane l holds A row l % 32 and W8 rows 8 (r/4) +
+// 4 (l/32) + r % 4 of register r, so (Gate, Up) pairs are adjacent registers.
+template <int NB>
+struct MxPacked {
+  static constexpr int kThreads = 64;
+  static constexpr int LDS_BYTES = 0;
+  static constexpr int SLAB_W = 32 * NB;  // W8 rows per workgroup
+  static constexpr int SLAB_Y = 16 * NB;  // output columns per workgroup
+};
+
+template <int NB>
+__global__ __launch_bounds__(64) void mx_packed_kernel(const uint8_t* __restrict__ A,
+                                                       const uint8_t* __restrict__ SA,
+                                                       const uint8_t* __restrict__ P,
+                                                       const uint8_t* __restrict__ SW,
+                                                       uint16_t* __restrict__ Y, int M, int N,
+                                                       int K, int ks) {
+  using C = MxPacked<NB>;
+  const int lane = threadIdx.x;
+  const int unit = xcd_remap(blockIdx.x, gridDim.x);
+  const int m0 = blockIdx.y * 32;
+  const int i32 = lane & 31, h = lane >> 5;
+  const int nsteps = K / 64;              // K % 64 == 0
+  const int nrb = (2 * N + 31) / 32;      // row blocks in P8 (padding included)
+  const int R = 2 * N;
+
+  // this lane's 16 bytes of half 0 of each of the workgroup's row blocks (a
+  // block past the last re-reads it; its outputs are past N), its A row
+  // (rows past M re-read row M-1, never stored), and its scale rows
+  const uint8_t* wp[NB];
+  const uint8_t* swr[NB];
+#pragma unroll
+  for (int b = 0; b < NB; ++b) {
+    const int rb = min(unit * NB + b, nrb - 1);
+    wp[b] = P + (size_t)rb * (size_t)nsteps * 2048 + lane * 16;
+    swr[b] = SW + (size_t)min(32 * rb + i32, R - 1) * ks;
+  }
+  const int arow = min(m0 + i32, M - 1);
+  const uint8_t* ap = A + (size_t)arow * K + 16 * h;
+  const uint8_t* sar = SA + (size_t)arow * ks;
+
+  f32x16 acc[NB];
+#pragma unroll
+  for (int b = 0; b < NB; ++b) acc[b] = f32x16{};
+
+  // scale bytes of 16 steps: row bytes [32 g, 32 g + 32) as two 16-byte
+  // chunks; a chunk at or past ks (its blocks lie past K) re-reads the last
+  // (ks % 16 == 0, ks >= K / 32 >= 2)
+  auto load_scales = [&](const uint8_t* row, int g, u32x4 (&sc)[2]) __attribute__((always_inline)) {
+    sc[0] = load16(row + min(32 * g, ks - 16));
+    sc[1] = load16(row + min(32 * g + 16, ks - 16));
+  };
+  // scale of step j (0..15) of a group for this lane's block 2t + h: byte
+  // 2 (j % 8) + h of chunk j / 8, moved to the low byte
+  auto pick = [&](const u32x4 (&sc)[2], int j) __attribute__((always_inline)) {
+    const uint32_t w = sc[j >> 3][(j & 7) >> 1];
+    return w >> (8 * (2 * (j & 1) + h));
+  };
+  auto load = [&](int t, u32x4 (&wv)[NB][2], u32x4 (&av)[2]) __attribute__((always_inline)) {
+    av[0] = load16(ap + (size_t)t * 64);
+    av[1] = load16(ap + (size_t)t * 64 + 32);
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      const uint8_t* p = wp[b] + (size_t)t * 2048;
+      wv[b][0] = load16_stream(p);
+      wv[b][1] = load16_stream(p + 1024);
+    }
+  };
+
+  // scales of the next group are loaded a group ahead, so no step waits for
+  // them (a group past the end re-reads in-bounds bytes, unused)
+  u32x4 wa[NB][2], aa[2], wb[NB][2], ab[2];
+  u32x4 sw_c[NB][2], sa_c[2], sw_n[NB][2], sa_n[2];
+  if (nsteps > 0) {
+#pragma unroll
+    for (int b = 0; b < NB; ++b) load_scales(swr[b], 0, sw_n[b]);
+    load_scales(sar, 0, sa_n);
+    load(0, wa, aa);
+  }
+  for (int g = 0; g * 16 < nsteps; ++g) {
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      sw_c[b][0] = sw_n[b][0];
+      sw_c[b][1] = sw_n[b][1];
+      load_scales(swr[b], g + 1, sw_n[b]);
+    }
+    sa_c[0] = sa_n[0];
+    sa_c[1] = sa_n[1];
+    load_scales(sar, g + 1, sa_n);
+#pragma unroll
+    for (int j = 0; j < 16; j += 2) {
+      const int t = 16 * g + j;
+      if (t >= nsteps) break;
+      load(min(t + 1, nsteps - 1), wb, ab);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int b = 0; b < NB; ++b)
+        acc[b] = mfma32_f8_scaled<0, 0>(wa[b], aa, acc[b], pick(sw_c[b], j), pick(sa_c, j));
+      if (t + 1 >= nsteps) break;
+      load(min(t + 2, nsteps - 1), wa, aa);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int b = 0; b < NB; ++b)
+        acc[b] = mfma32_f8_scaled<0, 0>(wb[b], ab, acc[b], pick(sw_c[b], j + 1),
+                                        pick(sa_c, j + 1));
+    }
+  }
+
+  // epilogue: registers (4q, 4q+1) and (4q+2, 4q+3) are (Gate, Up) pairs of
+  // W8 rows 8q + 4h + {0,1} and {2,3}: output columns of this lane's A row
+  const int row = m0 + i32;
+  if (row >= M) return;
+#pragma unroll
+  for (int b = 0; b < NB; ++b) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int col = unit * C::SLAB_Y + 16 * b + 4 * q + 2 * h;  // (W8 row) / 2
+      if (col < N) {
+        const float y0 = silu(acc[b][4 * q]) * acc[b][4 * q + 1];
+        const float y1 = silu(acc[b][4 * q + 2]) * acc[b][4 * q + 3];
+        *reinterpret_cast<uint32_t*>(Y + (size_t)row * N + col) = pack_bf16x2(y0, y1);
+      }
+    }
+  }
+}
+
+// Fragment-ordered W8 for the MXFP8 streaming kernel from W8 [R = 2N, K]
+// (layout in front of mx_packed_kernel): a thread copies one 16-byte chunk,
+// row 32 rb + i, bytes [64 t + 32 v + 16 h, +16), zeros past R.  Once per
+// weight set.
+__global__ __launch_bounds__(256) void pack_mx_frag_kernel(const uint8_t* __restrict__ W8,
+                                                           uint8_t* __restrict__ P, int R, int K,
+                                                           size_t nchunks) {
+  const int nsteps = K / 64;
+  for (size_t c = (size_t)blockIdx.x * blockDim.x + threadIdx.x; c < nchunks;
+       c += (size_t)gridDim.x * blockDim.x) {
+    const int lane = (int)(c & 63);
+    const int v = (int)((c >> 6) & 1);
+    const size_t bt = c >> 7;  // rb * nsteps + t
+    const int t = (int)(bt % (size_t)nsteps);
+    const long long rb = (long long)(bt / (size_t)nsteps);
+    const long long r = 32 * rb + (lane & 31);
+    const int k0 = 64 * t + 32 * v + 16 * (lane >> 5);
+    u32x4 x{0, 0, 0, 0};
+    if (r < R) x = load16(W8 + (size_t)r * (size_t)K + k0);  // K % 64 == 0
+    *reinterpret_cast<u32x4*>(P + c * 16) = x;
+  }
+}
+
 // Fragment-ordered W8 from W8 [R = 2N, K] (layout in front of
 // f8_packed_kernel): a thread copies one 16-byte chunk, row 16 rb + i, bytes
 // [128 t + 64 h + 16 g, +16), zeros past R and K.  Once per weight set.
@@ -2051,6 +2211,21 @@ static hipError_t launch_f8_packed(const LaunchArgs& a) {
 #define F8_PACKED(mt, nb, nw)                                                              \
   {VAR_F8_PACKED, 1, (mt) * 16, F8Packed<mt, nb, nw>::SLAB_Y, 128, nw, nw,                  \
    F8Packed<mt, nb, nw>::LDS_BYTES, &launch_f8_packed<mt, nb, nw>}
+template <int NB>
+static hipError_t launch_mx_packed(const LaunchArgs& a) {
+  using C = MxPacked<NB>;
+  const long long nunit = (2LL * a.N + C::SLAB_W - 1) / C::SLAB_W;
+  const long long nmb = (a.M + 31) / 32;
+  if (nunit <= 0 || nmb <= 0) return hipSuccess;
+  if (nunit > 0x7fffffffLL || nmb > 65535) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((mx_packed_kernel<NB>), dim3((unsigned)nunit, (unsigned)nmb), dim3(64), 0,
+                     a.stream, (const uint8_t*)a.A, a.SA, (const uint8_t*)a.W1, a.SW, a.Y, a.M,
+                     a.N, a.K, a.ks);
+  return hipGetLastError();
+}
+
+#define MX_PACKED(nb)                                                                      \
+  {VAR_MX_PACKED, 1, 32, MxPacked<nb>::SLAB_Y, 64, 1, 1, 0, &launch_mx_packed<nb>}
 #define F8_SKINNY(mt, nb, nw)                                                              \
   {VAR_F8, 1, (mt) * 16, F8Skinny<mt, nb, nw>::SLAB_Y, 128, nw, nw,                         \
    F8Skinny<mt, nb, nw>::LDS_BYTES, &launch_f8_skinny<mt, nb, nw>}
@@ -2172,6 +2347,10 @@ static const KernelConfig kConfigs[] = {
     F8_PACKED(1, 4, 2),                                             // 74
     F8_PACKED(2, 2, 1),                                             // 75
     F8_PACKED(4, 2, 1),                                             // 76
+    // ---- MXFP8 on fragment-ordered W8 (streaming, 32x32x64 scaled MFMA) -----
+    MX_PACKED(1),                                                   // 77
+    MX_PACKED(2),                                                   // 78
+    MX_PACKED(4),                                                   // 79
 };
 
 int config_count() { return (int)(sizeof(kConfigs) / sizeof(kConfigs[0])); }
@@ -2235,6 +2414,18 @@ hipError_t launch_pack_f8(const uint8_t* W1, const uint8_t* W2, uint8_t* W8, int
   if (blocks > cap) blocks = cap;
   hipLaunchKernelGGL(pack_f8_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, W1, W2, W8, N,
                      K);
+  return hipGetLastError();
+}
+
+hipError_t launch_pack_mx_frag(const uint8_t* W8, uint8_t* P, int R, int K, hipStream_t stream,
+                              int cu_count) {
+  const size_t nchunks = (size_t)((R + 31) / 32) * (size_t)(K / 64) * 128;
+  if (nchunks == 0) return hipSuccess;
+  size_t blocks = (nchunks + 255) / 256;
+  const size_t cap = (size_t)(cu_count > 0 ? cu_count : 256) * 8;
+  if (blocks > cap) blocks = cap;
+  hipLaunchKernelGGL(pack_mx_frag_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, W8, P, R,
+                     K, nchunks);
   return hipGetLastError();
 }
 

@@ -25,10 +25,12 @@ import gemm_epilogues_mlp_amd as sw
 
 VARIANTS = {"interleave": sw.VARIANT_INTERLEAVE, "sync": sw.VARIANT_SYNC, "gemm": sw.VARIANT_GEMM,
             "fp8": sw.VARIANT_FP8, "fp8-sync": sw.VARIANT_FP8_SYNC, "mxfp8": sw.VARIANT_MXFP8,
-            "packed": sw.VARIANT_PACKED, "fp8-packed": sw.VARIANT_FP8_PACKED}
+            "packed": sw.VARIANT_PACKED, "fp8-packed": sw.VARIANT_FP8_PACKED,
+            "mxfp8-packed": sw.VARIANT_MXFP8_PACKED}
 # the forward's variant argument for each FP8 configuration family
 _FP8_ORDER = {sw.VARIANT_FP8: sw.VARIANT_INTERLEAVE, sw.VARIANT_FP8_SYNC: sw.VARIANT_SYNC,
-              sw.VARIANT_MXFP8: sw.VARIANT_MXFP8, sw.VARIANT_FP8_PACKED: sw.VARIANT_FP8_PACKED}
+              sw.VARIANT_MXFP8: sw.VARIANT_MXFP8, sw.VARIANT_FP8_PACKED: sw.VARIANT_FP8_PACKED,
+              sw.VARIANT_MXFP8_PACKED: sw.VARIANT_MXFP8_PACKED}
 
 
 def _candidates(variant, M, configs=None):
@@ -70,8 +72,9 @@ def _time_configs(h, variant, M, N, K, ids, reps, rotate_bytes, seed=0):
             codes = lambda shape: torch.randint(0, 0x7E, shape, device=dev, generator=g,
                                                 dtype=torch.uint8)
             y = torch.empty((M, N), dtype=torch.int16, device=dev)
-            wshape = (sw.swiglu_fp8_packed_bytes(N, K),) if variant == sw.VARIANT_FP8_PACKED \
-                else (2 * N, K)
+            wshape = {sw.VARIANT_FP8_PACKED: (sw.swiglu_fp8_packed_bytes(N, K),),
+                      sw.VARIANT_MXFP8_PACKED: (sw.swiglu_mx_packed_bytes(N, K),)}.get(
+                          variant, (2 * N, K))
             sets.append((codes((M, K)), codes(wshape),
                          torch.full((M, ks), 120, dtype=torch.uint8, device=dev),
                          torch.full((2 * N, ks), 120, dtype=torch.uint8, device=dev), y, None))
@@ -96,6 +99,8 @@ def _time_configs(h, variant, M, N, K, ids, reps, rotate_bytes, seed=0):
             a8, w8, sa, sw8, y, _ = sets[i % nsets]
             if variant == sw.VARIANT_MXFP8:
                 sw.swiglu_forward_mx(h, a8, sa, w8, sw8, y, M, N, K, ks, cid, stream)
+            elif variant == sw.VARIANT_MXFP8_PACKED:
+                sw.swiglu_forward_mx_packed(h, a8, sa, w8, sw8, y, M, N, K, ks, cid, stream)
             else:
                 sw.swiglu_forward_fp8(h, a8, w8, y, M, N, K, config_id=cid, stream=stream,
                                       variant=_FP8_ORDER[variant])

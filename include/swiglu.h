@@ -92,8 +92,11 @@ typedef enum {
                                     (swiglu_forward_mx; swiglu_query_fp8)      */
   SWIGLU_VARIANT_PACKED = 7,     /* Kernel-2 order on fragment-ordered W_fused
                                     (PACKED layout)                            */
-  SWIGLU_VARIANT_FP8_PACKED = 8  /* Kernel-2 order on FP8 inputs with
+  SWIGLU_VARIANT_FP8_PACKED = 8, /* Kernel-2 order on FP8 inputs with
                                     fragment-ordered W8 (swiglu_forward_fp8)   */
+  SWIGLU_VARIANT_MXFP8_PACKED = 9 /* Kernel-2 order on MXFP8 inputs with
+                                    fragment-ordered W8 (swiglu_forward_mx_packed;
+                                    swiglu_query_fp8)                          */
 } swiglu_variant_t;
 
 /* Description of one compiled kernel configuration. */
@@ -208,7 +211,7 @@ swiglu_status_t swiglu_query_unfused(swiglu_handle_t h, int64_t M, int64_t N,
 /* Tuned per-shape configurations.  A tuned file (written by the package's
  * tuner, python -m gemm_epilogues_mlp_amd.tune) is text:
  *   swiglu-tuned <signature: 16 hex digits> <arch>        first non-comment line
- *   <variant 1..8> <M> <N> <K> <config id> [ignored provenance]    one per shape
+ *   <variant 1..9> <M> <N> <K> <config id> [ignored provenance]    one per shape
  * with '#' comment lines.  The signature (swiglu_config_signature) identifies
  * the list of compiled configurations; a file written for a library with a
  * different list is refused, so an id can never name the wrong kernel.
@@ -326,6 +329,32 @@ swiglu_status_t swiglu_forward_mx(swiglu_handle_t h, const void* A8, const void*
 swiglu_status_t swiglu_quantize_mx(swiglu_handle_t h, const void* X, void* Q, void* S,
                                    int64_t rows, int64_t K, int64_t ks, hipStream_t stream);
 
+/* The MXFP8 forward of swiglu_forward_mx with W8 passed in the fragment order
+ * of a streaming kernel made for decode-sized batches (any M; the weights are
+ * read once per 32 rows of A).  The order is that of the 32x32x64 scaled MFMA's
+ * sources: W8 cut into blocks of 32 rows and steps of 64 k (K % 64 == 0), each
+ * 2048-byte block stored as two 1 KB halves, with T = K / 64:
+ *   P8[((rb*T + t)*2 + v)*1024 + (i + 32*h)*16 + e] = W8[32*rb + i][64*t + 32*v + 16*h + e]
+ * for rb < ceil(2N / 32), v < 2, h < 2, i < 32, e < 16, and 0 for rows >= 2N.
+ * SA, SW and ks are those of swiglu_forward_mx (the scales are not reordered).
+ * config_id < 0 uses the table; a given id must be of variant MXFP8_PACKED.
+ * Errors and other conventions as swiglu_forward_mx. */
+swiglu_status_t swiglu_forward_mx_packed(swiglu_handle_t h, const void* A8, const void* SA,
+                                         const void* P8, const void* SW, void* Y, int64_t M,
+                                         int64_t N, int64_t K, int64_t ks, int32_t config_id,
+                                         hipStream_t stream);
+
+/* Bytes of that P8: ceil(2N / 32) * (K / 64) * 2048 (0 when N <= 0, K <= 0,
+ * K % 64 != 0 or a size is out of range). */
+int64_t swiglu_mx_packed_bytes(int64_t N, int64_t K);
+
+/* P8 (swiglu_mx_packed_bytes(N, K) bytes) from E4M3 W8 [2N, K], a byte copy
+ * done once per weight set.  N % 8 == 0, K % 64 == 0, 16-byte aligned
+ * pointers and tensors under 2 GiB (else UNSUPPORTED); P8 must not overlap
+ * W8 (INVALID_ARG).  K == 0 or N == 0 is a no-op. */
+swiglu_status_t swiglu_pack_mx_fragments(swiglu_handle_t h, const void* W8, void* P8, int64_t K,
+                                         int64_t N, hipStream_t stream);
+
 /* bf16 Wt [2N, K] from W1, W2 [K, N]: Wt[2n, k] = W1[k, n], Wt[2n+1, k] =
  * W2[k, n] (the k-major pairing, a bit copy), the input of swiglu_quantize_mx
  * for the weights.  K % 8 == 0, N % 8 == 0; Wt must not overlap W1 or W2. */
@@ -333,8 +362,8 @@ swiglu_status_t swiglu_pack_kmajor(swiglu_handle_t h, const void* W1, const void
                                    int64_t K, int64_t N, hipStream_t stream);
 
 /* The configuration swiglu_forward_fp8 (variant AUTO, INTERLEAVE, SYNC or
- * FP8_PACKED) or swiglu_forward_mx (variant MXFP8) with config_id < 0 runs for
- * a shape. */
+ * FP8_PACKED), swiglu_forward_mx (variant MXFP8) or swiglu_forward_mx_packed
+ * (variant MXFP8_PACKED) with config_id < 0 runs for a shape. */
 swiglu_status_t swiglu_query_fp8(swiglu_handle_t h, int64_t M, int64_t N, int64_t K,
                                  swiglu_variant_t variant, swiglu_tile_t* tile);
 

@@ -80,8 +80,10 @@ def _load():
     lib.oracle_pack_kmajor_bf16.argtypes = [p, p, p, i64, i64]
     lib.oracle_pack_fragments.argtypes = [p, p, p, i64, i64]
     lib.oracle_pack_fp8_fragments.argtypes = [p, p, i64, i64]
+    lib.oracle_pack_mx_fragments.argtypes = [p, p, i64, i64]
     for fn in (lib.oracle_quantize_mx, lib.oracle_decode_mx, lib.oracle_pack_kmajor_bf16,
-               lib.oracle_pack_fragments, lib.oracle_pack_fp8_fragments):
+               lib.oracle_pack_fragments, lib.oracle_pack_fp8_fragments,
+               lib.oracle_pack_mx_fragments):
         fn.restype = None
     lib.oracle_swiglu_mx_rows.argtypes = [p, p, p, p, i64, i64, i64, i64, p, i64, p, p, p,
                                           c_int]
@@ -387,6 +389,25 @@ def pack_fp8_fragments(w8):
     R, K = w8.shape
     out = np.empty(((R + 15) // 16) * ((K + 127) // 128) * 2048, np.uint8)
     _load().oracle_pack_fp8_fragments(_ptr(w8), _ptr(out), R, K)
+    return out
+
+
+def mx_packed_size(N: int, K: int) -> int:
+    """Bytes of the MX fragment-ordered W8 (K % 64 == 0): ceil(2N/32) * (K/64) * 2048."""
+    return ((2 * N + 31) // 32) * (K // 64) * 2048
+
+
+def pack_mx_fragments(w8):
+    """MX fragment-ordered W8 (flat bytes, mx_packed_size(N, K)) from W8 [2N, K]
+    with K % 64 == 0: byte W8[r, k] at ((rb*T + t)*2 + v)*1024 + (i + 32h)*16 + e
+    (rb = r // 32, i = r % 32, t = k // 64, v = k % 64 // 32, h = k % 32 // 16,
+    e = k % 16, T = K/64), zeros elsewhere."""
+    w8 = _u8(w8, "W8")
+    R, K = w8.shape
+    if K % 64:
+        raise ValueError("K must be a multiple of 64")
+    out = np.empty(((R + 31) // 32) * (K // 64) * 2048, np.uint8)
+    _load().oracle_pack_mx_fragments(_ptr(w8), _ptr(out), R, K)
     return out
 
 

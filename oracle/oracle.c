@@ -568,6 +568,23 @@ void oracle_pack_fp8_fragments(const uint8_t* w8, uint8_t* p, int64_t R, int64_t
     }
 }
 
+/* Fragment-ordered W8 for the library's MXFP8 streaming kernel (K a multiple
+ * of 64): every byte W8[r][k] of W8 [R, K] is placed at
+ *   ((rb*T + t)*2 + v)*1024 + (i + 32*h)*16 + e
+ * with rb = r / 32, i = r % 32, t = k / 64, v = (k % 64) / 32,
+ * h = (k % 32) / 16, e = k % 16 and T = K / 64; every other position of the
+ * ceil(R / 32) * T * 2048 bytes is 0.  A byte copy. */
+void oracle_pack_mx_fragments(const uint8_t* w8, uint8_t* p, int64_t R, int64_t K) {
+  const int64_t RB = (R + 31) / 32, T = K / 64;
+  memset(p, 0, (size_t)(RB * T * 2048));
+  for (int64_t r = 0; r < R; ++r)
+    for (int64_t k = 0; k < T * 64; ++k) {
+      const int64_t rb = r / 32, i = r % 32;
+      const int64_t t = k / 64, v = (k % 64) / 32, h = (k % 32) / 16, e = k % 16;
+      p[((rb * T + t) * 2 + v) * 1024 + (i + 32 * h) * 16 + e] = w8[r * K + k];
+    }
+}
+
 /* bf16 W1, W2 [K, N] -> Wt [2N, K] bf16: row 2n = W1[:, n], row 2n+1 = W2[:, n]
  * (the Kernel-2 pairing with k contiguous), a bit copy. */
 void oracle_pack_kmajor_bf16(const uint16_t* w1, const uint16_t* w2, uint16_t* wt, int64_t K,

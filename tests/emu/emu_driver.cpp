@@ -111,15 +111,16 @@ bool run_config(int id, int M, int N, int K) {
     a.ldw = N;
   }
   if (c->variant == VAR_F8 || c->variant == VAR_F8_SYNC || c->variant == VAR_MX ||
-      c->variant == VAR_F8_PACKED) {
+      c->variant == VAR_F8_PACKED || c->variant == VAR_MX_PACKED) {
     // byte tensors: A8 [M, K], W8 [2N, K] (or its fragment order P8); MX
     // scales SA [M, ks], SW [2N, ks]
     a.A = alloc16(((size_t)M * K + 1) / 2, "A8");
-    a.W1 = c->variant == VAR_F8_PACKED ? alloc16((size_t)f8_packed_bytes(N, K) / 2, "P8")
-                                       : alloc16((size_t)N * K, "W8");
+    a.W1 = c->variant == VAR_F8_PACKED   ? alloc16((size_t)f8_packed_bytes(N, K) / 2, "P8")
+           : c->variant == VAR_MX_PACKED ? alloc16((size_t)mx_packed_bytes(N, K) / 2, "P8mx")
+                                         : alloc16((size_t)N * K, "W8");
     a.ldw = K;
     a.scale_g = a.scale_u = 1.0f;
-    if (c->variant == VAR_MX) {
+    if (c->variant == VAR_MX || c->variant == VAR_MX_PACKED) {
       a.ks = (K / 32 + 15) / 16 * 16;
       a.SA = (const uint8_t*)alloc16(((size_t)M * a.ks + 1) / 2, "SA");
       a.SW = (const uint8_t*)alloc16((size_t)N * a.ks, "SW");
@@ -168,6 +169,15 @@ bool run_elementwise(size_t n) {
       uint8_t* w8s = (uint8_t*)alloc16((size_t)Rp8 * Kp8 / 2, "W8s");
       uint8_t* p8 = (uint8_t*)alloc16((size_t)f8_packed_bytes(Rp8 / 2, Kp8) / 2, "P8s");
       launch_pack_f8_frag(w8s, p8, Rp8, Kp8, nullptr, 256);
+      free_all();
+    }
+    // MX fragment order from W8 [R, 128] (R = n / 128 rounded down to a
+    // multiple of 8: a partial block of 32 rows)
+    const int Kmx = 128, Rmx = (int)(n / 128) / 8 * 8;
+    if (Rmx > 0) {
+      uint8_t* w8m = (uint8_t*)alloc16((size_t)Rmx * Kmx / 2, "W8m");
+      uint8_t* pm = (uint8_t*)alloc16((size_t)mx_packed_bytes(Rmx / 2, Kmx) / 2, "P8m");
+      launch_pack_mx_frag(w8m, pm, Rmx, Kmx, nullptr, 256);
       free_all();
     }
   }
@@ -230,7 +240,7 @@ int main(int argc, char** argv) {
     if (one_shape) {
       run_config(id, shape[0], shape[1], shape[2]);
     } else {
-      if (config_at(id) && config_at(id)->variant == VAR_MX)
+      if (config_at(id) && (config_at(id)->variant == VAR_MX || config_at(id)->variant == VAR_MX_PACKED))
         for (const auto& s : shapes_mx) run_config(id, s[0], s[1], s[2]);
       else if (config_at(id) && (config_at(id)->variant == VAR_F8 || config_at(id)->variant == VAR_F8_SYNC ||
                                  config_at(id)->variant == VAR_F8_PACKED))

@@ -74,6 +74,11 @@ def test_null_handle_and_bad_arguments_rejected():
     assert lib.swiglu_packed_bytes(72, 40) == 2 * 2 * 2 * 4096
     assert lib.swiglu_pack_fp8_fragments(None, 16, 16, 16, 8, None) == sw.ERR_INVALID_ARG
     assert lib.swiglu_fp8_packed_bytes(12, 144) == 2 * 2 * 2048
+    assert lib.swiglu_pack_mx_fragments(None, 16, 16, 64, 8, None) == sw.ERR_INVALID_ARG
+    assert lib.swiglu_forward_mx_packed(None, 16, 16, 16, 16, 16, 8, 8, 64, 16, -1, None) == \
+        sw.ERR_INVALID_ARG
+    assert lib.swiglu_mx_packed_bytes(20, 128) == 2 * 2 * 2048
+    assert lib.swiglu_mx_packed_bytes(20, 100) == 0
 
 
 def test_status_strings_and_workspace_size():
@@ -88,7 +93,7 @@ def test_config_list_is_consistent():
     assert n > 0
     seen = {sw.VARIANT_SYNC: 0, sw.VARIANT_INTERLEAVE: 0, sw.VARIANT_GEMM: 0, sw.VARIANT_FP8: 0,
             sw.VARIANT_FP8_SYNC: 0, sw.VARIANT_MXFP8: 0, sw.VARIANT_PACKED: 0,
-            sw.VARIANT_FP8_PACKED: 0}
+            sw.VARIANT_FP8_PACKED: 0, sw.VARIANT_MXFP8_PACKED: 0}
     for i in range(n):
         c = sw.swiglu_config_info(i)
         assert c["id"] == i
@@ -98,13 +103,15 @@ def test_config_list_is_consistent():
         assert c["tail_split"] in (0, 4)
         if c["tail_split"]:
             assert c["family"] == 0 and c["bm"] % 64 == 0 and c["bn"] % 64 == 0
-        assert 0 < c["lds_bytes"] <= 160 * 1024
+        # the MX streaming kernel uses no LDS (one wave, no reduction)
+        assert 0 < c["lds_bytes"] <= 160 * 1024 or (c["variant"] == sw.VARIANT_MXFP8_PACKED
+                                                   and c["lds_bytes"] == 0)
         assert c["waves"] * 64 <= 1024
         if c["family"] in (0, 2):
             assert c["bm"] % 32 == 0 and c["bn"] % 32 == 0
         if c["variant"] in (sw.VARIANT_FP8, sw.VARIANT_FP8_SYNC, sw.VARIANT_MXFP8,
-                            sw.VARIANT_FP8_PACKED):
-            assert (c["family"], c["bk"]) in ((0, 64), (1, 128))
+                            sw.VARIANT_FP8_PACKED, sw.VARIANT_MXFP8_PACKED):
+            assert (c["family"], c["bk"]) in ((0, 64), (1, 128), (1, 64))
         if c["variant"] == sw.VARIANT_PACKED:  # streaming, 64 outputs per slab
             assert c["family"] == 1 and c["bn"] in (16, 32, 64) and c["bk"] == 32
     assert all(v > 0 for v in seen.values())

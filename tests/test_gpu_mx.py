@@ -232,3 +232,105 @@ def test_mx_workload_device_pipeline_matches(handle, workload):
     assert np.array_equal(host(wt), d["wt"])
     assert np.array_equal(q.cpu().numpy(), d["q"][2]) and np.array_equal(s.cpu().numpy(), d["q"][3])
     assert np.array_equal(qa.cpu().numpy(), d["q"][0]) and np.array_equal(sa.cpu().numpy(), d["q"][1])
+
+
+# --------------------------------------------------------------------------- fragment order
+def mx_packed_configs():
+    return [i for i in range(sw.swiglu_config_count())
+            if sw.swiglu_config_info(i)["variant"] == sw.VARIANT_MXFP8_PACKED]
+
+
+def forward_packed(handle, qa, sa, p8, sw_, M, N, K, cfg=-1):
+    t = torch()
+    y = empty_poisoned((M, N))
+    sw.swiglu_forward_mx_packed(handle, dev(qa), dev(sa), dev(p8), dev(sw_), y, M, N, K,
+                                sa.shape[1], config_id=cfg)
+    t.cuda.synchronize()
+    return host(y)
+
+
+# the tile shapes plus a row count past 32, many 16-step scale groups and a
+# partial one, and the 0.5B shape at a decode-sized M
+PACKED_SHAPES = SHAPES + [(33, 72, 1088), (16, 4864, 896)]
+
+
+@pytest.fixture(scope="module")
+def packed_cases():
+    out = {}
+    for i, (M, N, K) in enumerate(PACKED_SHAPES):
+        a, w1, w2 = I.make_inputs(M, K, N, 60 + i)
+        qa, sa, qw, sw_, _ = mx_inputs(a, w1, w2)
+        out[(M, N, K)] = dict(qa=qa, sa=sa, qw=qw, sw=sw_, p8=oracle.pack_mx_fragments(qw),
+                              y=oracle.swiglu_mx_rows(qa, sa, qw, sw_))
+    return out
+
+
+@pytest.mark.parametrize("shape", PACKED_SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_mx_fragment_pack_bitwise(handle, packed_cases, shape):
+    t = torch()
+    M, N, K = shape
+    c = packed_cases[shape]
+    p8 = t.full((sw.swiglu_mx_packed_bytes(N, K),), 0x55, dtype=t.uint8, device="cuda")
+    sw.swiglu_pack_mx_fragments(handle, dev(c["qw"]), p8, K, N)
+    t.cuda.synchronize()
+    assert np.array_equal(p8.cpu().numpy(), c["p8"])
+
+
+@pytest.mark.parametrize("shape", PACKED_SHAPES, ids=lambda s: "x".join(map(str, s)))
+@pytest.mark.parametrize("cfg", mx_packed_configs())
+def test_mx_packed_config_parity(handle, packed_cases, cfg, shape):
+    M, N, K = shape
+    c = packed_cases[shape]
+    log(f"mx packed config {cfg} {sw.swiglu_config_info(cfg)} shape {shape}")
+    y = forward_packed(handle, c["qa"], c["sa"], c["p8"], c["sw"], M, N, K, cfg)
+    assert_parity(y, c["y"], f"mx packed cfg {cfg} {shape}")
+
+
+def test_mx_packed_block_scales_matter(handle):
+    """Changing one Up block scale of one column changes exactly that column."""
+    M, N, K = 16, 128, 256
+    a, w1, w2 = I.make_inputs(M, K, N, 89)
+    qa, sa, qw, sw_, _ = mx_inputs(a, w1, w2)
+    p8 = oracle.pack_mx_fragments(qw)
+    sw2 = sw_.copy()
+    sw2[2 * 5 + 1, 3] += 2
+    y0 = forward_packed(handle, qa, sa, p8, sw_, M, N, K)
+    y1 = forward_packed(handle, qa, sa, p8, sw2, M, N, K)
+    assert_parity(y1, oracle.swiglu_mx_rows(qa, sa, qw, sw2), "mx packed modified scale")
+    changed = np.any(y0 != y1, axis=0)
+    assert changed[5] and not np.any(np.delete(changed, 5))
+
+
+def test_mx_packed_k_zero_and_errors(handle):
+    t = torch()
+    M, N = 40, 72
+    y = t.full((M, N), -1, dtype=t.int16, device="cuda")
+    sw.swiglu_forward_mx_packed(handle, 0, 0, 0, 0, y, M, N, 0, 0)
+    t.cuda.synchronize()
+    assert np.all(decode(host(y)) == 0.0)
+    a = t.zeros((M, 128), dtype=t.uint8, device="cuda")
+    s = t.zeros((M, 16), dtype=t.uint8, device="cuda")
+    p = t.zeros((sw.swiglu_mx_packed_bytes(N, 128),), dtype=t.uint8, device="cuda")
+    ws = t.zeros((2 * N, 16), dtype=t.uint8, device="cuda")
+    with pytest.raises(sw.SwiGLUError) as e:               # a k-major MX config on P8
+        sw.swiglu_forward_mx_packed(handle, a, s, p, ws, y, M, N, 128, 16,
+                                    config_id=mx_configs()[0])
+    assert e.value.status == sw.ERR_INVALID_ARG
+    with pytest.raises(sw.SwiGLUError) as e:               # K % 64
+        sw.swiglu_pack_mx_fragments(handle, a, p, 96, N)
+    assert e.value.status == sw.ERR_UNSUPPORTED
+    with pytest.raises(sw.SwiGLUError) as e:               # P8 overlaps W8
+        sw.swiglu_pack_mx_fragments(handle, p, p, 128, N)
+    assert e.value.status == sw.ERR_INVALID_ARG
+
+
+def test_mx_packed_workload_parity(handle, workload):
+    d = workload
+    w = d["w"]
+    qa, sa, qw, sw_ = d["q"]
+    cfg = sw.swiglu_query_fp8(handle, w.M, w.N, w.K, sw.VARIANT_MXFP8_PACKED)
+    log(f"mx packed {w.name}: config {cfg['id']}")
+    p8 = oracle.pack_mx_fragments(qw)
+    y = forward_packed(handle, qa, sa, p8, sw_, w.M, w.N, w.K)
+    assert np.all(np.isfinite(decode(y))), "unwritten or non-finite outputs"
+    assert_parity(y[d["rows"]], d["y_ref"], f"mx packed {w.name} sampled rows")

@@ -143,3 +143,56 @@ def test_fp8_matches_axis_algebra(N, K):
     pad[:2 * N, :K] = w8
     ref = pad.reshape(RB, 16, T, 2, 4, 16).transpose(0, 2, 3, 4, 1, 5).reshape(-1)
     assert np.array_equal(oracle.pack_fp8_fragments(w8), ref)
+
+
+# ---- MXFP8: W8 in the 32x32x64 fragment order ------------------------------------
+#   P8[((rb T + t) 2 + v) 1024 + (i + 32 h) 16 + e] = W8[32 rb + i][64 t + 32 v + 16 h + e]
+
+
+def test_mx_hand_derived_positions():
+    path = os.path.join(os.path.dirname(__file__), "golden", "mx_fragment_layout.txt")
+    entries, shape = [], None
+    for line in open(path):
+        line = line.split("#")[0].strip()
+        if not line:
+            continue
+        if line.startswith("shape"):
+            shape = tuple(int(x) for x in line.split()[1:])
+            continue
+        i, v = line.split()
+        entries.append((int(i), int(v)))
+    N, K = shape
+    r = np.arange(2 * N, dtype=np.int64)[:, None]
+    k = np.arange(K, dtype=np.int64)[None, :]
+    w8 = ((128 * r + k) % 251 + 1).astype(np.uint8)
+    p = oracle.pack_mx_fragments(w8)
+    assert p.size == 8192 == oracle.mx_packed_size(N, K)
+    for i, v in entries:
+        assert int(p[i]) == v, f"P8[{i}] = {int(p[i])}, hand derivation says {v}"
+
+
+@pytest.mark.parametrize("N,K", [(20, 128), (8, 64), (64, 256), (36, 448), (100, 64)])
+def test_mx_every_byte_once_zeros_elsewhere(N, K):
+    R = 2 * N
+    tag = np.arange(1, R * K + 1, dtype=np.int64).reshape(R, K)
+    assert tag.max() < 65536
+    lo, hi = (tag & 0xFF).astype(np.uint8), (tag >> 8).astype(np.uint8)
+    got = oracle.pack_mx_fragments(lo).astype(np.int64) | \
+        (oracle.pack_mx_fragments(hi).astype(np.int64) << 8)
+    assert got.size == ((R + 31) // 32) * (K // 64) * 2048
+    nz = got[got != 0]
+    assert nz.size == R * K
+    assert np.array_equal(np.sort(nz), tag.reshape(-1))
+
+
+@pytest.mark.parametrize("N,K", [(20, 128), (8, 64), (64, 256), (36, 448), (9472, 3584)])
+def test_mx_matches_axis_algebra(N, K):
+    """Pad W8 to [32 RB, K], split the row as (rb, i) and k as (t, v, h, e),
+    and order the axes (rb, t, v, h, i, e)."""
+    rng = np.random.default_rng(N * 7 + K)
+    w8 = rng.integers(0, 256, (2 * N, K), dtype=np.uint8)
+    RB, T = (2 * N + 31) // 32, K // 64
+    pad = np.zeros((32 * RB, K), np.uint8)
+    pad[:2 * N] = w8
+    ref = pad.reshape(RB, 32, T, 2, 2, 16).transpose(0, 2, 3, 4, 1, 5).reshape(-1)
+    assert np.array_equal(oracle.pack_mx_fragments(w8), ref)
