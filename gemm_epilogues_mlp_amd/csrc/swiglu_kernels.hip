@@ -1691,33 +1691,42 @@ __global__ __launch_bounds__(64 * NW) void f8_packed_kernel(const uint8_t* __res
 // block 2t + v of every row, so lane i + 32 h passes the scale of its row for
 // block 2t + h (the instruction's convention for both sources), read straight
 // from the E8M0 scale rows SW [2N, ks] and SA [M, ks]: 32 bytes per row cover
-// 16 steps.  One wave per workgroup streams NB row blocks over the whole K
-// (no split, no reduction); the next step's loads are in flight while a step
-// multiplies.  Output: lane l holds A row l % 32 and W8 rows 8 (r/4) +
-// 4 (l/32) + r % 4 of register r, so (Gate, Up) pairs are adjacent registers.
-template <int NB>
+// 16 steps.  NW waves per workgroup stream NB row blocks; each wave takes a
+// contiguous range of whole 16-step groups (NW = 1: all of K, no reduction;
+// NW > 1 for narrow N, the fp32 partials then added through LDS in wave order
+// before SiLU); the next step's loads are in flight while a step multiplies.
+// Output: lane l holds A row l % 32 and W8 rows 8 (r/4) + 4 (l/32) + r % 4
+// of register r, so (Gate, Up) pairs are adjacent registers.
+template <int NB, int NW>
 struct MxPacked {
-  static constexpr int kThreads = 64;
-  static constexpr int LDS_BYTES = 0;
+  static constexpr int kThreads = 64 * NW;
+  static constexpr int LDS_BYTES = NW > 1 ? NW * NB * 16 * 64 * 4 : 0;
+  static_assert(LDS_BYTES <= 160 * 1024, "LDS");
   static constexpr int SLAB_W = 32 * NB;  // W8 rows per workgroup
   static constexpr int SLAB_Y = 16 * NB;  // output columns per workgroup
 };
 
-template <int NB>
-__global__ __launch_bounds__(64) void mx_packed_kernel(const uint8_t* __restrict__ A,
-                                                       const uint8_t* __restrict__ SA,
-                                                       const uint8_t* __restrict__ P,
-                                                       const uint8_t* __restrict__ SW,
-                                                       uint16_t* __restrict__ Y, int M, int N,
-                                                       int K, int ks) {
-  using C = MxPacked<NB>;
-  const int lane = threadIdx.x;
+template <int NB, int NW>
+__global__ __launch_bounds__(64 * NW) void mx_packed_kernel(const uint8_t* __restrict__ A,
+                                                            const uint8_t* __restrict__ SA,
+                                                            const uint8_t* __restrict__ P,
+                                                            const uint8_t* __restrict__ SW,
+                                                            uint16_t* __restrict__ Y, int M,
+                                                            int N, int K, int ks) {
+  using C = MxPacked<NB, NW>;
+  __shared__ __attribute__((aligned(16))) float red[NW > 1 ? NW * NB * 16 * 64 : 1];
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
   const int unit = xcd_remap(blockIdx.x, gridDim.x);
   const int m0 = blockIdx.y * 32;
   const int i32 = lane & 31, h = lane >> 5;
   const int nsteps = K / 64;              // K % 64 == 0
   const int nrb = (2 * N + 31) / 32;      // row blocks in P8 (padding included)
   const int R = 2 * N;
+  // this wave's groups of 16 steps: [g0, g1), steps [16 g0, s1)
+  const int ngroups = (nsteps + 15) / 16;
+  const int g0 = wave * ngroups / NW, g1 = (wave + 1) * ngroups / NW;
+  const int s1 = min(16 * g1, nsteps);
 
   // this lane's 16 bytes of half 0 of each of the workgroup's row blocks (a
   // block past the last re-reads it; its outputs are past N), its A row
@@ -1766,13 +1775,13 @@ __global__ __launch_bounds__(64) void mx_packed_kernel(const uint8_t* __restrict
   // them (a group past the end re-reads in-bounds bytes, unused)
   u32x4 wa[NB][2], aa[2], wb[NB][2], ab[2];
   u32x4 sw_c[NB][2], sa_c[2], sw_n[NB][2], sa_n[2];
-  if (nsteps > 0) {
+  if (g0 < g1) {
 #pragma unroll
-    for (int b = 0; b < NB; ++b) load_scales(swr[b], 0, sw_n[b]);
-    load_scales(sar, 0, sa_n);
-    load(0, wa, aa);
+    for (int b = 0; b < NB; ++b) load_scales(swr[b], g0, sw_n[b]);
+    load_scales(sar, g0, sa_n);
+    load(16 * g0, wa, aa);
   }
-  for (int g = 0; g * 16 < nsteps; ++g) {
+  for (int g = g0; g < g1; ++g) {
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
       sw_c[b][0] = sw_n[b][0];
@@ -1785,20 +1794,39 @@ __global__ __launch_bounds__(64) void mx_packed_kernel(const uint8_t* __restrict
 #pragma unroll
     for (int j = 0; j < 16; j += 2) {
       const int t = 16 * g + j;
-      if (t >= nsteps) break;
-      load(min(t + 1, nsteps - 1), wb, ab);
+      if (t >= s1) break;
+      load(min(t + 1, s1 - 1), wb, ab);
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int b = 0; b < NB; ++b)
         acc[b] = mfma32_f8_scaled<0, 0>(wa[b], aa, acc[b], pick(sw_c[b], j), pick(sa_c, j));
-      if (t + 1 >= nsteps) break;
-      load(min(t + 2, nsteps - 1), wa, aa);
+      if (t + 1 >= s1) break;
+      load(min(t + 2, s1 - 1), wa, aa);
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int b = 0; b < NB; ++b)
         acc[b] = mfma32_f8_scaled<0, 0>(wb[b], ab, acc[b], pick(sw_c[b], j + 1),
                                         pick(sa_c, j + 1));
     }
+  }
+
+  if constexpr (NW > 1) {
+    // split-K reduction through LDS (fixed order: wave 0, 1, ..., NW-1);
+    // wave 0 finishes
+#pragma unroll
+    for (int b = 0; b < NB; ++b)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) red[((wave * NB + b) * 16 + r) * 64 + lane] = acc[b][r];
+    __syncthreads();
+    if (wave != 0) return;
+#pragma unroll
+    for (int b = 0; b < NB; ++b)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float v = red[(b * 16 + r) * 64 + lane];
+        for (int w = 1; w < NW; ++w) v += red[((w * NB + b) * 16 + r) * 64 + lane];
+        acc[b][r] = v;
+      }
   }
 
   // epilogue: registers (4q, 4q+1) and (4q+2, 4q+3) are (Gate, Up) pairs of
@@ -2211,21 +2239,23 @@ static hipError_t launch_f8_packed(const LaunchArgs& a) {
 #define F8_PACKED(mt, nb, nw)                                                              \
   {VAR_F8_PACKED, 1, (mt) * 16, F8Packed<mt, nb, nw>::SLAB_Y, 128, nw, nw,                  \
    F8Packed<mt, nb, nw>::LDS_BYTES, &launch_f8_packed<mt, nb, nw>}
-template <int NB>
+template <int NB, int NW>
 static hipError_t launch_mx_packed(const LaunchArgs& a) {
-  using C = MxPacked<NB>;
+  using C = MxPacked<NB, NW>;
   const long long nunit = (2LL * a.N + C::SLAB_W - 1) / C::SLAB_W;
   const long long nmb = (a.M + 31) / 32;
   if (nunit <= 0 || nmb <= 0) return hipSuccess;
   if (nunit > 0x7fffffffLL || nmb > 65535) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((mx_packed_kernel<NB>), dim3((unsigned)nunit, (unsigned)nmb), dim3(64), 0,
+  hipLaunchKernelGGL((mx_packed_kernel<NB, NW>), dim3((unsigned)nunit, (unsigned)nmb),
+                     dim3(C::kThreads), 0,
                      a.stream, (const uint8_t*)a.A, a.SA, (const uint8_t*)a.W1, a.SW, a.Y, a.M,
                      a.N, a.K, a.ks);
   return hipGetLastError();
 }
 
-#define MX_PACKED(nb)                                                                      \
-  {VAR_MX_PACKED, 1, 32, MxPacked<nb>::SLAB_Y, 64, 1, 1, 0, &launch_mx_packed<nb>}
+#define MX_PACKED(nb, nw)                                                                  \
+  {VAR_MX_PACKED, 1, 32, MxPacked<nb, nw>::SLAB_Y, 64, nw, nw, MxPacked<nb, nw>::LDS_BYTES,    \
+   &launch_mx_packed<nb, nw>}
 #define F8_SKINNY(mt, nb, nw)                                                              \
   {VAR_F8, 1, (mt) * 16, F8Skinny<mt, nb, nw>::SLAB_Y, 128, nw, nw,                         \
    F8Skinny<mt, nb, nw>::LDS_BYTES, &launch_f8_skinny<mt, nb, nw>}
@@ -2348,9 +2378,11 @@ static const KernelConfig kConfigs[] = {
     F8_PACKED(2, 2, 1),                                             // 75
     F8_PACKED(4, 2, 1),                                             // 76
     // ---- MXFP8 on fragment-ordered W8 (streaming, 32x32x64 scaled MFMA) -----
-    MX_PACKED(1),                                                   // 77
-    MX_PACKED(2),                                                   // 78
-    MX_PACKED(4),                                                   // 79
+    MX_PACKED(1, 1),                                                // 77
+    MX_PACKED(2, 1),                                                // 78
+    MX_PACKED(4, 1),                                                // 79
+    MX_PACKED(1, 2),                                                // 80
+    MX_PACKED(1, 4),                                                // 81
 };
 
 int config_count() { return (int)(sizeof(kConfigs) / sizeof(kConfigs[0])); }

@@ -66,13 +66,15 @@ int select_config(int variant, long long M, long long N, long long K, int cu_cou
   // M = 2048, the split 256-row tiles at M = 4096 and 8192)
   // MXFP8: 64 x 128 tiles for small M, the split 256 x 256 tiles above
   if (variant == VAR_MX) return M <= 192 ? 57 : 56;
-  // MXFP8 on fragment-ordered W8: one wave streaming blocks of 32 W8 rows by
-  // 32-row groups of A at any M; one block per workgroup (7B decode: 1184
-  // workgroups, 25.6 us against 27.1 with two), four from 6 blocks per CU
-  // (72B: 79.5 us against 92.1 with one)
+  // MXFP8 on fragment-ordered W8: blocks of 32 W8 rows by 32-row groups of A
+  // at any M; one block and one wave per workgroup (7B decode: 1184
+  // workgroups, 25.6 us against 27.1 with two blocks), four blocks from 6
+  // blocks per CU (72B: 79.5 us against 92.1 with one), and K split over four
+  // waves below one block per CU (8-way tensor-parallel shares of 7B and 72B:
+  // 8.9 and 17.6 us against 19.7 and 42.0 with one wave)
   if (variant == VAR_MX_PACKED) {
     const long long blocks = (2 * N + 31) / 32, cus = cu_count > 0 ? cu_count : 256;
-    return blocks >= 6 * cus ? 79 : 77;
+    return blocks >= 6 * cus ? 79 : (blocks >= cus ? 77 : 81);
   }
   if (variant == VAR_PACKED) {
     // fragment-ordered weights (measured at M = 16, 32, 48, 64 on the 0.5B,

@@ -65,9 +65,10 @@ CASES = [
     (128, 4864, 896, list(range(70, 77))),
     (33, 72, 144, list(range(70, 77))),
     # MXFP8 on fragment-ordered W8: decode, 0.5B, ragged row blocks and groups
-    (16, 18944, 3584, [77, 78, 79]),
-    (128, 4864, 896, [77, 78, 79]),
-    (33, 72, 1088, [77, 78, 79]),
+    (16, 18944, 3584, [77, 78, 79, 80, 81]),
+    (128, 4864, 896, [77, 78, 79, 80, 81]),
+    (16, 2368, 3584, [80, 81]),
+    (33, 72, 1088, [77, 78, 79, 80, 81]),
 ]
 
 
@@ -91,7 +92,7 @@ LIMIT_CASES = [
     # fragment-ordered W8 just under 2 GiB: 4096 row blocks x 255 steps x 2 KB
     (16, 32768, 32640, list(range(70, 77)), 8),
     # MX fragment-ordered W8 just under 2 GiB: 2048 row blocks x 511 steps x 2 KB
-    (16, 32768, 32704, [77, 78, 79], 8),
+    (16, 32768, 32704, [77, 78, 79, 80, 81], 8),
     (256, 32768, 16376, [1, 8, 16], 4),
     # byte tensors: A8 = 65536 x 32704 B, W8 = 2 x 32768 x 32704 B (K % 64 == 0)
     (65536, 64, 32704, [43, 53, 56], 4),
