@@ -241,7 +241,8 @@ def swiglu_query_unfused(handle, M, N, K):
 
 def swiglu_forward_fp8(handle, A8, W8, Y, M, N, K, scale_a=1.0, scale_w1=1.0, scale_w2=1.0,
                        config_id=-1, stream=None, variant=VARIANT_AUTO):
-    """A8 [M, K] and W8 [2N, K] hold E4M3 codes (uint8 tensors); Y bf16 [M, N]."""
+    """A8 [M, K] and W8 [2N, K] hold E4M3 codes (uint8 tensors; with variant
+    VARIANT_FP8_PACKED, W8 is the fragment-ordered copy); Y bf16 [M, N]."""
     _check(load().swiglu_forward_fp8(handle, _ptr(A8), _ptr(W8), _ptr(Y), M, N, K, scale_a,
                                      scale_w1, scale_w2, variant, config_id, _stream(stream)),
            "swiglu_forward_fp8")

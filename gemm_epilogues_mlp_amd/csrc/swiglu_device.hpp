@@ -10,9 +10,10 @@
 //                             B: lane l holds col l%16, k = 8*(l/16) + [0,8)
 //                             D: lane l, reg r -> col l%16, row 4*(l/16) + r
 // Both sources want 8 consecutive k per lane.  A [M,K] is k-contiguous in HBM;
-// the weights [K,N] are n-contiguous, so weight tiles are transposed in
-// registers (8x8 blocks of bf16 with v_perm_b32) on their way to LDS or to the
-// MFMA.
+// the weights [K,N] are n-contiguous, so the LDS-tiled kernels read weight
+// fragments with the transposing LDS read, the strided streaming kernel
+// transposes 8x8 blocks of bf16 in registers (v_perm_b32), and the
+// fragment-ordered layouts store the weights k-contiguous in the first place.
 #pragma once
 
 #include <hip/hip_runtime.h>

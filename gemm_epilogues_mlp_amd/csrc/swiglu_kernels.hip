@@ -13,16 +13,15 @@
 //   §Definizione del Problema: the unfused baseline (two GEMMs that write
 //     Gate and Up to HBM, then a separate activation).
 //
-// Two kernel families, both built on the MFMA conventions in swiglu_device.hpp:
+// Kernel families, all on the MFMA conventions in swiglu_device.hpp (each is
+// described in detail where it is defined):
 //
-//  * tiled_kernel   LDS-tiled, v_mfma_f32_32x32x16_bf16, 256 threads.  Tiles of
-//    A [BM, BK] and of the weights are staged through registers into a
-//    double-buffered, row-padded LDS tile (one barrier per K step); the
-//    weight tile is transposed to k-contiguous rows on the way in.  For the
-//    interleave mode the transposition also separates even (Gate) and odd (Up)
-//    columns into two LDS regions, so a lane's Gate and Up accumulators for
-//    the same output column sit in the same register of two accumulator sets
-//    and the pair-multiply epilogue needs no data exchange.
+//  * tiled_kernel / tiled_split_kernel / pingpong_kernel  LDS-tiled bf16,
+//    v_mfma_f32_32x32x16_bf16, 4 or 8 waves.  A and weight k-tiles go from HBM
+//    straight into a ring of LDS stages by DMA; weight fragments are read with
+//    the transposing LDS read; the MFMA computes D^T = W^T A^T so that a Gate
+//    / Up pair of the interleave mode sits in two adjacent registers of one
+//    lane.  Interleave, sync and plain-GEMM (unfused baseline) modes.
 //
 //  * skinny_kernel  split-K weight streaming for small M (decode-sized
 //    batches), v_mfma_f32_16x16x32_bf16.  Each lane loads an 8 (k) x 8 (column)
@@ -34,6 +33,17 @@
 //    accumulation across tiles for the baseline's errors]).  In interleave
 //    mode a lane holds 8 consecutive W_fused columns in 8 accumulators, so the
 //    pair (2n, 2n+1) is two adjacent accumulators of one lane.
+//
+//  * packed_kernel  the same streaming on W_fused stored once in MFMA
+//    fragment order: 1 KB contiguous per load, no transposition.
+//
+//  * f8_kernel / f8_split_kernel / f8_skinny_kernel / f8_packed_kernel  FP8
+//    (E4M3) inputs on the scaled MFMAs, LDS-tiled and streaming; MX mode of
+//    the tile and mx_packed_kernel for MXFP8 (E8M0 block scales applied by
+//    the MFMA).
+//
+//  * element-wise kernels: the unfused gate, the weight packs and the FP8 /
+//    MX quantisers.
 #include "swiglu_device.hpp"
 #include "swiglu_internal.h"
 
@@ -896,16 +906,16 @@ void skinny_kernel(const uint16_t* __restrict__ A,
 // The 1 KB run c of a block is the B fragment of MFMA c for all 64 lanes (lane
 // 16 g + l: 8 consecutive k of column 128 s + 8 l + c), so every load
 // instruction reads 1 KB contiguous, a block is 8 KB contiguous, and the
-// blocks of a slab follow one another: a workgroup streams one contiguous
-// span of the weights.  The accumulators of MFMA 2q and 2q+1 hold the Gate
-// and the Up column of output 64 s + 4 l + q in the same lane, as in the
-// skinny kernel.
+// blocks of a slab follow one another.  The accumulators of MFMA 2q and 2q+1
+// hold the Gate and the Up column of output 64 s + 4 l + q in the same lane,
+// as in the skinny kernel.
 //
 // A workgroup takes CH of the 8 MFMA column groups of one slab (CH = 8, 4 or
 // 2; CH/2 outputs per lane and row), i.e. a contiguous CH KB run of every
-// block of the slab.  Each CU streams at a bounded rate, so the time follows
-// the most loaded CU: splitting a slab into 8/CH workgroups evens the load
-// (Qwen2.5-7B decode: 296 slabs on 256 CUs, but 1184 quarter slabs).
+// block of the slab (with CH = 8 the whole slab, one contiguous span).  Each
+// CU streams at a bounded rate, so the time follows the most loaded CU:
+// splitting a slab into 8/CH workgroups evens the load (Qwen2.5-7B decode:
+// 296 slabs on 256 CUs, run as 592 half slabs).
 //
 // Waves of a workgroup take the slab's steps in turn (wave w: t = w, w + NW,
 // ...), so at any time they read neighbouring blocks; each wave keeps two
