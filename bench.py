@@ -55,9 +55,10 @@ def parse():
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py measures a single GPU; --gpus {args.gpus} is not supported "
-              "(the op needs no collective; see the sharding note in the design notes).",
-              file=sys.stderr)
+        print(f"bench.py measures a single GPU; --gpus {args.gpus} is not supported. The op "
+              "needs no collective: under tensor parallelism each GPU runs its own slice of "
+              "W_fused columns (cut on Gate/Up pair boundaries) on the full A, so one GPU's "
+              "throughput is the per-GPU figure.", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np

@@ -140,7 +140,7 @@ def _time_configs(h, variant, M, N, K, ids, reps, rotate_bytes, seed=0):
 
 def read_entries(path):
     """Entries of a valid tuned file as {(variant, M, N, K): line}."""
-    sw.swiglu_tuned_check(path)  # raises unless valid for this build
+    sw.swiglu_tuned_check(path)  # raises unless its signature matches the loaded library
     out = {}
     header = False
     for line in open(path):
