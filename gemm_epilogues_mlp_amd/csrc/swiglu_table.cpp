@@ -44,6 +44,14 @@ const ShapeEntry kTable[] = {
     {VAR_INTERLEAVE, 4096, 29568, 8192, 40},
     {VAR_SYNC, 4096, 29568, 8192, 42},
     {VAR_GEMM, 4096, 29568, 8192, 41},
+    // one GPU's share under 8-way tensor parallelism (N / 8), where the tuner
+    // beat the fallback rule by more than 3 %
+    {VAR_SYNC, 8192, 2368, 3584, 8},          // 7B prefill share: 348 vs 376 us
+    {VAR_INTERLEAVE, 16, 2368, 3584, 27},     // 7B decode share: 22.9 vs 23.6 us
+    {VAR_GEMM, 16, 2368, 3584, 30},           // 32.1 vs 49.2 us
+    {VAR_INTERLEAVE, 128, 608, 896, 5},       // 0.5B share: 7.6 vs 7.9 us
+    {VAR_SYNC, 128, 608, 896, 12},            // 9.0 vs 13.6 us
+    {VAR_PACKED, 128, 608, 896, 67},          // 4.6 vs 9.2 us
 };
 
 int find_config(int variant, int family, int bm, int bn, int waves) {
@@ -119,9 +127,15 @@ int select_config(int variant, long long M, long long N, long long K, int cu_cou
   // M = 128, 128-row tiles around M = 256, and from M = 512 on the 256-row
   // eight-wave tiles (4x2 waves, short last round split into quarter tiles),
   // which won even where they leave CUs idle (M = 512: 140 tiles on 256 CUs).
+  // Narrow N: when the 256-row tiles would leave more than half of the CUs
+  // without a tile, the 128-row tiles win (tuner, 1.5B share under 8-way
+  // tensor parallelism, M = 2048, N = 1120: 72 big tiles; 25.9 vs 34.5 us
+  // interleave, 36.4 vs 48.6 us sync).
+  const long long cus = cu_count > 0 ? cu_count : 256;
+  const bool few_big = ((M + 255) / 256) * ((N + 127) / 128) * 2 < cus;
   if (variant == VAR_GEMM) return M <= 192 ? 30 : (M <= 384 ? 16 : 41);
-  if (variant == VAR_SYNC) return M <= 192 ? 29 : (M <= 384 ? 8 : 42);
-  return M <= 192 ? 3 : (M <= 384 ? 1 : 40);
+  if (variant == VAR_SYNC) return M <= 192 ? 29 : ((M <= 384 || few_big) ? 8 : 42);
+  return M <= 192 ? 3 : ((M <= 384 || few_big) ? 1 : 40);
 }
 
 int recommend_layout(long long M, long long N, long long K, int cu_count) {

@@ -48,6 +48,12 @@ CASES = [
     (2048, 8960, 40, [40, 41, 42]),    # 1.5B M and N: 512 big + 48 split
     (128, 4864, 40, [3, 29, 30]),      # 0.5B M and N
     (16, 18944, 64, [23, 12, 18]),     # 7B decode M and N
+    # the table's choices at one GPU's share under 8-way tensor parallelism
+    (2048, 1120, 1536, [1, 8]),
+    (8192, 2368, 96, [8, 40, 41]),
+    (16, 2368, 3584, [27, 30, 64, 11]),
+    (128, 608, 896, [5, 12, 67, 30]),
+    (4096, 3696, 64, [40, 42, 41]),
     # FP8 / MXFP8 (K a multiple of 64): split-tail tiles at 1.5B M and N in
     # both orders and with block scales, the small-M tiles and the streaming
     # kernel at the 0.5B and decode shapes
