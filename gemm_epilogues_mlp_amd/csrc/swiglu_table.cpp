@@ -70,10 +70,17 @@ int select_config(int variant, long long M, long long N, long long K, int cu_cou
   for (const ShapeEntry& e : kTable)
     if (e.variant == variant && e.M == M && e.N == N && e.K == K) return e.config_id;
   (void)K;
+  // Narrow N: when the 256-row tiles (128 output columns each) would leave more
+  // than half of the CUs without a tile, smaller tiles win (tuner, 1.5B share
+  // under 8-way tensor parallelism, M = 2048, N = 1120: 72 big tiles; bf16
+  // 25.9 vs 34.5 us interleave, 36.4 vs 48.6 us sync; FP8 15.8 vs 20.4 us;
+  // MXFP8 20.6 vs 23.1 us).
+  const long long cus = cu_count > 0 ? cu_count : 256;
+  const bool few_big = ((M + 255) / 256) * ((N + 127) / 128) * 2 < cus;
   // FP8 sync order (measured on the five workloads: 128 x 128 tiles won at
   // M = 2048, the split 256-row tiles at M = 4096 and 8192)
   // MXFP8: 64 x 128 tiles for small M, the split 256 x 256 tiles above
-  if (variant == VAR_MX) return M <= 192 ? 57 : 56;
+  if (variant == VAR_MX) return (M <= 192 || few_big) ? 57 : 56;
   // MXFP8 on fragment-ordered W8: blocks of 32 W8 rows by 32-row groups of A
   // at any M; one block and one wave per workgroup (7B decode: 1184
   // workgroups, 25.6 us against 27.1 with two blocks), four blocks from 6
@@ -81,7 +88,7 @@ int select_config(int variant, long long M, long long N, long long K, int cu_cou
   // waves below one block per CU (8-way tensor-parallel shares of 7B and 72B:
   // 8.9 and 17.6 us against 19.7 and 42.0 with one wave)
   if (variant == VAR_MX_PACKED) {
-    const long long blocks = (2 * N + 31) / 32, cus = cu_count > 0 ? cu_count : 256;
+    const long long blocks = (2 * N + 31) / 32;
     return blocks >= 6 * cus ? 79 : (blocks >= cus ? 77 : 81);
   }
   if (variant == VAR_PACKED) {
@@ -94,7 +101,7 @@ int select_config(int variant, long long M, long long N, long long K, int cu_cou
     // are re-read once per 64 rows (a fallback, not a fast path).
     // Narrow N (under 64 slabs: one GPU's share under 8-way tensor
     // parallelism) takes 8 waves per quarter slab (tuner: +3-5 %).
-    const long long slabs = packed_slabs(N), cus = cu_count > 0 ? cu_count : 256;
+    const long long slabs = packed_slabs(N);
     if (M <= 16)
       return 4 * slabs >= 7 * cus ? 58 : (2 * slabs >= cus ? 65 : (slabs >= 64 ? 63 : 64));
     return M <= 32 ? 69 : 62;
@@ -103,7 +110,7 @@ int select_config(int variant, long long M, long long N, long long K, int cu_cou
   // wave per 32 W8 rows, two waves splitting K when that leaves fewer than two
   // workgroups per CU (tuner at N = 2368 and 3696: +29 %)
   if (variant == VAR_F8_PACKED) {
-    const long long units = (2 * N + 31) / 32, cus = cu_count > 0 ? cu_count : 256;
+    const long long units = (2 * N + 31) / 32;
     if (M <= 16) return units >= 2 * cus ? 70 : 72;
     return M <= 32 ? 75 : 76;
   }
@@ -113,9 +120,11 @@ int select_config(int variant, long long M, long long N, long long K, int cu_cou
     // tiles around M = 256, and the eight-wave 256 x 256 tiles (split tail)
     // (measured: M = 16 and 32 at K = 3584, N = 18944; M = 64 there and at
     // K = 896, N = 4864; M = 128 at the 0.5B shape)
-    if (M <= 16) return 52;
+    // (narrow N at M <= 16: fewer than two one-wave workgroups per CU, the
+    // split-K configuration wins: 7B decode share 12.2 vs 15.7 us)
+    if (M <= 16) return (2 * N + 31) / 32 >= 2 * cus ? 52 : 51;
     if (M <= 32) return 51;
-    return M <= 192 ? 46 : (M <= 384 ? 45 : 43);
+    return M <= 192 ? 46 : ((M <= 384 || few_big) ? 45 : 43);
   }
   if (M <= 64) {
     // decode-sized batches: split-K weight streaming, 16-row MFMA blocks
@@ -127,12 +136,7 @@ int select_config(int variant, long long M, long long N, long long K, int cu_cou
   // M = 128, 128-row tiles around M = 256, and from M = 512 on the 256-row
   // eight-wave tiles (4x2 waves, short last round split into quarter tiles),
   // which won even where they leave CUs idle (M = 512: 140 tiles on 256 CUs).
-  // Narrow N: when the 256-row tiles would leave more than half of the CUs
-  // without a tile, the 128-row tiles win (tuner, 1.5B share under 8-way
-  // tensor parallelism, M = 2048, N = 1120: 72 big tiles; 25.9 vs 34.5 us
-  // interleave, 36.4 vs 48.6 us sync).
-  const long long cus = cu_count > 0 ? cu_count : 256;
-  const bool few_big = ((M + 255) / 256) * ((N + 127) / 128) * 2 < cus;
+  // narrow N (few_big above): the 128-row tiles
   if (variant == VAR_GEMM) return M <= 192 ? 30 : (M <= 384 ? 16 : 41);
   if (variant == VAR_SYNC) return M <= 192 ? 29 : ((M <= 384 || few_big) ? 8 : 42);
   return M <= 192 ? 3 : ((M <= 384 || few_big) ? 1 : 40);

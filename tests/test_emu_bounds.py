@@ -54,6 +54,8 @@ CASES = [
     (16, 2368, 3584, [27, 30, 64, 11]),
     (128, 608, 896, [5, 12, 67, 30]),
     (4096, 3696, 64, [40, 42, 41]),
+    (2048, 1120, 1536, [45, 57, 54]),
+    (16, 2368, 3584, [51, 72, 81]),
     # FP8 / MXFP8 (K a multiple of 64): split-tail tiles at 1.5B M and N in
     # both orders and with block scales, the small-M tiles and the streaming
     # kernel at the 0.5B and decode shapes

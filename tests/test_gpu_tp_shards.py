@@ -74,3 +74,51 @@ def test_shard_unfused(handle, shard):
     g, u = host(ws[0])[d["rows"]], host(ws[1])[d["rows"]]
     assert_parity(host(y)[d["rows"]], oracle.gate(oracle.decode_bf16(g), oracle.decode_bf16(u)),
                   f"shard {(M, K, N)} unfused")
+
+
+def _e4m3(x):
+    """(codes, scale): the oracle's quantiser, scale = max|x| / 448 per tensor."""
+    amax = np.float32(np.max(np.abs(x)))
+    s = np.float32(amax / np.float32(448.0)) if amax > 0 else np.float32(1.0)
+    return oracle.quantize_e4m3(x, np.float32(1.0) / s), float(s)
+
+
+@pytest.mark.parametrize("fmt", ["fp8", "fp8-sync", "fp8-packed", "mxfp8", "mxfp8-packed"])
+def test_shard_fp8_parity(handle, shard, fmt):
+    """The FP8 (per-tensor E4M3) and MXFP8 forwards at the shard shapes, in
+    the table's configuration, against the oracle on the same codes."""
+    import torch
+    d = shard
+    M, K, N = d["M"], d["K"], d["N"]
+    rows = d["rows"]
+    t8 = lambda x: torch.from_numpy(np.ascontiguousarray(x)).cuda()
+    y = empty_poisoned((M, N))
+    if fmt.startswith("fp8"):
+        (a8, sa), (w18, s1), (w28, s2) = (_e4m3(I.bf16_bits_to_f32(x))
+                                          for x in (d["a"], d["w1"], d["w2"]))
+        w8 = oracle.pack_fp8_kmajor(w18, w28)
+        variant = {"fp8": sw.VARIANT_INTERLEAVE, "fp8-sync": sw.VARIANT_SYNC,
+                   "fp8-packed": sw.VARIANT_FP8_PACKED}[fmt]
+        wt = oracle.pack_fp8_fragments(w8) if fmt == "fp8-packed" else w8
+        log(f"shard {(M, K, N)} {fmt} -> config "
+            f"{sw.swiglu_query_fp8(handle, M, N, K, variant)['id']}")
+        sw.swiglu_forward_fp8(handle, t8(a8), t8(wt), y, M, N, K, sa, s1, s2, variant=variant)
+        y_ref = oracle.swiglu_fp8_rows(a8, w18, w28, sa, s1, s2, rows=rows)
+    else:
+        qa, sa = oracle.quantize_mx(I.bf16_bits_to_f32(d["a"]))
+        qw, sw_ = oracle.quantize_mx(I.bf16_bits_to_f32(oracle.pack_kmajor_bf16(d["w1"], d["w2"])))
+        ks = sa.shape[1]
+        if fmt == "mxfp8":
+            log(f"shard {(M, K, N)} {fmt} -> config "
+                f"{sw.swiglu_query_fp8(handle, M, N, K, sw.VARIANT_MXFP8)['id']}")
+            sw.swiglu_forward_mx(handle, t8(qa), t8(sa), t8(qw), t8(sw_), y, M, N, K, ks)
+        else:
+            log(f"shard {(M, K, N)} {fmt} -> config "
+                f"{sw.swiglu_query_fp8(handle, M, N, K, sw.VARIANT_MXFP8_PACKED)['id']}")
+            sw.swiglu_forward_mx_packed(handle, t8(qa), t8(sa), t8(oracle.pack_mx_fragments(qw)),
+                                        t8(sw_), y, M, N, K, ks)
+        y_ref = oracle.swiglu_mx_rows(qa, sa, qw, sw_, rows=rows)
+    torch.cuda.synchronize()
+    yb = host(y)
+    assert np.all(np.isfinite(decode(yb))), "unwritten or non-finite outputs"
+    assert_parity(yb[rows], y_ref, f"shard {(M, K, N)} {fmt}")
