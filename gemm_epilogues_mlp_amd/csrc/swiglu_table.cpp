@@ -52,6 +52,13 @@ const ShapeEntry kTable[] = {
     {VAR_INTERLEAVE, 128, 608, 896, 5},       // 0.5B share: 7.6 vs 7.9 us
     {VAR_SYNC, 128, 608, 896, 12},            // 9.0 vs 13.6 us
     {VAR_PACKED, 128, 608, 896, 67},          // 4.6 vs 9.2 us
+    // batches of 32 and 64 rows on the 72B matrices: the 128 x 256 tile beats
+    // weight streaming (tuner: 156.4 vs 172.3 us at M = 32, 157.3 vs 193.3 us at
+    // M = 64); FP8 split-K streaming with 32-row blocks at M = 32
+    {VAR_INTERLEAVE, 32, 29568, 8192, 1},
+    {VAR_INTERLEAVE, 64, 29568, 8192, 1},
+    {VAR_F8, 32, 29568, 8192, 50},            // 93.1 vs 108.0 us
+    {VAR_PACKED, 32, 29568, 8192, 62},        // 163.1 vs 182.6 us
 };
 
 int find_config(int variant, int family, int bm, int bn, int waves) {
@@ -69,7 +76,6 @@ int find_config(int variant, int family, int bm, int bn, int waves) {
 int select_config(int variant, long long M, long long N, long long K, int cu_count) {
   for (const ShapeEntry& e : kTable)
     if (e.variant == variant && e.M == M && e.N == N && e.K == K) return e.config_id;
-  (void)K;
   // Narrow N: when the 256-row tiles (128 output columns each) would leave more
   // than half of the CUs without a tile, smaller tiles win (tuner, 1.5B share
   // under 8-way tensor parallelism, M = 2048, N = 1120: 72 big tiles; bf16
@@ -77,10 +83,16 @@ int select_config(int variant, long long M, long long N, long long K, int cu_cou
   // MXFP8 20.6 vs 23.1 us).
   const long long cus = cu_count > 0 ? cu_count : 256;
   const bool few_big = ((M + 255) / 256) * ((N + 127) / 128) * 2 < cus;
+  // Wide N (at least half a CU's worth of 256-wide W_fused column tiles, i.e.
+  // N >= 16384 on 256 CUs): from M = 65 on, 256-row tiles already give every
+  // CU work and their higher arithmetic intensity wins over the small tiles
+  // chosen for narrower matrices (tuner, 7B and 72B K and N: M = 128 35-38 %,
+  // M = 256 37 % faster in bf16; FP8 20-28 %, MXFP8 10-21 %).
+  const bool wide = (2 * N + 255) / 256 * 2 >= cus;
   // FP8 sync order (measured on the five workloads: 128 x 128 tiles won at
   // M = 2048, the split 256-row tiles at M = 4096 and 8192)
   // MXFP8: 64 x 128 tiles for small M, the split 256 x 256 tiles above
-  if (variant == VAR_MX) return (M <= 192 || few_big) ? 57 : 56;
+  if (variant == VAR_MX) return ((M <= 192 && !wide) || few_big) ? 57 : 56;
   // MXFP8 on fragment-ordered W8: blocks of 32 W8 rows by 32-row groups of A
   // at any M; one block and one wave per workgroup (7B decode: 1184
   // workgroups, 25.6 us against 27.1 with two blocks), four blocks from 6
@@ -124,6 +136,7 @@ int select_config(int variant, long long M, long long N, long long K, int cu_cou
     // split-K configuration wins: 7B decode share 12.2 vs 15.7 us)
     if (M <= 16) return (2 * N + 31) / 32 >= 2 * cus ? 52 : 51;
     if (M <= 32) return 51;
+    if (wide && M <= 384) return M <= 192 ? 45 : 44;
     return M <= 192 ? 46 : ((M <= 384 || few_big) ? 45 : 43);
   }
   if (M <= 64) {
@@ -139,6 +152,7 @@ int select_config(int variant, long long M, long long N, long long K, int cu_cou
   // narrow N (few_big above): the 128-row tiles
   if (variant == VAR_GEMM) return M <= 192 ? 30 : (M <= 384 ? 16 : 41);
   if (variant == VAR_SYNC) return M <= 192 ? 29 : ((M <= 384 || few_big) ? 8 : 42);
+  if (wide && M <= 384) return M <= 192 ? (K >= 6144 ? 31 : 35) : 21;
   return M <= 192 ? 3 : ((M <= 384 || few_big) ? 1 : 40);
 }
 

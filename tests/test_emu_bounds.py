@@ -56,6 +56,11 @@ CASES = [
     (4096, 3696, 64, [40, 42, 41]),
     (2048, 1120, 1536, [45, 57, 54]),
     (16, 2368, 3584, [51, 72, 81]),
+    # mid-size batches on the 7B and 72B matrices (wide N)
+    (128, 18944, 64, [35, 45, 56]),
+    (256, 18944, 64, [21, 44]),
+    (128, 29568, 64, [31, 45, 56]),
+    (32, 29568, 64, [1, 50, 62]),
     # FP8 / MXFP8 (K a multiple of 64): split-tail tiles at 1.5B M and N in
     # both orders and with block scales, the small-M tiles and the streaming
     # kernel at the 0.5B and decode shapes

@@ -1,9 +1,14 @@
-"""GPU parity at one GPU's share of the Qwen2.5-shaped MLPs under 8-way tensor
-parallelism (W_fused columns split eight ways on Gate/Up pair boundaries:
-[M, N/8, K]), in the configuration the table picks for each layout, and the
-unfused baseline.  Inputs follow the workloads' recipe (A ~ N(0, 1),
-W ~ N(0, 1/K), seeded, bf16); sampled rows (every column) are checked against
-the oracle, the whole Y for unwritten or non-finite elements."""
+"""GPU parity at the shapes where the table's choice was set by the tuner
+beyond the five workloads, in the configuration the table picks for each
+layout and input format, and the unfused baseline:
+
+* one GPU's share of the Qwen2.5-shaped MLPs under 8-way tensor parallelism
+  (W_fused columns split eight ways on Gate/Up pair boundaries: [M, N/8, K]);
+* mid-size batches (M = 32 ... 256) on the 7B and 72B matrices.
+
+Inputs follow the workloads' recipe (A ~ N(0, 1), W ~ N(0, 1/K), seeded,
+bf16); sampled rows (every column) are checked against the oracle, the whole
+Y for unwritten or non-finite elements."""
 import numpy as np
 import pytest
 
@@ -14,9 +19,12 @@ from gpu_util import assert_parity, decode, dev, empty_poisoned, host, log
 
 pytestmark = pytest.mark.gpu
 
-# (M, K, N): 72B, 7B prefill, 1.5B, 0.5B and 7B decode shares
+# (M, K, N): 72B, 7B prefill, 1.5B, 0.5B and 7B decode shares; then mid-size
+# batches on the 72B and 7B matrices
 SHARDS = [(4096, 8192, 3696), (8192, 3584, 2368), (2048, 1536, 1120), (128, 896, 608),
-          (16, 3584, 2368)]
+          (16, 3584, 2368),
+          (32, 8192, 29568), (64, 8192, 29568), (128, 8192, 29568), (128, 3584, 18944),
+          (256, 3584, 18944)]
 
 
 @pytest.fixture(scope="module")
