@@ -92,7 +92,7 @@ int select_config(int variant, long long M, long long N, long long K, int cu_cou
   // FP8 sync order (measured on the five workloads: 128 x 128 tiles won at
   // M = 2048, the split 256-row tiles at M = 4096 and 8192)
   // MXFP8: 64 x 128 tiles for small M, the split 256 x 256 tiles above
-  if (variant == VAR_MX) return ((M <= 192 && !wide) || few_big) ? 57 : 56;
+  if (variant == VAR_MX) return (M <= 64 || (M <= 192 && !wide) || few_big) ? 57 : 56;
   // MXFP8 on fragment-ordered W8: blocks of 32 W8 rows by 32-row groups of A
   // at any M; one block and one wave per workgroup (7B decode: 1184
   // workgroups, 25.6 us against 27.1 with two blocks), four blocks from 6
@@ -126,7 +126,12 @@ int select_config(int variant, long long M, long long N, long long K, int cu_cou
     if (M <= 16) return units >= 2 * cus ? 70 : 72;
     return M <= 32 ? 75 : 76;
   }
-  if (variant == VAR_F8_SYNC) return M <= 192 ? 55 : (M <= 3072 ? 54 : 53);
+  if (variant == VAR_F8_SYNC) {
+    // wide N: 128-row tiles from M = 33, the split 256-row tiles from M = 193
+    // (tuner: M = 64 46.7 vs 53.6 us, M = 128 24-30 %, M = 1024 10.5 %)
+    if (wide && M > 32) return M <= 192 ? 54 : 53;
+    return M <= 192 ? 55 : (M <= 3072 ? 54 : 53);
+  }
   if (variant == VAR_F8) {
     // FP8: split-K weight streaming up to M = 64, then 64 x 128 tiles, 128-row
     // tiles around M = 256, and the eight-wave 256 x 256 tiles (split tail)
@@ -136,8 +141,16 @@ int select_config(int variant, long long M, long long N, long long K, int cu_cou
     // split-K configuration wins: 7B decode share 12.2 vs 15.7 us)
     if (M <= 16) return (2 * N + 31) / 32 >= 2 * cus ? 52 : 51;
     if (M <= 32) return 51;
-    if (wide && M <= 384) return M <= 192 ? 45 : 44;
+    if (wide && M > 32 && M <= 384) return M <= 192 ? 45 : 44;
     return M <= 192 ? 46 : ((M <= 384 || few_big) ? 45 : 43);
+  }
+  if (M <= 64 && M > 32 && wide) {
+    // 33-64 rows on wide matrices: the LDS-tiled kernels beat split-K
+    // streaming (tuner, 7B M = 64: interleave 256 x 192 60.3 vs 84.7 us, sync
+    // 128 x 128 82.3 vs 93.5 us, GEMM 128 x 128 85.4 vs 89.7 us)
+    if (variant == VAR_GEMM) return 16;
+    if (variant == VAR_SYNC) return 8;
+    return 35;
   }
   if (M <= 64) {
     // decode-sized batches: split-K weight streaming, 16-row MFMA blocks
@@ -150,21 +163,36 @@ int select_config(int variant, long long M, long long N, long long K, int cu_cou
   // eight-wave tiles (4x2 waves, short last round split into quarter tiles),
   // which won even where they leave CUs idle (M = 512: 140 tiles on 256 CUs).
   // narrow N (few_big above): the 128-row tiles
-  if (variant == VAR_GEMM) return M <= 192 ? 30 : (M <= 384 ? 16 : 41);
-  if (variant == VAR_SYNC) return M <= 192 ? 29 : ((M <= 384 || few_big) ? 8 : 42);
+  if (variant == VAR_GEMM) {
+    // wide N (tuner, 7B and 72B): 128 x 128 to M = 192 (21-39 %), 256 x 128
+    // to M = 384 (19 %), 256 x 192 to M = 768 (5 %)
+    if (wide) return M <= 192 ? 16 : (M <= 384 ? 15 : (M <= 768 ? 22 : 41));
+    return M <= 192 ? 30 : (M <= 384 ? 16 : 41);
+  }
+  if (variant == VAR_SYNC) {
+    // wide N (tuner): 128 x 128 to M = 192 (24-44 %), 256 x 128 with 4 x 2
+    // waves to M = 384 (19 %)
+    if (wide) return M <= 192 ? 8 : (M <= 384 ? 39 : 42);
+    return M <= 192 ? 29 : ((M <= 384 || few_big) ? 8 : 42);
+  }
   if (wide && M <= 384) return M <= 192 ? (K >= 6144 ? 31 : 35) : 21;
   return M <= 192 ? 3 : ((M <= 384 || few_big) ? 1 : 40);
 }
 
 int recommend_layout(long long M, long long N, long long K, int cu_count) {
-  (void)N, (void)K, (void)cu_count;
+  (void)K;
   // The page prefers the sync kernel above M = 2048.  On MI355X the interleave
   // kernel was faster at every measured M (0.5B-72B shapes, M = 16..8192): it
   // loads A once and keeps every accumulator busy in every K step, while the
   // sync kernel alternates between half of its registers (Gate, then Up).
   // Up to M = 64 the same Kernel-2 order on fragment-ordered weights streams
-  // them fastest (1.16-1.6x the interleaved layout at M = 16 ... 64).
-  return M <= 64 ? 2 : 1;
+  // them fastest (1.16-1.6x the interleaved layout at M = 16 ... 64), except
+  // on wide matrices above M = 32, where the LDS-tiled kernel wins (7B M = 64:
+  // 60.3 us against 74.5 us on the packed layout).
+  const long long cus = cu_count > 0 ? cu_count : 256;
+  const bool wide = (2 * N + 255) / 256 * 2 >= cus;
+  if (M <= 32 || (M <= 64 && !wide)) return 2;
+  return 1;
 }
 
 }  // namespace swiglu
