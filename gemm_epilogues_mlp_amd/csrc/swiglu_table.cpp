@@ -59,6 +59,10 @@ const ShapeEntry kTable[] = {
     {VAR_INTERLEAVE, 64, 29568, 8192, 1},
     {VAR_F8, 32, 29568, 8192, 50},            // 93.1 vs 108.0 us
     {VAR_PACKED, 32, 29568, 8192, 62},        // 163.1 vs 182.6 us
+    // larger batches on the 7B and 72B matrices (tuner)
+    {VAR_F8, 2048, 29568, 8192, 44},          // no split tail: 879 vs 957 us
+    {VAR_SYNC, 1024, 18944, 3584, 8},         // 359 vs 375 us
+    {VAR_F8_SYNC, 1024, 18944, 3584, 54},     // 184 vs 196 us
 };
 
 int find_config(int variant, int family, int bm, int bn, int waves) {
@@ -144,13 +148,14 @@ int select_config(int variant, long long M, long long N, long long K, int cu_cou
     if (wide && M > 32 && M <= 384) return M <= 192 ? 45 : 44;
     return M <= 192 ? 46 : ((M <= 384 || few_big) ? 45 : 43);
   }
-  if (M <= 64 && M > 32 && wide) {
-    // 33-64 rows on wide matrices: the LDS-tiled kernels beat split-K
-    // streaming (tuner, 7B M = 64: interleave 256 x 192 60.3 vs 84.7 us, sync
-    // 128 x 128 82.3 vs 93.5 us, GEMM 128 x 128 85.4 vs 89.7 us)
+  if (M <= 64 && M > 16 && wide) {
+    // 17-64 rows on wide matrices: the LDS-tiled kernels beat split-K
+    // streaming (tuner, 7B: interleave 128 x 256 at M = 32 54.8 vs 72.5 us,
+    // 256 x 192 at M = 64 60.3 vs 84.7 us; sync 128 x 128 73.2 vs 79.1 us and
+    // 82.3 vs 93.5 us; GEMM 128 x 128 73.9 vs 76.4 us and 85.4 vs 89.7 us)
     if (variant == VAR_GEMM) return 16;
     if (variant == VAR_SYNC) return 8;
-    return 35;
+    return M <= 32 ? 1 : 35;
   }
   if (M <= 64) {
     // decode-sized batches: split-K weight streaming, 16-row MFMA blocks
@@ -187,11 +192,11 @@ int recommend_layout(long long M, long long N, long long K, int cu_count) {
   // sync kernel alternates between half of its registers (Gate, then Up).
   // Up to M = 64 the same Kernel-2 order on fragment-ordered weights streams
   // them fastest (1.16-1.6x the interleaved layout at M = 16 ... 64), except
-  // on wide matrices above M = 32, where the LDS-tiled kernel wins (7B M = 64:
-  // 60.3 us against 74.5 us on the packed layout).
+  // on wide matrices above M = 16, where the LDS-tiled kernel wins (7B: 54.8
+  // vs 59.7 us at M = 32, 60.3 vs 74.5 us at M = 64).
   const long long cus = cu_count > 0 ? cu_count : 256;
   const bool wide = (2 * N + 255) / 256 * 2 >= cus;
-  if (M <= 32 || (M <= 64 && !wide)) return 2;
+  if (M <= 16 || (M <= 64 && !wide)) return 2;
   return 1;
 }
 

@@ -198,7 +198,7 @@ swiglu_status_t swiglu_pack_fragments(swiglu_handle_t h, const void* W1, const v
 /* What swiglu_forward / _ex(AUTO) would run for this shape and layout, and
  * which layout the table recommends for the shape (the per-batch choice of
  * kernel family [RT §Contributi Chiave, item 2]): PACKED up to M = 64 (up to
- * M = 32 when N >= 16384 on 256 CUs), INTERLEAVED above (measured on
+ * M = 16 when N >= 16384 on 256 CUs), INTERLEAVED above (measured on
  * MI355X).  Any out-pointer may be NULL.
  * For variant GEMM pass layout SEPARATE to ask for the unfused GEMM config. */
 swiglu_status_t swiglu_query(swiglu_handle_t h, int64_t M, int64_t N, int64_t K,

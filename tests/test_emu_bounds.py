@@ -64,6 +64,8 @@ CASES = [
     (64, 18944, 64, [35, 8, 16, 54]),
     (256, 18944, 64, [39, 15, 53]),
     (512, 18944, 64, [22, 42]),
+    (32, 18944, 64, [1, 8, 16]),
+    (2048, 29568, 64, [44]),
     # FP8 / MXFP8 (K a multiple of 64): split-tail tiles at 1.5B M and N in
     # both orders and with block scales, the small-M tiles and the streaming
     # kernel at the 0.5B and decode shapes

@@ -149,8 +149,8 @@ def test_query_reports_a_valid_config(env):
             assert tile["variant"] == v
             # fragment-ordered weights up to M = 64, the interleaved layout above
             assert rec == (sw.LAYOUT_PACKED if M <= 64 else sw.LAYOUT_INTERLEAVED)
-    # wide matrices (N >= 16384 on 256 CUs): packed only up to M = 32
-    for M, rec_want in ((16, sw.LAYOUT_PACKED), (32, sw.LAYOUT_PACKED),
-                        (33, sw.LAYOUT_INTERLEAVED), (64, sw.LAYOUT_INTERLEAVED)):
+    # wide matrices (N >= 16384 on 256 CUs): packed only up to M = 16
+    for M, rec_want in ((1, sw.LAYOUT_PACKED), (16, sw.LAYOUT_PACKED),
+                        (17, sw.LAYOUT_INTERLEAVED), (64, sw.LAYOUT_INTERLEAVED)):
         assert sw.swiglu_query(h, M, 18944, 3584, sw.LAYOUT_SEPARATE)[2] == rec_want
         assert sw.swiglu_query_unfused(h, M, 4864, 896)["variant"] == sw.VARIANT_GEMM
