@@ -63,6 +63,10 @@ const ShapeEntry kTable[] = {
     {VAR_F8, 2048, 29568, 8192, 44},          // no split tail: 879 vs 957 us
     {VAR_SYNC, 1024, 18944, 3584, 8},         // 359 vs 375 us
     {VAR_F8_SYNC, 1024, 18944, 3584, 54},     // 184 vs 196 us
+    // decode-sized batches on the 0.5B and 1.5B matrices (tuner)
+    {VAR_SYNC, 64, 4864, 896, 12},            // 11.4 vs 14.6 us
+    {VAR_PACKED, 64, 4864, 896, 69},          // 8.3 vs 11.2 us
+    {VAR_PACKED, 16, 8960, 1536, 63},         // 14.3 vs 15.1 us
 };
 
 int find_config(int variant, int family, int bm, int bn, int waves) {
@@ -128,7 +132,8 @@ int select_config(int variant, long long M, long long N, long long K, int cu_cou
   if (variant == VAR_F8_PACKED) {
     const long long units = (2 * N + 31) / 32;
     if (M <= 16) return units >= 2 * cus ? 70 : 72;
-    return M <= 32 ? 75 : 76;
+    // 33-64 rows: 32-row blocks on narrower matrices (0.5B: 5.8 vs 6.9 us)
+    return (M <= 32 || !wide) ? 75 : 76;
   }
   if (variant == VAR_F8_SYNC) {
     // wide N: 128-row tiles from M = 33, the split 256-row tiles from M = 193
@@ -144,7 +149,8 @@ int select_config(int variant, long long M, long long N, long long K, int cu_cou
     // (narrow N at M <= 16: fewer than two one-wave workgroups per CU, the
     // split-K configuration wins: 7B decode share 12.2 vs 15.7 us)
     if (M <= 16) return (2 * N + 31) / 32 >= 2 * cus ? 52 : 51;
-    if (M <= 32) return 51;
+    // 17-32 rows on narrower matrices: the 64 x 128 tile (1.5B: 11.6 vs 15.6 us)
+    if (M <= 32) return wide ? 51 : 46;
     if (wide && M > 32 && M <= 384) return M <= 192 ? 45 : 44;
     return M <= 192 ? 46 : ((M <= 384 || few_big) ? 45 : 43);
   }
@@ -157,6 +163,15 @@ int select_config(int variant, long long M, long long N, long long K, int cu_cou
     if (variant == VAR_SYNC) return 8;
     return M <= 32 ? 1 : 35;
   }
+  if (M <= 64 && M > 16 && variant != VAR_SYNC) {
+    // 17-64 rows on narrower matrices: the small LDS-tiled tiles beat split-K
+    // streaming (tuner, 0.5B and 1.5B K and N: interleave 64 x 128 with 8
+    // stages at M = 32 7-8 %, 64 x 128 at M = 64 16-24 %; GEMM 64 x 64 with 8
+    // stages 28-32 %)
+    if (variant == VAR_GEMM) return 30;
+    return M <= 32 ? 27 : 3;
+  }
+  if (M <= 64 && variant == VAR_GEMM && !wide) return 30;  // 25 % at M = 16
   if (M <= 64) {
     // decode-sized batches: split-K weight streaming, 16-row MFMA blocks
     const int mt = M <= 16 ? 1 : (M <= 32 ? 2 : 4);

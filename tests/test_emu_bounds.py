@@ -65,6 +65,10 @@ CASES = [
     (256, 18944, 64, [39, 15, 53]),
     (512, 18944, 64, [22, 42]),
     (32, 18944, 64, [1, 8, 16]),
+    # decode-sized batches on the 0.5B and 1.5B matrices
+    (32, 8960, 1536, [27, 30, 46, 75]),
+    (64, 4864, 896, [3, 12, 30, 69, 75]),
+    (2048, 8960, 1536, [75]),
     (2048, 29568, 64, [44]),
     # FP8 / MXFP8 (K a multiple of 64): split-tail tiles at 1.5B M and N in
     # both orders and with block scales, the small-M tiles and the streaming
