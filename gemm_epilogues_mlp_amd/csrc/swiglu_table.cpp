@@ -67,6 +67,14 @@ const ShapeEntry kTable[] = {
     {VAR_SYNC, 64, 4864, 896, 12},            // 11.4 vs 14.6 us
     {VAR_PACKED, 64, 4864, 896, 69},          // 8.3 vs 11.2 us
     {VAR_PACKED, 16, 8960, 1536, 63},         // 14.3 vs 15.1 us
+    // batch sizes where tile rounds quantise against the wide-matrix rules
+    // (tuner, 7B K and N): three exact 128-row tiles beat two 256-row ones at
+    // M = 384 for sync and FP8; the 256 x 256 GEMM tile keeps M = 768 in one
+    // round (222 tiles, 198.5 us; 256 x 192 needs 297 tiles, 327.9 us)
+    {VAR_SYNC, 384, 18944, 3584, 8},          // 163.3 vs 205.9 us
+    {VAR_F8, 384, 18944, 3584, 45},           // 74.8 vs 94.7 us
+    {VAR_GEMM, 768, 18944, 3584, 14},         // 198.5 vs 327.9 us
+    {VAR_INTERLEAVE, 384, 18944, 3584, 40},   // 130.5 vs 137.1 us (the round model says 1)
 };
 
 int find_config(int variant, int family, int bm, int bn, int waves) {
@@ -77,6 +85,21 @@ int find_config(int variant, int family, int bm, int bn, int waves) {
       return i;
   }
   return -1;
+}
+
+// Estimated time of covering an M x N output with tiles of bm rows and bny
+// output columns, in rounds of one workgroup per CU weighted by tile size:
+// whole rounds, then a partial last round, which split configurations run as
+// quarter tiles (counted as half a round when it is at most a quarter full).
+// A 256-row tile costs 1.8 times a 128-row one: fitted to the tuner's
+// measurements on the 7B matrices (sync and FP8, M = 128 ... 1024), where it
+// picks the measured best at every point; used only up to M = 768, the range
+// measured for every family.
+double tile_rounds(long long M, long long N, int bm, int bny, bool split, long long cus) {
+  const long long tiles = ((M + bm - 1) / bm) * ((N + bny - 1) / bny);
+  const long long full = tiles / cus, tail = tiles % cus;
+  const double last = tail == 0 ? 0.0 : ((split && 4 * tail <= cus) ? 0.5 : 1.0);
+  return ((double)full + last) * (bm == 256 ? 1.8 : 1.0);
 }
 
 }  // namespace
@@ -138,7 +161,12 @@ int select_config(int variant, long long M, long long N, long long K, int cu_cou
   if (variant == VAR_F8_SYNC) {
     // wide N: 128-row tiles from M = 33, the split 256-row tiles from M = 193
     // (tuner: M = 64 46.7 vs 53.6 us, M = 128 24-30 %, M = 1024 10.5 %)
-    if (wide && M > 32) return M <= 192 ? 54 : 53;
+    if (wide && M > 32) {
+      if (M <= 128) return 54;
+      return M <= 768 && tile_rounds(M, N, 128, 128, false, cus) <
+                             tile_rounds(M, N, 256, 128, true, cus)
+                 ? 54 : 53;
+    }
     return M <= 192 ? 55 : (M <= 3072 ? 54 : 53);
   }
   if (variant == VAR_F8) {
@@ -151,7 +179,15 @@ int select_config(int variant, long long M, long long N, long long K, int cu_cou
     if (M <= 16) return (2 * N + 31) / 32 >= 2 * cus ? 52 : 51;
     // 17-32 rows on narrower matrices: the 64 x 128 tile (1.5B: 11.6 vs 15.6 us)
     if (M <= 32) return wide ? 51 : 46;
-    if (wide && M > 32 && M <= 384) return M <= 192 ? 45 : 44;
+    // wide N from M = 33: 128-row tiles, or the split 256-row tiles where
+    // they take fewer weighted rounds (M = 192: 52.9 vs 71.9 us; M = 320:
+    // 128-row 71.7 vs 91.8 us)
+    if (wide && M > 32) {
+      if (M <= 128) return 45;
+      return M <= 768 && tile_rounds(M, N, 128, 128, false, cus) <
+                             tile_rounds(M, N, 256, 128, true, cus)
+                 ? 45 : 43;
+    }
     return M <= 192 ? 46 : ((M <= 384 || few_big) ? 45 : 43);
   }
   if (M <= 64 && M > 16 && wide) {
@@ -184,18 +220,29 @@ int select_config(int variant, long long M, long long N, long long K, int cu_cou
   // which won even where they leave CUs idle (M = 512: 140 tiles on 256 CUs).
   // narrow N (few_big above): the 128-row tiles
   if (variant == VAR_GEMM) {
-    // wide N (tuner, 7B and 72B): 128 x 128 to M = 192 (21-39 %), 256 x 128
-    // to M = 384 (19 %), 256 x 192 to M = 768 (5 %)
-    if (wide) return M <= 192 ? 16 : (M <= 384 ? 15 : (M <= 768 ? 22 : 41));
+    // wide N (tuner, 7B and 72B): 128 x 128 to M = 128 (21-39 %), 256 x 128
+    // to M = 256 (19 %, 8.7 % at M = 192), 256 x 192 to M = 512 (32.5 % at
+    // M = 384, 5 % at M = 512)
+    if (wide) return M <= 128 ? 16 : (M <= 256 ? 15 : (M <= 512 ? 22 : 41));
     return M <= 192 ? 30 : (M <= 384 ? 16 : 41);
   }
   if (variant == VAR_SYNC) {
-    // wide N (tuner): 128 x 128 to M = 192 (24-44 %), 256 x 128 with 4 x 2
-    // waves to M = 384 (19 %)
-    if (wide) return M <= 192 ? 8 : (M <= 384 ? 39 : 42);
+    // wide N (tuner): 128 x 128 to M = 128 (24-44 %), then 128-row or split
+    // 256-row tiles by weighted rounds (M = 192: 256-row 126.6 vs 142.6 us;
+    // M = 320 and 384: 128-row 150.7 and 163.0 vs 173.6 and 205.9 us)
+    if (wide) {
+      if (M <= 128) return 8;
+      return M <= 768 && tile_rounds(M, N, 128, 128, false, cus) <
+                             tile_rounds(M, N, 256, 128, true, cus)
+                 ? 8 : 42;
+    }
     return M <= 192 ? 29 : ((M <= 384 || few_big) ? 8 : 42);
   }
-  if (wide && M <= 384) return M <= 192 ? (K >= 6144 ? 31 : 35) : 21;
+  if (wide && M <= 256) return M <= 192 ? (K >= 6144 ? 31 : 35) : 21;
+  if (wide)  // 128 x 256 or the split 256-row tiles by weighted rounds (M = 320: 1)
+    return M <= 768 && tile_rounds(M, N, 128, 128, false, cus) <
+                           tile_rounds(M, N, 256, 128, true, cus)
+               ? 1 : 40;
   return M <= 192 ? 3 : ((M <= 384 || few_big) ? 1 : 40);
 }
 

@@ -69,6 +69,9 @@ CASES = [
     (32, 8960, 1536, [27, 30, 46, 75]),
     (64, 4864, 896, [3, 12, 30, 69, 75]),
     (2048, 8960, 1536, [75]),
+    (192, 18944, 64, [42, 15, 44, 35]),
+    (384, 18944, 64, [8, 45, 22, 40]),
+    (768, 18944, 64, [14, 40, 42, 43]),
     (2048, 29568, 64, [44]),
     # FP8 / MXFP8 (K a multiple of 64): split-tail tiles at 1.5B M and N in
     # both orders and with block scales, the small-M tiles and the streaming

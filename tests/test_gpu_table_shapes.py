@@ -25,7 +25,8 @@ SHARDS = [(4096, 8192, 3696), (8192, 3584, 2368), (2048, 1536, 1120), (128, 896,
           (16, 3584, 2368),
           (32, 8192, 29568), (64, 8192, 29568), (128, 8192, 29568), (128, 3584, 18944),
           (256, 3584, 18944), (64, 3584, 18944), (512, 3584, 18944), (32, 3584, 18944),
-          (1024, 3584, 18944), (32, 1536, 8960), (64, 896, 4864)]
+          (1024, 3584, 18944), (32, 1536, 8960), (64, 896, 4864), (192, 3584, 18944),
+          (384, 3584, 18944), (768, 3584, 18944), (320, 3584, 18944)]
 
 
 @pytest.fixture(scope="module")
