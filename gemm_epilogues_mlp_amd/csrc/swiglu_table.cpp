@@ -91,15 +91,18 @@ int find_config(int variant, int family, int bm, int bn, int waves) {
 // output columns, in rounds of one workgroup per CU weighted by tile size:
 // whole rounds, then a partial last round, which split configurations run as
 // quarter tiles (counted as half a round when it is at most a quarter full).
-// A 256-row tile costs 1.8 times a 128-row one: fitted to the tuner's
-// measurements on the 7B matrices (sync and FP8, M = 128 ... 1024), where it
-// picks the measured best at every point; used only up to M = 768, the range
-// measured for every family.
-double tile_rounds(long long M, long long N, int bm, int bny, bool split, long long cus) {
+// A 256-row tile costs 1.8 times a 128-row one at K = 3584 and 1.4 times at
+// K = 8192 (its fixed per-tile cost is spread over a longer K loop): fitted to
+// the tuner's measurements on the 7B and 72B matrices (sync, FP8 and
+// interleave, M = 160 ... 1024), where it picks the measured best or a
+// configuration within 2 % of it; used only up to M = 768, the range measured
+// for every family.
+double tile_rounds(long long M, long long N, long long K, int bm, int bny, bool split,
+                   long long cus) {
   const long long tiles = ((M + bm - 1) / bm) * ((N + bny - 1) / bny);
   const long long full = tiles / cus, tail = tiles % cus;
   const double last = tail == 0 ? 0.0 : ((split && 4 * tail <= cus) ? 0.5 : 1.0);
-  return ((double)full + last) * (bm == 256 ? 1.8 : 1.0);
+  return ((double)full + last) * (bm == 256 ? (K >= 6144 ? 1.4 : 1.8) : 1.0);
 }
 
 }  // namespace
@@ -163,8 +166,8 @@ int select_config(int variant, long long M, long long N, long long K, int cu_cou
     // (tuner: M = 64 46.7 vs 53.6 us, M = 128 24-30 %, M = 1024 10.5 %)
     if (wide && M > 32) {
       if (M <= 128) return 54;
-      return M <= 768 && tile_rounds(M, N, 128, 128, false, cus) <
-                             tile_rounds(M, N, 256, 128, true, cus)
+      return M <= 768 && tile_rounds(M, N, K, 128, 128, false, cus) <
+                             tile_rounds(M, N, K, 256, 128, true, cus)
                  ? 54 : 53;
     }
     return M <= 192 ? 55 : (M <= 3072 ? 54 : 53);
@@ -184,8 +187,8 @@ int select_config(int variant, long long M, long long N, long long K, int cu_cou
     // 128-row 71.7 vs 91.8 us)
     if (wide && M > 32) {
       if (M <= 128) return 45;
-      return M <= 768 && tile_rounds(M, N, 128, 128, false, cus) <
-                             tile_rounds(M, N, 256, 128, true, cus)
+      return M <= 768 && tile_rounds(M, N, K, 128, 128, false, cus) <
+                             tile_rounds(M, N, K, 256, 128, true, cus)
                  ? 45 : 43;
     }
     return M <= 192 ? 46 : ((M <= 384 || few_big) ? 45 : 43);
@@ -232,16 +235,16 @@ int select_config(int variant, long long M, long long N, long long K, int cu_cou
     // M = 320 and 384: 128-row 150.7 and 163.0 vs 173.6 and 205.9 us)
     if (wide) {
       if (M <= 128) return 8;
-      return M <= 768 && tile_rounds(M, N, 128, 128, false, cus) <
-                             tile_rounds(M, N, 256, 128, true, cus)
+      return M <= 768 && tile_rounds(M, N, K, 128, 128, false, cus) <
+                             tile_rounds(M, N, K, 256, 128, true, cus)
                  ? 8 : 42;
     }
     return M <= 192 ? 29 : ((M <= 384 || few_big) ? 8 : 42);
   }
   if (wide && M <= 256) return M <= 192 ? (K >= 6144 ? 31 : 35) : 21;
   if (wide)  // 128 x 256 or the split 256-row tiles by weighted rounds (M = 320: 1)
-    return M <= 768 && tile_rounds(M, N, 128, 128, false, cus) <
-                           tile_rounds(M, N, 256, 128, true, cus)
+    return M <= 768 && tile_rounds(M, N, K, 128, 128, false, cus) <
+                           tile_rounds(M, N, K, 256, 128, true, cus)
                ? 1 : 40;
   return M <= 192 ? 3 : ((M <= 384 || few_big) ? 1 : 40);
 }
