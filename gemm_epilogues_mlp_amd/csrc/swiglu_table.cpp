@@ -123,6 +123,17 @@ int select_config(int variant, long long M, long long N, long long K, int cu_cou
   // chosen for narrower matrices (tuner, 7B and 72B K and N: M = 128 35-38 %,
   // M = 256 37 % faster in bf16; FP8 20-28 %, MXFP8 10-21 %).
   const bool wide = (2 * N + 255) / 256 * 2 >= cus;
+  // Mid-width N (not wide, but 64-wide W_fused column tiles alone give every
+  // CU a tile: the 1.5B and 3B matrices, not the 0.5B one): from M = 65 one
+  // band of 128-row tiles already fills the chip, and the 64-row tiles' second
+  // pass over W_fused costs more than their parallelism gains (tuner, 1.5B and
+  // 3B, M = 80 ... 192: interleave 19-23 %, sync 9-28 %, GEMM 4-17 %).
+  const bool mid = !wide && (2 * N + 63) / 64 >= cus;
+  // On mid-width N from M = 129 to 160, 64-row tiles still win while all of
+  // them fit in one round of four workgroups per CU (1.5B, M = 144: sync
+  // 31.3 vs 34.7 us, GEMM 36.8 vs 39.6 us); past that (3B, M = 160: 1032
+  // tiles) the 128 x 128 tiles do (sync 44.5 vs 61.3 us, GEMM 49.8 vs 59.5 us).
+  const bool one_round64 = ((M + 63) / 64) * ((2 * N + 63) / 64) <= 4 * cus;
   // FP8 sync order (measured on the five workloads: 128 x 128 tiles won at
   // M = 2048, the split 256-row tiles at M = 4096 and 8192)
   // MXFP8: 64 x 128 tiles for small M, the split 256 x 256 tiles above
@@ -170,6 +181,9 @@ int select_config(int variant, long long M, long long N, long long K, int cu_cou
                              tile_rounds(M, N, K, 256, 128, true, cus)
                  ? 54 : 53;
     }
+    // mid-width N around M = 768: three 256-row bands fill one round where
+    // six 128-row bands need two (tuner, 1.5B: 36.3 vs 41.3 us; 3B 3 %)
+    if (mid && M > 640 && M <= 1024) return 53;
     return M <= 192 ? 55 : (M <= 3072 ? 54 : 53);
   }
   if (variant == VAR_F8) {
@@ -227,6 +241,15 @@ int select_config(int variant, long long M, long long N, long long K, int cu_cou
     // to M = 256 (19 %, 8.7 % at M = 192), 256 x 192 to M = 512 (32.5 % at
     // M = 384, 5 % at M = 512)
     if (wide) return M <= 128 ? 16 : (M <= 256 ? 15 : (M <= 512 ? 22 : 41));
+    // mid-width N: 64 x 64 with the shallow ring to M = 96, split-K streaming
+    // 64 x 128 to M = 128 (8.5-10 %), 128 x 128 to M = 192 (3B: 49.7 vs
+    // 59.5 us at M = 160), and 256 x 128 from M = 385 while those tiles fit
+    // in two rounds (1.5B: 72.7 vs 85.1 us at M = 512, 76.5 vs 88.4 us at
+    // M = 768; 3B at M = 768 needs three: 144.2 vs 107.8 us for 256 x 256)
+    if (mid && M <= 96) return 17;
+    if (mid && M <= 128) return 20;
+    if (mid && M <= 192 && (M > 160 || !one_round64)) return 16;
+    if (mid && M > 384 && ((M + 255) / 256) * ((N + 127) / 128) <= cus) return 15;
     return M <= 192 ? 30 : (M <= 384 ? 16 : 41);
   }
   if (variant == VAR_SYNC) {
@@ -239,6 +262,12 @@ int select_config(int variant, long long M, long long N, long long K, int cu_cou
                              tile_rounds(M, N, K, 256, 128, true, cus)
                  ? 8 : 42;
     }
+    // mid-width N: 128 x 64 to M = 128 (3B: 43.0 vs 53.3 us), then 64 x 64
+    // while those fit one round, else 128 x 128 (3B, M = 160: 44.4 vs 61.3 us)
+    if (mid && M <= 192) return M <= 128 ? 9 : ((M <= 160 && one_round64) ? 10 : 8);
+    // narrower matrices to M = 96: split-K streaming, 32-row blocks (0.5B:
+    // 11.3 vs 14.0 us at M = 96)
+    if (!wide && !mid && M <= 96) return 12;
     return M <= 192 ? 29 : ((M <= 384 || few_big) ? 8 : 42);
   }
   if (wide && M <= 256) return M <= 192 ? (K >= 6144 ? 31 : 35) : 21;
@@ -246,6 +275,12 @@ int select_config(int variant, long long M, long long N, long long K, int cu_cou
     return M <= 768 && tile_rounds(M, N, K, 128, 128, false, cus) <
                            tile_rounds(M, N, K, 256, 128, true, cus)
                ? 1 : 40;
+  // mid-width N: 128 x 64 to M = 128, 128 x 128 to M = 192 (1.5B M = 96
+  // 21.7 vs 27.3 us; 3B M = 160 33.6 vs 41.7 us, M = 192 37.1 vs 45.1 us)
+  if (mid && M <= 192) return M <= 128 ? 2 : 1;
+  // narrower matrices, M = 65 ... 96: 64 x 64 with the deep stage ring (7B
+  // share under 8-way tensor parallelism, M = 96: 25.8 vs 30.7 us)
+  if (!wide && !mid && M <= 96) return 27;
   return M <= 192 ? 3 : ((M <= 384 || few_big) ? 1 : 40);
 }
 
