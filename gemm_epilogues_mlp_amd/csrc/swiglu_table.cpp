@@ -134,6 +134,12 @@ int select_config(int variant, long long M, long long N, long long K, int cu_cou
   // 31.3 vs 34.7 us, GEMM 36.8 vs 39.6 us); past that (3B, M = 160: 1032
   // tiles) the 128 x 128 tiles do (sync 44.5 vs 61.3 us, GEMM 49.8 vs 59.5 us).
   const bool one_round64 = ((M + 63) / 64) * ((2 * N + 63) / 64) <= 4 * cus;
+  // Mid-width N with a long K loop (14B: K = 5120, N = 13824): from M = 129
+  // (interleave: 257) to 768 the tiles follow the wide-matrix rules, because
+  // a 256-row tile's fixed cost is spread over the long loop (tuner, M = 384:
+  // interleave 109.7 vs 187.2 us, sync 156.8 vs 228.7 us, FP8 70.6 vs 111.3
+  // us; M = 192: FP8 sync 64.4 vs 92.3 us).
+  const bool long_k = mid && K >= 4096 && M <= 768;
   // FP8 sync order (measured on the five workloads: 128 x 128 tiles won at
   // M = 2048, the split 256-row tiles at M = 4096 and 8192)
   // MXFP8: 64 x 128 tiles for small M, the split 256 x 256 tiles above
@@ -175,15 +181,15 @@ int select_config(int variant, long long M, long long N, long long K, int cu_cou
   if (variant == VAR_F8_SYNC) {
     // wide N: 128-row tiles from M = 33, the split 256-row tiles from M = 193
     // (tuner: M = 64 46.7 vs 53.6 us, M = 128 24-30 %, M = 1024 10.5 %)
-    if (wide && M > 32) {
-      if (M <= 128) return 54;
+    if ((wide && M > 32) || (long_k && M > 128)) {
+      if (M <= 128 || (!wide && M > 512)) return 54;  // 14B, M = 768: 160.5 vs 192.8 us
       return M <= 768 && tile_rounds(M, N, K, 128, 128, false, cus) <
                              tile_rounds(M, N, K, 256, 128, true, cus)
                  ? 54 : 53;
     }
     // mid-width N around M = 768: three 256-row bands fill one round where
     // six 128-row bands need two (tuner, 1.5B: 36.3 vs 41.3 us; 3B 3 %)
-    if (mid && M > 640 && M <= 1024) return 53;
+    if (mid && K < 4096 && M > 640 && M <= 1024) return 53;
     return M <= 192 ? 55 : (M <= 3072 ? 54 : 53);
   }
   if (variant == VAR_F8) {
@@ -199,7 +205,7 @@ int select_config(int variant, long long M, long long N, long long K, int cu_cou
     // wide N from M = 33: 128-row tiles, or the split 256-row tiles where
     // they take fewer weighted rounds (M = 192: 52.9 vs 71.9 us; M = 320:
     // 128-row 71.7 vs 91.8 us)
-    if (wide && M > 32) {
+    if ((wide && M > 32) || (long_k && M > 128 && M <= 512)) {
       if (M <= 128) return 45;
       return M <= 768 && tile_rounds(M, N, K, 128, 128, false, cus) <
                              tile_rounds(M, N, K, 256, 128, true, cus)
@@ -246,6 +252,10 @@ int select_config(int variant, long long M, long long N, long long K, int cu_cou
     // 59.5 us at M = 160), and 256 x 128 from M = 385 while those tiles fit
     // in two rounds (1.5B: 72.7 vs 85.1 us at M = 512, 76.5 vs 88.4 us at
     // M = 768; 3B at M = 768 needs three: 144.2 vs 107.8 us for 256 x 256)
+    // long K: 256 x 128 to M = 384, 256 x 192 from M = 641 (14B: 170.8 vs
+    // 245.2 us at M = 384, 234.3 vs 252.2 us at M = 768)
+    if (long_k && M > 256 && M <= 384) return 15;
+    if (long_k && M > 640) return 22;
     if (mid && M <= 96) return 17;
     if (mid && M <= 128) return 20;
     if (mid && M <= 192 && (M > 160 || !one_round64)) return 16;
@@ -256,7 +266,7 @@ int select_config(int variant, long long M, long long N, long long K, int cu_cou
     // wide N (tuner): 128 x 128 to M = 128 (24-44 %), then 128-row or split
     // 256-row tiles by weighted rounds (M = 192: 256-row 126.6 vs 142.6 us;
     // M = 320 and 384: 128-row 150.7 and 163.0 vs 173.6 and 205.9 us)
-    if (wide) {
+    if (wide || (long_k && M > 128)) {
       if (M <= 128) return 8;
       return M <= 768 && tile_rounds(M, N, K, 128, 128, false, cus) <
                              tile_rounds(M, N, K, 256, 128, true, cus)
@@ -271,7 +281,10 @@ int select_config(int variant, long long M, long long N, long long K, int cu_cou
     return M <= 192 ? 29 : ((M <= 384 || few_big) ? 8 : 42);
   }
   if (wide && M <= 256) return M <= 192 ? (K >= 6144 ? 31 : 35) : 21;
-  if (wide)  // 128 x 256 or the split 256-row tiles by weighted rounds (M = 320: 1)
+  // long K on mid-width N: 256 x 128 (split only from M = 385), 256 x 192 from
+  // M = 641 (14B: M = 384 114.3 vs 187.2 us, M = 768 225.7 vs 245.5 us)
+  if (long_k && M > 256) return M <= 384 ? 31 : (M <= 640 ? 40 : 21);
+  if (wide)  // 128 x 256 or the split 256-row tiles by weighted rounds
     return M <= 768 && tile_rounds(M, N, K, 128, 128, false, cus) <
                            tile_rounds(M, N, K, 256, 128, true, cus)
                ? 1 : 40;
