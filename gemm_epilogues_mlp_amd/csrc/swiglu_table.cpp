@@ -91,18 +91,19 @@ int find_config(int variant, int family, int bm, int bn, int waves) {
 // output columns, in rounds of one workgroup per CU weighted by tile size:
 // whole rounds, then a partial last round, which split configurations run as
 // quarter tiles (counted as half a round when it is at most a quarter full).
-// A 256-row tile costs 1.8 times a 128-row one at K = 3584 and 1.4 times at
-// K = 8192 (its fixed per-tile cost is spread over a longer K loop): fitted to
+// A 256-row tile costs 1.8 times a 128-row one at K = 3584 and 1.4 times from
+// K = 4096 (its fixed per-tile cost is spread over a longer K loop): fitted to
 // the tuner's measurements on the 7B and 72B matrices (sync, FP8 and
-// interleave, M = 160 ... 1024), where it picks the measured best or a
-// configuration within 2 % of it; used only up to M = 768, the range measured
-// for every family.
+// interleave, M = 160 ... 1024; the 32B matrices at K = 5120 follow the 72B
+// weight: M = 384 sync 307.7 vs 348.1 us, FP8 140.2 vs 163.2 us), where it
+// picks the measured best or a configuration within 2 % of it; used only up
+// to M = 768, the range measured for every family.
 double tile_rounds(long long M, long long N, long long K, int bm, int bny, bool split,
                    long long cus) {
   const long long tiles = ((M + bm - 1) / bm) * ((N + bny - 1) / bny);
   const long long full = tiles / cus, tail = tiles % cus;
   const double last = tail == 0 ? 0.0 : ((split && 4 * tail <= cus) ? 0.5 : 1.0);
-  return ((double)full + last) * (bm == 256 ? (K >= 6144 ? 1.4 : 1.8) : 1.0);
+  return ((double)full + last) * (bm == 256 ? (K >= 4096 ? 1.4 : 1.8) : 1.0);
 }
 
 }  // namespace
@@ -267,7 +268,7 @@ int select_config(int variant, long long M, long long N, long long K, int cu_cou
     // 256-row tiles by weighted rounds (M = 192: 256-row 126.6 vs 142.6 us;
     // M = 320 and 384: 128-row 150.7 and 163.0 vs 173.6 and 205.9 us)
     if (wide || (long_k && M > 128)) {
-      if (M <= 128) return 8;
+      if (M <= 128 || (!wide && M > 512)) return 8;  // 14B, M = 768: 339.9 vs 357.7 us
       return M <= 768 && tile_rounds(M, N, K, 128, 128, false, cus) <
                              tile_rounds(M, N, K, 256, 128, true, cus)
                  ? 8 : 42;
@@ -280,7 +281,7 @@ int select_config(int variant, long long M, long long N, long long K, int cu_cou
     if (!wide && !mid && M <= 96) return 12;
     return M <= 192 ? 29 : ((M <= 384 || few_big) ? 8 : 42);
   }
-  if (wide && M <= 256) return M <= 192 ? (K >= 6144 ? 31 : 35) : 21;
+  if (wide && M <= 256) return M <= 192 ? (K >= 4096 ? 31 : 35) : 21;
   // long K on mid-width N: 256 x 128 (split only from M = 385), 256 x 192 from
   // M = 641 (14B: M = 384 114.3 vs 187.2 us, M = 768 225.7 vs 245.5 us)
   if (long_k && M > 256) return M <= 384 ? 31 : (M <= 640 ? 40 : 21);

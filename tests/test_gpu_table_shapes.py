@@ -4,7 +4,7 @@ layout and input format, and the unfused baseline:
 
 * one GPU's share of the Qwen2.5-shaped MLPs under 8-way tensor parallelism
   (W_fused columns split eight ways on Gate/Up pair boundaries: [M, N/8, K]);
-* mid-size batches (M = 32 ... 1024) on the 7B and 72B matrices, and on the
+* mid-size batches (M = 32 ... 1024) on the 7B, 32B and 72B matrices, and on the
   1.5B, 3B and 14B ones (Qwen2.5-3B: K = 2048, N = 11008; 14B: K = 5120,
   N = 13824).
 
@@ -22,7 +22,7 @@ from gpu_util import assert_parity, decode, dev, empty_poisoned, host, log
 pytestmark = pytest.mark.gpu
 
 # (M, K, N): 72B, 7B prefill, 1.5B, 0.5B and 7B decode shares; then mid-size
-# batches on the 72B, 7B, 1.5B, 3B and 14B matrices
+# batches on the 72B, 32B, 7B, 1.5B, 3B and 14B matrices
 SHARDS = [(4096, 8192, 3696), (8192, 3584, 2368), (2048, 1536, 1120), (128, 896, 608),
           (16, 3584, 2368),
           (32, 8192, 29568), (64, 8192, 29568), (128, 8192, 29568), (128, 3584, 18944),
@@ -30,7 +30,8 @@ SHARDS = [(4096, 8192, 3696), (8192, 3584, 2368), (2048, 1536, 1120), (128, 896,
           (1024, 3584, 18944), (32, 1536, 8960), (64, 896, 4864), (192, 3584, 18944),
           (384, 3584, 18944), (768, 3584, 18944), (320, 3584, 18944),
           (96, 1536, 8960), (160, 2048, 11008), (768, 1536, 8960), (96, 896, 4864),
-          (96, 3584, 2368), (192, 5120, 13824), (384, 5120, 13824)]
+          (96, 3584, 2368), (192, 5120, 13824), (384, 5120, 13824), (128, 5120, 27648),
+          (384, 5120, 27648)]
 
 
 @pytest.fixture(scope="module")
