@@ -141,6 +141,10 @@ int select_config(int variant, long long M, long long N, long long K, int cu_cou
   // interleave 109.7 vs 187.2 us, sync 156.8 vs 228.7 us, FP8 70.6 vs 111.3
   // us; M = 192: FP8 sync 64.4 vs 92.3 us).
   const bool long_k = mid && K >= 4096 && M <= 768;
+  // Narrower, but 64-wide W_fused column tiles still cover half of the CUs,
+  // with a long K loop (72B share under 4-way tensor parallelism; not the
+  // 8-way one, N = 3696, where the rules for narrow matrices stay best).
+  const bool half_long_k = !wide && !mid && K >= 4096 && 2 * ((2 * N + 63) / 64) >= cus;
   // FP8 sync order (measured on the five workloads: 128 x 128 tiles won at
   // M = 2048, the split 256-row tiles at M = 4096 and 8192)
   // MXFP8: 64 x 128 tiles for small M, the split 256 x 256 tiles above
@@ -279,6 +283,9 @@ int select_config(int variant, long long M, long long N, long long K, int cu_cou
     // narrower matrices to M = 96: split-K streaming, 32-row blocks (0.5B:
     // 11.3 vs 14.0 us at M = 96)
     if (!wide && !mid && M <= 96) return 12;
+    // narrower matrices with a long K loop, M = 97 ... 128: split-K streaming,
+    // 64-row blocks (72B share under 4-way tensor parallelism: 97.1 vs 109.7 us)
+    if (half_long_k && M <= 128) return 13;
     return M <= 192 ? 29 : ((M <= 384 || few_big) ? 8 : 42);
   }
   if (wide && M <= 256) return M <= 192 ? (K >= 4096 ? 31 : 35) : 21;
@@ -295,6 +302,10 @@ int select_config(int variant, long long M, long long N, long long K, int cu_cou
   // narrower matrices, M = 65 ... 96: 64 x 64 with the deep stage ring (7B
   // share under 8-way tensor parallelism, M = 96: 25.8 vs 30.7 us)
   if (!wide && !mid && M <= 96) return 27;
+  // narrower matrices with a long K loop, M = 257 ... 768: 256 x 192 tiles
+  // (72B share under 4-way tensor parallelism: M = 384 134.3 vs 142.3 us,
+  // M = 768 170.3 vs 185.5 us)
+  if (half_long_k && M > 256 && M <= 768) return 21;
   return M <= 192 ? 3 : ((M <= 384 || few_big) ? 1 : 40);
 }
 
