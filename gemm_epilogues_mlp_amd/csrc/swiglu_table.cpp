@@ -286,6 +286,8 @@ int select_config(int variant, long long M, long long N, long long K, int cu_cou
     // narrower matrices with a long K loop, M = 97 ... 128: split-K streaming,
     // 64-row blocks (72B share under 4-way tensor parallelism: 97.1 vs 109.7 us)
     if (half_long_k && M <= 128) return 13;
+    // narrower still (72B 8-way share, N = 3696): 32-row blocks (82.4 vs 116.2 us)
+    if (!wide && !mid && K >= 4096 && M <= 128) return 12;
     return M <= 192 ? 29 : ((M <= 384 || few_big) ? 8 : 42);
   }
   if (wide && M <= 256) return M <= 192 ? (K >= 4096 ? 31 : 35) : 21;

@@ -31,7 +31,7 @@ SHARDS = [(4096, 8192, 3696), (8192, 3584, 2368), (2048, 1536, 1120), (128, 896,
           (384, 3584, 18944), (768, 3584, 18944), (320, 3584, 18944),
           (96, 1536, 8960), (160, 2048, 11008), (768, 1536, 8960), (96, 896, 4864),
           (96, 3584, 2368), (192, 5120, 13824), (384, 5120, 13824), (128, 5120, 27648),
-          (384, 5120, 27648), (128, 8192, 7392), (384, 8192, 7392)]
+          (384, 5120, 27648), (128, 8192, 7392), (384, 8192, 7392), (128, 8192, 3696)]
 
 
 @pytest.fixture(scope="module")
