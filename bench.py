@@ -2,8 +2,9 @@
 """Benchmark of the fused SwiGLU MLP GEMM on one MI355X.
 
 One step = one fused forward Y = SiLU(A W1) (.) (A W2) over one batch of the
-chosen Qwen2.5-shaped workload (default: the Qwen2.5-1.5B MLP, M=2048, K=1536,
-N=8960), inputs already resident in HBM.  Batches rotate through enough copies
+chosen Qwen2.5-shaped workload (default: the Qwen2.5-72B MLP, M=4096, K=8192,
+N=29568, the largest of the five and the MFMA-bound regime), inputs already
+resident in HBM.  Batches rotate through enough copies
 of {A, W, Y} to exceed the 256 MB Infinity Cache several times, so every step
 streams its operands from HBM.  Prints ONE JSON line.
 
@@ -32,12 +33,18 @@ def kernel_source_hash() -> str:
     return hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
 
 
+def _workloads():
+    from gemm_epilogues_mlp_amd import inputs as I
+    return I.WORKLOADS
+
+
 def parse():
     p = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=200)
     p.add_argument("--warmup", type=int, default=20)
-    p.add_argument("--workload", default="qwen2.5-1.5b-mlp")
+    p.add_argument("--workload", default="qwen2.5-72b-mlp",
+                   choices=[w.name for w in _workloads()])
     p.add_argument("--layout", choices=["auto", "separate", "interleaved", "packed"],
                    default="auto")
     p.add_argument("--config", type=int, default=-1, help="force a fused config id")

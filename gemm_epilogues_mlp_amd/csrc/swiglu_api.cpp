@@ -3,7 +3,7 @@
 // contract of each entry point.
 #include "swiglu.h"
 
-#include <hip/hip_runtime_api.h>
+#include <hip/hip_runtime.h>
 #include <stdio.h>
 #include <stdlib.h>
 #include <string.h>
@@ -177,7 +177,8 @@ swiglu_status_t launch(const swiglu_ctx* h, const KernelConfig* cfg, int id,
   if (h->log)
     fprintf(stderr, "[swiglu] M=%d N=%d K=%d -> config %d (variant %d family %d %dx%d)\n", a.M,
             a.N, a.K, id, cfg->variant, cfg->family, cfg->bm, cfg->bn);
-  (void)hipGetLastError();  // clear a stale error so the check below is ours
+  // the launch functions return the status of their own launch (hipLaunchKernel),
+  // so an error pending from a caller's earlier HIP call is left alone
   return cfg->launch(a) == hipSuccess ? SWIGLU_OK : SWIGLU_ERR_LAUNCH;
 }
 
@@ -237,6 +238,41 @@ int fp8_family(int variant) {
   if (variant == SWIGLU_VARIANT_FP8_PACKED) return VAR_F8_PACKED;
   if (variant == SWIGLU_VARIANT_MXFP8_PACKED) return VAR_MX_PACKED;  // queries only
   return -1;
+}
+
+// The unfused baseline on a Gate/Up buffer `gu` of 4 M N bytes (G then U,
+// bf16): two GEMM launches and the separate gate kernel.
+swiglu_status_t unfused(const swiglu_ctx* h, const void* A, const void* W1, const void* W2,
+                        void* gu, void* Y, int64_t M, int64_t N, int64_t K,
+                        int32_t gemm_config_id, hipStream_t stream) {
+  bool noop = false;
+  swiglu_status_t st =
+      check_forward(h, A, W1, W2, Y, M, N, K, SWIGLU_LAYOUT_SEPARATE, &noop);
+  if (st != SWIGLU_OK) return st;
+  int id = gemm_config_id;
+  if (id >= 0) {
+    const KernelConfig* c = config_at(id);
+    if (!c || c->variant != VAR_GEMM) return SWIGLU_ERR_INVALID_ARG;
+  }
+  if (noop) return SWIGLU_OK;
+  if (!gu) return SWIGLU_ERR_INVALID_ARG;
+  if (!aligned16(gu)) return SWIGLU_ERR_UNSUPPORTED;
+  const long long wsb = 4LL * M * N;
+  const long long wb = 2LL * K * N;
+  if (overlaps(gu, wsb, Y, 2LL * M * N) || overlaps(gu, wsb, A, 2LL * M * K) ||
+      overlaps(gu, wsb, W1, wb) || overlaps(gu, wsb, W2, wb))
+    return SWIGLU_ERR_INVALID_ARG;
+  if (id < 0) id = choose(h, VAR_GEMM, M, N, K);
+  if (id < 0) return SWIGLU_ERR_UNSUPPORTED;
+  uint16_t* G = (uint16_t*)gu;
+  uint16_t* U = G + (size_t)M * (size_t)N;
+  st = run(h, config_at(id), id, A, W1, nullptr, G, M, N, K, stream);
+  if (st != SWIGLU_OK) return st;
+  st = run(h, config_at(id), id, A, W2, nullptr, U, M, N, K, stream);
+  if (st != SWIGLU_OK) return st;
+  if (launch_gate(G, U, (uint16_t*)Y, (size_t)M * (size_t)N, stream, h->cu_count) != hipSuccess)
+    return SWIGLU_ERR_LAUNCH;
+  return SWIGLU_OK;
 }
 
 }  // namespace
@@ -311,35 +347,7 @@ swiglu_status_t swiglu_forward_unfused(swiglu_handle_t h, const void* A, const v
                                        const void* W2, void* workspace, void* Y, int64_t M,
                                        int64_t N, int64_t K, int32_t gemm_config_id,
                                        hipStream_t stream) {
-  bool noop = false;
-  swiglu_status_t st =
-      check_forward(h, A, W1, W2, Y, M, N, K, SWIGLU_LAYOUT_SEPARATE, &noop);
-  if (st != SWIGLU_OK) return st;
-  int id = gemm_config_id;
-  if (id >= 0) {
-    const KernelConfig* c = config_at(id);
-    if (!c || c->variant != VAR_GEMM) return SWIGLU_ERR_INVALID_ARG;
-  }
-  if (noop) return SWIGLU_OK;
-  if (!workspace) return SWIGLU_ERR_INVALID_ARG;
-  if (!aligned16(workspace)) return SWIGLU_ERR_UNSUPPORTED;
-  const long long wsb = 4LL * M * N;
-  const long long wb = 2LL * K * N;
-  if (overlaps(workspace, wsb, Y, 2LL * M * N) || overlaps(workspace, wsb, A, 2LL * M * K) ||
-      overlaps(workspace, wsb, W1, wb) || overlaps(workspace, wsb, W2, wb))
-    return SWIGLU_ERR_INVALID_ARG;
-  if (id < 0) id = choose(h, VAR_GEMM, M, N, K);
-  if (id < 0) return SWIGLU_ERR_UNSUPPORTED;
-  uint16_t* G = (uint16_t*)workspace;
-  uint16_t* U = G + (size_t)M * (size_t)N;
-  st = run(h, config_at(id), id, A, W1, nullptr, G, M, N, K, stream);
-  if (st != SWIGLU_OK) return st;
-  st = run(h, config_at(id), id, A, W2, nullptr, U, M, N, K, stream);
-  if (st != SWIGLU_OK) return st;
-  (void)hipGetLastError();
-  if (launch_gate(G, U, (uint16_t*)Y, (size_t)M * (size_t)N, stream, h->cu_count) != hipSuccess)
-    return SWIGLU_ERR_LAUNCH;
-  return SWIGLU_OK;
+  return unfused(h, A, W1, W2, workspace, Y, M, N, K, gemm_config_id, stream);
 }
 
 swiglu_status_t swiglu_pack_interleaved(swiglu_handle_t h, const void* W1, const void* W2,
@@ -356,7 +364,6 @@ swiglu_status_t swiglu_pack_interleaved(swiglu_handle_t h, const void* W1, const
     return SWIGLU_ERR_INVALID_ARG;
   swiglu_status_t st = check_device(h);
   if (st != SWIGLU_OK) return st;
-  (void)hipGetLastError();
   if (launch_pack((const uint16_t*)W1, (const uint16_t*)W2, (uint16_t*)W_fused,
                   (size_t)K * (size_t)N, stream, h->cu_count) != hipSuccess)
     return SWIGLU_ERR_LAUNCH;
@@ -381,7 +388,6 @@ swiglu_status_t swiglu_pack_fp8_fragments(swiglu_handle_t h, const void* W8, voi
   if (overlaps(P8, pb, W8, wb)) return SWIGLU_ERR_INVALID_ARG;
   swiglu_status_t st = check_device(h);
   if (st != SWIGLU_OK) return st;
-  (void)hipGetLastError();
   if (launch_pack_f8_frag((const uint8_t*)W8, (uint8_t*)P8, (int)(2 * N), (int)K, stream,
                           h->cu_count) != hipSuccess)
     return SWIGLU_ERR_LAUNCH;
@@ -406,7 +412,6 @@ swiglu_status_t swiglu_pack_fragments(swiglu_handle_t h, const void* W1, const v
   if (overlaps(P, pb, W1, wb) || overlaps(P, pb, W2, wb)) return SWIGLU_ERR_INVALID_ARG;
   swiglu_status_t st = check_device(h);
   if (st != SWIGLU_OK) return st;
-  (void)hipGetLastError();
   if (launch_pack_frag((const uint16_t*)W1, (const uint16_t*)W2, (uint16_t*)P, (int)N, (int)K,
                        stream, h->cu_count) != hipSuccess)
     return SWIGLU_ERR_LAUNCH;
@@ -492,6 +497,7 @@ swiglu_status_t forward_mx(swiglu_handle_t h, const void* A8, const void* SA, co
   if (st != SWIGLU_OK) return st;
   if (id < 0) id = choose(h, want, M, N, K);
   if (id < 0) return SWIGLU_ERR_UNSUPPORTED;
+  if (!config_fits(config_at(id), M)) return SWIGLU_ERR_UNSUPPORTED;
   LaunchArgs a;
   a.A = (const uint16_t*)A8;
   a.W1 = (const uint16_t*)W8;
@@ -545,7 +551,6 @@ swiglu_status_t swiglu_pack_mx_fragments(swiglu_handle_t h, const void* W8, void
   if (overlaps(P8, pb, W8, wb)) return SWIGLU_ERR_INVALID_ARG;
   swiglu_status_t st = check_device(h);
   if (st != SWIGLU_OK) return st;
-  (void)hipGetLastError();
   if (launch_pack_mx_frag((const uint8_t*)W8, (uint8_t*)P8, (int)(2 * N), (int)K, stream,
                           h->cu_count) != hipSuccess)
     return SWIGLU_ERR_LAUNCH;
@@ -567,7 +572,6 @@ swiglu_status_t swiglu_quantize_mx(swiglu_handle_t h, const void* X, void* Q, vo
     return SWIGLU_ERR_INVALID_ARG;
   swiglu_status_t st = check_device(h);
   if (st != SWIGLU_OK) return st;
-  (void)hipGetLastError();
   if (launch_quantize_mx((const uint16_t*)X, (uint8_t*)Q, (uint8_t*)S, (int)rows, (int)K,
                          (int)ks, stream, h->cu_count) != hipSuccess)
     return SWIGLU_ERR_LAUNCH;
@@ -587,7 +591,6 @@ swiglu_status_t swiglu_pack_kmajor(swiglu_handle_t h, const void* W1, const void
   if (overlaps(Wt, 2 * wb, W1, wb) || overlaps(Wt, 2 * wb, W2, wb)) return SWIGLU_ERR_INVALID_ARG;
   swiglu_status_t st = check_device(h);
   if (st != SWIGLU_OK) return st;
-  (void)hipGetLastError();
   if (launch_pack_kmajor((const uint16_t*)W1, (const uint16_t*)W2, (uint16_t*)Wt, (int)N, (int)K,
                          stream, h->cu_count) != hipSuccess)
     return SWIGLU_ERR_LAUNCH;
@@ -604,7 +607,6 @@ swiglu_status_t swiglu_quantize_fp8(swiglu_handle_t h, const void* X, void* Q, i
   if (overlaps(Q, count, X, 2 * count)) return SWIGLU_ERR_INVALID_ARG;
   swiglu_status_t st = check_device(h);
   if (st != SWIGLU_OK) return st;
-  (void)hipGetLastError();
   if (launch_quantize_f8((const uint16_t*)X, (uint8_t*)Q, (size_t)count, inv_scale, stream,
                          h->cu_count) != hipSuccess)
     return SWIGLU_ERR_LAUNCH;
@@ -624,7 +626,6 @@ swiglu_status_t swiglu_pack_fp8(swiglu_handle_t h, const void* W1, const void* W
   if (overlaps(W8, 2 * wb, W1, wb) || overlaps(W8, 2 * wb, W2, wb)) return SWIGLU_ERR_INVALID_ARG;
   swiglu_status_t st = check_device(h);
   if (st != SWIGLU_OK) return st;
-  (void)hipGetLastError();
   if (launch_pack_f8((const uint8_t*)W1, (const uint8_t*)W2, (uint8_t*)W8, (int)N, (int)K, stream,
                      h->cu_count) != hipSuccess)
     return SWIGLU_ERR_LAUNCH;

@@ -47,6 +47,7 @@
 #include "swiglu_device.hpp"
 #include "swiglu_internal.h"
 
+#include <tuple>
 #include <type_traits>
 #include <utility>
 
@@ -110,8 +111,11 @@ struct Tiled {
   static_assert(STAGES >= 2 && LOADS * (STAGES - 2) + LOADS / 2 <= 63, "vmcnt range");
   static constexpr int YLD = BNY + 8;    // padded row of the output staging tile
   static constexpr int Y_BYTES = BM * YLD * 2;
-  static constexpr int JUNK = STAGES * STAGE_BYTES;  // 1 KB slot for zero DMA
-  static constexpr int LDS_BYTES = JUNK + 1024 > Y_BYTES ? JUNK + 1024 : Y_BYTES;
+  // 1 KB slot for zero DMA, allocated only when some wave can lack a chunk
+  static constexpr bool NEED_JUNK = A_CHUNKS % kThreads != 0 || W_CHUNKS % kThreads != 0;
+  static constexpr int JUNK = STAGES * STAGE_BYTES;
+  static constexpr int RING_END = JUNK + (NEED_JUNK ? 1024 : 0);
+  static constexpr int LDS_BYTES = RING_END > Y_BYTES ? RING_END : Y_BYTES;
   static_assert(LDS_BYTES <= 160 * 1024, "LDS");
   static_assert(WCH % 8 == 0, "W swizzle works on aligned groups of 8 chunks");
 
@@ -484,6 +488,334 @@ __global__ __launch_bounds__(64 * WGM * WGN) void tiled_split_kernel(
     if (m0 >= M || tq * Small::BNY >= N) return;  // quarter past a ragged edge
     tiled_tile<MODE, BM / 2, BNW / 2, BK, STAGES, SWGM, SWGN>(A, W1, W2, Y, M, N, K, ldw, ldy,
                                                               m0, tq, smem);
+  }
+}
+
+// ============================================================================
+// Persistent LDS-tiled kernel: the next tile's loads under this tile's tail
+// ============================================================================
+// [RT §Metodologia, Kernel-2, "Sovrapposizione"]: the page overlaps a tile's
+// arithmetic with the previous tile's memory traffic.  On MI355X the stores
+// are fire-and-forget; what a new tile costs is its pipeline fill, a full
+// memory latency before the first MFMA.  Here one workgroup per CU keeps its
+// CU for a run of tiles and runs the DMA ring across tile boundaries: K is a
+// whole number of rings, so every tile starts on stage 0, and during a tile's
+// last STAGES - 1 K steps the ring already loads the first steps of the
+// workgroup's next tile (the same DMA slots, with that tile's offsets); the
+// next tile's first fragments are read before the epilogue.  The epilogue
+// (SiLU, pair multiply, bf16) stages Y through an LDS region of its own beside
+// the ring, a slab of wave rows at a time, so the loads in flight are never
+// overwritten, and its 16-byte stores overlap the next tile's first steps.
+// Tiles follow the XCD-aware launch order: the workgroups of one XCD take that
+// XCD's contiguous range of the order in turn.  A last round at most a quarter
+// full runs as quarter tiles after the loop, as in tiled_split_kernel.
+template <int MODE, int BM, int BNW, int BK, int STAGES, int WGM, int WGN>
+struct Persist {
+  using C = Tiled<MODE, BM, BNW, BK, STAGES, WGM, WGN>;
+  static_assert(MODE == MODE_INTERLEAVE || MODE == MODE_GEMM, "one K loop per tile");
+  static_assert(!C::NEED_JUNK, "every wave owns chunks of every K step");
+  static constexpr int RING = STAGES * C::STAGE_BYTES;
+  static constexpr int LDS_BYTES = 160 * 1024;
+  static constexpr int YCH = C::BNY / 8;  // 16-byte chunks per Y row
+  static_assert(YCH % 16 == 0, "the staging swizzle permutes aligned groups of 16 chunks");
+  static constexpr int WPP = (LDS_BYTES - RING) / (C::BNY * 2) / C::WTM;  // wave rows per slab
+  static_assert(WPP >= 1 && WGM % WPP == 0, "Y staging");
+  static constexpr int PASSES = WGM / WPP;
+  static constexpr int SROWS = WPP * C::WTM;  // Y rows staged per pass
+  static_assert(RING + SROWS * C::BNY * 2 <= LDS_BYTES, "LDS");
+  // chunk c of staged row r at c ^ y_swz(r): a wave writes one column of 32
+  // consecutive rows at a time, which this spreads over 16 chunks
+  __host__ __device__ static constexpr int y_swz(int row) { return row & 15; }
+};
+
+// Tiles t0, t0 + stride, ... (< t_end) of the launch order, one after another
+// on this workgroup, with the ring running across tile boundaries.  K must be
+// a positive multiple of BK * STAGES.  Ends with every DMA drained.
+//
+// Registers: the accumulators of a tile are live through its epilogue, so no
+// per-thread address may be: everything per-thread is derived, inside each
+// tile's iteration, from a copy of the thread index that the compiler cannot
+// see through (an empty asm statement), and only wave-uniform tile offsets
+// cross the epilogue.
+template <int MODE, int BM, int BNW, int BK, int STAGES, int WGM, int WGN>
+__device__ __forceinline__ void tiled_persist(const uint16_t* __restrict__ A,
+                                              const uint16_t* __restrict__ W,
+                                              uint16_t* __restrict__ Y, int M, int N, int K,
+                                              int ldw, int ldy, int group_m, int t0, int stride,
+                                              int t_end, uint8_t* smem) {
+  using C = Tiled<MODE, BM, BNW, BK, STAGES, WGM, WGN>;
+  using P = Persist<MODE, BM, BNW, BK, STAGES, WGM, WGN>;
+  static_assert(C::swizzles_permute_rows(), "LDS swizzle is not a permutation of a row");
+
+  const int ntm = (M + BM - 1) / BM, ntn = (N + C::BNY - 1) / C::BNY;
+  const int nk = K / BK;  // a multiple of STAGES
+  const int wave_u = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  const int wm = wave_u / WGN, wn = wave_u % WGN;
+  const int wcols = (MODE == MODE_INTERLEAVE) ? 2 * N : N;
+  const uint32_t wbytes = (uint32_t)(((size_t)(K - 1) * ldw + wcols) * 2);
+  const i32x4 rsA = make_rsrc(A, (uint32_t)((size_t)M * K * 2));
+  const i32x4 rsW = make_rsrc(W, wbytes);
+  const uint32_t lds0 = lds_addr(smem);
+  uint16_t* ys = reinterpret_cast<uint16_t*>(smem + P::RING);  // [SROWS][BNY], swizzled
+
+  // A tile's offsets are wave-uniform (scalar registers).  K is a multiple of
+  // BK, so no chunk reaches past K; rows of A past M lie past the end of A and
+  // read zeros by the buffer bound, so only weight columns past the matrix
+  // need a mask.  A tile at or past t_end gets offsets out of range everywhere.
+  struct TileOffs {
+    uint32_t a;  // byte offset of the tile's first row of A
+    uint32_t w;  // byte offset of its first weight column
+    int wlim;    // weight columns of the tile inside the matrix
+  };
+  auto offsets = [&](int t) __attribute__((always_inline)) {
+    TileOffs o{(uint32_t)M * (uint32_t)K * 2u, 0u, 0};
+    if (t < t_end) {
+      int tm, tn;
+      tile_of(t, ntm, ntn, group_m, tm, tn);
+      o.a = (uint32_t)(tm * BM) * (uint32_t)K * 2u;
+      o.w = (uint32_t)(tn * BNW) * 2u;
+      o.wlim = wcols - tn * BNW;
+    }
+    o.a = __builtin_amdgcn_readfirstlane(o.a);
+    o.w = __builtin_amdgcn_readfirstlane(o.w);
+    o.wlim = __builtin_amdgcn_readfirstlane(o.wlim);
+    return o;
+  };
+  // this tile's offsets and the next tile's
+  TileOffs oc = offsets(t0), on = oc;
+  u32x4 wf[2][C::FW], af[2][C::FA];  // fragments (double-buffered by sub-step)
+
+  for (int t = t0; t < t_end; t += stride) {
+    int tid = threadIdx.x;
+    asm volatile("" : "+v"(tid));
+    const int lane = tid & 63;
+
+    // per-thread DMA parts (the tile's parts are in oc / on)
+    uint32_t a_base[C::A_LOADS], w_base[C::W_LOADS];
+    int w_c8[C::W_LOADS];
+#pragma unroll
+    for (int i = 0; i < C::A_LOADS; ++i) {
+      const int p = tid + C::kThreads * i;
+      const int row = p / C::ACH;
+      const int c = (p % C::ACH) ^ C::a_swz(row);
+      a_base[i] = (uint32_t)(row * K + c * 8) * 2u;
+    }
+#pragma unroll
+    for (int i = 0; i < C::W_LOADS; ++i) {
+      const int p = tid + C::kThreads * i;
+      const int row = p / C::WCH;
+      const int c = (p % C::WCH) ^ C::w_swz(row);
+      w_base[i] = (uint32_t)(row * ldw + c * 8) * 2u;
+      w_c8[i] = c * 8;
+    }
+    // DMA instruction q of K step `it` into stage ST: steps [0, nk) of the
+    // current tile, steps [nk, nk + STAGES) the first ones of the next tile
+    auto dma = [&](int it, auto st_c, int q) __attribute__((always_inline)) {
+      constexpr int ST = decltype(st_c)::value;
+      const bool nxt = it >= nk;  // wave-uniform
+      const TileOffs o = nxt ? on : oc;
+      const uint32_t k0 = (uint32_t)((nxt ? it - nk : it) * BK);
+      const uint32_t sbase = lds0 + ST * C::STAGE_BYTES;
+      if (q < C::A_LOADS) {
+        const int p0 = C::kThreads * q + 64 * wave_u;
+        lds_dma16(sbase + p0 * 16, a_base[q] + o.a + k0 * 2u, rsA);
+      } else {
+        const int i = q - C::A_LOADS;
+        const int p0 = C::kThreads * i + 64 * wave_u;
+        const uint32_t off =
+            w_c8[i] < o.wlim ? w_base[i] + o.w + k0 * (uint32_t)ldw * 2u : kOutOfRange;
+        lds_dma16(sbase + C::A_BYTES + p0 * 16, off, rsW);
+      }
+    };
+
+    // fragments (as in tiled_tile)
+    const int g16 = lane >> 4, s16 = lane & 15;
+    const int w_row = 8 * (g16 >> 1) + (s16 >> 2);
+    const int w_col = wn * C::WTW + 16 * (g16 & 1) + 4 * (s16 & 3);
+    const int a_row = wm * C::WTM + (lane & 31);
+    const int a_chk = lane >> 5;
+    constexpr int NFRAG = 2 * C::FW + C::FA;
+    auto frag = [&](auto st_c, int sub, int fb, int r) __attribute__((always_inline)) {
+      constexpr int ST = decltype(st_c)::value;
+      const uint8_t* st = smem + ST * C::STAGE_BYTES;
+      const int kk = sub * 16;
+      if (r < 2 * C::FW) {
+        const int fw = r >> 1, h = r & 1;
+        const int col = w_col + fw * 32;
+        const int row = kk + w_row + 4 * h;
+        const int chunk = (col >> 3) ^ C::w_swz(row);
+        const u32x2 v = lds_read_tr16(st + C::A_BYTES + row * (BNW * 2) + chunk * 16 +
+                                      ((col >> 2) & 1) * 8);
+        wf[fb][fw][2 * h] = v[0];
+        wf[fb][fw][2 * h + 1] = v[1];
+      } else {
+        const int fa = r - 2 * C::FW;
+        const int row = a_row + fa * 32;
+        const int chunk = (kk / 8 + a_chk) ^ C::a_swz(row);
+        af[fb][fa] = *reinterpret_cast<const u32x4*>(st + row * (BK * 2) + chunk * 16);
+      }
+    };
+
+    f32x16 acc[C::FW][C::FA];
+
+    // one K step on stage ST (the schedule of tiled_tile); the tile's last
+    // step reads the next tile's first fragments, whose data has landed by
+    // then (its wait and barrier cover step nk, the next tile's step 0)
+    constexpr int LH = C::LOADS / 2;
+    auto kstep = [&](int it, auto st_c) __attribute__((always_inline)) {
+      constexpr int ST = decltype(st_c)::value;
+      constexpr int NMF = C::FW * C::FA;
+      constexpr int HALF = NMF / 2 > 0 ? NMF / 2 : 1;
+      constexpr int DSLOTS = NMF - HALF > 0 ? NMF - HALF : 1;
+      constexpr int DBEGIN = NMF - DSLOTS;
+      using Next = std::integral_constant<int, (ST + 1) % STAGES>;
+      using Prev = std::integral_constant<int, (ST + STAGES - 1) % STAGES>;
+#pragma unroll
+      for (int sub = 0; sub < C::NSUB; ++sub) {
+        const int fb = sub & 1;
+        const bool last = sub == C::NSUB - 1;
+        if (last) {
+          wait_vmcnt<(STAGES - 2) * C::LOADS>();
+          __syncthreads();
+        }
+        const int nd = (sub == 0) ? C::LOADS - LH : (last ? LH : 0);
+#pragma unroll
+        for (int q = 0; q < NMF; ++q) {
+          const int i = q / C::FA, j = q % C::FA;
+          acc[i][j] = mfma32(wf[fb][i], af[fb][j], acc[i][j]);
+          if (q < HALF) {
+#pragma unroll
+            for (int x = q * NFRAG / HALF; x < (q + 1) * NFRAG / HALF; ++x) {
+              if (last) frag(Next{}, 0, fb ^ 1, x);
+              else frag(st_c, sub + 1, fb ^ 1, x);
+            }
+          }
+          if (nd > 0 && q >= DBEGIN) {
+#pragma unroll
+            for (int x = (q - DBEGIN) * nd / DSLOTS; x < (q - DBEGIN + 1) * nd / DSLOTS; ++x) {
+              if (sub == 0) dma(it + STAGES - 1, Prev{}, LH + x);
+              else dma(it + STAGES, st_c, x);
+            }
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+    };
+    auto round = [&](int it0) __attribute__((always_inline)) {
+      [&]<int... S>(std::integer_sequence<int, S...>) __attribute__((always_inline)) {
+        (kstep(it0 + S, std::integral_constant<int, S>{}), ...);
+      }(std::make_integer_sequence<int, STAGES>{});
+    };
+
+    if (t == t0) {
+      // prologue: the first tile's steps 0..STAGES-2 and half of STAGES-1
+      auto fill = [&](int it, auto st_c, int q0, int q1) __attribute__((always_inline)) {
+#pragma unroll
+        for (int q = 0; q < C::LOADS; ++q)
+          if (q >= q0 && q < q1) dma(it, st_c, q);
+      };
+      [&]<int... S>(std::integer_sequence<int, S...>) __attribute__((always_inline)) {
+        (fill(S, std::integral_constant<int, S>{}, 0, C::LOADS), ...);
+      }(std::make_integer_sequence<int, STAGES - 1>{});
+      fill(STAGES - 1, std::integral_constant<int, STAGES - 1>{}, 0, LH);
+      wait_vmcnt<(STAGES - 2) * C::LOADS + LH>();
+      __syncthreads();
+#pragma unroll
+      for (int r = 0; r < NFRAG; ++r) frag(std::integral_constant<int, 0>{}, 0, 0, r);
+    }
+    // this tile's step-0 fragments are in registers (read above, or in the
+    // previous tile's last step)
+#pragma unroll
+    for (int i = 0; i < C::FW; ++i)
+#pragma unroll
+      for (int j = 0; j < C::FA; ++j) acc[i][j] = f32x16{};
+    on = offsets(t + stride);
+    for (int it = 0; it < nk; it += STAGES) round(it);
+    // The next tile's first STAGES - 1 steps (and half of the one after) are
+    // in flight or landed, and its step-0 fragments are in registers.
+
+    // ---- epilogue: one slab of wave rows at a time through the staging region
+    const int h32 = lane >> 5;
+    int tm, tn;
+    tile_of(t, ntm, ntn, group_m, tm, tn);
+    const int m0 = tm * BM, y0 = tn * C::BNY;
+#pragma unroll
+    for (int pass = 0; pass < P::PASSES; ++pass) {
+      if (wm / P::WPP == pass) {
+#pragma unroll
+        for (int i = 0; i < C::FW; ++i)
+#pragma unroll
+          for (int j = 0; j < C::FA; ++j) {
+            const int row = (wm % P::WPP) * C::WTM + (lane & 31) + j * 32;  // staged row
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              const int wcl = wn * C::WTW + i * 32 + 8 * q + 4 * h32;
+              const f32x16& d = acc[i][j];
+              if constexpr (MODE == MODE_INTERLEAVE) {
+                const int col = wcl / 2;
+                const int e = (((col >> 3) ^ P::y_swz(row)) << 3) | (col & 7);
+                const float ya = silu(d[4 * q + 0]) * d[4 * q + 1];  // pair (wcl, wcl+1)
+                const float yb = silu(d[4 * q + 2]) * d[4 * q + 3];  // pair (wcl+2, wcl+3)
+                *reinterpret_cast<uint32_t*>(ys + row * C::BNY + e) = pack_bf16x2(ya, yb);
+              } else {
+                const int e = (((wcl >> 3) ^ P::y_swz(row)) << 3) | (wcl & 7);
+                *reinterpret_cast<u32x2*>(ys + row * C::BNY + e) =
+                    u32x2{pack_bf16x2(d[4 * q], d[4 * q + 1]),
+                          pack_bf16x2(d[4 * q + 2], d[4 * q + 3])};
+              }
+            }
+          }
+      }
+      __syncthreads();
+      for (int p = tid; p < P::SROWS * P::YCH; p += C::kThreads) {
+        const int row = p / P::YCH, cq = p % P::YCH;
+        const int gr = m0 + pass * P::SROWS + row, gc = y0 + cq * 8;
+        if (gr < M && gc < N)
+          *reinterpret_cast<u32x4*>(Y + (size_t)gr * ldy + gc) = *reinterpret_cast<const u32x4*>(
+              ys + row * C::BNY + ((cq ^ P::y_swz(row)) << 3));
+      }
+      // the next pass (or the next tile's epilogue, after its K loop's
+      // barriers) overwrites the staging rows
+      if (pass + 1 < P::PASSES) __syncthreads();
+    }
+    oc = on;
+  }
+  // the zero loads issued past the last tile still write LDS
+  wait_vmcnt<0>();
+  __syncthreads();
+}
+
+template <int MODE, int BM, int BNW, int BK, int STAGES, int WGM, int WGN, int SWGM, int SWGN>
+__global__ __launch_bounds__(64 * WGM * WGN) void tiled_persist_kernel(
+    const uint16_t* __restrict__ A, const uint16_t* __restrict__ W, uint16_t* __restrict__ Y,
+    int M, int N, int K, int ldw, int ldy, int group_m, int n_big, int n_quarter) {
+  using P = Persist<MODE, BM, BNW, BK, STAGES, WGM, WGN>;
+  using Small = Tiled<MODE, BM / 2, BNW / 2, BK, STAGES, SWGM, SWGN>;
+  static_assert(Small::kThreads == P::C::kThreads, "one workgroup size for both tile kinds");
+  static_assert(Small::LDS_BYTES <= P::LDS_BYTES, "LDS");
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[P::LDS_BYTES];
+  // workgroup b runs on XCD b % 8; each XCD owns a contiguous range of the
+  // first n_big tiles of the order, which its workgroups take in turn
+  const int G = gridDim.x, b = blockIdx.x;
+  const int x = b % 8, i = b / 8;
+  const int gx = G / 8 + (x < G % 8 ? 1 : 0);
+  const int q = n_big / 8, r = n_big % 8;
+  const int lo = x * q + min(x, r), cnt = q + (x < r ? 1 : 0);
+  if (i < cnt)
+    tiled_persist<MODE, BM, BNW, BK, STAGES, WGM, WGN>(A, W, Y, M, N, K, ldw, ldy, group_m,
+                                                       lo + i, gx, lo + cnt, smem);
+  // the short last round, as quarter tiles (BM/2 x BNW/2): quarter u % 4 of
+  // big tile n_big + u / 4
+  const int ntm = (M + BM - 1) / BM, ntn = (N + P::C::BNY - 1) / P::C::BNY;
+  for (int u = b; u < n_quarter; u += G) {
+    int tm, tn;
+    tile_of(n_big + u / 4, ntm, ntn, group_m, tm, tn);
+    const int m0 = tm * BM + ((u & 3) >> 1) * (BM / 2);
+    const int tq = 2 * tn + (u & 1);
+    if (m0 < M && tq * Small::BNY < N)
+      tiled_tile<MODE, BM / 2, BNW / 2, BK, STAGES, SWGM, SWGN>(A, W, W, Y, M, N, K, ldw, ldy,
+                                                                m0, tq, smem);
+    __syncthreads();  // the next quarter tile's loads overwrite this one's LDS
   }
 }
 
@@ -2111,6 +2443,23 @@ __global__ __launch_bounds__(256) void pack_frag_kernel(const uint16_t* __restri
 // faster than 8 on the 1.5B shape, 0.5-1 % on the other two).
 constexpr int kGroupM = 4;
 
+// ---- launches ------------------------------------------------------------------
+// Every launch goes through hipLaunchKernel, whose return value is the status
+// of that launch alone: an error that an earlier call left pending on the
+// calling thread is neither reported as this launch's nor cleared.
+template <typename... P, typename... Args>
+static hipError_t launch_kernel(void (*k)(P...), dim3 grid, dim3 block, size_t shm,
+                                hipStream_t stream, Args... args) {
+  static_assert(sizeof...(P) == sizeof...(Args), "kernel argument count");
+  std::tuple<std::decay_t<P>...> vals(static_cast<std::decay_t<P>>(args)...);
+  return std::apply(
+      [&](auto&... v) {
+        void* argv[] = {static_cast<void*>(&v)...};
+        return hipLaunchKernel(reinterpret_cast<const void*>(k), grid, block, argv, shm, stream);
+      },
+      vals);
+}
+
 template <int MODE, int BM, int BNW, int BK, int STAGES, int WGM, int WGN>
 static hipError_t launch_tiled(const LaunchArgs& a) {
   using C = Tiled<MODE, BM, BNW, BK, STAGES, WGM, WGN>;
@@ -2120,10 +2469,9 @@ static hipError_t launch_tiled(const LaunchArgs& a) {
   if (nwg > 0x7fffffffLL) return hipErrorInvalidValue;
   int group_m = a.group_m > 0 ? a.group_m : kGroupM;
   if (group_m > ntm) group_m = ntm;
-  hipLaunchKernelGGL((tiled_kernel<MODE, BM, BNW, BK, STAGES, WGM, WGN>), dim3((unsigned)nwg),
+  return launch_kernel((tiled_kernel<MODE, BM, BNW, BK, STAGES, WGM, WGN>), dim3((unsigned)nwg),
                      dim3(C::kThreads), 0, a.stream, a.A, a.W1, a.W2, a.Y, a.M, a.N, a.K,
                      a.ldw, a.ldy, group_m);
-  return hipGetLastError();
 }
 
 // Split-tail launch: whole rounds of big tiles plus, when the last round is at
@@ -2141,10 +2489,30 @@ static hipError_t launch_tiled_split(const LaunchArgs& a) {
     return launch_tiled<MODE, BM, BNW, BK, STAGES, WGM, WGN>(a);
   int group_m = a.group_m > 0 ? a.group_m : kGroupM;
   if (group_m > ntm) group_m = ntm;
-  hipLaunchKernelGGL((tiled_split_kernel<MODE, BM, BNW, BK, STAGES, WGM, WGN, SWGM, SWGN>),
+  return launch_kernel((tiled_split_kernel<MODE, BM, BNW, BK, STAGES, WGM, WGN, SWGM, SWGN>),
                      dim3((unsigned)(n_big + 4 * tail)), dim3(C::kThreads), 0, a.stream, a.A,
                      a.W1, a.W2, a.Y, a.M, a.N, a.K, a.ldw, a.ldy, group_m, (int)n_big);
-  return hipGetLastError();
+}
+
+// Persistent launch: one workgroup per CU over whole rounds of big tiles, the
+// last round as quarter tiles when it is at most a quarter full.  Needs K a
+// positive multiple of BK * STAGES and at least two tiles per CU; other shapes
+// take the split-tail launch of the same tiles.
+template <int MODE, int BM, int BNW, int BK, int STAGES, int WGM, int WGN, int SWGM, int SWGN>
+static hipError_t launch_tiled_persist(const LaunchArgs& a) {
+  using C = Tiled<MODE, BM, BNW, BK, STAGES, WGM, WGN>;
+  const int ntm = (a.M + BM - 1) / BM, ntn = (a.N + C::BNY - 1) / C::BNY;
+  const long long nt = (long long)ntm * ntn;
+  const long long slots = a.cu_count > 0 ? a.cu_count : 256;  // one workgroup per CU
+  if (a.K <= 0 || a.K % (BK * STAGES) != 0 || nt < 2 * slots || 4 * nt > 0x7fffffffLL)
+    return launch_tiled_split<MODE, BM, BNW, BK, STAGES, WGM, WGN, SWGM, SWGN>(a);
+  long long n_big = nt / slots * slots, tail = nt - n_big;
+  if (tail == 0 || 4 * tail > slots) n_big = nt, tail = 0;
+  int group_m = a.group_m > 0 ? a.group_m : kGroupM;
+  if (group_m > ntm) group_m = ntm;
+  return launch_kernel((tiled_persist_kernel<MODE, BM, BNW, BK, STAGES, WGM, WGN, SWGM, SWGN>),
+                       dim3((unsigned)slots), dim3(C::kThreads), 0, a.stream, a.A, a.W1, a.Y,
+                       a.M, a.N, a.K, a.ldw, a.ldy, group_m, (int)n_big, (int)(4 * tail));
 }
 
 template <int MODE>
@@ -2156,9 +2524,8 @@ static hipError_t launch_pingpong(const LaunchArgs& a) {
   if (nwg > 0x7fffffffLL) return hipErrorInvalidValue;
   int group_m = a.group_m > 0 ? a.group_m : kGroupM;
   if (group_m > ntm) group_m = ntm;
-  hipLaunchKernelGGL(pingpong_kernel<MODE>, dim3((unsigned)nwg), dim3(512), 0, a.stream, a.A,
+  return launch_kernel(pingpong_kernel<MODE>, dim3((unsigned)nwg), dim3(512), 0, a.stream, a.A,
                      a.W1, a.Y, a.M, a.N, a.K, a.ldw, a.ldy, group_m);
-  return hipGetLastError();
 }
 
 template <int MODE, int MT, int NW>
@@ -2168,9 +2535,8 @@ static hipError_t launch_skinny(const LaunchArgs& a) {
   const long long nmb = (a.M + MT * 16 - 1) / (MT * 16);
   if (nslab <= 0 || nmb <= 0) return hipSuccess;
   if (nslab > 0x7fffffffLL || nmb > 65535) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((skinny_kernel<MODE, MT, NW>), dim3((unsigned)nslab, (unsigned)nmb),
+  return launch_kernel((skinny_kernel<MODE, MT, NW>), dim3((unsigned)nslab, (unsigned)nmb),
                      dim3(C::kThreads), 0, a.stream, a.A, a.W1, a.W2, a.Y, a.M, a.N, a.K);
-  return hipGetLastError();
 }
 
 template <int MT, int NW, int CH>
@@ -2180,9 +2546,8 @@ static hipError_t launch_packed(const LaunchArgs& a) {
   const long long nmb = (a.M + MT * 16 - 1) / (MT * 16);
   if (nunit <= 0 || nmb <= 0) return hipSuccess;
   if (nunit > 0x7fffffffLL || nmb > 65535) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((packed_kernel<MT, NW, CH>), dim3((unsigned)nunit, (unsigned)nmb),
+  return launch_kernel((packed_kernel<MT, NW, CH>), dim3((unsigned)nunit, (unsigned)nmb),
                      dim3(C::kThreads), 0, a.stream, a.A, a.W1, a.Y, a.M, a.N, a.K);
-  return hipGetLastError();
 }
 
 template <int MODE, int BM, int BNW, int STAGES, int WGM, int WGN>
@@ -2194,11 +2559,10 @@ static hipError_t launch_f8(const LaunchArgs& a) {
   if (nwg > 0x7fffffffLL) return hipErrorInvalidValue;
   int group_m = a.group_m > 0 ? a.group_m : kGroupM;
   if (group_m > ntm) group_m = ntm;
-  hipLaunchKernelGGL((f8_kernel<MODE, BM, BNW, STAGES, WGM, WGN>), dim3((unsigned)nwg),
+  return launch_kernel((f8_kernel<MODE, BM, BNW, STAGES, WGM, WGN>), dim3((unsigned)nwg),
                      dim3(C::kThreads), 0, a.stream, (const uint8_t*)a.A,
                      (const uint8_t*)a.W1, a.Y, a.M, a.N, a.K, a.scale_g, a.scale_u, a.SA, a.SW,
                      a.ks, group_m);
-  return hipGetLastError();
 }
 
 template <int MODE, int BM, int BNW, int STAGES, int WGM, int WGN, int SWGM, int SWGN>
@@ -2213,11 +2577,10 @@ static hipError_t launch_f8_split(const LaunchArgs& a) {
   if (tail == 0 || 4 * tail > slots) return launch_f8<MODE, BM, BNW, STAGES, WGM, WGN>(a);
   int group_m = a.group_m > 0 ? a.group_m : kGroupM;
   if (group_m > ntm) group_m = ntm;
-  hipLaunchKernelGGL((f8_split_kernel<MODE, BM, BNW, STAGES, WGM, WGN, SWGM, SWGN>),
+  return launch_kernel((f8_split_kernel<MODE, BM, BNW, STAGES, WGM, WGN, SWGM, SWGN>),
                      dim3((unsigned)(n_big + 4 * tail)), dim3(C::kThreads), 0, a.stream,
                      (const uint8_t*)a.A, (const uint8_t*)a.W1, a.Y, a.M, a.N, a.K, a.scale_g,
                      a.scale_u, a.SA, a.SW, a.ks, group_m, (int)n_big);
-  return hipGetLastError();
 }
 
 template <int MT, int NB, int NW>
@@ -2227,10 +2590,9 @@ static hipError_t launch_f8_skinny(const LaunchArgs& a) {
   const long long nmb = (a.M + MT * 16 - 1) / (MT * 16);
   if (nslab <= 0 || nmb <= 0) return hipSuccess;
   if (nslab > 0x7fffffffLL || nmb > 65535) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((f8_skinny_kernel<MT, NB, NW>), dim3((unsigned)nslab, (unsigned)nmb),
+  return launch_kernel((f8_skinny_kernel<MT, NB, NW>), dim3((unsigned)nslab, (unsigned)nmb),
                      dim3(C::kThreads), 0, a.stream, (const uint8_t*)a.A, (const uint8_t*)a.W1,
                      a.Y, a.M, a.N, a.K, a.scale_g, a.scale_u);
-  return hipGetLastError();
 }
 
 template <int MT, int NB, int NW>
@@ -2240,10 +2602,9 @@ static hipError_t launch_f8_packed(const LaunchArgs& a) {
   const long long nmb = (a.M + MT * 16 - 1) / (MT * 16);
   if (nunit <= 0 || nmb <= 0) return hipSuccess;
   if (nunit > 0x7fffffffLL || nmb > 65535) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((f8_packed_kernel<MT, NB, NW>), dim3((unsigned)nunit, (unsigned)nmb),
+  return launch_kernel((f8_packed_kernel<MT, NB, NW>), dim3((unsigned)nunit, (unsigned)nmb),
                      dim3(C::kThreads), 0, a.stream, (const uint8_t*)a.A, (const uint8_t*)a.W1,
                      a.Y, a.M, a.N, a.K, a.scale_g, a.scale_u);
-  return hipGetLastError();
 }
 
 #define F8_PACKED(mt, nb, nw)                                                              \
@@ -2256,11 +2617,10 @@ static hipError_t launch_mx_packed(const LaunchArgs& a) {
   const long long nmb = (a.M + 31) / 32;
   if (nunit <= 0 || nmb <= 0) return hipSuccess;
   if (nunit > 0x7fffffffLL || nmb > 65535) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((mx_packed_kernel<NB, NW>), dim3((unsigned)nunit, (unsigned)nmb),
+  return launch_kernel((mx_packed_kernel<NB, NW>), dim3((unsigned)nunit, (unsigned)nmb),
                      dim3(C::kThreads), 0,
                      a.stream, (const uint8_t*)a.A, a.SA, (const uint8_t*)a.W1, a.SW, a.Y, a.M,
                      a.N, a.K, a.ks);
-  return hipGetLastError();
 }
 
 #define MX_PACKED(nb, nw)                                                                  \
@@ -2283,6 +2643,10 @@ static hipError_t launch_mx_packed(const LaunchArgs& a) {
   {v, 0, bm, Tiled<mode, bm, bnw, bk, st, wgm, wgn>::BNY, bk, (wgm) * (wgn), 1,             \
    Tiled<mode, bm, bnw, bk, st, wgm, wgn>::LDS_BYTES,                                       \
    &launch_tiled_split<mode, bm, bnw, bk, st, wgm, wgn, swgm, swgn>, 4}
+#define TILED_PERSIST(mode, v, bm, bnw, bk, st, wgm, wgn, swgm, swgn)                        \
+  {v, 0, bm, Tiled<mode, bm, bnw, bk, st, wgm, wgn>::BNY, bk, (wgm) * (wgn), 1,             \
+   Persist<mode, bm, bnw, bk, st, wgm, wgn>::LDS_BYTES,                                     \
+   &launch_tiled_persist<mode, bm, bnw, bk, st, wgm, wgn, swgm, swgn>, 4}
 #define PINGPONG(mode, v) \
   {v, 2, 256, PingPong<mode>::BNY, 32, 8, 1, PingPong<mode>::LDS_BYTES, &launch_pingpong<mode>}
 #define PACKED(mt, nw, ch)                                                                 \
@@ -2393,6 +2757,10 @@ static const KernelConfig kConfigs[] = {
     MX_PACKED(4, 1),                                                // 79
     MX_PACKED(1, 2),                                                // 80
     MX_PACKED(1, 4),                                                // 81
+    // ---- the split 256-row tiles on one persistent workgroup per CU, the
+    //      next tile's loads running under each tile's last steps ----------
+    TILED_PERSIST(MODE_INTERLEAVE, VAR_INTERLEAVE, 256, 256, 32, 4, 4, 2, 2, 4),  // 82
+    TILED_PERSIST(MODE_GEMM, VAR_GEMM, 256, 256, 32, 4, 4, 2, 2, 4),              // 83
 };
 
 int config_count() { return (int)(sizeof(kConfigs) / sizeof(kConfigs[0])); }
@@ -2407,8 +2775,7 @@ hipError_t launch_gate(const uint16_t* G, const uint16_t* U, uint16_t* Y, size_t
   size_t blocks = (n8 + 255) / 256;
   const size_t cap = (size_t)(cu_count > 0 ? cu_count : 256) * 8;
   if (blocks > cap) blocks = cap;
-  hipLaunchKernelGGL(gate_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, G, U, Y, n8);
-  return hipGetLastError();
+  return launch_kernel(gate_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, G, U, Y, n8);
 }
 
 hipError_t launch_quantize_f8(const uint16_t* X, uint8_t* Q, size_t n, float inv_scale,
@@ -2418,9 +2785,8 @@ hipError_t launch_quantize_f8(const uint16_t* X, uint8_t* Q, size_t n, float inv
   size_t blocks = (n16 + 255) / 256;
   const size_t cap = (size_t)(cu_count > 0 ? cu_count : 256) * 8;
   if (blocks > cap) blocks = cap;
-  hipLaunchKernelGGL(quantize_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, X, Q, n16,
+  return launch_kernel(quantize_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, X, Q, n16,
                      inv_scale);
-  return hipGetLastError();
 }
 
 hipError_t launch_quantize_mx(const uint16_t* X, uint8_t* Q, uint8_t* S, int rows, int K, int ks,
@@ -2430,9 +2796,8 @@ hipError_t launch_quantize_mx(const uint16_t* X, uint8_t* Q, uint8_t* S, int row
   size_t blocks = (total + 255) / 256;
   const size_t cap = (size_t)(cu_count > 0 ? cu_count : 256) * 8;
   if (blocks > cap) blocks = cap;
-  hipLaunchKernelGGL(quantize_mx_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, X, Q, S,
+  return launch_kernel(quantize_mx_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, X, Q, S,
                      rows, K, ks);
-  return hipGetLastError();
 }
 
 hipError_t launch_pack_kmajor(const uint16_t* W1, const uint16_t* W2, uint16_t* Wt, int N, int K,
@@ -2442,9 +2807,8 @@ hipError_t launch_pack_kmajor(const uint16_t* W1, const uint16_t* W2, uint16_t* 
   size_t blocks = (runs + 255) / 256;
   const size_t cap = (size_t)(cu_count > 0 ? cu_count : 256) * 8;
   if (blocks > cap) blocks = cap;
-  hipLaunchKernelGGL(pack_kmajor_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, W1, W2, Wt,
+  return launch_kernel(pack_kmajor_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, W1, W2, Wt,
                      N, K);
-  return hipGetLastError();
 }
 
 hipError_t launch_pack_f8(const uint8_t* W1, const uint8_t* W2, uint8_t* W8, int N, int K,
@@ -2454,9 +2818,8 @@ hipError_t launch_pack_f8(const uint8_t* W1, const uint8_t* W2, uint8_t* W8, int
   size_t blocks = (runs + 255) / 256;
   const size_t cap = (size_t)(cu_count > 0 ? cu_count : 256) * 8;
   if (blocks > cap) blocks = cap;
-  hipLaunchKernelGGL(pack_f8_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, W1, W2, W8, N,
+  return launch_kernel(pack_f8_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, W1, W2, W8, N,
                      K);
-  return hipGetLastError();
 }
 
 hipError_t launch_pack_mx_frag(const uint8_t* W8, uint8_t* P, int R, int K, hipStream_t stream,
@@ -2466,9 +2829,8 @@ hipError_t launch_pack_mx_frag(const uint8_t* W8, uint8_t* P, int R, int K, hipS
   size_t blocks = (nchunks + 255) / 256;
   const size_t cap = (size_t)(cu_count > 0 ? cu_count : 256) * 8;
   if (blocks > cap) blocks = cap;
-  hipLaunchKernelGGL(pack_mx_frag_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, W8, P, R,
+  return launch_kernel(pack_mx_frag_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, W8, P, R,
                      K, nchunks);
-  return hipGetLastError();
 }
 
 hipError_t launch_pack_f8_frag(const uint8_t* W8, uint8_t* P, int R, int K, hipStream_t stream,
@@ -2478,9 +2840,8 @@ hipError_t launch_pack_f8_frag(const uint8_t* W8, uint8_t* P, int R, int K, hipS
   size_t blocks = (nchunks + 255) / 256;
   const size_t cap = (size_t)(cu_count > 0 ? cu_count : 256) * 8;
   if (blocks > cap) blocks = cap;
-  hipLaunchKernelGGL(pack_f8_frag_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, W8, P, R,
+  return launch_kernel(pack_f8_frag_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, W8, P, R,
                      K, nchunks);
-  return hipGetLastError();
 }
 
 hipError_t launch_pack_frag(const uint16_t* W1, const uint16_t* W2, uint16_t* P, int N, int K,
@@ -2490,9 +2851,8 @@ hipError_t launch_pack_frag(const uint16_t* W1, const uint16_t* W2, uint16_t* P,
   size_t blocks = (nruns + 255) / 256;
   const size_t cap = (size_t)(cu_count > 0 ? cu_count : 256) * 8;
   if (blocks > cap) blocks = cap;
-  hipLaunchKernelGGL(pack_frag_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, W1, W2, P,
+  return launch_kernel(pack_frag_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, W1, W2, P,
                      N, K, nruns);
-  return hipGetLastError();
 }
 
 hipError_t launch_pack(const uint16_t* W1, const uint16_t* W2, uint16_t* WF, size_t n,
@@ -2502,8 +2862,7 @@ hipError_t launch_pack(const uint16_t* W1, const uint16_t* W2, uint16_t* WF, siz
   size_t blocks = (n8 + 255) / 256;
   const size_t cap = (size_t)(cu_count > 0 ? cu_count : 256) * 8;
   if (blocks > cap) blocks = cap;
-  hipLaunchKernelGGL(pack_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, W1, W2, WF, n8);
-  return hipGetLastError();
+  return launch_kernel(pack_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, W1, W2, WF, n8);
 }
 
 }  // namespace swiglu

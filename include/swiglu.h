@@ -41,12 +41,20 @@
  *  - Shapes: M, N, K >= 0.  M == 0 or N == 0 is a no-op (pointers may then be
  *    NULL).  K == 0 writes Y = 0 (empty sums).  The kernels need N % 8 == 0,
  *    K % 8 == 0 and 16-byte aligned pointers; other shapes or alignments give
- *    SWIGLU_ERR_UNSUPPORTED.  M is unrestricted (ragged row tiles are masked).
+ *    SWIGLU_ERR_UNSUPPORTED.  Ragged row tiles are masked, so M needs no
+ *    multiple; M is bounded by the tensor-size rule below and, for the
+ *    split-K streaming configurations (family 1, chosen for small M or forced
+ *    by id), by 65535 row blocks of `bm` rows (bm = 16 ... 64, so M up to
+ *    1,048,560 ... 4,194,240): a larger M on such a configuration gives
+ *    SWIGLU_ERR_UNSUPPORTED before anything is enqueued.
  *    Every byte offset must fit in 31 bits (each tensor < 2 GiB), otherwise
  *    SWIGLU_ERR_UNSUPPORTED.
  *  - Execution is asynchronous on the given stream (0 = the null stream of the
- *    current device); SWIGLU_OK means "enqueued".  A failed launch
- *    (hipGetLastError after the launch) gives SWIGLU_ERR_LAUNCH.
+ *    current device); SWIGLU_OK means "enqueued".  Each kernel is launched
+ *    with hipLaunchKernel and judged by that call's own return value: a
+ *    failed launch gives SWIGLU_ERR_LAUNCH.  An error left pending on the
+ *    calling thread by an earlier HIP call is neither cleared nor reported
+ *    (hipGetLastError still returns it to the caller).
  *  - A handle holds host state only, is immutable after creation and may be
  *    used from several host threads and streams at once.  It is bound to the
  *    device it was created for; that device must be current when calling.

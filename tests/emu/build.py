@@ -1,10 +1,12 @@
 """Build the CPU bounds emulation of the kernels (host clang++ with
 AddressSanitizer) from the current kernel source.  Returns the binary path.
 
-The kernel file is copied with three mechanical rewrites that only the
+The kernel file is copied with five mechanical rewrites that only the
 emulation needs: each `__shared__` array becomes a pointer from emu_lds(),
-the raw `s_barrier` becomes emu_barrier(), and the AMDGPU-only occupancy
-attribute is dropped."""
+the raw `s_barrier` becomes emu_barrier(), the empty asm statement that pins
+a value in a register is dropped, the AMDGPU-only occupancy attribute is
+dropped, and the single hipLaunchKernel call runs the kernel's workgroups on
+the host (emu_launch)."""
 import os
 import re
 import shutil
@@ -28,7 +30,15 @@ def rewrite(src: str) -> str:
     src = re.sub(r"__shared__\s+__attribute__\(\(aligned\(\d+\)\)\)\s+(\w+)\s+(\w+)\[([^\]]+)\];",
                  r"\1* \2 = reinterpret_cast<\1*>(::emu_lds(sizeof(\1) * (\3)));", src)
     src = src.replace('asm volatile("s_barrier" ::: "memory");', "::emu_barrier();")
+    # the empty register-pinning statement has no effect on the host
+    src = src.replace('asm volatile("" : "+v"(tid));', "(void)tid;")
     src = re.sub(r"__attribute__\(\(amdgpu_waves_per_eu\([^)]*\)\)\)", "", src)
+    # the one hipLaunchKernel call (in launch_kernel) runs the kernel on the host
+    launch = ("return hipLaunchKernel(reinterpret_cast<const void*>(k), grid, block, argv, "
+              "shm, stream);")
+    if src.count(launch) != 1:
+        raise RuntimeError("kernel source: expected exactly one hipLaunchKernel call")
+    src = src.replace(launch, "(void)argv; emu_launch(k, grid, block, v...); return hipSuccess;")
     if "__shared__" in src or "asm volatile" in src:
         raise RuntimeError("kernel source has a construct the emulation does not rewrite")
     return src

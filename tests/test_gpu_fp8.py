@@ -5,9 +5,8 @@
 * the forward, in both kernel orders (interleave and sync, on the same W8):
   every FP8 configuration on seeded shapes with ragged tails in M, N and K,
   launches that exercise the split tail, K = 0, and the five Qwen2.5-shaped
-  workloads at full size in the table's configuration (the
-  whole Y checked for unwritten or non-finite elements, sampled rows against
-  the oracle).  Bar: |y - y_ref| <= 0.01 |y_ref| + 2^-10 against the oracle's
+  workloads at full size in the table's configuration, every element of Y
+  against the oracle's full Y.  Bar: |y - y_ref| <= 0.01 |y_ref| + 2^-10 against the oracle's
   fp32 value computed from the same E4M3 codes and scales.
 
 Input recipe: the seeded bf16 draws of the bf16 tests (A ~ N(0, 1),
@@ -15,13 +14,15 @@ W ~ N(0, 1/K)), quantised by the oracle with one scale per tensor,
 scale = max|x| / 448 (the tensor's largest magnitude maps to the largest
 E4M3 value).
 """
+import time
+
 import numpy as np
 import pytest
 
 import gemm_epilogues_mlp_amd as sw
 import oracle
 from gemm_epilogues_mlp_amd import inputs as I
-from gpu_util import assert_parity, decode, empty_poisoned, host, log
+from gpu_util import assert_parity, decode, empty_poisoned, full_check, host, log
 
 pytestmark = pytest.mark.gpu
 
@@ -226,26 +227,28 @@ def workload(request):
     a, w1, w2 = I.workload_inputs(w)
     (a8, sa), (w18, s1), (w28, s2) = (quantised(I.bf16_bits_to_f32(x)) for x in (a, w1, w2))
     del a, w1, w2
-    rng = np.random.default_rng(w.index)
-    rows = np.unique(np.concatenate([[0, 1, w.M // 2, w.M - 1], rng.integers(0, w.M, 12)]))
-    y_ref = oracle.swiglu_fp8_rows(a8, w18, w28, sa, s1, s2, rows=rows)
+    t0 = time.perf_counter()
+    y_ref = oracle.swiglu_fp8_rows(a8, w18, w28, sa, s1, s2)
+    log(f"fp8 {w.name}: oracle full Y in {time.perf_counter() - t0:.1f} s")
     w8 = oracle.pack_fp8_kmajor(w18, w28)
     return dict(w=w, a8=a8, w8=w8, p8=oracle.pack_fp8_fragments(w8), w18=w18, w28=w28,
-                s=(sa, s1, s2), rows=rows, y_ref=y_ref)
+                s=(sa, s1, s2), y_ref=y_ref)
 
 
 @pytest.mark.parametrize("variant", [sw.VARIANT_AUTO, sw.VARIANT_SYNC, sw.VARIANT_FP8_PACKED],
                          ids=["auto", "sync", "packed"])
 def test_fp8_workload_parity(handle, workload, variant):
+    """Every output element of the FP8 forward at full size, in both kernel
+    orders and on fragment-ordered weights."""
     d = workload
     w = d["w"]
     cfg = sw.swiglu_query_fp8(handle, w.M, w.N, w.K, variant)
     log(f"fp8 {w.name} variant {variant}: config {cfg['id']}")
     wt = d["p8"] if variant == sw.VARIANT_FP8_PACKED else d["w8"]
     y = forward(handle, d["a8"], wt, w.M, w.N, w.K, d["s"], variant=variant)
-    yv = decode(y)
-    assert np.all(np.isfinite(yv)), "unwritten or non-finite outputs"
-    assert_parity(y[d["rows"]], d["y_ref"], f"fp8 {w.name} sampled rows")
+    s = full_check(y, d["y_ref"], f"fp8 {w.name} variant {variant}")
+    log(f"fp8 {w.name} variant {variant}: all {s['elements']} elements within the bar "
+        f"(worst {s['worst_frac']:.3f}); share > 1 % off: {s['rel_gt_1pct']:.2e}")
 
 
 def test_fp8_workload_device_pack_and_quantise_match(handle, workload):

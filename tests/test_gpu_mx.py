@@ -6,22 +6,24 @@ scale per 32 consecutive k) against the CPU oracle.
 * the bf16 k-major pairing W1, W2 [K, N] -> Wt [2N, K]: bit for bit;
 * the forward, every MX configuration on seeded shapes with ragged tails in M
   and N (K a multiple of 64), a split-tail launch, and the five Qwen2.5-shaped
-  workloads at full size (the whole Y checked for unwritten or non-finite
-  elements, sampled rows against the oracle); at full size the device's pack
-  and quantiser also reproduce the oracle's bits.  Bar: |y - y_ref| <=
+  workloads at full size (every element of Y against the oracle's full Y);
+  at full size the device's pack and quantiser also reproduce the oracle's
+  bits.  Bar: |y - y_ref| <=
   0.01 |y_ref| + 2^-10 against the oracle's value for the same codes and scales.
 
 Input recipe: the seeded bf16 draws of the bf16 tests (A ~ N(0, 1),
 W ~ N(0, 1/K)); A's rows and the rows of the k-major pairing of W1, W2 are
 quantised by the oracle's MX quantiser.
 """
+import time
+
 import numpy as np
 import pytest
 
 import gemm_epilogues_mlp_amd as sw
 import oracle
 from gemm_epilogues_mlp_amd import inputs as I
-from gpu_util import assert_parity, decode, empty_poisoned, host, log
+from gpu_util import assert_parity, decode, empty_poisoned, full_check, host, log
 
 pytestmark = pytest.mark.gpu
 
@@ -197,10 +199,10 @@ def workload(request):
     log(f"mx inputs for {w.name} M={w.M} K={w.K} N={w.N}")
     a, w1, w2 = I.workload_inputs(w)
     qa, sa, qw, sw_, wt = mx_inputs(a, w1, w2)
-    rng = np.random.default_rng(w.index)
-    rows = np.unique(np.concatenate([[0, 1, w.M // 2, w.M - 1], rng.integers(0, w.M, 12)]))
-    y_ref = oracle.swiglu_mx_rows(qa, sa, qw, sw_, rows=rows)
-    return dict(w=w, a=a, w1=w1, w2=w2, wt=wt, q=(qa, sa, qw, sw_), rows=rows, y_ref=y_ref)
+    t0 = time.perf_counter()
+    y_ref = oracle.swiglu_mx_rows(qa, sa, qw, sw_)
+    log(f"mx {w.name}: oracle full Y in {time.perf_counter() - t0:.1f} s")
+    return dict(w=w, a=a, w1=w1, w2=w2, wt=wt, q=(qa, sa, qw, sw_), y_ref=y_ref)
 
 
 def test_mx_workload_parity(handle, workload):
@@ -208,8 +210,9 @@ def test_mx_workload_parity(handle, workload):
     w = d["w"]
     log(f"mx {w.name}: config {sw.swiglu_query_fp8(handle, w.M, w.N, w.K, sw.VARIANT_MXFP8)['id']}")
     y = forward(handle, *d["q"], w.M, w.N, w.K)
-    assert np.all(np.isfinite(decode(y))), "unwritten or non-finite outputs"
-    assert_parity(y[d["rows"]], d["y_ref"], f"mx {w.name} sampled rows")
+    s = full_check(y, d["y_ref"], f"mx {w.name}")
+    log(f"mx {w.name}: all {s['elements']} elements within the bar (worst "
+        f"{s['worst_frac']:.3f}); share > 1 % off: {s['rel_gt_1pct']:.2e}")
 
 
 def test_mx_workload_device_pipeline_matches(handle, workload):
@@ -332,5 +335,6 @@ def test_mx_packed_workload_parity(handle, workload):
     log(f"mx packed {w.name}: config {cfg['id']}")
     p8 = oracle.pack_mx_fragments(qw)
     y = forward_packed(handle, qa, sa, p8, sw_, w.M, w.N, w.K)
-    assert np.all(np.isfinite(decode(y))), "unwritten or non-finite outputs"
-    assert_parity(y[d["rows"]], d["y_ref"], f"mx packed {w.name} sampled rows")
+    s = full_check(y, d["y_ref"], f"mx packed {w.name}")
+    log(f"mx packed {w.name}: all {s['elements']} elements within the bar (worst "
+        f"{s['worst_frac']:.3f})")

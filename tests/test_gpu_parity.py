@@ -11,7 +11,7 @@ import pytest
 import gemm_epilogues_mlp_amd as sw
 import oracle
 from gemm_epilogues_mlp_amd import inputs as I
-from gpu_util import Run, assert_parity, configs_of, decode, dev, host, log
+from gpu_util import Run, assert_parity, configs_of, decode, dev, host, log, rounding_check
 
 pytestmark = pytest.mark.gpu
 
@@ -76,10 +76,11 @@ def test_sync_config_parity(handle, cases, cfg, shape):
 @pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "x".join(map(str, s)))
 @pytest.mark.parametrize("cfg", configs_of(sw.VARIANT_GEMM))
 def test_unfused_config_parity(handle, cases, cfg, shape):
-    """Unfused baseline: G and U against the oracle's fp32 products, and the
-    separate gate kernel against the oracle's gate applied to the GPU's own
-    bf16 G and U (so a 1-ulp difference in a rounded intermediate cannot make
-    the check flaky)."""
+    """Unfused baseline: G and U against the oracle's fp32 products and as
+    their bf16 rounding (up to what the summation order changes), then the
+    separate gate kernel against the oracle's gate on those accepted G and U
+    (so a rounded intermediate that summation order moved by one bf16 step
+    cannot make the check flaky)."""
     M, N, K = shape
     c = cases[shape]
     log(f"unfused gemm config {cfg} {sw.swiglu_config_info(cfg)} shape {shape}")
@@ -87,6 +88,8 @@ def test_unfused_config_parity(handle, cases, cfg, shape):
     g, u, y = host(g), host(u), host(y)
     assert_parity(g, c["g"], f"unfused G cfg {cfg} {shape}")
     assert_parity(u, c["u"], f"unfused U cfg {cfg} {shape}")
+    rounding_check(g, c["g"], K, f"unfused G rounding cfg {cfg} {shape}")
+    rounding_check(u, c["u"], K, f"unfused U rounding cfg {cfg} {shape}")
     y_ref = oracle.gate(oracle.decode_bf16(g), oracle.decode_bf16(u))
     assert_parity(y, y_ref, f"unfused Y cfg {cfg} {shape}")
 
@@ -168,3 +171,38 @@ def test_k_zero_writes_zeros(handle):
         t.cuda.synchronize()
         assert np.all(decode(host(y)) == 0.0)
 
+
+
+def _persistent_configs():
+    return [i for i in range(sw.swiglu_config_count())
+            if sw.swiglu_config_info(i)["lds_bytes"] == 160 * 1024
+            and sw.swiglu_config_info(i)["variant"] in (sw.VARIANT_INTERLEAVE, sw.VARIANT_GEMM)]
+
+
+# shapes on which the persistent configurations run their tile loop (K a
+# whole number of 128-deep rings, at least two tiles per CU): a quarter-tile
+# last round, an unsplit partial last round, ragged M and N, several tiles per
+# workgroup
+PERSIST_SHAPES = {sw.VARIANT_INTERLEAVE: [(2048, 8960, 128), (4000, 9000, 256), (1280, 30000, 384)],
+                  sw.VARIANT_GEMM: [(4000, 8440, 128), (4000, 9400, 256), (2304, 16360, 384)]}
+
+
+@pytest.mark.parametrize("cfg", _persistent_configs())
+def test_persistent_parity(handle, cfg):
+    """The persistent tile loop (the next tile's loads under each tile's last
+    steps, Y staged through its own LDS region), every output element."""
+    from gpu_util import full_check
+    info = sw.swiglu_config_info(cfg)
+    for i, (M, N, K) in enumerate(PERSIST_SHAPES[info["variant"]]):
+        a, w1, w2 = _inputs(M, N, K, 900 + i)
+        log(f"persistent config {cfg} shape {(M, N, K)}")
+        if info["variant"] == sw.VARIANT_GEMM:
+            y, g, u = Run(handle).unfused(dev(a), dev(w1), dev(w2), M, N, K, cfg)
+            _, g_ref, u_ref = oracle.swiglu_rows(a, w1, w2, with_gate_up=True)
+            full_check(host(g), g_ref, f"persistent G cfg {cfg} {(M, N, K)}")
+            full_check(host(u), u_ref, f"persistent U cfg {cfg} {(M, N, K)}")
+        else:
+            wf = I.interleave_columns(w1, w2)
+            y = Run(handle).fused(dev(a), dev(wf), None, M, N, K, sw.LAYOUT_INTERLEAVED, cfg,
+                                  sw.VARIANT_INTERLEAVE)
+            full_check(host(y), oracle.swiglu_rows(a, w1, w2), f"persistent cfg {cfg} {(M, N, K)}")

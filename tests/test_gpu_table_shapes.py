@@ -17,7 +17,7 @@ import pytest
 import gemm_epilogues_mlp_amd as sw
 import oracle
 from gemm_epilogues_mlp_amd import inputs as I
-from gpu_util import assert_parity, decode, dev, empty_poisoned, host, log
+from gpu_util import assert_parity, decode, dev, empty_poisoned, host, log, rounding_check
 
 pytestmark = pytest.mark.gpu
 
@@ -46,8 +46,9 @@ def shard(request):
     M, K, N = request.param
     a, w1, w2 = I.make_inputs(M, K, N, 40 + SHARDS.index(request.param))
     rows = np.unique(np.r_[0, 1, M // 2, M - 1, np.random.default_rng(M + N).integers(0, M, 4)])
-    y_ref = oracle.swiglu_rows(a, w1, w2, rows=rows)
-    return dict(M=M, K=K, N=N, a=a, w1=w1, w2=w2, rows=rows, y_ref=y_ref)
+    y_ref, g_ref, u_ref = oracle.swiglu_rows(a, w1, w2, rows=rows, with_gate_up=True)
+    return dict(M=M, K=K, N=N, a=a, w1=w1, w2=w2, rows=rows, y_ref=y_ref, g_ref=g_ref,
+                u_ref=u_ref)
 
 
 @pytest.mark.parametrize("layout", [sw.LAYOUT_INTERLEAVED, sw.LAYOUT_SEPARATE, sw.LAYOUT_PACKED],
@@ -87,6 +88,10 @@ def test_shard_unfused(handle, shard):
     sw.swiglu_forward_unfused(handle, dev(d["a"]), dev(d["w1"]), dev(d["w2"]), ws, y, M, N, K)
     torch.cuda.synchronize()
     g, u = host(ws[0])[d["rows"]], host(ws[1])[d["rows"]]
+    # G and U: the bf16 rounding of the oracle's sums (up to summation order),
+    # then Y against the oracle's gate on those values
+    rounding_check(g, d["g_ref"], K, f"shard {(M, K, N)} unfused G")
+    rounding_check(u, d["u_ref"], K, f"shard {(M, K, N)} unfused U")
     assert_parity(host(y)[d["rows"]], oracle.gate(oracle.decode_bf16(g), oracle.decode_bf16(u)),
                   f"shard {(M, K, N)} unfused")
 

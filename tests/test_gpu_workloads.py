@@ -1,19 +1,30 @@
 """GPU parity at the full Qwen2.5-shaped workload sizes, in the launch
-configuration the benchmark times (the table's AUTO choice).
+configuration the benchmark times (the table's AUTO choice), on EVERY output
+element.
 
-The whole Y is checked for unwritten (NaN-poisoned) or non-finite elements;
-the oracle then recomputes sampled rows (every column) and sampled columns
-(every row), which together touch every output tile, and every sampled
-element must meet the parity bar.
+For each workload the oracle computes the whole Y (and the fp32 Gate and Up
+products g, u) once on the host; every fused layout is then checked element
+by element against it, and the page's accuracy statistic (share of elements
+more than 1 % off an FP32 reference, "Riepilogo Tecnico: Sovrapposizione
+delle Attivazioni...", §Contributi Chiave, item 3) must be 0.
+
+The unfused baseline stores Gate and Up as bf16 between its launches, so its
+reference is the oracle's unfused emulation: G and U must be the
+round-to-nearest-even of the oracle's g and u, up to what the summation order
+alone can change (a bf16 value that rounds some sum within 2^-20 sqrt(K) of
+the oracle's: another value only next to a rounding midpoint or near zero),
+and Y must meet the bar against SiLU(G) * U computed by the oracle on those
+accepted values.
 """
+import time
+
 import numpy as np
 import pytest
 
 import gemm_epilogues_mlp_amd as sw
 import oracle
 from gemm_epilogues_mlp_amd import inputs as I
-from gpu_util import (assert_parity, decode, dev, empty_poisoned, host, log,
-                      rel_err_share, violations)
+from gpu_util import dev, empty_poisoned, full_check, host, log, rounding_check, violations
 
 pytestmark = pytest.mark.gpu
 
@@ -25,62 +36,31 @@ def handle():
     sw.swiglu_destroy(h)
 
 
-def sample_rows(M, seed):
-    rng = np.random.default_rng(seed)
-    picks = [0, 1, M - 1, M // 2] + [b + d for b in (16, 32, 64, 128, 256) for d in (-1, 0)
-                                       if 0 <= b + d < M]
-    picks += list(rng.integers(0, M, 8))
-    return np.unique(np.array(picks, dtype=np.int64))
-
-
-def sample_cols(N, seed):
-    rng = np.random.default_rng(seed + 1)
-    picks = [0, 1, N - 1, N // 2] + [b + d for b in (32, 64, 128, 256) for d in (-1, 0)
-                                       if 0 <= b + d < N]
-    picks += list(rng.integers(0, N, 20))
-    return np.unique(np.array(picks, dtype=np.int64))
-
-
 @pytest.fixture(scope="module", params=I.WORKLOADS, ids=lambda w: w.name)
 def workload(request):
+    import torch
     w = request.param
     log(f"generating inputs for {w.name} M={w.M} K={w.K} N={w.N}")
     a, w1, w2 = I.workload_inputs(w)
-    rows = sample_rows(w.M, w.index)
-    cols = sample_cols(w.N, w.index)
-    y_r, g_r, u_r = oracle.swiglu_rows(a, w1, w2, rows=rows, with_gate_up=True)
-    y_c, g_c, u_c = oracle.swiglu_cols(a, w1, w2, cols=cols, with_gate_up=True)
-    d = dict(w=w, a=dev(a), w1=dev(w1), w2=dev(w2), rows=rows, cols=cols,
-             y_r=y_r, g_r=g_r, u_r=u_r, y_c=y_c, g_c=g_c, u_c=u_c)
-    import torch
-    wf = torch.empty((w.K, 2 * w.N), dtype=torch.int16, device="cuda")
+    t0 = time.perf_counter()
+    y_ref, g_ref, u_ref = oracle.swiglu_rows(a, w1, w2, with_gate_up=True)
+    log(f"{w.name}: oracle full Y ({w.M} x {w.N}) in {time.perf_counter() - t0:.1f} s")
+    d = dict(w=w, a=dev(a), w1=dev(w1), w2=dev(w2), y=y_ref, g=g_ref, u=u_ref)
     h = sw.swiglu_create(0)
+    wf = torch.empty((w.K, 2 * w.N), dtype=torch.int16, device="cuda")
     sw.swiglu_pack_interleaved(h, d["w1"], d["w2"], wf, w.K, w.N)
-    torch.cuda.synchronize()
-    sw.swiglu_destroy(h)
-    d["wf"] = wf
-    # pack kernel vs the host interleave on a few rows (bitwise)
-    ks = np.unique([0, w.K - 1, w.K // 3])
-    assert np.array_equal(host(wf[ks]), I.interleave_columns(w1[ks], w2[ks]))
-    # fragment-ordered W_fused: device pack vs the oracle's, whole buffer
     pk = torch.empty((sw.swiglu_packed_bytes(w.N, w.K) // 2,), dtype=torch.int16,
                      device="cuda")
-    h = sw.swiglu_create(0)
     sw.swiglu_pack_fragments(h, d["w1"], d["w2"], pk, w.K, w.N)
     torch.cuda.synchronize()
     sw.swiglu_destroy(h)
+    # both device packs against the oracle's, every value
+    assert np.array_equal(host(wf), oracle.pack_interleaved(w1, w2))
     assert np.array_equal(host(pk), oracle.pack_fragments(w1, w2))
-    d["pk"] = pk
+    d["wf"], d["pk"] = wf, pk
+    del a, w1, w2
     yield d
     del d
-
-
-def _check_sampled(y_full, d, what):
-    yb = host(y_full)
-    assert not np.isnan(decode(yb)).any(), f"{what}: unwritten or NaN outputs"
-    assert_parity(yb[d["rows"]], d["y_r"], f"{what} rows")
-    assert_parity(yb[:, d["cols"]], d["y_c"], f"{what} cols")
-    return yb
 
 
 @pytest.mark.parametrize("layout", [sw.LAYOUT_INTERLEAVED, sw.LAYOUT_SEPARATE,
@@ -99,17 +79,19 @@ def test_workload_fused_parity(handle, workload, layout):
     else:
         sw.swiglu_forward(handle, d["a"], d["w1"], d["w2"], y, w.M, w.N, w.K, layout)
     torch.cuda.synchronize()
-    yb = _check_sampled(y, d, f"{w.name} layout {layout}")
-    # the accuracy statistic of the page (share of elements > 1 % off): 0 expected
-    share = rel_err_share(yb[d["rows"]], d["y_r"])
-    log(f"{w.name} layout={layout}: share of sampled elements with rel err > 1 %: {share:.2e}")
-    assert share == 0.0
+    s = full_check(host(y), d["y"], f"{w.name} layout {layout}")
+    log(f"{w.name} layout={layout}: all {s['elements']} elements within the bar "
+        f"(worst {s['worst_frac']:.3f} of the allowance); share > 1 % off: "
+        f"{s['rel_gt_1pct']:.2e}")
+    # the accuracy statistic of the page for a fused kernel: 0
+    assert s["rel_gt_1pct"] == 0.0
 
 
 def test_workload_unfused(handle, workload):
-    """The unfused baseline at full size: G, U against the oracle's products;
-    Y against the oracle's gate on the GPU's own bf16 G, U; and the share of Y
-    elements that miss the fused bar against the plain oracle (reported)."""
+    """The unfused baseline at full size against the oracle's unfused
+    emulation, every element of G, U and Y; the share of Y elements that miss
+    the fused bar against the plain oracle is reported (bf16 Gate/Up, the
+    analogue of the page's finding for its cuBLAS baseline)."""
     import torch
     d, w = workload, workload["w"]
     tile = sw.swiglu_query_unfused(handle, w.M, w.N, w.K)
@@ -119,15 +101,18 @@ def test_workload_unfused(handle, workload):
     sw.swiglu_forward_unfused(handle, d["a"], d["w1"], d["w2"], ws, y, w.M, w.N, w.K)
     torch.cuda.synchronize()
     g, u, yb = host(ws[0]), host(ws[1]), host(y)
-    assert not np.isnan(decode(yb)).any()
-    rows, cols = d["rows"], d["cols"]
-    assert_parity(g[rows], d["g_r"], "unfused G rows")
-    assert_parity(u[rows], d["u_r"], "unfused U rows")
-    assert_parity(g[:, cols], d["g_c"], "unfused G cols")
-    assert_parity(u[:, cols], d["u_c"], "unfused U cols")
-    y_from_gu = oracle.gate(oracle.decode_bf16(g[rows]), oracle.decode_bf16(u[rows]))
-    assert_parity(yb[rows], y_from_gu, "unfused Y rows (gate of GPU G, U)")
-    miss = violations(yb[rows], d["y_r"]).mean()
-    log(f"{w.name} unfused: share of sampled Y outside the fused bar vs plain oracle: "
-        f"{miss:.2e}; rel err > 1 %: {rel_err_share(yb[rows], d['y_r']):.2e}")
     del ws, y
+    full_check(g, d["g"], f"{w.name} unfused G")
+    full_check(u, d["u"], f"{w.name} unfused U")
+    fg = rounding_check(g, d["g"], w.K, f"{w.name} unfused G rounding")
+    fu = rounding_check(u, d["u"], w.K, f"{w.name} unfused U rounding")
+    # the emulation on the accepted bf16 values (RNE of the oracle's g, u,
+    # or the other neighbour where the check above allowed it)
+    y_emul = oracle.gate(oracle.decode_bf16(g), oracle.decode_bf16(u))
+    full_check(yb, y_emul, f"{w.name} unfused Y vs the oracle's unfused emulation")
+    miss = 0
+    for r0 in range(0, w.M, 512):
+        miss += int(violations(yb[r0:r0 + 512], d["y"][r0:r0 + 512]).sum())
+    log(f"{w.name} unfused: {fg} G and {fu} U elements differ from RNE of the oracle's "
+        f"sums (summation order); Y outside the fused bar vs the plain oracle: {miss} of "
+        f"{w.M * w.N} ({miss / (w.M * w.N):.2e})")
