@@ -167,6 +167,12 @@ def swiglu_tuned_check(path: str) -> int:
     return n.value
 
 
+# Tuned configurations measured on MI355X for shapes beyond the five built-in
+# workload entries (tensor-parallel shares, other Qwen2.5 matrices, mid-size
+# batches); pass to swiglu_create_tuned.
+TUNED_MI355X = os.path.join(os.path.dirname(os.path.abspath(__file__)), "tuned_mi355x.txt")
+
+
 def swiglu_create_tuned(device: int = 0, path: str | None = None) -> int:
     h = ctypes.c_void_p()
     _check(load().swiglu_create_tuned(ctypes.byref(h), device,

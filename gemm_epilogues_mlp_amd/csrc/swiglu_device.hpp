@@ -103,49 +103,6 @@ __device__ __forceinline__ u32x2 lds_read_tr16(const void* p) {
   return __builtin_bit_cast(u32x2, v);
 }
 
-// The same two LDS reads addressed by an LDS byte offset (a constant added to
-// the offset folds into the instruction's immediate field).
-typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
-typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
-__device__ __forceinline__ u32x4 lds_load16_at(uint32_t addr) {
-  return *(const lds_u32x4*)(uintptr_t)addr;
-}
-__device__ __forceinline__ u32x2 lds_read_tr16_at(uint32_t addr) {
-  const i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(uintptr_t)addr);
-  return __builtin_bit_cast(u32x2, v);
-}
-
-// The same reads as inline assembly, with the LDS byte offset OFF folded into
-// the instruction.  The compiler does not see these as loads: it inserts no
-// waits for them, and the caller must wait (lgkm_wait) before reading the
-// result.  Used where the compiler's own wait placement is too conservative.
-template <int OFF>
-__device__ __forceinline__ u32x4 lds_load16_async(uint32_t addr) {
-  u32x4 r;
-  asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(OFF) : "memory");
-  return r;
-}
-template <int OFF>
-__device__ __forceinline__ u32x2 lds_read_tr16_async(uint32_t addr) {
-  u32x2 r;
-  asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(OFF) : "memory");
-  return r;
-}
-__device__ __forceinline__ u32x4 join(u32x2 lo, u32x2 hi) { return u32x4{lo[0], lo[1], hi[0], hi[1]}; }
-
-// Wait until at most N LDS reads of this wave are outstanding.  The values
-// passed in are tied to the wait, so their consumers cannot move above it.
-template <int N>
-__device__ __forceinline__ void lgkm_wait(u32x4& a) {
-  static_assert(N >= 0 && N <= 15, "lgkmcnt range");
-  asm volatile("s_waitcnt lgkmcnt(%1)" : "+v"(a) : "n"(N) : "memory");
-}
-template <int N>
-__device__ __forceinline__ void lgkm_wait(u32x4& a, u32x4& b, u32x4& c) {
-  static_assert(N >= 0 && N <= 15, "lgkmcnt range");
-  asm volatile("s_waitcnt lgkmcnt(%3)" : "+v"(a), "+v"(b), "+v"(c) : "n"(N) : "memory");
-}
-
 // SiLU(x) = x * sigmoid(x) = x / (1 + e^-x) in fp32 on the hardware exp and
 // reciprocal (each within about an ulp).  x << 0: e^-x -> +inf, rcp -> 0,
 // result -0; x >> 0: result x.  No NaN for finite x.

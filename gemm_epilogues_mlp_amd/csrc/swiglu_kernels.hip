@@ -16,7 +16,7 @@
 // Kernel families, all on the MFMA conventions in swiglu_device.hpp (each is
 // described in detail where it is defined):
 //
-//  * tiled_kernel / tiled_split_kernel / pingpong_kernel  LDS-tiled bf16,
+//  * tiled_kernel / tiled_split_kernel / tiled_persist_kernel  LDS-tiled bf16,
 //    v_mfma_f32_32x32x16_bf16, 4 or 8 waves.  A and weight k-tiles go from HBM
 //    straight into a ring of LDS stages by DMA; weight fragments are read with
 //    the transposing LDS read; the MFMA computes D^T = W^T A^T so that a Gate
@@ -816,261 +816,6 @@ __global__ __launch_bounds__(64 * WGM * WGN) void tiled_persist_kernel(
       tiled_tile<MODE, BM / 2, BNW / 2, BK, STAGES, SWGM, SWGN>(A, W, W, Y, M, N, K, ldw, ldy,
                                                                 m0, tq, smem);
     __syncthreads();  // the next quarter tile's loads overwrite this one's LDS
-  }
-}
-
-// ============================================================================
-// LDS-tiled MFMA kernel, ping-pong schedule
-// ============================================================================
-// Same tile (256 rows of A x 256 weight columns, K steps of 32), LDS layouts,
-// swizzles and direct HBM -> LDS loads as tiled_kernel, but the eight waves
-// split into two groups of four that take turns.  A workgroup's waves w and
-// w+4 run on the same SIMD, so with group = wave / 4 every SIMD holds one wave
-// of each group.  Each group owns 128 of the 256 rows (a wave: 64 rows x 128
-// weight columns, 8 accumulators of 32 x 32).  Time is cut into phases
-// separated by workgroup barriers; in every phase one group only issues MFMAs
-// (one whole K step, 16 per wave) while the other only moves data: it reads
-// all fragments of its next K step from LDS into registers and issues half of
-// a later K step's HBM -> LDS loads (group 0 the A tile, group 1 the weight
-// tile).  The matrix core of each SIMD is then fed by one wave while the other
-// wave's LDS and memory traffic runs beside it, instead of both waves mixing
-// the two kinds of work and stalling on each other.
-//
-// Phase q (0 <= q <= 2 nk):  group 0 loads fragments of step q/2 for even q
-// and computes step (q-1)/2 for odd q; group 1 runs one phase behind.  The
-// phase barriers do not wait for outstanding LDS reads: a wave's fragment
-// reads may still be in flight while its MFMAs start (each MFMA waits only
-// for its own operands), so a read of stage j % 5 can last until the end of
-// the phase after it.  Five stages (the whole 160 KB of LDS) keep that safe:
-// stage j % 5 holds step j from before phase 2j until the end of phase 2j+2,
-// and the loads of step j+3 are issued in phases 2j (A) and 2j+1 (weights)
-// into the stage that step j-2 left by the end of phase 2j-2.  Every wave
-// executes the same phases and barriers, whatever its role in each.
-template <int MODE>
-struct PingPong {
-  static constexpr int BM = 256, BNW = 256, BK = 32;
-  static constexpr int STAGES = 5, AHEAD = 3;  // LDS stages; K steps loaded ahead of the reads
-  using C = Tiled<MODE, BM, BNW, BK, 4, 2, 4>;  // stage layout and swizzles
-  static constexpr int BNY = C::BNY;
-  static constexpr int LDS_BYTES =
-      STAGES * C::STAGE_BYTES > C::Y_BYTES ? STAGES * C::STAGE_BYTES : C::Y_BYTES;
-  static_assert(LDS_BYTES <= 160 * 1024, "LDS");
-};
-
-template <int MODE>
-__global__ __launch_bounds__(512) void pingpong_kernel(const uint16_t* __restrict__ A,
-                                                       const uint16_t* __restrict__ W,
-                                                       uint16_t* __restrict__ Y, int M, int N,
-                                                       int K, int ldw, int ldy, int group_m) {
-  static_assert(MODE == MODE_INTERLEAVE || MODE == MODE_GEMM, "one weight tensor per K step");
-  using P = PingPong<MODE>;
-  constexpr int BM = P::BM, BNW = P::BNW, BK = P::BK, STAGES = P::STAGES, AHEAD = P::AHEAD;
-  using C = typename P::C;
-  constexpr int LDS_BYTES = P::LDS_BYTES;
-  static_assert(C::swizzles_permute_rows(), "LDS swizzle is not a permutation of a row");
-  static_assert(C::A_CHUNKS == 4 * 256 && C::W_CHUNKS == 4 * 256,
-                "each group moves its half of a K step in 4 loads per thread");
-  constexpr int LOADS = 4;       // DMA instructions per thread and phase
-  constexpr int FA = 2, FW = 4;  // 32-row and 32-column blocks of a wave
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[LDS_BYTES];
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave_u = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int grp = wave_u >> 2;  // 0: rows 0..127 and the A loads; 1: rows 128..255 and W loads
-  const int gw = wave_u & 3;    // wave within its group
-  const int gt = tid & 255;     // thread within its group
-
-  // ---- tile id (as tiled_kernel) ---------------------------------------------
-  const int ntm = (M + BM - 1) / BM;
-  const int ntn = (N + C::BNY - 1) / C::BNY;
-  int tm, tn;
-  tile_of(xcd_remap(blockIdx.x, gridDim.x), ntm, ntn, group_m, tm, tn);
-  const int m0 = tm * BM;
-  const int wc0 = tn * BNW;
-  const int y0 = tn * C::BNY;
-  const int nk = (K + BK - 1) / BK;
-
-  // ---- this thread's four DMA chunks of its group's half of a K step -----------
-  // chunk i of K step it: byte offset off[i] + k0 * kstride if k0 + lim[i] < K,
-  // else zeros (A: lim = k of the chunk, or huge past row M; weights: lim = 0,
-  // or huge past the last column; weight rows past K lie past the end of the
-  // buffer and read as zeros by themselves)
-  const int wcols = (MODE == MODE_INTERLEAVE) ? 2 * N : N;
-  const uint32_t wbytes = K > 0 ? (uint32_t)(((size_t)(K - 1) * ldw + wcols) * 2) : 0u;
-  const i32x4 rs = grp == 0 ? make_rsrc(A, (uint32_t)((size_t)M * K * 2)) : make_rsrc(W, wbytes);
-  const uint32_t kstride = grp == 0 ? 2u : (uint32_t)ldw * 2u;
-  const uint32_t lds0 = lds_addr(smem);
-  const uint32_t dma_dst = lds0 + (grp == 0 ? 0u : (uint32_t)C::A_BYTES) + 1024u * gw;
-  uint32_t off[LOADS];
-  int lim[LOADS];
-#pragma unroll
-  for (int i = 0; i < LOADS; ++i) {
-    const int p = gt + 256 * i;
-    const int arow = p / C::ACH, wrow = p / C::WCH;
-    const int ac = (p % C::ACH) ^ C::a_swz(arow);
-    const int wc = (p % C::WCH) ^ C::w_swz(wrow);
-    const bool win = wc0 + wc * 8 < wcols;
-    off[i] = grp == 0 ? (uint32_t)((m0 + arow) * K + ac * 8) * 2u
-                      : (uint32_t)(wrow * ldw + wc0 + wc * 8) * 2u;
-    lim[i] = grp == 0 ? (m0 + arow < M ? ac * 8 : 0x3fffffff) : (win ? 0 : 0x3fffffff);
-  }
-  // the group's half of K step `it` into stage it % STAGES (steps past the end
-  // load zeros, so every phase issues the same number of loads)
-  auto dma = [&](int it) __attribute__((always_inline)) {
-    const int k0 = it < nk ? it * BK : K;
-    const uint32_t dst = dma_dst + (uint32_t)(it % STAGES) * C::STAGE_BYTES;
-#pragma unroll
-    for (int i = 0; i < LOADS; ++i) {
-      const uint32_t o = k0 + lim[i] < K ? off[i] + (uint32_t)k0 * kstride : kOutOfRange;
-      lds_dma16(dst + 4096u * i, o, rs);  // chunks 256 i + 64 gw + lane
-    }
-  };
-
-  // ---- fragments of one K step (two 16-deep sub-steps) ---------------------------
-  // A: row rbase + 32 fa + lane % 32, k chunk 2 sub + lane / 32; the swizzle
-  // depends on row bits 1..3 only, so the fa blocks are 2 KB apart.
-  // W: columns cbase + 32 fw + 16 (g16 & 1) + 4 (s16 & 3), k rows
-  // 16 sub + 8 (g16 >> 1) + (s16 >> 2) + 4 h; the swizzle depends on k % 4
-  // only, so sub and h are whole rows apart.
-  const int g16 = lane >> 4, s16 = lane & 15;
-  const int rbase = 128 * grp + 64 * (gw >> 1);  // first A row of this wave
-  const int cbase = 128 * (gw & 1);              // first weight column of this wave
-  uint32_t a_at[2], w_at[FW];
-  {
-    const int row = rbase + (lane & 31);
-#pragma unroll
-    for (int sub = 0; sub < 2; ++sub)
-      a_at[sub] = lds0 + row * (BK * 2) + (((2 * sub + (lane >> 5)) ^ C::a_swz(row)) * 16);
-    const int krow = 8 * (g16 >> 1) + (s16 >> 2);
-#pragma unroll
-    for (int fw = 0; fw < FW; ++fw) {
-      const int col = cbase + 32 * fw + 16 * (g16 & 1) + 4 * (s16 & 3);
-      w_at[fw] = lds0 + C::A_BYTES + krow * (BNW * 2) + ((col >> 3) ^ C::w_swz(krow)) * 16 +
-                 ((col >> 2) & 1) * 8;
-    }
-  }
-  // Fragment reads are issued in a fixed order (r = 1..20: sub-step 0 A, A,
-  // then W blocks 0..3 two reads each; the same for sub-step 1) and waited
-  // for explicitly in the MFMA phase: an MFMA on W block fw of sub-step sub
-  // needs reads 1..10 sub + 2 fw + 4, i.e. at most 20 - that many still
-  // outstanding (the counter holds 15 at most).
-  u32x4 wf[2][FW], af[2][FA];
-  auto load_frags = [&](int it) __attribute__((always_inline)) {
-    const uint32_t so = (uint32_t)(it % STAGES) * C::STAGE_BYTES;
-    const uint32_t a0 = a_at[0] + so, a1 = a_at[1] + so;
-    uint32_t w[FW];
-#pragma unroll
-    for (int fw = 0; fw < FW; ++fw) w[fw] = w_at[fw] + so;
-    constexpr int ROW = BNW * 2;  // bytes per k row of the weight tile
-    af[0][0] = lds_load16_async<0>(a0);
-    af[0][1] = lds_load16_async<2048>(a0);
-    [&]<int... F>(std::integer_sequence<int, F...>) __attribute__((always_inline)) {
-      ((wf[0][F] = join(lds_read_tr16_async<0>(w[F]), lds_read_tr16_async<4 * ROW>(w[F]))), ...);
-    }(std::make_integer_sequence<int, FW>{});
-    af[1][0] = lds_load16_async<0>(a1);
-    af[1][1] = lds_load16_async<2048>(a1);
-    [&]<int... F>(std::integer_sequence<int, F...>) __attribute__((always_inline)) {
-      ((wf[1][F] = join(lds_read_tr16_async<16 * ROW>(w[F]), lds_read_tr16_async<20 * ROW>(w[F]))),
-       ...);
-    }(std::make_integer_sequence<int, FW>{});
-  };
-
-  f32x16 acc[FW][FA];
-#pragma unroll
-  for (int i = 0; i < FW; ++i)
-#pragma unroll
-    for (int j = 0; j < FA; ++j) acc[i][j] = f32x16{};
-
-  // ---- prologue: steps 0 .. AHEAD-1, each wave its group's half ----------------
-#pragma unroll
-  for (int it = 0; it < AHEAD; ++it) dma(it);
-  wait_vmcnt<(AHEAD - 1) * LOADS>();
-  __syncthreads();
-
-  // ---- phases ----------------------------------------------------------------------
-  // Group 0: [load j] | [MFMA j] | ... for j = 0..nk-1, then one idle phase.
-  // Group 1: one idle phase, then [load j] | [MFMA j] | ...  Both pass 2 nk
-  // barriers (none if K = 0).  Before every even phase 2j the loads of step j must have
-  // landed: each wave waits for its own (all but its last two groups of loads
-  // outstanding) right before the barrier that opens that phase.
-  auto compute = [&]() __attribute__((always_inline)) {
-    [&]<int... I>(std::integer_sequence<int, I...>) __attribute__((always_inline)) {
-      (
-          [&]() __attribute__((always_inline)) {
-            constexpr int sub = I / FW, fw = I % FW;
-            constexpr int need = 10 * sub + 2 * fw + 4;  // reads that must have landed
-            constexpr int left = 20 - need < 15 ? 20 - need : 15;
-            if constexpr (fw == 0) lgkm_wait<left>(wf[sub][fw], af[sub][0], af[sub][1]);
-            else lgkm_wait<left>(wf[sub][fw]);
-#pragma unroll
-            for (int k = 0; k < FA; ++k) acc[fw][k] = mfma32(wf[sub][fw], af[sub][k], acc[fw][k]);
-            __builtin_amdgcn_sched_barrier(0);
-          }(),
-          ...);
-    }(std::make_integer_sequence<int, 2 * FW>{});
-  };
-  // workgroup barrier that leaves LDS reads in flight (no fence: the memory
-  // clobber only keeps the compiler from moving memory accesses across it)
-  auto barrier = [&]() __attribute__((always_inline)) {
-    __builtin_amdgcn_sched_barrier(0);
-    asm volatile("s_barrier" ::: "memory");
-    __builtin_amdgcn_sched_barrier(0);
-  };
-  if (grp == 0) {
-    for (int j = 0; j < nk; ++j) {
-      dma(j + AHEAD);
-      load_frags(j);
-      barrier();
-      compute();
-      __builtin_amdgcn_sched_barrier(0);
-      wait_vmcnt<(AHEAD - 1) * LOADS>();
-      barrier();
-    }
-  } else {
-    if (nk > 0) barrier();
-    for (int j = 0; j < nk; ++j) {
-      dma(j + AHEAD);
-      load_frags(j);
-      wait_vmcnt<(AHEAD - 1) * LOADS>();
-      barrier();
-      compute();
-      if (j + 1 < nk) barrier();
-    }
-  }
-
-  // ---- epilogue: bf16 tile through LDS, then 16-byte row stores -------------------
-  wait_vmcnt<0>();
-  __syncthreads();
-  uint16_t* ys = reinterpret_cast<uint16_t*>(smem);  // [BM][YLD]
-  const int h32 = lane >> 5;
-#pragma unroll
-  for (int i = 0; i < FW; ++i)
-#pragma unroll
-    for (int k = 0; k < FA; ++k) {
-      const int row = rbase + 32 * k + (lane & 31);
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int wcl = cbase + i * 32 + 8 * q + 4 * h32;
-        const f32x16& d = acc[i][k];
-        if constexpr (MODE == MODE_INTERLEAVE) {
-          const float ya = silu(d[4 * q + 0]) * d[4 * q + 1];
-          const float yb = silu(d[4 * q + 2]) * d[4 * q + 3];
-          *reinterpret_cast<uint32_t*>(ys + row * C::YLD + wcl / 2) = pack_bf16x2(ya, yb);
-        } else {
-          *reinterpret_cast<u32x2*>(ys + row * C::YLD + wcl) =
-              u32x2{pack_bf16x2(d[4 * q], d[4 * q + 1]), pack_bf16x2(d[4 * q + 2], d[4 * q + 3])};
-        }
-      }
-    }
-  __syncthreads();
-  constexpr int YCH = C::BNY / 8;
-  for (int p = tid; p < BM * YCH; p += 512) {
-    const int row = p / YCH, cq = p % YCH;
-    const int gr = m0 + row, gc = y0 + cq * 8;
-    if (gr < M && gc < N)
-      *reinterpret_cast<u32x4*>(Y + (size_t)gr * ldy + gc) =
-          *reinterpret_cast<const u32x4*>(ys + row * C::YLD + cq * 8);
   }
 }
 
@@ -2515,19 +2260,6 @@ static hipError_t launch_tiled_persist(const LaunchArgs& a) {
                        a.M, a.N, a.K, a.ldw, a.ldy, group_m, (int)n_big, (int)(4 * tail));
 }
 
-template <int MODE>
-static hipError_t launch_pingpong(const LaunchArgs& a) {
-  using P = PingPong<MODE>;
-  const int ntm = (a.M + P::BM - 1) / P::BM, ntn = (a.N + P::BNY - 1) / P::BNY;
-  const long long nwg = (long long)ntm * ntn;
-  if (nwg <= 0) return hipSuccess;
-  if (nwg > 0x7fffffffLL) return hipErrorInvalidValue;
-  int group_m = a.group_m > 0 ? a.group_m : kGroupM;
-  if (group_m > ntm) group_m = ntm;
-  return launch_kernel(pingpong_kernel<MODE>, dim3((unsigned)nwg), dim3(512), 0, a.stream, a.A,
-                     a.W1, a.Y, a.M, a.N, a.K, a.ldw, a.ldy, group_m);
-}
-
 template <int MODE, int MT, int NW>
 static hipError_t launch_skinny(const LaunchArgs& a) {
   using C = Skinny<MODE, MT, NW>;
@@ -2644,11 +2376,9 @@ static hipError_t launch_mx_packed(const LaunchArgs& a) {
    Tiled<mode, bm, bnw, bk, st, wgm, wgn>::LDS_BYTES,                                       \
    &launch_tiled_split<mode, bm, bnw, bk, st, wgm, wgn, swgm, swgn>, 4}
 #define TILED_PERSIST(mode, v, bm, bnw, bk, st, wgm, wgn, swgm, swgn)                        \
-  {v, 0, bm, Tiled<mode, bm, bnw, bk, st, wgm, wgn>::BNY, bk, (wgm) * (wgn), 1,             \
+  {v, 2, bm, Tiled<mode, bm, bnw, bk, st, wgm, wgn>::BNY, bk, (wgm) * (wgn), 1,             \
    Persist<mode, bm, bnw, bk, st, wgm, wgn>::LDS_BYTES,                                     \
    &launch_tiled_persist<mode, bm, bnw, bk, st, wgm, wgn, swgm, swgn>, 4}
-#define PINGPONG(mode, v) \
-  {v, 2, 256, PingPong<mode>::BNY, 32, 8, 1, PingPong<mode>::LDS_BYTES, &launch_pingpong<mode>}
 #define PACKED(mt, nw, ch)                                                                 \
   {VAR_PACKED, 1, (mt) * 16, Packed<mt, nw, ch>::COLS_Y, 32, nw, nw,                          \
    Packed<mt, nw, ch>::LDS_BYTES, &launch_packed<mt, nw, ch>}
@@ -2700,9 +2430,10 @@ static const KernelConfig kConfigs[] = {
     TILED(MODE_GEMM, VAR_GEMM, 256, 256, 32, 4, 2, 4),              // 33
     TILED(MODE_SYNC, VAR_SYNC, 256, 128, 32, 4, 2, 4),              // 34
     TILED(MODE_INTERLEAVE, VAR_INTERLEAVE, 256, 192, 32, 4, 4, 2),  // 35
-    // ---- eight waves in two groups that alternate MFMA and memory phases ---
-    PINGPONG(MODE_INTERLEAVE, VAR_INTERLEAVE),                      // 36
-    PINGPONG(MODE_GEMM, VAR_GEMM),                                  // 37
+    // ---- the split 256-row tiles on one persistent workgroup per CU, the
+    //      next tile's loads running under each tile's last steps ----------
+    TILED_PERSIST(MODE_INTERLEAVE, VAR_INTERLEAVE, 256, 256, 32, 4, 4, 2, 2, 4),  // 36
+    TILED_PERSIST(MODE_GEMM, VAR_GEMM, 256, 256, 32, 4, 4, 2, 2, 4),              // 37
     // ---- eight waves as 4 x 2 (64-row wave tiles) for the other modes -----
     TILED(MODE_GEMM, VAR_GEMM, 256, 256, 32, 4, 4, 2),              // 38
     TILED(MODE_SYNC, VAR_SYNC, 256, 128, 32, 4, 4, 2),              // 39
@@ -2757,10 +2488,6 @@ static const KernelConfig kConfigs[] = {
     MX_PACKED(4, 1),                                                // 79
     MX_PACKED(1, 2),                                                // 80
     MX_PACKED(1, 4),                                                // 81
-    // ---- the split 256-row tiles on one persistent workgroup per CU, the
-    //      next tile's loads running under each tile's last steps ----------
-    TILED_PERSIST(MODE_INTERLEAVE, VAR_INTERLEAVE, 256, 256, 32, 4, 4, 2, 2, 4),  // 82
-    TILED_PERSIST(MODE_GEMM, VAR_GEMM, 256, 256, 32, 4, 4, 2, 2, 4),              // 83
 };
 
 int config_count() { return (int)(sizeof(kConfigs) / sizeof(kConfigs[0])); }

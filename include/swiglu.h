@@ -115,8 +115,9 @@ typedef struct swiglu_tile {
   int32_t family;      /* 0 = LDS-tiled MFMA 32x32x16 (FP8: 32x32x64 with
                           unit block scales), 1 = split-K streaming
                           MFMA 16x16x32 (weights straight to registers),
-                          2 = LDS-tiled with two wave groups alternating
-                          MFMA and memory phases (ping-pong)                  */
+                          2 = LDS-tiled on one persistent workgroup per
+                          CU looping over tiles, the next tile's loads
+                          issued under the current tile's last K steps     */
   int32_t bm;          /* output rows per workgroup                           */
   int32_t bn;          /* output (Y or G) columns per workgroup               */
   int32_t bk;          /* K depth of one pipeline stage                       */

@@ -142,35 +142,6 @@ inline u32x2 lds_read_tr16(const void* p) {
   memcpy(&r, p, 8);
   return r;
 }
-inline u32x4 lds_load16_at(uint32_t addr) {
-  emu_check_lds(addr, 16, "lds_load16_at");
-  u32x4 r;
-  memcpy(&r, emu_lds_base() + addr, 16);
-  return r;
-}
-inline u32x2 lds_read_tr16_at(uint32_t addr) {
-  emu_check_lds(addr, 8, "lds_read_tr16_at");
-  u32x2 r;
-  memcpy(&r, emu_lds_base() + addr, 8);
-  return r;
-}
-template <int OFF>
-inline u32x4 lds_load16_async(uint32_t addr) {
-  return lds_load16_at(addr + OFF);
-}
-template <int OFF>
-inline u32x2 lds_read_tr16_async(uint32_t addr) {
-  return lds_read_tr16_at(addr + OFF);
-}
-inline u32x4 join(u32x2 lo, u32x2 hi) { return u32x4{lo[0], lo[1], hi[0], hi[1]}; }
-template <int N>
-inline void lgkm_wait(u32x4&) {
-  static_assert(N >= 0 && N <= 15, "lgkmcnt range");
-}
-template <int N>
-inline void lgkm_wait(u32x4&, u32x4&, u32x4&) {
-  static_assert(N >= 0 && N <= 15, "lgkmcnt range");
-}
 inline float silu(float x) { return x / (1.0f + expf(-x)); }
 inline uint16_t bf16_bits(float x) { return __builtin_bit_cast(uint16_t, static_cast<__bf16>(x)); }
 inline uint32_t pack_bf16x2(float lo, float hi) {

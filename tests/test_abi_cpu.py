@@ -102,7 +102,9 @@ def test_config_list_is_consistent():
         assert c["family"] in (0, 1, 2)
         assert c["tail_split"] in (0, 4)
         if c["tail_split"]:
-            assert c["family"] == 0 and c["bm"] % 64 == 0 and c["bn"] % 64 == 0
+            assert c["family"] in (0, 2) and c["bm"] % 64 == 0 and c["bn"] % 64 == 0
+        if c["family"] == 2:  # persistent: one workgroup per CU, all of LDS
+            assert c["lds_bytes"] == 160 * 1024 and c["tail_split"] == 4
         # the MX streaming kernel uses no LDS (one wave, no reduction)
         assert 0 < c["lds_bytes"] <= 160 * 1024 or (c["variant"] == sw.VARIANT_MXFP8_PACKED
                                                    and c["lds_bytes"] == 0)

@@ -48,11 +48,11 @@ CASES = [
     (2048, 8960, 40, [40, 41, 42]),    # 1.5B M and N: 512 big + 48 split
     # the persistent tiles: whole rings of K (K = 128, 256), two or more tiles
     # per workgroup, with and without a quarter-tile last round, ragged M and N
-    (2048, 8960, 128, [82]),           # 560 tiles: 2 per workgroup + 48 as quarters
-    (4000, 8440, 256, [83]),           # 528 GEMM tiles: + 16 as quarters, ragged M and N
-    (4000, 9000, 128, [82]),           # 1136 tiles: a last round of 112, not split
-    (4000, 9400, 128, [83]),           # 592 GEMM tiles: a last round of 80, not split
-    (2048, 8960, 72, [82]),            # K not a whole ring: the split-tail launch
+    (2048, 8960, 128, [36]),           # 560 tiles: 2 per workgroup + 48 as quarters
+    (4000, 8440, 256, [37]),           # 528 GEMM tiles: + 16 as quarters, ragged M and N
+    (4000, 9000, 128, [36]),           # 1136 tiles: a last round of 112, not split
+    (4000, 9400, 128, [37]),           # 592 GEMM tiles: a last round of 80, not split
+    (2048, 8960, 72, [36]),            # K not a whole ring: the split-tail launch
     (128, 4864, 40, [3, 29, 30]),      # 0.5B M and N
     (16, 18944, 64, [23, 12, 18]),     # 7B decode M and N
     # the table's choices at one GPU's share under 8-way tensor parallelism
@@ -119,7 +119,7 @@ def test_table_configs_at_workload_sizes(emu, case):
 LIMIT_CASES = [
     (65536, 64, 16376, [40, 42, 41], 4),
     # the persistent tiles (K a whole number of rings: 2 * 65536 * 16256 B of A)
-    (65536, 512, 16256, [82, 83], 4),
+    (65536, 512, 16256, [36, 37], 4),
     (16, 32768, 16376, [4, 11, 18, 23, 12], 8),
     # fragment-ordered W_fused just under 2 GiB: 511 slabs x 512 steps x 8 KB
     (16, 32704, 16376, list(range(58, 70)), 8),

@@ -174,9 +174,7 @@ def test_k_zero_writes_zeros(handle):
 
 
 def _persistent_configs():
-    return [i for i in range(sw.swiglu_config_count())
-            if sw.swiglu_config_info(i)["lds_bytes"] == 160 * 1024
-            and sw.swiglu_config_info(i)["variant"] in (sw.VARIANT_INTERLEAVE, sw.VARIANT_GEMM)]
+    return [i for i in range(sw.swiglu_config_count()) if sw.swiglu_config_info(i)["family"] == 2]
 
 
 # shapes on which the persistent configurations run their tile loop (K a

@@ -77,3 +77,20 @@ def test_create_tuned_checks_the_file_before_the_device(tmp_path):
         with pytest.raises(sw.SwiGLUError) as e:
             sw.swiglu_create_tuned(0, _write(tmp_path, _header(), "ok.txt"))
         assert e.value.status == sw.ERR_DEVICE
+
+
+def test_shipped_tuned_file_matches_this_build():
+    """The package's tuned file for MI355X is signed for the compiled
+    configuration list, every entry names a configuration of its own variant,
+    and it adds only shapes beyond the five built-in workload entries."""
+    n = sw.swiglu_tuned_check(sw.TUNED_MI355X)
+    assert n > 0
+    five = {(128, 4864, 896), (2048, 8960, 1536), (16, 18944, 3584), (8192, 18944, 3584),
+            (4096, 29568, 8192)}
+    lines = [ln.split() for ln in open(sw.TUNED_MI355X)
+             if ln.strip() and not ln.startswith("#") and not ln.startswith("swiglu-tuned")]
+    assert len(lines) == n
+    for t in lines:
+        v, M, N, K, cid = (int(x) for x in t[:5])
+        assert (M, N, K) not in five
+        assert sw.swiglu_config_info(cid)["variant"] == v
