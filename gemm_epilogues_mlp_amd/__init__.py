@@ -88,6 +88,7 @@ def load():
                                i32, p], st),
         "swiglu_unfused_workspace_bytes": ([i64, i64], i64),
         "swiglu_forward_unfused": ([p, p, p, p, p, p, i64, i64, i64, i32, p], st),
+        "swiglu_forward_unfused_static": ([p, p, p, p, p, i64, i64, i64, i32, p], st),
         "swiglu_pack_interleaved": ([p, p, p, p, i64, i64, p], st),
         "swiglu_query": ([p, i64, i64, i64, ctypes.c_int, ctypes.POINTER(ctypes.c_int),
                           ctypes.POINTER(Tile), ctypes.POINTER(ctypes.c_int)], st),
@@ -206,6 +207,16 @@ def swiglu_forward_unfused(handle, A, W1, W2, workspace, Y, M, N, K, gemm_config
     _check(load().swiglu_forward_unfused(handle, _ptr(A), _ptr(W1), _ptr(W2), _ptr(workspace),
                                          _ptr(Y), M, N, K, gemm_config_id, _stream(stream)),
            "swiglu_forward_unfused")
+
+
+def swiglu_forward_unfused_static(handle, A, W1, W2, Y, M, N, K, gemm_config_id=-1,
+                                  stream=None):
+    _check(load().swiglu_forward_unfused_static(handle, _ptr(A), _ptr(W1), _ptr(W2), _ptr(Y),
+                                                M, N, K, gemm_config_id, _stream(stream)),
+           "swiglu_forward_unfused_static")
+
+
+STATIC_SCRATCH_BYTES = 128 * 1024 * 1024  # SWIGLU_STATIC_SCRATCH_BYTES in include/swiglu.h
 
 
 def swiglu_pack_interleaved(handle, W1, W2, W_fused, K, N, stream=None):

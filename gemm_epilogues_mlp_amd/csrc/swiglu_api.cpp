@@ -8,6 +8,7 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <mutex>
 #include <new>
 #include <vector>
 
@@ -25,7 +26,40 @@ struct swiglu_ctx {
   char arch[64];
   int log;  // SWIGLU_LOG=1: print the configuration chosen for each call
   std::vector<swiglu_tuned_entry> tuned;  // exact-shape overrides, read at creation
+  void* scratch;  // this device's copy of the fixed scratch array (device address)
 };
+
+// ---- fixed device scratch for callers that cannot allocate -------------------
+// swiglu_forward_unfused_static keeps the unfused baseline's bf16 Gate and Up
+// tensors here instead of in a caller workspace.  One copy per device, held
+// until the process ends; every call on a device shares it.  In host code the
+// array's name is only a stand-in: its device address on each device comes
+// from hipGetSymbolAddress (resolved once per device in swiglu_create, with
+// that device current) and only that address is ever passed to a kernel.
+static __device__ __align__(256) uint8_t scratch[SWIGLU_STATIC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_addr[kMaxDevices] = {};  // device address of `scratch`, per device
+
+// Device address of this device's `scratch` (resolving it on first use);
+// nullptr if it cannot be resolved.
+void* scratch_address(int device) {
+  if (device < 0 || device >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_addr[device]) return g_scratch_addr[device];
+  int prev = -1;
+  if (hipGetDevice(&prev) != hipSuccess) return nullptr;
+  if (prev != device && hipSetDevice(device) != hipSuccess) return nullptr;
+  void* ptr = nullptr;
+  const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+  if (prev != device) (void)hipSetDevice(prev);
+  if (e != hipSuccess || !ptr) return nullptr;
+  g_scratch_addr[device] = ptr;
+  return ptr;
+}
+}  // namespace
 
 namespace {
 
@@ -302,6 +336,11 @@ swiglu_status_t swiglu_create(swiglu_handle_t* out, int device) {
   h->arch[sizeof(h->arch) - 1] = 0;
   const char* lg = getenv("SWIGLU_LOG");
   h->log = (lg && lg[0] == '1') ? 1 : 0;
+  h->scratch = scratch_address(device);
+  if (!h->scratch) {
+    delete h;
+    return SWIGLU_ERR_DEVICE;
+  }
   *out = h;
   return SWIGLU_OK;
 }
@@ -348,6 +387,21 @@ swiglu_status_t swiglu_forward_unfused(swiglu_handle_t h, const void* A, const v
                                        int64_t N, int64_t K, int32_t gemm_config_id,
                                        hipStream_t stream) {
   return unfused(h, A, W1, W2, workspace, Y, M, N, K, gemm_config_id, stream);
+}
+
+swiglu_status_t swiglu_forward_unfused_static(swiglu_handle_t h, const void* A,
+                                              const void* W1, const void* W2, void* Y,
+                                              int64_t M, int64_t N, int64_t K,
+                                              int32_t gemm_config_id, hipStream_t stream) {
+  if (!h) return SWIGLU_ERR_INVALID_ARG;
+  if (M >= 0 && N >= 0 && N <= (kMaxDim >> 1) && M <= kMaxDim &&
+      4LL * M * N > SWIGLU_STATIC_SCRATCH_BYTES) {
+    if (h->log)
+      fprintf(stderr, "[swiglu] unfused_static: Gate and Up need %lld bytes, the fixed "
+              "scratch holds %lld\n", 4LL * M * N, (long long)SWIGLU_STATIC_SCRATCH_BYTES);
+    return SWIGLU_ERR_UNSUPPORTED;
+  }
+  return unfused(h, A, W1, W2, h->scratch, Y, M, N, K, gemm_config_id, stream);
 }
 
 swiglu_status_t swiglu_pack_interleaved(swiglu_handle_t h, const void* W1, const void* W2,

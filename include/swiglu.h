@@ -130,8 +130,12 @@ typedef struct swiglu_tile {
 } swiglu_tile_t;
 
 /* Create a handle for HIP device `device`.  Checks that the device exists and
- * is gfx950; reads its compute-unit count.  *out is set to NULL on error.
- * Errors: INVALID_ARG (out NULL), DEVICE, ALLOC. */
+ * is gfx950; reads its compute-unit count; the first handle on a device also
+ * resolves that device's address of the fixed scratch array of
+ * swiglu_forward_unfused_static (making the device current for that lookup
+ * and restoring the caller's current device).  *out is set to NULL on error.
+ * Errors: INVALID_ARG (out NULL), DEVICE (also: the scratch address could not
+ * be resolved), ALLOC. */
 swiglu_status_t swiglu_create(swiglu_handle_t* out, int device);
 
 /* Release a handle (NULL is accepted).  No call using it may be executing. */
@@ -172,6 +176,30 @@ swiglu_status_t swiglu_forward_unfused(swiglu_handle_t h, const void* A,
                                        void* workspace, void* Y, int64_t M,
                                        int64_t N, int64_t K, int32_t gemm_config_id,
                                        hipStream_t stream);
+
+/* Size of the fixed device scratch array of swiglu_forward_unfused_static:
+ * 128 MiB on each device the library runs on (Gate and Up of M * N <= 2^25
+ * outputs, e.g. the Qwen2.5-1.5B MLP at M = 2048). */
+#define SWIGLU_STATIC_SCRATCH_BYTES (128LL * 1024 * 1024)
+
+/* The unfused baseline with no allocation of any kind, for callers that
+ * cannot allocate device memory: code running under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc.  The same launches and
+ * result as swiglu_forward_unfused, but G and U live in a fixed array of
+ * SWIGLU_STATIC_SCRATCH_BYTES that the library holds on each device from its
+ * first swiglu_create there until the process ends, instead of a caller
+ * workspace.  The caller still passes A, W1, W2 and Y (separate layout).
+ * 4 * M * N > SWIGLU_STATIC_SCRATCH_BYTES gives SWIGLU_ERR_UNSUPPORTED with
+ * nothing enqueued; the other argument rules and errors are those of
+ * swiglu_forward_unfused.  Every call on one device shares that device's
+ * array, which keeps the last call's Gate and Up (nothing in it has to start
+ * at zero): calls that can overlap on one device -- on different streams, from
+ * different host threads or handles -- race on it, and the caller must order
+ * them (one stream, or events). */
+swiglu_status_t swiglu_forward_unfused_static(swiglu_handle_t h, const void* A,
+                                              const void* W1, const void* W2, void* Y,
+                                              int64_t M, int64_t N, int64_t K,
+                                              int32_t gemm_config_id, hipStream_t stream);
 
 /* Build W_fused [K, 2N] from W1, W2 [K, N] [RT §Metodologia, Kernel-2]:
  * W_fused[k, 2n] = W1[k, n], W_fused[k, 2n+1] = W2[k, n].  A bit copy done

@@ -55,6 +55,8 @@ def test_null_handle_and_bad_arguments_rejected():
     assert lib.swiglu_forward(None, 16, 16, 16, 16, 8, 8, 8, 0, None) == sw.ERR_INVALID_ARG
     assert lib.swiglu_forward_unfused(None, 16, 16, 16, 16, 16, 8, 8, 8, -1, None) == \
         sw.ERR_INVALID_ARG
+    assert lib.swiglu_forward_unfused_static(None, 16, 16, 16, 16, 8, 8, 8, -1, None) == \
+        sw.ERR_INVALID_ARG
     assert lib.swiglu_pack_interleaved(None, 16, 16, 16, 8, 8, None) == sw.ERR_INVALID_ARG
     assert lib.swiglu_query(None, 8, 8, 8, 0, None, None, None) == sw.ERR_INVALID_ARG
     assert lib.swiglu_create(None, 0) == sw.ERR_INVALID_ARG
