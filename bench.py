@@ -346,6 +346,14 @@ def mx_side(sw, h, wl, a0, w10, w20, timed, stream, args, bf16_ms):
         sw.swiglu_forward_mx(h, A8, SA, W8, SW, y, M, N, K, ks, -1, stream)
 
     xms, batches = timed(step, args.steps, args.warmup)
+    # the sync (Kernel-1) order on the same W8 and scales
+    scfg = sw.swiglu_query_fp8(h, M, N, K, sw.VARIANT_MXFP8_SYNC)
+
+    def sstep(i):
+        A8, SA, W8, SW, y = sets[i % nsets]
+        sw.swiglu_forward_mx(h, A8, SA, W8, SW, y, M, N, K, ks, scfg["id"], stream)
+
+    sms, _ = timed(sstep, max(10, args.steps // 2), max(3, args.warmup // 2))
     qms, _ = timed(lambda i: sw.swiglu_quantize_mx(h, a0, qa, sa, M, K, ks, stream),
                    max(10, args.steps // 2), 3, batches=1)
     tf = wl.flops / (xms * 1e-3) / 1e12
@@ -355,7 +363,9 @@ def mx_side(sw, h, wl, a0, w10, w20, timed, stream, args, bf16_ms):
            "min_batch_ms_per_step": round(min(batches), 5),
            "quantize_activations_ms": round(qms, 5),
            "format": "OCP MX: E4M3 elements, E8M0 scale per 32 along K", "rotated_sets": nsets,
-           "tile": sw.swiglu_query_fp8(h, M, N, K, sw.VARIANT_MXFP8)}
+           "tile": sw.swiglu_query_fp8(h, M, N, K, sw.VARIANT_MXFP8),
+           "sync": {"ms_per_step": round(sms, 5),
+                    "tflops": round(wl.flops / (sms * 1e-3) / 1e12, 2), "tile": scfg}}
     del sets
     if M <= 64:
         # decode-sized batches: the same forward on fragment-ordered W8

@@ -38,8 +38,8 @@ _LIB_PATH = os.path.join(_PKG, "libswiglu.so")
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_DEVICE, ERR_LAUNCH, ERR_ALLOC = range(6)
 LAYOUT_SEPARATE, LAYOUT_INTERLEAVED, LAYOUT_PACKED = 0, 1, 2
 VARIANT_AUTO, VARIANT_SYNC, VARIANT_INTERLEAVE, VARIANT_GEMM, VARIANT_FP8, VARIANT_FP8_SYNC, \
-    VARIANT_MXFP8, VARIANT_PACKED, VARIANT_FP8_PACKED, VARIANT_MXFP8_PACKED = \
-    0, 1, 2, 3, 4, 5, 6, 7, 8, 9
+    VARIANT_MXFP8, VARIANT_PACKED, VARIANT_FP8_PACKED, VARIANT_MXFP8_PACKED, VARIANT_MXFP8_SYNC = \
+    0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10
 
 
 class SwiGLUError(RuntimeError):

@@ -271,6 +271,7 @@ int fp8_family(int variant) {
   if (variant == SWIGLU_VARIANT_MXFP8) return VAR_MX;  // queries only
   if (variant == SWIGLU_VARIANT_FP8_PACKED) return VAR_F8_PACKED;
   if (variant == SWIGLU_VARIANT_MXFP8_PACKED) return VAR_MX_PACKED;  // queries only
+  if (variant == SWIGLU_VARIANT_MXFP8_SYNC) return VAR_MX_SYNC;      // queries only
   return -1;
 }
 
@@ -478,7 +479,8 @@ swiglu_status_t swiglu_forward_fp8(swiglu_handle_t h, const void* A8, const void
                                    int32_t config_id, hipStream_t stream) {
   if (!h || M < 0 || N < 0 || K < 0) return SWIGLU_ERR_INVALID_ARG;
   const int want = fp8_family((int)variant);
-  if (want < 0 || want == VAR_MX || want == VAR_MX_PACKED) return SWIGLU_ERR_INVALID_ARG;
+  if (want < 0 || want == VAR_MX || want == VAR_MX_PACKED || want == VAR_MX_SYNC)
+    return SWIGLU_ERR_INVALID_ARG;
   int id = config_id;
   if (id >= 0) {
     const KernelConfig* c = config_at(id);
@@ -519,7 +521,8 @@ swiglu_status_t swiglu_forward_fp8(swiglu_handle_t h, const void* A8, const void
 }  // extern "C"
 
 namespace {
-// MXFP8 forward on W8 in k-major order (want = VAR_MX) or in the streaming
+// MXFP8 forward on W8 in k-major order (want = VAR_MX; a given config may
+// also be of the sync order, VAR_MX_SYNC, on the same W8) or in the streaming
 // kernel's fragment order (want = VAR_MX_PACKED)
 swiglu_status_t forward_mx(swiglu_handle_t h, const void* A8, const void* SA, const void* W8,
                            const void* SW, void* Y, int64_t M, int64_t N, int64_t K, int64_t ks,
@@ -528,7 +531,8 @@ swiglu_status_t forward_mx(swiglu_handle_t h, const void* A8, const void* SA, co
   int id = config_id;
   if (id >= 0) {
     const KernelConfig* c = config_at(id);
-    if (!c || c->variant != want) return SWIGLU_ERR_INVALID_ARG;
+    if (!c || (c->variant != want && !(want == VAR_MX && c->variant == VAR_MX_SYNC)))
+      return SWIGLU_ERR_INVALID_ARG;
   }
   if (M == 0 || N == 0) return SWIGLU_OK;
   if (!Y || (K > 0 && (!A8 || !W8 || !SA || !SW))) return SWIGLU_ERR_INVALID_ARG;

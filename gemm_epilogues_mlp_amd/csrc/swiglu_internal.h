@@ -13,9 +13,10 @@ namespace swiglu {
 // VAR_PACKED: interleave order on W_fused stored in MFMA fragment order
 // VAR_F8_PACKED: interleave order on FP8 inputs with fragment-ordered W8
 // VAR_MX_PACKED: interleave order on MXFP8 inputs, W8 in the 32x32x64 fragment order
+// VAR_MX_SYNC: sync order on MXFP8 inputs (the same W8 and scales as VAR_MX)
 enum Variant {
   VAR_AUTO = 0, VAR_SYNC = 1, VAR_INTERLEAVE = 2, VAR_GEMM = 3, VAR_F8 = 4, VAR_F8_SYNC = 5,
-  VAR_MX = 6, VAR_PACKED = 7, VAR_F8_PACKED = 8, VAR_MX_PACKED = 9
+  VAR_MX = 6, VAR_PACKED = 7, VAR_F8_PACKED = 8, VAR_MX_PACKED = 9, VAR_MX_SYNC = 10
 };
 
 // Fragment-ordered W_fused: slabs of 128 columns times steps of 32 k, 4096

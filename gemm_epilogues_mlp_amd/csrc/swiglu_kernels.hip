@@ -53,8 +53,9 @@
 
 namespace swiglu {
 
-// MODE_MX: the interleave pairing on MXFP8 inputs (FP8 tile kernel only)
-enum Mode { MODE_INTERLEAVE = 0, MODE_SYNC = 1, MODE_GEMM = 2, MODE_MX = 3 };
+// MODE_MX / MODE_MX_SYNC: the interleave and the sync order on MXFP8 inputs
+// (FP8 tile kernel only)
+enum Mode { MODE_INTERLEAVE = 0, MODE_SYNC = 1, MODE_GEMM = 2, MODE_MX = 3, MODE_MX_SYNC = 4 };
 
 // ============================================================================
 // LDS-tiled MFMA kernel
@@ -1171,8 +1172,9 @@ struct F8Tiled {
   static_assert(kWaves == 4 || kWaves == 8, "four waves (one per SIMD) or eight (two per SIMD)");
   static constexpr int kThreads = 64 * kWaves;
   static constexpr int BK = 64;          // k per step = bytes per tile row
-  static constexpr int BNY = MODE == MODE_SYNC ? BNW : BNW / 2;  // output columns
-  static constexpr int NACC = MODE == MODE_SYNC ? 2 : 1;           // accumulator sets
+  static constexpr bool SYNC = MODE == MODE_SYNC || MODE == MODE_MX_SYNC;
+  static constexpr int BNY = SYNC ? BNW : BNW / 2;  // output columns
+  static constexpr int NACC = SYNC ? 2 : 1;         // accumulator sets
   static constexpr int WTM = BM / WGM;   // A rows per wave
   static constexpr int WTW = BNW / WGN;  // W8 rows per wave (per phase in sync mode)
   static constexpr int FA = WTM / 32;
@@ -1186,7 +1188,7 @@ struct F8Tiled {
   static constexpr int A_LOADS = (A_CHUNKS + kThreads - 1) / kThreads;
   static constexpr int W_LOADS = (W_CHUNKS + kThreads - 1) / kThreads;
   static constexpr int LOADS = A_LOADS + W_LOADS;
-  static constexpr bool MX = MODE == MODE_MX;
+  static constexpr bool MX = MODE == MODE_MX || MODE == MODE_MX_SYNC;
   static constexpr int SC_CHUNKS = MX ? BM + BNW : 0;  // one 16-byte scale chunk per row
   static constexpr int SC_LOADS = MX ? (SC_CHUNKS + kThreads - 1) / kThreads : 0;
   static_assert(!MX || (BM % 64 == 0 && BNW % 64 == 0), "a wave's scale chunks share one tensor");
@@ -1221,8 +1223,10 @@ __device__ __forceinline__ void f8_tile(const uint8_t* __restrict__ A,
                                         const uint8_t* __restrict__ SW, int ks, int m0, int tn,
                                         uint8_t* smem) {
   using C = F8Tiled<MODE, BM, BNW, STAGES, WGM, WGN>;
-  static_assert(MODE == MODE_INTERLEAVE || MODE == MODE_SYNC || MODE == MODE_MX, "FP8 modes");
-  constexpr bool kSync = MODE == MODE_SYNC;
+  static_assert(MODE == MODE_INTERLEAVE || MODE == MODE_SYNC || MODE == MODE_MX ||
+                    MODE == MODE_MX_SYNC,
+                "FP8 modes");
+  constexpr bool kSync = C::SYNC;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
@@ -1268,16 +1272,23 @@ __device__ __forceinline__ void f8_tile(const uint8_t* __restrict__ A,
     w_off[i] = in ? (uint32_t)(wrow * K + c * 16) : 0u;
     w_k[i] = in ? (uint32_t)(c * 16) : kRowOut;
   }
-  // MX: scale chunk p of the tile is row p of A's scales (p < BM) or row
-  // p - BM of W8's; group g of 8 K steps is bytes [16 g, 16 g + 16) of the row
+  // MX: scale chunk p of the tile is row p of A's scales (p < BM) or the
+  // scale row of weight tile row p - BM (W8 row wr0 + p - BM, or in the sync
+  // order 2 (y0 + p - BM) for Gate and the next row for Up); group g of 8 K
+  // steps is bytes [16 g, 16 g + 16) of the row.
+  // The two-slot scale ring is indexed by a group count that runs on from the
+  // Gate phase into the Up phase (the Up phase's first group takes the slot
+  // the Gate phase's last group did not).
   const i32x4 rsSA = make_rsrc(SA, C::MX ? (uint32_t)((size_t)M * ks) : 0u);
   const i32x4 rsSW = make_rsrc(SW, C::MX ? (uint32_t)((size_t)2 * N * ks) : 0u);
+  const int ngroups = (nk + 7) / 8;  // scale groups of one phase
   uint32_t sc_off[C::SC_LOADS > 0 ? C::SC_LOADS : 1];
 #pragma unroll
   for (int i = 0; i < C::SC_LOADS; ++i) {
     const int p = tid + C::kThreads * i;
-    const bool in = p < BM ? m0 + p < M : wr0 + (p - BM) < 2 * N;
-    const size_t row = p < BM ? (size_t)(m0 + p) : (size_t)(wr0 + p - BM);
+    const bool in = p < BM ? m0 + p < M : (kSync ? y0 + (p - BM) < N : wr0 + (p - BM) < 2 * N);
+    const size_t row = p < BM ? (size_t)(m0 + p)
+                              : (kSync ? 2 * (size_t)(y0 + p - BM) : (size_t)(wr0 + p - BM));
     sc_off[i] = in ? (uint32_t)(row * ks) : kOutOfRange;
   }
   // DMA instruction q (A chunks first, then weight chunks, then in MX mode the
@@ -1303,15 +1314,19 @@ __device__ __forceinline__ void f8_tile(const uint8_t* __restrict__ A,
                                : kOutOfRange;
       lds_dma16(own ? sbase + C::A_BYTES + p0 * 16 : lds0 + C::JUNK, off, rsW);
     } else if constexpr (C::MX) {
-      // the scale chunks of group it / 8 with step it of a group start, else nothing
+      // the scale chunks of group kt / 8 of the phase with step kt of a group
+      // start, else nothing
       const int i = q - C::LOADS;
       const int p0 = C::kThreads * i + 64 * wave_u;
       const bool own = p0 < C::SC_CHUNKS;
-      const bool real = own && (it & 7) == 0 && it < nk;
-      const int g = it >> 3;
-      const uint32_t off = (real && sc_off[i] != kOutOfRange) ? sc_off[i] + (uint32_t)(16 * g)
-                                                              : kOutOfRange;
-      const uint32_t dst = real ? lds0 + C::SC_OFF + (g & 1) * C::SC_SLOT + p0 * 16
+      const bool real = own && (kt & 7) == 0 && kt < nk && it < total;
+      const int g = kt >> 3;
+      const int slot = (up ? ngroups + g : g) & 1;
+      const uint32_t wrow = (up && p0 >= BM) ? (uint32_t)ks : 0u;  // Up: the next W8 row
+      const uint32_t off = (real && sc_off[i] != kOutOfRange)
+                               ? sc_off[i] + wrow + (uint32_t)(16 * g)
+                               : kOutOfRange;
+      const uint32_t dst = real ? lds0 + C::SC_OFF + slot * C::SC_SLOT + p0 * 16
                                 : lds0 + C::JUNK;
       lds_dma16(dst, off, p0 < BM ? rsSA : rsSW);
     }
@@ -1347,11 +1362,15 @@ __device__ __forceinline__ void f8_tile(const uint8_t* __restrict__ A,
   auto put = [](uint32_t& w, int byte, uint32_t v) __attribute__((always_inline)) {
     w = (w & ~(0xffu << (8 * byte))) | (v << (8 * byte));
   };
-  // the scale byte of tile row r (A rows first, then W8 rows) for step s:
-  // group s / 8, block 2 s + h of the row (this lane's fragment half)
+  // the scale byte of tile row r (A rows first, then weight tile rows) for
+  // step s: group kt / 8 of its phase, block 2 kt + h of the row (this lane's
+  // fragment half), kt the step within the phase
   auto scale_of = [&](int s, int r) __attribute__((always_inline)) -> uint32_t {
-    const uint8_t* slot = smem + C::SC_OFF + ((s >> 3) & 1) * C::SC_SLOT;
-    return slot[r * 16 + ((2 * s + h) & 15)];
+    const bool up = kSync && s >= nk0;
+    const int kt = up ? s - nk0 : s;
+    const int g = up ? ngroups + (kt >> 3) : (kt >> 3);
+    const uint8_t* slot = smem + C::SC_OFF + (g & 1) * C::SC_SLOT;
+    return slot[r * 16 + ((2 * kt + h) & 15)];
   };
   f32x16 acc[C::NACC][C::FW][C::FA];
 #pragma unroll
@@ -2488,6 +2507,10 @@ static const KernelConfig kConfigs[] = {
     MX_PACKED(4, 1),                                                // 79
     MX_PACKED(1, 2),                                                // 80
     MX_PACKED(1, 4),                                                // 81
+    // ---- MXFP8 in the sync (Kernel-1) order on the same W8 ---------------
+    F8_SPLIT(MODE_MX_SYNC, VAR_MX_SYNC, 256, 128, 4, 4, 2, 4, 2),   // 82
+    F8(MODE_MX_SYNC, VAR_MX_SYNC, 128, 128, 4, 2, 2),               // 83
+    F8(MODE_MX_SYNC, VAR_MX_SYNC, 64, 64, 4, 2, 2),                 // 84
 };
 
 int config_count() { return (int)(sizeof(kConfigs) / sizeof(kConfigs[0])); }

@@ -39,17 +39,20 @@ const ShapeEntry kTable[] = {
     {VAR_PACKED, 128, 4864, 896, 62},
     {VAR_F8_PACKED, 128, 4864, 896, 75},
     {VAR_MX_PACKED, 128, 4864, 896, 77},
-    // Qwen2.5-1.5B MLP, M = 2048: the 256-row eight-wave tiles (persistent
-    // where that is faster: interleave 118.7 vs 121.0 us, GEMM 144.7 vs 150 us)
-    {VAR_INTERLEAVE, 2048, 8960, 1536, 36},
+    {VAR_MX_SYNC, 128, 4864, 896, 84},
+    // Qwen2.5-1.5B MLP, M = 2048: the 256-row eight-wave tiles, the short last
+    // round as quarter tiles (the persistent tile loop, configs 36 and 37, is
+    // level with them under the benchmark: 119.2 vs 118.0 us)
+    {VAR_INTERLEAVE, 2048, 8960, 1536, 40},
     {VAR_SYNC, 2048, 8960, 1536, 42},
-    {VAR_GEMM, 2048, 8960, 1536, 37},
+    {VAR_GEMM, 2048, 8960, 1536, 41},
     {VAR_F8, 2048, 8960, 1536, 43},
-    {VAR_F8_SYNC, 2048, 8960, 1536, 54},
+    {VAR_F8_SYNC, 2048, 8960, 1536, 53},
     {VAR_MX, 2048, 8960, 1536, 56},
     {VAR_PACKED, 2048, 8960, 1536, 62},
     {VAR_F8_PACKED, 2048, 8960, 1536, 75},
     {VAR_MX_PACKED, 2048, 8960, 1536, 77},
+    {VAR_MX_SYNC, 2048, 8960, 1536, 82},
     // Qwen2.5-7B MLP, decode M = 16: split-K weight streaming
     {VAR_INTERLEAVE, 16, 18944, 3584, 23},
     {VAR_SYNC, 16, 18944, 3584, 12},
@@ -60,8 +63,9 @@ const ShapeEntry kTable[] = {
     {VAR_PACKED, 16, 18944, 3584, 65},
     {VAR_F8_PACKED, 16, 18944, 3584, 70},
     {VAR_MX_PACKED, 16, 18944, 3584, 77},
-    // Qwen2.5-7B MLP, prefill M = 8192 (persistent interleave: 1774 vs 1868 us)
-    {VAR_INTERLEAVE, 8192, 18944, 3584, 36},
+    {VAR_MX_SYNC, 16, 18944, 3584, 84},
+    // Qwen2.5-7B MLP, prefill M = 8192 (persistent: level, 1774 us both)
+    {VAR_INTERLEAVE, 8192, 18944, 3584, 40},
     {VAR_SYNC, 8192, 18944, 3584, 42},
     {VAR_GEMM, 8192, 18944, 3584, 41},
     {VAR_F8, 8192, 18944, 3584, 43},
@@ -70,8 +74,9 @@ const ShapeEntry kTable[] = {
     {VAR_PACKED, 8192, 18944, 3584, 62},
     {VAR_F8_PACKED, 8192, 18944, 3584, 76},
     {VAR_MX_PACKED, 8192, 18944, 3584, 77},
-    // Qwen2.5-72B MLP, M = 4096
-    {VAR_INTERLEAVE, 4096, 29568, 8192, 36},
+    {VAR_MX_SYNC, 8192, 18944, 3584, 83},
+    // Qwen2.5-72B MLP, M = 4096 (persistent: 3078-3097 vs 3036-3045 us)
+    {VAR_INTERLEAVE, 4096, 29568, 8192, 40},
     {VAR_SYNC, 4096, 29568, 8192, 42},
     {VAR_GEMM, 4096, 29568, 8192, 41},
     {VAR_F8, 4096, 29568, 8192, 43},
@@ -80,6 +85,7 @@ const ShapeEntry kTable[] = {
     {VAR_PACKED, 4096, 29568, 8192, 62},
     {VAR_F8_PACKED, 4096, 29568, 8192, 76},
     {VAR_MX_PACKED, 4096, 29568, 8192, 79},
+    {VAR_MX_SYNC, 4096, 29568, 8192, 82},
 };
 
 }  // namespace
@@ -121,6 +127,9 @@ int select_config(int variant, long long M, long long N, long long K, int cu_cou
     }
     case VAR_MX:
       return (M <= 64 || few_big) ? 57 : 56;
+    case VAR_MX_SYNC:
+      if (M <= 192) return 84;
+      return (M <= 384 || few_big) ? 83 : 82;
     case VAR_F8:
       if (M <= 16) return (2 * N + 31) / 32 >= 2 * cus ? 52 : 51;
       if (M <= 32) return wide ? 51 : 46;
@@ -128,7 +137,7 @@ int select_config(int variant, long long M, long long N, long long K, int cu_cou
       return (M <= 384 || few_big) ? 45 : 43;
     case VAR_F8_SYNC:
       if (M <= 192) return (wide && M > 32) ? 54 : 55;
-      return (M <= 3072 || few_big) ? 54 : 53;
+      return (M <= 384 || few_big) ? 54 : 53;
     case VAR_SYNC:
       if (M <= 64) return (wide && M > 16) ? 8 : (M <= 32 ? 12 : 13);
       if (M <= 192) return wide ? 8 : 29;
@@ -141,7 +150,7 @@ int select_config(int variant, long long M, long long N, long long K, int cu_cou
       if (M <= 16) return 23;
       if (M <= 64) return wide ? (M <= 32 ? 1 : 35) : (M <= 32 ? 27 : 3);
       if (M <= 192) return wide ? 35 : 3;
-      return (M <= 384 || few_big) ? 1 : 36;
+      return (M <= 384 || few_big) ? 1 : 40;
     default:
       return -1;
   }

@@ -26,11 +26,12 @@ import gemm_epilogues_mlp_amd as sw
 VARIANTS = {"interleave": sw.VARIANT_INTERLEAVE, "sync": sw.VARIANT_SYNC, "gemm": sw.VARIANT_GEMM,
             "fp8": sw.VARIANT_FP8, "fp8-sync": sw.VARIANT_FP8_SYNC, "mxfp8": sw.VARIANT_MXFP8,
             "packed": sw.VARIANT_PACKED, "fp8-packed": sw.VARIANT_FP8_PACKED,
-            "mxfp8-packed": sw.VARIANT_MXFP8_PACKED}
+            "mxfp8-packed": sw.VARIANT_MXFP8_PACKED, "mxfp8-sync": sw.VARIANT_MXFP8_SYNC}
 # the forward's variant argument for each FP8 configuration family
 _FP8_ORDER = {sw.VARIANT_FP8: sw.VARIANT_INTERLEAVE, sw.VARIANT_FP8_SYNC: sw.VARIANT_SYNC,
               sw.VARIANT_MXFP8: sw.VARIANT_MXFP8, sw.VARIANT_FP8_PACKED: sw.VARIANT_FP8_PACKED,
-              sw.VARIANT_MXFP8_PACKED: sw.VARIANT_MXFP8_PACKED}
+              sw.VARIANT_MXFP8_PACKED: sw.VARIANT_MXFP8_PACKED,
+              sw.VARIANT_MXFP8_SYNC: sw.VARIANT_MXFP8_SYNC}
 
 
 def _candidates(variant, M, configs=None):
@@ -97,7 +98,7 @@ def _time_configs(h, variant, M, N, K, ids, reps, rotate_bytes, seed=0):
     def call(i, cid):
         if fp8:
             a8, w8, sa, sw8, y, _ = sets[i % nsets]
-            if variant == sw.VARIANT_MXFP8:
+            if variant in (sw.VARIANT_MXFP8, sw.VARIANT_MXFP8_SYNC):
                 sw.swiglu_forward_mx(h, a8, sa, w8, sw8, y, M, N, K, ks, cid, stream)
             elif variant == sw.VARIANT_MXFP8_PACKED:
                 sw.swiglu_forward_mx_packed(h, a8, sa, w8, sw8, y, M, N, K, ks, cid, stream)

@@ -102,9 +102,12 @@ typedef enum {
                                     (PACKED layout)                            */
   SWIGLU_VARIANT_FP8_PACKED = 8, /* Kernel-2 order on FP8 inputs with
                                     fragment-ordered W8 (swiglu_forward_fp8)   */
-  SWIGLU_VARIANT_MXFP8_PACKED = 9 /* Kernel-2 order on MXFP8 inputs with
+  SWIGLU_VARIANT_MXFP8_PACKED = 9, /* Kernel-2 order on MXFP8 inputs with
                                     fragment-ordered W8 (swiglu_forward_mx_packed;
                                     swiglu_query_fp8)                          */
+  SWIGLU_VARIANT_MXFP8_SYNC = 10  /* Kernel-1 order on MXFP8 inputs, the same W8
+                                    and scales (swiglu_forward_mx with a config
+                                    of this variant; swiglu_query_fp8)         */
 } swiglu_variant_t;
 
 /* Description of one compiled kernel configuration. */
@@ -350,8 +353,14 @@ swiglu_status_t swiglu_pack_fp8_fragments(swiglu_handle_t h, const void* W8, voi
 
 /* Y = bf16(SiLU(g) * u), g = A x W1 and u = A x W2 on the MX values: the MFMA
  * applies the block scales to exact E4M3 products, fp32 accumulation.
- * config_id < 0 uses the table; a given id must be of variant MXFP8 (else
- * INVALID_ARG).  Y must not overlap any input. */
+ * config_id < 0 uses the table (the interleave order, [RT §Metodologia,
+ * Kernel-2]); a given id must be of variant MXFP8 or MXFP8_SYNC (else
+ * INVALID_ARG).  A MXFP8_SYNC configuration runs the sync order on the same
+ * W8 and scales ([RT §Metodologia, Kernel-1]: each output tile's Gate rows
+ * first, SiLU on the register-resident Gate sums while the Up rows' tiles and
+ * scales are in flight, then the Up rows); swiglu_query_fp8 with
+ * SWIGLU_VARIANT_MXFP8_SYNC reports the table's choice of it.  Y must not
+ * overlap any input. */
 swiglu_status_t swiglu_forward_mx(swiglu_handle_t h, const void* A8, const void* SA,
                                   const void* W8, const void* SW, void* Y, int64_t M, int64_t N,
                                   int64_t K, int64_t ks, int32_t config_id, hipStream_t stream);

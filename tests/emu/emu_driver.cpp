@@ -111,7 +111,7 @@ bool run_config(int id, int M, int N, int K) {
     a.ldw = N;
   }
   if (c->variant == VAR_F8 || c->variant == VAR_F8_SYNC || c->variant == VAR_MX ||
-      c->variant == VAR_F8_PACKED || c->variant == VAR_MX_PACKED) {
+      c->variant == VAR_MX_SYNC || c->variant == VAR_F8_PACKED || c->variant == VAR_MX_PACKED) {
     // byte tensors: A8 [M, K], W8 [2N, K] (or its fragment order P8); MX
     // scales SA [M, ks], SW [2N, ks]
     a.A = alloc16(((size_t)M * K + 1) / 2, "A8");
@@ -120,7 +120,7 @@ bool run_config(int id, int M, int N, int K) {
                                          : alloc16((size_t)N * K, "W8");
     a.ldw = K;
     a.scale_g = a.scale_u = 1.0f;
-    if (c->variant == VAR_MX || c->variant == VAR_MX_PACKED) {
+    if (c->variant == VAR_MX || c->variant == VAR_MX_SYNC || c->variant == VAR_MX_PACKED) {
       a.ks = (K / 32 + 15) / 16 * 16;
       a.SA = (const uint8_t*)alloc16(((size_t)M * a.ks + 1) / 2, "SA");
       a.SW = (const uint8_t*)alloc16((size_t)N * a.ks, "SW");
@@ -240,7 +240,8 @@ int main(int argc, char** argv) {
     if (one_shape) {
       run_config(id, shape[0], shape[1], shape[2]);
     } else {
-      if (config_at(id) && (config_at(id)->variant == VAR_MX || config_at(id)->variant == VAR_MX_PACKED))
+      if (config_at(id) && (config_at(id)->variant == VAR_MX || config_at(id)->variant == VAR_MX_SYNC ||
+                            config_at(id)->variant == VAR_MX_PACKED))
         for (const auto& s : shapes_mx) run_config(id, s[0], s[1], s[2]);
       else if (config_at(id) && (config_at(id)->variant == VAR_F8 || config_at(id)->variant == VAR_F8_SYNC ||
                                  config_at(id)->variant == VAR_F8_PACKED))

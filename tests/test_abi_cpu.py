@@ -95,7 +95,7 @@ def test_config_list_is_consistent():
     assert n > 0
     seen = {sw.VARIANT_SYNC: 0, sw.VARIANT_INTERLEAVE: 0, sw.VARIANT_GEMM: 0, sw.VARIANT_FP8: 0,
             sw.VARIANT_FP8_SYNC: 0, sw.VARIANT_MXFP8: 0, sw.VARIANT_PACKED: 0,
-            sw.VARIANT_FP8_PACKED: 0, sw.VARIANT_MXFP8_PACKED: 0}
+            sw.VARIANT_FP8_PACKED: 0, sw.VARIANT_MXFP8_PACKED: 0, sw.VARIANT_MXFP8_SYNC: 0}
     for i in range(n):
         c = sw.swiglu_config_info(i)
         assert c["id"] == i
@@ -114,7 +114,8 @@ def test_config_list_is_consistent():
         if c["family"] in (0, 2):
             assert c["bm"] % 32 == 0 and c["bn"] % 32 == 0
         if c["variant"] in (sw.VARIANT_FP8, sw.VARIANT_FP8_SYNC, sw.VARIANT_MXFP8,
-                            sw.VARIANT_FP8_PACKED, sw.VARIANT_MXFP8_PACKED):
+                            sw.VARIANT_FP8_PACKED, sw.VARIANT_MXFP8_PACKED,
+                            sw.VARIANT_MXFP8_SYNC):
             assert (c["family"], c["bk"]) in ((0, 64), (1, 128), (1, 64))
         if c["variant"] == sw.VARIANT_PACKED:  # streaming, 64 outputs per slab
             assert c["family"] == 1 and c["bn"] in (16, 32, 64) and c["bk"] == 32

@@ -46,6 +46,7 @@ CASES = [
     (2008, 4216, 72, [40, 42]),        # 264 tiles: 256 big + 8 split
     (2008, 8440, 72, [41]),            # the same for the 256-column GEMM tiles
     (2048, 8960, 40, [40, 41, 42]),    # 1.5B M and N: 512 big + 48 split
+    (2008, 4216, 1088, [82]),          # MXFP8 sync split tiles: 17 steps, 3 scale groups a phase
     # the persistent tiles: whole rings of K (K = 128, 256), two or more tiles
     # per workgroup, with and without a quarter-tile last round, ragged M and N
     (2048, 8960, 128, [36]),           # 560 tiles: 2 per workgroup + 48 as quarters

@@ -133,12 +133,14 @@ SHAPES = [
     (37, 136, 576),    # ragged 64-row tiles, K = 9 steps (a partial scale group)
     (1, 8, 64),        # one row, one 8-column chunk, one step
     (129, 520, 128),   # one row past a tile
+    (130, 264, 1088),  # 17 steps: three scale groups per phase, the last partial
 ]
 
 
 def mx_configs():
+    """MX configurations of both kernel orders (the same W8 and scales)."""
     return [i for i in range(sw.swiglu_config_count())
-            if sw.swiglu_config_info(i)["variant"] == sw.VARIANT_MXFP8]
+            if sw.swiglu_config_info(i)["variant"] in (sw.VARIANT_MXFP8, sw.VARIANT_MXFP8_SYNC)]
 
 
 @pytest.fixture(scope="module")
@@ -177,19 +179,24 @@ def test_mx_split_tail_parity(handle, cfg):
     assert_parity(y, oracle.swiglu_mx_rows(qa, sa, qw, sw_), f"mx split cfg {cfg}")
 
 
-def test_mx_block_scales_matter(handle):
-    """Changing one Up block scale of one column changes exactly that column."""
-    M, N, K = 64, 128, 256
+@pytest.mark.parametrize("order", ["interleave", "sync"])
+def test_mx_block_scales_matter(handle, order):
+    """Changing one Up block scale of one column changes exactly that column
+    (and one Gate block scale, in a later scale group, likewise), in both
+    kernel orders."""
+    M, N, K = 64, 128, 768
+    cfg = -1 if order == "interleave" else \
+        sw.swiglu_query_fp8(handle, M, N, K, sw.VARIANT_MXFP8_SYNC)["id"]
     a, w1, w2 = I.make_inputs(M, K, N, 88)
     qa, sa, qw, sw_, _ = mx_inputs(a, w1, w2)
-    sw2 = sw_.copy()
-    sw2[2 * 5 + 1, 3] += 2                                           # Up column 5, k block 3: x4
-    y0 = forward(handle, qa, sa, qw, sw_, M, N, K)
-    y1 = forward(handle, qa, sa, qw, sw2, M, N, K)
-    ref = oracle.swiglu_mx_rows(qa, sa, qw, sw2)
-    assert_parity(y1, ref, "mx modified scale")
-    changed = np.any(y0 != y1, axis=0)
-    assert changed[5] and not np.any(np.delete(changed, 5))
+    y0 = forward(handle, qa, sa, qw, sw_, M, N, K, cfg)
+    for row, blk, col in [(2 * 5 + 1, 3, 5), (2 * 9, 20, 9)]:       # Up of column 5, Gate of 9
+        sw2 = sw_.copy()
+        sw2[row, blk] += 2                                           # that k block x4
+        y1 = forward(handle, qa, sa, qw, sw2, M, N, K, cfg)
+        assert_parity(y1, oracle.swiglu_mx_rows(qa, sa, qw, sw2), f"mx {order} modified scale")
+        changed = np.any(y0 != y1, axis=0)
+        assert changed[col] and not np.any(np.delete(changed, col))
 
 
 # --------------------------------------------------------------------------- workloads
@@ -212,6 +219,19 @@ def test_mx_workload_parity(handle, workload):
     y = forward(handle, *d["q"], w.M, w.N, w.K)
     s = full_check(y, d["y_ref"], f"mx {w.name}")
     log(f"mx {w.name}: all {s['elements']} elements within the bar (worst "
+        f"{s['worst_frac']:.3f}); share > 1 % off: {s['rel_gt_1pct']:.2e}")
+
+
+def test_mx_sync_workload_parity(handle, workload):
+    """The sync (Kernel-1) order on the same W8 and scales, the table's choice
+    for the shape, every output element."""
+    d = workload
+    w = d["w"]
+    cfg = sw.swiglu_query_fp8(handle, w.M, w.N, w.K, sw.VARIANT_MXFP8_SYNC)["id"]
+    log(f"mx sync {w.name}: config {cfg}")
+    y = forward(handle, *d["q"], w.M, w.N, w.K, cfg)
+    s = full_check(y, d["y_ref"], f"mx sync {w.name}")
+    log(f"mx sync {w.name}: all {s['elements']} elements within the bar (worst "
         f"{s['worst_frac']:.3f}); share > 1 % off: {s['rel_gt_1pct']:.2e}")
 
 
