@@ -1339,18 +1339,36 @@ __device__ __forceinline__ void f8_tile(const uint8_t* __restrict__ A,
   // The swizzle depends on row bits 1-3 only, so the rows +32, +64, ... of a
   // lane's fragments share it: one pair of per-lane offsets per tile, the
   // fragment index a compile-time displacement of 32 rows.
-  const int a_lo = a_row * C::BK + ((h ^ C::swz(a_row)) * 16);
-  const int a_hi = a_row * C::BK + (((2 + h) ^ C::swz(a_row)) * 16);
-  const int w_lo = C::A_BYTES + w_row * C::BK + ((h ^ C::swz(w_row)) * 16);
-  const int w_hi = C::A_BYTES + w_row * C::BK + (((2 + h) ^ C::swz(w_row)) * 16);
-  // fragment f of the A tile (f < FA) or of the weight tile (W) in a stage
-  auto readA = [&](const uint8_t* stage, int f, u32x4 (&d)[2]) __attribute__((always_inline)) {
-    d[0] = *reinterpret_cast<const u32x4*>(stage + a_lo + f * 32 * C::BK);
-    d[1] = *reinterpret_cast<const u32x4*>(stage + a_hi + f * 32 * C::BK);
+  // Offsets from the LDS base: an LDS read adds at most 65535 to its address
+  // register, so the stages above 64 KB read through a second copy of each
+  // offset raised by 64 KB, which the compiler cannot see through (an empty
+  // asm statement).  Otherwise it formed one address register per stage and
+  // fragment (the largest tile then spilled).
+  int frag_off[2][4];  // [window][a_lo, a_hi, w_lo, w_hi]
+  frag_off[0][0] = a_row * C::BK + ((h ^ C::swz(a_row)) * 16);
+  frag_off[0][1] = a_row * C::BK + (((2 + h) ^ C::swz(a_row)) * 16);
+  frag_off[0][2] = C::A_BYTES + w_row * C::BK + ((h ^ C::swz(w_row)) * 16);
+  frag_off[0][3] = C::A_BYTES + w_row * C::BK + (((2 + h) ^ C::swz(w_row)) * 16);
+#pragma unroll
+  for (int v = 0; v < 4; ++v) {
+    int hi = frag_off[0][v] + 65536;
+    asm volatile("" : "+v"(hi));
+    frag_off[1][v] = hi;
+  }
+  // fragment f of the A tile (f < FA) or of the weight tile (W) in stage ST
+  auto frag_read = [&](auto st_c, int v, int f) __attribute__((always_inline)) -> u32x4 {
+    constexpr int BASE = C::ST0 + decltype(st_c)::value * C::STAGE_BYTES;
+    constexpr int WIN = BASE >= 65536 ? 1 : 0;
+    return *reinterpret_cast<const u32x4*>(smem + frag_off[WIN][v] + (BASE - WIN * 65536) +
+                                           f * 32 * C::BK);
   };
-  auto readW = [&](const uint8_t* stage, int f, u32x4 (&d)[2]) __attribute__((always_inline)) {
-    d[0] = *reinterpret_cast<const u32x4*>(stage + w_lo + f * 32 * C::BK);
-    d[1] = *reinterpret_cast<const u32x4*>(stage + w_hi + f * 32 * C::BK);
+  auto readA = [&](auto st_c, int f, u32x4 (&d)[2]) __attribute__((always_inline)) {
+    d[0] = frag_read(st_c, 0, f);
+    d[1] = frag_read(st_c, 1, f);
+  };
+  auto readW = [&](auto st_c, int f, u32x4 (&d)[2]) __attribute__((always_inline)) {
+    d[0] = frag_read(st_c, 2, f);
+    d[1] = frag_read(st_c, 3, f);
   };
   u32x4 wf[C::FW][2];
   u32x4 af[2][C::FA][2];
@@ -1392,7 +1410,6 @@ __device__ __forceinline__ void f8_tile(const uint8_t* __restrict__ A,
     constexpr int PH = decltype(phase_c)::value;
     constexpr int P = ST & 1;
     using Next = std::integral_constant<int, (ST + 1) % STAGES>;
-    const uint8_t* nxt = smem + C::ST0 + Next::value * C::STAGE_BYTES;
     wait_vmcnt<(STAGES - 2) * C::TLOADS>();
     __syncthreads();
     // MFMA slot q (compile time): MFMA (i, j), then its share of the reads of
@@ -1405,11 +1422,11 @@ __device__ __forceinline__ void f8_tile(const uint8_t* __restrict__ A,
       else
         acc[PH][i][j] = mfma32_f8(wf[i], af[P][j], acc[PH][i][j]);
       if constexpr (q < C::FA) {
-        readA(nxt, q, af[P ^ 1][q]);
+        readA(Next{}, q, af[P ^ 1][q]);
         if constexpr (C::MX) put(sca, 2 * (P ^ 1) + q, scale_of(it + 1, a_row + 32 * q));
       }
       if constexpr (j == C::FA - 1) {
-        readW(nxt, i, wf[i]);
+        readW(Next{}, i, wf[i]);
         if constexpr (C::MX) put(scw, i, scale_of(it + 1, BM + w_row + 32 * i));
       }
       if constexpr (q >= DBEGIN) {
@@ -1449,12 +1466,12 @@ __device__ __forceinline__ void f8_tile(const uint8_t* __restrict__ A,
   __syncthreads();
 #pragma unroll
   for (int j = 0; j < C::FA; ++j) {
-    readA(smem + C::ST0, j, af[0][j]);
+    readA(std::integral_constant<int, 0>{}, j, af[0][j]);
     if constexpr (C::MX) put(sca, j, scale_of(0, a_row + 32 * j));
   }
 #pragma unroll
   for (int i = 0; i < C::FW; ++i) {
-    readW(smem + C::ST0, i, wf[i]);
+    readW(std::integral_constant<int, 0>{}, i, wf[i]);
     if constexpr (C::MX) put(scw, i, scale_of(0, BM + w_row + 32 * i));
   }
 
@@ -1475,17 +1492,26 @@ __device__ __forceinline__ void f8_tile(const uint8_t* __restrict__ A,
   // ---- epilogue: scales, SiLU(Gate) * Up, bf16 tile through LDS, row stores -------
   wait_vmcnt<0>();
   __syncthreads();
+  // The lane's epilogue offsets come from a copy of the thread index the
+  // compiler cannot see through (an empty asm statement): otherwise they were
+  // computed before the K loop and kept live through it, where the largest
+  // tile needs every register, and spilled to scratch.
+  int etid = threadIdx.x;
+  asm volatile("" : "+v"(etid));
+  const int e_lane = etid & 63, e_wave = etid >> 6;
+  const int e_row = (e_wave / WGN) * C::WTM + (e_lane & 31);
+  const int e_wcl = (e_wave % WGN) * C::WTW + 4 * (e_lane >> 5);
   uint16_t* ys = reinterpret_cast<uint16_t*>(smem);  // [BM][YLD]
 #pragma unroll
   for (int i = 0; i < C::FW; ++i)
 #pragma unroll
     for (int j = 0; j < C::FA; ++j) {
-      const int row = a_row + j * 32;
+      const int row = e_row + j * 32;
       const f32x16& d = acc[0][i][j];
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         // registers 4q..4q+3: weight tile rows wcl..wcl+3
-        const int wcl = wn * C::WTW + i * 32 + 8 * q + 4 * h;
+        const int wcl = e_wcl + i * 32 + 8 * q;
         if constexpr (kSync) {
           // output columns wcl..wcl+3: SiLU(Gate) (already applied) * Up
           const f32x16& u = acc[C::NACC - 1][i][j];

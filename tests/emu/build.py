@@ -6,7 +6,8 @@ emulation needs: each `__shared__` array becomes a pointer from emu_lds(),
 the raw `s_barrier` becomes emu_barrier(), the empty asm statement that pins
 a value in a register is dropped, the AMDGPU-only occupancy attribute is
 dropped, and the single hipLaunchKernel call runs the kernel's workgroups on
-the host (emu_launch)."""
+the host (emu_launch).  Three planted mistakes, off unless the driver is run
+with --plant N, show that the LDS ordering check catches what it exists for."""
 import os
 import re
 import shutil
@@ -31,7 +32,7 @@ def rewrite(src: str) -> str:
                  r"\1* \2 = reinterpret_cast<\1*>(::emu_lds(sizeof(\1) * (\3)));", src)
     src = src.replace('asm volatile("s_barrier" ::: "memory");', "::emu_barrier();")
     # the empty register-pinning statement has no effect on the host
-    src = src.replace('asm volatile("" : "+v"(tid));', "(void)tid;")
+    src = re.sub(r'asm volatile\(""\s*:\s*"\+v"\((\w+)\)\);', r"(void)\1;", src)
     src = re.sub(r"__attribute__\(\(amdgpu_waves_per_eu\([^)]*\)\)\)", "", src)
     # the one hipLaunchKernel call (in launch_kernel) runs the kernel on the host
     launch = ("return hipLaunchKernel(reinterpret_cast<const void*>(k), grid, block, argv, "
@@ -41,6 +42,30 @@ def rewrite(src: str) -> str:
     src = src.replace(launch, "(void)argv; emu_launch(k, grid, block, v...); return hipSuccess;")
     if "__shared__" in src or "asm volatile" in src:
         raise RuntimeError("kernel source has a construct the emulation does not rewrite")
+    return plant_points(src)
+
+
+# Mistakes the LDS ordering check must catch, planted in the emulation copy
+# only and switched on at run time (emu_driver --plant N; 0 = none):
+#  1: the LDS-tiled K loop waits for one K step fewer of its DMA
+#  2: the epilogues reuse the stage ring without the barrier that ends the K loop
+#  3: the persistent kernel ends without draining the loads issued past its last tile
+PLANTS = [
+    (r"^        wait_vmcnt<\(STAGES - 2\) \* C::LOADS>\(\);$",
+     "        if (::g_emu_plant == 1) wait_vmcnt<(STAGES - 1) * C::LOADS>();"
+     " else wait_vmcnt<(STAGES - 2) * C::LOADS>();", 1),
+    (r"^  wait_vmcnt<0>\(\);\n  __syncthreads\(\);\n(?=  uint16_t\* ys = |  // The lane's epilogue)",
+     "  wait_vmcnt<0>();\n  if (::g_emu_plant != 2) __syncthreads();\n", 2),
+    (r"^(  // the zero loads issued past the last tile still write LDS\n)  wait_vmcnt<0>\(\);$",
+     "\\1  if (::g_emu_plant != 3) wait_vmcnt<0>();", 1),
+]
+
+
+def plant_points(src: str) -> str:
+    for pattern, repl, count in PLANTS:
+        src, n = re.subn(pattern, repl, src, flags=re.M)
+        if n != count:
+            raise RuntimeError(f"plant point found {n} times, expected {count}: {pattern}")
     return src
 
 
@@ -55,13 +80,18 @@ def build(out_dir: str) -> str:
         f.write(src)
     for name in ("swiglu_internal.h",):
         shutil.copy(os.path.join(CSRC, name), out_dir)
-    for name in ("swiglu_device.hpp", "emu_driver.cpp"):
+    for name in ("swiglu_device.hpp", "emu_driver.cpp", "emu_race.cpp"):
         shutil.copy(os.path.join(HERE, name), out_dir)
     exe = os.path.join(out_dir, "emu_driver")
-    cmd = [cc, "-std=c++20", "-O1", "-g", "-fsanitize=address", "-fno-omit-frame-pointer",
-           "-Wno-unknown-attributes", "-Wno-ignored-attributes", "-Wno-psabi", "-I", out_dir, "-I", HERE,
-           os.path.join(out_dir, "emu_driver.cpp"), "-o", exe]
-    subprocess.run(cmd, check=True)
+    common = [cc, "-std=c++20", "-O1", "-g", "-fsanitize=address", "-fno-omit-frame-pointer",
+              "-Wno-unknown-attributes", "-Wno-ignored-attributes", "-Wno-psabi", "-I", out_dir,
+              "-I", HERE]
+    # the kernels' translation unit reports every load and store (the LDS
+    # ordering check); the checker itself is built without that
+    race_o = os.path.join(out_dir, "emu_race.o")
+    subprocess.run(common + ["-c", os.path.join(out_dir, "emu_race.cpp"), "-o", race_o], check=True)
+    subprocess.run(common + ["-fsanitize-coverage=func,trace-loads,trace-stores",
+                             os.path.join(out_dir, "emu_driver.cpp"), race_o, "-o", exe], check=True)
     return exe
 
 

@@ -4,12 +4,16 @@
 // through the real launch functions, and every LDS offset, DMA source and
 // direct global load is checked against the buffers actually allocated (the
 // build adds AddressSanitizer for the plain pointer accesses: LDS staging,
-// global stores).  Barriers are no-ops, so the data is not meaningful; only
-// where each access goes is checked.
+// global stores).  The threads run one after another, so the data is not
+// meaningful; where each access goes is checked, and (emu_race.cpp) whether
+// the barriers and DMA waits order every LDS access as a GPU needs.
 //
 // usage: emu_driver [cfg ...]          all shapes for the listed configs (default: all)
 //        emu_driver --shape M N K cfg  one shape
 //        --last-blocks B               only the last B workgroups of each launch
+//        --no-races                    bounds only (no LDS ordering check)
+//        --race-blocks B               the ordering check on the last B workgroups only
+//        --plant P                     switch on planted mistake P (build.py)
 #include <stdio.h>
 #include <stdlib.h>
 
@@ -20,6 +24,15 @@
 
 dim3 threadIdx, blockIdx, gridDim, blockDim;
 long g_emu_last_blocks = 0;
+long g_emu_race_errors = 0;
+long g_emu_race_blocks = 0;
+int g_emu_plant = 0;
+
+// the LDS ordering check (emu_race.cpp)
+void emu_race_context(const char* ctx);
+void emu_race_lds(const uint8_t* base, size_t n);
+void emu_race_global(const void* p, size_t n);
+void emu_race_globals_clear();
 
 namespace {
 struct Alloc {
@@ -48,11 +61,12 @@ uint8_t* emu_lds(size_t bytes) {
     g_lds = (uint8_t*)malloc(bytes ? bytes : 1);
     memset(g_lds, 0, bytes);
     g_lds_size = bytes;
+    emu_race_lds(g_lds, bytes);
   }
   return g_lds;
 }
 uint8_t* emu_lds_base() { return g_lds; }
-void emu_barrier() {}
+void emu_barrier() { emu_race_barrier(); }
 void emu_check_lds(uint32_t off, size_t n, const char* what) {
   ++g_lds_checks;
   if (!g_lds || (size_t)off + n > g_lds_size) report(what, g_lds ? g_lds + off : nullptr, n);
@@ -72,11 +86,13 @@ uint16_t* alloc16(size_t elems, const char* name) {
   uint16_t* p = (uint16_t*)malloc(n ? n : 1);
   memset(p, 0, n);
   g_allocs.push_back({(const uint8_t*)p, n, name});
+  emu_race_global(p, n);
   return p;
 }
 void free_all() {
   for (const Alloc& a : g_allocs) free((void*)a.p);
   g_allocs.clear();
+  emu_race_globals_clear();
 }
 
 // one configuration on one shape, through the same LaunchArgs the C ABI builds
@@ -88,7 +104,8 @@ bool run_config(int id, int M, int N, int K) {
   snprintf(buf, sizeof buf, "config %d (variant %d family %d %dx%d) shape M=%d N=%d K=%d", id,
            c->variant, c->family, c->bm, c->bn, M, N, K);
   g_ctx = buf;
-  const long before = g_errors;
+  emu_race_context(buf);
+  const long before = g_errors + g_emu_race_errors;
   const long l0 = g_lds_checks, g0 = g_global_checks;
   LaunchArgs a{};
   a.M = M, a.N = N, a.K = K;
@@ -134,15 +151,17 @@ bool run_config(int id, int M, int N, int K) {
   const hipError_t e = c->launch(a);
   free_all();
   if (e != hipSuccess) fprintf(stderr, "launch refused: %s\n", g_ctx.c_str());
+  const bool ok = g_errors + g_emu_race_errors == before;
   printf("%s: %s (%ld LDS accesses, %ld global reads checked)\n", g_ctx.c_str(),
-         g_errors == before ? "ok" : "OUT OF BOUNDS", g_lds_checks - l0, g_global_checks - g0);
-  return g_errors == before;
+         ok ? "ok" : "OUT OF BOUNDS OR LDS RACE", g_lds_checks - l0, g_global_checks - g0);
+  return ok;
 }
 
 bool run_elementwise(size_t n) {
   using namespace swiglu;
   g_ctx = "gate/pack n=" + std::to_string(n);
-  const long before = g_errors;
+  emu_race_context(g_ctx.c_str());
+  const long before = g_errors + g_emu_race_errors;
   uint16_t* g = alloc16(n, "G");
   uint16_t* u = alloc16(n, "U");
   uint16_t* y = alloc16(n, "Y");
@@ -207,8 +226,9 @@ bool run_elementwise(size_t n) {
       free_all();
     }
   }
-  printf("%s: %s\n", g_ctx.c_str(), g_errors == before ? "ok" : "OUT OF BOUNDS");
-  return g_errors == before;
+  const bool ok = g_errors + g_emu_race_errors == before;
+  printf("%s: %s\n", g_ctx.c_str(), ok ? "ok" : "OUT OF BOUNDS OR LDS RACE");
+  return ok;
 }
 }  // namespace
 
@@ -216,9 +236,15 @@ int main(int argc, char** argv) {
   using namespace swiglu;
   std::vector<int> ids;
   int shape[3] = {0, 0, 0};
-  bool one_shape = false;
+  bool one_shape = false, races = true;
   for (int i = 1; i < argc; ++i) {
-    if (std::string(argv[i]) == "--last-blocks" && i + 1 < argc) {
+    if (std::string(argv[i]) == "--no-races") {
+      races = false;
+    } else if (std::string(argv[i]) == "--race-blocks" && i + 1 < argc) {
+      g_emu_race_blocks = atol(argv[++i]);
+    } else if (std::string(argv[i]) == "--plant" && i + 1 < argc) {
+      g_emu_plant = atoi(argv[++i]);
+    } else if (std::string(argv[i]) == "--last-blocks" && i + 1 < argc) {
       g_emu_last_blocks = atol(argv[++i]);
     } else if (std::string(argv[i]) == "--shape" && i + 3 < argc) {
       shape[0] = atoi(argv[i + 1]), shape[1] = atoi(argv[i + 2]), shape[2] = atoi(argv[i + 3]);
@@ -228,6 +254,7 @@ int main(int argc, char** argv) {
       ids.push_back(atoi(argv[i]));
     }
   }
+  emu_race_enable(races);
   if (ids.empty())
     for (int i = 0; i < config_count(); ++i) ids.push_back(i);
   // the GPU parity shapes (ragged tails in every dimension) and K = 0
@@ -254,6 +281,6 @@ int main(int argc, char** argv) {
     run_elementwise(8);
     run_elementwise(200 * 264);
   }
-  printf("errors: %ld\n", g_errors);
-  return g_errors ? 1 : 0;
+  printf("errors: %ld\n", g_errors + g_emu_race_errors);
+  return g_errors + g_emu_race_errors ? 1 : 0;
 }

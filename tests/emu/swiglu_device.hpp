@@ -23,6 +23,21 @@ void emu_barrier();
 void emu_check_global(const void* p, size_t n, const char* what);
 void emu_check_lds(uint32_t off, size_t n, const char* what);
 uint8_t* emu_lds_base();
+// LDS ordering check (emu_race.cpp)
+void emu_race_block_begin();
+void emu_race_thread(unsigned t);
+long emu_race_block_end();
+void emu_race_barrier();
+void emu_race_wait(int n);
+void emu_race_vmop();
+void emu_race_dma(uint32_t dst, uint32_t n);
+void emu_race_read(const void* p, uint32_t n);
+extern long g_emu_race_errors;
+extern int g_emu_plant;  // a planted mistake to switch on (build.py), 0: none
+// byte copies outside the instrumented translation unit (so that the data
+// movement of a DMA or of a checked load is not logged as a plain access)
+void emu_copy(void* d, const void* s, size_t n);
+void emu_zero(void* d, size_t n);
 
 #define __global__
 #define __device__
@@ -48,22 +63,33 @@ inline uint32_t emu_perm(uint32_t s0, uint32_t s1, uint32_t sel) {
 #define __builtin_amdgcn_perm(a, b, s) emu_perm((a), (b), (s))
 
 // emulate only the last g_emu_last_blocks workgroups of each launch (0: all);
-// the last workgroups of a launch touch the largest offsets
+// the last workgroups of a launch touch the largest offsets.  The LDS
+// ordering check runs on the last g_emu_race_blocks of them (0: all).
 extern long g_emu_last_blocks;
+extern long g_emu_race_blocks;
+void emu_race_enable(bool on);
+bool emu_race_enabled();
 template <class K, class... Args>
 void emu_launch(K kernel, dim3 grid, dim3 block, Args... args) {
   gridDim = grid;
   blockDim = block;
   const long total = (long)grid.x * grid.y;
   const long first = g_emu_last_blocks > 0 && g_emu_last_blocks < total ? total - g_emu_last_blocks : 0;
+  const long race_first = g_emu_race_blocks > 0 && g_emu_race_blocks < total ? total - g_emu_race_blocks : 0;
+  const bool race_on = emu_race_enabled();
   for (unsigned by = 0; by < grid.y; ++by)
     for (unsigned bx = 0; bx < grid.x; ++bx) {
       if ((long)by * grid.x + bx < first) continue;
       blockIdx = dim3(bx, by, 0);
+      emu_race_enable(race_on && (long)by * grid.x + bx >= race_first);
+      emu_race_block_begin();
       for (unsigned t = 0; t < block.x; ++t) {
         threadIdx = dim3(t, 0, 0);
+        emu_race_thread(t);
         kernel(args...);
       }
+      g_emu_race_errors += emu_race_block_end();
+      emu_race_enable(race_on);
     }
 }
 #define hipLaunchKernelGGL(K, G, B, SHM, STREAM, ...) emu_launch(K, dim3(G), dim3(B), __VA_ARGS__)
@@ -82,14 +108,16 @@ inline bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
 inline u32x4 load16(const void* p) {
   emu_check_global(p, 16, "load16");
+  emu_race_vmop();
   u32x4 r;
-  memcpy(&r, p, 16);
+  emu_copy(&r, p, 16);
   return r;
 }
 inline u32x2 load8(const void* p) {
   emu_check_global(p, 8, "load8");
+  emu_race_vmop();
   u32x2 r;
-  memcpy(&r, p, 8);
+  emu_copy(&r, p, 8);
   return r;
 }
 inline u32x4 load16_stream(const void* p) { return load16(p); }
@@ -119,27 +147,30 @@ inline void lds_dma16(uint32_t lds_wave_base, uint32_t voffset, i32x4 rsrc) {
   const uint32_t lane = threadIdx.x & 63u;
   const uint32_t dst = lds_wave_base + 16u * lane;
   emu_check_lds(dst, 16, "lds_dma16 destination");
+  emu_race_dma(dst, 16);
   uint8_t* d = emu_lds_base() + dst;
   const uint32_t bound = (uint32_t)rsrc[2];
   if (voffset >= bound) {
-    memset(d, 0, 16);
+    emu_zero(d, 16);
     return;
   }
   if (voffset + 16u > bound) emu_check_global(nullptr, 0, "lds_dma16 read straddles the resource bound");
   const uint8_t* base =
       (const uint8_t*)(uintptr_t)(((uint64_t)(uint32_t)rsrc[1] << 32) | (uint32_t)rsrc[0]);
   emu_check_global(base + voffset, 16, "lds_dma16 source");
-  memcpy(d, base + voffset, 16);
+  emu_copy(d, base + voffset, 16);
 }
 template <int N>
 inline void wait_vmcnt() {
   static_assert(N >= 0 && N <= 63, "vmcnt range");
+  emu_race_wait(N);
 }
 inline u32x2 lds_read_tr16(const void* p) {
   const uint8_t* b = emu_lds_base();
   emu_check_lds((uint32_t)((const uint8_t*)p - b), 8, "lds_read_tr16");
+  emu_race_read(p, 8);
   u32x2 r;
-  memcpy(&r, p, 8);
+  emu_copy(&r, p, 8);
   return r;
 }
 inline float silu(float x) { return x / (1.0f + expf(-x)); }

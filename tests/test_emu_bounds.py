@@ -6,8 +6,11 @@ threads are run through the real launch functions: each LDS offset, DMA
 source, direct global load and (via the sanitizer) global store and LDS
 pointer access is checked against the buffers actually allocated.  A kernel
 that would touch memory outside its inputs, outputs or LDS fails here instead
-of faulting a GPU.  Data values are not checked (barriers are no-ops);
-parity is the GPU tests' job.
+of faulting a GPU.  The same runs check LDS ordering (tests/emu/emu_race.cpp):
+every LDS access must be separated by the barriers and DMA waits from any
+DMA or other wave's access that could land on the same bytes meanwhile.
+Data values are not checked (the threads run one after another); parity is
+the GPU tests' job.
 """
 import os
 import subprocess
@@ -39,6 +42,26 @@ def test_all_configs_on_the_parity_shapes(emu):
     assert out.count(": ok") >= 5 * 40  # every config ran on every shape
 
 
+# The LDS ordering check (tests/emu/emu_race.cpp) against mistakes planted in
+# the emulation's copy of the kernels (tests/emu/build.py): a K-loop wait one
+# step short, an epilogue that reuses the stage ring without the barrier that
+# ends the K loop, a persistent kernel that does not drain its last loads.
+PLANTED = [
+    (1, 40, "LDS read while a DMA into it may land"),
+    (1, 42, "LDS read while a DMA into it may land"),
+    (2, 40, "LDS accesses of two waves between the same barriers"),
+    (2, 43, "LDS write while a DMA into it may land"),
+    (3, 36, "DMA still in flight when its thread ends"),
+]
+
+
+@pytest.mark.parametrize("plant,cfg,message", PLANTED)
+def test_lds_ordering_check_catches_planted_mistakes(emu, plant, cfg, message):
+    # the same launch without the plant is one of the workload cases below
+    rc, out = _run(emu, "--plant", plant, "--race-blocks", 8, "--shape", 2048, 8960, 128, cfg)
+    assert rc != 0 and message in out, out[-4000:]
+
+
 # (M, N, K, configs): launches whose tile counts exercise the split tail
 # (whole rounds of 256-row tiles plus a short last round), the table's
 # choices at the workloads' M and N, and decode-sized streaming
@@ -49,7 +72,7 @@ CASES = [
     (2008, 4216, 1088, [82]),          # MXFP8 sync split tiles: 17 steps, 3 scale groups a phase
     # the persistent tiles: whole rings of K (K = 128, 256), two or more tiles
     # per workgroup, with and without a quarter-tile last round, ragged M and N
-    (2048, 8960, 128, [36]),           # 560 tiles: 2 per workgroup + 48 as quarters
+    (2048, 8960, 128, [36, 40, 42, 43]),  # 560 tiles: 2 per workgroup + 48 as quarters
     (4000, 8440, 256, [37]),           # 528 GEMM tiles: + 16 as quarters, ragged M and N
     (4000, 9000, 128, [36]),           # 1136 tiles: a last round of 112, not split
     (4000, 9400, 128, [37]),           # 592 GEMM tiles: a last round of 80, not split
@@ -84,7 +107,7 @@ CASES = [
     # FP8 / MXFP8 (K a multiple of 64): split-tail tiles at 1.5B M and N in
     # both orders and with block scales, the small-M tiles and the streaming
     # kernel at the 0.5B and decode shapes
-    (2048, 8960, 1536, [43, 53, 56]),
+    (2048, 8960, 576, [43, 53, 56]),
     (2008, 4216, 128, [43, 53, 56]),   # whole rounds plus a short split round
     (128, 4864, 896, [46, 55, 57]),
     (16, 18944, 3584, [52, 57]),
@@ -105,18 +128,25 @@ CASES = [
 ]
 
 
+# the LDS ordering check runs on the last workgroups of each launch (the
+# ragged edges, the split tail's quarter tiles, the persistent workgroups'
+# last tiles); the bounds checks on every workgroup
+RACE_BLOCKS = 24
+
+
 @pytest.mark.parametrize("case", CASES, ids=lambda c: f"{c[0]}x{c[1]}x{c[2]}")
 def test_table_configs_at_workload_sizes(emu, case):
     M, N, K, cfgs = case
     for cfg in cfgs:
-        rc, out = _run(emu, "--shape", M, N, K, cfg)
+        rc, out = _run(emu, "--race-blocks", RACE_BLOCKS, "--shape", M, N, K, cfg)
         assert rc == 0 and "errors: 0" in out, out[-4000:]
 
 
 # tensors just under the 2 GiB limit (largest byte offsets the kernels form):
 # A = 2 * 65536 * 16376 B, and W_fused = 4 * 16376 * 32768 B (bf16), and the
 # byte tensors of the FP8 kernels; only the last workgroups of each launch are
-# emulated (they touch the largest offsets)
+# emulated (they touch the largest offsets), bounds only (the LDS ordering
+# does not depend on the tensor sizes)
 LIMIT_CASES = [
     (65536, 64, 16376, [40, 42, 41], 4),
     # the persistent tiles (K a whole number of rings: 2 * 65536 * 16256 B of A)
@@ -139,5 +169,6 @@ LIMIT_CASES = [
 def test_tensors_just_under_2gib(emu, case):
     M, N, K, cfgs, last = case
     for cfg in cfgs:
-        rc, out = _run(emu, "--last-blocks", last, "--shape", M, N, K, cfg, timeout=900)
+        rc, out = _run(emu, "--no-races", "--last-blocks", last, "--shape", M, N, K, cfg,
+                       timeout=900)
         assert rc == 0 and "errors: 0" in out, out[-4000:]
