@@ -160,7 +160,7 @@ LIMIT_CASES = [
     (16, 32768, 32704, [77, 78, 79, 80, 81], 8),
     (256, 32768, 16376, [1, 8, 16], 4),
     # byte tensors: A8 = 65536 x 32704 B, W8 = 2 x 32768 x 32704 B (K % 64 == 0)
-    (65536, 64, 32704, [43, 53, 56], 4),
+    (65536, 64, 32704, [43, 53, 56, 82], 4),
     (16, 32768, 32704, [47, 52, 55, 57], 8),
 ]
 

@@ -114,3 +114,47 @@ def test_largest_fp8_packed_weights(handle):
     t.cuda.synchronize()
     assert_parity(host(y)[rows], y_ref, "fp8 packed limit")
     del p8, y
+
+
+# FP8 and MXFP8 activations just under 2 GiB (A8 = M K bytes), through the
+# k-major tiles of both orders: the split 256-row tile of each order and the
+# table's own choice.  Codes are drawn on the GPU; sampled rows go to the oracle.
+def test_largest_fp8_and_mx_activations(handle):
+    import torch as t
+    M, N, K = 65536, 64, 32704
+    assert M * K < 2 ** 31 <= M * K + 2 ** 23 and K % 64 == 0
+    log(f"fp8 / mx activation limit M={M} N={N} K={K}")
+    g = t.Generator(device="cuda").manual_seed(29)
+    # finite E4M3 codes of both signs, magnitudes up to 0.25 (code 0x28)
+    codes = lambda shape: (t.randint(0, 0x29, shape, device="cuda", generator=g, dtype=t.uint8) |
+                           (t.randint(0, 2, shape, device="cuda", generator=g, dtype=t.uint8) << 7))
+    h8 = lambda x: x.cpu().numpy()  # uint8 tensor -> numpy (host() views as bf16 bits)
+    a8 = codes((M, K))
+    w18, w28 = codes((K, N)), codes((K, N))
+    rows = np.unique(np.r_[0, M - 1, np.random.default_rng(K).integers(0, M, 2)])
+    a8_rows = h8(a8[t.from_numpy(rows).cuda()])
+    w18_h, w28_h = h8(w18), h8(w28)
+    w8 = t.empty((2 * N, K), dtype=t.uint8, device="cuda")
+    sw.swiglu_pack_fp8(handle, w18, w28, w8, K, N)
+    y = t.full((M, N), -1, dtype=t.int16, device="cuda")
+
+    scales = (1.0, 2.0 ** -4, 2.0 ** -4)
+    y_ref = oracle.swiglu_fp8_rows(a8_rows, w18_h, w28_h, *scales)
+    for variant, cfg in ((sw.VARIANT_INTERLEAVE, 43), (sw.VARIANT_AUTO, -1), (sw.VARIANT_SYNC, 53),
+                         (sw.VARIANT_SYNC, -1)):
+        y.fill_(-1)
+        sw.swiglu_forward_fp8(handle, a8, w8, y, M, N, K, *scales, config_id=cfg, variant=variant)
+        t.cuda.synchronize()
+        assert_parity(host(y)[rows], y_ref, f"fp8 limit variant {variant} config {cfg}")
+
+    # MXFP8: E8M0 scales around 2^-4 on both sides
+    ks = sw.mx_scale_stride(K)
+    sa = t.randint(119, 127, (M, ks), device="cuda", generator=g, dtype=t.uint8)
+    swt = t.randint(119, 127, (2 * N, ks), device="cuda", generator=g, dtype=t.uint8)
+    y_ref = oracle.swiglu_mx_rows(a8_rows, h8(sa[t.from_numpy(rows).cuda()]), h8(w8), h8(swt))
+    for cfg in (56, 82):
+        y.fill_(-1)
+        sw.swiglu_forward_mx(handle, a8, sa, w8, swt, y, M, N, K, ks, config_id=cfg)
+        t.cuda.synchronize()
+        assert_parity(host(y)[rows], y_ref, f"mx limit config {cfg}")
+    del a8, sa, y
