@@ -145,6 +145,25 @@ def main():
     tflops = wl.flops / (ms * 1e-3) / 1e12
     hbm_gbs = wl.fused_bytes / (ms * 1e-3) / 1e9
 
+    # ---- decode on the packed weights with K split over workgroups: a side
+    #      measurement (its own entry point, with a caller workspace) ----------
+    splitk = None
+    if layout == sw.LAYOUT_PACKED and M <= 16 and args.config < 0:
+        cfg_k, s_k = sw.swiglu_packed_splitk_plan(h, M, N, K)
+        wsk = [torch.zeros((sw.swiglu_packed_splitk_workspace_bytes(N, K, s_k),),
+                           dtype=torch.uint8, device=dev) for _ in range(nsets)]
+
+        def splitk_step(i):
+            a, w1, _, y = sets[i % nsets]
+            sw.swiglu_forward_packed_splitk(h, a, w1, y, M, N, K, wsk[i % nsets], s_k, cfg_k,
+                                            stream)
+
+        kms, _ = timed(splitk_step, args.steps, args.warmup)
+        splitk = {"ms_per_step": round(kms, 5),
+                  "hbm_gbs_algorithmic": round(wl.fused_bytes / (kms * 1e-3) / 1e9, 1),
+                  "ksplit": s_k, "tile": sw.swiglu_config_info(cfg_k)}
+        del wsk
+
     # ---- unfused baseline on the same GEMM core (3 launches per step) -------
     unfused = None
     if not args.no_unfused:
@@ -236,6 +255,7 @@ def main():
         "pct_mfma_peak": round(100 * tflops / PEAK_BF16_TFLOPS, 2),
         "hbm_gbs_algorithmic": round(hbm_gbs, 1),
         "unfused": unfused,
+        "packed_splitk": splitk,
         "fp8": fp8,
         "roofline": roofline,
         "cpu_baseline": cpu,

@@ -38,8 +38,8 @@ _LIB_PATH = os.path.join(_PKG, "libswiglu.so")
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_DEVICE, ERR_LAUNCH, ERR_ALLOC = range(6)
 LAYOUT_SEPARATE, LAYOUT_INTERLEAVED, LAYOUT_PACKED = 0, 1, 2
 VARIANT_AUTO, VARIANT_SYNC, VARIANT_INTERLEAVE, VARIANT_GEMM, VARIANT_FP8, VARIANT_FP8_SYNC, \
-    VARIANT_MXFP8, VARIANT_PACKED, VARIANT_FP8_PACKED, VARIANT_MXFP8_PACKED, VARIANT_MXFP8_SYNC = \
-    0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10
+    VARIANT_MXFP8, VARIANT_PACKED, VARIANT_FP8_PACKED, VARIANT_MXFP8_PACKED, VARIANT_MXFP8_SYNC, \
+    VARIANT_PACKED_SPLITK = 0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11
 
 
 class SwiGLUError(RuntimeError):
@@ -114,6 +114,10 @@ def load():
         "swiglu_forward_mx_packed": ([p, p, p, p, p, p, i64, i64, i64, i64, i32, p], st),
         "swiglu_mx_packed_bytes": ([i64, i64], i64),
         "swiglu_pack_mx_fragments": ([p, p, p, i64, i64, p], st),
+        "swiglu_packed_splitk_workspace_bytes": ([i64, i64, i32], i64),
+        "swiglu_packed_splitk_plan": ([p, i64, i64, i64, ctypes.POINTER(i32),
+                                       ctypes.POINTER(i32)], st),
+        "swiglu_forward_packed_splitk": ([p, p, p, p, i64, i64, i64, i32, i32, p, i64, p], st),
     }
     for name, (args, res) in sig.items():
         fn = getattr(lib, name)
@@ -276,6 +280,31 @@ def swiglu_forward_mx_packed(handle, A8, SA, P8, SW, Y, M, N, K, ks, config_id=-
     _check(load().swiglu_forward_mx_packed(handle, _ptr(A8), _ptr(SA), _ptr(P8), _ptr(SW),
                                            _ptr(Y), M, N, K, ks, config_id, _stream(stream)),
            "swiglu_forward_mx_packed")
+
+
+def swiglu_packed_splitk_workspace_bytes(N: int, K: int, ksplit: int) -> int:
+    return int(load().swiglu_packed_splitk_workspace_bytes(N, K, ksplit))
+
+
+def swiglu_packed_splitk_plan(handle, M, N, K):
+    """(config id, S) the library picks for a split-K decode of this shape."""
+    cid, s = ctypes.c_int32(), ctypes.c_int32()
+    _check(load().swiglu_packed_splitk_plan(handle, M, N, K, ctypes.byref(cid), ctypes.byref(s)),
+           "swiglu_packed_splitk_plan")
+    return cid.value, s.value
+
+
+def swiglu_forward_packed_splitk(handle, A, P, Y, M, N, K, workspace, ksplit=0, config_id=-1,
+                                 stream=None):
+    """Decode forward (M <= 16) on fragment-ordered W_fused P with K split over
+    workgroups; `workspace` (a byte tensor, zeroed before its first use) holds
+    the counters and fp32 partials."""
+    _check(load().swiglu_forward_packed_splitk(handle, _ptr(A), _ptr(P), _ptr(Y), M, N, K,
+                                               config_id, ksplit, _ptr(workspace),
+                                               0 if workspace is None else
+                                               workspace.numel() * workspace.element_size(),
+                                               _stream(stream)),
+           "swiglu_forward_packed_splitk")
 
 
 def swiglu_mx_packed_bytes(N: int, K: int) -> int:

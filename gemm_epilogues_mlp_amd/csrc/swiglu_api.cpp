@@ -10,6 +10,7 @@
 
 #include <mutex>
 #include <new>
+#include <algorithm>
 #include <vector>
 
 #include "swiglu_internal.h"
@@ -582,6 +583,96 @@ swiglu_status_t swiglu_forward_mx(swiglu_handle_t h, const void* A8, const void*
                                   const void* W8, const void* SW, void* Y, int64_t M, int64_t N,
                                   int64_t K, int64_t ks, int32_t config_id, hipStream_t stream) {
   return forward_mx(h, A8, SA, W8, SW, Y, M, N, K, ks, config_id, stream, VAR_MX);
+}
+
+// ---- split-K streaming decode ---------------------------------------------------
+
+constexpr int kMaxSplit = 64;  // workgroups per (slab, part) along K
+
+// The split for a decode shape.  Slab parts as in the packed table (whole
+// slabs from 1.75 slabs per CU, config 85; half slabs from one per CU, 86;
+// quarter slabs below, 87), then K in as many pieces as it takes to give
+// every CU a workgroup, each piece keeping at least 16 K steps.  Measured on
+// MI355X at M = 16: the split pays only where the parts alone leave CUs idle
+// (N = 1184, K = 3584: 10.0 us with the 4 pieces this rule takes, 9.0 with 3,
+// 11.6 with one), since
+// the handoff adds memory round trips to the last workgroup of each part.
+void splitk_plan(long long N, long long K, int cus, int32_t* id, int32_t* S) {
+  const long long c = cus > 0 ? cus : 256;
+  const long long slabs = packed_slabs(N), steps = packed_steps(K);
+  int parts;
+  if (4 * slabs >= 7 * c) {
+    *id = 85, parts = 1;
+  } else if (slabs >= c) {
+    *id = 86, parts = 2;
+  } else {
+    *id = 87, parts = 4;
+  }
+  const long long units = slabs * parts;
+  long long s = (c + units - 1) / units;
+  s = std::min<long long>(s, std::max<long long>(1, steps / 16));
+  *S = (int32_t)std::max<long long>(1, std::min<long long>(s, kMaxSplit));
+}
+
+int64_t swiglu_packed_splitk_workspace_bytes(int64_t N, int64_t K, int32_t ksplit) {
+  if (N <= 0 || K < 0 || N > (kMaxDim >> 1) || K > kMaxDim || ksplit < 1 || ksplit > kMaxSplit)
+    return 0;
+  return splitk_workspace_bytes(packed_slabs(N), ksplit);
+}
+
+swiglu_status_t swiglu_packed_splitk_plan(swiglu_handle_t h, int64_t M, int64_t N, int64_t K,
+                                          int32_t* config_id, int32_t* ksplit) {
+  if (!h || M < 0 || N < 0 || K < 0) return SWIGLU_ERR_INVALID_ARG;
+  if (M > 16 || N > (kMaxDim >> 1) || K > kMaxDim) return SWIGLU_ERR_UNSUPPORTED;
+  int32_t id, S;
+  splitk_plan(N, K, h->cu_count, &id, &S);
+  if (config_id) *config_id = id;
+  if (ksplit) *ksplit = S;
+  return SWIGLU_OK;
+}
+
+swiglu_status_t swiglu_forward_packed_splitk(swiglu_handle_t h, const void* A, const void* P,
+                                             void* Y, int64_t M, int64_t N, int64_t K,
+                                             int32_t config_id, int32_t ksplit, void* workspace,
+                                             int64_t workspace_bytes, hipStream_t stream) {
+  bool noop = false;
+  swiglu_status_t st = check_forward(h, A, P, nullptr, Y, M, N, K, SWIGLU_LAYOUT_PACKED, &noop);
+  if (st != SWIGLU_OK) return st;
+  if (config_id >= 0) {
+    const KernelConfig* c = config_at(config_id);
+    if (!c || c->variant != VAR_PACKED_SPLITK) return SWIGLU_ERR_INVALID_ARG;
+  }
+  if (ksplit > kMaxSplit) return SWIGLU_ERR_UNSUPPORTED;
+  if (noop) return SWIGLU_OK;
+  if (M > 16) return SWIGLU_ERR_UNSUPPORTED;
+  int32_t id = config_id, S = ksplit;
+  if (id < 0 || S < 1) {
+    int32_t pid, pS;
+    splitk_plan(N, K, h->cu_count, &pid, &pS);
+    if (id < 0) id = pid;
+    if (S < 1) S = pS;
+  }
+  const long long need = splitk_workspace_bytes(packed_slabs(N), S);
+  if (!workspace || workspace_bytes < need) return SWIGLU_ERR_INVALID_ARG;
+  if (!aligned16(workspace)) return SWIGLU_ERR_UNSUPPORTED;
+  if (overlaps(workspace, need, Y, 2LL * M * N) || overlaps(workspace, need, A, 2LL * M * K) ||
+      overlaps(workspace, need, P, 2LL * packed_elems(N, K)))
+    return SWIGLU_ERR_INVALID_ARG;
+  const KernelConfig* cfg = config_at(id);
+  LaunchArgs a;
+  a.A = (const uint16_t*)A;
+  a.W1 = (const uint16_t*)P;
+  a.W2 = nullptr;
+  a.Y = (uint16_t*)Y;
+  a.M = (int)M, a.N = (int)N, a.K = (int)K;
+  a.ldw = 0;
+  a.ldy = (int)N;
+  a.group_m = 0;
+  a.cu_count = h->cu_count;
+  a.stream = stream;
+  a.ws = workspace;
+  a.ksplit = S;
+  return launch(h, cfg, id, a);
 }
 
 swiglu_status_t swiglu_forward_mx_packed(swiglu_handle_t h, const void* A8, const void* SA,

@@ -86,6 +86,28 @@ __device__ __forceinline__ void lds_dma16(uint32_t lds_wave_base, uint32_t voffs
                : "memory");
 }
 
+// Cross-workgroup handoff of fp32 partial sums (the split-K decode kernel).
+// The partials are written and read with agent-scope atomic stores and loads
+// (device-coherent accesses, which do not stay in one XCD's L2), so no
+// cache-wide writeback or invalidate is needed: after its partial stores
+// have completed (s_waitcnt vmcnt(0)) a workgroup increments the counter, and
+// the last one to arrive reads every partial with agent-scope loads.
+__device__ __forceinline__ void store_agent(f32x4* p, f32x4 v) {
+  float* f = reinterpret_cast<float*>(p);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) __hip_atomic_store(f + i, v[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ f32x4 load_agent(const f32x4* p) {
+  const float* f = reinterpret_cast<const float*>(p);
+  f32x4 v;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) v[i] = __hip_atomic_load(f + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return v;
+}
+__device__ __forceinline__ uint32_t atomic_add_agent(uint32_t* p, uint32_t v) {
+  return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
   static_assert(N >= 0 && N <= 63, "vmcnt range");

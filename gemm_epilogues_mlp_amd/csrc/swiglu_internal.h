@@ -14,9 +14,12 @@ namespace swiglu {
 // VAR_F8_PACKED: interleave order on FP8 inputs with fragment-ordered W8
 // VAR_MX_PACKED: interleave order on MXFP8 inputs, W8 in the 32x32x64 fragment order
 // VAR_MX_SYNC: sync order on MXFP8 inputs (the same W8 and scales as VAR_MX)
+// VAR_PACKED_SPLITK: VAR_PACKED with K also split over workgroups (M <= 16;
+// needs a workspace, swiglu_forward_packed_splitk only)
 enum Variant {
   VAR_AUTO = 0, VAR_SYNC = 1, VAR_INTERLEAVE = 2, VAR_GEMM = 3, VAR_F8 = 4, VAR_F8_SYNC = 5,
-  VAR_MX = 6, VAR_PACKED = 7, VAR_F8_PACKED = 8, VAR_MX_PACKED = 9, VAR_MX_SYNC = 10
+  VAR_MX = 6, VAR_PACKED = 7, VAR_F8_PACKED = 8, VAR_MX_PACKED = 9, VAR_MX_SYNC = 10,
+  VAR_PACKED_SPLITK = 11
 };
 
 // Fragment-ordered W_fused: slabs of 128 columns times steps of 32 k, 4096
@@ -37,6 +40,14 @@ inline long long mx_packed_bytes(long long N, long long K) {
   return ((2 * N + 31) / 32) * (K / 64) * 2048;
 }
 
+// Workspace of the split-K streaming kernel for `slabs` slabs of W_fused and
+// S pieces of K: a uint32 counter per (slab, part) -- slabs * 4 reserved,
+// rounded to 256 bytes -- then the fp32 partials, 8 KB per slab and piece.
+inline long long splitk_counter_bytes(long long slabs) { return (slabs * 16 + 255) / 256 * 256; }
+inline long long splitk_workspace_bytes(long long slabs, long long S) {
+  return splitk_counter_bytes(slabs) + slabs * S * 8192;
+}
+
 struct LaunchArgs {
   const uint16_t* A;
   const uint16_t* W1;  // W1, W_fused, or the single GEMM weight
@@ -51,13 +62,15 @@ struct LaunchArgs {
   const uint8_t* SW;
   int ks;                  // MXFP8: scale row stride (bytes, a multiple of 16)
   hipStream_t stream;
+  void* ws = nullptr;      // split-K streaming: workspace (splitk_workspace_bytes)
+  int ksplit = 1;          // split-K streaming: workgroups per (slab, part) along K
 };
 
 typedef hipError_t (*LaunchFn)(const LaunchArgs&);
 
 struct KernelConfig {
   int variant;  // Variant
-  int family;   // 0 tiled, 1 skinny
+  int family;   // 0 tiled, 1 streaming, 2 persistent tiled, 3 streaming split over workgroups
   int bm, bn, bk, waves, split_k, lds_bytes;
   LaunchFn launch;
   int tail_split;  // 0, or 4: big tiles of a partial last round run as quarter tiles

@@ -1145,6 +1145,124 @@ void packed_kernel(const uint16_t* __restrict__ A, const uint16_t* __restrict__ 
   }
 }
 
+// ---- the same streaming with K split over workgroups (M <= 16) -------------
+// When the slabs cannot spread over the CUs (few output columns, e.g. one
+// GPU's share of a tensor-parallel MLP at decode), S workgroups share each
+// (slab, part): workgroup kp of S takes the contiguous K steps
+// [kp n / S, (kp + 1) n / S) of it (n = ceil(K / 32)), reduces its waves in
+// LDS, and writes the fp32 partial sums of its 16 x 8CH block to the
+// workspace (device-coherent stores).  The last of the S to arrive (a counter per (slab, part)) adds
+// the S partials in K order -- fixed, so the result does not depend on which
+// arrives last -- and does SiLU and the pair product: every partial is fp32
+// and fully reduced before SiLU, as the page requires for split sums across
+// tiles ([RT §Risultati], the FP32 cross-tile accumulation behind its 0 %
+// error claim).  Nothing waits on another workgroup, so no order of
+// execution can stall the launch.  The last one also puts the counter back to
+// zero, so a workspace that starts zeroed stays ready for the next call.
+//
+// Workspace (splitk_workspace_bytes): the counters, then the partials, each
+// workgroup's CH KB (CH f32x4 per lane) at its unit index.
+template <int NW, int CH>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(4)))
+void packed_splitk_kernel(const uint16_t* __restrict__ A, const uint16_t* __restrict__ P,
+                          uint16_t* __restrict__ Y, int M, int N, int K, int S,
+                          uint32_t* __restrict__ counters, f32x4* __restrict__ partials) {
+  using C = Packed<1, NW, CH>;
+  __shared__ __attribute__((aligned(16))) f32x4 red[NW * CH * 64];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  // units in memory order: (slab, part) major, the S pieces of K minor, so
+  // concurrently running workgroups stream neighbouring weight runs
+  const int unit = blockIdx.x;
+  const int sp = unit / S, kp = unit % S;
+  const int slab = sp / C::PARTS, part = sp % C::PARTS;
+  const int nsteps = (K + 31) / 32;
+  const int s0 = (int)((long long)kp * nsteps / S), s1 = (int)((long long)(kp + 1) * nsteps / S);
+  const uint16_t* wp = P + (size_t)slab * (size_t)nsteps * 4096 + part * CH * 512 + lane * 8;
+
+  f32x4 acc[CH];
+#pragma unroll
+  for (int c = 0; c < CH; ++c) acc[c] = f32x4{};
+  auto mma = [&](const u32x4 (&b)[CH], const u32x4 (&af)[1], int step) {
+    const bool kin = step * 32 + (lane >> 4) * 8 < K;  // K % 8 == 0
+    const u32x4 a = kin ? af[0] : u32x4{0, 0, 0, 0};
+#pragma unroll
+    for (int c = 0; c < CH; ++c) acc[c] = mfma16(a, b[c], acc[c]);
+  };
+  // this wave's steps s0 + wave, s0 + wave + NW, ... (< s1): pairs loaded
+  // together, then multiplied (the one-row-group loop of packed_kernel)
+  {
+    u32x4 b0[CH], a0[1], b1[CH], a1[1];
+    int s = s0 + wave;
+    for (; s + NW < s1; s += 2 * NW) {
+      packed_load<1, CH>(A, wp, M, K, 0, lane, s, b0, a0);
+      packed_load<1, CH>(A, wp, M, K, 0, lane, s + NW, b1, a1);
+      mma(b0, a0, s);
+      mma(b1, a1, s + NW);
+    }
+    if (s < s1) {
+      packed_load<1, CH>(A, wp, M, K, 0, lane, s, b0, a0);
+      mma(b0, a0, s);
+    }
+  }
+
+  // the waves' sums in LDS, added in wave order by wave 0
+#pragma unroll
+  for (int c = 0; c < CH; ++c) red[(wave * CH + c) * 64 + lane] = acc[c];
+  __syncthreads();
+  if (wave != 0) return;
+  f32x4 v[CH];
+#pragma unroll
+  for (int c = 0; c < CH; ++c) {
+    v[c] = red[c * 64 + lane];
+    for (int w = 1; w < NW; ++w) v[c] += red[(w * CH + c) * 64 + lane];
+  }
+
+  if (S > 1) {
+    // hand the partial over; the last of the S workgroups of this (slab, part)
+    // continues with the sum of all S in K order
+    f32x4* mine = partials + (size_t)unit * CH * 64;
+#pragma unroll
+    for (int c = 0; c < CH; ++c) store_agent(mine + c * 64 + lane, v[c]);
+    wait_vmcnt<0>();  // the partial has reached the device-coherent level
+    uint32_t before = 0;
+    if (lane == 0) before = atomic_add_agent(counters + sp, 1u);
+    before = (uint32_t)__builtin_amdgcn_readfirstlane((int)before);
+    if (before != (uint32_t)(S - 1)) return;
+    const f32x4* all = partials + (size_t)sp * S * CH * 64;
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+      v[c] = load_agent(all + c * 64 + lane);
+      for (int k = 1; k < S; ++k) v[c] += load_agent(all + (k * CH + c) * 64 + lane);
+    }
+    if (lane == 0) counters[sp] = 0u;  // every workgroup of this (slab, part) has counted
+  }
+
+  // lane l holds W_fused columns 128 slab + 8 (l % 16) + part CH + c of rows
+  // 4 (l / 16) + r: the pair (c, c + 1), c even, is output column
+  // 64 slab + 4 (l % 16) + (part CH + c) / 2
+  const int col = slab * 64 + (lane & 15) * 4 + part * CH / 2;
+  if (col >= N) return;  // N % 8 == 0: a lane's outputs are all in or all out
+  const int rq = (lane >> 4) * 4;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int row = rq + r;
+    if (row >= M) continue;
+    float y[CH / 2];
+#pragma unroll
+    for (int q = 0; q < CH / 2; ++q) y[q] = silu(v[2 * q][r]) * v[2 * q + 1][r];
+    uint16_t* out = Y + (size_t)row * N + col;
+    if constexpr (CH == 8) {
+      *reinterpret_cast<u32x2*>(out) = u32x2{pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3])};
+    } else if constexpr (CH == 4) {
+      *reinterpret_cast<uint32_t*>(out) = pack_bf16x2(y[0], y[1]);
+    } else {
+      *out = bf16_bits(y[0]);
+    }
+  }
+}
+
 // ============================================================================
 // FP8 (OCP E4M3) inputs: LDS-tiled interleave and sync kernels
 // ============================================================================
@@ -2350,6 +2468,20 @@ static hipError_t launch_packed(const LaunchArgs& a) {
                      dim3(C::kThreads), 0, a.stream, a.A, a.W1, a.Y, a.M, a.N, a.K);
 }
 
+template <int NW, int CH>
+static hipError_t launch_packed_splitk(const LaunchArgs& a) {
+  using C = Packed<1, NW, CH>;
+  const long long slabs = packed_slabs(a.N);
+  const long long nunit = slabs * C::PARTS * (long long)a.ksplit;
+  if (a.M <= 0 || nunit <= 0) return hipSuccess;
+  if (a.ksplit < 1 || a.M > 16 || nunit > 0x7fffffffLL || !a.ws) return hipErrorInvalidValue;
+  uint32_t* counters = static_cast<uint32_t*>(a.ws);
+  f32x4* partials =
+      reinterpret_cast<f32x4*>(static_cast<uint8_t*>(a.ws) + splitk_counter_bytes(slabs));
+  return launch_kernel((packed_splitk_kernel<NW, CH>), dim3((unsigned)nunit), dim3(C::kThreads),
+                       0, a.stream, a.A, a.W1, a.Y, a.M, a.N, a.K, a.ksplit, counters, partials);
+}
+
 template <int MODE, int BM, int BNW, int STAGES, int WGM, int WGN>
 static hipError_t launch_f8(const LaunchArgs& a) {
   using C = F8Tiled<MODE, BM, BNW, STAGES, WGM, WGN>;
@@ -2447,6 +2579,9 @@ static hipError_t launch_mx_packed(const LaunchArgs& a) {
   {v, 2, bm, Tiled<mode, bm, bnw, bk, st, wgm, wgn>::BNY, bk, (wgm) * (wgn), 1,             \
    Persist<mode, bm, bnw, bk, st, wgm, wgn>::LDS_BYTES,                                     \
    &launch_tiled_persist<mode, bm, bnw, bk, st, wgm, wgn, swgm, swgn>, 4}
+#define PACKED_SPLITK(nw, ch)                                                              \
+  {VAR_PACKED_SPLITK, 3, 16, Packed<1, nw, ch>::COLS_Y, 32, nw, nw, Packed<1, nw, ch>::LDS_BYTES, \
+   &launch_packed_splitk<nw, ch>}
 #define PACKED(mt, nw, ch)                                                                 \
   {VAR_PACKED, 1, (mt) * 16, Packed<mt, nw, ch>::COLS_Y, 32, nw, nw,                          \
    Packed<mt, nw, ch>::LDS_BYTES, &launch_packed<mt, nw, ch>}
@@ -2560,6 +2695,10 @@ static const KernelConfig kConfigs[] = {
     F8_SPLIT(MODE_MX_SYNC, VAR_MX_SYNC, 256, 128, 4, 4, 2, 4, 2),   // 82
     F8(MODE_MX_SYNC, VAR_MX_SYNC, 128, 128, 4, 2, 2),               // 83
     F8(MODE_MX_SYNC, VAR_MX_SYNC, 64, 64, 4, 2, 2),                 // 84
+    // ---- fragment-ordered W_fused streaming with K split over workgroups ----
+    PACKED_SPLITK(4, 8),                                            // 85
+    PACKED_SPLITK(4, 4),                                            // 86
+    PACKED_SPLITK(4, 2),                                            // 87
 };
 
 int config_count() { return (int)(sizeof(kConfigs) / sizeof(kConfigs[0])); }

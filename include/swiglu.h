@@ -105,9 +105,11 @@ typedef enum {
   SWIGLU_VARIANT_MXFP8_PACKED = 9, /* Kernel-2 order on MXFP8 inputs with
                                     fragment-ordered W8 (swiglu_forward_mx_packed;
                                     swiglu_query_fp8)                          */
-  SWIGLU_VARIANT_MXFP8_SYNC = 10  /* Kernel-1 order on MXFP8 inputs, the same W8
+  SWIGLU_VARIANT_MXFP8_SYNC = 10, /* Kernel-1 order on MXFP8 inputs, the same W8
                                     and scales (swiglu_forward_mx with a config
                                     of this variant; swiglu_query_fp8)         */
+  SWIGLU_VARIANT_PACKED_SPLITK = 11 /* PACKED with K also split over workgroups
+                                    (swiglu_forward_packed_splitk only)        */
 } swiglu_variant_t;
 
 /* Description of one compiled kernel configuration. */
@@ -120,7 +122,9 @@ typedef struct swiglu_tile {
                           MFMA 16x16x32 (weights straight to registers),
                           2 = LDS-tiled on one persistent workgroup per
                           CU looping over tiles, the next tile's loads
-                          issued under the current tile's last K steps     */
+                          issued under the current tile's last K steps,
+                          3 = streaming as 1 with K also split over
+                          workgroups (fp32 partials in a workspace)        */
   int32_t bm;          /* output rows per workgroup                           */
   int32_t bn;          /* output (Y or G) columns per workgroup               */
   int32_t bk;          /* K depth of one pipeline stage                       */
@@ -235,6 +239,48 @@ int64_t swiglu_packed_bytes(int64_t N, int64_t K);
 swiglu_status_t swiglu_pack_fragments(swiglu_handle_t h, const void* W1, const void* W2,
                                       void* P, int64_t K, int64_t N, hipStream_t stream);
 
+/* ---- decode with K split over workgroups (PACKED layout, 1 <= M <= 16) ----
+ * For decode shapes whose weight slabs are too few to give every CU work (a
+ * narrow N, such as one GPU's share of a tensor-parallel MLP), S workgroups
+ * share each slab part: each streams a contiguous range of its K steps and
+ * writes fp32 partial sums to a caller workspace; the last of the S to finish
+ * adds them in K order (fixed, so results are reproducible) and applies SiLU
+ * and the pair product [RT §Metodologia, Kernel-2 pairing; §Risultati: split
+ * sums kept in FP32 and reduced before the activation].  No workgroup waits
+ * for another.
+ *
+ * Workspace: swiglu_packed_splitk_workspace_bytes(N, K, S) bytes, 16-byte
+ * aligned, caller-owned, **all zero before its first use**: it holds a counter
+ * per slab part, and every call leaves those back at zero when it completes,
+ * so a workspace zeroed once can serve any number of calls in stream order.
+ * Calls that may run at the same time on the GPU need workspaces of their own;
+ * a call that did not complete (an aborted launch) leaves it to be zeroed
+ * again. */
+
+/* Bytes of the split-K workspace for N, K and S pieces of K: a 256-byte
+ * aligned block of counters (ceil(2N/128) * 16 bytes, rounded up) plus
+ * ceil(2N/128) * S * 8192 bytes of fp32 partials.  0 for N <= 0, K < 0,
+ * S outside [1, 64] or sizes out of range. */
+int64_t swiglu_packed_splitk_workspace_bytes(int64_t N, int64_t K, int32_t ksplit);
+
+/* The configuration (variant PACKED_SPLITK) and S the library picks for the
+ * shape on this handle's device (either out-pointer may be NULL).
+ * UNSUPPORTED for M > 16. */
+swiglu_status_t swiglu_packed_splitk_plan(swiglu_handle_t h, int64_t M, int64_t N, int64_t K,
+                                          int32_t* config_id, int32_t* ksplit);
+
+/* Y = SiLU(A W1) * (A W2) for 1 <= M <= 16 on the fragment-ordered W_fused P
+ * (swiglu_pack_fragments), K split into S = ksplit pieces over workgroups.
+ * config_id < 0 or ksplit < 1: the plan's choice for that argument.  The
+ * arguments are checked as for swiglu_forward with the PACKED layout; also
+ * INVALID_ARG for a config of another variant, a NULL or too small workspace,
+ * or one overlapping A, P or Y; UNSUPPORTED for M > 16, S > 64 or a
+ * workspace not 16-byte aligned. */
+swiglu_status_t swiglu_forward_packed_splitk(swiglu_handle_t h, const void* A, const void* P,
+                                             void* Y, int64_t M, int64_t N, int64_t K,
+                                             int32_t config_id, int32_t ksplit, void* workspace,
+                                             int64_t workspace_bytes, hipStream_t stream);
+
 /* What swiglu_forward / _ex(AUTO) would run for this shape and layout, and
  * which layout the table recommends for the shape (the per-batch choice of
  * kernel family [RT §Contributi Chiave, item 2]): PACKED up to M = 64 (up to
@@ -252,7 +298,8 @@ swiglu_status_t swiglu_query_unfused(swiglu_handle_t h, int64_t M, int64_t N,
 /* Tuned per-shape configurations.  A tuned file (written by the package's
  * tuner, python -m gemm_epilogues_mlp_amd.tune) is text:
  *   swiglu-tuned <signature: 16 hex digits> <arch>        first non-comment line
- *   <variant 1..9> <M> <N> <K> <config id> [ignored provenance]    one per shape
+ *   <variant> <M> <N> <K> <config id> [ignored provenance]    one per shape
+ * (variant: a swiglu_variant_t value, the one of the config)
  * with '#' comment lines.  The signature (swiglu_config_signature) identifies
  * the list of compiled configurations; a file written for a library with a
  * different list is refused, so an id can never name the wrong kernel.

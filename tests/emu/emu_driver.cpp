@@ -13,6 +13,7 @@
 //        --last-blocks B               only the last B workgroups of each launch
 //        --no-races                    bounds only (no LDS ordering check)
 //        --race-blocks B               the ordering check on the last B workgroups only
+//        --ksplit S                    pieces of K for the split-K streaming configs (3)
 //        --plant P                     switch on planted mistake P (build.py)
 #include <stdio.h>
 #include <stdlib.h>
@@ -26,6 +27,7 @@ dim3 threadIdx, blockIdx, gridDim, blockDim;
 long g_emu_last_blocks = 0;
 long g_emu_race_errors = 0;
 long g_emu_race_blocks = 0;
+int g_emu_ksplit = 3;  // pieces of K for the split-K streaming configs
 int g_emu_plant = 0;
 
 // the LDS ordering check (emu_race.cpp)
@@ -109,15 +111,22 @@ bool run_config(int id, int M, int N, int K) {
   const long l0 = g_lds_checks, g0 = g_global_checks;
   LaunchArgs a{};
   a.M = M, a.N = N, a.K = K;
+  if (c->variant == VAR_PACKED_SPLITK && M > 16) a.M = M = 16;
   a.A = alloc16((size_t)M * K, "A");
   if (c->variant == VAR_INTERLEAVE) {
     a.W1 = alloc16((size_t)K * 2 * N, "W_fused");
     a.W2 = nullptr;
     a.ldw = 2 * N;
-  } else if (c->variant == VAR_PACKED) {
+  } else if (c->variant == VAR_PACKED || c->variant == VAR_PACKED_SPLITK) {
     a.W1 = alloc16((size_t)packed_elems(N, K), "P");  // fragment-ordered W_fused
     a.W2 = nullptr;
     a.ldw = 0;
+    if (c->variant == VAR_PACKED_SPLITK) {
+      // decode rows only; the workspace zeroed as the API requires
+      if (M > 16) a.M = M = 16;
+      a.ksplit = g_emu_ksplit;
+      a.ws = alloc16((size_t)splitk_workspace_bytes(packed_slabs(N), a.ksplit) / 2, "splitk ws");
+    }
   } else if (c->variant == VAR_SYNC) {
     a.W1 = alloc16((size_t)K * N, "W1");
     a.W2 = alloc16((size_t)K * N, "W2");
@@ -149,6 +158,17 @@ bool run_config(int id, int M, int N, int K) {
   a.cu_count = 256;
   a.stream = nullptr;
   const hipError_t e = c->launch(a);
+  if (c->variant == VAR_PACKED_SPLITK && e == hipSuccess && g_emu_last_blocks == 0) {
+    // every (slab, part) counter is back at zero once the last piece is done
+    // (when every workgroup of the launch ran)
+    const uint32_t* cnt = (const uint32_t*)a.ws;
+    for (long long i = 0; i < packed_slabs(N) * 4; ++i)
+      if (cnt[i] != 0) {
+        fprintf(stderr, "split-K counter %lld left at %u in %s\n", i, cnt[i], g_ctx.c_str());
+        ++g_errors;
+        break;
+      }
+  }
   free_all();
   if (e != hipSuccess) fprintf(stderr, "launch refused: %s\n", g_ctx.c_str());
   const bool ok = g_errors + g_emu_race_errors == before;
@@ -240,6 +260,8 @@ int main(int argc, char** argv) {
   for (int i = 1; i < argc; ++i) {
     if (std::string(argv[i]) == "--no-races") {
       races = false;
+    } else if (std::string(argv[i]) == "--ksplit" && i + 1 < argc) {
+      g_emu_ksplit = atoi(argv[++i]);
     } else if (std::string(argv[i]) == "--race-blocks" && i + 1 < argc) {
       g_emu_race_blocks = atol(argv[++i]);
     } else if (std::string(argv[i]) == "--plant" && i + 1 < argc) {

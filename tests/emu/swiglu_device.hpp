@@ -160,6 +160,26 @@ inline void lds_dma16(uint32_t lds_wave_base, uint32_t voffset, i32x4 rsrc) {
   emu_check_global(base + voffset, 16, "lds_dma16 source");
   emu_copy(d, base + voffset, 16);
 }
+// cross-workgroup handoff: the workgroups run one after another here, so the
+// coherent accesses are plain copies (their addresses checked) and the
+// counter a plain add
+inline void store_agent(f32x4* p, f32x4 v) {
+  emu_check_global(p, 16, "store_agent");
+  emu_copy(p, &v, 16);
+}
+inline f32x4 load_agent(const f32x4* p) {
+  emu_check_global(p, 16, "load_agent");
+  emu_race_vmop();
+  f32x4 v;
+  emu_copy(&v, p, 16);
+  return v;
+}
+inline uint32_t atomic_add_agent(uint32_t* p, uint32_t v) {
+  emu_check_global(p, 4, "atomic_add_agent");
+  const uint32_t old = *p;
+  *p = old + v;
+  return old;
+}
 template <int N>
 inline void wait_vmcnt() {
   static_assert(N >= 0 && N <= 63, "vmcnt range");

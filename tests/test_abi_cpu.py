@@ -81,6 +81,20 @@ def test_null_handle_and_bad_arguments_rejected():
         sw.ERR_INVALID_ARG
     assert lib.swiglu_mx_packed_bytes(20, 128) == 2 * 2 * 2048
     assert lib.swiglu_mx_packed_bytes(20, 100) == 0
+    assert lib.swiglu_forward_packed_splitk(None, None, None, None, 16, 72, 40, -1, 2, None, 0,
+                                            None) == sw.ERR_INVALID_ARG
+    assert lib.swiglu_packed_splitk_plan(None, 16, 72, 40, None, None) == sw.ERR_INVALID_ARG
+
+
+def test_splitk_workspace_bytes():
+    # a 256-byte block of counters (16 bytes per slab, rounded up), then 8 KB
+    # of partials per slab and piece of K
+    assert sw.swiglu_packed_splitk_workspace_bytes(72, 40, 3) == 256 + 2 * 3 * 8192
+    assert sw.swiglu_packed_splitk_workspace_bytes(18944, 3584, 4) == 4864 + 296 * 4 * 8192
+    assert sw.swiglu_packed_splitk_workspace_bytes(2368, 3584, 1) == 768 + 37 * 8192
+    assert sw.swiglu_packed_splitk_workspace_bytes(72, 0, 2) == 256 + 2 * 2 * 8192
+    for bad in ((0, 40, 2), (72, -1, 2), (72, 40, 0), (72, 40, 65)):
+        assert sw.swiglu_packed_splitk_workspace_bytes(*bad) == 0
 
 
 def test_status_strings_and_workspace_size():
@@ -95,13 +109,17 @@ def test_config_list_is_consistent():
     assert n > 0
     seen = {sw.VARIANT_SYNC: 0, sw.VARIANT_INTERLEAVE: 0, sw.VARIANT_GEMM: 0, sw.VARIANT_FP8: 0,
             sw.VARIANT_FP8_SYNC: 0, sw.VARIANT_MXFP8: 0, sw.VARIANT_PACKED: 0,
-            sw.VARIANT_FP8_PACKED: 0, sw.VARIANT_MXFP8_PACKED: 0, sw.VARIANT_MXFP8_SYNC: 0}
+            sw.VARIANT_FP8_PACKED: 0, sw.VARIANT_MXFP8_PACKED: 0, sw.VARIANT_MXFP8_SYNC: 0,
+            sw.VARIANT_PACKED_SPLITK: 0}
     for i in range(n):
         c = sw.swiglu_config_info(i)
         assert c["id"] == i
         assert c["variant"] in seen
         seen[c["variant"]] += 1
-        assert c["family"] in (0, 1, 2)
+        assert c["family"] in (0, 1, 2, 3)
+        assert (c["family"] == 3) == (c["variant"] == sw.VARIANT_PACKED_SPLITK)
+        if c["family"] == 3:  # decode rows, 32-deep K steps, the packed slab parts
+            assert c["bm"] == 16 and c["bk"] == 32 and c["bn"] in (16, 32, 64)
         assert c["tail_split"] in (0, 4)
         if c["tail_split"]:
             assert c["family"] in (0, 2) and c["bm"] % 64 == 0 and c["bn"] % 64 == 0

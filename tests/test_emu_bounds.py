@@ -120,6 +120,10 @@ CASES = [
     (16, 18944, 3584, list(range(70, 77))),
     (128, 4864, 896, list(range(70, 77))),
     (33, 72, 144, list(range(70, 77))),
+    # fragment-ordered W_fused with K split over workgroups (3 pieces): a
+    # narrow N (one GPU's share under 8-way tensor parallelism), 7B decode
+    (16, 2368, 3584, [85, 86, 87]),
+    (16, 18944, 3584, [86]),
     # MXFP8 on fragment-ordered W8: decode, 0.5B, ragged row blocks and groups
     (16, 18944, 3584, [77, 78, 79, 80, 81]),
     (128, 4864, 896, [77, 78, 79, 80, 81]),
@@ -142,6 +146,17 @@ def test_table_configs_at_workload_sizes(emu, case):
         assert rc == 0 and "errors: 0" in out, out[-4000:]
 
 
+# the split-K streaming configs with other numbers of pieces of K: one (no
+# handoff), two, more pieces than a shape has K steps (empty pieces)
+@pytest.mark.parametrize("ksplit", [1, 2, 7, 64])
+def test_splitk_pieces(emu, ksplit):
+    for shape in ((13, 264, 200), (16, 2368, 3584), (1, 8, 8)):
+        for cfg in (85, 86, 87):
+            rc, out = _run(emu, "--ksplit", ksplit, "--race-blocks", RACE_BLOCKS, "--shape",
+                           *shape, cfg)
+            assert rc == 0 and "errors: 0" in out, out[-4000:]
+
+
 # tensors just under the 2 GiB limit (largest byte offsets the kernels form):
 # A = 2 * 65536 * 16376 B, and W_fused = 4 * 16376 * 32768 B (bf16), and the
 # byte tensors of the FP8 kernels; only the last workgroups of each launch are
@@ -153,7 +168,7 @@ LIMIT_CASES = [
     (65536, 512, 16256, [36, 37], 4),
     (16, 32768, 16376, [4, 11, 18, 23, 12], 8),
     # fragment-ordered W_fused just under 2 GiB: 511 slabs x 512 steps x 8 KB
-    (16, 32704, 16376, list(range(58, 70)), 8),
+    (16, 32704, 16376, list(range(58, 70)) + [85, 86, 87], 8),
     # fragment-ordered W8 just under 2 GiB: 4096 row blocks x 255 steps x 2 KB
     (16, 32768, 32640, list(range(70, 77)), 8),
     # MX fragment-ordered W8 just under 2 GiB: 2048 row blocks x 511 steps x 2 KB
