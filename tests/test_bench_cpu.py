@@ -24,18 +24,30 @@ def test_more_than_one_gpu_is_refused(n):
 
 
 def test_counter_traffic_follows_the_kernel_source(tmp_path, monkeypatch):
-    data = json.load(open(os.path.join(ROOT, "profiles", "traffic.json")))
     sha = bench.kernel_source_hash()
-    keys = [k for k, v in data.items() if "/" in k and v.get("kernel_source_sha") == sha]
-    # the headline workload's table choice has a summary on the current source
-    assert any(k.startswith("qwen2.5-72b-mlp/interleaved/") for k in keys), sorted(data)
-    k = next(k for k in keys if k.startswith("qwen2.5-72b-mlp/interleaved/"))
-    cfg = int(k.rsplit("config", 1)[1])
-    got = bench.counter_traffic("qwen2.5-72b-mlp", 1, {"id": cfg})
-    assert got == data[k]["hbm_bytes_per_launch"] and got > data[k]["algorithmic_bytes"]
-    # another kernel source: no traffic figure
-    monkeypatch.setattr(bench, "kernel_source_hash", lambda: "0" * 16)
-    assert bench.counter_traffic("qwen2.5-72b-mlp", 1, {"id": cfg}) is None
-    # an unknown configuration: none either
-    monkeypatch.undo()
-    assert bench.counter_traffic("qwen2.5-72b-mlp", 1, {"id": 9999}) is None
+    (tmp_path / "profiles").mkdir()
+    data = {"qwen2.5-72b-mlp/interleaved/config40": {
+        "hbm_bytes_per_launch": 6479065631, "algorithmic_bytes": 1278214144,
+        "kernel_source_sha": sha},
+            "qwen2.5-1.5b-mlp/interleaved/config40": {
+        "hbm_bytes_per_launch": 235100000, "algorithmic_bytes": 98041856,
+        "kernel_source_sha": "0" * 16}}
+    (tmp_path / "profiles" / "traffic.json").write_text(json.dumps(data))
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    assert bench.counter_traffic("qwen2.5-72b-mlp", 1, {"id": 40}) == 6479065631
+    # a summary taken on another kernel source gives no traffic figure
+    assert bench.counter_traffic("qwen2.5-1.5b-mlp", 1, {"id": 40}) is None
+    # nor does another layout or configuration
+    assert bench.counter_traffic("qwen2.5-72b-mlp", 0, {"id": 40}) is None
+    assert bench.counter_traffic("qwen2.5-72b-mlp", 1, {"id": 41}) is None
+    # nor a missing or unreadable file
+    (tmp_path / "profiles" / "traffic.json").write_text("{not json")
+    assert bench.counter_traffic("qwen2.5-72b-mlp", 1, {"id": 40}) is None
+
+
+def test_committed_traffic_summaries_are_well_formed():
+    data = json.load(open(os.path.join(ROOT, "profiles", "traffic.json")))
+    assert data
+    for key, v in data.items():
+        assert v["hbm_bytes_per_launch"] > 0 and v["algorithmic_bytes"] > 0, key
+        assert len(v["kernel_source_sha"]) == 16, key
