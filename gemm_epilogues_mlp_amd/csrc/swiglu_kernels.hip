@@ -21,7 +21,10 @@
 //    straight into a ring of LDS stages by DMA; weight fragments are read with
 //    the transposing LDS read; the MFMA computes D^T = W^T A^T so that a Gate
 //    / Up pair of the interleave mode sits in two adjacent registers of one
-//    lane.  Interleave, sync and plain-GEMM (unfused baseline) modes.
+//    lane.  Interleave, sync and plain-GEMM (unfused baseline) modes.  The
+//    split launch runs a short last round as quarter tiles; the persistent one
+//    keeps one workgroup per CU looping over tiles, the next tile's loads
+//    issued under the current tile's last K steps (Kernel-2's overlap).
 //
 //  * skinny_kernel  split-K weight streaming for small M (decode-sized
 //    batches), v_mfma_f32_16x16x32_bf16.  Each lane loads an 8 (k) x 8 (column)
@@ -36,11 +39,14 @@
 //
 //  * packed_kernel  the same streaming on W_fused stored once in MFMA
 //    fragment order: 1 KB contiguous per load, no transposition.
+//    packed_splitk_kernel also splits K over workgroups (decode shapes with
+//    few slabs): fp32 partials handed to the last workgroup of each slab part,
+//    which reduces them in K order before SiLU.
 //
 //  * f8_kernel / f8_split_kernel / f8_skinny_kernel / f8_packed_kernel  FP8
-//    (E4M3) inputs on the scaled MFMAs, LDS-tiled and streaming; MX mode of
-//    the tile and mx_packed_kernel for MXFP8 (E8M0 block scales applied by
-//    the MFMA).
+//    (E4M3) inputs on the scaled MFMAs, LDS-tiled and streaming, in both
+//    orders; MX modes of the tile (both orders) and mx_packed_kernel for
+//    MXFP8 (E8M0 block scales applied by the MFMA).
 //
 //  * element-wise kernels: the unfused gate, the weight packs and the FP8 /
 //    MX quantisers.
