@@ -1515,13 +1515,21 @@ __device__ __forceinline__ void f8_tile(const uint8_t* __restrict__ A,
   };
   u32x4 wf[C::FW][2];
   u32x4 af[2][C::FA][2];
-  // MX: scale bytes of the lane's rows for the current step, packed (the MFMA
-  // selects a byte): weight block i in byte i of scw, activation block j of
-  // parity P in byte 2 P + j of sca
-  static_assert(!C::MX || (C::FW <= 4 && C::FA <= 2), "packed scale bytes");
-  uint32_t scw = 0, sca = 0;
-  auto put = [](uint32_t& w, int byte, uint32_t v) __attribute__((always_inline)) {
-    w = (w & ~(0xffu << (8 * byte))) | (v << (8 * byte));
+  // MX: scale bytes of the lane's rows, packed (the MFMA selects a byte):
+  // weight block i in byte i of scw[P], activation block j in byte j of
+  // sca[P], for the steps of parity P.  The bytes of the next step are read
+  // into scn during a step and packed after its last MFMA: no VALU write to
+  // a scale register then falls between the MFMAs that read it, and the LDS
+  // byte reads are waited for where the step's fragment reads are anyway.
+  static_assert(!C::MX || (C::FW <= 4 && C::FA <= 4), "packed scale bytes");
+  uint32_t scw[2] = {0u, 0u}, sca[2] = {0u, 0u};
+  uint32_t scn[C::MX ? C::FA + C::FW : 1];
+  auto pack_scales = [&](uint32_t& a, uint32_t& w) __attribute__((always_inline)) {
+    a = 0u, w = 0u;
+#pragma unroll
+    for (int j = 0; j < C::FA; ++j) a |= scn[j] << (8 * j);
+#pragma unroll
+    for (int i = 0; i < C::FW; ++i) w |= scn[C::FA + i] << (8 * i);
   };
   // the scale byte of tile row r (A rows first, then weight tile rows) for
   // step s: group kt / 8 of its phase, block 2 kt + h of the row (this lane's
@@ -1561,16 +1569,16 @@ __device__ __forceinline__ void f8_tile(const uint8_t* __restrict__ A,
       constexpr int q = decltype(q_c)::value;
       constexpr int i = q / C::FA, j = q % C::FA;
       if constexpr (C::MX)
-        acc[PH][i][j] = mfma32_f8_scaled<i, 2 * P + j>(wf[i], af[P][j], acc[PH][i][j], scw, sca);
+        acc[PH][i][j] = mfma32_f8_scaled<i, j>(wf[i], af[P][j], acc[PH][i][j], scw[P], sca[P]);
       else
         acc[PH][i][j] = mfma32_f8(wf[i], af[P][j], acc[PH][i][j]);
       if constexpr (q < C::FA) {
         readA(Next{}, q, af[P ^ 1][q]);
-        if constexpr (C::MX) put(sca, 2 * (P ^ 1) + q, scale_of(it + 1, a_row + 32 * q));
+        if constexpr (C::MX) scn[q] = scale_of(it + 1, a_row + 32 * q);
       }
       if constexpr (j == C::FA - 1) {
         readW(Next{}, i, wf[i]);
-        if constexpr (C::MX) put(scw, i, scale_of(it + 1, BM + w_row + 32 * i));
+        if constexpr (C::MX) scn[C::FA + i] = scale_of(it + 1, BM + w_row + 32 * i);
       }
       if constexpr (q >= DBEGIN) {
 #pragma unroll
@@ -1583,6 +1591,7 @@ __device__ __forceinline__ void f8_tile(const uint8_t* __restrict__ A,
     [&]<int... Q>(std::integer_sequence<int, Q...>) __attribute__((always_inline)) {
       (slot(std::integral_constant<int, Q>{}), ...);
     }(std::make_integer_sequence<int, NMF>{});
+    if constexpr (C::MX) pack_scales(sca[P ^ 1], scw[P ^ 1]);
   };
   // steps [b, e) with b on a ring boundary: whole rounds, then the rest
   auto run = [&](int b, int e, auto phase_c) __attribute__((always_inline)) {
@@ -1610,13 +1619,14 @@ __device__ __forceinline__ void f8_tile(const uint8_t* __restrict__ A,
 #pragma unroll
   for (int j = 0; j < C::FA; ++j) {
     readA(std::integral_constant<int, 0>{}, j, af[0][j]);
-    if constexpr (C::MX) put(sca, j, scale_of(0, a_row + 32 * j));
+    if constexpr (C::MX) scn[j] = scale_of(0, a_row + 32 * j);
   }
 #pragma unroll
   for (int i = 0; i < C::FW; ++i) {
     readW(std::integral_constant<int, 0>{}, i, wf[i]);
-    if constexpr (C::MX) put(scw, i, scale_of(0, BM + w_row + 32 * i));
+    if constexpr (C::MX) scn[C::FA + i] = scale_of(0, BM + w_row + 32 * i);
   }
+  if constexpr (C::MX) pack_scales(sca[0], scw[0]);
 
   if constexpr (kSync) {
     run(0, nk0, std::integral_constant<int, 0>{});

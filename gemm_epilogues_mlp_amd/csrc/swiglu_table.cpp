@@ -38,7 +38,7 @@ const ShapeEntry kTable[] = {
     {VAR_MX, 128, 4864, 896, 57},
     {VAR_PACKED, 128, 4864, 896, 62},
     {VAR_F8_PACKED, 128, 4864, 896, 75},
-    {VAR_MX_PACKED, 128, 4864, 896, 77},
+    {VAR_MX_PACKED, 128, 4864, 896, 78},
     {VAR_MX_SYNC, 128, 4864, 896, 84},
     // Qwen2.5-1.5B MLP, M = 2048: the 256-row eight-wave tiles, the short last
     // round as quarter tiles (the persistent tile loop, configs 36 and 37, is
