@@ -1305,9 +1305,11 @@ void packed_splitk_kernel(const uint16_t* __restrict__ A, const uint16_t* __rest
 // block its fragment half belongs to), so the accumulators come out fully
 // scaled.  A 16-byte chunk of a scale row covers 8 K steps; the tile's chunks
 // (BM + BNW rows) are loaded by the same DMA into a two-slot ring in LDS, with
-// the K step that starts a group of 8; in the other steps the same
-// instruction loads nothing (a junk slot), so every step issues the same
-// number of loads.  Each lane reads its scale bytes for the next step with the
+// the K step that starts a group of 8 and by that step only: the K loop is
+// unrolled by groups of 8 in this mode, so the number of loads a step has in
+// flight is still a compile-time constant at every position.  (An extra,
+// empty load in each of the other 7 steps cost about a tenth of the MX
+// tile's time.)  Each lane reads its scale bytes for the next step with the
 // fragments.
 template <int MODE, int BM, int BNW, int STAGES, int WGM, int WGN>
 struct F8Tiled {
@@ -1335,9 +1337,33 @@ struct F8Tiled {
   static constexpr int SC_CHUNKS = MX ? BM + BNW : 0;  // one 16-byte scale chunk per row
   static constexpr int SC_LOADS = MX ? (SC_CHUNKS + kThreads - 1) / kThreads : 0;
   static_assert(!MX || (BM % 64 == 0 && BNW % 64 == 0), "a wave's scale chunks share one tensor");
-  static constexpr int TLOADS = LOADS + SC_LOADS;  // DMA instructions per thread and K step
+  static constexpr int TLOADS = LOADS + SC_LOADS;  // most DMA instructions per thread and K step
   static_assert(STAGES >= 2 && STAGES % 2 == 0, "an even stage ring");
   static_assert((STAGES - 1) * TLOADS <= 63, "vmcnt range");
+  // K steps unrolled together: one stage ring, or in MX mode one group of 8
+  // steps (the steps one 16-byte scale chunk covers), so that a step's
+  // position in its group is a compile-time constant
+  static constexpr int UNR = MX ? 8 : STAGES;
+  static_assert(UNR % STAGES == 0, "whole stage rings per unrolled block");
+  // DMA instructions per thread of the step at position t of the block: the
+  // scale chunks travel with the first step of their group only
+  __host__ __device__ static constexpr int step_loads(int t) {
+    return LOADS + ((MX && t % UNR == 0) ? SC_LOADS : 0);
+  }
+  // loads a thread may still have in flight at the top of the step at
+  // position t, when the step after it must have landed: those of steps
+  // t + 2 ... t + STAGES - 1 (the DMA runs STAGES - 1 steps ahead)
+  __host__ __device__ static constexpr int in_flight(int t) {
+    int n = 0;
+    for (int d = 2; d < STAGES; ++d) n += step_loads(t + d);
+    return n;
+  }
+  // the same after the prologue, when step 0 must have landed
+  __host__ __device__ static constexpr int prologue_in_flight() {
+    int n = 0;
+    for (int d = 1; d < STAGES; ++d) n += step_loads(d);
+    return n;
+  }
   static constexpr int YLD = BNY + 8;
   static constexpr int Y_BYTES = BM * YLD * 2;
   // LDS: [scale ring (MX only) | STAGES stages | 1 KB junk slot for zero DMA]
@@ -1378,9 +1404,11 @@ __device__ __forceinline__ void f8_tile(const uint8_t* __restrict__ A,
   const int y0 = tn * C::BNY;
   // K steps: the sync mode runs them twice (Gate, then Up), its Gate phase
   // padded with zero steps to a ring boundary (nk0) so that the Up phase
-  // starts on stage 0 with the same fragment-buffer parity
+  // starts on stage 0 with the same fragment-buffer parity -- in MX mode to a
+  // scale-group boundary, so that its steps keep their positions in the
+  // unrolled blocks
   const int nk = (K + C::BK - 1) / C::BK;
-  const int nk0 = kSync ? (nk + STAGES - 1) / STAGES * STAGES : nk;
+  const int nk0 = kSync ? (nk + C::UNR - 1) / C::UNR * C::UNR : nk;
   const int total = kSync ? nk0 + nk : nk;
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
 
@@ -1531,15 +1559,21 @@ __device__ __forceinline__ void f8_tile(const uint8_t* __restrict__ A,
 #pragma unroll
     for (int i = 0; i < C::FW; ++i) w |= scn[C::FA + i] << (8 * i);
   };
-  // the scale byte of tile row r (A rows first, then weight tile rows) for
-  // step s: group kt / 8 of its phase, block 2 kt + h of the row (this lane's
-  // fragment half), kt the step within the phase
-  auto scale_of = [&](int s, int r) __attribute__((always_inline)) -> uint32_t {
+  // Step s (kt the step within its phase) takes block 2 kt + h of each row's
+  // scales (h: this lane's fragment half): byte 2 (kt % 8) + h of the row's
+  // chunk of group kt / 8.  In MX mode kt % 8 is the step's position in the
+  // unrolled block, a compile-time constant, so a scale read is a per-lane
+  // row base, a wave-uniform ring slot and an immediate.
+  const int sca_base = a_row * 16 + h;         // + 512 q for activation fragment q
+  const int scw_base = (BM + w_row) * 16 + h;  // + 512 i for weight fragment i
+  auto scale_slot = [&](int s) __attribute__((always_inline)) -> int {
     const bool up = kSync && s >= nk0;
     const int kt = up ? s - nk0 : s;
     const int g = up ? ngroups + (kt >> 3) : (kt >> 3);
-    const uint8_t* slot = smem + C::SC_OFF + (g & 1) * C::SC_SLOT;
-    return slot[r * 16 + ((2 * kt + h) & 15)];
+    return C::SC_OFF + (g & 1) * C::SC_SLOT;
+  };
+  auto scale_at = [&](int slot, int base, int imm) __attribute__((always_inline)) -> uint32_t {
+    return smem[slot + base + imm];
   };
   f32x16 acc[C::NACC][C::FW][C::FA];
 #pragma unroll
@@ -1556,13 +1590,17 @@ __device__ __forceinline__ void f8_tile(const uint8_t* __restrict__ A,
   constexpr int NMF = C::FW * C::FA;
   constexpr int DBEGIN = NMF / 2;
   constexpr int DSLOTS = NMF - DBEGIN;
-  auto kstep = [&](int it, auto st_c, auto phase_c) __attribute__((always_inline)) {
+  auto kstep = [&](int it, auto st_c, auto phase_c, auto pos_c) __attribute__((always_inline)) {
     constexpr int ST = decltype(st_c)::value;
     constexpr int PH = decltype(phase_c)::value;
+    constexpr int T = decltype(pos_c)::value;  // position in the unrolled block
     constexpr int P = ST & 1;
+    constexpr int TL = C::step_loads(T + STAGES);  // DMA instructions of step it + STAGES
+    constexpr int NB = 2 * ((T + 1) % 8);            // the next step's byte in its group's chunk
     using Next = std::integral_constant<int, (ST + 1) % STAGES>;
-    wait_vmcnt<(STAGES - 2) * C::TLOADS>();
+    wait_vmcnt<C::in_flight(T)>();
     __syncthreads();
+    const int nslot = C::MX ? scale_slot(it + 1) : 0;
     // MFMA slot q (compile time): MFMA (i, j), then its share of the reads of
     // step it+1 and of the DMA of step it+STAGES
     auto slot = [&](auto q_c) __attribute__((always_inline)) {
@@ -1574,16 +1612,15 @@ __device__ __forceinline__ void f8_tile(const uint8_t* __restrict__ A,
         acc[PH][i][j] = mfma32_f8(wf[i], af[P][j], acc[PH][i][j]);
       if constexpr (q < C::FA) {
         readA(Next{}, q, af[P ^ 1][q]);
-        if constexpr (C::MX) scn[q] = scale_of(it + 1, a_row + 32 * q);
+        if constexpr (C::MX) scn[q] = scale_at(nslot, sca_base, 512 * q + NB);
       }
       if constexpr (j == C::FA - 1) {
         readW(Next{}, i, wf[i]);
-        if constexpr (C::MX) scn[C::FA + i] = scale_of(it + 1, BM + w_row + 32 * i);
+        if constexpr (C::MX) scn[C::FA + i] = scale_at(nslot, scw_base, 512 * i + NB);
       }
       if constexpr (q >= DBEGIN) {
 #pragma unroll
-        for (int x = (q - DBEGIN) * C::TLOADS / DSLOTS; x < (q - DBEGIN + 1) * C::TLOADS / DSLOTS;
-             ++x)
+        for (int x = (q - DBEGIN) * TL / DSLOTS; x < (q - DBEGIN + 1) * TL / DSLOTS; ++x)
           dma(it + STAGES, st_c, x);
       }
       __builtin_amdgcn_sched_barrier(0);
@@ -1593,16 +1630,23 @@ __device__ __forceinline__ void f8_tile(const uint8_t* __restrict__ A,
     }(std::make_integer_sequence<int, NMF>{});
     if constexpr (C::MX) pack_scales(sca[P ^ 1], scw[P ^ 1]);
   };
-  // steps [b, e) with b on a ring boundary: whole rounds, then the rest
+  // steps [b, e) with b on a block boundary: whole unrolled blocks (stage
+  // rings, or MX scale groups), then the rest
   auto run = [&](int b, int e, auto phase_c) __attribute__((always_inline)) {
     int it = b;
-    for (; it + STAGES <= e; it += STAGES)
+    for (; it + C::UNR <= e; it += C::UNR)
       [&]<int... S>(std::integer_sequence<int, S...>) __attribute__((always_inline)) {
-        (kstep(it + S, std::integral_constant<int, S>{}, phase_c), ...);
-      }(std::make_integer_sequence<int, STAGES>{});
+        (kstep(it + S, std::integral_constant<int, S % STAGES>{}, phase_c,
+               std::integral_constant<int, S>{}),
+         ...);
+      }(std::make_integer_sequence<int, C::UNR>{});
     [&]<int... S>(std::integer_sequence<int, S...>) __attribute__((always_inline)) {
-      ((it + S < e ? (kstep(it + S, std::integral_constant<int, S>{}, phase_c), 0) : 0), ...);
-    }(std::make_integer_sequence<int, STAGES - 1>{});
+      ((it + S < e ? (kstep(it + S, std::integral_constant<int, S % STAGES>{}, phase_c,
+                            std::integral_constant<int, S>{}),
+                      0)
+                   : 0),
+       ...);
+    }(std::make_integer_sequence<int, C::UNR - 1>{});
   };
 
   // ---- prologue: steps 0 .. STAGES-1 in flight, fragments of step 0 --------------
@@ -1610,21 +1654,21 @@ __device__ __forceinline__ void f8_tile(const uint8_t* __restrict__ A,
     ((
          [&] {
 #pragma unroll
-           for (int q = 0; q < C::TLOADS; ++q) dma(S, std::integral_constant<int, S>{}, q);
+           for (int q = 0; q < C::step_loads(S); ++q) dma(S, std::integral_constant<int, S>{}, q);
          }()),
      ...);
   }(std::make_integer_sequence<int, STAGES>{});
-  wait_vmcnt<(STAGES - 1) * C::TLOADS>();
+  wait_vmcnt<C::prologue_in_flight()>();
   __syncthreads();
 #pragma unroll
   for (int j = 0; j < C::FA; ++j) {
     readA(std::integral_constant<int, 0>{}, j, af[0][j]);
-    if constexpr (C::MX) scn[j] = scale_of(0, a_row + 32 * j);
+    if constexpr (C::MX) scn[j] = scale_at(scale_slot(0), sca_base, 512 * j);
   }
 #pragma unroll
   for (int i = 0; i < C::FW; ++i) {
     readW(std::integral_constant<int, 0>{}, i, wf[i]);
-    if constexpr (C::MX) scn[C::FA + i] = scale_of(0, BM + w_row + 32 * i);
+    if constexpr (C::MX) scn[C::FA + i] = scale_at(scale_slot(0), scw_base, 512 * i);
   }
   if constexpr (C::MX) pack_scales(sca[0], scw[0]);
 

@@ -6,7 +6,7 @@ emulation needs: each `__shared__` array becomes a pointer from emu_lds(),
 the raw `s_barrier` becomes emu_barrier(), the empty asm statement that pins
 a value in a register is dropped, the AMDGPU-only occupancy attribute is
 dropped, and the single hipLaunchKernel call runs the kernel's workgroups on
-the host (emu_launch).  Three planted mistakes, off unless the driver is run
+the host (emu_launch).  Five planted mistakes, off unless the driver is run
 with --plant N, show that the LDS ordering check catches what it exists for."""
 import os
 import re
@@ -50,6 +50,9 @@ def rewrite(src: str) -> str:
 #  1: the LDS-tiled K loop waits for one K step fewer of its DMA
 #  2: the epilogues reuse the stage ring without the barrier that ends the K loop
 #  3: the persistent kernel ends without draining the loads issued past its last tile
+#  4: the FP8 tile in MX mode lets the step before a scale group starts leave
+#     that group's scale chunks in flight
+#  5: the FP8 tile's K loop waits for one K step fewer of its DMA
 PLANTS = [
     (r"^        wait_vmcnt<\(STAGES - 2\) \* C::LOADS>\(\);$",
      "        if (::g_emu_plant == 1) wait_vmcnt<(STAGES - 1) * C::LOADS>();"
@@ -58,6 +61,10 @@ PLANTS = [
      "  wait_vmcnt<0>();\n  if (::g_emu_plant != 2) __syncthreads();\n", 2),
     (r"^(  // the zero loads issued past the last tile still write LDS\n)  wait_vmcnt<0>\(\);$",
      "\\1  if (::g_emu_plant != 3) wait_vmcnt<0>();", 1),
+    (r"^    wait_vmcnt<C::in_flight\(T\)>\(\);$",
+     "    if (::g_emu_plant == 4 && C::MX && T == 7) wait_vmcnt<C::in_flight(T) + 1>();"
+     " else if (::g_emu_plant == 5) wait_vmcnt<C::in_flight(T) + C::LOADS>();"
+     " else wait_vmcnt<C::in_flight(T)>();", 1),
 ]
 
 

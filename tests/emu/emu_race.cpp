@@ -224,4 +224,6 @@ void __sanitizer_cov_store16(__int128* p) { log_access(p, 16, EV_WRITE); }
 }
 
 void emu_copy(void* d, const void* s, size_t n) { memcpy(d, s, n); }
+// sink for the operands of the emulated matrix products (keeps their loads)
+void emu_use(const void*, size_t) {}
 void emu_zero(void* d, size_t n) { memset(d, 0, n); }

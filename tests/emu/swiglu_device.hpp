@@ -37,6 +37,7 @@ extern int g_emu_plant;  // a planted mistake to switch on (build.py), 0: none
 // byte copies outside the instrumented translation unit (so that the data
 // movement of a DMA or of a checked load is not logged as a plain access)
 void emu_copy(void* d, const void* s, size_t n);
+void emu_use(const void* p, size_t n);
 void emu_zero(void* d, size_t n);
 
 #define __global__
@@ -207,14 +208,31 @@ inline void transpose8x8(const u32x4 row[8], u32x4 col[8]) {
       col[2 * j + 1][p] = emu_perm(hi, lo, 0x07060302u);
     }
 }
-inline f32x16 mfma32(const u32x4&, const u32x4&, const f32x16& c) { return c; }
-inline f32x4 mfma16(const u32x4&, const u32x4&, const f32x4& c) { return c; }
-inline f32x16 mfma32_f8(const u32x4 (&)[2], const u32x4 (&)[2], const f32x16& c) { return c; }
-inline f32x4 mfma16_f8(const u32x4 (&)[2], const u32x4 (&)[2], const f32x4& c) { return c; }
+// The matrix products are not computed (values are the GPU tests' job), but
+// their operands are handed to emu_use, a function of another translation
+// unit: otherwise the compiler drops every LDS read whose only use is an MFMA
+// operand, and the LDS ordering check never sees those reads.
+inline f32x16 mfma32(const u32x4& a, const u32x4& b, const f32x16& c) {
+  emu_use(&a, 16), emu_use(&b, 16);
+  return c;
+}
+inline f32x4 mfma16(const u32x4& a, const u32x4& b, const f32x4& c) {
+  emu_use(&a, 16), emu_use(&b, 16);
+  return c;
+}
+inline f32x16 mfma32_f8(const u32x4 (&a)[2], const u32x4 (&b)[2], const f32x16& c) {
+  emu_use(a, 32), emu_use(b, 32);
+  return c;
+}
+inline f32x4 mfma16_f8(const u32x4 (&a)[2], const u32x4 (&b)[2], const f32x4& c) {
+  emu_use(a, 32), emu_use(b, 32);
+  return c;
+}
 template <int SEL0, int SEL1>
-inline f32x16 mfma32_f8_scaled(const u32x4 (&)[2], const u32x4 (&)[2], const f32x16& c, uint32_t,
-                               uint32_t) {
+inline f32x16 mfma32_f8_scaled(const u32x4 (&a)[2], const u32x4 (&b)[2], const f32x16& c,
+                               uint32_t sa, uint32_t sb) {
   static_assert(SEL0 >= 0 && SEL0 < 4 && SEL1 >= 0 && SEL1 < 4, "byte select");
+  emu_use(a, 32), emu_use(b, 32), emu_use(&sa, 4), emu_use(&sb, 4);
   return c;
 }
 inline uint32_t e4m3_code(float v) {

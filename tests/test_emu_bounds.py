@@ -44,21 +44,26 @@ def test_all_configs_on_the_parity_shapes(emu):
 
 # The LDS ordering check (tests/emu/emu_race.cpp) against mistakes planted in
 # the emulation's copy of the kernels (tests/emu/build.py): a K-loop wait one
-# step short, an epilogue that reuses the stage ring without the barrier that
-# ends the K loop, a persistent kernel that does not drain its last loads.
+# step short (bf16 and FP8 tiles), an epilogue that reuses the stage ring
+# without the barrier that ends the K loop, a persistent kernel that does not
+# drain its last loads, an MX K loop that reads a scale group's bytes while
+# their DMA may still be in flight.
 PLANTED = [
-    (1, 40, "LDS read while a DMA into it may land"),
-    (1, 42, "LDS read while a DMA into it may land"),
-    (2, 40, "LDS accesses of two waves between the same barriers"),
-    (2, 43, "LDS write while a DMA into it may land"),
-    (3, 36, "DMA still in flight when its thread ends"),
+    (1, 40, 128, "LDS read while a DMA into it may land"),
+    (1, 42, 128, "LDS read while a DMA into it may land"),
+    (2, 40, 128, "LDS accesses of two waves between the same barriers"),
+    (2, 43, 128, "LDS write while a DMA into it may land"),
+    (3, 36, 128, "DMA still in flight when its thread ends"),
+    (4, 56, 1088, "LDS read while a DMA into it may land"),
+    (4, 82, 1088, "LDS read while a DMA into it may land"),
+    (5, 43, 1088, "LDS read while a DMA into it may land"),
 ]
 
 
-@pytest.mark.parametrize("plant,cfg,message", PLANTED)
-def test_lds_ordering_check_catches_planted_mistakes(emu, plant, cfg, message):
+@pytest.mark.parametrize("plant,cfg,K,message", PLANTED)
+def test_lds_ordering_check_catches_planted_mistakes(emu, plant, cfg, K, message):
     # the same launch without the plant is one of the workload cases below
-    rc, out = _run(emu, "--plant", plant, "--race-blocks", 8, "--shape", 2048, 8960, 128, cfg)
+    rc, out = _run(emu, "--plant", plant, "--race-blocks", 8, "--shape", 2048, 8960, K, cfg)
     assert rc != 0 and message in out, out[-4000:]
 
 
@@ -108,6 +113,7 @@ CASES = [
     # both orders and with block scales, the small-M tiles and the streaming
     # kernel at the 0.5B and decode shapes
     (2048, 8960, 576, [43, 53, 56]),
+    (2048, 8960, 1088, [43, 56, 82]),  # 17 steps: MX scale groups of 8 and a short last one
     (2008, 4216, 128, [43, 53, 56]),   # whole rounds plus a short split round
     (128, 4864, 896, [46, 55, 57]),
     (16, 18944, 3584, [52, 57]),
