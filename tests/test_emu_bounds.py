@@ -58,12 +58,15 @@ PLANTED = [
     (4, 82, 1088, "LDS read while a DMA into it may land"),
     (5, 43, 1088, "LDS read while a DMA into it may land"),
 ]
+# the plants of the FP8 tile's K loop run on a smaller launch with 17 K steps
+# (two scale groups of 8 and a short last one)
+PLANT_SHAPE = {128: (2048, 8960, 128), 1088: (2008, 4216, 1088)}
 
 
 @pytest.mark.parametrize("plant,cfg,K,message", PLANTED)
 def test_lds_ordering_check_catches_planted_mistakes(emu, plant, cfg, K, message):
     # the same launch without the plant is one of the workload cases below
-    rc, out = _run(emu, "--plant", plant, "--race-blocks", 8, "--shape", 2048, 8960, K, cfg)
+    rc, out = _run(emu, "--plant", plant, "--race-blocks", 8, "--shape", *PLANT_SHAPE[K], cfg)
     assert rc != 0 and message in out, out[-4000:]
 
 
@@ -74,7 +77,7 @@ CASES = [
     (2008, 4216, 72, [40, 42]),        # 264 tiles: 256 big + 8 split
     (2008, 8440, 72, [41]),            # the same for the 256-column GEMM tiles
     (2048, 8960, 40, [40, 41, 42]),    # 1.5B M and N: 512 big + 48 split
-    (2008, 4216, 1088, [82]),          # MXFP8 sync split tiles: 17 steps, 3 scale groups a phase
+    (2008, 4216, 1088, [43, 56, 82]),  # FP8, MX and MX sync split tiles: 17 steps, 3 scale groups a phase
     # the persistent tiles: whole rings of K (K = 128, 256), two or more tiles
     # per workgroup, with and without a quarter-tile last round, ragged M and N
     (2048, 8960, 128, [36, 40, 42, 43]),  # 560 tiles: 2 per workgroup + 48 as quarters
@@ -113,7 +116,6 @@ CASES = [
     # both orders and with block scales, the small-M tiles and the streaming
     # kernel at the 0.5B and decode shapes
     (2048, 8960, 576, [43, 53, 56]),
-    (2048, 8960, 1088, [43, 56, 82]),  # 17 steps: MX scale groups of 8 and a short last one
     (2008, 4216, 128, [43, 53, 56]),   # whole rounds plus a short split round
     (128, 4864, 896, [46, 55, 57]),
     (16, 18944, 3584, [52, 57]),
