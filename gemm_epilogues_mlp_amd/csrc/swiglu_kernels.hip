@@ -1601,6 +1601,10 @@ __device__ __forceinline__ void f8_tile(const uint8_t* __restrict__ A,
     wait_vmcnt<C::in_flight(T)>();
     __syncthreads();
     const int nslot = C::MX ? scale_slot(it + 1) : 0;
+    // the sync order's Gate padding steps (zero tiles) take scale 1 (byte
+    // 127) whatever a scale row holds past K / 32: a NaN code there (255)
+    // would turn their zero products into NaN
+    const bool npad = kSync && it + 1 >= nk && it + 1 < nk0;
     // MFMA slot q (compile time): MFMA (i, j), then its share of the reads of
     // step it+1 and of the DMA of step it+STAGES
     auto slot = [&](auto q_c) __attribute__((always_inline)) {
@@ -1628,7 +1632,10 @@ __device__ __forceinline__ void f8_tile(const uint8_t* __restrict__ A,
     [&]<int... Q>(std::integer_sequence<int, Q...>) __attribute__((always_inline)) {
       (slot(std::integral_constant<int, Q>{}), ...);
     }(std::make_integer_sequence<int, NMF>{});
-    if constexpr (C::MX) pack_scales(sca[P ^ 1], scw[P ^ 1]);
+    if constexpr (C::MX) {
+      pack_scales(sca[P ^ 1], scw[P ^ 1]);
+      if (npad) sca[P ^ 1] = scw[P ^ 1] = 0x7f7f7f7fu;
+    }
   };
   // steps [b, e) with b on a block boundary: whole unrolled blocks (stage
   // rings, or MX scale groups), then the rest

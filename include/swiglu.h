@@ -394,7 +394,8 @@ swiglu_status_t swiglu_pack_fp8_fragments(swiglu_handle_t h, const void* W8, voi
  *   W8 [2N, K] + SW [2N, ks]     the k-major paired weights (row 2n Gate
  *                                column n, row 2n+1 Up column n) and scales
  * Scale rows have a stride of ks bytes, ks a multiple of 16 and >= K/32;
- * bytes past K/32 are not read by the forward.  The forward needs K % 64 == 0,
+ * bytes past K/32 (the row padding) may be loaded with their 16-byte chunk
+ * but never affect the result, whatever they hold.  The forward needs K % 64 == 0,
  * N % 8 == 0, 16-byte aligned pointers and every tensor under 2 GiB (else
  * UNSUPPORTED). */
 

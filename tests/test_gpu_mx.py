@@ -163,6 +163,21 @@ def test_mx_config_parity(handle, cases, cfg, shape):
     assert_parity(y, c["y"], f"mx cfg {cfg} {shape}")
 
 
+@pytest.mark.parametrize("cfg", mx_configs())
+def test_mx_scale_row_padding_is_not_used(handle, cases, cfg):
+    """Scale bytes past K/32 (the row padding up to ks) hold the NaN code 255
+    here; the result must not change (the sync order's Gate phase runs zero
+    padding steps, whose scales must not come from those bytes)."""
+    M, N, K = 130, 264, 1088  # 17 steps: 34 scale bytes a row, ks = 48
+    qa, sa, qw, sw_ = cases[(M, N, K)]["q"]
+    sa2, sw2 = sa.copy(), sw_.copy()
+    assert sa2.shape[1] > K // 32
+    sa2[:, K // 32:] = 255
+    sw2[:, K // 32:] = 255
+    y = forward(handle, qa, sa2, qw, sw2, M, N, K, cfg)
+    assert_parity(y, cases[(M, N, K)]["y"], f"mx cfg {cfg}, NaN codes in the scale-row padding")
+
+
 @pytest.mark.parametrize("cfg", [i for i in mx_configs() if sw.swiglu_config_info(i)["tail_split"]])
 def test_mx_split_tail_parity(handle, cfg):
     info = sw.swiglu_config_info(cfg)
