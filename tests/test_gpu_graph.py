@@ -93,3 +93,42 @@ def test_graph_replay_fp8_fragment_order(handle):
         torch.cuda.synchronize()
         assert torch.equal(y, y_eager), f"replay {r} differs from the eager forward"
     del g
+
+
+def test_graph_replay_splitk(handle):
+    """The decode forward with K split over workgroups, captured: its counters
+    return to zero in every launch, so every replay runs the handoff afresh on
+    the same workspace and equals the eager result bit for bit."""
+    import torch
+    M, N, K = 9, 1184, 3584
+    a, w1, w2 = I.make_inputs(M, K, N, 23)
+    a_d, w1_d, w2_d = dev(a), dev(w1), dev(w2)
+    P = torch.empty((sw.swiglu_packed_bytes(N, K) // 2,), dtype=torch.int16, device="cuda")
+    sw.swiglu_pack_fragments(handle, w1_d, w2_d, P, K, N)
+    S = 3
+    ws = torch.zeros((sw.swiglu_packed_splitk_workspace_bytes(N, K, S),), dtype=torch.uint8,
+                     device="cuda")
+    y_eager = torch.full((M, N), -1, dtype=torch.int16, device="cuda")
+    sw.swiglu_forward_packed_splitk(handle, a_d, P, y_eager, M, N, K, ws, ksplit=S)
+    torch.cuda.synchronize()
+    assert_parity(host(y_eager), oracle.swiglu(a, w1, w2), "split-K eager")
+    log(f"graph split-K {(M, N, K)} S={S}")
+    y = torch.full((M, N), -1, dtype=torch.int16, device="cuda")
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):  # warm the capture stream once, eagerly
+        sw.swiglu_forward_packed_splitk(handle, a_d, P, y, M, N, K, ws, ksplit=S)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        sw.swiglu_forward_packed_splitk(handle, a_d, P, y, M, N, K, ws, ksplit=S)
+    slabs = (2 * N + 127) // 128
+    for r in range(4):
+        y.fill_(-1)                      # eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(y, y_eager), f"replay {r} differs from the eager forward"
+        assert int(ws[:slabs * 16].count_nonzero().item()) == 0, f"counters after replay {r}"
+    del g
