@@ -39,6 +39,8 @@
 //
 //  * packed_kernel  the same streaming on W_fused stored once in MFMA
 //    fragment order: 1 KB contiguous per load, no transposition.
+//    packed_mixed_kernel runs whole slabs and quarter slabs in one launch, so
+//    that slab counts a little above a whole number per CU stay balanced;
 //    packed_splitk_kernel also splits K over workgroups (decode shapes with
 //    few slabs): fp32 partials handed to the last workgroup of each slab part,
 //    which reduces them in K order before SiLU.
@@ -1037,18 +1039,17 @@ __device__ __forceinline__ void packed_load(const uint16_t* __restrict__ A,
   for (int c = 0; c < CH; ++c) b[c] = MT == 1 ? load16_stream(p + c * 512) : load16(p + c * 512);
 }
 
+// Part `part` (CH of the 8 column groups) of slab `slab`, rows m0 ... m0 +
+// 16 MT - 1, by the workgroup's NW waves; red: LDS for the wave reduction
+// (NW MT CH 64 f32x4).
 template <int MT, int NW, int CH>
-__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(MT == 1 ? 4 : 2)))
-void packed_kernel(const uint16_t* __restrict__ A, const uint16_t* __restrict__ P,
-                   uint16_t* __restrict__ Y, int M, int N, int K) {
+__device__ __forceinline__ void packed_unit(const uint16_t* __restrict__ A,
+                                            const uint16_t* __restrict__ P,
+                                            uint16_t* __restrict__ Y, int M, int N, int K,
+                                            int slab, int part, int m0, f32x4* red) {
   using C = Packed<MT, NW, CH>;
-  __shared__ __attribute__((aligned(16))) f32x4 red[NW * MT * CH * 64];
-
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  const int unit = xcd_remap(blockIdx.x, gridDim.x);
-  const int slab = unit / C::PARTS, part = unit % C::PARTS;
-  const int m0 = blockIdx.y * MT * 16;
   const int nsteps = (K + 31) / 32;
   // this lane's 16 bytes in each of the workgroup's 1 KB runs (column groups
   // part*CH ... part*CH + CH-1) of the slab's blocks
@@ -1148,6 +1149,39 @@ void packed_kernel(const uint16_t* __restrict__ A, const uint16_t* __restrict__ 
         *out = bf16_bits(y[0]);
       }
     }
+  }
+}
+
+template <int MT, int NW, int CH>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(MT == 1 ? 4 : 2)))
+void packed_kernel(const uint16_t* __restrict__ A, const uint16_t* __restrict__ P,
+                   uint16_t* __restrict__ Y, int M, int N, int K) {
+  using C = Packed<MT, NW, CH>;
+  __shared__ __attribute__((aligned(16))) f32x4 red[NW * MT * CH * 64];
+  const int unit = xcd_remap(blockIdx.x, gridDim.x);
+  packed_unit<MT, NW, CH>(A, P, Y, M, N, K, unit / C::PARTS, unit % C::PARTS,
+                          (int)blockIdx.y * MT * 16, red);
+}
+
+// ---- the same streaming with whole and quarter slabs in one launch ----------
+// For slab counts a little above a whole number per CU (Qwen2.5-7B decode:
+// 296 slabs on 256 CUs), one size of work unit leaves some CUs a third more
+// to stream than others.  Here the first nwhole = floor(slabs / CUs) * CUs
+// slabs run as whole slabs, one workgroup of NW waves each, and the rest as
+// quarter slabs, so that no CU streams more than one whole and one quarter
+// slab beyond an even share.  One row group of 16 rows per grid row.
+template <int NW>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(4)))
+void packed_mixed_kernel(const uint16_t* __restrict__ A, const uint16_t* __restrict__ P,
+                         uint16_t* __restrict__ Y, int M, int N, int K, int nwhole) {
+  __shared__ __attribute__((aligned(16))) f32x4 red[NW * 8 * 64];
+  const int b = blockIdx.x;
+  const int m0 = (int)blockIdx.y * 16;
+  if (b < nwhole) {
+    packed_unit<1, NW, 8>(A, P, Y, M, N, K, b, 0, m0, red);
+  } else {
+    const int u = b - nwhole;
+    packed_unit<1, NW, 2>(A, P, Y, M, N, K, nwhole + u / 4, u % 4, m0, red);
   }
 }
 
@@ -2535,6 +2569,19 @@ static hipError_t launch_packed(const LaunchArgs& a) {
                      dim3(C::kThreads), 0, a.stream, a.A, a.W1, a.Y, a.M, a.N, a.K);
 }
 
+template <int NW>
+static hipError_t launch_packed_mixed(const LaunchArgs& a) {
+  const long long slabs = packed_slabs(a.N);
+  const long long nmb = (a.M + 15) / 16;
+  if (slabs <= 0 || nmb <= 0) return hipSuccess;
+  const long long cus = a.cu_count > 0 ? a.cu_count : 256;
+  const long long nwhole = slabs / cus * cus;
+  const long long nunit = nwhole + (slabs - nwhole) * 4;
+  if (nunit > 0x7fffffffLL || nmb > 65535) return hipErrorInvalidValue;
+  return launch_kernel((packed_mixed_kernel<NW>), dim3((unsigned)nunit, (unsigned)nmb),
+                       dim3(64 * NW), 0, a.stream, a.A, a.W1, a.Y, a.M, a.N, a.K, (int)nwhole);
+}
+
 template <int NW, int CH>
 static hipError_t launch_packed_splitk(const LaunchArgs& a) {
   using C = Packed<1, NW, CH>;
@@ -2766,6 +2813,9 @@ static const KernelConfig kConfigs[] = {
     PACKED_SPLITK(4, 8),                                            // 85
     PACKED_SPLITK(4, 4),                                            // 86
     PACKED_SPLITK(4, 2),                                            // 87
+    // ---- fragment-ordered W_fused: whole slabs, then quarter slabs --------
+    {VAR_PACKED, 1, 16, Packed<1, 8, 8>::COLS_Y, 32, 8, 8, Packed<1, 8, 8>::LDS_BYTES,
+     &launch_packed_mixed<8>},                                      // 88
 };
 
 int config_count() { return (int)(sizeof(kConfigs) / sizeof(kConfigs[0])); }

@@ -60,7 +60,7 @@ const ShapeEntry kTable[] = {
     {VAR_F8, 16, 18944, 3584, 52},
     {VAR_F8_SYNC, 16, 18944, 3584, 55},
     {VAR_MX, 16, 18944, 3584, 57},
-    {VAR_PACKED, 16, 18944, 3584, 65},
+    {VAR_PACKED, 16, 18944, 3584, 88},
     {VAR_F8_PACKED, 16, 18944, 3584, 70},
     {VAR_MX_PACKED, 16, 18944, 3584, 77},
     {VAR_MX_SYNC, 16, 18944, 3584, 84},
@@ -104,12 +104,15 @@ int select_config(int variant, long long M, long long N, long long K, int cu_cou
   switch (variant) {
     case VAR_PACKED: {
       // each CU streams at a bounded rate, so the slabs of 128 W_fused columns
-      // are spread evenly: whole slabs from 1.75 per CU, half slabs from half
-      // a slab per CU, quarter slabs below (8 waves under 64 slabs); 32- and
-      // 64-row blocks above M = 16
+      // are spread evenly: whole slabs from 1.75 per CU, whole slabs for the
+      // whole rounds and quarter slabs for the rest from one per CU, half
+      // slabs from half a slab per CU, quarter slabs below (8 waves under 64
+      // slabs); 32- and 64-row blocks above M = 16
       const long long slabs = packed_slabs(N);
       if (M <= 16)
-        return 4 * slabs >= 7 * cus ? 58 : (2 * slabs >= cus ? 65 : (slabs >= 64 ? 63 : 64));
+        return 4 * slabs >= 7 * cus
+                   ? 58
+                   : (slabs >= cus ? 88 : (2 * slabs >= cus ? 65 : (slabs >= 64 ? 63 : 64)));
       return M <= 32 ? 69 : 62;
     }
     case VAR_F8_PACKED: {

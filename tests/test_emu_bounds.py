@@ -121,9 +121,10 @@ CASES = [
     (16, 18944, 3584, [52, 57]),
     # fragment-ordered weights: decode, 0.5B and ragged shapes for every
     # packed config (odd and even step counts per wave)
-    (16, 18944, 3584, list(range(58, 70))),
-    (128, 4864, 896, list(range(58, 70))),
-    (33, 72, 40, list(range(58, 70))),
+    (16, 18944, 3584, list(range(58, 70)) + [88]),  # 88: 256 whole and 160 quarter slabs
+    (128, 4864, 896, list(range(58, 70)) + [88]),
+    (33, 72, 40, list(range(58, 70)) + [88]),
+    (13, 16504, 72, [88]),             # 258 slabs, the last partial: 256 whole, then quarters
     # FP8 on fragment-ordered W8: decode, 0.5B, ragged (partial step of 128)
     (16, 18944, 3584, list(range(70, 77))),
     (128, 4864, 896, list(range(70, 77))),
@@ -176,7 +177,7 @@ LIMIT_CASES = [
     (65536, 512, 16256, [36, 37], 4),
     (16, 32768, 16376, [4, 11, 18, 23, 12], 8),
     # fragment-ordered W_fused just under 2 GiB: 511 slabs x 512 steps x 8 KB
-    (16, 32704, 16376, list(range(58, 70)) + [85, 86, 87], 8),
+    (16, 32704, 16376, list(range(58, 70)) + [85, 86, 87, 88], 8),
     # fragment-ordered W8 just under 2 GiB: 4096 row blocks x 255 steps x 2 KB
     (16, 32768, 32640, list(range(70, 77)), 8),
     # MX fragment-ordered W8 just under 2 GiB: 2048 row blocks x 511 steps x 2 KB

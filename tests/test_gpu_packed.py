@@ -27,6 +27,7 @@ SHAPES = [
     (129, 520, 96),
     (33, 72, 40),
     (16, 4864, 896),
+    (13, 16504, 72),   # 258 slabs, the last partial: whole slabs on every CU, then quarters
 ]
 
 
