@@ -62,8 +62,12 @@
 namespace swiglu {
 
 // MODE_MX / MODE_MX_SYNC: the interleave and the sync order on MXFP8 inputs
-// (FP8 tile kernel only)
-enum Mode { MODE_INTERLEAVE = 0, MODE_SYNC = 1, MODE_GEMM = 2, MODE_MX = 3, MODE_MX_SYNC = 4 };
+// (FP8 tile kernel only).  MODE_PAIR: the sync family's output tile on W1 and
+// W2 as stored, with the Gate and Up GEMMs run by two groups of waves over the
+// same A k-tiles (bf16 tile kernel only).
+enum Mode {
+  MODE_INTERLEAVE = 0, MODE_SYNC = 1, MODE_GEMM = 2, MODE_MX = 3, MODE_MX_SYNC = 4, MODE_PAIR = 5
+};
 
 // ============================================================================
 // LDS-tiled MFMA kernel
@@ -93,7 +97,8 @@ struct Tiled {
   static constexpr int kWaves = WGM * WGN;
   static_assert(kWaves == 4 || kWaves == 8, "four waves (one per SIMD) or eight (two per SIMD)");
   static constexpr int kThreads = 64 * kWaves;
-  static constexpr int BNY = (MODE == MODE_INTERLEAVE) ? BNW / 2 : BNW;  // output columns
+  static constexpr int BNY =
+      (MODE == MODE_INTERLEAVE || MODE == MODE_PAIR) ? BNW / 2 : BNW;  // output columns
   static constexpr int WTM = BM / WGM;   // A rows per wave
   static constexpr int WTW = BNW / WGN;  // weight columns per wave
   static constexpr int FA = WTM / 32;    // 32-row blocks of A per wave
@@ -106,6 +111,17 @@ struct Tiled {
   static_assert(ACH == 4 || ACH == 8, "A swizzle covers 4 or 8 chunks");
   static constexpr int WCH = BNW / 8;    // 16-byte chunks per weight row
   static_assert(WCH % 8 == 0 && WCH <= 64, "W swizzle stays inside groups of 8 chunks");
+  // A pair tile stores its weight stage as two parts, [BK][BNY] of W1 and
+  // then [BK][BNY] of W2, so that every DMA instruction of a wave reads one
+  // tensor (the buffer resource is wave-uniform).
+  static constexpr int WPARTS = (MODE == MODE_PAIR) ? 2 : 1;
+  static constexpr int WCHP = WCH / WPARTS;       // chunks per weight row of a part
+  static constexpr int PART_COLS = BNW / WPARTS;  // weight columns per part
+  static constexpr int PART_BYTES = BK * PART_COLS * 2;
+  static_assert(WCHP % 8 == 0, "W swizzle works on aligned groups of 8 chunks of a part");
+  static_assert((BK * WCHP) % 64 == 0, "a wave's 64 weight chunks lie in one part");
+  static_assert(MODE != MODE_PAIR || (PART_COLS % WTW == 0 && WGN % 2 == 0),
+                "pair tile: each wave's weight columns lie in one part, half the waves each");
   static constexpr int A_BYTES = BM * BK * 2;
   static constexpr int W_BYTES = BK * BNW * 2;
   static constexpr int STAGE_BYTES = A_BYTES + W_BYTES;
@@ -119,7 +135,9 @@ struct Tiled {
   static constexpr int LOADS = A_LOADS + W_LOADS;
   static_assert(STAGES >= 2 && LOADS * (STAGES - 2) + LOADS / 2 <= 63, "vmcnt range");
   static constexpr int YLD = BNY + 8;    // padded row of the output staging tile
-  static constexpr int Y_BYTES = BM * YLD * 2;
+  // pair tile: the Gate waves hand SiLU(Gate) to the Up waves as fp32 [BM][SLD]
+  static constexpr int SLD = BNY + 4;
+  static constexpr int Y_BYTES = (MODE == MODE_PAIR) ? BM * SLD * 4 : BM * YLD * 2;
   // 1 KB slot for zero DMA, allocated only when some wave can lack a chunk
   static constexpr bool NEED_JUNK = A_CHUNKS % kThreads != 0 || W_CHUNKS % kThreads != 0;
   static constexpr int JUNK = STAGES * STAGE_BYTES;
@@ -143,7 +161,7 @@ struct Tiled {
   // of 256 B by themselves, so g = k % 4 suffices there; rows a multiple of
   // 256 B all start at the same bank and take g = 0, 3, 5, 6 for k % 4 = 0..3.
   __host__ __device__ static constexpr int w_swz(int row) {
-    if ((WCH / 8) % 2 == 1) return (row & 3) << 1;  // rows an odd multiple of 128 B
+    if ((WCHP / 8) % 2 == 1) return (row & 3) << 1;  // rows an odd multiple of 128 B
     return ((0x6530 >> (4 * (row & 3))) & 0xf) << 1;
   }
   // every swizzle must permute the chunks of its own row (checked at compile
@@ -153,12 +171,12 @@ struct Tiled {
     for (int r = 0; r < 16; ++r) {
       unsigned long long a_seen = 0, w_seen = 0;
       for (int c = 0; c < ACH; ++c) a_seen |= 1ull << (c ^ a_swz(r));
-      for (int c = 0; c < WCH; ++c) {
+      for (int c = 0; c < WCHP; ++c) {
         const int x = c ^ w_swz(r);
-        if (x < 0 || x >= WCH) return false;
+        if (x < 0 || x >= WCHP) return false;
         w_seen |= 1ull << x;
       }
-      if (a_seen != (1ull << ACH) - 1 || w_seen != (WCH >= 64 ? ~0ull : (1ull << WCH) - 1))
+      if (a_seen != (1ull << ACH) - 1 || w_seen != (WCHP >= 64 ? ~0ull : (1ull << WCHP) - 1))
         return false;
     }
     return true;
@@ -194,8 +212,9 @@ __device__ __forceinline__ void tiled_tile(const uint16_t* __restrict__ A,
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int wm = wave / WGN, wn = wave % WGN;
-  const int wc0 = tn * BNW;  // first weight column (W_fused, W1/W2 or W)
   const int y0 = tn * C::BNY;
+  // first weight column (of W_fused, of W1 and W2, or of W)
+  const int wc0 = (MODE == MODE_PAIR) ? y0 : tn * BNW;
 
   // K steps.  Step `it` always uses stage it % STAGES and the main loop is
   // unrolled over the stage ring, so every stage offset is a compile-time
@@ -216,7 +235,8 @@ __device__ __forceinline__ void tiled_tile(const uint16_t* __restrict__ A,
   const uint32_t wbytes = K > 0 ? (uint32_t)(((size_t)(K - 1) * ldw + wcols) * 2) : 0u;
   const i32x4 rsA = make_rsrc(A, (uint32_t)((size_t)M * K * 2));
   const i32x4 rsW1 = make_rsrc(W1, wbytes);
-  const i32x4 rsW2 = (MODE == MODE_SYNC) ? make_rsrc(W2, wbytes) : rsW1;
+  const i32x4 rsW2 =
+      (MODE == MODE_SYNC || MODE == MODE_PAIR) ? make_rsrc(W2, wbytes) : rsW1;
   const uint32_t lds0 = lds_addr(smem);
 
   uint32_t a_off[C::A_LOADS];
@@ -232,9 +252,9 @@ __device__ __forceinline__ void tiled_tile(const uint16_t* __restrict__ A,
   uint32_t w_off[C::W_LOADS];  // kOutOfRange-based if the column is out of range
 #pragma unroll
   for (int i = 0; i < C::W_LOADS; ++i) {
-    const int p = tid + C::kThreads * i;
-    const int row = p / C::WCH;
-    const int c = (p % C::WCH) ^ C::w_swz(row);
+    const int p = (tid + C::kThreads * i) % (BK * C::WCHP);  // chunk within its part
+    const int row = p / C::WCHP;
+    const int c = (p % C::WCHP) ^ C::w_swz(row);
     w_off[i] = (wc0 + c * 8 < wcols) ? (uint32_t)(row * ldw + wc0 + c * 8) * 2u : kOutOfRange;
   }
 
@@ -258,7 +278,9 @@ __device__ __forceinline__ void tiled_tile(const uint16_t* __restrict__ A,
       const int p0 = C::kThreads * i + 64 * wave_u;
       const bool own = p0 < C::W_CHUNKS;
       const uint32_t off = own ? w_off[i] + (uint32_t)k0 * (uint32_t)ldw * 2u : kOutOfRange;
-      lds_dma16(own ? sbase + C::A_BYTES + p0 * 16 : lds0 + C::JUNK, off, up ? rsW2 : rsW1);
+      // the W2 part of a pair stage: this wave's chunks all lie in one part
+      const bool w2 = up || (MODE == MODE_PAIR && p0 >= BK * C::WCHP);
+      lds_dma16(own ? sbase + C::A_BYTES + p0 * 16 : lds0 + C::JUNK, off, w2 ? rsW2 : rsW1);
     }
   };
 
@@ -281,11 +303,13 @@ __device__ __forceinline__ void tiled_tile(const uint16_t* __restrict__ A,
     const int kk = sub * 16;
     if (r < 2 * C::FW) {
       const int fw = r >> 1, h = r & 1;
-      const int col = w_col + fw * 32;
+      const int wcol = w_col + fw * 32;
+      const int part = (C::WPARTS == 1) ? 0 : wcol / C::PART_COLS;
+      const int col = wcol - part * C::PART_COLS;
       const int row = kk + w_row + 4 * h;
       const int chunk = (col >> 3) ^ C::w_swz(row);
-      const u32x2 v =
-          lds_read_tr16(st + C::A_BYTES + row * (BNW * 2) + chunk * 16 + ((col >> 2) & 1) * 8);
+      const u32x2 v = lds_read_tr16(st + C::A_BYTES + part * C::PART_BYTES +
+                                    row * (C::PART_COLS * 2) + chunk * 16 + ((col >> 2) & 1) * 8);
       wf[fb][fw][2 * h] = v[0];
       wf[fb][fw][2 * h + 1] = v[1];
     } else {
@@ -409,8 +433,49 @@ __device__ __forceinline__ void tiled_tile(const uint16_t* __restrict__ A,
   // ---- epilogue: bf16 tile through LDS, then 16-byte row stores -------------------
   wait_vmcnt<0>();
   __syncthreads();
-  uint16_t* ys = reinterpret_cast<uint16_t*>(smem);  // [BM][YLD]
   const int h32 = lane >> 5;
+  if constexpr (MODE == MODE_PAIR) {
+    // The Gate waves hand SiLU(Gate) of their rows and columns to the Up
+    // waves through LDS in fp32; the Up waves form the products and store Y
+    // straight from registers, 4 columns (8 bytes) per lane.
+    float* ss = reinterpret_cast<float*>(smem);  // [BM][SLD]
+    const bool gate_wave = wn * C::WTW < C::PART_COLS;
+    if (gate_wave) {
+#pragma unroll
+      for (int i = 0; i < C::FW; ++i)
+#pragma unroll
+        for (int j = 0; j < C::FA; ++j)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int row = a_row + j * 32;
+            const int col = wn * C::WTW + i * 32 + 8 * q + 4 * h32;
+            const f32x16& d = acc[0][i][j];
+            *reinterpret_cast<f32x4*>(ss + row * C::SLD + col) =
+                f32x4{silu(d[4 * q]), silu(d[4 * q + 1]), silu(d[4 * q + 2]), silu(d[4 * q + 3])};
+          }
+    }
+    __syncthreads();
+    if (!gate_wave) {
+#pragma unroll
+      for (int i = 0; i < C::FW; ++i)
+#pragma unroll
+        for (int j = 0; j < C::FA; ++j)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int row = a_row + j * 32;
+            const int col = wn * C::WTW - C::PART_COLS + i * 32 + 8 * q + 4 * h32;
+            const f32x4 sv = *reinterpret_cast<const f32x4*>(ss + row * C::SLD + col);
+            const f32x16& d = acc[0][i][j];
+            const int gr = m0 + row, gc = y0 + col;
+            if (gr < M && gc < N)  // N % 8 == 0: four columns are in range together
+              *reinterpret_cast<u32x2*>(Y + (size_t)gr * ldy + gc) =
+                  u32x2{pack_bf16x2(sv[0] * d[4 * q], sv[1] * d[4 * q + 1]),
+                        pack_bf16x2(sv[2] * d[4 * q + 2], sv[3] * d[4 * q + 3])};
+          }
+    }
+    return;
+  }
+  uint16_t* ys = reinterpret_cast<uint16_t*>(smem);  // [BM][YLD]
 #pragma unroll
   for (int i = 0; i < C::FW; ++i)
 #pragma unroll
@@ -2816,6 +2881,12 @@ static const KernelConfig kConfigs[] = {
     // ---- fragment-ordered W_fused: whole slabs, then quarter slabs --------
     {VAR_PACKED, 1, 16, Packed<1, 8, 8>::COLS_Y, 32, 8, 8, Packed<1, 8, 8>::LDS_BYTES,
      &launch_packed_mixed<8>},                                      // 88
+    // ---- sync family on W1 and W2 as stored: Gate and Up wave groups share
+    //      each A k-tile, SiLU(Gate) handed over through LDS ----------------
+    TILED_SPLIT(MODE_PAIR, VAR_SYNC, 256, 256, 32, 4, 4, 2, 4, 2),  // 89
+    TILED(MODE_PAIR, VAR_SYNC, 128, 256, 32, 4, 2, 2),              // 90
+    TILED(MODE_PAIR, VAR_SYNC, 128, 128, 32, 4, 2, 2),              // 91
+    TILED(MODE_PAIR, VAR_SYNC, 64, 128, 32, 4, 2, 2),               // 92
 };
 
 int config_count() { return (int)(sizeof(kConfigs) / sizeof(kConfigs[0])); }

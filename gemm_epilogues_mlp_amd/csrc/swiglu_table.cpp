@@ -31,7 +31,7 @@ struct ShapeEntry {
 const ShapeEntry kTable[] = {
     // Qwen2.5-0.5B MLP, M = 128: 64-row tiles with deep stage rings
     {VAR_INTERLEAVE, 128, 4864, 896, 3},
-    {VAR_SYNC, 128, 4864, 896, 29},
+    {VAR_SYNC, 128, 4864, 896, 92},  // pair tile: 11.6 vs 14.8 us (phase tile 29)
     {VAR_GEMM, 128, 4864, 896, 30},
     {VAR_F8, 128, 4864, 896, 46},
     {VAR_F8_SYNC, 128, 4864, 896, 55},
@@ -44,7 +44,7 @@ const ShapeEntry kTable[] = {
     // round as quarter tiles (the persistent tile loop, configs 36 and 37, is
     // level with them under the benchmark: 119.2 vs 118.0 us)
     {VAR_INTERLEAVE, 2048, 8960, 1536, 40},
-    {VAR_SYNC, 2048, 8960, 1536, 42},
+    {VAR_SYNC, 2048, 8960, 1536, 89},  // pair tile: 119-123 vs 158 us (phase tile 42)
     {VAR_GEMM, 2048, 8960, 1536, 41},
     {VAR_F8, 2048, 8960, 1536, 43},
     {VAR_F8_SYNC, 2048, 8960, 1536, 53},
@@ -66,7 +66,7 @@ const ShapeEntry kTable[] = {
     {VAR_MX_SYNC, 16, 18944, 3584, 84},
     // Qwen2.5-7B MLP, prefill M = 8192 (persistent: level, 1774 us both)
     {VAR_INTERLEAVE, 8192, 18944, 3584, 40},
-    {VAR_SYNC, 8192, 18944, 3584, 42},
+    {VAR_SYNC, 8192, 18944, 3584, 89},  // pair tile: 1807-1820 vs 2414-2476 us
     {VAR_GEMM, 8192, 18944, 3584, 41},
     {VAR_F8, 8192, 18944, 3584, 43},
     {VAR_F8_SYNC, 8192, 18944, 3584, 53},
@@ -77,7 +77,7 @@ const ShapeEntry kTable[] = {
     {VAR_MX_SYNC, 8192, 18944, 3584, 83},
     // Qwen2.5-72B MLP, M = 4096 (persistent: 3078-3097 vs 3036-3045 us)
     {VAR_INTERLEAVE, 4096, 29568, 8192, 40},
-    {VAR_SYNC, 4096, 29568, 8192, 42},
+    {VAR_SYNC, 4096, 29568, 8192, 89},  // pair tile: 3011-3021 vs 4079-4134 us
     {VAR_GEMM, 4096, 29568, 8192, 41},
     {VAR_F8, 4096, 29568, 8192, 43},
     {VAR_F8_SYNC, 4096, 29568, 8192, 53},
@@ -142,9 +142,15 @@ int select_config(int variant, long long M, long long N, long long K, int cu_cou
       if (M <= 192) return (wide && M > 32) ? 54 : 55;
       return (M <= 384 || few_big) ? 54 : 53;
     case VAR_SYNC:
+      // from M = 65 the pair tiles (Gate and Up wave groups over one A
+      // k-tile): on wide matrices 128-row tiles to M = 128 and the 256-row
+      // eight-wave tile above; otherwise 128 x 64 (N >= 8192) or 64 x 64
+      // output tiles to M = 192, then the 256-row tile unless it leaves most
+      // CUs idle
       if (M <= 64) return (wide && M > 16) ? 8 : (M <= 32 ? 12 : 13);
-      if (M <= 192) return wide ? 8 : 29;
-      return (M <= 384 || few_big) ? 8 : 42;
+      if (wide) return M <= 128 ? 90 : 89;
+      if (M <= 192) return N >= 8192 ? 91 : 92;
+      return few_big ? 91 : 89;
     case VAR_GEMM:
       if (M <= 16) return wide ? 18 : 30;
       if (M <= 192) return wide ? 16 : 30;
@@ -163,8 +169,10 @@ int recommend_layout(long long M, long long N, long long K, int cu_count) {
   (void)K;
   // The page prefers the sync kernel above M = 2048.  On MI355X the interleave
   // kernel was faster at every measured M (0.5B-72B shapes, M = 16..8192): it
-  // loads A once and keeps every accumulator busy in every K step, while the
-  // sync kernel alternates between half of its registers (Gate, then Up).
+  // loads A once and keeps every accumulator busy in every K step.  The sync
+  // family's pair tile does both as well and comes within 2 % at the 72B shape
+  // (3011-3021 vs 2946-2969 us) and 7 % at the 1.5B shape; the phase tiles,
+  // which run Gate and then Up over A twice, are 1.3-1.4x slower.
   // Up to M = 64 the same Kernel-2 order on fragment-ordered weights streams
   // them fastest (1.16-1.6x the interleaved layout at M = 16 ... 64), except
   // on wide matrices above M = 16, where the LDS-tiled kernel wins (7B: 54.8

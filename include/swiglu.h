@@ -149,7 +149,10 @@ swiglu_status_t swiglu_create(swiglu_handle_t* out, int device);
 swiglu_status_t swiglu_destroy(swiglu_handle_t h);
 
 /* Fused forward [RT §Metodologia]: SEPARATE layout runs the sync family
- * (Kernel-1), INTERLEAVED runs the interleave family (Kernel-2), PACKED runs
+ * (Kernel-1: from M = 65 a Gate and an Up wave group share each A k-tile and
+ * SiLU(Gate) is applied to the Gate group's register-resident accumulator;
+ * the phase tiles that run the Gate and then the Up K loop are selectable by
+ * config id), INTERLEAVED runs the interleave family (Kernel-2), PACKED runs
  * the Kernel-2 order on fragment-ordered W_fused (split-K weight streaming, any
  * M; made for decode-sized batches); the tile configuration comes from the
  * per-shape table. */

@@ -53,11 +53,13 @@ def rewrite(src: str) -> str:
 #  4: the FP8 tile in MX mode lets the step before a scale group starts leave
 #     that group's scale chunks in flight
 #  5: the FP8 tile's K loop waits for one K step fewer of its DMA
+#  6: the pair tile's Up waves read SiLU(Gate) without the barrier after the
+#     Gate waves' writes
 PLANTS = [
     (r"^        wait_vmcnt<\(STAGES - 2\) \* C::LOADS>\(\);$",
      "        if (::g_emu_plant == 1) wait_vmcnt<(STAGES - 1) * C::LOADS>();"
      " else wait_vmcnt<(STAGES - 2) * C::LOADS>();", 1),
-    (r"^  wait_vmcnt<0>\(\);\n  __syncthreads\(\);\n(?=  uint16_t\* ys = |  // The lane's epilogue)",
+    (r"^  wait_vmcnt<0>\(\);\n  __syncthreads\(\);\n(?=  const int h32 = lane >> 5;|  // The lane's epilogue)",
      "  wait_vmcnt<0>();\n  if (::g_emu_plant != 2) __syncthreads();\n", 2),
     (r"^(  // the zero loads issued past the last tile still write LDS\n)  wait_vmcnt<0>\(\);$",
      "\\1  if (::g_emu_plant != 3) wait_vmcnt<0>();", 1),
@@ -65,6 +67,8 @@ PLANTS = [
      "    if (::g_emu_plant == 4 && C::MX && T == 7) wait_vmcnt<C::in_flight(T) + 1>();"
      " else if (::g_emu_plant == 5) wait_vmcnt<C::in_flight(T) + C::LOADS>();"
      " else wait_vmcnt<C::in_flight(T)>();", 1),
+    (r"^    __syncthreads\(\);\n(?=    if \(!gate_wave\) \{)",
+     "    if (::g_emu_plant != 6) __syncthreads();\n", 1),
 ]
 
 

@@ -47,7 +47,8 @@ def test_all_configs_on_the_parity_shapes(emu):
 # step short (bf16 and FP8 tiles), an epilogue that reuses the stage ring
 # without the barrier that ends the K loop, a persistent kernel that does not
 # drain its last loads, an MX K loop that reads a scale group's bytes while
-# their DMA may still be in flight.
+# their DMA may still be in flight, a pair tile whose Up waves read the Gate
+# waves' hand-over without the barrier between them.
 PLANTED = [
     (1, 40, 128, "LDS read while a DMA into it may land"),
     (1, 42, 128, "LDS read while a DMA into it may land"),
@@ -57,6 +58,9 @@ PLANTED = [
     (4, 56, 1088, "LDS read while a DMA into it may land"),
     (4, 82, 1088, "LDS read while a DMA into it may land"),
     (5, 43, 1088, "LDS read while a DMA into it may land"),
+    (1, 89, 128, "LDS read while a DMA into it may land"),
+    (2, 89, 128, "LDS accesses of two waves between the same barriers"),
+    (6, 89, 128, "LDS accesses of two waves between the same barriers"),
 ]
 # the plants of the FP8 tile's K loop run on a smaller launch with 17 K steps
 # (two scale groups of 8 and a short last one)
@@ -76,11 +80,17 @@ def test_lds_ordering_check_catches_planted_mistakes(emu, plant, cfg, K, message
 CASES = [
     (2008, 4216, 72, [40, 42]),        # 264 tiles: 256 big + 8 split
     (2008, 8440, 72, [41]),            # the same for the 256-column GEMM tiles
-    (2048, 8960, 40, [40, 41, 42]),    # 1.5B M and N: 512 big + 48 split
+    (2048, 8960, 40, [40, 41, 42, 89]),  # 1.5B M and N: 512 big + 48 split
+    # the pair tiles (sync family on W1, W2 as stored): split tail at the
+    # 1.5B shape above, ragged edges, the smaller tiles at mid and small M
+    (2008, 4216, 72, [89, 90, 91, 92]),
+    (512, 18944, 64, [90, 91]),
+    (128, 4864, 40, [92]),
+    (4096, 29568, 40, [89]),           # 72B M and N: whole rounds, no split
     (2008, 4216, 1088, [43, 56, 82]),  # FP8, MX and MX sync split tiles: 17 steps, 3 scale groups a phase
     # the persistent tiles: whole rings of K (K = 128, 256), two or more tiles
     # per workgroup, with and without a quarter-tile last round, ragged M and N
-    (2048, 8960, 128, [36, 40, 42, 43]),  # 560 tiles: 2 per workgroup + 48 as quarters
+    (2048, 8960, 128, [36, 40, 42, 43, 89]),  # 560 tiles: 2 per workgroup + 48 as quarters
     (4000, 8440, 256, [37]),           # 528 GEMM tiles: + 16 as quarters, ragged M and N
     (4000, 9000, 128, [36]),           # 1136 tiles: a last round of 112, not split
     (4000, 9400, 128, [37]),           # 592 GEMM tiles: a last round of 80, not split

@@ -94,6 +94,31 @@ def test_unfused_config_parity(handle, cases, cfg, shape):
     assert_parity(y, y_ref, f"unfused Y cfg {cfg} {shape}")
 
 
+# The sync family's pair tiles (Gate and Up wave groups over the same A
+# k-tiles) sum each output's Gate and Up products in the same order, with the
+# same MFMA blocks, as the sync tiles that run the Gate phase and then the Up
+# phase: both must give the same Y bit for bit (signed zeros aside).
+PAIR_CONFIGS = [89, 90, 91, 92]
+
+
+@pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_pair_tiles_match_phase_tiles_bitwise(handle, cases, shape):
+    M, N, K = shape
+    c = cases[shape]
+    ref = None
+    for cfg in [8] + PAIR_CONFIGS:
+        assert sw.swiglu_config_info(cfg)["variant"] == sw.VARIANT_SYNC
+        log(f"sync config {cfg} bitwise shape {shape}")
+        y = host(Run(handle).fused(dev(c["a"]), dev(c["w1"]), dev(c["w2"]), M, N, K,
+                                   sw.LAYOUT_SEPARATE, cfg, sw.VARIANT_SYNC))
+        y = np.where(y == np.uint16(0x8000), np.uint16(0), y.astype(np.uint16))
+        if ref is None:
+            ref = y
+        else:
+            bad = np.flatnonzero(y != ref)
+            assert bad.size == 0, f"config {cfg} differs from config 8 at {bad[:8]} of {shape}"
+
+
 def _split_configs():
     """bf16 split-tail configurations (the FP8 ones are covered in test_gpu_fp8.py)."""
     return [i for i in range(sw.swiglu_config_count())
