@@ -141,16 +141,19 @@ int select_config(int variant, long long M, long long N, long long K, int cu_cou
     case VAR_F8_SYNC:
       if (M <= 192) return (wide && M > 32) ? 54 : 55;
       return (M <= 384 || few_big) ? 54 : 53;
-    case VAR_SYNC:
+    case VAR_SYNC: {
       // from M = 65 the pair tiles (Gate and Up wave groups over one A
-      // k-tile): on wide matrices 128-row tiles to M = 128 and the 256-row
-      // eight-wave tile above; otherwise 128 x 64 (N >= 8192) or 64 x 64
-      // output tiles to M = 192, then the 256-row tile unless it leaves most
-      // CUs idle
+      // k-tile): the largest output tile -- 256 x 128 (above M = 128),
+      // 128 x 128, 128 x 64 -- whose launch still gives at least half of the
+      // CUs a tile, else 64 x 64
       if (M <= 64) return (wide && M > 16) ? 8 : (M <= 32 ? 12 : 13);
-      if (wide) return M <= 128 ? 90 : 89;
-      if (M <= 192) return N >= 8192 ? 91 : 92;
-      return few_big ? 91 : 89;
+      const long long t256 = (M + 255) / 256 * ((N + 127) / 128);
+      const long long t128 = (M + 127) / 128 * ((N + 127) / 128);
+      if (M > 128 && 2 * t256 >= cus) return 89;
+      if (2 * t128 >= cus) return 90;
+      if (4 * t128 >= cus) return 91;  // 128 x 64 tiles: twice as many
+      return 92;
+    }
     case VAR_GEMM:
       if (M <= 16) return wide ? 18 : 30;
       if (M <= 192) return wide ? 16 : 30;
