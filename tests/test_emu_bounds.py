@@ -12,6 +12,7 @@ DMA or other wave's access that could land on the same bytes meanwhile.
 Data values are not checked (the threads run one after another); parity is
 the GPU tests' job.
 """
+import concurrent.futures as cf
 import os
 import subprocess
 import sys
@@ -36,8 +37,35 @@ def _run(exe, *args, timeout=600):
     return r.returncode, r.stdout + r.stderr
 
 
-def test_all_configs_on_the_parity_shapes(emu):
-    rc, out = _run(emu)
+# Every emulation run is its own process, so the module starts them all at
+# once (the test functions below only collect their results): the small
+# launches on up to 8 host threads, the runs with tensors near 2 GiB (a few GiB
+# of host memory each) two at a time.
+_SMALL_WORKERS = max(1, min(8, os.cpu_count() or 1))
+_LARGE_WORKERS = 2
+
+
+@pytest.fixture(scope="module")
+def runs(emu):
+    small = cf.ThreadPoolExecutor(_SMALL_WORKERS)
+    large = cf.ThreadPoolExecutor(_LARGE_WORKERS)
+    futs = {}
+    for args in _small_jobs():
+        futs[args] = small.submit(_run, emu, *args)
+    for args in _large_jobs():
+        futs[args] = large.submit(_run, emu, *args, timeout=900)
+
+    def result(*args):
+        args = tuple(map(str, args))
+        return futs[args].result() if args in futs else _run(emu, *args)
+
+    yield result
+    for ex in (small, large):
+        ex.shutdown(wait=False, cancel_futures=True)
+
+
+def test_all_configs_on_the_parity_shapes(runs):
+    rc, out = runs()
     assert rc == 0 and "errors: 0" in out, out[-4000:]
     assert out.count(": ok") >= 5 * 40  # every config ran on every shape
 
@@ -68,9 +96,9 @@ PLANT_SHAPE = {128: (2048, 8960, 128), 1088: (2008, 4216, 1088)}
 
 
 @pytest.mark.parametrize("plant,cfg,K,message", PLANTED)
-def test_lds_ordering_check_catches_planted_mistakes(emu, plant, cfg, K, message):
+def test_lds_ordering_check_catches_planted_mistakes(runs, plant, cfg, K, message):
     # the same launch without the plant is one of the workload cases below
-    rc, out = _run(emu, "--plant", plant, "--race-blocks", 8, "--shape", *PLANT_SHAPE[K], cfg)
+    rc, out = runs(*_plant_args(plant, cfg, K))
     assert rc != 0 and message in out, out[-4000:]
 
 
@@ -158,21 +186,20 @@ RACE_BLOCKS = 24
 
 
 @pytest.mark.parametrize("case", CASES, ids=lambda c: f"{c[0]}x{c[1]}x{c[2]}")
-def test_table_configs_at_workload_sizes(emu, case):
+def test_table_configs_at_workload_sizes(runs, case):
     M, N, K, cfgs = case
     for cfg in cfgs:
-        rc, out = _run(emu, "--race-blocks", RACE_BLOCKS, "--shape", M, N, K, cfg)
+        rc, out = runs(*_case_args(M, N, K, cfg))
         assert rc == 0 and "errors: 0" in out, out[-4000:]
 
 
 # the split-K streaming configs with other numbers of pieces of K: one (no
 # handoff), two, more pieces than a shape has K steps (empty pieces)
-@pytest.mark.parametrize("ksplit", [1, 2, 7, 64])
-def test_splitk_pieces(emu, ksplit):
-    for shape in ((13, 264, 200), (16, 2368, 3584), (1, 8, 8)):
-        for cfg in (85, 86, 87):
-            rc, out = _run(emu, "--ksplit", ksplit, "--race-blocks", RACE_BLOCKS, "--shape",
-                           *shape, cfg)
+@pytest.mark.parametrize("ksplit", [1, 2, 7, 64])  # SPLITK_PIECES
+def test_splitk_pieces(runs, ksplit):
+    for shape in SPLITK_SHAPES:
+        for cfg in SPLITK_CONFIGS:
+            rc, out = runs(*_splitk_args(ksplit, shape, cfg))
             assert rc == 0 and "errors: 0" in out, out[-4000:]
 
 
@@ -200,9 +227,45 @@ LIMIT_CASES = [
 
 
 @pytest.mark.parametrize("case", LIMIT_CASES, ids=lambda c: f"{c[0]}x{c[1]}x{c[2]}")
-def test_tensors_just_under_2gib(emu, case):
+def test_tensors_just_under_2gib(runs, case):
     M, N, K, cfgs, last = case
     for cfg in cfgs:
-        rc, out = _run(emu, "--no-races", "--last-blocks", last, "--shape", M, N, K, cfg,
-                       timeout=900)
+        rc, out = runs(*_limit_args(M, N, K, cfg, last))
         assert rc == 0 and "errors: 0" in out, out[-4000:]
+
+
+SPLITK_PIECES = [1, 2, 7, 64]
+SPLITK_SHAPES = ((13, 264, 200), (16, 2368, 3584), (1, 8, 8))
+SPLITK_CONFIGS = (85, 86, 87)
+
+
+# command lines of the emulation driver, one per run
+def _plant_args(plant, cfg, K):
+    return tuple(map(str, ("--plant", plant, "--race-blocks", 8, "--shape", *PLANT_SHAPE[K],
+                           cfg)))
+
+
+def _case_args(M, N, K, cfg):
+    return tuple(map(str, ("--race-blocks", RACE_BLOCKS, "--shape", M, N, K, cfg)))
+
+
+def _splitk_args(ksplit, shape, cfg):
+    return tuple(map(str, ("--ksplit", ksplit, "--race-blocks", RACE_BLOCKS, "--shape", *shape,
+                           cfg)))
+
+
+def _limit_args(M, N, K, cfg, last):
+    return tuple(map(str, ("--no-races", "--last-blocks", last, "--shape", M, N, K, cfg)))
+
+
+def _small_jobs():
+    jobs = [()]
+    jobs += [_plant_args(p, c, K) for p, c, K, _ in PLANTED]
+    jobs += [_case_args(M, N, K, c) for M, N, K, cfgs in CASES for c in cfgs]
+    jobs += [_splitk_args(k, s, c) for k in SPLITK_PIECES for s in SPLITK_SHAPES
+             for c in SPLITK_CONFIGS]
+    return jobs
+
+
+def _large_jobs():
+    return [_limit_args(M, N, K, c, last) for M, N, K, cfgs, last in LIMIT_CASES for c in cfgs]
